@@ -1,0 +1,296 @@
+"""Benchmark of the delta-rule operator on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one chunkwise Gated DeltaNet prefill of the workload
+B=4, H=8, T=2048, d_k=d_v=128, bf16 (seeded synthetic inputs resident in HBM),
+i.e. dn_chunk_fwd = the chunk-parallel UT/WY phase followed by the sequential
+inter-chunk scan. The JSON line reports whole-job token-heads/s (B*H*T per
+second) as `value`, the roofline of the dominant kernel (timed live with HIP
+events on the stream it runs on), the fp64 CPU oracle timed on this host as
+`cpu_baseline`, and, under `decode`, the fused decode step of
+B=256 x H=16, d=128 (1000 steps, fp32 state updated in place) in state-HBM GB/s
+against the HBM peak. The other workloads (long-context prefill, KDA prefill,
+the fp32 DeltaNet recurrent and chunked forms) are timed under `workloads`.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill tokens/s (B*H*T/s) at d=128 + decode state HBM GB/s, % of peak"
+PEAK_BF16_TFLOPS = 2516.6     # dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0         # HBM3E
+C = 64
+
+# Algorithmic work per token and head at d_k = d_v = d (full 64 x 64 tiles, as
+# the chunk algorithm is written): the chunk-parallel phase does K K^T, Q K^T,
+# W = T X and u = T V (4 x 2*C*d); the scan does W S, Q~ S, K~^T U (3 x 2*d*d)
+# and attn U (2*C*d).
+def flops_prep(d):
+    return 4 * 2 * C * d
+
+
+def flops_scan(d):
+    return 3 * 2 * d * d + 2 * C * d
+
+
+def bytes_prefill(B, H, T, d, esize=2):
+    """Compulsory HBM bytes: q, k, v, beta, g read, o written, S_final written."""
+    return B * H * T * (4 * d * esize + 2 * esize) + B * H * d * d * 4
+
+
+def decode_bytes_per_step(B, H, d, esize=2):
+    """State read + write, q, k, v, beta, g read, o written."""
+    return B * H * (2 * d * d * 4 + 3 * d * esize + 2 * esize + d * esize)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def event_time_ms(torch, fn, reps):
+    """Average duration of fn() (one kernel launch) bracketed by events on the current stream."""
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record()
+        fn()
+        ends[i].record()
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this operator shards over (sequence, head) with "
+              "no communication, and multi-GPU runs are not part of this build (got --gpus %d)"
+              % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import delta_rule_recurrent_amd as dn
+    import synthetic
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    def to_dev(d):
+        return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+    # ------------------------------------------------------------------ prefill
+    name = "gdn_prefill_b4_h8_t2048_d128"
+    cfg = synthetic.CONFIGS[name]
+    B, H, T, d = cfg["B"], cfg["H"], cfg["T"], cfg["dk"]
+    log("generating", name)
+    inp_cpu = synthetic.make_config(name)
+    inp = to_dev(inp_cpu)
+    ws = torch.empty(dn.workspace_bytes(B, H, T, d, d, torch.bfloat16), dtype=torch.uint8, device=dev)
+    o = torch.empty(B, H, T, d, dtype=torch.bfloat16, device=dev)
+    S_final = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+
+    def step():
+        dn.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], None, o=o,
+                     S_final=S_final, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    tokens = B * H * T
+    value = tokens / (ms_step * 1e-3)
+    log("prefill %.4f ms/step  %.3e token-heads/s (wall %.3f s for %d steps)"
+        % (ms_step, value, t_wall, args.steps))
+
+    # per-kernel live timing of the two phases (same stream, events around each launch)
+    prep_ms = event_time_ms(torch, lambda: dn.chunk_prep(inp["q"], inp["k"], inp["v"], inp["beta"],
+                                                         inp["g"], ws), args.steps)
+    scan_ms = event_time_ms(torch, lambda: dn.chunk_scan(o, ws, None, S_final), args.steps)
+    kern = {
+        "chunk_prep_kernel": dict(ms=prep_ms, flop=flops_prep(d) * tokens),
+        "chunk_scan_kernel": dict(ms=scan_ms, flop=flops_scan(d) * tokens),
+    }
+    for k_, v_ in kern.items():
+        v_["tflops"] = v_["flop"] / (v_["ms"] * 1e-3) / 1e12
+        v_["frac_mfma"] = v_["tflops"] / PEAK_BF16_TFLOPS
+        log("  %s %.4f ms  %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)"
+            % (k_, v_["ms"], v_["tflops"], 100 * v_["frac_mfma"]))
+    dom = max(kern, key=lambda k_: kern[k_]["ms"])
+    total_flop = (flops_prep(d) + flops_scan(d)) * tokens
+    path_tflops = total_flop / (ms_step * 1e-3) / 1e12
+    roofline = {
+        "kernel": dom,
+        "bound": "mfma",
+        "achieved": round(kern[dom]["tflops"], 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(kern[dom]["frac_mfma"], 4),
+        "traffic": None,
+        "algorithmic_flop_per_launch": kern[dom]["flop"],
+        "avg_launch_ms": round(kern[dom]["ms"], 5),
+    }
+
+    # parity of the benchmarked output and the CPU baseline (fp64 oracle, same inputs)
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "H": H, "T": T, "d_k": d, "d_v": d, "chunk": C,
+                   "variant": "gated_deltanet", "S0": "zeros"},
+        "roofline": roofline,
+        "prefill_path": {
+            "tflops": round(path_tflops, 2), "frac_mfma": round(path_tflops / PEAK_BF16_TFLOPS, 4),
+            "gbs_algorithmic": round(bytes_prefill(B, H, T, d) / (ms_step * 1e-3) / 1e9, 1),
+            "frac_hbm": round(bytes_prefill(B, H, T, d) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "kernels": {k_: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
+                             for kk, vv in v_.items()} for k_, v_ in kern.items()},
+        },
+    }
+
+    if not args.no_cpu:
+        import oracle
+
+        nthreads = len(os.sched_getaffinity(0))
+        log("cpu oracle on %d threads" % nthreads)
+        t = time.perf_counter()
+        o_ref, S_ref = oracle.recurrent(inp_cpu["q"], inp_cpu["k"], inp_cpu["v"], inp_cpu["beta"],
+                                        inp_cpu["g"], None, nthreads=nthreads)
+        t = time.perf_counter() - t
+        result["cpu_baseline"] = {
+            "value": round(tokens / t, 1), "unit": "tokens/s",
+            "cores": oracle.max_threads(nthreads), "kind": "oracle",
+            "sample": "the whole workload (B=4, H=8, T=2048, d=128; fp64 token-by-token "
+                      "recurrence, one rep, %.2f s)" % t,
+        }
+        og = o.float().cpu().double().numpy()
+        sg = S_final.cpu().double().numpy()
+        result["parity"] = {
+            "o": float(np.abs(og - o_ref).max() / np.abs(o_ref).max()),
+            "S_final": float(np.abs(sg - S_ref).max() / np.abs(S_ref).max()),
+            "bound": 2e-2, "metric": "max|gpu-ref|/max|ref|",
+        }
+        log("cpu oracle %.2f s, parity %s" % (t, result["parity"]))
+
+    # ------------------------------------------------------------------- decode
+    if not args.no_decode:
+        name_d = "gdn_decode_b256_h16_d128"
+        cd = synthetic.CONFIGS[name_d]
+        Bd, Hd, dd = cd["B"], cd["H"], cd["dk"]
+        nsteps = args.decode_steps
+        log("generating", name_d, nsteps, "steps")
+        dinp = to_dev(synthetic.make_config(name_d, steps=nsteps))
+        S = dinp["S0"].clone()
+        od = torch.empty(Bd, Hd, dd, dtype=torch.bfloat16, device=dev)
+        xs = [(dinp["q"][s], dinp["k"][s], dinp["v"][s], dinp["beta"][s], dinp["g"][s])
+              for s in range(nsteps)]
+
+        def dstep(s):
+            q_, k_, v_, b_, g_ = xs[s]
+            dn.decode_step(q_, k_, v_, b_, g_, S, o=od)
+
+        for s in range(min(10, nsteps)):
+            dstep(s)
+        torch.cuda.synchronize()
+        runs = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for s in range(nsteps):
+                dstep(s)
+            e1.record()
+            torch.cuda.synchronize()
+            runs.append(e0.elapsed_time(e1))
+        loop_ms = sorted(runs)[1]
+        per_launch = event_time_ms(torch, lambda: dstep(0), 200)
+        bps = decode_bytes_per_step(Bd, Hd, dd)
+        gbs_loop = bps * nsteps / (loop_ms * 1e-3) / 1e9
+        gbs_kernel = bps / (per_launch * 1e-3) / 1e9
+        result["decode"] = {
+            "workload": name_d, "B": Bd, "H": Hd, "d": dd, "steps": nsteps,
+            "ms_per_1000_steps": round(loop_ms * 1000.0 / nsteps, 3),
+            "us_per_step": round(loop_ms * 1000.0 / nsteps, 2),
+            "token_heads_per_s": round(Bd * Hd * nsteps / (loop_ms * 1e-3), 1),
+            "state_gbs": round(gbs_loop, 1), "frac_hbm": round(gbs_loop / PEAK_HBM_GBS, 4),
+            "bytes_per_step": bps,
+            "roofline": {"kernel": "decode_step_kernel", "bound": "hbm",
+                         "achieved": round(gbs_kernel, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs_kernel / PEAK_HBM_GBS, 4), "traffic": None,
+                         "avg_launch_ms": round(per_launch, 5)},
+        }
+        log("decode %.2f us/step  %.1f GB/s loop, %.1f GB/s per launch"
+            % (loop_ms * 1000 / nsteps, gbs_loop, gbs_kernel))
+        del dinp, xs, S
+
+    # ---------------------------------------------------------- other workloads
+    if not args.no_workloads:
+        wl = {}
+        for wname, form in (("gdn_prefill_b1_h16_t65536_d128", "chunk"),
+                            ("kda_prefill_b2_h16_t8192_d128", "chunk"),
+                            ("deltanet_fp32_t512_d64", "chunk"),
+                            ("deltanet_fp32_t512_d64", "recurrent")):
+            c = synthetic.CONFIGS[wname]
+            log("generating", wname)
+            x = to_dev(synthetic.make_config(wname))
+            Bw, Hw, Tw, dw = c["B"], c["H"], c["T"], c["dk"]
+            dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+            kda = c["kind"] == "kda"
+            wsw = torch.empty(max(dn.workspace_bytes(Bw, Hw, Tw, dw, dw, dt), 1), dtype=torch.uint8,
+                              device=dev)
+            ow = torch.empty(Bw, Hw, Tw, dw, dtype=dt, device=dev)
+            Sw = torch.empty(Bw, Hw, dw, dw, dtype=torch.float32, device=dev)
+            if form == "chunk":
+                f = dn.kda_chunk_fwd if kda else dn.chunk_fwd
+                run = lambda: f(x["q"], x["k"], x["v"], x["beta"], x["g"], None, o=ow, S_final=Sw,
+                                workspace=wsw)
+            else:
+                run = lambda: dn.recurrent_fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], None)
+            for _ in range(3):
+                run()
+            reps = 5 if Tw >= 8192 else 20
+            ms = event_time_ms(torch, run, reps)
+            tok = Bw * Hw * Tw
+            entry = {"form": form, "ms": round(ms, 4), "tokens_per_s": round(tok / (ms * 1e-3), 1)}
+            if form == "chunk":
+                tf = (flops_prep(dw) + flops_scan(dw)) * tok / (ms * 1e-3) / 1e12
+                entry["tflops"] = round(tf, 2)
+                entry["frac_mfma"] = round(tf / (PEAK_BF16_TFLOPS if dt == torch.bfloat16 else 157.3), 4)
+                entry["gbs_algorithmic"] = round(bytes_prefill(Bw, Hw, Tw, dw, 2 if dt == torch.bfloat16 else 4)
+                                                 / (ms * 1e-3) / 1e9, 1)
+            wl["%s/%s" % (wname, form)] = entry
+            log("  %s %s %.4f ms" % (wname, form, ms))
+            del x, wsw, ow, Sw
+        result["workloads"] = wl
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,213 @@
+"""MI355X (gfx950) delta-rule linear attention: DeltaNet, Gated DeltaNet, KDA.
+
+Thin binding over the C ABI of ``include/deltanet.h``: it checks shapes and
+dtypes, allocates outputs with PyTorch (device memory and streams only), and
+calls the HIP library on the current stream. Every step of the operator runs
+in the library's kernels; there is no CPU or PyTorch fallback, and a missing
+library or GPU raises.
+
+Tensor contract (page "28. Linear attention and Gated DeltaNet", section "The
+recurrent form"): q, k [B,H,T,dk]; v [B,H,T,dv]; beta, g [B,H,T] (KDA: g
+[B,H,T,dk]); states fp32 [B,H,dk,dv]. q and k are expected L2-normalised with
+q already scaled by dk^-1/2 (the kernels apply no scale). Inputs are bf16 or
+fp32; outputs o have the input dtype.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import DeltaNetError, lib
+
+__all__ = ["chunk_fwd", "kda_chunk_fwd", "chunk_prep", "chunk_scan", "recurrent_fwd",
+           "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
+           "DeltaNetError", "lib", "library_path"]
+
+_DT = {torch.float32: _lib.DN_F32, torch.bfloat16: _lib.DN_BF16}
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device or t.device.type != "cuda":
+        raise ValueError("%s must be on %s (got %s)" % (name, device, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _prefill_args(q, k, v, beta, g, S0, kda):
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,T,dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("inputs must be float32 or bfloat16")
+    _check_tensor("q", q, (B, H, T, dk), dt, dev)
+    _check_tensor("k", k, (B, H, T, dk), dt, dev)
+    _check_tensor("v", v, (B, H, T, dv), dt, dev)
+    _check_tensor("beta", beta, (B, H, T), dt, dev)
+    if kda:
+        if g is None:
+            raise ValueError("KDA needs g [B,H,T,dk]")
+        _check_tensor("g", g, (B, H, T, dk), dt, dev)
+    elif g is not None:
+        _check_tensor("g", g, (B, H, T), dt, dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    return B, H, T, dk, dv, dev, dt
+
+
+def workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, dtype: torch.dtype) -> int:
+    """Bytes of device workspace chunk_fwd / kda_chunk_fwd need at these sizes."""
+    return int(lib().dn_chunk_fwd_workspace(B, H, T, dk, dv, _DT[dtype]))
+
+
+def _alloc_workspace(nbytes, dev):
+    # 256-byte alignment is guaranteed by the caching allocator's block granularity
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+
+
+def _chunk(fn_name, q, k, v, beta, g, S0, output_final_state, o, S_final, workspace, stream,
+           kda):
+    B, H, T, dk, dv, dev, dt = _prefill_args(q, k, v, beta, g, S0, kda)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, T, dv), dt, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    elif S_final is not None:
+        _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
+    need = int(lib().dn_chunk_fwd_workspace(B, H, T, dk, dv, _DT[dt]))
+    if workspace is None:
+        workspace = _alloc_workspace(need, dev)
+    fn = getattr(lib(), fn_name)
+    st = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o), _ptr(S_final),
+            B, H, T, dk, dv, _DT[dt], _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream(stream))
+    _lib.check(fn_name, st)
+    return o, S_final
+
+
+def chunk_fwd(q, k, v, beta, g=None, S0=None, *, output_final_state=True, o=None, S_final=None,
+              workspace=None, stream=None):
+    """Chunkwise (C=64) prefill of DeltaNet (g=None) or Gated DeltaNet (g [B,H,T]).
+
+    Returns (o [B,H,T,dv] in the input dtype, S_final fp32 [B,H,dk,dv] or None).
+    S_final may be S0 for an in-place state update.
+    """
+    return _chunk("dn_chunk_fwd", q, k, v, beta, g, S0, output_final_state, o, S_final,
+                  workspace, stream, kda=False)
+
+
+def kda_chunk_fwd(q, k, v, beta, g, S0=None, *, output_final_state=True, o=None, S_final=None,
+                  workspace=None, stream=None):
+    """Chunkwise (C=64) KDA prefill; g [B,H,T,dk] per-key-channel log-decay."""
+    return _chunk("dn_kda_chunk_fwd", q, k, v, beta, g, S0, output_final_state, o, S_final,
+                  workspace, stream, kda=True)
+
+
+def chunk_prep(q, k, v, beta, g, workspace, *, kda=False, stream=None):
+    """Phase 1 of the chunkwise prefill (all chunks in parallel) into ``workspace``."""
+    B, H, T, dk, dv, dev, dt = _prefill_args(q, k, v, beta, g, None, kda)
+    st = lib().dn_chunk_prep(int(kda), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), B, H, T, dk,
+                             dv, _DT[dt], _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("dn_chunk_prep", st)
+
+
+def chunk_scan(o, workspace, S0=None, S_final=None, *, kda=False, stream=None):
+    """Phase 2 of the chunkwise prefill: the sequential scan over ``workspace``.
+
+    o [B,H,T,dv] (input dtype) receives the outputs; S_final (fp32) the end state.
+    """
+    B, H, T, dv = o.shape
+    dk = dv
+    dev, dt = o.device, o.dtype
+    _check_tensor("o", o, (B, H, T, dv), dt, dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    if S_final is not None:
+        _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
+    st = lib().dn_chunk_scan(int(kda), _ptr(S0), _ptr(o), _ptr(S_final), B, H, T, dk, dv, _DT[dt],
+                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                             _stream(stream))
+    _lib.check("dn_chunk_scan", st)
+
+
+def _recurrent(fn_name, q, k, v, beta, g, S0, output_final_state, stream, kda):
+    B, H, T, dk, dv, dev, dt = _prefill_args(q, k, v, beta, g, S0, kda)
+    o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    S_final = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) if output_final_state else None
+    st = getattr(lib(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o),
+                                 _ptr(S_final), B, H, T, dk, dv, _DT[dt], _stream(stream))
+    _lib.check(fn_name, st)
+    return o, S_final
+
+
+def recurrent_fwd(q, k, v, beta, g=None, S0=None, *, output_final_state=True, stream=None):
+    """Token-by-token recurrent form (same contract and result as chunk_fwd)."""
+    return _recurrent("dn_recurrent_fwd", q, k, v, beta, g, S0, output_final_state, stream, False)
+
+
+def kda_recurrent_fwd(q, k, v, beta, g, S0=None, *, output_final_state=True, stream=None):
+    """Token-by-token KDA recurrence; g [B,H,T,dk]."""
+    return _recurrent("dn_kda_recurrent_fwd", q, k, v, beta, g, S0, output_final_state, stream,
+                      True)
+
+
+def _decode(fn_name, q, k, v, beta, g, S, o, stream, kda):
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("inputs must be float32 or bfloat16")
+    _check_tensor("k", k, (B, H, dk), dt, dev)
+    _check_tensor("v", v, (B, H, dv), dt, dev)
+    _check_tensor("beta", beta, (B, H), dt, dev)
+    if kda:
+        if g is None:
+            raise ValueError("KDA needs g [B,H,dk]")
+        _check_tensor("g", g, (B, H, dk), dt, dev)
+    elif g is not None:
+        _check_tensor("g", g, (B, H), dt, dev)
+    _check_tensor("S", S, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, H, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, dv), dt, dev)
+    st = getattr(lib(), fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S), _ptr(o),
+                                 B, H, dk, dv, _DT[dt], _stream(stream))
+    _lib.check(fn_name, st)
+    return o
+
+
+def decode_step(q, k, v, beta, g, S, *, o=None, stream=None):
+    """One decode step: S [B,H,dk,dv] fp32 is updated in place; returns o [B,H,dv]."""
+    return _decode("dn_decode_step", q, k, v, beta, g, S, o, stream, False)
+
+
+def kda_decode_step(q, k, v, beta, g, S, *, o=None, stream=None):
+    """One KDA decode step; g [B,H,dk]."""
+    return _decode("dn_kda_decode_step", q, k, v, beta, g, S, o, stream, True)

@@ -1,0 +1,208 @@
+// abi.hip -- extern "C" entry points of the delta-rule library (see include/deltanet.h).
+// Every argument check runs before the first HIP call, so every error return
+// is synchronous and independent of device state.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/deltanet.h"
+#include "dn_launch.h"
+
+namespace {
+
+constexpr int kVersion = 1;
+
+bool misaligned(const void* p, unsigned a = 16) {
+    return (reinterpret_cast<uintptr_t>(p) & (uintptr_t)(a - 1)) != 0;
+}
+
+// Validation shared by all entry points. Vector-loaded tensors (q, k, v, o
+// and the fp32 states) must be 16-byte aligned; beta and g are read element by
+// element and need only the alignment of their element type. With T == 0 the
+// per-token tensors are never read and may be NULL (empty tensors).
+int check_common(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                 bool g_required, const void* S0, const void* o, const void* S_final, int B,
+                 int H, int T, int dk, int dv, int dtype) {
+    if (B < 1 || H < 1 || T < 0) return DN_EINVAL;
+    if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+    if (T > 0) {
+        if (!q || !k || !v || !beta || !o) return DN_EINVAL;
+        if (g_required && !g) return DN_EINVAL;
+    }
+    const unsigned esz = dtype == DN_F32 ? 4u : 2u;
+    if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) ||
+        misaligned(beta, esz) || misaligned(g, esz) || misaligned(S0) || misaligned(S_final))
+        return DN_EINVAL;
+    if ((dk != 64 && dk != 128) || dk != dv) return DN_ENOTSUP;
+    const long long BH = (long long)B * H;
+    // grid sizes and 32-bit block indices: heads * chunks must fit the grid
+    const long long nchunks = ((long long)T + 63) / 64;
+    if (BH > (1LL << 24) || nchunks * BH > 0x7fffffffLL) return DN_EINVAL;
+    return DN_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? DN_OK : DN_EHIP; }
+
+int check_workspace(long long BH, int T, int dk, int dv, int dtype, const void* workspace,
+                    size_t workspace_bytes) {
+    const size_t need = dn::chunk_workspace_bytes(BH, T, dk, dv, dtype);
+    if (!workspace || workspace_bytes < need) return DN_EWORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return DN_EWORKSPACE;
+    return DN_OK;
+}
+
+int chunk_kind(bool kda, const void* g) {
+    return kda ? dn::KIND_KDA : (g ? dn::KIND_GATED : dn::KIND_DELTANET);
+}
+
+int chunk_common(int kind, const void* q, const void* k, const void* v, const void* beta,
+                 const void* g, const float* S0, void* o, float* S_final, int B, int H, int T,
+                 int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    int st = check_common(q, k, v, beta, g, kind == dn::KIND_KDA, S0, o, S_final, B, H, T, dk,
+                          dv, dtype);
+    if (st != DN_OK) return st;
+    // fp32 KDA at d = 128 does not fit the prep kernel's LDS budget
+    if (kind == dn::KIND_KDA && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
+    const long long BH = (long long)B * H;
+    if (T == 0) {
+        if (!S_final) return DN_OK;
+        return hip_status(dn::launch_state_copy(S0, S_final, BH * dk * dv, as_stream(stream)));
+    }
+    st = check_workspace(BH, T, dk, dv, dtype, workspace, workspace_bytes);
+    if (st != DN_OK) return st;
+    hipError_t e = dn::launch_chunk_prep(kind, dtype, q, k, v, beta, g, workspace, (int)BH, T, dk,
+                                         dv, as_stream(stream));
+    if (e != hipSuccess) return DN_EHIP;
+    return hip_status(dn::launch_chunk_scan(kind, dtype, S0, o, S_final, workspace, (int)BH, T, dk,
+                                            dv, as_stream(stream)));
+}
+
+int recurrent_common(int kind, const void* q, const void* k, const void* v, const void* beta,
+                     const void* g, const float* S0, void* o, float* S_final, int B, int H,
+                     int T, int dk, int dv, int dtype, void* stream) {
+    int st = check_common(q, k, v, beta, g, kind == dn::KIND_KDA, S0, o, S_final, B, H, T, dk,
+                          dv, dtype);
+    if (st != DN_OK) return st;
+    const long long BH = (long long)B * H;
+    if (T == 0) {
+        if (!S_final) return DN_OK;
+        return hip_status(dn::launch_state_copy(S0, S_final, BH * dk * dv, as_stream(stream)));
+    }
+    return hip_status(dn::launch_recurrent(kind, dtype, q, k, v, beta, g, S0, o, S_final,
+                                           (int)BH, T, dk, dv, as_stream(stream)));
+}
+
+int decode_common(int kind, const void* q, const void* k, const void* v, const void* beta,
+                  const void* g, float* S, void* o, int B, int H, int dk, int dv, int dtype,
+                  void* stream) {
+    if (!S) return DN_EINVAL;
+    int st = check_common(q, k, v, beta, g, kind == dn::KIND_KDA, S, o, S, B, H, 1, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    const long long BH = (long long)B * H;
+    return hip_status(dn::launch_decode(kind, dtype, q, k, v, beta, g, S, o, (int)BH, dk, dv,
+                                        as_stream(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dn_strerror(int status) {
+    switch (status) {
+        case DN_OK: return "success";
+        case DN_EINVAL: return "invalid argument (NULL or misaligned pointer, bad size or dtype)";
+        case DN_ENOTSUP: return "unsupported head size (d_k, d_v must be equal and in {64, 128})";
+        case DN_EWORKSPACE: return "workspace missing, misaligned or smaller than dn_chunk_fwd_workspace()";
+        case DN_EHIP: return "HIP runtime error at kernel launch";
+        default: return "unknown status";
+    }
+}
+
+int dn_version(void) { return kVersion; }
+
+size_t dn_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int dtype) {
+    if (B < 1 || H < 1 || T < 0) return 0;
+    if ((dk != 64 && dk != 128) || dk != dv) return 0;
+    if (dtype != DN_F32 && dtype != DN_BF16) return 0;
+    if (T == 0) return 0;
+    return dn::chunk_workspace_bytes((long long)B * H, T, dk, dv, dtype);
+}
+
+int dn_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                 const float* S0, void* o, float* S_final, int B, int H, int T, int dk, int dv,
+                 int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return chunk_common(g ? dn::KIND_GATED : dn::KIND_DELTANET, q, k, v, beta, g, S0, o, S_final,
+                        B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream);
+}
+
+int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
+                     const void* g, const float* S0, void* o, float* S_final, int B, int H,
+                     int T, int dk, int dv, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    return chunk_common(dn::KIND_KDA, q, k, v, beta, g, S0, o, S_final, B, H, T, dk, dv, dtype,
+                        workspace, workspace_bytes, stream);
+}
+
+int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,
+                  const void* g, int B, int H, int T, int dk, int dv, int dtype, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    // o is not touched by this phase: q stands in for it in the shared checks
+    int st = check_common(q, k, v, beta, g, kda != 0, nullptr, q, nullptr, B, H, T, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    if (kda && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
+    if (T == 0) return DN_OK;
+    const long long BH = (long long)B * H;
+    st = check_workspace(BH, T, dk, dv, dtype, workspace, workspace_bytes);
+    if (st != DN_OK) return st;
+    return hip_status(dn::launch_chunk_prep(chunk_kind(kda != 0, g), dtype, q, k, v, beta, g,
+                                            workspace, (int)BH, T, dk, dv, as_stream(stream)));
+}
+
+int dn_chunk_scan(int kda, const float* S0, void* o, float* S_final, int B, int H, int T, int dk,
+                  int dv, int dtype, const void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    // the per-token inputs are not read by this phase: o stands in for them
+    int st = check_common(o, o, o, o, nullptr, false, S0, o, S_final, B, H, T, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    if (kda && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
+    const long long BH = (long long)B * H;
+    if (T == 0) {
+        if (!S_final) return DN_OK;
+        return hip_status(dn::launch_state_copy(S0, S_final, BH * dk * dv, as_stream(stream)));
+    }
+    st = check_workspace(BH, T, dk, dv, dtype, workspace, workspace_bytes);
+    if (st != DN_OK) return st;
+    return hip_status(dn::launch_chunk_scan(kda ? dn::KIND_KDA : dn::KIND_GATED, dtype, S0, o,
+                                            S_final, workspace, (int)BH, T, dk, dv,
+                                            as_stream(stream)));
+}
+
+int dn_recurrent_fwd(const void* q, const void* k, const void* v, const void* beta,
+                     const void* g, const float* S0, void* o, float* S_final, int B, int H,
+                     int T, int dk, int dv, int dtype, void* stream) {
+    return recurrent_common(g ? dn::KIND_GATED : dn::KIND_DELTANET, q, k, v, beta, g, S0, o,
+                            S_final, B, H, T, dk, dv, dtype, stream);
+}
+
+int dn_kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* beta,
+                         const void* g, const float* S0, void* o, float* S_final, int B, int H,
+                         int T, int dk, int dv, int dtype, void* stream) {
+    return recurrent_common(dn::KIND_KDA, q, k, v, beta, g, S0, o, S_final, B, H, T, dk, dv,
+                            dtype, stream);
+}
+
+int dn_decode_step(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                   float* S, void* o, int B, int H, int dk, int dv, int dtype, void* stream) {
+    return decode_common(g ? dn::KIND_GATED : dn::KIND_DELTANET, q, k, v, beta, g, S, o, B, H,
+                         dk, dv, dtype, stream);
+}
+
+int dn_kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                       const void* g, float* S, void* o, int B, int H, int dk, int dv, int dtype,
+                       void* stream) {
+    return decode_common(dn::KIND_KDA, q, k, v, beta, g, S, o, B, H, dk, dv, dtype, stream);
+}
+
+}  // extern "C"

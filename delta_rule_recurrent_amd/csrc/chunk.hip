@@ -1,0 +1,606 @@
+// chunk.hip -- chunkwise-parallel prefill (chunk C = 64) on gfx950 matrix cores.
+//
+// For one chunk of one (sequence, head), with G_i the running sum of the
+// log-decay inside the chunk (per key channel for KDA), the UT/WY form is
+//     A   = strict_tril(beta_i k_i . k_j exp(G_i - G_j))
+//     T   = (I + A)^-1                      (unit lower triangular)
+//     W   = T (beta exp(G) K),  u = T (beta V)
+//     U   = u - W S0                         (values actually written)
+//     O   = (Q exp(G)) S0 + tril(Q K^T exp(G_i - G_j)) U
+//     S1  = exp(G_C) S0 + (K exp(G_C - G))^T U
+// (page "28. Linear attention and Gated DeltaNet", section "The chunked form:
+// recurrence as matrix multiplication"; page "DeltaNet: Memory That Edits",
+// section "Training it: the WY trick"; with per-channel decay for KDA,
+// page "A walk through of the DeltaNet family of linear attention variants").
+//
+// Two kernels:
+//   chunk_prep_kernel  one workgroup per (head, chunk), all chunks in parallel:
+//                      G, A (MFMA), T (forward substitution in LDS), W, u
+//                      (MFMA), the masked decayed Q K^T and the decay-scaled
+//                      Q and K^T; everything the sequential part needs is
+//                      written to the workspace in the exact per-lane MFMA
+//                      fragment order the scan loads (one coalesced 16-byte
+//                      load per lane per fragment).
+//   chunk_scan_kernel  one workgroup per (head, 32- or 16-column value tile):
+//                      the fp32 state tile lives in MFMA accumulators across
+//                      all chunks; per chunk U = u - W S, O = Q~ S + attn U,
+//                      S = gamma S + K~^T U, chained through two small LDS
+//                      exchanges of bf16 fragments.
+#include "dn_device.h"
+#include "dn_launch.h"
+
+namespace dn {
+
+// ---------------------------------------------------------------------------
+// Workspace layout of one (head, chunk) block. Fragment arrays are
+// [tile][k-block][lane][8] elements of E (see the fragment convention in
+// dn_device.h); D-tile arrays are [tile][tile][lane][4].
+//   W   [4 token tiles][DK/32][64][8]      W = T (beta e^G K)          A-fragments
+//   Qt  [4 token tiles][DK/32][64][8]      Q~ = e^G Q                  A-fragments
+//   Kt  [DK/16 chan tiles][2][64][8]       K~^T = (e^{G_C - G} K)^T    A-fragments
+//   At  [4 token tiles][2][64][8]          attn = tril(Q K^T D)         A-fragments
+//   Uu  [4 token tiles][DV/16][64][4]      u = T (beta V)              D-tiles
+//   gam [DK] float                         e^{G_C} (Gated: entry 0 only)
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+struct WsLayout {
+    static constexpr long W_OFF = 0;
+    static constexpr long Q_OFF = W_OFF + 4L * (DK / 32) * 64 * 8;
+    static constexpr long K_OFF = Q_OFF + 4L * (DK / 32) * 64 * 8;
+    static constexpr long A_OFF = K_OFF + (DK / 16) * 2L * 64 * 8;
+    static constexpr long U_OFF = A_OFF + 4L * 2 * 64 * 8;
+    static constexpr long E_END = U_OFF + 4L * (DV / 16) * 64 * 4;
+    static constexpr long GAM_BYTE_OFF = (E_END * (long)sizeof(E) + 255) / 256 * 256;
+    static constexpr long BYTES = (GAM_BYTE_OFF + DK * 4L + 255) / 256 * 256;
+};
+
+template <typename E> struct Vec16;
+template <> struct Vec16<bf16> { typedef bf16x8 type; };
+template <> struct Vec16<float> { typedef f32x4 type; };
+
+// Stage a [64 x D] token-major tile (rows >= L zero) into LDS as row-major
+// rows[64][ldr] and/or transposed trans[D][ldt] (token index contiguous).
+// Each thread loads four tokens of one 16-byte column vector and writes the
+// transpose as 4-token vectors.
+template <typename E, int D, bool ROWS, bool TRANS>
+__device__ __forceinline__ void stage_tile(const E* __restrict__ src, int L, E* rows, int ldr,
+                                           E* trans, int ldt, int tid) {
+    typedef typename Vec16<E>::type V16;
+    typedef typename Vec4<E>::type V4;
+    constexpr int VEC = 16 / sizeof(E);
+    constexpr int NV = D / VEC;
+    for (int idx = tid; idx < 16 * NV; idx += 256) {
+        const int tq = idx / NV, cv = idx % NV;
+        V16 x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int t = 4 * tq + u;
+            if (t < L) x[u] = *reinterpret_cast<const V16*>(src + (long)t * D + cv * VEC);
+            else x[u] = V16{};
+        }
+        if (ROWS) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) *reinterpret_cast<V16*>(rows + (4 * tq + u) * ldr + cv * VEC) = x[u];
+        }
+        if (TRANS) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) {
+                V4 c4;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) c4[u] = x[u][e];
+                *reinterpret_cast<V4*>(trans + (cv * VEC + e) * ldt + 4 * tq) = c4;
+            }
+        }
+    }
+}
+
+// KDA: fragment of a row-major [64][ld] token tile (rows = tokens, contraction
+// = key channels) with each value multiplied by exp(sgn * (G[row][c] - G[ref][c])).
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::type frag_rows_decay(const E* M, int ld, const float* G,
+                                                                  int ldg, int row0, int k0,
+                                                                  int lane, int ref, float sgn) {
+    const int g = lane >> 4, r = lane & 15;
+    const int row = row0 + r;
+    typename Frag<E>::type f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int c = k0 + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
+        const float e = __expf(sgn * (G[row * ldg + c] - G[ref * ldg + c]));
+        f[j] = from_f32<E>(to_f32(M[row * ld + c]) * e);
+    }
+    return f;
+}
+
+// ---------------------------------------------------------------------------
+// Prep kernel
+//
+// LDS lifetimes (one workgroup = one chunk of one head, 4 wavefronts):
+//   R1   : K rows | Q rows            (staging .. step 2)
+//          then T' | T''  (Gated / DeltaNet)  or  X^T | T''  (KDA)   (step 3 ..)
+//   KsT  : K^T (token index contiguous)  (KDA: becomes K~^T in place after step 2)
+//   VsT  : V^T                          (.. step 5)
+//   As   : fp32 system matrix           (step 2 .. step 3)
+//   Gk   : KDA only, fp32 running log-decay per (token, key channel)
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV, int KIND>
+__global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q,
+                                                         const E* __restrict__ k,
+                                                         const E* __restrict__ v,
+                                                         const E* __restrict__ beta,
+                                                         const E* __restrict__ g,
+                                                         char* __restrict__ ws, int T,
+                                                         int nchunks) {
+    typedef WsLayout<E, DK, DV> Lw;
+    typedef typename Frag<E>::type F;
+    typedef typename Vec4<E>::type V4;
+    constexpr int KP = 16 / sizeof(E);   // row padding: one 16-byte vector
+    constexpr int LDK = DK + KP;         // leading dim of [64][DK] tiles
+    constexpr int LDT = 64 + KP;         // leading dim of [D][64] tiles
+    constexpr int LDA = 68;              // fp32 system matrix
+    constexpr bool KDA = (KIND == KIND_KDA);
+    constexpr int LDG = KDA ? DK + 4 : 1;
+    static_assert((KDA ? DK + 64 : 128) * LDT <= 2 * 64 * LDK, "R1 too small");
+
+    __shared__ __align__(16) E R1[2 * 64 * LDK];
+    __shared__ __align__(16) E KsT[DK * LDT];
+    __shared__ __align__(16) E VsT[DV * LDT];
+    __shared__ __align__(16) float As[64 * LDA];
+    __shared__ float Gs[KDA ? 1 : 64], eG[KDA ? 1 : 64], eGC[KDA ? 1 : 64], bs[64];
+    __shared__ __align__(16) float Gk[KDA ? 64 * LDG : 1];
+    E* Ks = R1;
+    E* Qs = R1 + 64 * LDK;
+    E* XsT = R1;                                  // KDA, after step 2
+    E* Tp = R1;                                   // Gated / DeltaNet, after step 2
+    E* Tpp = R1 + (KDA ? DK : 64) * LDT;          // after step 2
+
+    const int c = blockIdx.x % nchunks;
+    const long bh = blockIdx.x / nchunks;
+    const int t0 = c * CHUNK;
+    const int L = min(CHUNK, T - t0);
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int gq = lane >> 4, n = lane & 15;
+
+    char* blk = ws + ((long)bh * nchunks + c) * Lw::BYTES;
+    E* Wf = reinterpret_cast<E*>(blk) + Lw::W_OFF;
+    E* Qf = reinterpret_cast<E*>(blk) + Lw::Q_OFF;
+    E* Kf = reinterpret_cast<E*>(blk) + Lw::K_OFF;
+    E* Af = reinterpret_cast<E*>(blk) + Lw::A_OFF;
+    E* Uf = reinterpret_cast<E*>(blk) + Lw::U_OFF;
+    float* gam = reinterpret_cast<float*>(blk + Lw::GAM_BYTE_OFF);
+
+    const long tok0 = (long)bh * T + t0;
+
+    // ---- 1. beta, log-decay and its running sum inside the chunk; stage tiles
+    if (w == 0) bs[lane] = (lane < L) ? to_f32(beta[tok0 + lane]) : 0.f;
+    if (!KDA) {
+        if (w == 0) {
+            const float gv = (KIND == KIND_GATED && lane < L) ? to_f32(g[tok0 + lane]) : 0.f;
+            const float G = wave_inclusive_sum(gv, lane);
+            const float GC = readlane_f(G, 63);
+            Gs[lane] = G;
+            eG[lane] = __expf(G);
+            eGC[lane] = __expf(GC - G);
+            if (lane == 0) gam[0] = __expf(GC);
+        }
+    } else {
+        // one thread per key channel, sequential over the 64 tokens (tokens
+        // past the end of the sequence add nothing)
+        for (int ch = tid; ch < DK; ch += 256) {
+            float acc = 0.f;
+            for (int t = 0; t < CHUNK; ++t) {
+                if (t < L) acc += to_f32(g[(tok0 + t) * DK + ch]);
+                Gk[t * LDG + ch] = acc;
+            }
+            gam[ch] = __expf(acc);
+        }
+    }
+    stage_tile<E, DK, true, true>(k + tok0 * DK, L, Ks, LDK, KsT, LDT, tid);
+    stage_tile<E, DK, true, false>(q + tok0 * DK, L, Qs, LDK, nullptr, 0, tid);
+    stage_tile<E, DV, false, true>(v + tok0 * DV, L, nullptr, 0, VsT, LDT, tid);
+    __syncthreads();
+
+    // ---- 2. A = strict_tril(beta K K^T D) -> As;  attn -> A-fragments;  Q~ ---
+    // Wave w owns token tile w: rows i in [16w, 16w+16) of A and of attn.
+    // KDA: the decay exp(G_ic - G_jc) sits inside the contraction, so both
+    // operands are scaled around a reference token ref of the row tile:
+    // k_i exp(G_i - G_ref) and k_j exp(G_ref - G_j). With ref in the middle of
+    // the tile every factor is bounded by the decay over at most 8 tokens.
+    {
+        F ka[DK / 32], qa[DK / 32];
+        const int ref = 16 * w + 8;
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            if (!KDA) {
+                ka[kb] = frag_rows<E>(Ks, LDK, 16 * w, 32 * kb, lane);
+                qa[kb] = frag_rows<E>(Qs, LDK, 16 * w, 32 * kb, lane);
+            } else {
+                ka[kb] = frag_rows_decay<E>(Ks, LDK, Gk, LDG, 16 * w, 32 * kb, lane, ref, 1.f);
+                qa[kb] = frag_rows_decay<E>(Qs, LDK, Gk, LDG, 16 * w, 32 * kb, lane, ref, 1.f);
+            }
+        }
+        f32x4 at[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            f32x4 sa = zero4();
+            at[jt] = zero4();
+            if (jt <= w) {
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    const F kj = KDA ? frag_rows_decay<E>(Ks, LDK, Gk, LDG, 16 * jt, 32 * kb, lane, ref, -1.f)
+                                     : frag_rows<E>(Ks, LDK, 16 * jt, 32 * kb, lane);
+                    sa = mma(ka[kb], kj, sa);          // (K K^T)[i][j]
+                    at[jt] = mma(kj, qa[kb], at[jt]);  // (K Q^T)[j][i] = attn^T
+                }
+            }
+            // system matrix: lane (gq, n) holds rows i = 16w + 4gq + e, column j = 16jt + n
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * w + 4 * gq + e, j = 16 * jt + n;
+                float val = 0.f;
+                if (i > j) val = KDA ? bs[i] * sa[e] : bs[i] * __expf(Gs[i] - Gs[j]) * sa[e];
+                As[i * LDA + j] = val;
+            }
+            // attn^T tile: rows j = 16jt + 4gq + e, column i = 16w + n (causal, incl. diagonal)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * jt + 4 * gq + e, i = 16 * w + n;
+                float val = 0.f;
+                if (i >= j) val = KDA ? at[jt][e] : __expf(Gs[i] - Gs[j]) * at[jt][e];
+                at[jt][e] = val;
+            }
+        }
+        // attn^T computed with rows = j lands directly as A-fragments of attn (rows i)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            reinterpret_cast<F*>(Af)[(w * 2 + kb) * 64 + lane] = frag_from_tiles<E>(at[2 * kb], at[2 * kb + 1]);
+        // Q~ = e^G Q, A-fragments of token tile w
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            F f;
+            if (!KDA) {
+                f = frag_rows_scaled<E>(Qs, LDK, 16 * w, 32 * kb, lane, eG[16 * w + n], nullptr);
+            } else {
+                const int row = 16 * w + n;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int cc = 32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
+                    f[j] = from_f32<E>(to_f32(Qs[row * LDK + cc]) * __expf(Gk[row * LDG + cc]));
+                }
+            }
+            reinterpret_cast<F*>(Qf)[(w * (DK / 32) + kb) * 64 + lane] = f;
+        }
+    }
+    if (!KDA) {
+        // K~^T = (e^{G_C - G} K)^T, A-fragments with rows = key channels
+        for (int p = w; p < (DK / 16) * 2; p += 4) {
+            const int mt = p >> 1, kb = p & 1;
+            reinterpret_cast<F*>(Kf)[p * 64 + lane] =
+                frag_rows_scaled<E>(KsT, LDT, 16 * mt, 32 * kb, lane, 1.f, eGC);
+        }
+    }
+    __syncthreads();
+
+    if (KDA) {
+        // X^T = (e^G K)^T into R1 (K and Q rows are dead); K^T -> K~^T in place
+        for (int idx = tid; idx < DK * 64; idx += 256) {
+            const int ch = idx / 64, t = idx % 64;
+            const float kv = to_f32(KsT[ch * LDT + t]);
+            const float Gt = Gk[t * LDG + ch], GC = Gk[63 * LDG + ch];
+            XsT[ch * LDT + t] = from_f32<E>(kv * __expf(Gt));
+            KsT[ch * LDT + t] = from_f32<E>(kv * __expf(GC - Gt));
+        }
+    }
+
+    // ---- 3. T = (I + A)^-1 by forward substitution (wave 0, lane = column) --
+    // Column j of T: T_jj = 1, T_ij = -sum_{j <= m < i} A_im T_mj for i > j.
+    if (w == 0) {
+        const int j = lane;
+        float tc[64];
+#pragma unroll
+        for (int i = 0; i < 64; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 1; i < 64; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc += As[i * LDA + m] * tc[m];
+            if (i > j) tc[i] = -acc;
+        }
+        const float sb = bs[j];
+        const float sbg = KDA ? 0.f : bs[j] * eG[j];
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+            if (!KDA) Tp[i * LDT + j] = from_f32<E>(tc[i] * sbg);
+            Tpp[i * LDT + j] = from_f32<E>(tc[i] * sb);
+        }
+    }
+    __syncthreads();
+
+    if (KDA) {
+        for (int p = w; p < (DK / 16) * 2; p += 4) {
+            const int mt = p >> 1, kb = p & 1;
+            reinterpret_cast<F*>(Kf)[p * 64 + lane] = frag_rows<E>(KsT, LDT, 16 * mt, 32 * kb, lane);
+        }
+    }
+
+    // ---- 4. W^T = X^T T'^T, computed transposed so it lands as A-fragments of W
+    //         (Gated / DeltaNet: X = K, T' = T diag(beta e^G); KDA: X = e^G K, T' = T diag(beta))
+    {
+        const E* XT = KDA ? XsT : KsT;
+        const E* TT = KDA ? Tpp : Tp;
+        f32x4 wt[DK / 16];
+#pragma unroll
+        for (int mt = 0; mt < DK / 16; ++mt) {
+            wt[mt] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                wt[mt] = mma(frag_rows<E>(XT, LDT, 16 * mt, 32 * kb, lane),
+                             frag_rows<E>(TT, LDT, 16 * w, 32 * kb, lane), wt[mt]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < DK / 32; ++kb)
+            reinterpret_cast<F*>(Wf)[(w * (DK / 32) + kb) * 64 + lane] =
+                frag_from_tiles<E>(wt[2 * kb], wt[2 * kb + 1]);
+    }
+    // ---- 5. u = T diag(beta) V for token tile w (D-tiles) -------------------
+#pragma unroll
+    for (int nt = 0; nt < DV / 16; ++nt) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+            acc = mma(frag_rows<E>(Tpp, LDT, 16 * w, 32 * kb, lane),
+                      frag_rows<E>(VsT, LDT, 16 * nt, 32 * kb, lane), acc);
+        V4 u4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u4[e] = from_f32<E>(acc[e]);
+        reinterpret_cast<V4*>(Uf)[(w * (DV / 16) + nt) * 64 + lane] = u4;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Scan kernel
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV, int BV>
+struct ScanOps {
+    typedef typename Frag<E>::type F;
+    typedef typename Vec4<E>::type V4;
+    static constexpr int KB = DK / 32;   // contraction blocks over key channels
+    static constexpr int MTW = DK / 64;  // key-channel tiles per wave
+    static constexpr int NT = BV / 16;   // value tiles (16 columns) per workgroup
+    F w[KB], q[KB], a[2], k[MTW][2];
+    V4 u[NT];
+    f32x4 gam[MTW];
+};
+
+template <typename E, int DK, int DV, int BV, int KIND>
+__device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV>& x, const char* blk, int vt,
+                                          int w, int lane) {
+    typedef WsLayout<E, DK, DV> Lw;
+    typedef ScanOps<E, DK, DV, BV> O;
+    typedef typename O::F F;
+    typedef typename O::V4 V4;
+    const E* base = reinterpret_cast<const E*>(blk);
+    const F* Wf = reinterpret_cast<const F*>(base + Lw::W_OFF);
+    const F* Qf = reinterpret_cast<const F*>(base + Lw::Q_OFF);
+    const F* Kf = reinterpret_cast<const F*>(base + Lw::K_OFF);
+    const F* Af = reinterpret_cast<const F*>(base + Lw::A_OFF);
+    const V4* Uf = reinterpret_cast<const V4*>(base + Lw::U_OFF);
+    const float* gam = reinterpret_cast<const float*>(blk + Lw::GAM_BYTE_OFF);
+#pragma unroll
+    for (int kb = 0; kb < O::KB; ++kb) {
+        x.w[kb] = Wf[(w * O::KB + kb) * 64 + lane];
+        x.q[kb] = Qf[(w * O::KB + kb) * 64 + lane];
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) x.a[kb] = Af[(w * 2 + kb) * 64 + lane];
+#pragma unroll
+    for (int m = 0; m < O::MTW; ++m)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) x.k[m][kb] = Kf[((w * O::MTW + m) * 2 + kb) * 64 + lane];
+#pragma unroll
+    for (int nt = 0; nt < O::NT; ++nt) x.u[nt] = Uf[(w * (DV / 16) + vt * O::NT + nt) * 64 + lane];
+    const int gq = lane >> 4;
+#pragma unroll
+    for (int m = 0; m < O::MTW; ++m) {
+        if (KIND == KIND_KDA) x.gam[m] = *reinterpret_cast<const f32x4*>(gam + 16 * (w * O::MTW + m) + 4 * gq);
+        else {
+            const float s = gam[0];
+            x.gam[m] = f32x4{s, s, s, s};
+        }
+    }
+}
+
+template <typename E, int DK, int DV, int KIND, int BV>
+__global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict__ ws,
+                                                         const float* __restrict__ S0,
+                                                         E* __restrict__ o,
+                                                         float* __restrict__ S_final, int T,
+                                                         int nchunks, int BH) {
+    typedef WsLayout<E, DK, DV> Lw;
+    typedef ScanOps<E, DK, DV, BV> Ops;
+    typedef typename Ops::F F;
+    typedef typename Ops::V4 V4;
+    constexpr int NV = DV / BV, NT = Ops::NT, KB = Ops::KB, MTW = Ops::MTW;
+
+    // XCD-aware mapping: consecutive workgroups go to different XCDs
+    // (round-robin over 8); the NV value tiles of one head share an XCD so
+    // that their common operands (W, Q~, K~^T, attn) hit the same L2.
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int vt = slot % NV;
+    const long bh = (long)(slot / NV) * 8 + xcd;
+    if (bh >= BH) return;
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int gq = lane >> 4, n = lane & 15;
+
+    __shared__ F Sx[KB][NT][64];   // state as B-fragments (contraction over key channels)
+    __shared__ F Ux[2][NT][64];    // U as B-fragments (contraction over tokens)
+
+    // fp32 state tile: rows 16*(w*MTW + m) + 4gq + e, columns vt*BV + 16nt + n
+    f32x4 S[MTW][NT];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * (w * MTW + m) + 4 * gq + e, col = vt * BV + 16 * nt + n;
+                S[m][nt][e] = S0 ? S0[(bh * DK + row) * DV + col] : 0.f;
+            }
+
+    const char* wsh = ws + (long)bh * nchunks * Lw::BYTES;
+    Ops cur, nxt;
+    scan_load<E, DK, DV, BV, KIND>(cur, wsh, vt, w, lane);
+
+    for (int c = 0; c < nchunks; ++c) {
+        // state -> bf16/fp32 B-fragments. Key-channel block kb covers tiles 2kb, 2kb+1.
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            if (MTW == 2) {
+                Sx[w][nt][lane] = frag_from_tiles<E>(S[0][nt], S[MTW - 1][nt]);
+            } else {
+                V4 h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = from_f32<E>(S[0][nt][e]);
+                reinterpret_cast<V4*>(&Sx[w >> 1][nt][lane])[w & 1] = h;
+            }
+        }
+        if (c + 1 < nchunks) scan_load<E, DK, DV, BV, KIND>(nxt, wsh + (long)(c + 1) * Lw::BYTES, vt, w, lane);
+        __syncthreads();
+
+        f32x4 U[NT], O[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            U[nt] = zero4();
+            O[nt] = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) {
+                const F sb = Sx[kb][nt][lane];
+                U[nt] = mma(cur.w[kb], sb, U[nt]);
+                O[nt] = mma(cur.q[kb], sb, O[nt]);
+            }
+            V4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                U[nt][e] = to_f32(cur.u[nt][e]) - U[nt][e];
+                h[e] = from_f32<E>(U[nt][e]);
+            }
+            reinterpret_cast<V4*>(&Ux[w >> 1][nt][lane])[w & 1] = h;
+        }
+        // decay the state (its pre-decay value is already captured in Sx)
+#pragma unroll
+        for (int m = 0; m < MTW; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) S[m][nt] *= cur.gam[m];
+        __syncthreads();
+
+        const int t0 = c * CHUNK;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const F ub = Ux[kb][nt][lane];
+                O[nt] = mma(cur.a[kb], ub, O[nt]);
+#pragma unroll
+                for (int m = 0; m < MTW; ++m) S[m][nt] = mma(cur.k[m][kb], ub, S[m][nt]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = t0 + 16 * w + 4 * gq + e;
+                if (t < T) o[((long)bh * T + t) * DV + vt * BV + 16 * nt + n] = from_f32<E>(O[nt][e]);
+            }
+        }
+        cur = nxt;
+    }
+
+    if (S_final) {
+#pragma unroll
+        for (int m = 0; m < MTW; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * (w * MTW + m) + 4 * gq + e, col = vt * BV + 16 * nt + n;
+                    S_final[(bh * DK + row) * DV + col] = S[m][nt][e];
+                }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+static size_t ws_bytes_t(long long BH, long long nchunks) {
+    return (size_t)(BH * nchunks * WsLayout<E, D, D>::BYTES);
+}
+
+size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype) {
+    (void)dv;
+    const long long nchunks = (T + CHUNK - 1) / CHUNK;
+    if (dtype == DT_BF16) return dk == 128 ? ws_bytes_t<bf16, 128>(BH, nchunks) : ws_bytes_t<bf16, 64>(BH, nchunks);
+    return dk == 128 ? ws_bytes_t<float, 128>(BH, nchunks) : ws_bytes_t<float, 64>(BH, nchunks);
+}
+
+template <typename E, int D, int KIND>
+static hipError_t prep_t(const void* q, const void* k, const void* v, const void* beta,
+                         const void* g, void* ws, int BH, int T, hipStream_t st) {
+    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    hipLaunchKernelGGL((chunk_prep_kernel<E, D, D, KIND>), dim3((unsigned)(nchunks * (long)BH)),
+                       dim3(256), 0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta,
+                       (const E*)g, (char*)ws, T, nchunks);
+    return hipGetLastError();
+}
+
+template <typename E, int D, int KIND>
+static hipError_t scan_t(const float* S0, void* o, float* S_final, const void* ws, int BH, int T,
+                         hipStream_t st) {
+    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    constexpr int BV = 32;
+    const long groups = ((long)BH + 7) / 8;
+    const long nblk = groups * 8 * (D / BV);
+    hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
+                       st, (const char*)ws, S0, (E*)o, S_final, T, nchunks, BH);
+    return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t prep_kind(int kind, const void* q, const void* k, const void* v,
+                            const void* beta, const void* g, void* ws, int BH, int T,
+                            hipStream_t st) {
+    if (kind == KIND_DELTANET) return prep_t<E, D, KIND_DELTANET>(q, k, v, beta, g, ws, BH, T, st);
+    if (kind == KIND_GATED) return prep_t<E, D, KIND_GATED>(q, k, v, beta, g, ws, BH, T, st);
+    // fp32 KDA at d = 128 exceeds the prep kernel's LDS budget (rejected by the ABI layer)
+    if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
+    else return prep_t<E, D, KIND_KDA>(q, k, v, beta, g, ws, BH, T, st);
+}
+
+template <typename E, int D>
+static hipError_t scan_kind(int kind, const float* S0, void* o, float* S_final, const void* ws,
+                            int BH, int T, hipStream_t st) {
+    // DeltaNet and Gated DeltaNet share the scan (a unit decay is stored for DeltaNet)
+    if (kind == KIND_KDA) return scan_t<E, D, KIND_KDA>(S0, o, S_final, ws, BH, T, st);
+    return scan_t<E, D, KIND_GATED>(S0, o, S_final, ws, BH, T, st);
+}
+
+hipError_t launch_chunk_prep(int kind, int dtype, const void* q, const void* k, const void* v,
+                             const void* beta, const void* g, void* ws, int BH, int T, int dk,
+                             int dv, hipStream_t st) {
+    (void)dv;
+    if (dtype == DT_BF16)
+        return dk == 128 ? prep_kind<bf16, 128>(kind, q, k, v, beta, g, ws, BH, T, st)
+                         : prep_kind<bf16, 64>(kind, q, k, v, beta, g, ws, BH, T, st);
+    return dk == 128 ? prep_kind<float, 128>(kind, q, k, v, beta, g, ws, BH, T, st)
+                     : prep_kind<float, 64>(kind, q, k, v, beta, g, ws, BH, T, st);
+}
+
+hipError_t launch_chunk_scan(int kind, int dtype, const float* S0, void* o, float* S_final,
+                             const void* ws, int BH, int T, int dk, int dv, hipStream_t st) {
+    (void)dv;
+    if (dtype == DT_BF16)
+        return dk == 128 ? scan_kind<bf16, 128>(kind, S0, o, S_final, ws, BH, T, st)
+                         : scan_kind<bf16, 64>(kind, S0, o, S_final, ws, BH, T, st);
+    return dk == 128 ? scan_kind<float, 128>(kind, S0, o, S_final, ws, BH, T, st)
+                     : scan_kind<float, 64>(kind, S0, o, S_final, ws, BH, T, st);
+}
+
+}  // namespace dn

@@ -1,0 +1,41 @@
+// dn_launch.h -- host-side launchers behind the C ABI (internal; not installed).
+// Arguments are assumed validated by the ABI layer (abi.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace dn {
+
+enum Kind { KIND_DELTANET = 0, KIND_GATED = 1, KIND_KDA = 2 };
+enum DType { DT_F32 = 0, DT_BF16 = 1 };
+
+constexpr int CHUNK = 64;
+
+// One fused decode step for BH (sequence, head) states.
+hipError_t launch_decode(int kind, int dtype, const void* q, const void* k, const void* v,
+                         const void* beta, const void* g, float* S, void* o, int BH, int dk,
+                         int dv, hipStream_t stream);
+
+// Token-by-token recurrence over T tokens.
+hipError_t launch_recurrent(int kind, int dtype, const void* q, const void* k, const void* v,
+                            const void* beta, const void* g, const float* S0, void* o,
+                            float* S_final, int BH, int T, int dk, int dv, hipStream_t stream);
+
+// Chunkwise prefill, phase 1: every chunk in parallel, intermediates -> workspace.
+hipError_t launch_chunk_prep(int kind, int dtype, const void* q, const void* k, const void* v,
+                             const void* beta, const void* g, void* workspace, int BH, int T,
+                             int dk, int dv, hipStream_t stream);
+
+// Chunkwise prefill, phase 2: sequential scan over the chunks of every head.
+hipError_t launch_chunk_scan(int kind, int dtype, const float* S0, void* o, float* S_final,
+                             const void* workspace, int BH, int T, int dk, int dv,
+                             hipStream_t stream);
+
+// Workspace bytes of the chunkwise prefill (per call).
+size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype);
+
+// S_final = S0 (or zeros when S0 == NULL), n floats; used when T == 0.
+hipError_t launch_state_copy(const float* S0, float* S_final, long long n, hipStream_t stream);
+
+}  // namespace dn

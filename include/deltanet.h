@@ -1,0 +1,173 @@
+/*
+ * deltanet.h -- C ABI of the MI355X (gfx950) delta-rule linear-attention library.
+ *
+ * The operator (DeltaNet, Gated DeltaNet, KDA) keeps one d_k x d_v fp32 state
+ * S per (sequence, head) and, for every token t,
+ *     S~ = Diag(alpha_t) S          (decay; alpha_t = exp(g_t): one scalar per
+ *                                    token for Gated DeltaNet, one per key
+ *                                    channel for KDA, 1 for DeltaNet)
+ *     u  = beta_t (v_t - S~^T k_t)  (scaled prediction error)
+ *     S  = S~ + k_t u^T             (rank-1 write)
+ *     o_t = S^T q_t                 (read-out)
+ * Pages: "28. Linear attention and Gated DeltaNet" (sections "Gated DeltaNet",
+ * "The recurrent form": the tensor contract below), "DeltaNet: Memory That
+ * Edits" (section "The delta rule"), "A walk through of the DeltaNet family of
+ * linear attention variants" (KDA recurrence, per-key-channel decay).
+ *
+ * Common conventions for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or synchronises. Work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the default stream) and the call returns after
+ *     validation and enqueue. Kernel faults surface at the caller's next sync.
+ *   - Tensors are contiguous, row-major, in the layouts given per argument.
+ *   - `dtype` (DN_F32 or DN_BF16) is the type of q, k, v, beta, g AND o.
+ *     States (S0, S_final, S) are always fp32 [B,H,d_k,d_v] with S^T k as the
+ *     read (d_k rows = key channels).
+ *   - q is used as given: callers that follow the pages' contract pass q and
+ *     k L2-normalised per head and q already scaled by d_k^-1/2. beta is not
+ *     clamped (values in [0, 2) are valid: the reflection range).
+ *   - Supported head sizes: d_k, d_v in {64, 128} with d_k == d_v.
+ *   - q, k, v, o and the fp32 states must be 16-byte aligned; beta and g need
+ *     only the alignment of their element type. When T == 0 the per-token
+ *     tensors (q, k, v, beta, g, o) are not read and may be NULL.
+ *   - All argument checks run before any HIP call, so every error return is
+ *     synchronous, touches no device state and is testable without a GPU.
+ *   - No global mutable state: calls are thread-safe. Calls that share output
+ *     buffers or a workspace must be ordered by the caller (same stream).
+ */
+#ifndef DELTANET_H
+#define DELTANET_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dn_status {
+    DN_OK = 0,
+    DN_EINVAL = -1,     /* a required pointer is NULL or misaligned, B/H < 1, T < 0,
+                           an unknown dtype, or more than 2^24 heads / 2^31-1 chunks */
+    DN_ENOTSUP = -2,    /* d_k, d_v outside {64, 128} or d_k != d_v */
+    DN_EWORKSPACE = -3, /* workspace NULL or smaller than dn_chunk_fwd_workspace() */
+    DN_EHIP = -4        /* the HIP runtime reported an error at launch */
+} dn_status;
+
+typedef enum dn_dtype { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* dn_strerror(int status);
+
+/* Library ABI version (incremented on incompatible changes). */
+int dn_version(void);
+
+/*
+ * Workspace bytes that dn_chunk_fwd and dn_kda_chunk_fwd need for these sizes
+ * (0 when T == 0; (size_t)0 also for invalid sizes, which the entry points
+ * then reject). The workspace holds per-chunk intermediates of the UT/WY form
+ * and is fully overwritten by every call; its contents between calls are
+ * unspecified.
+ */
+size_t dn_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int dtype);
+
+/*
+ * Chunkwise-parallel prefill (chunk size 64) of DeltaNet (g == NULL) or Gated
+ * DeltaNet (g != NULL). Pages: "28. Linear attention and Gated DeltaNet",
+ * section "The chunked form: recurrence as matrix multiplication" (the UT
+ * system, outputs and end-of-chunk state); "DeltaNet: Memory That Edits",
+ * section "Training it: the WY trick".
+ *   q, k     [B,H,T,dk]        v [B,H,T,dv]         (dtype)
+ *   beta     [B,H,T]           g [B,H,T] log-decay, or NULL => alpha == 1
+ *   S0       [B,H,dk,dv] fp32 start state, or NULL => zeros
+ *   o        [B,H,T,dv] (dtype) outputs, written for every t < T
+ *   S_final  [B,H,dk,dv] fp32, or NULL => not written. S_final == S0 is
+ *            allowed (in-place update of a state buffer).
+ *   workspace/workspace_bytes: device scratch of at least
+ *            dn_chunk_fwd_workspace(B,H,T,dk,dv,dtype) bytes, 256-byte aligned.
+ * T == 0 writes S_final = S0 (or zeros) and nothing else. A last chunk shorter
+ * than 64 tokens is handled by masking (identical to zero padding).
+ * The result equals the token-by-token recurrence up to rounding.
+ */
+int dn_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
+                 const void* g, const float* S0, void* o, float* S_final,
+                 int B, int H, int T, int dk, int dv, int dtype,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * KDA chunkwise prefill: as dn_chunk_fwd but g is REQUIRED and holds one
+ * log-decay per key channel, g [B,H,T,dk] (page "A walk through of the
+ * DeltaNet family of linear attention variants", KDA section). Uses the same
+ * workspace size function.
+ */
+int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
+                     const void* g, const float* S0, void* o, float* S_final,
+                     int B, int H, int T, int dk, int dv, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two phases of the chunkwise prefill, for callers that schedule them
+ * separately (for example to overlap one request's chunk-parallel phase with
+ * another's sequential phase, or to time them). On one stream,
+ *     dn_chunk_prep(kda, ...) then dn_chunk_scan(kda, ...)
+ * is exactly dn_chunk_fwd (kda = 0) or dn_kda_chunk_fwd (kda = 1).
+ *
+ * dn_chunk_prep: every 64-token chunk of every head in parallel. Computes the
+ *   running log-decay G, the UT transform T = (I + strict_tril(beta K K^T D))^-1,
+ *   W = T (beta e^G K), u = T (beta V), the causal decayed Q K^T and the
+ *   decay-scaled Q and K of each chunk (page "28. Linear attention and Gated
+ *   DeltaNet", section "The chunked form", the triangular system and the
+ *   attention matrix), and writes them to `workspace`. Arguments as in
+ *   dn_chunk_fwd; with kda = 0, g == NULL selects DeltaNet.
+ * dn_chunk_scan: the sequential inter-chunk recurrence of every head over the
+ *   workspace filled by dn_chunk_prep with the same sizes, dtype and kda: per
+ *   chunk U = u - W S, O = Q~ S + attn U, S = e^{G_C} S + K~^T U (same section,
+ *   the chunk loop). Writes o and S_final exactly as dn_chunk_fwd; S0/S_final
+ *   may alias. The workspace is read only.
+ */
+int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,
+                  const void* g, int B, int H, int T, int dk, int dv, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+int dn_chunk_scan(int kda, const float* S0, void* o, float* S_final, int B, int H, int T,
+                  int dk, int dv, int dtype, const void* workspace, size_t workspace_bytes,
+                  void* stream);
+
+/*
+ * Token-by-token recurrent form over T tokens (page "28. Linear attention and
+ * Gated DeltaNet", section "The recurrent form"), same arguments and result as
+ * dn_chunk_fwd without a workspace. One wavefront per (sequence, head,
+ * 64-column slice of the state) carries the state in registers through all T
+ * tokens.
+ */
+int dn_recurrent_fwd(const void* q, const void* k, const void* v, const void* beta,
+                     const void* g, const float* S0, void* o, float* S_final,
+                     int B, int H, int T, int dk, int dv, int dtype, void* stream);
+
+/* KDA twin of dn_recurrent_fwd: g REQUIRED, [B,H,T,dk]. */
+int dn_kda_recurrent_fwd(const void* q, const void* k, const void* v, const void* beta,
+                         const void* g, const float* S0, void* o, float* S_final,
+                         int B, int H, int T, int dk, int dv, int dtype, void* stream);
+
+/*
+ * One decode step for B sequences (one new token each), updating the state in
+ * place and returning the read-out. Decay, predict, correct, write and read are
+ * fused; every fp32 state element is read once and written once.
+ * (Page "28. Linear attention and Gated DeltaNet", section "The recurrent
+ * form", one loop iteration; page "A walk through ...", fused recurrent KDA.)
+ *   q, k [B,H,dk]   v [B,H,dv]   beta [B,H]   g [B,H] or NULL (DeltaNet)
+ *   S    [B,H,dk,dv] fp32, updated in place     o [B,H,dv] (dtype)
+ */
+int dn_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                   const void* g, float* S, void* o,
+                   int B, int H, int dk, int dv, int dtype, void* stream);
+
+/* KDA decode step: g REQUIRED, [B,H,dk] (one log-decay per key channel). */
+int dn_kda_decode_step(const void* q, const void* k, const void* v, const void* beta,
+                       const void* g, float* S, void* o,
+                       int B, int H, int dk, int dv, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTANET_H */

@@ -1,0 +1,174 @@
+"""The C-ABI library loads, exports every declared symbol, and validates its
+arguments synchronously before any HIP call (so these run without a GPU).
+
+No test here passes a complete set of valid arguments: that would enqueue
+work. Fake device pointers are plain aligned integers and are never touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from delta_rule_recurrent_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "deltanet.h")
+
+P = 0x10000          # aligned fake device pointer
+MIS = 0x10008        # 8-byte aligned only
+ODD = 0x10001        # not even element-aligned
+WS = 0x100000        # 256-aligned fake workspace
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = _lib.lib()
+    names = declared_functions()
+    assert len(names) == 11, names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_version_and_strerror():
+    lib = _lib.lib()
+    assert lib.dn_version() >= 1
+    for code in (0, -1, -2, -3, -4, 7):
+        s = lib.dn_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 0
+
+
+def test_workspace_size_function():
+    lib = _lib.lib()
+    ws = lib.dn_chunk_fwd_workspace
+    assert ws(1, 1, 0, 64, 64, 0) == 0
+    assert ws(1, 1, 64, 64, 64, 0) > 0
+    a = ws(4, 8, 2048, 128, 128, 1)
+    assert a == 32 * ws(1, 1, 2048, 128, 128, 1)
+    assert ws(1, 1, 65, 128, 128, 1) == 2 * ws(1, 1, 64, 128, 128, 1)
+    assert ws(1, 1, 64, 96, 96, 1) == 0     # unsupported head size
+    assert ws(0, 1, 64, 64, 64, 1) == 0
+    assert ws(1, 1, 64, 64, 64, 5) == 0     # unknown dtype
+
+
+def _chunk(fn, **kw):
+    args = dict(q=P, k=P, v=P, beta=P, g=P, S0=P, o=P, S_final=P, B=1, H=1, T=64, dk=64, dv=64,
+                dtype=1, ws=WS, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return getattr(_lib.lib(), fn)(args["q"], args["k"], args["v"], args["beta"], args["g"],
+                                    args["S0"], args["o"], args["S_final"], args["B"], args["H"],
+                                    args["T"], args["dk"], args["dv"], args["dtype"], args["ws"],
+                                    args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("fn", ["dn_chunk_fwd", "dn_kda_chunk_fwd"])
+def test_chunk_validation(fn):
+    E, N, W = _lib.DN_EINVAL, _lib.DN_ENOTSUP, _lib.DN_EWORKSPACE
+    for name in ("q", "k", "v", "beta", "o"):
+        assert _chunk(fn, **{name: None}) == E, name
+    assert _chunk(fn, B=0) == E
+    assert _chunk(fn, H=-1) == E
+    assert _chunk(fn, T=-5) == E
+    assert _chunk(fn, dtype=2) == E
+    assert _chunk(fn, q=MIS) == E
+    assert _chunk(fn, S_final=MIS) == E
+    assert _chunk(fn, g=ODD) == E
+    assert _chunk(fn, dk=96, dv=96) == N
+    assert _chunk(fn, dk=64, dv=128) == N
+    assert _chunk(fn, dk=256, dv=256) == N
+    assert _chunk(fn, ws=None) == W
+    assert _chunk(fn, ws_bytes=16) == W
+    assert _chunk(fn, ws=WS + 16) == W
+    assert _chunk(fn, B=1 << 20, H=1 << 10) == E   # heads beyond the grid limit
+    if fn == "dn_kda_chunk_fwd":
+        assert _chunk(fn, g=None) == E               # KDA needs its per-channel decay
+        assert _chunk(fn, dtype=0, dk=128, dv=128) == N
+
+
+def _rec(fn, **kw):
+    args = dict(q=P, k=P, v=P, beta=P, g=P, S0=P, o=P, S_final=P, B=1, H=1, T=64, dk=64, dv=64,
+                dtype=1, stream=None)
+    args.update(kw)
+    return getattr(_lib.lib(), fn)(*[args[n] for n in ("q", "k", "v", "beta", "g", "S0", "o",
+                                                        "S_final", "B", "H", "T", "dk", "dv",
+                                                        "dtype", "stream")])
+
+
+@pytest.mark.parametrize("fn", ["dn_recurrent_fwd", "dn_kda_recurrent_fwd"])
+def test_recurrent_validation(fn):
+    E, N = _lib.DN_EINVAL, _lib.DN_ENOTSUP
+    assert _rec(fn, q=None) == E
+    assert _rec(fn, o=None) == E
+    assert _rec(fn, B=0) == E
+    assert _rec(fn, dk=32, dv=32) == N
+    assert _rec(fn, beta=ODD) == E
+    assert _rec(fn, v=MIS) == E
+    if fn == "dn_kda_recurrent_fwd":
+        assert _rec(fn, g=None) == E
+
+
+def _dec(fn, **kw):
+    args = dict(q=P, k=P, v=P, beta=P, g=P, S=P, o=P, B=1, H=1, dk=128, dv=128, dtype=1,
+                stream=None)
+    args.update(kw)
+    return getattr(_lib.lib(), fn)(*[args[n] for n in ("q", "k", "v", "beta", "g", "S", "o", "B",
+                                                        "H", "dk", "dv", "dtype", "stream")])
+
+
+@pytest.mark.parametrize("fn", ["dn_decode_step", "dn_kda_decode_step"])
+def test_decode_validation(fn):
+    E, N = _lib.DN_EINVAL, _lib.DN_ENOTSUP
+    assert _dec(fn, S=None) == E
+    assert _dec(fn, o=None) == E
+    assert _dec(fn, k=None) == E
+    assert _dec(fn, S=MIS) == E
+    assert _dec(fn, B=0) == E
+    assert _dec(fn, dk=64, dv=128) == N
+    assert _dec(fn, dtype=-1) == E
+    if fn == "dn_kda_decode_step":
+        assert _dec(fn, g=None) == E
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    import delta_rule_recurrent_amd as dn
+
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        dn.chunk_fwd(q, q, q, torch.zeros(1, 1, 4, dtype=torch.bfloat16))
+
+
+def _prep(**kw):
+    a = dict(kda=0, q=P, k=P, v=P, beta=P, g=P, B=1, H=1, T=64, dk=64, dv=64, dtype=1, ws=WS,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return _lib.lib().dn_chunk_prep(*[a[n] for n in ("kda", "q", "k", "v", "beta", "g", "B", "H",
+                                                     "T", "dk", "dv", "dtype", "ws", "wsb",
+                                                     "stream")])
+
+
+def _scan(**kw):
+    a = dict(kda=0, S0=P, o=P, S_final=P, B=1, H=1, T=64, dk=64, dv=64, dtype=1, ws=WS,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return _lib.lib().dn_chunk_scan(*[a[n] for n in ("kda", "S0", "o", "S_final", "B", "H", "T",
+                                                     "dk", "dv", "dtype", "ws", "wsb", "stream")])
+
+
+def test_phase_validation():
+    E, W = _lib.DN_EINVAL, _lib.DN_EWORKSPACE
+    assert _prep(q=None) == E
+    assert _prep(kda=1, g=None) == E
+    assert _prep(ws=None) == W
+    assert _prep(wsb=8) == W
+    assert _prep(kda=1, dtype=0, dk=128, dv=128) == _lib.DN_ENOTSUP
+    assert _scan(o=None) == E
+    assert _scan(S0=MIS) == E
+    assert _scan(ws=None) == W
+    assert _scan(dk=96, dv=96) == _lib.DN_ENOTSUP
