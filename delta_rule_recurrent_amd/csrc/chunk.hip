@@ -36,11 +36,11 @@ namespace dn {
 // [tile][k-block][lane][8] elements of E (see the fragment convention in
 // dn_device.h); D-tile arrays are [tile][tile][lane][4].
 //   W   [4 token tiles][DK/32][64][8]      W = T (beta e^G K)          A-fragments
-//   Qt  [4 token tiles][DK/32][64][8]      Q~ = e^G Q                  A-fragments
+//   Qt  [4 token tiles][DK/32][64][8]      Q~ = e^G * Q                A-fragments
 //   Kt  [DK/16 chan tiles][2][64][8]       K~^T = (e^{G_C - G} K)^T    A-fragments
 //   At  [4 token tiles][2][64][8]          attn = tril(Q K^T D)         A-fragments
 //   Uu  [4 token tiles][DV/16][64][4]      u = T (beta V)              D-tiles
-//   gam [DK] float                         e^{G_C} (Gated: entry 0 only)
+//   gam [DK] float                         e^{G_C} per key channel (Gated: all equal)
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 struct WsLayout {
@@ -112,16 +112,50 @@ __device__ __forceinline__ typename Frag<E>::type frag_rows_decay(const E* M, in
     return f;
 }
 
+// fp32 16x16x16 product on the matrix cores, acc += X * Y, with X a 16x16
+// block of a row-major fp32 LDS matrix and Y a 16x16 D-tile held in
+// registers. Step s of the four 16x16x4 products contracts index 4g + s from
+// lane group g, which is exactly the value D-tile lane (g, n) holds in its
+// element s, so Y never goes through LDS.
+__device__ __forceinline__ f32x4 mma16_lds_reg(const float* X, int ldx, int lane, const f32x4& Y,
+                                               f32x4 acc) {
+    const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[r * ldx + 4 * g + s], Y[s], acc, 0, 0, 0);
+    return acc;
+}
+
+// LDS carve-up of the prep kernel (bytes). Regions X and Y are reused as the
+// work moves on (each switch is separated by a workgroup barrier):
+//   X : K rows     -> fp32 T (diagonal 16x16 inverses)          -> T' = T diag(beta e^G)
+//   Y : Q rows     -> fp32 system matrix A                      -> T'' = T diag(beta)
+//   KT: K^T (token index contiguous; KDA: becomes K~^T in place)
+//   VT: V^T
+//   XT: KDA only, (e^G K)^T
+//   GK: KDA only, fp32 running log-decay per (token, key channel)
+template <typename E, int DK, int DV, int KIND>
+struct PrepSmem {
+    static constexpr int KP = 16 / sizeof(E);  // row padding: one 16-byte vector
+    static constexpr int LDK = DK + KP;        // [64][DK] tiles
+    static constexpr int LDT = 64 + KP;        // [D][64] tiles
+    static constexpr int LDF = 68;             // fp32 64x64 matrices
+    static constexpr bool KDA = (KIND == KIND_KDA);
+    static constexpr int LDG = DK + 4;
+    static constexpr long cmax(long a, long b) { return a > b ? a : b; }
+    static constexpr long SZ_X = cmax(cmax(64L * LDK * sizeof(E), 64L * LDF * 4), 64L * LDT * sizeof(E));
+    static constexpr long SZ_Y = SZ_X;
+    static constexpr long OFF_X = 0;
+    static constexpr long OFF_Y = OFF_X + SZ_X;
+    static constexpr long OFF_KT = OFF_Y + SZ_Y;
+    static constexpr long OFF_VT = OFF_KT + (long)DK * LDT * sizeof(E);
+    static constexpr long OFF_XT = OFF_VT + (long)DV * LDT * sizeof(E);
+    static constexpr long OFF_GK = OFF_XT + (KDA ? (long)DK * LDT * sizeof(E) : 0);
+    static constexpr long TOTAL = OFF_GK + (KDA ? 64L * LDG * 4 : 0);
+};
+
 // ---------------------------------------------------------------------------
-// Prep kernel
-//
-// LDS lifetimes (one workgroup = one chunk of one head, 4 wavefronts):
-//   R1   : K rows | Q rows            (staging .. step 2)
-//          then T' | T''  (Gated / DeltaNet)  or  X^T | T''  (KDA)   (step 3 ..)
-//   KsT  : K^T (token index contiguous)  (KDA: becomes K~^T in place after step 2)
-//   VsT  : V^T                          (.. step 5)
-//   As   : fp32 system matrix           (step 2 .. step 3)
-//   Gk   : KDA only, fp32 running log-decay per (token, key channel)
+// Prep kernel: one workgroup (4 wavefronts) per (head, chunk).
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV, int KIND>
 __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q,
@@ -132,27 +166,24 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
                                                          char* __restrict__ ws, int T,
                                                          int nchunks) {
     typedef WsLayout<E, DK, DV> Lw;
+    typedef PrepSmem<E, DK, DV, KIND> Sm;
     typedef typename Frag<E>::type F;
     typedef typename Vec4<E>::type V4;
-    constexpr int KP = 16 / sizeof(E);   // row padding: one 16-byte vector
-    constexpr int LDK = DK + KP;         // leading dim of [64][DK] tiles
-    constexpr int LDT = 64 + KP;         // leading dim of [D][64] tiles
-    constexpr int LDA = 68;              // fp32 system matrix
-    constexpr bool KDA = (KIND == KIND_KDA);
-    constexpr int LDG = KDA ? DK + 4 : 1;
-    static_assert((KDA ? DK + 64 : 128) * LDT <= 2 * 64 * LDK, "R1 too small");
+    constexpr int LDK = Sm::LDK, LDT = Sm::LDT, LDF = Sm::LDF, LDG = Sm::LDG;
+    constexpr bool KDA = Sm::KDA;
 
-    __shared__ __align__(16) E R1[2 * 64 * LDK];
-    __shared__ __align__(16) E KsT[DK * LDT];
-    __shared__ __align__(16) E VsT[DV * LDT];
-    __shared__ __align__(16) float As[64 * LDA];
-    __shared__ float Gs[KDA ? 1 : 64], eG[KDA ? 1 : 64], eGC[KDA ? 1 : 64], bs[64];
-    __shared__ __align__(16) float Gk[KDA ? 64 * LDG : 1];
-    E* Ks = R1;
-    E* Qs = R1 + 64 * LDK;
-    E* XsT = R1;                                  // KDA, after step 2
-    E* Tp = R1;                                   // Gated / DeltaNet, after step 2
-    E* Tpp = R1 + (KDA ? DK : 64) * LDT;          // after step 2
+    __shared__ __align__(16) char smem[Sm::TOTAL];
+    __shared__ float Gs[64], eG[64], eGC[64], bs[64];
+    E* Ks = reinterpret_cast<E*>(smem + Sm::OFF_X);
+    E* Qs = reinterpret_cast<E*>(smem + Sm::OFF_Y);
+    float* Tf = reinterpret_cast<float*>(smem + Sm::OFF_X);
+    float* As = reinterpret_cast<float*>(smem + Sm::OFF_Y);
+    E* Tp = reinterpret_cast<E*>(smem + Sm::OFF_X);
+    E* Tpp = reinterpret_cast<E*>(smem + Sm::OFF_Y);
+    E* KsT = reinterpret_cast<E*>(smem + Sm::OFF_KT);
+    E* VsT = reinterpret_cast<E*>(smem + Sm::OFF_VT);
+    E* XsT = reinterpret_cast<E*>(smem + Sm::OFF_XT);
+    float* Gk = reinterpret_cast<float*>(smem + Sm::OFF_GK);
 
     const int c = blockIdx.x % nchunks;
     const long bh = blockIdx.x / nchunks;
@@ -181,7 +212,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
             Gs[lane] = G;
             eG[lane] = __expf(G);
             eGC[lane] = __expf(GC - G);
-            if (lane == 0) gam[0] = __expf(GC);
+            // the chunk decay, replicated per key channel so that the scan reads
+            // it like KDA's (vector loads; no scalar load on its critical path)
+            for (int ch = lane; ch < DK; ch += 64) gam[ch] = __expf(GC);
         }
     } else {
         // one thread per key channel, sequential over the 64 tokens (tokens
@@ -200,12 +233,13 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
     stage_tile<E, DV, false, true>(v + tok0 * DV, L, nullptr, 0, VsT, LDT, tid);
     __syncthreads();
 
-    // ---- 2. A = strict_tril(beta K K^T D) -> As;  attn -> A-fragments;  Q~ ---
+    // ---- 2. attn -> A-fragments, Q~ -> A-fragments; raw K K^T kept in registers
     // Wave w owns token tile w: rows i in [16w, 16w+16) of A and of attn.
     // KDA: the decay exp(G_ic - G_jc) sits inside the contraction, so both
     // operands are scaled around a reference token ref of the row tile:
     // k_i exp(G_i - G_ref) and k_j exp(G_ref - G_j). With ref in the middle of
     // the tile every factor is bounded by the decay over at most 8 tokens.
+    f32x4 sa[4];
     {
         F ka[DK / 32], qa[DK / 32];
         const int ref = 16 * w + 8;
@@ -222,24 +256,16 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
         f32x4 at[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-            f32x4 sa = zero4();
+            sa[jt] = zero4();
             at[jt] = zero4();
             if (jt <= w) {
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
                     const F kj = KDA ? frag_rows_decay<E>(Ks, LDK, Gk, LDG, 16 * jt, 32 * kb, lane, ref, -1.f)
                                      : frag_rows<E>(Ks, LDK, 16 * jt, 32 * kb, lane);
-                    sa = mma(ka[kb], kj, sa);          // (K K^T)[i][j]
+                    sa[jt] = mma(ka[kb], kj, sa[jt]);  // (K K^T)[i][j]
                     at[jt] = mma(kj, qa[kb], at[jt]);  // (K Q^T)[j][i] = attn^T
                 }
-            }
-            // system matrix: lane (gq, n) holds rows i = 16w + 4gq + e, column j = 16jt + n
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * w + 4 * gq + e, j = 16 * jt + n;
-                float val = 0.f;
-                if (i > j) val = KDA ? bs[i] * sa[e] : bs[i] * __expf(Gs[i] - Gs[j]) * sa[e];
-                As[i * LDA + j] = val;
             }
             // attn^T tile: rows j = 16jt + 4gq + e, column i = 16w + n (causal, incl. diagonal)
 #pragma unroll
@@ -254,7 +280,9 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             reinterpret_cast<F*>(Af)[(w * 2 + kb) * 64 + lane] = frag_from_tiles<E>(at[2 * kb], at[2 * kb + 1]);
-        // Q~ = e^G Q, A-fragments of token tile w
+        // Q~ = e^G * Q, A-fragments of token tile w (one factor per token, or
+        // per token and key channel for KDA). Stored in fragment order so the
+        // scan reads it with one 16-byte load per lane per fragment.
 #pragma unroll
         for (int kb = 0; kb < DK / 32; ++kb) {
             F f;
@@ -279,10 +307,20 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
                 frag_rows_scaled<E>(KsT, LDT, 16 * mt, 32 * kb, lane, 1.f, eGC);
         }
     }
-    __syncthreads();
+    __syncthreads();  // K and Q rows are dead from here on
 
+    // ---- 2b. system matrix A = strict_tril(beta_i K K^T D) into region Y -----
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * w + 4 * gq + e, j = 16 * jt + n;
+            float val = 0.f;
+            if (i > j) val = KDA ? bs[i] * sa[jt][e] : bs[i] * __expf(Gs[i] - Gs[j]) * sa[jt][e];
+            As[i * LDF + j] = val;
+        }
     if (KDA) {
-        // X^T = (e^G K)^T into R1 (K and Q rows are dead); K^T -> K~^T in place
+        // X^T = (e^G K)^T; K^T -> K~^T = (e^{G_C - G} K)^T in place
         for (int idx = tid; idx < DK * 64; idx += 256) {
             const int ch = idx / 64, t = idx % 64;
             const float kv = to_f32(KsT[ch * LDT + t]);
@@ -291,37 +329,76 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
             KsT[ch * LDT + t] = from_f32<E>(kv * __expf(GC - Gt));
         }
     }
-
-    // ---- 3. T = (I + A)^-1 by forward substitution (wave 0, lane = column) --
-    // Column j of T: T_jj = 1, T_ij = -sum_{j <= m < i} A_im T_mj for i > j.
-    if (w == 0) {
-        const int j = lane;
-        float tc[64];
-#pragma unroll
-        for (int i = 0; i < 64; ++i) tc[i] = (i == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int i = 1; i < 64; ++i) {
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < i; ++m) acc += As[i * LDA + m] * tc[m];
-            if (i > j) tc[i] = -acc;
-        }
-        const float sb = bs[j];
-        const float sbg = KDA ? 0.f : bs[j] * eG[j];
-#pragma unroll
-        for (int i = 0; i < 64; ++i) {
-            if (!KDA) Tp[i * LDT + j] = from_f32<E>(tc[i] * sbg);
-            Tpp[i * LDT + j] = from_f32<E>(tc[i] * sb);
-        }
-    }
     __syncthreads();
 
+    // ---- 3. UT transform T = (I + A)^-1, blocked over 16x16 tiles ------------
+    // 3a: wave w inverts its diagonal tile by forward substitution, lane = column:
+    //     T_jj = 1, T_ij = -sum_{j <= m < i} A_im T_mj  (rows and columns inside the tile)
+    {
+        const int j = n;
+        const int b0 = 16 * w;
+        float tc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc += As[(b0 + i) * LDF + b0 + m] * tc[m];
+            if (i > j) tc[i] = -acc;
+        }
+        if (gq == 0) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) Tf[(b0 + i) * LDF + b0 + j] = tc[i];
+        }
+    }
     if (KDA) {
         for (int p = w; p < (DK / 16) * 2; p += 4) {
             const int mt = p >> 1, kb = p & 1;
             reinterpret_cast<F*>(Kf)[p * 64 + lane] = frag_rows<E>(KsT, LDT, 16 * mt, 32 * kb, lane);
         }
     }
+    __syncthreads();
+    // 3b: wave w computes column tile w of T downwards on the matrix cores:
+    //     T_Iw = -T_II * sum_{w <= K < I} A_IK T_Kw   (16x16 tiles, fp32)
+    f32x4 tcol[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) tcol[I] = zero4();
+    {
+        f32x4 d;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d[e] = Tf[(16 * w + 4 * gq + e) * LDF + 16 * w + n];
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+            if (I == w) tcol[I] = d;
+    }
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+        if (I > w) {
+            f32x4 R = zero4();
+#pragma unroll
+            for (int K = 0; K < I; ++K)
+                if (K >= w) R = mma16_lds_reg(As + 16 * I * LDF + 16 * K, LDF, lane, tcol[K], R);
+            const f32x4 t = mma16_lds_reg(Tf + 16 * I * LDF + 16 * I, LDF, lane, R, zero4());
+            tcol[I] = -t;
+        }
+    }
+    __syncthreads();  // A and the diagonal inverses are dead from here on
+    // T' = T diag(beta e^G) into region X, T'' = T diag(beta) into region Y
+    {
+        const int j = 16 * w + n;
+        const float sb = bs[j];
+        const float sbg = KDA ? 0.f : bs[j] * eG[j];
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * gq + e;
+                if (!KDA) Tp[i * LDT + j] = from_f32<E>(tcol[I][e] * sbg);
+                Tpp[i * LDT + j] = from_f32<E>(tcol[I][e] * sb);
+            }
+    }
+    __syncthreads();
 
     // ---- 4. W^T = X^T T'^T, computed transposed so it lands as A-fragments of W
     //         (Gated / DeltaNet: X = K, T' = T diag(beta e^G); KDA: X = e^G K, T' = T diag(beta))
@@ -372,6 +449,8 @@ struct ScanOps {
     f32x4 gam[MTW];
 };
 
+// Operands of one chunk for wave w of value tile vt: one coalesced load per
+// lane per fragment.
 template <typename E, int DK, int DV, int BV, int KIND>
 __device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV>& x, const char* blk, int vt,
                                           int w, int lane) {
@@ -386,6 +465,7 @@ __device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV>& x, const char*
     const F* Af = reinterpret_cast<const F*>(base + Lw::A_OFF);
     const V4* Uf = reinterpret_cast<const V4*>(base + Lw::U_OFF);
     const float* gam = reinterpret_cast<const float*>(blk + Lw::GAM_BYTE_OFF);
+    const int gq = lane >> 4;
 #pragma unroll
     for (int kb = 0; kb < O::KB; ++kb) {
         x.w[kb] = Wf[(w * O::KB + kb) * 64 + lane];
@@ -399,13 +479,81 @@ __device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV>& x, const char*
         for (int kb = 0; kb < 2; ++kb) x.k[m][kb] = Kf[((w * O::MTW + m) * 2 + kb) * 64 + lane];
 #pragma unroll
     for (int nt = 0; nt < O::NT; ++nt) x.u[nt] = Uf[(w * (DV / 16) + vt * O::NT + nt) * 64 + lane];
-    const int gq = lane >> 4;
 #pragma unroll
-    for (int m = 0; m < O::MTW; ++m) {
-        if (KIND == KIND_KDA) x.gam[m] = *reinterpret_cast<const f32x4*>(gam + 16 * (w * O::MTW + m) + 4 * gq);
-        else {
-            const float s = gam[0];
-            x.gam[m] = f32x4{s, s, s, s};
+    for (int m = 0; m < O::MTW; ++m)
+        x.gam[m] = *reinterpret_cast<const f32x4*>(gam + 16 * (w * O::MTW + m) + 4 * gq);
+}
+
+// One chunk of the scan for one workgroup: U = u - W S, O = Q~ S + attn U,
+// S = gamma S + K~^T U. S (fp32, MFMA accumulator layout) is updated in place.
+template <typename E, int DK, int DV, int KIND, int BV>
+__device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
+                                          f32x4 (&S)[DK / 64][BV / 16],
+                                          typename Frag<E>::type (*Sx)[BV / 16][64],
+                                          typename Frag<E>::type (*Ux)[BV / 16][64],
+                                          E* __restrict__ o, long bh, int T, int t0, int vt,
+                                          int w, int lane) {
+    typedef ScanOps<E, DK, DV, BV> Ops;
+    typedef typename Ops::F F;
+    typedef typename Ops::V4 V4;
+    constexpr int NT = Ops::NT, KB = Ops::KB, MTW = Ops::MTW;
+    const int gq = lane >> 4, n = lane & 15;
+
+    // state -> B-fragments of the contraction over key channels; key-channel
+    // block kb covers the tiles 2kb, 2kb+1, i.e. wave kb (d = 128) or the waves
+    // 2kb, 2kb+1 (d = 64, one tile each, half a fragment each)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        if (MTW == 2) {
+            Sx[w][nt][lane] = frag_from_tiles<E>(S[0][nt], S[MTW - 1][nt]);
+        } else {
+            V4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = from_f32<E>(S[0][nt][e]);
+            reinterpret_cast<V4*>(&Sx[w >> 1][nt][lane])[w & 1] = h;
+        }
+    }
+    lds_barrier();
+
+    f32x4 U[NT], O[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        U[nt] = zero4();
+        O[nt] = zero4();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const F sb = Sx[kb][nt][lane];
+            U[nt] = mma(cur.w[kb], sb, U[nt]);
+            O[nt] = mma(cur.q[kb], sb, O[nt]);
+        }
+        V4 h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            U[nt][e] = to_f32(cur.u[nt][e]) - U[nt][e];
+            h[e] = from_f32<E>(U[nt][e]);
+        }
+        reinterpret_cast<V4*>(&Ux[w >> 1][nt][lane])[w & 1] = h;
+    }
+    // decay the state (its pre-decay value is already captured in Sx)
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) S[m][nt] *= cur.gam[m];
+    lds_barrier();
+
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const F ub = Ux[kb][nt][lane];
+            O[nt] = mma(cur.a[kb], ub, O[nt]);
+#pragma unroll
+            for (int m = 0; m < MTW; ++m) S[m][nt] = mma(cur.k[m][kb], ub, S[m][nt]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = t0 + 16 * w + 4 * gq + e;
+            if (t < T) o[((long)bh * T + t) * DV + vt * BV + 16 * nt + n] = from_f32<E>(O[nt][e]);
         }
     }
 }
@@ -419,7 +567,6 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
     typedef WsLayout<E, DK, DV> Lw;
     typedef ScanOps<E, DK, DV, BV> Ops;
     typedef typename Ops::F F;
-    typedef typename Ops::V4 V4;
     constexpr int NV = DV / BV, NT = Ops::NT, KB = Ops::KB, MTW = Ops::MTW;
 
     // XCD-aware mapping: consecutive workgroups go to different XCDs
@@ -448,70 +595,29 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
                 S[m][nt][e] = S0 ? S0[(bh * DK + row) * DV + col] : 0.f;
             }
 
+    // Operands of chunks c + 1 and c + 2 are in flight while chunk c is
+    // processed (three register sets in rotation), so the sequential loop does
+    // not wait on memory latency. Prefetches are unconditional (the chunk index
+    // is clamped to the last chunk): straight-line code lets the compiler wait
+    // for exactly the set in use instead of draining every load in flight.
     const char* wsh = ws + (long)bh * nchunks * Lw::BYTES;
-    Ops cur, nxt;
-    scan_load<E, DK, DV, BV, KIND>(cur, wsh, vt, w, lane);
-
-    for (int c = 0; c < nchunks; ++c) {
-        // state -> bf16/fp32 B-fragments. Key-channel block kb covers tiles 2kb, 2kb+1.
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            if (MTW == 2) {
-                Sx[w][nt][lane] = frag_from_tiles<E>(S[0][nt], S[MTW - 1][nt]);
-            } else {
-                V4 h;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = from_f32<E>(S[0][nt][e]);
-                reinterpret_cast<V4*>(&Sx[w >> 1][nt][lane])[w & 1] = h;
-            }
-        }
-        if (c + 1 < nchunks) scan_load<E, DK, DV, BV, KIND>(nxt, wsh + (long)(c + 1) * Lw::BYTES, vt, w, lane);
-        __syncthreads();
-
-        f32x4 U[NT], O[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            U[nt] = zero4();
-            O[nt] = zero4();
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const F sb = Sx[kb][nt][lane];
-                U[nt] = mma(cur.w[kb], sb, U[nt]);
-                O[nt] = mma(cur.q[kb], sb, O[nt]);
-            }
-            V4 h;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                U[nt][e] = to_f32(cur.u[nt][e]) - U[nt][e];
-                h[e] = from_f32<E>(U[nt][e]);
-            }
-            reinterpret_cast<V4*>(&Ux[w >> 1][nt][lane])[w & 1] = h;
-        }
-        // decay the state (its pre-decay value is already captured in Sx)
-#pragma unroll
-        for (int m = 0; m < MTW; ++m)
-#pragma unroll
-            for (int nt = 0; nt < NT; ++nt) S[m][nt] *= cur.gam[m];
-        __syncthreads();
-
-        const int t0 = c * CHUNK;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const F ub = Ux[kb][nt][lane];
-                O[nt] = mma(cur.a[kb], ub, O[nt]);
-#pragma unroll
-                for (int m = 0; m < MTW; ++m) S[m][nt] = mma(cur.k[m][kb], ub, S[m][nt]);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int t = t0 + 16 * w + 4 * gq + e;
-                if (t < T) o[((long)bh * T + t) * DV + vt * BV + 16 * nt + n] = from_f32<E>(O[nt][e]);
-            }
-        }
-        cur = nxt;
+    const int last = nchunks - 1;
+#define DN_SCAN_LOAD(set, cc) \
+    scan_load<E, DK, DV, BV, KIND>(set, wsh + (long)min(cc, last) * Lw::BYTES, vt, w, lane)
+    Ops o0, o1, o2;
+    DN_SCAN_LOAD(o0, 0);
+    DN_SCAN_LOAD(o1, 1);
+    for (int c = 0; c < nchunks; c += 3) {
+        DN_SCAN_LOAD(o2, c + 2);
+        scan_step<E, DK, DV, KIND, BV>(o0, S, Sx, Ux, o, bh, T, c * CHUNK, vt, w, lane);
+        if (c + 1 >= nchunks) break;
+        DN_SCAN_LOAD(o0, c + 3);
+        scan_step<E, DK, DV, KIND, BV>(o1, S, Sx, Ux, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
+        if (c + 2 >= nchunks) break;
+        DN_SCAN_LOAD(o1, c + 4);
+        scan_step<E, DK, DV, KIND, BV>(o2, S, Sx, Ux, o, bh, T, (c + 2) * CHUNK, vt, w, lane);
     }
+#undef DN_SCAN_LOAD
 
     if (S_final) {
 #pragma unroll
@@ -555,11 +661,19 @@ template <typename E, int D, int KIND>
 static hipError_t scan_t(const float* S0, void* o, float* S_final, const void* ws, int BH, int T,
                          hipStream_t st) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
-    constexpr int BV = 32;
     const long groups = ((long)BH + 7) / 8;
-    const long nblk = groups * 8 * (D / BV);
-    hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
-                       st, (const char*)ws, S0, (E*)o, S_final, T, nchunks, BH);
+    // 32-column value tiles unless that leaves most of the 256 CUs idle
+    if ((long)BH * (D / 32) >= 256 || D == 64) {
+        constexpr int BV = 32;
+        const long nblk = groups * 8 * (D / BV);
+        hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
+                           st, (const char*)ws, S0, (E*)o, S_final, T, nchunks, BH);
+    } else {
+        constexpr int BV = 16;
+        const long nblk = groups * 8 * (D / BV);
+        hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
+                           st, (const char*)ws, S0, (E*)o, S_final, T, nchunks, BH);
+    }
     return hipGetLastError();
 }
 

@@ -121,6 +121,14 @@ __device__ __forceinline__ typename Frag<E>::type frag_rows_scaled(const E* M, i
     return f;
 }
 
+// Workgroup barrier that waits only for this wave's LDS (and scalar) memory
+// operations, leaving its global loads in flight. HIP's __syncthreads() also
+// drains outstanding global loads, which would stall a software pipeline that
+// prefetches the next iteration's operands across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 // Wave-wide inclusive prefix sum over the 64 lanes.

@@ -120,9 +120,9 @@ int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* be
  *   dn_chunk_fwd; with kda = 0, g == NULL selects DeltaNet.
  * dn_chunk_scan: the sequential inter-chunk recurrence of every head over the
  *   workspace filled by dn_chunk_prep with the same sizes, dtype and kda: per
- *   chunk U = u - W S, O = Q~ S + attn U, S = e^{G_C} S + K~^T U (same section,
- *   the chunk loop). Writes o and S_final exactly as dn_chunk_fwd; S0/S_final
- *   may alias. The workspace is read only.
+ *   chunk U = u - W S, O = (e^G * Q) S + attn U, S = e^{G_C} S + K~^T U (same
+ *   section, the chunk loop). Writes o and S_final exactly as dn_chunk_fwd;
+ *   S0/S_final may alias. The workspace is read only.
  */
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,
                   const void* g, int B, int H, int T, int dk, int dv, int dtype,
