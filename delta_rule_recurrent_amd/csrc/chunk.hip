@@ -39,7 +39,8 @@ namespace dn {
 //   Qt  [4 token tiles][DK/32][64][8]      Q~ = e^G * Q                A-fragments
 //   Kt  [DK/16 chan tiles][2][64][8]       K~^T = (e^{G_C - G} K)^T    A-fragments
 //   At  [4 token tiles][2][64][8]          attn = tril(Q K^T D)         A-fragments
-//   Uu  [4 token tiles][DV/16][64][4]      u = T (beta V)              D-tiles
+//   Uu  [DV/16 col tiles][4 token tiles][64][4]  u = T (beta V)         D-tiles
+//                                          (a 16-column slice is contiguous)
 //   gam [DK] float                         e^{G_C} per key channel (Gated: all equal)
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
@@ -430,7 +431,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
         V4 u4;
 #pragma unroll
         for (int e = 0; e < 4; ++e) u4[e] = from_f32<E>(acc[e]);
-        reinterpret_cast<V4*>(Uf)[(w * (DV / 16) + nt) * 64 + lane] = u4;
+        reinterpret_cast<V4*>(Uf)[(nt * 4 + w) * 64 + lane] = u4;
     }
 }
 
@@ -449,54 +450,78 @@ struct ScanOps {
     f32x4 gam[MTW];
 };
 
-// Operands of one chunk for wave w of value tile vt: one coalesced load per
-// lane per fragment.
-template <typename E, int DK, int DV, int BV, int KIND>
-__device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV>& x, const char* blk, int vt,
-                                          int w, int lane) {
+// Operands of one chunk for wave w of value tile vt, in four parts (one
+// coalesced load per lane per fragment). The parts are issued at different
+// points of the previous-but-one chunk's step, so the wave never stalls on a
+// burst of loads waiting for the memory pipeline to accept them.
+template <int PART, typename E, int DK, int DV, int BV>
+__device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV>& x, const char* blk, int vt,
+                                               int w, int lane) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef ScanOps<E, DK, DV, BV> O;
     typedef typename O::F F;
     typedef typename O::V4 V4;
     const E* base = reinterpret_cast<const E*>(blk);
-    const F* Wf = reinterpret_cast<const F*>(base + Lw::W_OFF);
-    const F* Qf = reinterpret_cast<const F*>(base + Lw::Q_OFF);
-    const F* Kf = reinterpret_cast<const F*>(base + Lw::K_OFF);
-    const F* Af = reinterpret_cast<const F*>(base + Lw::A_OFF);
-    const V4* Uf = reinterpret_cast<const V4*>(base + Lw::U_OFF);
-    const float* gam = reinterpret_cast<const float*>(blk + Lw::GAM_BYTE_OFF);
-    const int gq = lane >> 4;
+    if (PART == 0) {
+        const F* Wf = reinterpret_cast<const F*>(base + Lw::W_OFF);
 #pragma unroll
-    for (int kb = 0; kb < O::KB; ++kb) {
-        x.w[kb] = Wf[(w * O::KB + kb) * 64 + lane];
-        x.q[kb] = Qf[(w * O::KB + kb) * 64 + lane];
+        for (int kb = 0; kb < O::KB; ++kb) x.w[kb] = Wf[(w * O::KB + kb) * 64 + lane];
+    } else if (PART == 1) {
+        const F* Qf = reinterpret_cast<const F*>(base + Lw::Q_OFF);
+#pragma unroll
+        for (int kb = 0; kb < O::KB; ++kb) x.q[kb] = Qf[(w * O::KB + kb) * 64 + lane];
+    } else if (PART == 2) {
+        const F* Kf = reinterpret_cast<const F*>(base + Lw::K_OFF);
+        const F* Af = reinterpret_cast<const F*>(base + Lw::A_OFF);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) x.a[kb] = Af[(w * 2 + kb) * 64 + lane];
+#pragma unroll
+        for (int m = 0; m < O::MTW; ++m)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) x.k[m][kb] = Kf[((w * O::MTW + m) * 2 + kb) * 64 + lane];
+    } else {
+        const V4* Uf = reinterpret_cast<const V4*>(base + Lw::U_OFF);
+        const float* gam = reinterpret_cast<const float*>(blk + Lw::GAM_BYTE_OFF);
+        const int gq = lane >> 4;
+#pragma unroll
+        for (int nt = 0; nt < O::NT; ++nt) x.u[nt] = Uf[((vt * O::NT + nt) * 4 + w) * 64 + lane];
+#pragma unroll
+        for (int m = 0; m < O::MTW; ++m)
+            x.gam[m] = *reinterpret_cast<const f32x4*>(gam + 16 * (w * O::MTW + m) + 4 * gq);
     }
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) x.a[kb] = Af[(w * 2 + kb) * 64 + lane];
-#pragma unroll
-    for (int m = 0; m < O::MTW; ++m)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) x.k[m][kb] = Kf[((w * O::MTW + m) * 2 + kb) * 64 + lane];
-#pragma unroll
-    for (int nt = 0; nt < O::NT; ++nt) x.u[nt] = Uf[(w * (DV / 16) + vt * O::NT + nt) * 64 + lane];
-#pragma unroll
-    for (int m = 0; m < O::MTW; ++m)
-        x.gam[m] = *reinterpret_cast<const f32x4*>(gam + 16 * (w * O::MTW + m) + 4 * gq);
 }
 
+template <typename E, int DK, int DV, int BV>
+__device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV>& x, const char* blk, int vt,
+                                          int w, int lane) {
+    scan_load_part<0>(x, blk, vt, w, lane);
+    scan_load_part<1>(x, blk, vt, w, lane);
+    scan_load_part<2>(x, blk, vt, w, lane);
+    scan_load_part<3>(x, blk, vt, w, lane);
+}
+
+// Keeps the compiler from moving memory operations across this point (the
+// load parts stay where they are placed in the step).
+__device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
+
 // One chunk of the scan for one workgroup: U = u - W S, O = Q~ S + attn U,
-// S = gamma S + K~^T U. S (fp32, MFMA accumulator layout) is updated in place.
+// S = gamma S + K~^T U. S (fp32, MFMA accumulator layout) is updated in
+// place; the operands of chunk c+2 (`nxt`, from block `nblk`) are loaded in
+// parts along the way; the output tile leaves through LDS as 16-byte rows.
 template <typename E, int DK, int DV, int KIND, int BV>
 __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
+                                          ScanOps<E, DK, DV, BV>& nxt, const char* nblk,
                                           f32x4 (&S)[DK / 64][BV / 16],
                                           typename Frag<E>::type (*Sx)[BV / 16][64],
-                                          typename Frag<E>::type (*Ux)[BV / 16][64],
+                                          typename Frag<E>::type (*Ux)[BV / 16][64], E* ob,
                                           E* __restrict__ o, long bh, int T, int t0, int vt,
                                           int w, int lane) {
     typedef ScanOps<E, DK, DV, BV> Ops;
     typedef typename Ops::F F;
     typedef typename Ops::V4 V4;
+    typedef typename Vec16<E>::type V16;
     constexpr int NT = Ops::NT, KB = Ops::KB, MTW = Ops::MTW;
+    constexpr int LDO = BV + 16 / sizeof(E);   // output staging row (padded)
     const int gq = lane >> 4, n = lane & 15;
 
     // state -> B-fragments of the contraction over key channels; key-channel
@@ -513,6 +538,8 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
             reinterpret_cast<V4*>(&Sx[w >> 1][nt][lane])[w & 1] = h;
         }
     }
+    sched_fence();
+    scan_load_part<0>(nxt, nblk, vt, w, lane);
     lds_barrier();
 
     f32x4 U[NT], O[NT];
@@ -526,6 +553,11 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
             U[nt] = mma(cur.w[kb], sb, U[nt]);
             O[nt] = mma(cur.q[kb], sb, O[nt]);
         }
+    }
+    sched_fence();
+    scan_load_part<1>(nxt, nblk, vt, w, lane);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
         V4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -539,6 +571,8 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
     for (int m = 0; m < MTW; ++m)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) S[m][nt] *= cur.gam[m];
+    sched_fence();
+    scan_load_part<2>(nxt, nblk, vt, w, lane);
     lds_barrier();
 
 #pragma unroll
@@ -550,11 +584,21 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
 #pragma unroll
             for (int m = 0; m < MTW; ++m) S[m][nt] = mma(cur.k[m][kb], ub, S[m][nt]);
         }
+        // stage this wave's 16 output rows (token tile w) for row stores
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = t0 + 16 * w + 4 * gq + e;
-            if (t < T) o[((long)bh * T + t) * DV + vt * BV + 16 * nt + n] = from_f32<E>(O[nt][e]);
-        }
+        for (int e = 0; e < 4; ++e) ob[(4 * gq + e) * LDO + 16 * nt + n] = from_f32<E>(O[nt][e]);
+    }
+    sched_fence();
+    scan_load_part<3>(nxt, nblk, vt, w, lane);
+    // 16 rows x BV columns: BV*sizeof(E) bytes per row, 16 bytes per lane
+    constexpr int PER_ROW = BV * sizeof(E) / 16;
+    constexpr int VEC = 16 / sizeof(E);
+#pragma unroll
+    for (int p = lane; p < 16 * PER_ROW; p += 64) {
+        const int row = p / PER_ROW, col = (p % PER_ROW) * VEC;
+        const int t = t0 + 16 * w + row;
+        const V16 val = *reinterpret_cast<const V16*>(&ob[row * LDO + col]);
+        if (t < T) *reinterpret_cast<V16*>(o + ((long)bh * T + t) * DV + vt * BV + col) = val;
     }
 }
 
@@ -582,42 +626,47 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
 
     __shared__ F Sx[KB][NT][64];   // state as B-fragments (contraction over key channels)
     __shared__ F Ux[2][NT][64];    // U as B-fragments (contraction over tokens)
+    constexpr int LDO = BV + 16 / sizeof(E);
+    __shared__ __align__(16) E Ob[4][16 * LDO];   // per-wave output staging
 
     // fp32 state tile: rows 16*(w*MTW + m) + 4gq + e, columns vt*BV + 16nt + n
     f32x4 S[MTW][NT];
+    if (S0) {
 #pragma unroll
-    for (int m = 0; m < MTW; ++m)
+        for (int m = 0; m < MTW; ++m)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+            for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * (w * MTW + m) + 4 * gq + e, col = vt * BV + 16 * nt + n;
-                S[m][nt][e] = S0 ? S0[(bh * DK + row) * DV + col] : 0.f;
-            }
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * (w * MTW + m) + 4 * gq + e, col = vt * BV + 16 * nt + n;
+                    S[m][nt][e] = S0[(bh * DK + row) * DV + col];
+                }
+    } else {
+#pragma unroll
+        for (int m = 0; m < MTW; ++m)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) S[m][nt] = zero4();
+    }
 
     // Operands of chunks c + 1 and c + 2 are in flight while chunk c is
-    // processed (three register sets in rotation), so the sequential loop does
-    // not wait on memory latency. Prefetches are unconditional (the chunk index
-    // is clamped to the last chunk): straight-line code lets the compiler wait
-    // for exactly the set in use instead of draining every load in flight.
+    // processed (three register sets in rotation). Prefetches are
+    // unconditional (the chunk index is clamped to the last chunk):
+    // straight-line code lets the compiler wait for exactly the set in use
+    // instead of draining every load in flight.
     const char* wsh = ws + (long)bh * nchunks * Lw::BYTES;
     const int last = nchunks - 1;
-#define DN_SCAN_LOAD(set, cc) \
-    scan_load<E, DK, DV, BV, KIND>(set, wsh + (long)min(cc, last) * Lw::BYTES, vt, w, lane)
+    auto blk = [&](int cc) { return wsh + (long)min(cc, last) * Lw::BYTES; };
     Ops o0, o1, o2;
-    DN_SCAN_LOAD(o0, 0);
-    DN_SCAN_LOAD(o1, 1);
+    scan_load(o0, blk(0), vt, w, lane);
+    scan_load(o1, blk(1), vt, w, lane);
+    E* ob = Ob[w];
     for (int c = 0; c < nchunks; c += 3) {
-        DN_SCAN_LOAD(o2, c + 2);
-        scan_step<E, DK, DV, KIND, BV>(o0, S, Sx, Ux, o, bh, T, c * CHUNK, vt, w, lane);
+        scan_step<E, DK, DV, KIND, BV>(o0, o2, blk(c + 2), S, Sx, Ux, ob, o, bh, T, c * CHUNK, vt, w, lane);
         if (c + 1 >= nchunks) break;
-        DN_SCAN_LOAD(o0, c + 3);
-        scan_step<E, DK, DV, KIND, BV>(o1, S, Sx, Ux, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
+        scan_step<E, DK, DV, KIND, BV>(o1, o0, blk(c + 3), S, Sx, Ux, ob, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
         if (c + 2 >= nchunks) break;
-        DN_SCAN_LOAD(o1, c + 4);
-        scan_step<E, DK, DV, KIND, BV>(o2, S, Sx, Ux, o, bh, T, (c + 2) * CHUNK, vt, w, lane);
+        scan_step<E, DK, DV, KIND, BV>(o2, o1, blk(c + 4), S, Sx, Ux, ob, o, bh, T, (c + 2) * CHUNK, vt, w, lane);
     }
-#undef DN_SCAN_LOAD
 
     if (S_final) {
 #pragma unroll
