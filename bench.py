@@ -55,16 +55,58 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# HBM traffic per launch from rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE in
+# KiB per dispatch, each in a run of its own) on the workloads timed here. A plain
+# device copy of 512 MiB reads FETCH_SIZE = 262,158 KiB and WRITE_SIZE = 524,288 KiB,
+# so FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0. Each entry carries the
+# SHA-256 of the kernel sources it was taken on; when they have changed since,
+# the figure no longer describes the kernel and is reported as null.
+FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
+CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
+                 "delta_rule_recurrent_amd/csrc/dn_launch.h")
+DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
+                  "delta_rule_recurrent_amd/csrc/dn_launch.h")
+TRAFFIC = {
+    "chunk_prep_kernel": {"fetch_kib": 24822.4, "write_kib": 74240.0, "sources": CHUNK_SOURCES,
+                          "sha256": "e0a2804fd3558c7649c51c41fdbd4c005317bcd87b48d0981e9e783b231414e9"},
+    "chunk_scan_kernel": {"fetch_kib": 37166.2, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
+                          "sha256": "e0a2804fd3558c7649c51c41fdbd4c005317bcd87b48d0981e9e783b231414e9"},
+    "decode_step_kernel": {"fetch_kib": 132752.2, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+                           "sha256": "a64a53303fb0eb0c9c813ca7277b3d62e203d6b69865cf3320005df89f2e075b"},
+}
+
+
+def sources_sha256(sources):
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in sources:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_bytes(kernel):
+    """Measured HBM bytes per launch (read + write, calibrated), or None when the
+    kernel sources changed after the counters were taken."""
+    t = TRAFFIC.get(kernel)
+    if t is None or t["sha256"] != sources_sha256(t["sources"]):
+        return None
+    return int(round((t["fetch_kib"] * FETCH_SCALE + t["write_kib"] * WRITE_SCALE) * 1024))
+
+
 def event_time_ms(torch, fn, reps):
-    """Average duration of fn() (one kernel launch) bracketed by events on the current stream."""
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        starts[i].record()
+    """Average duration of one fn() (one kernel launch): `reps` launches back to
+    back on the current stream between one pair of HIP events, after one
+    untimed launch. Matches the per-dispatch average of a kernel trace."""
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
         fn()
-        ends[i].record()
+    e1.record()
     torch.cuda.synchronize()
-    return sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / reps
+    return e0.elapsed_time(e1) / reps
 
 
 def main():
@@ -74,8 +116,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the CPU oracle on the workload until this much time has passed")
     ap.add_argument("--no-workloads", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the headline prefill (for profiling the other kernels alone)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (three times) and exit: "
+                         "the reference kernel for scaling memory-traffic counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -97,7 +146,33 @@ def main():
     def to_dev(d):
         return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
 
+    if args.copy_mib:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "copies": 3}), flush=True)
+        return
+
     # ------------------------------------------------------------------ prefill
+    result = {}
+    if not args.no_prefill:
+        result = run_prefill(args, torch, np, dn, synthetic, to_dev, dev)
+
+    # ------------------------------------------------------------------- decode
+    if not args.no_decode:
+        result["decode"] = run_decode(args, torch, dn, synthetic, to_dev)
+
+    # ---------------------------------------------------------- other workloads
+    if not args.no_workloads:
+        result["workloads"] = run_workloads(torch, dn, synthetic, to_dev, dev)
+
+    print(json.dumps(result), flush=True)
+
+
+def run_prefill(args, torch, np, dn, synthetic, to_dev, dev):
     name = "gdn_prefill_b4_h8_t2048_d128"
     cfg = synthetic.CONFIGS[name]
     B, H, T, d = cfg["B"], cfg["H"], cfg["T"], cfg["dk"]
@@ -152,7 +227,8 @@ def main():
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(kern[dom]["frac_mfma"], 4),
-        "traffic": None,
+        "traffic": traffic_bytes(dom),
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
         "algorithmic_flop_per_launch": kern[dom]["flop"],
         "avg_launch_ms": round(kern[dom]["ms"], 5),
     }
@@ -180,15 +256,19 @@ def main():
 
         nthreads = len(os.sched_getaffinity(0))
         log("cpu oracle on %d threads" % nthreads)
-        t = time.perf_counter()
-        o_ref, S_ref = oracle.recurrent(inp_cpu["q"], inp_cpu["k"], inp_cpu["v"], inp_cpu["beta"],
-                                        inp_cpu["g"], None, nthreads=nthreads)
-        t = time.perf_counter() - t
+        # the whole workload, repeated until about 10 s of CPU time have passed
+        reps, t = 0, 0.0
+        while reps == 0 or t < args.cpu_seconds:
+            t0 = time.perf_counter()
+            o_ref, S_ref = oracle.recurrent(inp_cpu["q"], inp_cpu["k"], inp_cpu["v"],
+                                            inp_cpu["beta"], inp_cpu["g"], None, nthreads=nthreads)
+            t += time.perf_counter() - t0
+            reps += 1
         result["cpu_baseline"] = {
-            "value": round(tokens / t, 1), "unit": "tokens/s",
+            "value": round(tokens * reps / t, 1), "unit": "tokens/s",
             "cores": oracle.max_threads(nthreads), "kind": "oracle",
             "sample": "the whole workload (B=4, H=8, T=2048, d=128; fp64 token-by-token "
-                      "recurrence, one rep, %.2f s)" % t,
+                      "recurrence) run %d times back to back, %.2f s in total" % (reps, t),
         }
         og = o.float().cpu().double().numpy()
         sg = S_final.cpu().double().numpy()
@@ -199,97 +279,100 @@ def main():
         }
         log("cpu oracle %.2f s, parity %s" % (t, result["parity"]))
 
-    # ------------------------------------------------------------------- decode
-    if not args.no_decode:
-        name_d = "gdn_decode_b256_h16_d128"
-        cd = synthetic.CONFIGS[name_d]
-        Bd, Hd, dd = cd["B"], cd["H"], cd["dk"]
-        nsteps = args.decode_steps
-        log("generating", name_d, nsteps, "steps")
-        dinp = to_dev(synthetic.make_config(name_d, steps=nsteps))
-        S = dinp["S0"].clone()
-        od = torch.empty(Bd, Hd, dd, dtype=torch.bfloat16, device=dev)
-        xs = [(dinp["q"][s], dinp["k"][s], dinp["v"][s], dinp["beta"][s], dinp["g"][s])
-              for s in range(nsteps)]
+    return result
 
-        def dstep(s):
-            q_, k_, v_, b_, g_ = xs[s]
-            dn.decode_step(q_, k_, v_, b_, g_, S, o=od)
 
-        for s in range(min(10, nsteps)):
+def run_decode(args, torch, dn, synthetic, to_dev):
+    name_d = "gdn_decode_b256_h16_d128"
+    cd = synthetic.CONFIGS[name_d]
+    Bd, Hd, dd = cd["B"], cd["H"], cd["dk"]
+    nsteps = args.decode_steps
+    log("generating", name_d, nsteps, "steps")
+    dinp = to_dev(synthetic.make_config(name_d, steps=nsteps))
+    S = dinp["S0"].clone()
+    od = torch.empty(Bd, Hd, dd, dtype=torch.bfloat16, device=S.device)
+    xs = [(dinp["q"][s], dinp["k"][s], dinp["v"][s], dinp["beta"][s], dinp["g"][s])
+          for s in range(nsteps)]
+
+    def dstep(s):
+        q_, k_, v_, b_, g_ = xs[s]
+        dn.decode_step(q_, k_, v_, b_, g_, S, o=od)
+
+    for s in range(min(10, nsteps)):
+        dstep(s)
+    torch.cuda.synchronize()
+    runs = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(nsteps):
             dstep(s)
+        e1.record()
         torch.cuda.synchronize()
-        runs = []
+        runs.append(e0.elapsed_time(e1))
+    loop_ms = sorted(runs)[1]
+    per_launch = event_time_ms(torch, lambda: dstep(0), 200)
+    bps = decode_bytes_per_step(Bd, Hd, dd)
+    gbs_loop = bps * nsteps / (loop_ms * 1e-3) / 1e9
+    gbs_kernel = bps / (per_launch * 1e-3) / 1e9
+    log("decode %.2f us/step  %.1f GB/s loop, %.1f GB/s per launch"
+        % (loop_ms * 1000 / nsteps, gbs_loop, gbs_kernel))
+    return {
+        "workload": name_d, "B": Bd, "H": Hd, "d": dd, "steps": nsteps,
+        "ms_per_1000_steps": round(loop_ms * 1000.0 / nsteps, 3),
+        "us_per_step": round(loop_ms * 1000.0 / nsteps, 2),
+        "token_heads_per_s": round(Bd * Hd * nsteps / (loop_ms * 1e-3), 1),
+        "state_gbs": round(gbs_loop, 1), "frac_hbm": round(gbs_loop / PEAK_HBM_GBS, 4),
+        "bytes_per_step": bps,
+        "roofline": {"kernel": "decode_step_kernel", "bound": "hbm",
+                     "achieved": round(gbs_kernel, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs_kernel / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_bytes("decode_step_kernel"),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + "
+                                     "WRITE_SIZE x1.0)",
+                     "algorithmic_bytes_per_launch": bps,
+                     "avg_launch_ms": round(per_launch, 5)},
+    }
+
+
+def run_workloads(torch, dn, synthetic, to_dev, dev):
+    wl = {}
+    for wname, form in (("gdn_prefill_b1_h16_t65536_d128", "chunk"),
+                        ("kda_prefill_b2_h16_t8192_d128", "chunk"),
+                        ("deltanet_fp32_t512_d64", "chunk"),
+                        ("deltanet_fp32_t512_d64", "recurrent")):
+        c = synthetic.CONFIGS[wname]
+        log("generating", wname)
+        x = to_dev(synthetic.make_config(wname))
+        Bw, Hw, Tw, dw = c["B"], c["H"], c["T"], c["dk"]
+        dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+        kda = c["kind"] == "kda"
+        wsw = torch.empty(max(dn.workspace_bytes(Bw, Hw, Tw, dw, dw, dt), 1), dtype=torch.uint8,
+                          device=dev)
+        ow = torch.empty(Bw, Hw, Tw, dw, dtype=dt, device=dev)
+        Sw = torch.empty(Bw, Hw, dw, dw, dtype=torch.float32, device=dev)
+        if form == "chunk":
+            f = dn.kda_chunk_fwd if kda else dn.chunk_fwd
+            run = lambda: f(x["q"], x["k"], x["v"], x["beta"], x["g"], None, o=ow, S_final=Sw,
+                            workspace=wsw)
+        else:
+            run = lambda: dn.recurrent_fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], None)
         for _ in range(3):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for s in range(nsteps):
-                dstep(s)
-            e1.record()
-            torch.cuda.synchronize()
-            runs.append(e0.elapsed_time(e1))
-        loop_ms = sorted(runs)[1]
-        per_launch = event_time_ms(torch, lambda: dstep(0), 200)
-        bps = decode_bytes_per_step(Bd, Hd, dd)
-        gbs_loop = bps * nsteps / (loop_ms * 1e-3) / 1e9
-        gbs_kernel = bps / (per_launch * 1e-3) / 1e9
-        result["decode"] = {
-            "workload": name_d, "B": Bd, "H": Hd, "d": dd, "steps": nsteps,
-            "ms_per_1000_steps": round(loop_ms * 1000.0 / nsteps, 3),
-            "us_per_step": round(loop_ms * 1000.0 / nsteps, 2),
-            "token_heads_per_s": round(Bd * Hd * nsteps / (loop_ms * 1e-3), 1),
-            "state_gbs": round(gbs_loop, 1), "frac_hbm": round(gbs_loop / PEAK_HBM_GBS, 4),
-            "bytes_per_step": bps,
-            "roofline": {"kernel": "decode_step_kernel", "bound": "hbm",
-                         "achieved": round(gbs_kernel, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                         "frac": round(gbs_kernel / PEAK_HBM_GBS, 4), "traffic": None,
-                         "avg_launch_ms": round(per_launch, 5)},
-        }
-        log("decode %.2f us/step  %.1f GB/s loop, %.1f GB/s per launch"
-            % (loop_ms * 1000 / nsteps, gbs_loop, gbs_kernel))
-        del dinp, xs, S
-
-    # ---------------------------------------------------------- other workloads
-    if not args.no_workloads:
-        wl = {}
-        for wname, form in (("gdn_prefill_b1_h16_t65536_d128", "chunk"),
-                            ("kda_prefill_b2_h16_t8192_d128", "chunk"),
-                            ("deltanet_fp32_t512_d64", "chunk"),
-                            ("deltanet_fp32_t512_d64", "recurrent")):
-            c = synthetic.CONFIGS[wname]
-            log("generating", wname)
-            x = to_dev(synthetic.make_config(wname))
-            Bw, Hw, Tw, dw = c["B"], c["H"], c["T"], c["dk"]
-            dt = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
-            kda = c["kind"] == "kda"
-            wsw = torch.empty(max(dn.workspace_bytes(Bw, Hw, Tw, dw, dw, dt), 1), dtype=torch.uint8,
-                              device=dev)
-            ow = torch.empty(Bw, Hw, Tw, dw, dtype=dt, device=dev)
-            Sw = torch.empty(Bw, Hw, dw, dw, dtype=torch.float32, device=dev)
-            if form == "chunk":
-                f = dn.kda_chunk_fwd if kda else dn.chunk_fwd
-                run = lambda: f(x["q"], x["k"], x["v"], x["beta"], x["g"], None, o=ow, S_final=Sw,
-                                workspace=wsw)
-            else:
-                run = lambda: dn.recurrent_fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], None)
-            for _ in range(3):
-                run()
-            reps = 5 if Tw >= 8192 else 20
-            ms = event_time_ms(torch, run, reps)
-            tok = Bw * Hw * Tw
-            entry = {"form": form, "ms": round(ms, 4), "tokens_per_s": round(tok / (ms * 1e-3), 1)}
-            if form == "chunk":
-                tf = (flops_prep(dw) + flops_scan(dw)) * tok / (ms * 1e-3) / 1e12
-                entry["tflops"] = round(tf, 2)
-                entry["frac_mfma"] = round(tf / (PEAK_BF16_TFLOPS if dt == torch.bfloat16 else 157.3), 4)
-                entry["gbs_algorithmic"] = round(bytes_prefill(Bw, Hw, Tw, dw, 2 if dt == torch.bfloat16 else 4)
-                                                 / (ms * 1e-3) / 1e9, 1)
-            wl["%s/%s" % (wname, form)] = entry
-            log("  %s %s %.4f ms" % (wname, form, ms))
-            del x, wsw, ow, Sw
-        result["workloads"] = wl
-
-    print(json.dumps(result), flush=True)
+            run()
+        reps = 5 if Tw >= 8192 else 20
+        ms = event_time_ms(torch, run, reps)
+        tok = Bw * Hw * Tw
+        entry = {"form": form, "ms": round(ms, 4), "tokens_per_s": round(tok / (ms * 1e-3), 1)}
+        if form == "chunk":
+            tf = (flops_prep(dw) + flops_scan(dw)) * tok / (ms * 1e-3) / 1e12
+            entry["tflops"] = round(tf, 2)
+            entry["frac_mfma"] = round(tf / (PEAK_BF16_TFLOPS if dt == torch.bfloat16 else 157.3), 4)
+            entry["gbs_algorithmic"] = round(bytes_prefill(Bw, Hw, Tw, dw, 2 if dt == torch.bfloat16 else 4)
+                                             / (ms * 1e-3) / 1e9, 1)
+        wl["%s/%s" % (wname, form)] = entry
+        log("  %s %s %.4f ms" % (wname, form, ms))
+        del x, wsw, ow, Sw
+    return wl
 
 
 if __name__ == "__main__":
