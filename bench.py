@@ -207,7 +207,8 @@ def run_prefill(args, torch, np, dn, synthetic, to_dev, dev):
     # per-kernel live timing of the two phases (same stream, events around each launch)
     prep_ms = event_time_ms(torch, lambda: dn.chunk_prep(inp["q"], inp["k"], inp["v"], inp["beta"],
                                                          inp["g"], ws), args.steps)
-    scan_ms = event_time_ms(torch, lambda: dn.chunk_scan(o, ws, None, S_final), args.steps)
+    scan_ms = event_time_ms(torch, lambda: dn.chunk_scan(inp["q"], o, ws, None, S_final),
+                            args.steps)
     kern = {
         "chunk_prep_kernel": dict(ms=prep_ms, flop=flops_prep(d) * tokens),
         "chunk_scan_kernel": dict(ms=scan_ms, flop=flops_scan(d) * tokens),

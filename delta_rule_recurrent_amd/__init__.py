@@ -135,22 +135,24 @@ def chunk_prep(q, k, v, beta, g, workspace, *, kda=False, stream=None):
     _lib.check("dn_chunk_prep", st)
 
 
-def chunk_scan(o, workspace, S0=None, S_final=None, *, kda=False, stream=None):
+def chunk_scan(q, o, workspace, S0=None, S_final=None, *, kda=False, stream=None):
     """Phase 2 of the chunkwise prefill: the sequential scan over ``workspace``.
 
+    q is the query tensor given to chunk_prep (read again by this phase);
     o [B,H,T,dv] (input dtype) receives the outputs; S_final (fp32) the end state.
     """
     B, H, T, dv = o.shape
     dk = dv
     dev, dt = o.device, o.dtype
+    _check_tensor("q", q, (B, H, T, dk), dt, dev)
     _check_tensor("o", o, (B, H, T, dv), dt, dev)
     if S0 is not None:
         _check_tensor("S0", S0, (B, H, dk, dv), torch.float32, dev)
     if S_final is not None:
         _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
-    st = lib().dn_chunk_scan(int(kda), _ptr(S0), _ptr(o), _ptr(S_final), B, H, T, dk, dv, _DT[dt],
-                             _ptr(workspace), workspace.numel() * workspace.element_size(),
-                             _stream(stream))
+    st = lib().dn_chunk_scan(int(kda), _ptr(q), _ptr(S0), _ptr(o), _ptr(S_final), B, H, T, dk, dv,
+                             _DT[dt], _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
     _lib.check("dn_chunk_scan", st)
 
 

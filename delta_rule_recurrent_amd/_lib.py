@@ -27,7 +27,7 @@ SIGNATURES = {
     "dn_chunk_fwd": (_i, _PREFILL + [_vp, _sz, _vp]),
     "dn_kda_chunk_fwd": (_i, _PREFILL + [_vp, _sz, _vp]),
     "dn_chunk_prep": (_i, [_i] + [_vp] * 5 + [_i] * 6 + [_vp, _sz, _vp]),
-    "dn_chunk_scan": (_i, [_i] + [_vp] * 3 + [_i] * 6 + [_vp, _sz, _vp]),
+    "dn_chunk_scan": (_i, [_i] + [_vp] * 4 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_recurrent_fwd": (_i, _PREFILL + [_vp]),
     "dn_kda_recurrent_fwd": (_i, _PREFILL + [_vp]),
     "dn_decode_step": (_i, [_vp] * 7 + [_i] * 5 + [_vp]),

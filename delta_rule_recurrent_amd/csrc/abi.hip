@@ -75,8 +75,8 @@ int chunk_common(int kind, const void* q, const void* k, const void* v, const vo
     hipError_t e = dn::launch_chunk_prep(kind, dtype, q, k, v, beta, g, workspace, (int)BH, T, dk,
                                          dv, as_stream(stream));
     if (e != hipSuccess) return DN_EHIP;
-    return hip_status(dn::launch_chunk_scan(kind, dtype, S0, o, S_final, workspace, (int)BH, T, dk,
-                                            dv, as_stream(stream)));
+    return hip_status(dn::launch_chunk_scan(kind, dtype, q, S0, o, S_final, workspace, (int)BH, T,
+                                            dk, dv, as_stream(stream)));
 }
 
 int recurrent_common(int kind, const void* q, const void* k, const void* v, const void* beta,
@@ -160,11 +160,11 @@ int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const vo
                                             workspace, (int)BH, T, dk, dv, as_stream(stream)));
 }
 
-int dn_chunk_scan(int kda, const float* S0, void* o, float* S_final, int B, int H, int T, int dk,
-                  int dv, int dtype, const void* workspace, size_t workspace_bytes,
+int dn_chunk_scan(int kda, const void* q, const float* S0, void* o, float* S_final, int B, int H,
+                  int T, int dk, int dv, int dtype, const void* workspace, size_t workspace_bytes,
                   void* stream) {
-    // the per-token inputs are not read by this phase: o stands in for them
-    int st = check_common(o, o, o, o, nullptr, false, S0, o, S_final, B, H, T, dk, dv, dtype);
+    // k, v and beta are not read by this phase: q stands in for them
+    int st = check_common(q, q, q, q, nullptr, false, S0, o, S_final, B, H, T, dk, dv, dtype);
     if (st != DN_OK) return st;
     if (kda && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
     const long long BH = (long long)B * H;
@@ -174,7 +174,7 @@ int dn_chunk_scan(int kda, const float* S0, void* o, float* S_final, int B, int 
     }
     st = check_workspace(BH, T, dk, dv, dtype, workspace, workspace_bytes);
     if (st != DN_OK) return st;
-    return hip_status(dn::launch_chunk_scan(kda ? dn::KIND_KDA : dn::KIND_GATED, dtype, S0, o,
+    return hip_status(dn::launch_chunk_scan(kda ? dn::KIND_KDA : dn::KIND_GATED, dtype, q, S0, o,
                                             S_final, workspace, (int)BH, T, dk, dv,
                                             as_stream(stream)));
 }

@@ -26,6 +26,8 @@
 //                      all chunks; per chunk U = u - W S, O = Q~ S + attn U,
 //                      S = gamma S + K~^T U, chained through two small LDS
 //                      exchanges of bf16 fragments.
+#include <atomic>
+
 #include "dn_device.h"
 #include "dn_launch.h"
 
@@ -36,12 +38,14 @@ namespace dn {
 // [tile][k-block][lane][8] elements of E (see the fragment convention in
 // dn_device.h); D-tile arrays are [tile][tile][lane][4].
 //   W   [4 token tiles][DK/32][64][8]      W = T (beta e^G K)          A-fragments
-//   Qt  [4 token tiles][DK/32][64][8]      Q~ = e^G * Q                A-fragments
+//   Qt  [4 token tiles][DK/32][64][8]      Q~ = e^G * Q (KDA only)     A-fragments
 //   Kt  [DK/16 chan tiles][2][64][8]       K~^T = (e^{G_C - G} K)^T    A-fragments
 //   At  [4 token tiles][2][64][8]          attn = tril(Q K^T D)         A-fragments
 //   Uu  [DV/16 col tiles][4 token tiles][64][4]  u = T (beta V)         D-tiles
 //                                          (a 16-column slice is contiguous)
 //   gam [DK] float                         e^{G_C} per key channel (Gated: all equal)
+//   eg  [64] float                         e^{G_t} per token (Gated / DeltaNet: the
+//                                          scan reads Q itself and scales Q S by it)
 // ---------------------------------------------------------------------------
 template <typename E, int DK, int DV>
 struct WsLayout {
@@ -52,44 +56,71 @@ struct WsLayout {
     static constexpr long U_OFF = A_OFF + 4L * 2 * 64 * 8;
     static constexpr long E_END = U_OFF + 4L * (DV / 16) * 64 * 4;
     static constexpr long GAM_BYTE_OFF = (E_END * (long)sizeof(E) + 255) / 256 * 256;
-    static constexpr long BYTES = (GAM_BYTE_OFF + DK * 4L + 255) / 256 * 256;
+    static constexpr long EG_BYTE_OFF = GAM_BYTE_OFF + DK * 4L;
+    static constexpr long BYTES = (EG_BYTE_OFF + 64 * 4L + 255) / 256 * 256;
 };
 
 template <typename E> struct Vec16;
 template <> struct Vec16<bf16> { typedef bf16x8 type; };
 template <> struct Vec16<float> { typedef f32x4 type; };
 
-// Stage a [64 x D] token-major tile (rows >= L zero) into LDS as row-major
-// rows[64][ldr] and/or transposed trans[D][ldt] (token index contiguous).
-// Each thread loads four tokens of one 16-byte column vector and writes the
-// transpose as 4-token vectors.
-template <typename E, int D, bool ROWS, bool TRANS>
-__device__ __forceinline__ void stage_tile(const E* __restrict__ src, int L, E* rows, int ldr,
-                                           E* trans, int ldt, int tid) {
+// A [64 x D] token-major tile held in registers while it is in flight: each
+// thread carries four tokens of ITER 16-byte column vectors.
+template <typename E, int D>
+struct TileRegs {
     typedef typename Vec16<E>::type V16;
-    typedef typename Vec4<E>::type V4;
-    constexpr int VEC = 16 / sizeof(E);
-    constexpr int NV = D / VEC;
-    for (int idx = tid; idx < 16 * NV; idx += 256) {
-        const int tq = idx / NV, cv = idx % NV;
-        V16 x[4];
+    static constexpr int VEC = 16 / sizeof(E);
+    static constexpr int NV = D / VEC;
+    static constexpr int ITER = (16 * NV + 255) / 256;
+    V16 x[ITER][4];
+};
+
+// Load a tile (rows >= L read as zero). The row index is clamped instead of
+// the load being skipped, so every load is unconditional and the compiler can
+// wait for exactly these loads later, with other memory operations in flight.
+template <typename E, int D>
+__device__ __forceinline__ void tile_load(TileRegs<E, D>& r, const E* __restrict__ src, int L,
+                                          int tid) {
+    typedef TileRegs<E, D> R;
+    typedef typename R::V16 V16;
+#pragma unroll
+    for (int it = 0; it < R::ITER; ++it) {
+        const int idx = min(tid + 256 * it, 16 * R::NV - 1);
+        const int tq = idx / R::NV, cv = idx % R::NV;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int t = 4 * tq + u;
-            if (t < L) x[u] = *reinterpret_cast<const V16*>(src + (long)t * D + cv * VEC);
-            else x[u] = V16{};
+            const V16 val = *reinterpret_cast<const V16*>(src + (long)min(t, L - 1) * D + cv * R::VEC);
+            r.x[it][u] = (t < L) ? val : V16{};
         }
+    }
+}
+
+// Write a loaded tile into LDS as row-major rows[64][ldr] and/or transposed
+// trans[D][ldt] (token index contiguous, written as 4-token vectors).
+template <typename E, int D, bool ROWS, bool TRANS>
+__device__ __forceinline__ void tile_store(const TileRegs<E, D>& r, E* rows, int ldr, E* trans,
+                                           int ldt, int tid) {
+    typedef TileRegs<E, D> R;
+    typedef typename R::V16 V16;
+    typedef typename Vec4<E>::type V4;
+#pragma unroll
+    for (int it = 0; it < R::ITER; ++it) {
+        const int idx = tid + 256 * it;
+        if (idx >= 16 * R::NV) break;
+        const int tq = idx / R::NV, cv = idx % R::NV;
         if (ROWS) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) *reinterpret_cast<V16*>(rows + (4 * tq + u) * ldr + cv * VEC) = x[u];
+            for (int u = 0; u < 4; ++u)
+                *reinterpret_cast<V16*>(rows + (4 * tq + u) * ldr + cv * R::VEC) = r.x[it][u];
         }
         if (TRANS) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) {
+            for (int e = 0; e < R::VEC; ++e) {
                 V4 c4;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) c4[u] = x[u][e];
-                *reinterpret_cast<V4*>(trans + (cv * VEC + e) * ldt + 4 * tq) = c4;
+                for (int u = 0; u < 4; ++u) c4[u] = r.x[it][u][e];
+                *reinterpret_cast<V4*>(trans + (cv * R::VEC + e) * ldt + 4 * tq) = c4;
             }
         }
     }
@@ -158,14 +189,17 @@ struct PrepSmem {
 // ---------------------------------------------------------------------------
 // Prep kernel: one workgroup (4 wavefronts) per (head, chunk).
 // ---------------------------------------------------------------------------
+// Two workgroups share a compute unit where the LDS allows it; the register
+// budget is capped accordingly.
 template <typename E, int DK, int DV, int KIND>
-__global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q,
+__global__ __launch_bounds__(256, (PrepSmem<E, DK, DV, KIND>::TOTAL + 1024) * 2 <= 163840 ? 2 : 1)
+void chunk_prep_kernel(const E* __restrict__ q,
                                                          const E* __restrict__ k,
                                                          const E* __restrict__ v,
                                                          const E* __restrict__ beta,
                                                          const E* __restrict__ g,
                                                          char* __restrict__ ws, int T,
-                                                         int nchunks) {
+                                                         int nchunks, int nitems) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef PrepSmem<E, DK, DV, KIND> Sm;
     typedef typename Frag<E>::type F;
@@ -186,12 +220,37 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
     E* XsT = reinterpret_cast<E*>(smem + Sm::OFF_XT);
     float* Gk = reinterpret_cast<float*>(smem + Sm::OFF_GK);
 
-    const int c = blockIdx.x % nchunks;
-    const long bh = blockIdx.x / nchunks;
-    const int t0 = c * CHUNK;
-    const int L = min(CHUNK, T - t0);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int gq = lane >> 4, n = lane & 15;
+
+    // Persistent loop over (head, chunk) items: the inputs of the next item are
+    // loaded into registers while the current one is computed, and written to
+    // LDS when it is done. Prefetches are unconditional (the item index is
+    // clamped to the last item).
+    TileRegs<E, DK> rk, rq;
+    TileRegs<E, DV> rv;
+    float pb = 0.f, pg = 0.f;   // beta and log-decay of token `lane` (wave 0)
+    auto fetch = [&](int it) {
+        const int fc = it % nchunks;
+        const long ftok = (long)(it / nchunks) * T + (long)fc * CHUNK;
+        const int fL = min(CHUNK, T - fc * CHUNK);
+        tile_load<E, DK>(rk, k + ftok * DK, fL, tid);
+        tile_load<E, DK>(rq, q + ftok * DK, fL, tid);
+        tile_load<E, DV>(rv, v + ftok * DV, fL, tid);
+        if (w == 0) {
+            const long tk = ftok + min(lane, fL - 1);
+            pb = to_f32(beta[tk]);
+            if (KIND == KIND_GATED) pg = to_f32(g[tk]);
+            if (lane >= fL) pb = pg = 0.f;
+        }
+    };
+    int item = blockIdx.x;
+    fetch(item);
+    for (;;) {
+    const int c = item % nchunks;
+    const long bh = item / nchunks;
+    const int t0 = c * CHUNK;
+    const int L = min(CHUNK, T - t0);
 
     char* blk = ws + ((long)bh * nchunks + c) * Lw::BYTES;
     E* Wf = reinterpret_cast<E*>(blk) + Lw::W_OFF;
@@ -200,15 +259,15 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
     E* Af = reinterpret_cast<E*>(blk) + Lw::A_OFF;
     E* Uf = reinterpret_cast<E*>(blk) + Lw::U_OFF;
     float* gam = reinterpret_cast<float*>(blk + Lw::GAM_BYTE_OFF);
+    float* eg = reinterpret_cast<float*>(blk + Lw::EG_BYTE_OFF);
 
     const long tok0 = (long)bh * T + t0;
 
     // ---- 1. beta, log-decay and its running sum inside the chunk; stage tiles
-    if (w == 0) bs[lane] = (lane < L) ? to_f32(beta[tok0 + lane]) : 0.f;
+    if (w == 0) bs[lane] = pb;
     if (!KDA) {
         if (w == 0) {
-            const float gv = (KIND == KIND_GATED && lane < L) ? to_f32(g[tok0 + lane]) : 0.f;
-            const float G = wave_inclusive_sum(gv, lane);
+            const float G = wave_inclusive_sum(pg, lane);
             const float GC = readlane_f(G, 63);
             Gs[lane] = G;
             eG[lane] = __expf(G);
@@ -229,10 +288,11 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
             gam[ch] = __expf(acc);
         }
     }
-    stage_tile<E, DK, true, true>(k + tok0 * DK, L, Ks, LDK, KsT, LDT, tid);
-    stage_tile<E, DK, true, false>(q + tok0 * DK, L, Qs, LDK, nullptr, 0, tid);
-    stage_tile<E, DV, false, true>(v + tok0 * DV, L, nullptr, 0, VsT, LDT, tid);
-    __syncthreads();
+    tile_store<E, DK, true, true>(rk, Ks, LDK, KsT, LDT, tid);
+    tile_store<E, DK, true, false>(rq, Qs, LDK, nullptr, 0, tid);
+    tile_store<E, DV, false, true>(rv, nullptr, 0, VsT, LDT, tid);
+    lds_barrier();
+    fetch((int)min((long)item + gridDim.x, (long)nitems - 1));
 
     // ---- 2. attn -> A-fragments, Q~ -> A-fragments; raw K K^T kept in registers
     // Wave w owns token tile w: rows i in [16w, 16w+16) of A and of attn.
@@ -281,23 +341,23 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             reinterpret_cast<F*>(Af)[(w * 2 + kb) * 64 + lane] = frag_from_tiles<E>(at[2 * kb], at[2 * kb + 1]);
-        // Q~ = e^G * Q, A-fragments of token tile w (one factor per token, or
-        // per token and key channel for KDA). Stored in fragment order so the
-        // scan reads it with one 16-byte load per lane per fragment.
+        // KDA: Q~ = e^G * Q (one factor per token and key channel), A-fragments
+        // of token tile w in fragment order. Otherwise the scan reads Q itself
+        // and applies the per-token factor e^G (stored per token) to Q S.
+        if (!KDA) {
+            if (w == 0) eg[lane] = eG[lane];
+        } else {
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-            F f;
-            if (!KDA) {
-                f = frag_rows_scaled<E>(Qs, LDK, 16 * w, 32 * kb, lane, eG[16 * w + n], nullptr);
-            } else {
+            for (int kb = 0; kb < DK / 32; ++kb) {
+                F f;
                 const int row = 16 * w + n;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int cc = 32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
                     f[j] = from_f32<E>(to_f32(Qs[row * LDK + cc]) * __expf(Gk[row * LDG + cc]));
                 }
+                reinterpret_cast<F*>(Qf)[(w * (DK / 32) + kb) * 64 + lane] = f;
             }
-            reinterpret_cast<F*>(Qf)[(w * (DK / 32) + kb) * 64 + lane] = f;
         }
     }
     if (!KDA) {
@@ -308,7 +368,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
                 frag_rows_scaled<E>(KsT, LDT, 16 * mt, 32 * kb, lane, 1.f, eGC);
         }
     }
-    __syncthreads();  // K and Q rows are dead from here on
+    lds_barrier();  // K and Q rows are dead from here on
 
     // ---- 2b. system matrix A = strict_tril(beta_i K K^T D) into region Y -----
 #pragma unroll
@@ -330,7 +390,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
             KsT[ch * LDT + t] = from_f32<E>(kv * __expf(GC - Gt));
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 3. UT transform T = (I + A)^-1, blocked over 16x16 tiles ------------
     // 3a: wave w inverts its diagonal tile by forward substitution, lane = column:
@@ -359,7 +419,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
             reinterpret_cast<F*>(Kf)[p * 64 + lane] = frag_rows<E>(KsT, LDT, 16 * mt, 32 * kb, lane);
         }
     }
-    __syncthreads();
+    lds_barrier();
     // 3b: wave w computes column tile w of T downwards on the matrix cores:
     //     T_Iw = -T_II * sum_{w <= K < I} A_IK T_Kw   (16x16 tiles, fp32)
     f32x4 tcol[4];
@@ -384,7 +444,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
             tcol[I] = -t;
         }
     }
-    __syncthreads();  // A and the diagonal inverses are dead from here on
+    lds_barrier();  // A and the diagonal inverses are dead from here on
     // T' = T diag(beta e^G) into region X, T'' = T diag(beta) into region Y
     {
         const int j = 16 * w + n;
@@ -399,7 +459,7 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
                 Tpp[i * LDT + j] = from_f32<E>(tcol[I][e] * sb);
             }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- 4. W^T = X^T T'^T, computed transposed so it lands as A-fragments of W
     //         (Gated / DeltaNet: X = K, T' = T diag(beta e^G); KDA: X = e^G K, T' = T diag(beta))
@@ -433,6 +493,331 @@ __global__ __launch_bounds__(256) void chunk_prep_kernel(const E* __restrict__ q
         for (int e = 0; e < 4; ++e) u4[e] = from_f32<E>(acc[e]);
         reinterpret_cast<V4*>(Uf)[(nt * 4 + w) * 64 + lane] = u4;
     }
+
+    if ((long)item + gridDim.x >= nitems) break;
+    item += gridDim.x;
+    lds_barrier();   // every wave is done with this item's LDS data
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Prep kernel, one wavefront per (head, chunk): Gated DeltaNet and DeltaNet.
+// ---------------------------------------------------------------------------
+// Same results and workspace layout as chunk_prep_kernel, organised for a
+// single wavefront so that no workgroup barrier is needed (about 18 KB of LDS
+// per chunk; one wavefront per SIMD, with up to 512 registers):
+//  * K, Q and V fragments with rows = tokens come straight from global memory.
+//  * With the token index as the contraction index (B-fragments of
+//    X = beta e^G K and of beta V, A-fragments of K~^T = (e^{G_C - G} K)^T),
+//    K and V come from a product with an identity fragment on the matrix
+//    cores: D = K I holds K as D-tiles (exactly), and two D-tiles stacked over
+//    tokens are such a fragment. The per-token scale is applied on the way.
+//  * W = (T diag(beta e^G)) K and u = (T diag(beta)) V, with each scaled T
+//    rounded once to the operand type.
+
+// B-fragment of the identity for the 16 columns 16h .. 16h+15 of a 32-wide
+// contraction block: lane (g, n) supplies I[pi(g, j)][16h + n].
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::type ident_frag(int h, int lane) {
+    const int g = lane >> 4, n = lane & 15;
+    typename Frag<E>::type f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int kk = j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
+        f[j] = from_f32<E>(kk == 16 * h + n ? 1.f : 0.f);
+    }
+    return f;
+}
+
+// frag_rows on a [rows][ld] token tile in global memory. Rows >= L (past the
+// end of the sequence, only in its last chunk) repeat row L - 1: the row index
+// is clamped so that every load is unconditional and in bounds. Such rows
+// never reach a stored result: their beta and log-decay are zero, so they add
+// nothing to A, T, W, u or the state, and the outputs of those rows are not
+// written.
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::type frag_rows_g(const E* __restrict__ M, int ld, int row0,
+                                                              int k0, int lane, int L) {
+    typedef typename Vec4<E>::type V4;
+    const int g = lane >> 4, r = lane & 15;
+    const int row = row0 + r;
+    const E* p = M + (long)min(row, L - 1) * ld + k0 + 4 * g;
+    const V4 a = *reinterpret_cast<const V4*>(p);
+    const V4 b = *reinterpret_cast<const V4*>(p + 16);
+    typename Frag<E>::type f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[i] = a[i];
+        f[4 + i] = b[i];
+    }
+    return f;
+}
+
+// Fragment from two D-tiles (rows r0 + 4gq + e and r0 + 16 + 4gq + e) with
+// each row scaled by s[row] (an LDS table) before rounding.
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::type frag_from_tiles_rs(const f32x4& lo, const f32x4& hi,
+                                                                     const float* s, int r0, int lane) {
+    const int gq = lane >> 4;
+    const f32x4 slo = *reinterpret_cast<const f32x4*>(s + r0 + 4 * gq);
+    const f32x4 shi = *reinterpret_cast<const f32x4*>(s + r0 + 16 + 4 * gq);
+    typename Frag<E>::type f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f[e] = from_f32<E>(lo[e] * slo[e]);
+        f[4 + e] = from_f32<E>(hi[e] * shi[e]);
+    }
+    return f;
+}
+
+// Orders this wavefront's LDS accesses around a switch of who reads what
+// (LDS operations of one wavefront complete in order; this also waits for
+// them, and keeps the compiler from moving LDS accesses across).
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+template <typename E, int DK, int DV>
+struct Prep1Smem {
+    static constexpr int LDF = 68;                     // fp32 64x64: A, then T's diagonal blocks
+    static constexpr int LDT = 64 + 16 / sizeof(E);    // T diag(.) in the operand type (two)
+    static constexpr long BYTES = 64L * LDF * 4 > 2 * 64L * LDT * (long)sizeof(E)
+                                      ? 64L * LDF * 4
+                                      : 2 * 64L * LDT * (long)sizeof(E);
+};
+
+template <typename E, int DK, int DV, int KIND>
+__global__ __launch_bounds__(64, 1) void chunk_prep1_kernel(const E* __restrict__ q,
+                                                            const E* __restrict__ k,
+                                                            const E* __restrict__ v,
+                                                            const E* __restrict__ beta,
+                                                            const E* __restrict__ g,
+                                                            char* __restrict__ ws, int T,
+                                                            int nchunks) {
+    typedef WsLayout<E, DK, DV> Lw;
+    typedef Prep1Smem<E, DK, DV> Sm;
+    typedef typename Frag<E>::type F;
+    typedef typename Vec4<E>::type V4;
+    constexpr int KB = DK / 32, CT = DK / 16, VB = DV / 32, VT = DV / 16;
+    constexpr int LDF = Sm::LDF, LDT = Sm::LDT;
+
+    __shared__ __align__(16) char smem[Sm::BYTES];
+    // per token: running log-decay, beta e^G, e^{G_C - G}, beta
+    __shared__ __align__(16) float Gs[64], sX[64], sK[64], bs[64];
+    float* As = reinterpret_cast<float*>(smem);   // A, then T's diagonal blocks in place
+    E* Tw = reinterpret_cast<E*>(smem);           // T diag(beta e^G), once the inverse is done
+    E* Tu = Tw + 64 * LDT;                        // T diag(beta)
+
+    const int lane = threadIdx.x, gq = lane >> 4, n = lane & 15;
+    const long item = blockIdx.x;
+    const int c = (int)(item % nchunks);
+    const long bh = item / nchunks;
+    const int t0 = c * CHUNK;
+    const int L = min(CHUNK, T - t0);
+    const long tok0 = bh * T + t0;
+
+    char* blk = ws + item * Lw::BYTES;
+    F* Wf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::W_OFF);
+    F* Kf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::K_OFF);
+    F* Af = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::A_OFF);
+    V4* Uf = reinterpret_cast<V4*>(reinterpret_cast<E*>(blk) + Lw::U_OFF);
+    float* gam = reinterpret_cast<float*>(blk + Lw::GAM_BYTE_OFF);
+    float* eg = reinterpret_cast<float*>(blk + Lw::EG_BYTE_OFF);
+
+    // ---- 1. beta and log-decay of token `lane`, running sum, per-token tables
+    {
+        const long tk = tok0 + min(lane, L - 1);
+        float bv = to_f32(beta[tk]);
+        float gv = KIND == KIND_GATED ? to_f32(g[tk]) : 0.f;
+        if (lane >= L) bv = gv = 0.f;
+        const float G = wave_inclusive_sum(gv, lane);
+        const float GC = readlane_f(G, 63);
+        const float e = __expf(G);
+        Gs[lane] = G;
+        eg[lane] = e;
+        sX[lane] = bv * e;
+        sK[lane] = __expf(GC - G);
+        bs[lane] = bv;
+        // the chunk decay, replicated per key channel (the scan reads it like KDA's)
+        for (int ch = lane; ch < DK; ch += 64) gam[ch] = __expf(GC);
+    }
+
+    // ---- 2. K and Q fragments (rows = tokens, contraction = key channels),
+    //         requested together so that one memory latency covers them
+    F kf[4][KB], qa[4][KB];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) kf[tt][kb] = frag_rows_g<E>(k + tok0 * DK, DK, 16 * tt, 32 * kb, lane, L);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) qa[tt][kb] = frag_rows_g<E>(q + tok0 * DK, DK, 16 * tt, 32 * kb, lane, L);
+    lds_fence();   // the per-token tables are written
+
+    // attn = tril(Q K^T exp(G_i - G_j)) as A-fragments: attn^T tiles (rows j)
+    // stacked over two j tiles
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const F* qf = qa[it];
+        f32x4 at[4];
+#pragma unroll
+        for (int jt = 0; jt < 4; ++jt) {
+            at[jt] = zero4();
+            if (jt <= it) {
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) at[jt] = mma(kf[jt][kb], qf[kb], at[jt]);
+                const int i = 16 * it + n;
+                const float Gi = Gs[i];
+                const f32x4 Gj = *reinterpret_cast<const f32x4*>(Gs + 16 * jt + 4 * gq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * jt + 4 * gq + e;
+                    at[jt][e] = (i >= j) ? __expf(Gi - Gj[e]) * at[jt][e] : 0.f;
+                }
+            }
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) Af[(it * 2 + kb) * 64 + lane] = frag_from_tiles<E>(at[2 * kb], at[2 * kb + 1]);
+    }
+
+    // system matrix A = strict_tril(beta_i K K^T exp(G_i - G_j)) into LDS (fp32)
+#pragma unroll
+    for (int it = 0; it < 4; ++it)
+#pragma unroll
+        for (int jt = 0; jt <= it; ++jt) {
+            f32x4 s = zero4();
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) s = mma(kf[it][kb], kf[jt][kb], s);
+            const int j = 16 * jt + n;
+            const float Gj = Gs[j];
+            const f32x4 Gi = *reinterpret_cast<const f32x4*>(Gs + 16 * it + 4 * gq);
+            const f32x4 bi = *reinterpret_cast<const f32x4*>(bs + 16 * it + 4 * gq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * it + 4 * gq + e;
+                As[i * LDF + j] = (i > j) ? bi[e] * __expf(Gi[e] - Gj) * s[e] : 0.f;
+            }
+        }
+
+    // K with tokens as the contraction index (D = K I): K as B-fragments (kept
+    // for W = T diag(beta e^G) K), K~^T = (e^{G_C - G} K)^T as A-fragments (stored)
+    const F id0 = ident_frag<E>(0, lane), id1 = ident_frag<E>(1, lane);
+    F xf[CT][2];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        f32x4 d[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) d[tt] = mma(kf[tt][ct >> 1], (ct & 1) ? id1 : id0, zero4());
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            xf[ct][kt] = frag_from_tiles<E>(d[2 * kt], d[2 * kt + 1]);
+            Kf[(ct * 2 + kt) * 64 + lane] = frag_from_tiles_rs<E>(d[2 * kt], d[2 * kt + 1], sK, 32 * kt, lane);
+        }
+    }
+    // V fragments, in flight while T is computed
+    F vf[4][VB];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int kb = 0; kb < VB; ++kb) vf[tt][kb] = frag_rows_g<E>(v + tok0 * DV, DV, 16 * tt, 32 * kb, lane, L);
+    lds_fence();   // A is written
+
+    // ---- 3. UT transform T = (I + A)^-1, blocked over 16x16 tiles ------------
+    // 3a: diagonal blocks by forward substitution, lane (block gq, column n):
+    //     T_jj = 1, T_ij = -sum_{j <= m < i} A_im T_mj; written over the block of A
+    {
+        const int b0 = 16 * gq, j = n;
+        float tc[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+            float acc = 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) acc += As[(b0 + i) * LDF + b0 + m] * tc[m];
+            if (i > j) tc[i] = -acc;
+        }
+        lds_fence();
+#pragma unroll
+        for (int i = 0; i < 16; ++i) As[(b0 + i) * LDF + b0 + j] = tc[i];
+    }
+    lds_fence();
+    // 3b: T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ on the matrix cores (fp32),
+    //     the column tiles J interleaved
+    f32x4 tm[4][4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) tm[J][J][e] = As[(16 * J + 4 * gq + e) * LDF + 16 * J + n];
+#pragma unroll
+    for (int I = 1; I < 4; ++I) {
+#pragma unroll
+        for (int J = 0; J < I; ++J) {
+            f32x4 R = zero4();
+#pragma unroll
+            for (int K = J; K < I; ++K) R = mma16_lds_reg(As + 16 * I * LDF + 16 * K, LDF, lane, tm[K][J], R);
+            tm[I][J] = -mma16_lds_reg(As + 16 * I * LDF + 16 * I, LDF, lane, R, zero4());
+        }
+    }
+    lds_fence();   // every read of A and of the diagonal blocks has returned
+    // T diag(beta e^G) and T diag(beta) (lower triangular) in the operand type,
+    // over the fp32 region; lane (gq, n) holds column 16J + n of tile (I, J)
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        const float cx = sX[16 * J + n], cb = bs[16 * J + n];
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int o = (16 * I + 4 * gq + e) * LDT + 16 * J + n;
+                Tw[o] = from_f32<E>(I >= J ? tm[I][J][e] * cx : 0.f);
+                Tu[o] = from_f32<E>(I >= J ? tm[I][J][e] * cb : 0.f);
+            }
+    }
+    lds_fence();
+
+    // ---- 4. W = T X: W^T tiles (rows = key channels) for each token tile,
+    //         stacked over channel tiles = A-fragments of W
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        F tf[2];   // T diag(beta e^G), rows = tokens of tile tt, contraction = tokens
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) tf[kt] = frag_rows<E>(Tw, LDT, 16 * tt, 32 * kt, lane);
+        f32x4 wt[CT];
+#pragma unroll
+        for (int mt = 0; mt < CT; ++mt) {
+            wt[mt] = zero4();
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) wt[mt] = mma(xf[mt][kt], tf[kt], wt[mt]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) Wf[(tt * KB + kb) * 64 + lane] = frag_from_tiles<E>(wt[2 * kb], wt[2 * kb + 1]);
+    }
+
+    // ---- 5. u = T diag(beta) V as D-tiles (rows = tokens), value tile by value tile
+    F tu[4][2];   // T diag(beta) A-fragments
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) tu[tt][kt] = frag_rows<E>(Tu, LDT, 16 * tt, 32 * kt, lane);
+#pragma unroll
+    for (int nt = 0; nt < VT; ++nt) {
+        f32x4 d[4];
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) d[tt] = mma(vf[tt][nt >> 1], (nt & 1) ? id1 : id0, zero4());
+        F vb[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) vb[kt] = frag_from_tiles<E>(d[2 * kt], d[2 * kt + 1]);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            f32x4 acc = zero4();
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) acc = mma(tu[tt][kt], vb[kt], acc);
+            V4 u4;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) u4[e] = from_f32<E>(acc[e]);
+            Uf[(nt * 4 + tt) * 64 + lane] = u4;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -445,18 +830,33 @@ struct ScanOps {
     static constexpr int KB = DK / 32;   // contraction blocks over key channels
     static constexpr int MTW = DK / 64;  // key-channel tiles per wave
     static constexpr int NT = BV / 16;   // value tiles (16 columns) per workgroup
+    typedef typename Vec16<E>::type V16;
+    // Gated / DeltaNet: the wave's 16 rows of Q as loaded (row-major, 16 bytes
+    // per lane per load); KDA: Q~ as A-fragments from the workspace
+    static constexpr int QR = 16 * DK * (int)sizeof(E) / (64 * 16);
     F w[KB], q[KB], a[2], k[MTW][2];
+    V16 qr[QR];
     V4 u[NT];
-    f32x4 gam[MTW];
+    f32x4 gam[MTW], eg;
+};
+
+// Where the operands of one chunk are: its workspace block and its rows of Q,
+// of which the first L are in the sequence.
+template <typename E>
+struct ChunkSrc {
+    const char* blk;
+    const E* q;
+    int L;
 };
 
 // Operands of one chunk for wave w of value tile vt, in four parts (one
 // coalesced load per lane per fragment). The parts are issued at different
 // points of the previous-but-one chunk's step, so the wave never stalls on a
 // burst of loads waiting for the memory pipeline to accept them.
-template <int PART, typename E, int DK, int DV, int BV>
-__device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV>& x, const char* blk, int vt,
-                                               int w, int lane) {
+template <int PART, int KIND, typename E, int DK, int DV, int BV>
+__device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV>& x, const ChunkSrc<E>& src,
+                                               int vt, int w, int lane) {
+    const char* blk = src.blk;
     typedef WsLayout<E, DK, DV> Lw;
     typedef ScanOps<E, DK, DV, BV> O;
     typedef typename O::F F;
@@ -467,9 +867,21 @@ __device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV>& x, const 
 #pragma unroll
         for (int kb = 0; kb < O::KB; ++kb) x.w[kb] = Wf[(w * O::KB + kb) * 64 + lane];
     } else if (PART == 1) {
-        const F* Qf = reinterpret_cast<const F*>(base + Lw::Q_OFF);
+        if (KIND == KIND_KDA) {
+            const F* Qf = reinterpret_cast<const F*>(base + Lw::Q_OFF);
 #pragma unroll
-        for (int kb = 0; kb < O::KB; ++kb) x.q[kb] = Qf[(w * O::KB + kb) * 64 + lane];
+            for (int kb = 0; kb < O::KB; ++kb) x.q[kb] = Qf[(w * O::KB + kb) * 64 + lane];
+        } else {
+            // contiguous 16-byte loads of the wave's rows; rows past the end of
+            // the sequence repeat its last row (their outputs are not written)
+            constexpr int VEC = 16 / sizeof(E);
+#pragma unroll
+            for (int i = 0; i < O::QR; ++i) {
+                const int off = (i * 64 + lane) * VEC;
+                const int row = min(16 * w + off / DK, src.L - 1);
+                x.qr[i] = *reinterpret_cast<const typename O::V16*>(src.q + (long)row * DK + off % DK);
+            }
+        }
     } else if (PART == 2) {
         const F* Kf = reinterpret_cast<const F*>(base + Lw::K_OFF);
         const F* Af = reinterpret_cast<const F*>(base + Lw::A_OFF);
@@ -488,16 +900,19 @@ __device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV>& x, const 
 #pragma unroll
         for (int m = 0; m < O::MTW; ++m)
             x.gam[m] = *reinterpret_cast<const f32x4*>(gam + 16 * (w * O::MTW + m) + 4 * gq);
+        if (KIND != KIND_KDA)
+            x.eg = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(blk + Lw::EG_BYTE_OFF) +
+                                                   16 * w + 4 * gq);
     }
 }
 
-template <typename E, int DK, int DV, int BV>
-__device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV>& x, const char* blk, int vt,
+template <int KIND, typename E, int DK, int DV, int BV>
+__device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV>& x, const ChunkSrc<E>& src, int vt,
                                           int w, int lane) {
-    scan_load_part<0>(x, blk, vt, w, lane);
-    scan_load_part<1>(x, blk, vt, w, lane);
-    scan_load_part<2>(x, blk, vt, w, lane);
-    scan_load_part<3>(x, blk, vt, w, lane);
+    scan_load_part<0, KIND>(x, src, vt, w, lane);
+    scan_load_part<1, KIND>(x, src, vt, w, lane);
+    scan_load_part<2, KIND>(x, src, vt, w, lane);
+    scan_load_part<3, KIND>(x, src, vt, w, lane);
 }
 
 // Keeps the compiler from moving memory operations across this point (the
@@ -510,10 +925,10 @@ __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 // parts along the way; the output tile leaves through LDS as 16-byte rows.
 template <typename E, int DK, int DV, int KIND, int BV>
 __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
-                                          ScanOps<E, DK, DV, BV>& nxt, const char* nblk,
+                                          ScanOps<E, DK, DV, BV>& nxt, const ChunkSrc<E>& nblk,
                                           f32x4 (&S)[DK / 64][BV / 16],
                                           typename Frag<E>::type (*Sx)[BV / 16][64],
-                                          typename Frag<E>::type (*Ux)[BV / 16][64], E* ob,
+                                          typename Frag<E>::type (*Ux)[BV / 16][64], E* ob, E* qs,
                                           E* __restrict__ o, long bh, int T, int t0, int vt,
                                           int w, int lane) {
     typedef ScanOps<E, DK, DV, BV> Ops;
@@ -523,6 +938,18 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
     constexpr int NT = Ops::NT, KB = Ops::KB, MTW = Ops::MTW;
     constexpr int LDO = BV + 16 / sizeof(E);   // output staging row (padded)
     const int gq = lane >> 4, n = lane & 15;
+
+    // Gated / DeltaNet: the wave's Q rows go through its own LDS slice
+    // (row-major, padded) to become A-fragments
+    constexpr int LDQ = DK + 16 / sizeof(E);
+    if (KIND != KIND_KDA) {
+        constexpr int VEC = 16 / sizeof(E);
+#pragma unroll
+        for (int i = 0; i < Ops::QR; ++i) {
+            const int off = (i * 64 + lane) * VEC;
+            *reinterpret_cast<V16*>(qs + (off / DK) * LDQ + off % DK) = cur.qr[i];
+        }
+    }
 
     // state -> B-fragments of the contraction over key channels; key-channel
     // block kb covers the tiles 2kb, 2kb+1, i.e. wave kb (d = 128) or the waves
@@ -539,9 +966,12 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
         }
     }
     sched_fence();
-    scan_load_part<0>(nxt, nblk, vt, w, lane);
+    scan_load_part<0, KIND>(nxt, nblk, vt, w, lane);
     lds_barrier();
 
+    F qf[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) qf[kb] = KIND == KIND_KDA ? cur.q[kb] : frag_rows<E>(qs, LDQ, 0, 32 * kb, lane);
     f32x4 U[NT], O[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -551,11 +981,13 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
         for (int kb = 0; kb < KB; ++kb) {
             const F sb = Sx[kb][nt][lane];
             U[nt] = mma(cur.w[kb], sb, U[nt]);
-            O[nt] = mma(cur.q[kb], sb, O[nt]);
+            O[nt] = mma(qf[kb], sb, O[nt]);
         }
+        // Gated / DeltaNet: (e^G Q) S = e^G (Q S), per token row
+        if (KIND != KIND_KDA) O[nt] *= cur.eg;
     }
     sched_fence();
-    scan_load_part<1>(nxt, nblk, vt, w, lane);
+    scan_load_part<1, KIND>(nxt, nblk, vt, w, lane);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         V4 h;
@@ -572,7 +1004,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) S[m][nt] *= cur.gam[m];
     sched_fence();
-    scan_load_part<2>(nxt, nblk, vt, w, lane);
+    scan_load_part<2, KIND>(nxt, nblk, vt, w, lane);
     lds_barrier();
 
 #pragma unroll
@@ -589,7 +1021,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
         for (int e = 0; e < 4; ++e) ob[(4 * gq + e) * LDO + 16 * nt + n] = from_f32<E>(O[nt][e]);
     }
     sched_fence();
-    scan_load_part<3>(nxt, nblk, vt, w, lane);
+    scan_load_part<3, KIND>(nxt, nblk, vt, w, lane);
     // 16 rows x BV columns: BV*sizeof(E) bytes per row, 16 bytes per lane
     constexpr int PER_ROW = BV * sizeof(E) / 16;
     constexpr int VEC = 16 / sizeof(E);
@@ -604,6 +1036,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
 
 template <typename E, int DK, int DV, int KIND, int BV>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict__ ws,
+                                                         const E* __restrict__ q,
                                                          const float* __restrict__ S0,
                                                          E* __restrict__ o,
                                                          float* __restrict__ S_final, int T,
@@ -628,6 +1061,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
     __shared__ F Ux[2][NT][64];    // U as B-fragments (contraction over tokens)
     constexpr int LDO = BV + 16 / sizeof(E);
     __shared__ __align__(16) E Ob[4][16 * LDO];   // per-wave output staging
+    constexpr int LDQ = DK + 16 / sizeof(E);
+    __shared__ __align__(16) E Qs[KIND == KIND_KDA ? 1 : 4][16 * LDQ];   // per-wave Q rows
 
     // fp32 state tile: rows 16*(w*MTW + m) + 4gq + e, columns vt*BV + 16nt + n
     f32x4 S[MTW][NT];
@@ -655,17 +1090,22 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
     // instead of draining every load in flight.
     const char* wsh = ws + (long)bh * nchunks * Lw::BYTES;
     const int last = nchunks - 1;
-    auto blk = [&](int cc) { return wsh + (long)min(cc, last) * Lw::BYTES; };
+    auto blk = [&](int cc) {
+        const int c2 = min(cc, last);
+        return ChunkSrc<E>{wsh + (long)c2 * Lw::BYTES, q + ((long)bh * T + (long)c2 * CHUNK) * DK,
+                           min(CHUNK, T - c2 * CHUNK)};
+    };
     Ops o0, o1, o2;
-    scan_load(o0, blk(0), vt, w, lane);
-    scan_load(o1, blk(1), vt, w, lane);
+    scan_load<KIND>(o0, blk(0), vt, w, lane);
+    scan_load<KIND>(o1, blk(1), vt, w, lane);
     E* ob = Ob[w];
+    E* qs = Qs[KIND == KIND_KDA ? 0 : w];
     for (int c = 0; c < nchunks; c += 3) {
-        scan_step<E, DK, DV, KIND, BV>(o0, o2, blk(c + 2), S, Sx, Ux, ob, o, bh, T, c * CHUNK, vt, w, lane);
+        scan_step<E, DK, DV, KIND, BV>(o0, o2, blk(c + 2), S, Sx, Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane);
         if (c + 1 >= nchunks) break;
-        scan_step<E, DK, DV, KIND, BV>(o1, o0, blk(c + 3), S, Sx, Ux, ob, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
+        scan_step<E, DK, DV, KIND, BV>(o1, o0, blk(c + 3), S, Sx, Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
         if (c + 2 >= nchunks) break;
-        scan_step<E, DK, DV, KIND, BV>(o2, o1, blk(c + 4), S, Sx, Ux, ob, o, bh, T, (c + 2) * CHUNK, vt, w, lane);
+        scan_step<E, DK, DV, KIND, BV>(o2, o1, blk(c + 4), S, Sx, Ux, ob, qs, o, bh, T, (c + 2) * CHUNK, vt, w, lane);
     }
 
     if (S_final) {
@@ -684,6 +1124,19 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+// Compute units of the current device (queried once per device).
+static int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 template <typename E, int D>
 static size_t ws_bytes_t(long long BH, long long nchunks) {
     return (size_t)(BH * nchunks * WsLayout<E, D, D>::BYTES);
@@ -700,15 +1153,28 @@ template <typename E, int D, int KIND>
 static hipError_t prep_t(const void* q, const void* k, const void* v, const void* beta,
                          const void* g, void* ws, int BH, int T, hipStream_t st) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
-    hipLaunchKernelGGL((chunk_prep_kernel<E, D, D, KIND>), dim3((unsigned)(nchunks * (long)BH)),
-                       dim3(256), 0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta,
-                       (const E*)g, (char*)ws, T, nchunks);
+    const int nitems = nchunks * BH;
+    // one wavefront per chunk where its fragments fit in 256 registers
+    if constexpr (KIND != KIND_KDA && (sizeof(E) == 2 || D == 64)) {
+        hipLaunchKernelGGL((chunk_prep1_kernel<E, D, D, KIND>), dim3((unsigned)nitems), dim3(64), 0, st,
+                           (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
+                           (char*)ws, T, nchunks);
+        return hipGetLastError();
+    }
+    // persistent workgroups: as many as fit on the device at once (LDS bound)
+    constexpr long lds = PrepSmem<E, D, D, KIND>::TOTAL + 1024;
+    constexpr int per_cu = (int)(163840 / lds) < 1 ? 1 : (int)(163840 / lds);
+    const long resident = (long)per_cu * device_cu_count();
+    const int grid = (int)(nitems < resident ? nitems : resident);
+    hipLaunchKernelGGL((chunk_prep_kernel<E, D, D, KIND>), dim3((unsigned)grid), dim3(256), 0, st,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
+                       (char*)ws, T, nchunks, nitems);
     return hipGetLastError();
 }
 
 template <typename E, int D, int KIND>
-static hipError_t scan_t(const float* S0, void* o, float* S_final, const void* ws, int BH, int T,
-                         hipStream_t st) {
+static hipError_t scan_t(const void* q, const float* S0, void* o, float* S_final, const void* ws,
+                         int BH, int T, hipStream_t st) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const long groups = ((long)BH + 7) / 8;
     // 32-column value tiles unless that leaves most of the 256 CUs idle
@@ -716,12 +1182,12 @@ static hipError_t scan_t(const float* S0, void* o, float* S_final, const void* w
         constexpr int BV = 32;
         const long nblk = groups * 8 * (D / BV);
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
-                           st, (const char*)ws, S0, (E*)o, S_final, T, nchunks, BH);
+                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH);
     } else {
         constexpr int BV = 16;
         const long nblk = groups * 8 * (D / BV);
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
-                           st, (const char*)ws, S0, (E*)o, S_final, T, nchunks, BH);
+                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH);
     }
     return hipGetLastError();
 }
@@ -738,11 +1204,11 @@ static hipError_t prep_kind(int kind, const void* q, const void* k, const void* 
 }
 
 template <typename E, int D>
-static hipError_t scan_kind(int kind, const float* S0, void* o, float* S_final, const void* ws,
-                            int BH, int T, hipStream_t st) {
+static hipError_t scan_kind(int kind, const void* q, const float* S0, void* o, float* S_final,
+                            const void* ws, int BH, int T, hipStream_t st) {
     // DeltaNet and Gated DeltaNet share the scan (a unit decay is stored for DeltaNet)
-    if (kind == KIND_KDA) return scan_t<E, D, KIND_KDA>(S0, o, S_final, ws, BH, T, st);
-    return scan_t<E, D, KIND_GATED>(S0, o, S_final, ws, BH, T, st);
+    if (kind == KIND_KDA) return scan_t<E, D, KIND_KDA>(q, S0, o, S_final, ws, BH, T, st);
+    return scan_t<E, D, KIND_GATED>(q, S0, o, S_final, ws, BH, T, st);
 }
 
 hipError_t launch_chunk_prep(int kind, int dtype, const void* q, const void* k, const void* v,
@@ -756,14 +1222,15 @@ hipError_t launch_chunk_prep(int kind, int dtype, const void* q, const void* k, 
                      : prep_kind<float, 64>(kind, q, k, v, beta, g, ws, BH, T, st);
 }
 
-hipError_t launch_chunk_scan(int kind, int dtype, const float* S0, void* o, float* S_final,
-                             const void* ws, int BH, int T, int dk, int dv, hipStream_t st) {
+hipError_t launch_chunk_scan(int kind, int dtype, const void* q, const float* S0, void* o,
+                             float* S_final, const void* ws, int BH, int T, int dk, int dv,
+                             hipStream_t st) {
     (void)dv;
     if (dtype == DT_BF16)
-        return dk == 128 ? scan_kind<bf16, 128>(kind, S0, o, S_final, ws, BH, T, st)
-                         : scan_kind<bf16, 64>(kind, S0, o, S_final, ws, BH, T, st);
-    return dk == 128 ? scan_kind<float, 128>(kind, S0, o, S_final, ws, BH, T, st)
-                     : scan_kind<float, 64>(kind, S0, o, S_final, ws, BH, T, st);
+        return dk == 128 ? scan_kind<bf16, 128>(kind, q, S0, o, S_final, ws, BH, T, st)
+                         : scan_kind<bf16, 64>(kind, q, S0, o, S_final, ws, BH, T, st);
+    return dk == 128 ? scan_kind<float, 128>(kind, q, S0, o, S_final, ws, BH, T, st)
+                     : scan_kind<float, 64>(kind, q, S0, o, S_final, ws, BH, T, st);
 }
 
 }  // namespace dn

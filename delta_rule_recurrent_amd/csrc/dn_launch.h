@@ -28,8 +28,8 @@ hipError_t launch_chunk_prep(int kind, int dtype, const void* q, const void* k, 
                              int dk, int dv, hipStream_t stream);
 
 // Chunkwise prefill, phase 2: sequential scan over the chunks of every head.
-hipError_t launch_chunk_scan(int kind, int dtype, const float* S0, void* o, float* S_final,
-                             const void* workspace, int BH, int T, int dk, int dv,
+hipError_t launch_chunk_scan(int kind, int dtype, const void* q, const float* S0, void* o,
+                             float* S_final, const void* workspace, int BH, int T, int dk, int dv,
                              hipStream_t stream);
 
 // Workspace bytes of the chunkwise prefill (per call).

@@ -113,23 +113,25 @@ int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* be
  *
  * dn_chunk_prep: every 64-token chunk of every head in parallel. Computes the
  *   running log-decay G, the UT transform T = (I + strict_tril(beta K K^T D))^-1,
- *   W = T (beta e^G K), u = T (beta V), the causal decayed Q K^T and the
- *   decay-scaled Q and K of each chunk (page "28. Linear attention and Gated
- *   DeltaNet", section "The chunked form", the triangular system and the
- *   attention matrix), and writes them to `workspace`. Arguments as in
- *   dn_chunk_fwd; with kda = 0, g == NULL selects DeltaNet.
+ *   W = T (beta e^G K), u = T (beta V), the causal decayed Q K^T, the
+ *   decay-scaled K and the decay factors of each chunk (page "28. Linear
+ *   attention and Gated DeltaNet", section "The chunked form", the triangular
+ *   system and the attention matrix), and writes them to `workspace`; for KDA
+ *   also the decay-scaled Q. Arguments as in dn_chunk_fwd; with kda = 0,
+ *   g == NULL selects DeltaNet.
  * dn_chunk_scan: the sequential inter-chunk recurrence of every head over the
  *   workspace filled by dn_chunk_prep with the same sizes, dtype and kda: per
  *   chunk U = u - W S, O = (e^G * Q) S + attn U, S = e^{G_C} S + K~^T U (same
- *   section, the chunk loop). Writes o and S_final exactly as dn_chunk_fwd;
- *   S0/S_final may alias. The workspace is read only.
+ *   section, the chunk loop). q is the tensor given to dn_chunk_prep, read
+ *   again here (kda = 0). Writes o and S_final exactly as dn_chunk_fwd;
+ *   S0/S_final may alias. q and the workspace are read only.
  */
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,
                   const void* g, int B, int H, int T, int dk, int dv, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream);
 
-int dn_chunk_scan(int kda, const float* S0, void* o, float* S_final, int B, int H, int T,
-                  int dk, int dv, int dtype, const void* workspace, size_t workspace_bytes,
+int dn_chunk_scan(int kda, const void* q, const float* S0, void* o, float* S_final, int B, int H,
+                  int T, int dk, int dv, int dtype, const void* workspace, size_t workspace_bytes,
                   void* stream);
 
 /*

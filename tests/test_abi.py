@@ -154,11 +154,12 @@ def _prep(**kw):
 
 
 def _scan(**kw):
-    a = dict(kda=0, S0=P, o=P, S_final=P, B=1, H=1, T=64, dk=64, dv=64, dtype=1, ws=WS,
+    a = dict(kda=0, q=P, S0=P, o=P, S_final=P, B=1, H=1, T=64, dk=64, dv=64, dtype=1, ws=WS,
              wsb=1 << 30, stream=None)
     a.update(kw)
-    return _lib.lib().dn_chunk_scan(*[a[n] for n in ("kda", "S0", "o", "S_final", "B", "H", "T",
-                                                     "dk", "dv", "dtype", "ws", "wsb", "stream")])
+    return _lib.lib().dn_chunk_scan(*[a[n] for n in ("kda", "q", "S0", "o", "S_final", "B", "H",
+                                                     "T", "dk", "dv", "dtype", "ws", "wsb",
+                                                     "stream")])
 
 
 def test_phase_validation():
@@ -169,6 +170,8 @@ def test_phase_validation():
     assert _prep(wsb=8) == W
     assert _prep(kda=1, dtype=0, dk=128, dv=128) == _lib.DN_ENOTSUP
     assert _scan(o=None) == E
+    assert _scan(q=None) == E
+    assert _scan(q=ODD) == E
     assert _scan(S0=MIS) == E
     assert _scan(ws=None) == W
     assert _scan(dk=96, dv=96) == _lib.DN_ENOTSUP
