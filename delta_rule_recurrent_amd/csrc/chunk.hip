@@ -501,55 +501,64 @@ void chunk_prep_kernel(const E* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// Prep kernel, one wavefront per (head, chunk): Gated DeltaNet and DeltaNet.
+// Prep kernel, two wavefronts per (head, chunk): Gated DeltaNet and DeltaNet.
 // ---------------------------------------------------------------------------
-// Same results and workspace layout as chunk_prep_kernel, organised for a
-// single wavefront so that no workgroup barrier is needed (about 18 KB of LDS
-// per chunk; one wavefront per SIMD, with up to 512 registers):
-//  * K, Q and V fragments with rows = tokens come straight from global memory.
-//  * With the token index as the contraction index (B-fragments of
-//    X = beta e^G K and of beta V, A-fragments of K~^T = (e^{G_C - G} K)^T),
-//    K and V come from a product with an identity fragment on the matrix
-//    cores: D = K I holds K as D-tiles (exactly), and two D-tiles stacked over
-//    tokens are such a fragment. The per-token scale is applied on the way.
-//  * W = (T diag(beta e^G)) K and u = (T diag(beta)) V, with each scaled T
-//    rounded once to the operand type.
+// Same results and workspace layout as chunk_prep_kernel, split over two
+// wavefronts that meet at a single LDS barrier (about 37 KB of LDS per chunk,
+// two wavefronts per SIMD):
+//   wavefront 0: A = strict_tril(beta K K^T D), the blocked inverse T, the
+//                scaled copies T diag(beta e^G) and T diag(beta) into LDS;
+//                after the barrier u = T diag(beta) V.
+//   wavefront 1: attn = tril(Q K^T D), K~^T, K and V with tokens as the
+//                contraction index (V into LDS); after the barrier
+//                W = T diag(beta e^G) K.
+//  * K, Q and V fragments with rows = tokens come straight from global memory,
+//    in the 8-consecutive-channel contraction order (16-byte loads).
+//  * With the token index as the contraction index (B-fragments of K and V,
+//    A-fragments of K~^T = (e^{G_C - G} K)^T), K and V come from a product
+//    with an identity fragment on the matrix cores: D = K I holds K as D-tiles
+//    (exactly), and two D-tiles stacked over tokens are such a fragment.
+//  * Each scaled T is rounded once to the operand type.
 
-// B-fragment of the identity for the 16 columns 16h .. 16h+15 of a 32-wide
-// contraction block: lane (g, n) supplies I[pi(g, j)][16h + n].
+// Fragments in a second contraction order, for products whose operands are
+// both loaded this way (K K^T, Q K^T, and K I / V I below): lane (g, r) holds
+// the 8 consecutive channels 8g .. 8g+7 of row r of a 32-wide block, one
+// 16-byte load. Any order works for a contraction as long as both operands
+// use it; this one reads each row in 64-byte pieces instead of 32-byte ones.
+// Rows >= L (past the end of the sequence, only in its last chunk) repeat row
+// L - 1: the row index is clamped so that every load is unconditional and in
+// bounds. Such rows never reach a stored result: their beta and log-decay are
+// zero, so they add nothing to A, T, W, u or the state, and the outputs of
+// those rows are not written.
 template <typename E>
-__device__ __forceinline__ typename Frag<E>::type ident_frag(int h, int lane) {
+__device__ __forceinline__ typename Frag<E>::type frag_rows8_g(const E* __restrict__ M, int ld,
+                                                               int row0, int k0, int lane, int L) {
+    typedef typename Frag<E>::type F;
+    const int g = lane >> 4, r = lane & 15;
+    const E* p = M + (long)min(row0 + r, L - 1) * ld + k0 + 8 * g;
+    if constexpr (sizeof(F) == 16) {
+        return *reinterpret_cast<const F*>(p);
+    } else {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+        F f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = a[i];
+            f[4 + i] = b[i];
+        }
+        return f;
+    }
+}
+
+// B-fragment of the identity in that order, for the 16 columns 16h .. 16h+15
+// of a 32-wide block: lane (g, n) supplies I[8g + j][16h + n].
+template <typename E>
+__device__ __forceinline__ typename Frag<E>::type ident8_frag(int h, int lane) {
     const int g = lane >> 4, n = lane & 15;
     typename Frag<E>::type f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int kk = j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4);
-        f[j] = from_f32<E>(kk == 16 * h + n ? 1.f : 0.f);
-    }
-    return f;
-}
-
-// frag_rows on a [rows][ld] token tile in global memory. Rows >= L (past the
-// end of the sequence, only in its last chunk) repeat row L - 1: the row index
-// is clamped so that every load is unconditional and in bounds. Such rows
-// never reach a stored result: their beta and log-decay are zero, so they add
-// nothing to A, T, W, u or the state, and the outputs of those rows are not
-// written.
-template <typename E>
-__device__ __forceinline__ typename Frag<E>::type frag_rows_g(const E* __restrict__ M, int ld, int row0,
-                                                              int k0, int lane, int L) {
-    typedef typename Vec4<E>::type V4;
-    const int g = lane >> 4, r = lane & 15;
-    const int row = row0 + r;
-    const E* p = M + (long)min(row, L - 1) * ld + k0 + 4 * g;
-    const V4 a = *reinterpret_cast<const V4*>(p);
-    const V4 b = *reinterpret_cast<const V4*>(p + 16);
-    typename Frag<E>::type f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f[i] = a[i];
-        f[4 + i] = b[i];
-    }
+    for (int j = 0; j < 8; ++j) f[j] = from_f32<E>(8 * g + j == 16 * h + n ? 1.f : 0.f);
     return f;
 }
 
@@ -576,37 +585,57 @@ __device__ __forceinline__ typename Frag<E>::type frag_from_tiles_rs(const f32x4
 __device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <typename E, int DK, int DV>
-struct Prep1Smem {
+struct Prep2Smem {
     static constexpr int LDF = 68;                     // fp32 64x64: A, then T's diagonal blocks
     static constexpr int LDT = 64 + 16 / sizeof(E);    // T diag(.) in the operand type (two)
-    static constexpr long BYTES = 64L * LDF * 4 > 2 * 64L * LDT * (long)sizeof(E)
-                                      ? 64L * LDF * 4
-                                      : 2 * 64L * LDT * (long)sizeof(E);
+    static constexpr long AT_BYTES = 64L * LDF * 4 > 2 * 64L * LDT * (long)sizeof(E)
+                                         ? 64L * LDF * 4
+                                         : 2 * 64L * LDT * (long)sizeof(E);
+    // V as B-fragments (contraction over tokens), [DV/16 value tiles][2][64 lanes]
+    static constexpr long V_BYTES = (DV / 16) * 2L * 64 * 8 * sizeof(E);
+    static constexpr long BYTES = AT_BYTES + V_BYTES;
 };
 
+// Per-token tables of one chunk in LDS: running log-decay G, beta e^G,
+// e^{G_C - G} and beta of token `lane`; returns e^{G_C}.
+__device__ __forceinline__ float token_tables(float bv, float gv, int lane, float* Gs, float* sX,
+                                              float* sK, float* bs, float* eG) {
+    const float G = wave_inclusive_sum(gv, lane);
+    const float GC = readlane_f(G, 63);
+    const float e = __expf(G);
+    Gs[lane] = G;
+    sX[lane] = bv * e;
+    sK[lane] = __expf(GC - G);
+    bs[lane] = bv;
+    if (eG) eG[lane] = e;
+    return __expf(GC);
+}
+
 template <typename E, int DK, int DV, int KIND>
-__global__ __launch_bounds__(64, 1) void chunk_prep1_kernel(const E* __restrict__ q,
-                                                            const E* __restrict__ k,
-                                                            const E* __restrict__ v,
-                                                            const E* __restrict__ beta,
-                                                            const E* __restrict__ g,
-                                                            char* __restrict__ ws, int T,
-                                                            int nchunks) {
+__global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict__ q,
+                                                             const E* __restrict__ k,
+                                                             const E* __restrict__ v,
+                                                             const E* __restrict__ beta,
+                                                             const E* __restrict__ g,
+                                                             char* __restrict__ ws, int T,
+                                                             int nchunks) {
     typedef WsLayout<E, DK, DV> Lw;
-    typedef Prep1Smem<E, DK, DV> Sm;
+    typedef Prep2Smem<E, DK, DV> Sm;
     typedef typename Frag<E>::type F;
     typedef typename Vec4<E>::type V4;
     constexpr int KB = DK / 32, CT = DK / 16, VB = DV / 32, VT = DV / 16;
     constexpr int LDF = Sm::LDF, LDT = Sm::LDT;
 
     __shared__ __align__(16) char smem[Sm::BYTES];
-    // per token: running log-decay, beta e^G, e^{G_C - G}, beta
-    __shared__ __align__(16) float Gs[64], sX[64], sK[64], bs[64];
+    // per wavefront: running log-decay, beta e^G, e^{G_C - G}, beta of each token
+    __shared__ __align__(16) float tab[2][4][64];
     float* As = reinterpret_cast<float*>(smem);   // A, then T's diagonal blocks in place
     E* Tw = reinterpret_cast<E*>(smem);           // T diag(beta e^G), once the inverse is done
     E* Tu = Tw + 64 * LDT;                        // T diag(beta)
+    F* Vl = reinterpret_cast<F*>(smem + Sm::AT_BYTES);
 
-    const int lane = threadIdx.x, gq = lane >> 4, n = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int gq = lane >> 4, n = lane & 15;
     const long item = blockIdx.x;
     const int c = (int)(item % nchunks);
     const long bh = item / nchunks;
@@ -622,191 +651,205 @@ __global__ __launch_bounds__(64, 1) void chunk_prep1_kernel(const E* __restrict_
     float* gam = reinterpret_cast<float*>(blk + Lw::GAM_BYTE_OFF);
     float* eg = reinterpret_cast<float*>(blk + Lw::EG_BYTE_OFF);
 
-    // ---- 1. beta and log-decay of token `lane`, running sum, per-token tables
-    {
-        const long tk = tok0 + min(lane, L - 1);
-        float bv = to_f32(beta[tk]);
-        float gv = KIND == KIND_GATED ? to_f32(g[tk]) : 0.f;
-        if (lane >= L) bv = gv = 0.f;
-        const float G = wave_inclusive_sum(gv, lane);
-        const float GC = readlane_f(G, 63);
-        const float e = __expf(G);
-        Gs[lane] = G;
-        eg[lane] = e;
-        sX[lane] = bv * e;
-        sK[lane] = __expf(GC - G);
-        bs[lane] = bv;
-        // the chunk decay, replicated per key channel (the scan reads it like KDA's)
-        for (int ch = lane; ch < DK; ch += 64) gam[ch] = __expf(GC);
+    // ---- 1. every load of this wavefront is issued up front, so that a single
+    //         memory latency covers them: beta and the log-decay of token
+    //         `lane`, then the K fragments (rows = tokens, contraction = key
+    //         channels, in the 8-consecutive-channel order; both wavefronts),
+    //         then (wavefront 1) Q and V in the same order
+    const long tk = tok0 + min(lane, L - 1);
+    const E braw = beta[tk];
+    const E graw = KIND == KIND_GATED ? g[tk] : E{};
+    F kf[4][KB];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) kf[tt][kb] = frag_rows8_g<E>(k + tok0 * DK, DK, 16 * tt, 32 * kb, lane, L);
+    F qa[4][KB], vf[4][VB];
+    if (w == 1) {
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) qa[tt][kb] = frag_rows8_g<E>(q + tok0 * DK, DK, 16 * tt, 32 * kb, lane, L);
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+            for (int kb = 0; kb < VB; ++kb) vf[tt][kb] = frag_rows8_g<E>(v + tok0 * DV, DV, 16 * tt, 32 * kb, lane, L);
     }
 
-    // ---- 2. K and Q fragments (rows = tokens, contraction = key channels),
-    //         requested together so that one memory latency covers them
-    F kf[4][KB], qa[4][KB];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[tt][kb] = frag_rows_g<E>(k + tok0 * DK, DK, 16 * tt, 32 * kb, lane, L);
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) qa[tt][kb] = frag_rows_g<E>(q + tok0 * DK, DK, 16 * tt, 32 * kb, lane, L);
-    lds_fence();   // the per-token tables are written
+    // per-token tables (each wavefront its own copy; wave 0 stores the per-token
+    // e^G and the chunk decay e^{G_C}, replicated per key channel)
+    float* Gs = tab[w][0];
+    float* sX = tab[w][1];
+    float* sK = tab[w][2];
+    float* bs = tab[w][3];
+    {
+        float bv = to_f32(braw), gv = to_f32(graw);
+        if (lane >= L) bv = gv = 0.f;
+        const float eGC = token_tables(bv, gv, lane, Gs, sX, sK, bs, w == 0 ? eg : nullptr);
+        if (w == 0)
+            for (int ch = lane; ch < DK; ch += 64) gam[ch] = eGC;
+    }
 
-    // attn = tril(Q K^T exp(G_i - G_j)) as A-fragments: attn^T tiles (rows j)
-    // stacked over two j tiles
+    if (w == 0) {
+        lds_fence();   // tables written
+        // ---- 2. A = strict_tril(beta_i K K^T exp(G_i - G_j)) into LDS (fp32)
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const F* qf = qa[it];
-        f32x4 at[4];
+        for (int it = 0; it < 4; ++it)
 #pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-            at[jt] = zero4();
-            if (jt <= it) {
+            for (int jt = 0; jt <= it; ++jt) {
+                f32x4 s = zero4();
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) at[jt] = mma(kf[jt][kb], qf[kb], at[jt]);
-                const int i = 16 * it + n;
-                const float Gi = Gs[i];
-                const f32x4 Gj = *reinterpret_cast<const f32x4*>(Gs + 16 * jt + 4 * gq);
+                for (int kb = 0; kb < KB; ++kb) s = mma(kf[it][kb], kf[jt][kb], s);
+                const int j = 16 * jt + n;
+                const float Gj = Gs[j];
+                const f32x4 Gi = *reinterpret_cast<const f32x4*>(Gs + 16 * it + 4 * gq);
+                const f32x4 bi = *reinterpret_cast<const f32x4*>(bs + 16 * it + 4 * gq);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int j = 16 * jt + 4 * gq + e;
-                    at[jt][e] = (i >= j) ? __expf(Gi - Gj[e]) * at[jt][e] : 0.f;
+                    const int i = 16 * it + 4 * gq + e;
+                    const float val = bi[e] * __expf(Gi[e] - Gj) * s[e];   // inf above the diagonal is dropped
+                    As[i * LDF + j] = (i > j) ? val : 0.f;
                 }
             }
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) Af[(it * 2 + kb) * 64 + lane] = frag_from_tiles<E>(at[2 * kb], at[2 * kb + 1]);
-    }
+        lds_fence();   // A is written
 
-    // system matrix A = strict_tril(beta_i K K^T exp(G_i - G_j)) into LDS (fp32)
+        // ---- 3. UT transform T = (I + A)^-1, blocked over 16x16 tiles
+        // 3a: diagonal blocks by forward substitution, lane (block gq, column n):
+        //     T_jj = 1, T_ij = -sum_{j <= m < i} A_im T_mj; written over the block of A
+        {
+            const int b0 = 16 * gq, j = n;
+            float tc[16];
 #pragma unroll
-    for (int it = 0; it < 4; ++it)
+            for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-        for (int jt = 0; jt <= it; ++jt) {
-            f32x4 s = zero4();
+            for (int i = 1; i < 16; ++i) {
+                float acc = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) s = mma(kf[it][kb], kf[jt][kb], s);
-            const int j = 16 * jt + n;
-            const float Gj = Gs[j];
-            const f32x4 Gi = *reinterpret_cast<const f32x4*>(Gs + 16 * it + 4 * gq);
-            const f32x4 bi = *reinterpret_cast<const f32x4*>(bs + 16 * it + 4 * gq);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * it + 4 * gq + e;
-                As[i * LDF + j] = (i > j) ? bi[e] * __expf(Gi[e] - Gj) * s[e] : 0.f;
+                for (int m = 0; m < i; ++m) acc += As[(b0 + i) * LDF + b0 + m] * tc[m];
+                tc[i] = (i > j) ? -acc : tc[i];
             }
-        }
-
-    // K with tokens as the contraction index (D = K I): K as B-fragments (kept
-    // for W = T diag(beta e^G) K), K~^T = (e^{G_C - G} K)^T as A-fragments (stored)
-    const F id0 = ident_frag<E>(0, lane), id1 = ident_frag<E>(1, lane);
-    F xf[CT][2];
+            lds_fence();
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-        f32x4 d[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) d[tt] = mma(kf[tt][ct >> 1], (ct & 1) ? id1 : id0, zero4());
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            xf[ct][kt] = frag_from_tiles<E>(d[2 * kt], d[2 * kt + 1]);
-            Kf[(ct * 2 + kt) * 64 + lane] = frag_from_tiles_rs<E>(d[2 * kt], d[2 * kt + 1], sK, 32 * kt, lane);
-        }
-    }
-    // V fragments, in flight while T is computed
-    F vf[4][VB];
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int kb = 0; kb < VB; ++kb) vf[tt][kb] = frag_rows_g<E>(v + tok0 * DV, DV, 16 * tt, 32 * kb, lane, L);
-    lds_fence();   // A is written
-
-    // ---- 3. UT transform T = (I + A)^-1, blocked over 16x16 tiles ------------
-    // 3a: diagonal blocks by forward substitution, lane (block gq, column n):
-    //     T_jj = 1, T_ij = -sum_{j <= m < i} A_im T_mj; written over the block of A
-    {
-        const int b0 = 16 * gq, j = n;
-        float tc[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
-#pragma unroll
-        for (int i = 1; i < 16; ++i) {
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < i; ++m) acc += As[(b0 + i) * LDF + b0 + m] * tc[m];
-            if (i > j) tc[i] = -acc;
+            for (int i = 0; i < 16; ++i) As[(b0 + i) * LDF + b0 + j] = tc[i];
         }
         lds_fence();
+        // 3b: T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ on the matrix cores (fp32),
+        //     the column tiles J interleaved
+        f32x4 tm[4][4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) As[(b0 + i) * LDF + b0 + j] = tc[i];
-    }
-    lds_fence();
-    // 3b: T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ on the matrix cores (fp32),
-    //     the column tiles J interleaved
-    f32x4 tm[4][4];
+        for (int J = 0; J < 4; ++J)
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
+            for (int e = 0; e < 4; ++e) tm[J][J][e] = As[(16 * J + 4 * gq + e) * LDF + 16 * J + n];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tm[J][J][e] = As[(16 * J + 4 * gq + e) * LDF + 16 * J + n];
+        for (int I = 1; I < 4; ++I) {
 #pragma unroll
-    for (int I = 1; I < 4; ++I) {
+            for (int J = 0; J < I; ++J) {
+                f32x4 R = zero4();
 #pragma unroll
-        for (int J = 0; J < I; ++J) {
-            f32x4 R = zero4();
-#pragma unroll
-            for (int K = J; K < I; ++K) R = mma16_lds_reg(As + 16 * I * LDF + 16 * K, LDF, lane, tm[K][J], R);
-            tm[I][J] = -mma16_lds_reg(As + 16 * I * LDF + 16 * I, LDF, lane, R, zero4());
-        }
-    }
-    lds_fence();   // every read of A and of the diagonal blocks has returned
-    // T diag(beta e^G) and T diag(beta) (lower triangular) in the operand type,
-    // over the fp32 region; lane (gq, n) holds column 16J + n of tile (I, J)
-#pragma unroll
-    for (int J = 0; J < 4; ++J) {
-        const float cx = sX[16 * J + n], cb = bs[16 * J + n];
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int o = (16 * I + 4 * gq + e) * LDT + 16 * J + n;
-                Tw[o] = from_f32<E>(I >= J ? tm[I][J][e] * cx : 0.f);
-                Tu[o] = from_f32<E>(I >= J ? tm[I][J][e] * cb : 0.f);
+                for (int K = J; K < I; ++K) R = mma16_lds_reg(As + 16 * I * LDF + 16 * K, LDF, lane, tm[K][J], R);
+                tm[I][J] = -mma16_lds_reg(As + 16 * I * LDF + 16 * I, LDF, lane, R, zero4());
             }
-    }
-    lds_fence();
-
-    // ---- 4. W = T X: W^T tiles (rows = key channels) for each token tile,
-    //         stacked over channel tiles = A-fragments of W
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-        F tf[2];   // T diag(beta e^G), rows = tokens of tile tt, contraction = tokens
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) tf[kt] = frag_rows<E>(Tw, LDT, 16 * tt, 32 * kt, lane);
-        f32x4 wt[CT];
-#pragma unroll
-        for (int mt = 0; mt < CT; ++mt) {
-            wt[mt] = zero4();
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) wt[mt] = mma(xf[mt][kt], tf[kt], wt[mt]);
         }
+        lds_fence();   // every read of A and of the diagonal blocks has returned
+        // T diag(beta e^G) and T diag(beta) (lower triangular) in the operand
+        // type, over the fp32 region; lane (gq, n) holds column 16J + n of tile (I, J)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) Wf[(tt * KB + kb) * 64 + lane] = frag_from_tiles<E>(wt[2 * kb], wt[2 * kb + 1]);
+        for (int J = 0; J < 4; ++J) {
+            const float cx = sX[16 * J + n], cb = bs[16 * J + n];
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int o = (16 * I + 4 * gq + e) * LDT + 16 * J + n;
+                    Tw[o] = from_f32<E>(I >= J ? tm[I][J][e] * cx : 0.f);
+                    Tu[o] = from_f32<E>(I >= J ? tm[I][J][e] * cb : 0.f);
+                }
+        }
+    } else {
+        // ---- 2'. attn = tril(Q K^T exp(G_i - G_j)) as A-fragments: attn^T tiles
+        //          (rows j) stacked over two j tiles
+        lds_fence();   // tables written
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+            f32x4 at[4];
+#pragma unroll
+            for (int jt = 0; jt < 4; ++jt) {
+                at[jt] = zero4();
+                if (jt <= it) {
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) at[jt] = mma(kf[jt][kb], qa[it][kb], at[jt]);
+                    const int i = 16 * it + n;
+                    const float Gi = Gs[i];
+                    const f32x4 Gj = *reinterpret_cast<const f32x4*>(Gs + 16 * jt + 4 * gq);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int j = 16 * jt + 4 * gq + e;
+                        const float val = __expf(Gi - Gj[e]) * at[jt][e];   // inf above the diagonal is dropped
+                        at[jt][e] = (i >= j) ? val : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) Af[(it * 2 + kb) * 64 + lane] = frag_from_tiles<E>(at[2 * kb], at[2 * kb + 1]);
+        }
+        // K and V with tokens as the contraction index (D = K I): K as
+        // B-fragments (kept for W = T diag(beta e^G) K), K~^T = (e^{G_C - G} K)^T
+        // as A-fragments (stored), V as B-fragments (to wavefront 0 through LDS)
+        const F id0 = ident8_frag<E>(0, lane), id1 = ident8_frag<E>(1, lane);
+#pragma unroll
+        for (int nt = 0; nt < VT; ++nt) {
+            f32x4 d[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) d[tt] = mma(vf[tt][nt >> 1], (nt & 1) ? id1 : id0, zero4());
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) Vl[(nt * 2 + kt) * 64 + lane] = frag_from_tiles<E>(d[2 * kt], d[2 * kt + 1]);
+        }
+        F xf[CT][2];
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            f32x4 d[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) d[tt] = mma(kf[tt][ct >> 1], (ct & 1) ? id1 : id0, zero4());
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                xf[ct][kt] = frag_from_tiles<E>(d[2 * kt], d[2 * kt + 1]);
+                Kf[(ct * 2 + kt) * 64 + lane] = frag_from_tiles_rs<E>(d[2 * kt], d[2 * kt + 1], sK, 32 * kt, lane);
+            }
+        }
+        lds_barrier();   // T diag(.) and V are in LDS
+
+        // ---- 4. W = T diag(beta e^G) K: W^T tiles (rows = key channels) for each
+        //         token tile, stacked over channel tiles = A-fragments of W
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+            F tf[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) tf[kt] = frag_rows<E>(Tw, LDT, 16 * tt, 32 * kt, lane);
+            f32x4 wt[CT];
+#pragma unroll
+            for (int mt = 0; mt < CT; ++mt) {
+                wt[mt] = zero4();
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) wt[mt] = mma(xf[mt][kt], tf[kt], wt[mt]);
+            }
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) Wf[(tt * KB + kb) * 64 + lane] = frag_from_tiles<E>(wt[2 * kb], wt[2 * kb + 1]);
+        }
+        return;
     }
+    lds_barrier();   // (wavefront 0) T diag(.) and V are in LDS
 
     // ---- 5. u = T diag(beta) V as D-tiles (rows = tokens), value tile by value tile
-    F tu[4][2];   // T diag(beta) A-fragments
+    F tu[4][2];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) tu[tt][kt] = frag_rows<E>(Tu, LDT, 16 * tt, 32 * kt, lane);
 #pragma unroll
     for (int nt = 0; nt < VT; ++nt) {
-        f32x4 d[4];
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) d[tt] = mma(vf[tt][nt >> 1], (nt & 1) ? id1 : id0, zero4());
         F vb[2];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) vb[kt] = frag_from_tiles<E>(d[2 * kt], d[2 * kt + 1]);
+        for (int kt = 0; kt < 2; ++kt) vb[kt] = Vl[(nt * 2 + kt) * 64 + lane];
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt) {
             f32x4 acc = zero4();
@@ -1154,9 +1197,9 @@ static hipError_t prep_t(const void* q, const void* k, const void* v, const void
                          const void* g, void* ws, int BH, int T, hipStream_t st) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int nitems = nchunks * BH;
-    // one wavefront per chunk where its fragments fit in 256 registers
+    // two wavefronts per chunk where their fragments fit in 256 registers
     if constexpr (KIND != KIND_KDA && (sizeof(E) == 2 || D == 64)) {
-        hipLaunchKernelGGL((chunk_prep1_kernel<E, D, D, KIND>), dim3((unsigned)nitems), dim3(64), 0, st,
+        hipLaunchKernelGGL((chunk_prep2_kernel<E, D, D, KIND>), dim3((unsigned)nitems), dim3(128), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
                            (char*)ws, T, nchunks);
         return hipGetLastError();
