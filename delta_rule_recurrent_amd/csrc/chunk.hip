@@ -883,6 +883,35 @@ struct ScanOps {
     f32x4 gam[MTW], eg;
 };
 
+// Raw buffer loads through a resource descriptor held in scalar registers:
+// the base address is uniform, each lane adds a fixed 32-bit offset, and no
+// per-load 64-bit address arithmetic is needed. Bytes at or past `bytes` read
+// as zero (the load is range-checked). 0x00020000 is the gfx9 descriptor word
+// for untyped 32-bit-element buffers.
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <typename T>
+__device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int voff) {
+    static_assert(sizeof(T) == 8 || sizeof(T) == 16 || sizeof(T) == 32, "8, 16 or 32 bytes");
+    T out;
+    if constexpr (sizeof(T) == 8) {
+        const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
+        __builtin_memcpy(&out, &x, 8);
+    } else if constexpr (sizeof(T) == 16) {
+        const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+        __builtin_memcpy(&out, &x, 16);
+    } else {
+        const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0);
+        const i32x4 y = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0);
+        __builtin_memcpy(&out, &x, 16);
+        __builtin_memcpy(reinterpret_cast<char*>(&out) + 16, &y, 16);
+    }
+    return out;
+}
+
 // Where the operands of one chunk are: its workspace block and its rows of Q,
 // of which the first L are in the sequence.
 template <typename E>
@@ -899,53 +928,49 @@ struct ChunkSrc {
 template <int PART, int KIND, typename E, int DK, int DV, int BV>
 __device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV>& x, const ChunkSrc<E>& src,
                                                int vt, int w, int lane) {
-    const char* blk = src.blk;
     typedef WsLayout<E, DK, DV> Lw;
     typedef ScanOps<E, DK, DV, BV> O;
     typedef typename O::F F;
     typedef typename O::V4 V4;
-    const E* base = reinterpret_cast<const E*>(blk);
+    constexpr int FB = (int)sizeof(F);    // bytes of one fragment per lane
+    constexpr int ES = (int)sizeof(E);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(src.blk, (unsigned)Lw::BYTES);
     if (PART == 0) {
-        const F* Wf = reinterpret_cast<const F*>(base + Lw::W_OFF);
 #pragma unroll
-        for (int kb = 0; kb < O::KB; ++kb) x.w[kb] = Wf[(w * O::KB + kb) * 64 + lane];
+        for (int kb = 0; kb < O::KB; ++kb)
+            x.w[kb] = buf_load<F>(rb, (int)(Lw::W_OFF * ES) + ((w * O::KB + kb) * 64 + lane) * FB);
     } else if (PART == 1) {
         if (KIND == KIND_KDA) {
-            const F* Qf = reinterpret_cast<const F*>(base + Lw::Q_OFF);
 #pragma unroll
-            for (int kb = 0; kb < O::KB; ++kb) x.q[kb] = Qf[(w * O::KB + kb) * 64 + lane];
+            for (int kb = 0; kb < O::KB; ++kb)
+                x.q[kb] = buf_load<F>(rb, (int)(Lw::Q_OFF * ES) + ((w * O::KB + kb) * 64 + lane) * FB);
         } else {
             // contiguous 16-byte loads of the wave's rows; rows past the end of
-            // the sequence repeat its last row (their outputs are not written)
-            constexpr int VEC = 16 / sizeof(E);
+            // the sequence are outside the descriptor's range and read as zero
+            // (their outputs are not written)
+            const __amdgpu_buffer_rsrc_t rq = make_rsrc(src.q, (unsigned)(src.L * DK * ES));
 #pragma unroll
-            for (int i = 0; i < O::QR; ++i) {
-                const int off = (i * 64 + lane) * VEC;
-                const int row = min(16 * w + off / DK, src.L - 1);
-                x.qr[i] = *reinterpret_cast<const typename O::V16*>(src.q + (long)row * DK + off % DK);
-            }
+            for (int i = 0; i < O::QR; ++i)
+                x.qr[i] = buf_load<typename O::V16>(rq, (16 * w * DK + (i * 64 + lane) * (16 / ES)) * ES);
         }
     } else if (PART == 2) {
-        const F* Kf = reinterpret_cast<const F*>(base + Lw::K_OFF);
-        const F* Af = reinterpret_cast<const F*>(base + Lw::A_OFF);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) x.a[kb] = Af[(w * 2 + kb) * 64 + lane];
+        for (int kb = 0; kb < 2; ++kb)
+            x.a[kb] = buf_load<F>(rb, (int)(Lw::A_OFF * ES) + ((w * 2 + kb) * 64 + lane) * FB);
 #pragma unroll
         for (int m = 0; m < O::MTW; ++m)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) x.k[m][kb] = Kf[((w * O::MTW + m) * 2 + kb) * 64 + lane];
+            for (int kb = 0; kb < 2; ++kb)
+                x.k[m][kb] = buf_load<F>(rb, (int)(Lw::K_OFF * ES) + (((w * O::MTW + m) * 2 + kb) * 64 + lane) * FB);
     } else {
-        const V4* Uf = reinterpret_cast<const V4*>(base + Lw::U_OFF);
-        const float* gam = reinterpret_cast<const float*>(blk + Lw::GAM_BYTE_OFF);
         const int gq = lane >> 4;
 #pragma unroll
-        for (int nt = 0; nt < O::NT; ++nt) x.u[nt] = Uf[((vt * O::NT + nt) * 4 + w) * 64 + lane];
+        for (int nt = 0; nt < O::NT; ++nt)
+            x.u[nt] = buf_load<V4>(rb, (int)(Lw::U_OFF * ES) + (((vt * O::NT + nt) * 4 + w) * 64 + lane) * (int)sizeof(V4));
 #pragma unroll
         for (int m = 0; m < O::MTW; ++m)
-            x.gam[m] = *reinterpret_cast<const f32x4*>(gam + 16 * (w * O::MTW + m) + 4 * gq);
-        if (KIND != KIND_KDA)
-            x.eg = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(blk + Lw::EG_BYTE_OFF) +
-                                                   16 * w + 4 * gq);
+            x.gam[m] = buf_load<f32x4>(rb, (int)Lw::GAM_BYTE_OFF + (16 * (w * O::MTW + m) + 4 * gq) * 4);
+        if (KIND != KIND_KDA) x.eg = buf_load<f32x4>(rb, (int)Lw::EG_BYTE_OFF + (16 * w + 4 * gq) * 4);
     }
 }
 
