@@ -67,12 +67,12 @@ CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurren
 DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
                   "delta_rule_recurrent_amd/csrc/dn_launch.h")
 TRAFFIC = {
-    "chunk_prep_kernel": {"fetch_kib": 24822.4, "write_kib": 74240.0, "sources": CHUNK_SOURCES,
-                          "sha256": "e0a2804fd3558c7649c51c41fdbd4c005317bcd87b48d0981e9e783b231414e9"},
-    "chunk_scan_kernel": {"fetch_kib": 37166.2, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
-                          "sha256": "e0a2804fd3558c7649c51c41fdbd4c005317bcd87b48d0981e9e783b231414e9"},
-    "decode_step_kernel": {"fetch_kib": 132752.2, "write_kib": 263168.0, "sources": DECODE_SOURCES,
-                           "sha256": "a64a53303fb0eb0c9c813ca7277b3d62e203d6b69865cf3320005df89f2e075b"},
+    "chunk_prep2_kernel": {"fetch_kib": 29079.4, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
+                          "sha256": "8d5b658c1cf8c9f512742195764e779a1e65ed16e978205bd35064c25ab5bf95"},
+    "chunk_scan_kernel": {"fetch_kib": 37294.7, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
+                          "sha256": "8d5b658c1cf8c9f512742195764e779a1e65ed16e978205bd35064c25ab5bf95"},
+    "decode_step_kernel": {"fetch_kib": 132751.6, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+                           "sha256": "20c589737f89c1bcd314771b06d08beb8639c1773e474a7b5c8f4bac9b266a16"},
 }
 
 
@@ -210,7 +210,7 @@ def run_prefill(args, torch, np, dn, synthetic, to_dev, dev):
     scan_ms = event_time_ms(torch, lambda: dn.chunk_scan(inp["q"], o, ws, None, S_final),
                             args.steps)
     kern = {
-        "chunk_prep_kernel": dict(ms=prep_ms, flop=flops_prep(d) * tokens),
+        "chunk_prep2_kernel": dict(ms=prep_ms, flop=flops_prep(d) * tokens),
         "chunk_scan_kernel": dict(ms=scan_ms, flop=flops_scan(d) * tokens),
     }
     for k_, v_ in kern.items():

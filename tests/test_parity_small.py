@@ -173,3 +173,37 @@ def test_decode_equals_one_token_prefill(kind):
     torch.cuda.synchronize()
     assert torch.allclose(o_d, o_p[:, :, 0], rtol=1e-5, atol=1e-5)
     assert torch.allclose(S, S_p, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T", [32 * 64 + 37, 48 * 64])
+def test_long_prefill(kind, dtype, T):
+    """Sequences of 32 chunks and more, with a ragged last chunk: same results as
+    the oracle with a start state, bitwise the same with the state updated in
+    place, and bitwise equal to calling the two phases one after the other."""
+    if not _supported(kind, dtype, 128, "chunk"):
+        pytest.skip("fp32 KDA at d = 128 has no chunked form")
+    dn = _dn()
+    say("long prefill", kind, dtype, T)
+    inp = make(kind, 1, 2, T, 128, dtype, seed=23, s0_std=0.5)
+    d = to_dev(inp)
+    fn = dn.kda_chunk_fwd if kind == "kda" else dn.chunk_fwd
+    o, S = fn(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"])
+    Sip = d["S0"].clone()
+    o2, _ = fn(d["q"], d["k"], d["v"], d["beta"], d["g"], Sip, S_final=Sip)
+    # the two phases called one after the other
+    ws = torch.empty(dn.workspace_bytes(1, 2, T, 128, 128, d["q"].dtype), dtype=torch.uint8,
+                     device="cuda")
+    o3 = torch.empty_like(o)
+    S3 = torch.empty_like(S)
+    dn.chunk_prep(d["q"], d["k"], d["v"], d["beta"], d["g"], ws, kda=kind == "kda")
+    dn.chunk_scan(d["q"], o3, ws, d["S0"], S3, kda=kind == "kda")
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(inp)
+    tol = TOL[dtype]
+    eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
+    say("  err o %.3e  S %.3e" % (eo, es))
+    assert eo <= tol and es <= tol
+    assert torch.equal(o2, o) and torch.equal(Sip, S)
+    assert torch.equal(o3, o) and torch.equal(S3, S)
