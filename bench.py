@@ -67,12 +67,14 @@ CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurren
 DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
                   "delta_rule_recurrent_amd/csrc/dn_launch.h")
 TRAFFIC = {
-    "chunk_prep2_kernel": {"fetch_kib": 29079.4, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
-                          "sha256": "8d5b658c1cf8c9f512742195764e779a1e65ed16e978205bd35064c25ab5bf95"},
-    "chunk_scan_kernel": {"fetch_kib": 37294.7, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
-                          "sha256": "8d5b658c1cf8c9f512742195764e779a1e65ed16e978205bd35064c25ab5bf95"},
-    "decode_step_kernel": {"fetch_kib": 132751.6, "write_kib": 263168.0, "sources": DECODE_SOURCES,
-                           "sha256": "20c589737f89c1bcd314771b06d08beb8639c1773e474a7b5c8f4bac9b266a16"},
+    "chunk_prep2_kernel": {"fetch_kib": 29418.6, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
+                           "sha256": "db9ff28f671bfc3cae2d609a36ef3ed30eb3646a7b52b936da9c35da13109855"},
+    "chunk_scan_kernel": {"fetch_kib": 37102.6, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
+                          "sha256": "db9ff28f671bfc3cae2d609a36ef3ed30eb3646a7b52b936da9c35da13109855"},
+    "chunk_fused_kernel": {"fetch_kib": 62001.6, "write_kib": 76630.5, "sources": CHUNK_SOURCES,
+                           "sha256": "db9ff28f671bfc3cae2d609a36ef3ed30eb3646a7b52b936da9c35da13109855"},
+    "decode_step_kernel": {"fetch_kib": 132752.1, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+                           "sha256": "97909e8bd3d430aff64cf62dc77a70178c67b1102cee5d38ce5c9af2002a88fa"},
 }
 
 
@@ -128,8 +130,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this operator shards over (sequence, head) with "
-              "no communication, and multi-GPU runs are not part of this build (got --gpus %d)"
+        print("bench.py measures one GPU only: the operator shards over (sequence, head) with "
+              "no communication, and no multi-GPU path is implemented (got --gpus %d)"
               % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -204,16 +206,23 @@ def run_prefill(args, torch, np, dn, synthetic, to_dev, dev):
     log("prefill %.4f ms/step  %.3e token-heads/s (wall %.3f s for %d steps)"
         % (ms_step, value, t_wall, args.steps))
 
-    # per-kernel live timing of the two phases (same stream, events around each launch)
+    # live per-kernel timing (same stream, events around back-to-back launches
+    # of each kernel alone): at 32 chunks per sequence the step is the two
+    # phase kernels; the one-launch form (prep and scan workgroups together,
+    # used from 64 chunks on) is timed beside them on the same inputs
     prep_ms = event_time_ms(torch, lambda: dn.chunk_prep(inp["q"], inp["k"], inp["v"], inp["beta"],
                                                          inp["g"], ws), args.steps)
     scan_ms = event_time_ms(torch, lambda: dn.chunk_scan(inp["q"], o, ws, None, S_final),
                             args.steps)
+    fused_ms = event_time_ms(torch, lambda: dn.chunk_fwd_fused(
+        inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], None, o=o, S_final=S_final,
+        workspace=ws), args.steps)
     kern = {
         "chunk_prep2_kernel": dict(ms=prep_ms, flop=flops_prep(d) * tokens),
         "chunk_scan_kernel": dict(ms=scan_ms, flop=flops_scan(d) * tokens),
     }
-    for k_, v_ in kern.items():
+    alt = {"chunk_fused_kernel": dict(ms=fused_ms, flop=(flops_prep(d) + flops_scan(d)) * tokens)}
+    for k_, v_ in list(kern.items()) + list(alt.items()):
         v_["tflops"] = v_["flop"] / (v_["ms"] * 1e-3) / 1e12
         v_["frac_mfma"] = v_["tflops"] / PEAK_BF16_TFLOPS
         log("  %s %.4f ms  %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)"
@@ -249,6 +258,8 @@ def run_prefill(args, torch, np, dn, synthetic, to_dev, dev):
             "frac_hbm": round(bytes_prefill(B, H, T, d) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
             "kernels": {k_: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
                              for kk, vv in v_.items()} for k_, v_ in kern.items()},
+            "one_launch_form": {k_: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
+                                     for kk, vv in v_.items()} for k_, v_ in alt.items()},
         },
     }
 

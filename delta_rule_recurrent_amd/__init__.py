@@ -19,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import DeltaNetError, lib
 
-__all__ = ["chunk_fwd", "kda_chunk_fwd", "chunk_prep", "chunk_scan", "recurrent_fwd",
+__all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_prep", "chunk_scan", "recurrent_fwd",
            "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
            "DeltaNetError", "lib", "library_path"]
 
@@ -116,6 +116,16 @@ def chunk_fwd(q, k, v, beta, g=None, S0=None, *, output_final_state=True, o=None
     S_final may be S0 for an in-place state update.
     """
     return _chunk("dn_chunk_fwd", q, k, v, beta, g, S0, output_final_state, o, S_final,
+                  workspace, stream, kda=False)
+
+
+def chunk_fwd_fused(q, k, v, beta, g=None, S0=None, *, output_final_state=True, o=None,
+                    S_final=None, workspace=None, stream=None):
+    """chunk_fwd as one kernel launch (prep and scan concurrently); bf16 only.
+
+    Results are bitwise equal to chunk_fwd. Raises DeltaNetError (DN_ENOTSUP)
+    where no one-launch form exists."""
+    return _chunk("dn_chunk_fwd_fused", q, k, v, beta, g, S0, output_final_state, o, S_final,
                   workspace, stream, kda=False)
 
 

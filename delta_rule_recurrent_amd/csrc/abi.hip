@@ -9,7 +9,7 @@
 
 namespace {
 
-constexpr int kVersion = 1;
+constexpr int kVersion = 2;
 
 bool misaligned(const void* p, unsigned a = 16) {
     return (reinterpret_cast<uintptr_t>(p) & (uintptr_t)(a - 1)) != 0;
@@ -59,7 +59,7 @@ int chunk_kind(bool kda, const void* g) {
 int chunk_common(int kind, const void* q, const void* k, const void* v, const void* beta,
                  const void* g, const float* S0, void* o, float* S_final, int B, int H, int T,
                  int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+                 void* stream, int mode) {
     int st = check_common(q, k, v, beta, g, kind == dn::KIND_KDA, S0, o, S_final, B, H, T, dk,
                           dv, dtype);
     if (st != DN_OK) return st;
@@ -72,11 +72,11 @@ int chunk_common(int kind, const void* q, const void* k, const void* v, const vo
     }
     st = check_workspace(BH, T, dk, dv, dtype, workspace, workspace_bytes);
     if (st != DN_OK) return st;
-    hipError_t e = dn::launch_chunk_prep(kind, dtype, q, k, v, beta, g, workspace, (int)BH, T, dk,
-                                         dv, as_stream(stream));
-    if (e != hipSuccess) return DN_EHIP;
-    return hip_status(dn::launch_chunk_scan(kind, dtype, q, S0, o, S_final, workspace, (int)BH, T,
-                                            dk, dv, as_stream(stream)));
+    const hipError_t e = dn::launch_chunk_fwd(kind, dtype, q, k, v, beta, g, S0, o, S_final,
+                                              workspace, (int)BH, T, dk, dv, mode,
+                                              as_stream(stream));
+    if (e == hipErrorNotSupported) return DN_ENOTSUP;
+    return hip_status(e);
 }
 
 int recurrent_common(int kind, const void* q, const void* k, const void* v, const void* beta,
@@ -113,7 +113,8 @@ const char* dn_strerror(int status) {
     switch (status) {
         case DN_OK: return "success";
         case DN_EINVAL: return "invalid argument (NULL or misaligned pointer, bad size or dtype)";
-        case DN_ENOTSUP: return "unsupported head size (d_k, d_v must be equal and in {64, 128})";
+        case DN_ENOTSUP: return "unsupported configuration (d_k, d_v must be equal and in {64, 128}; "
+                                "no chunked fp32 KDA at d = 128; dn_chunk_fwd_fused: no one-launch form)";
         case DN_EWORKSPACE: return "workspace missing, misaligned or smaller than dn_chunk_fwd_workspace()";
         case DN_EHIP: return "HIP runtime error at kernel launch";
         default: return "unknown status";
@@ -134,7 +135,19 @@ int dn_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, 
                  const float* S0, void* o, float* S_final, int B, int H, int T, int dk, int dv,
                  int dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return chunk_common(g ? dn::KIND_GATED : dn::KIND_DELTANET, q, k, v, beta, g, S0, o, S_final,
-                        B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream);
+                        B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream, dn::FWD_AUTO);
+}
+
+int dn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* beta,
+                       const void* g, const float* S0, void* o, float* S_final, int B, int H,
+                       int T, int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (dtype != DN_BF16) {
+        const int st = check_common(q, k, v, beta, g, false, S0, o, S_final, B, H, T, dk, dv, dtype);
+        return st != DN_OK ? st : DN_ENOTSUP;
+    }
+    return chunk_common(g ? dn::KIND_GATED : dn::KIND_DELTANET, q, k, v, beta, g, S0, o, S_final,
+                        B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream, dn::FWD_FUSED);
 }
 
 int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
@@ -142,7 +155,7 @@ int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* be
                      int T, int dk, int dv, int dtype, void* workspace,
                      size_t workspace_bytes, void* stream) {
     return chunk_common(dn::KIND_KDA, q, k, v, beta, g, S0, o, S_final, B, H, T, dk, dv, dtype,
-                        workspace, workspace_bytes, stream);
+                        workspace, workspace_bytes, stream, dn::FWD_TWO);
 }
 
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,

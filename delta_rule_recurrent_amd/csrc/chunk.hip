@@ -13,7 +13,7 @@
 // section "Training it: the WY trick"; with per-channel decay for KDA,
 // page "A walk through of the DeltaNet family of linear attention variants").
 //
-// Two kernels:
+// Kernels:
 //   chunk_prep_kernel  one workgroup per (head, chunk), all chunks in parallel:
 //                      G, A (MFMA), T (forward substitution in LDS), W, u
 //                      (MFMA), the masked decayed Q K^T and the decay-scaled
@@ -26,7 +26,13 @@
 //                      all chunks; per chunk U = u - W S, O = Q~ S + attn U,
 //                      S = gamma S + K~^T U, chained through two small LDS
 //                      exchanges of bf16 fragments.
+//   chunk_prep2_kernel the prep on two wavefronts per (head, chunk) (Gated
+//                      DeltaNet / DeltaNet; same workspace contents).
+//   chunk_fused_kernel both in one launch: prep workgroups hand chunk blocks
+//                      to the scan workgroups of the same XCD as they finish
+//                      (long sequences, bf16).
 #include <atomic>
+#include <random>
 
 #include "dn_device.h"
 #include "dn_launch.h"
@@ -611,14 +617,23 @@ __device__ __forceinline__ float token_tables(float bv, float gv, int lane, floa
     return __expf(GC);
 }
 
+// LDS of one two-wavefront prep unit.
+template <typename E, int DK, int DV>
+struct Prep2Lds {
+    __align__(16) char smem[Prep2Smem<E, DK, DV>::BYTES];
+    // per wavefront: running log-decay, beta e^G, e^{G_C - G}, beta of each token
+    __align__(16) float tab[2][4][64];
+};
+
+// One (head bh, chunk c) item on two wavefronts (w = 0, 1 of the unit), its
+// results written to the workspace block `blk`. Each of the two wavefronts
+// passes exactly one workgroup barrier.
 template <typename E, int DK, int DV, int KIND>
-__global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict__ q,
-                                                             const E* __restrict__ k,
-                                                             const E* __restrict__ v,
-                                                             const E* __restrict__ beta,
-                                                             const E* __restrict__ g,
-                                                             char* __restrict__ ws, int T,
-                                                             int nchunks) {
+__device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __restrict__ k,
+                                           const E* __restrict__ v, const E* __restrict__ beta,
+                                           const E* __restrict__ g, char* __restrict__ blk,
+                                           Prep2Lds<E, DK, DV>& lds, long bh, int c, int T, int w,
+                                           int lane) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef Prep2Smem<E, DK, DV> Sm;
     typedef typename Frag<E>::type F;
@@ -626,24 +641,18 @@ __global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict
     constexpr int KB = DK / 32, CT = DK / 16, VB = DV / 32, VT = DV / 16;
     constexpr int LDF = Sm::LDF, LDT = Sm::LDT;
 
-    __shared__ __align__(16) char smem[Sm::BYTES];
-    // per wavefront: running log-decay, beta e^G, e^{G_C - G}, beta of each token
-    __shared__ __align__(16) float tab[2][4][64];
+    char* smem = lds.smem;
+    float(*tab)[4][64] = lds.tab;
     float* As = reinterpret_cast<float*>(smem);   // A, then T's diagonal blocks in place
     E* Tw = reinterpret_cast<E*>(smem);           // T diag(beta e^G), once the inverse is done
     E* Tu = Tw + 64 * LDT;                        // T diag(beta)
     F* Vl = reinterpret_cast<F*>(smem + Sm::AT_BYTES);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int gq = lane >> 4, n = lane & 15;
-    const long item = blockIdx.x;
-    const int c = (int)(item % nchunks);
-    const long bh = item / nchunks;
     const int t0 = c * CHUNK;
     const int L = min(CHUNK, T - t0);
     const long tok0 = bh * T + t0;
 
-    char* blk = ws + item * Lw::BYTES;
     F* Wf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::W_OFF);
     F* Kf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::K_OFF);
     F* Af = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::A_OFF);
@@ -863,10 +872,25 @@ __global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict
     }
 }
 
+template <typename E, int DK, int DV, int KIND>
+__global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict__ q,
+                                                             const E* __restrict__ k,
+                                                             const E* __restrict__ v,
+                                                             const E* __restrict__ beta,
+                                                             const E* __restrict__ g,
+                                                             char* __restrict__ ws, int T,
+                                                             int nchunks) {
+    __shared__ Prep2Lds<E, DK, DV> lds;
+    const long item = blockIdx.x;
+    prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV>::BYTES, lds,
+                                item / nchunks, (int)(item % nchunks), T, (int)(threadIdx.x >> 6),
+                                (int)(threadIdx.x & 63));
+}
+
 // ---------------------------------------------------------------------------
 // Scan kernel
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV, int BV>
+template <typename E, int DK, int DV, int BV, int KIND>
 struct ScanOps {
     typedef typename Frag<E>::type F;
     typedef typename Vec4<E>::type V4;
@@ -880,7 +904,9 @@ struct ScanOps {
     F w[KB], q[KB], a[2], k[MTW][2];
     V16 qr[QR];
     V4 u[NT];
-    f32x4 gam[MTW], eg;
+    // chunk decay: KDA per key channel of the wave's rows (D-tile order),
+    // otherwise one value for the whole state (in gam[0][0])
+    f32x4 gam[KIND == KIND_KDA ? MTW : 1], eg;
 };
 
 // Raw buffer loads through a resource descriptor held in scalar registers:
@@ -895,9 +921,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, un
 }
 template <typename T>
 __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int voff) {
-    static_assert(sizeof(T) == 8 || sizeof(T) == 16 || sizeof(T) == 32, "8, 16 or 32 bytes");
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8 || sizeof(T) == 16 || sizeof(T) == 32,
+                  "4, 8, 16 or 32 bytes");
     T out;
-    if constexpr (sizeof(T) == 8) {
+    if constexpr (sizeof(T) == 4) {
+        const int x = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0);
+        __builtin_memcpy(&out, &x, 4);
+    } else if constexpr (sizeof(T) == 8) {
         const i32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0);
         __builtin_memcpy(&out, &x, 8);
     } else if constexpr (sizeof(T) == 16) {
@@ -926,10 +956,10 @@ struct ChunkSrc {
 // points of the previous-but-one chunk's step, so the wave never stalls on a
 // burst of loads waiting for the memory pipeline to accept them.
 template <int PART, int KIND, typename E, int DK, int DV, int BV>
-__device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV>& x, const ChunkSrc<E>& src,
+__device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV, KIND>& x, const ChunkSrc<E>& src,
                                                int vt, int w, int lane) {
     typedef WsLayout<E, DK, DV> Lw;
-    typedef ScanOps<E, DK, DV, BV> O;
+    typedef ScanOps<E, DK, DV, BV, KIND> O;
     typedef typename O::F F;
     typedef typename O::V4 V4;
     constexpr int FB = (int)sizeof(F);    // bytes of one fragment per lane
@@ -967,15 +997,19 @@ __device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV>& x, const 
 #pragma unroll
         for (int nt = 0; nt < O::NT; ++nt)
             x.u[nt] = buf_load<V4>(rb, (int)(Lw::U_OFF * ES) + (((vt * O::NT + nt) * 4 + w) * 64 + lane) * (int)sizeof(V4));
+        if (KIND == KIND_KDA) {
 #pragma unroll
-        for (int m = 0; m < O::MTW; ++m)
-            x.gam[m] = buf_load<f32x4>(rb, (int)Lw::GAM_BYTE_OFF + (16 * (w * O::MTW + m) + 4 * gq) * 4);
+            for (int m = 0; m < O::MTW; ++m)
+                x.gam[m] = buf_load<f32x4>(rb, (int)Lw::GAM_BYTE_OFF + (16 * (w * O::MTW + m) + 4 * gq) * 4);
+        } else {
+            x.gam[0][0] = buf_load<float>(rb, (int)Lw::GAM_BYTE_OFF);
+        }
         if (KIND != KIND_KDA) x.eg = buf_load<f32x4>(rb, (int)Lw::EG_BYTE_OFF + (16 * w + 4 * gq) * 4);
     }
 }
 
 template <int KIND, typename E, int DK, int DV, int BV>
-__device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV>& x, const ChunkSrc<E>& src, int vt,
+__device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV, KIND>& x, const ChunkSrc<E>& src, int vt,
                                           int w, int lane) {
     scan_load_part<0, KIND>(x, src, vt, w, lane);
     scan_load_part<1, KIND>(x, src, vt, w, lane);
@@ -992,14 +1026,14 @@ __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 // place; the operands of chunk c+2 (`nxt`, from block `nblk`) are loaded in
 // parts along the way; the output tile leaves through LDS as 16-byte rows.
 template <typename E, int DK, int DV, int KIND, int BV>
-__device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
-                                          ScanOps<E, DK, DV, BV>& nxt, const ChunkSrc<E>& nblk,
+__device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cur,
+                                          ScanOps<E, DK, DV, BV, KIND>& nxt, const ChunkSrc<E>& nblk,
                                           f32x4 (&S)[DK / 64][BV / 16],
                                           typename Frag<E>::type (*Sx)[BV / 16][64],
                                           typename Frag<E>::type (*Ux)[BV / 16][64], E* ob, E* qs,
                                           E* __restrict__ o, long bh, int T, int t0, int vt,
                                           int w, int lane) {
-    typedef ScanOps<E, DK, DV, BV> Ops;
+    typedef ScanOps<E, DK, DV, BV, KIND> Ops;
     typedef typename Ops::F F;
     typedef typename Ops::V4 V4;
     typedef typename Vec16<E>::type V16;
@@ -1070,7 +1104,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
 #pragma unroll
     for (int m = 0; m < MTW; ++m)
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) S[m][nt] *= cur.gam[m];
+        for (int nt = 0; nt < NT; ++nt) S[m][nt] *= KIND == KIND_KDA ? cur.gam[m] : cur.gam[0][0];
     sched_fence();
     scan_load_part<2, KIND>(nxt, nblk, vt, w, lane);
     lds_barrier();
@@ -1102,35 +1136,91 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV>& cur,
     }
 }
 
+// LDS of one scan workgroup.
 template <typename E, int DK, int DV, int KIND, int BV>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict__ ws,
-                                                         const E* __restrict__ q,
-                                                         const float* __restrict__ S0,
-                                                         E* __restrict__ o,
-                                                         float* __restrict__ S_final, int T,
-                                                         int nchunks, int BH) {
+struct ScanLds {
+    typedef typename Frag<E>::type F;
+    static constexpr int KB = DK / 32, NT = BV / 16;
+    static constexpr int LDO = BV + 16 / sizeof(E);   // output staging row (padded)
+    static constexpr int LDQ = DK + 16 / sizeof(E);   // Q row (padded)
+    F Sx[KB][NT][64];   // state as B-fragments (contraction over key channels)
+    F Ux[2][NT][64];    // U as B-fragments (contraction over tokens)
+    __align__(16) E Ob[4][16 * LDO];                              // per-wave output staging
+    __align__(16) E Qs[KIND == KIND_KDA ? 1 : 4][16 * LDQ];      // per-wave Q rows
+};
+
+// ---------------------------------------------------------------------------
+// Hand-off of workspace blocks from prep wavefronts to scan wavefronts inside
+// one launch. A block is published by each of its two producing wavefronts
+// with a 64-bit tag once that wavefront's stores to it have completed; the
+// tag is the launch's epoch combined with the producer's XCD number, and a
+// consumer accepts a block only if both tags equal the epoch combined with
+// its own XCD number. Producer and consumer therefore always share an XCD
+// and its L2, where completed stores are visible, so no cache write-back or
+// invalidation is needed: the consumer has not read the block's lines before
+// (the vector L1 starts every launch empty), so it cannot hold stale copies.
+// A tag left over from an earlier launch never matches (the epoch is new for
+// every launch). Waits are bounded: after about a second a wavefront marks
+// the launch as failed (it writes the epoch into an error word after the tags)
+// and stops waiting; the others stop waiting once they see that.
+// ---------------------------------------------------------------------------
+typedef unsigned long long u64;
+constexpr int SPIN_LIMIT = 1 << 20;
+
+__device__ __forceinline__ unsigned xcc_id() {
+    unsigned x;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+    return x & 15u;
+}
+__device__ __forceinline__ u64 xcc_tag(u64 epoch) { return epoch ^ ((u64)xcc_id() << 56); }
+__device__ __forceinline__ u64 flag_load(const u64* f) {
+    return __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Producer: after this wavefront's stores to the block have completed.
+__device__ __forceinline__ void publish(u64* f, u64 tag, int lane) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (lane == 0) __hip_atomic_store(f, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Consumer: (a, b) are the block's two tags as loaded earlier; poll until both
+// equal `tag` (or give up, see above).
+__device__ __forceinline__ void wait_block(const u64* f, u64 a, u64 b, u64 tag, u64* err, u64 epoch,
+                                        int lane) {
+    if (a == tag && b == tag) return;
+    for (int i = 0; i < SPIN_LIMIT; ++i) {
+        __builtin_amdgcn_s_sleep(8);
+        a = flag_load(f);
+        b = flag_load(f + 1);
+        if (a == tag && b == tag) return;
+        if ((i & 1023) == 1023 && flag_load(err) == epoch) return;
+    }
+    if (lane == 0) __hip_atomic_store(err, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Where the hand-off tags live: after the BH * nchunks workspace blocks, two
+// 64-bit tags per block, then the error word.
+template <typename E, int DK, int DV>
+__device__ __forceinline__ u64* block_tags(char* ws, long BH, int nchunks) {
+    return reinterpret_cast<u64*>(ws + BH * nchunks * WsLayout<E, DK, DV>::BYTES);
+}
+
+// The sequential scan of one (head bh, value tile vt) on four wavefronts.
+// SYNC: the chunk blocks are produced concurrently in the same launch and
+// each is waited for (tags at `tags`, expected value `tag`) before its
+// operands are loaded. RING: 3 (two chunks prefetched) or 2 (one chunk; fewer
+// registers held, which leaves the fused launch's register budget room).
+template <typename E, int DK, int DV, int KIND, int BV, bool SYNC, int RING>
+__device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* __restrict__ q,
+                                          const float* __restrict__ S0, E* __restrict__ o,
+                                          float* __restrict__ S_final, int T, int nchunks,
+                                          long bh, int vt, int w, int lane,
+                                          ScanLds<E, DK, DV, KIND, BV>& lds, const u64* tags,
+                                          u64 tag, u64* err, u64 epoch) {
     typedef WsLayout<E, DK, DV> Lw;
-    typedef ScanOps<E, DK, DV, BV> Ops;
-    typedef typename Ops::F F;
-    constexpr int NV = DV / BV, NT = Ops::NT, KB = Ops::KB, MTW = Ops::MTW;
-
-    // XCD-aware mapping: consecutive workgroups go to different XCDs
-    // (round-robin over 8); the NV value tiles of one head share an XCD so
-    // that their common operands (W, Q~, K~^T, attn) hit the same L2.
-    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-    const int vt = slot % NV;
-    const long bh = (long)(slot / NV) * 8 + xcd;
-    if (bh >= BH) return;
-
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    typedef ScanOps<E, DK, DV, BV, KIND> Ops;
+    constexpr int NT = Ops::NT, MTW = Ops::MTW;
     const int gq = lane >> 4, n = lane & 15;
-
-    __shared__ F Sx[KB][NT][64];   // state as B-fragments (contraction over key channels)
-    __shared__ F Ux[2][NT][64];    // U as B-fragments (contraction over tokens)
-    constexpr int LDO = BV + 16 / sizeof(E);
-    __shared__ __align__(16) E Ob[4][16 * LDO];   // per-wave output staging
-    constexpr int LDQ = DK + 16 / sizeof(E);
-    __shared__ __align__(16) E Qs[KIND == KIND_KDA ? 1 : 4][16 * LDQ];   // per-wave Q rows
 
     // fp32 state tile: rows 16*(w*MTW + m) + 4gq + e, columns vt*BV + 16nt + n
     f32x4 S[MTW][NT];
@@ -1151,29 +1241,71 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
             for (int nt = 0; nt < NT; ++nt) S[m][nt] = zero4();
     }
 
-    // Operands of chunks c + 1 and c + 2 are in flight while chunk c is
-    // processed (three register sets in rotation). Prefetches are
+    // The operands of the next RING - 1 chunks are in flight while chunk c is
+    // processed (RING register sets in rotation). Prefetches are
     // unconditional (the chunk index is clamped to the last chunk):
     // straight-line code lets the compiler wait for exactly the set in use
     // instead of draining every load in flight.
-    const char* wsh = ws + (long)bh * nchunks * Lw::BYTES;
+    const char* wsh = ws + bh * nchunks * Lw::BYTES;
     const int last = nchunks - 1;
     auto blk = [&](int cc) {
         const int c2 = min(cc, last);
-        return ChunkSrc<E>{wsh + (long)c2 * Lw::BYTES, q + ((long)bh * T + (long)c2 * CHUNK) * DK,
+        return ChunkSrc<E>{wsh + (long)c2 * Lw::BYTES, q + (bh * T + (long)c2 * CHUNK) * DK,
                            min(CHUNK, T - c2 * CHUNK)};
     };
-    Ops o0, o1, o2;
-    scan_load<KIND>(o0, blk(0), vt, w, lane);
-    scan_load<KIND>(o1, blk(1), vt, w, lane);
-    E* ob = Ob[w];
-    E* qs = Qs[KIND == KIND_KDA ? 0 : w];
-    for (int c = 0; c < nchunks; c += 3) {
-        scan_step<E, DK, DV, KIND, BV>(o0, o2, blk(c + 2), S, Sx, Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane);
-        if (c + 1 >= nchunks) break;
-        scan_step<E, DK, DV, KIND, BV>(o1, o0, blk(c + 3), S, Sx, Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
-        if (c + 2 >= nchunks) break;
-        scan_step<E, DK, DV, KIND, BV>(o2, o1, blk(c + 4), S, Sx, Ux, ob, qs, o, bh, T, (c + 2) * CHUNK, vt, w, lane);
+    // SYNC: the tags of the next block to be waited for are loaded one chunk
+    // step ahead, so a block that is already published costs no wait
+    u64 ta = 0, tb = 0;
+    auto tags_of = [&](int cc) { return tags + 2 * min(cc, last); };
+    auto ready = [&](int cc) {
+        if (SYNC) {
+            wait_block(tags_of(cc), ta, tb, tag, err, epoch, lane);
+            sched_fence();
+            ta = flag_load(tags_of(cc + 1));
+            tb = flag_load(tags_of(cc + 1) + 1);
+        }
+    };
+    if (SYNC) {
+        ta = flag_load(tags_of(0));
+        tb = flag_load(tags_of(0) + 1);
+    }
+    E* ob = lds.Ob[w];
+    E* qs = lds.Qs[KIND == KIND_KDA ? 0 : w];
+    if constexpr (RING == 2) {
+        // operands of chunk c + 1 in flight while chunk c is processed
+        Ops o0, o1;
+        ready(0);
+        scan_load<KIND>(o0, blk(0), vt, w, lane);
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), see below
+        for (int c = 0; c < nchunks; c += 2) {
+            ready(c + 1);
+            scan_step<E, DK, DV, KIND, BV>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane);
+            if (c + 1 >= nchunks) break;
+            ready(c + 2);
+            scan_step<E, DK, DV, KIND, BV>(o1, o0, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
+        }
+    } else {
+        // operands of chunks c + 1 and c + 2 in flight while chunk c is processed
+        Ops o0, o1, o2;
+        ready(0);
+        scan_load<KIND>(o0, blk(0), vt, w, lane);
+        ready(1);
+        scan_load<KIND>(o1, blk(1), vt, w, lane);
+        // Wait here for the sets loaded above: the loop then starts from the
+        // same outstanding loads on entry as on every later iteration, and the
+        // compiler waits in it for the set each step uses rather than (on the
+        // strength of the entry path) for nearly everything in flight.
+        __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+        for (int c = 0; c < nchunks; c += 3) {
+            ready(c + 2);
+            scan_step<E, DK, DV, KIND, BV>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane);
+            if (c + 1 >= nchunks) break;
+            ready(c + 3);
+            scan_step<E, DK, DV, KIND, BV>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
+            if (c + 2 >= nchunks) break;
+            ready(c + 4);
+            scan_step<E, DK, DV, KIND, BV>(o2, o1, blk(c + 4), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 2) * CHUNK, vt, w, lane);
+        }
     }
 
     if (S_final) {
@@ -1187,6 +1319,99 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
                     S_final[(bh * DK + row) * DV + col] = S[m][nt][e];
                 }
     }
+}
+
+template <typename E, int DK, int DV, int KIND, int BV>
+__global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict__ ws,
+                                                         const E* __restrict__ q,
+                                                         const float* __restrict__ S0,
+                                                         E* __restrict__ o,
+                                                         float* __restrict__ S_final, int T,
+                                                         int nchunks, int BH) {
+    constexpr int NV = DV / BV;
+    // XCD-aware mapping: consecutive workgroups go to different XCDs
+    // (round-robin over 8); the NV value tiles of one head share an XCD so
+    // that their common operands (W, Q~, K~^T, attn) hit the same L2.
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int vt = slot % NV;
+    const long bh = (long)(slot / NV) * 8 + xcd;
+    if (bh >= BH) return;
+    __shared__ ScanLds<E, DK, DV, KIND, BV> lds;
+    scan_body<E, DK, DV, KIND, BV, false, 3>(ws, q, S0, o, S_final, T, nchunks, bh, vt,
+                                          (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63), lds,
+                                          nullptr, 0, nullptr, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Fused prefill: prep and scan in one launch (Gated DeltaNet / DeltaNet).
+// ---------------------------------------------------------------------------
+// Workgroup b runs on XCD b % 8 (the hardware deals workgroups out to the
+// eight XCDs round-robin, starting over with every launch) and serves the
+// heads h = x, x + 8, ... of its XCD x. On each XCD the first NP workgroups
+// are prep workgroups: two units of two wavefronts, each unit taking the
+// XCD's (chunk, head) items in chunk-major order, so that every head's early
+// chunks come first. The workgroups after them are the scan workgroups of
+// the XCD's heads, one per (head, value tile), exactly as in the scan kernel,
+// except that each chunk block is waited for before it is loaded.
+// Workgroups start in index order, so every prep workgroup of an XCD has
+// started before the first scan workgroup there waits, and prep wavefronts
+// never wait on anything: every wait ends.
+template <typename E, int DK, int DV, int KIND, int BV>
+union FusedLds {
+    Prep2Lds<E, DK, DV> prep[2];
+    ScanLds<E, DK, DV, KIND, BV> scan;
+};
+
+template <typename E, int DK, int DV, int KIND, int BV>
+__global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict__ q,
+                                                             const E* __restrict__ k,
+                                                             const E* __restrict__ v,
+                                                             const E* __restrict__ beta,
+                                                             const E* __restrict__ g,
+                                                             char* __restrict__ ws,
+                                                             const float* __restrict__ S0,
+                                                             E* __restrict__ o,
+                                                             float* __restrict__ S_final, int T,
+                                                             int nchunks, int BH, int NP, u64 epoch) {
+    typedef WsLayout<E, DK, DV> Lw;
+    constexpr int NV = DV / BV;
+    __shared__ FusedLds<E, DK, DV, KIND, BV> lds;
+    const int xcd = blockIdx.x & 7, s = blockIdx.x >> 3;
+    const int nh = xcd < BH ? (BH - 1 - xcd) / 8 + 1 : 0;   // heads xcd, xcd + 8, ...
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    u64* tags = block_tags<E, DK, DV>(ws, BH, nchunks);
+    u64* err = tags + 2L * BH * nchunks;
+    const u64 tag = xcc_tag(epoch);
+
+    if (s < NP) {
+        const int unit = w >> 1, wu = w & 1;
+        const long total = (long)nh * nchunks;
+        for (long m0 = 2L * s; m0 < total; m0 += 2L * NP) {
+            const long m = m0 + unit;
+            if (m < total) {
+                const int c = (int)(m / nh);
+                const long bh = xcd + 8L * (m % nh);
+                // a lane index the compiler cannot see to be the same in every
+                // iteration, so that it keeps the item's lane-dependent offsets
+                // and constants inside the loop instead of holding them in
+                // registers across it
+                int ln;
+                asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+                prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + (bh * nchunks + c) * Lw::BYTES,
+                                            lds.prep[unit], bh, c, T, wu, ln);
+                publish(tags + 2 * (bh * nchunks + c) + wu, tag, ln);
+            } else {
+                lds_barrier();   // the item's one barrier, passed with the other unit
+            }
+            lds_barrier();   // this item's LDS reads are done before the next item writes
+        }
+        return;
+    }
+    const int slot = s - NP, vt = slot % NV, i = slot / NV;
+    if (i >= nh) return;
+    const long bh = xcd + 8L * i;
+    scan_body<E, DK, DV, KIND, BV, true, 2>(ws, q, S0, o, S_final, T, nchunks, bh, vt, w, lane, lds.scan,
+                                         tags + 2 * bh * nchunks, tag, err, epoch);
 }
 
 // ---------------------------------------------------------------------------
@@ -1205,9 +1430,11 @@ static int device_cu_count() {
     return n;
 }
 
+// The chunk blocks, then the hand-off tags of the fused launch (two 64-bit
+// words per block) and its error word, padded to 256 bytes.
 template <typename E, int D>
 static size_t ws_bytes_t(long long BH, long long nchunks) {
-    return (size_t)(BH * nchunks * WsLayout<E, D, D>::BYTES);
+    return (size_t)(BH * nchunks * WsLayout<E, D, D>::BYTES + (BH * nchunks * 16 + 8 + 255) / 256 * 256);
 }
 
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype) {
@@ -1215,6 +1442,12 @@ size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtyp
     const long long nchunks = (T + CHUNK - 1) / CHUNK;
     if (dtype == DT_BF16) return dk == 128 ? ws_bytes_t<bf16, 128>(BH, nchunks) : ws_bytes_t<bf16, 64>(BH, nchunks);
     return dk == 128 ? ws_bytes_t<float, 128>(BH, nchunks) : ws_bytes_t<float, 64>(BH, nchunks);
+}
+
+// Value tile width of the scan for BH heads (shared by the scan and the fused launch).
+template <int D>
+static int scan_bv(int BH) {
+    return ((long)BH * (D / 32) >= 256 || D == 64) ? 32 : 16;
 }
 
 template <typename E, int D, int KIND>
@@ -1246,7 +1479,7 @@ static hipError_t scan_t(const void* q, const float* S0, void* o, float* S_final
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const long groups = ((long)BH + 7) / 8;
     // 32-column value tiles unless that leaves most of the 256 CUs idle
-    if ((long)BH * (D / 32) >= 256 || D == 64) {
+    if (scan_bv<D>(BH) == 32) {
         constexpr int BV = 32;
         const long nblk = groups * 8 * (D / BV);
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
@@ -1257,6 +1490,36 @@ static hipError_t scan_t(const void* q, const float* S0, void* o, float* S_final
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
                            st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH);
     }
+    return hipGetLastError();
+}
+
+// A new 64-bit epoch per fused launch: a random per-process prefix and a
+// launch counter.
+static u64 next_epoch() {
+    static const u64 salt = [] {
+        std::random_device rd;
+        return ((u64)rd() << 32) | 1u;
+    }();
+    static std::atomic<unsigned> counter{0};
+    return salt ^ (u64)counter.fetch_add(1, std::memory_order_relaxed);
+}
+
+// Fused launch when every XCD's scan workgroups leave room for at least 16
+// prep workgroups among the two workgroups per CU that can be resident.
+template <typename E, int D, int KIND, int BV>
+static hipError_t fused_t(const void* q, const void* k, const void* v, const void* beta,
+                          const void* g, const float* S0, void* o, float* S_final, void* ws, int BH,
+                          int T, hipStream_t st) {
+    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    const int per_xcd = 2 * device_cu_count() / 8;
+    const int ns = (BH + 7) / 8 * (D / BV);   // scan workgroups of the busiest XCD
+    const long items = (long)(BH + 7) / 8 * nchunks;
+    int np = per_xcd - ns;
+    if (np < 16) return hipErrorNotSupported;
+    if ((long)np > (items + 1) / 2) np = (int)((items + 1) / 2);
+    hipLaunchKernelGGL((chunk_fused_kernel<E, D, D, KIND, BV>), dim3((unsigned)(8 * (np + ns))), dim3(256),
+                       0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
+                       (char*)ws, S0, (E*)o, S_final, T, nchunks, BH, np, next_epoch());
     return hipGetLastError();
 }
 
@@ -1299,6 +1562,57 @@ hipError_t launch_chunk_scan(int kind, int dtype, const void* q, const float* S0
                          : scan_kind<bf16, 64>(kind, q, S0, o, S_final, ws, BH, T, st);
     return dk == 128 ? scan_kind<float, 128>(kind, q, S0, o, S_final, ws, BH, T, st)
                      : scan_kind<float, 64>(kind, q, S0, o, S_final, ws, BH, T, st);
+}
+
+// One-launch prefill where it exists: bf16, DeltaNet or Gated DeltaNet, and
+// few enough heads that every XCD keeps room for at least 16 prep workgroups.
+template <typename E, int D>
+static hipError_t fused_kind(int kind, const void* q, const void* k, const void* v, const void* beta,
+                             const void* g, const float* S0, void* o, float* S_final, void* ws,
+                             int BH, int T, hipStream_t st) {
+    if constexpr (sizeof(E) != 2) {
+        return hipErrorNotSupported;
+    } else {
+        if (kind == KIND_KDA) return hipErrorNotSupported;
+        const bool wide = scan_bv<D>(BH) == 32;
+        if (kind == KIND_GATED)
+            return wide ? fused_t<E, D, KIND_GATED, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st)
+                        : fused_t<E, D, KIND_GATED, 16>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st);
+        return wide ? fused_t<E, D, KIND_DELTANET, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st)
+                    : fused_t<E, D, KIND_DELTANET, 16>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st);
+    }
+}
+
+// The one-launch form pays about one prep item's latency (some 10 us) before
+// the scan can start, against the whole prep phase and the gap between two
+// launches saved. Measured at d = 128 with 16 to 32 heads: level with the two
+// launches at 32 chunks per sequence, 8 to 14 % faster from 64 chunks on.
+constexpr int FUSED_MIN_CHUNKS = 64;
+
+template <typename E, int D>
+static hipError_t fwd_t(int kind, const void* q, const void* k, const void* v, const void* beta,
+                        const void* g, const float* S0, void* o, float* S_final, void* ws, int BH,
+                        int T, int mode, hipStream_t st) {
+    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    if (mode == FWD_FUSED || (mode == FWD_AUTO && nchunks >= FUSED_MIN_CHUNKS)) {
+        const hipError_t e = fused_kind<E, D>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, st);
+        if (e != hipErrorNotSupported || mode == FWD_FUSED) return e;
+    }
+    hipError_t e = prep_kind<E, D>(kind, q, k, v, beta, g, ws, BH, T, st);
+    if (e != hipSuccess) return e;
+    return scan_kind<E, D>(kind, q, S0, o, S_final, ws, BH, T, st);
+}
+
+hipError_t launch_chunk_fwd(int kind, int dtype, const void* q, const void* k, const void* v,
+                            const void* beta, const void* g, const float* S0, void* o,
+                            float* S_final, void* ws, int BH, int T, int dk, int dv, int mode,
+                            hipStream_t st) {
+    (void)dv;
+    if (dtype == DT_BF16)
+        return dk == 128 ? fwd_t<bf16, 128>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st)
+                         : fwd_t<bf16, 64>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st);
+    return dk == 128 ? fwd_t<float, 128>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st)
+                     : fwd_t<float, 64>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st);
 }
 
 }  // namespace dn

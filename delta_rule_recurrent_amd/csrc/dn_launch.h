@@ -32,6 +32,16 @@ hipError_t launch_chunk_scan(int kind, int dtype, const void* q, const float* S0
                              float* S_final, const void* workspace, int BH, int T, int dk, int dv,
                              hipStream_t stream);
 
+// Whole chunkwise prefill. FWD_TWO: the two phases above in order.
+// FWD_FUSED: one launch (prep and scan workgroups together), or
+// hipErrorNotSupported where that form does not exist. FWD_AUTO: the fused
+// launch for long sequences where it exists, the two phases otherwise.
+enum FwdMode { FWD_TWO = 0, FWD_FUSED = 1, FWD_AUTO = 2 };
+hipError_t launch_chunk_fwd(int kind, int dtype, const void* q, const void* k, const void* v,
+                            const void* beta, const void* g, const float* S0, void* o,
+                            float* S_final, void* workspace, int BH, int T, int dk, int dv,
+                            int mode, hipStream_t stream);
+
 // Workspace bytes of the chunkwise prefill (per call).
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype);
 

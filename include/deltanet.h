@@ -48,7 +48,8 @@ typedef enum dn_status {
     DN_OK = 0,
     DN_EINVAL = -1,     /* a required pointer is NULL or misaligned, B/H < 1, T < 0,
                            an unknown dtype, or more than 2^24 heads / 2^31-1 chunks */
-    DN_ENOTSUP = -2,    /* d_k, d_v outside {64, 128} or d_k != d_v */
+    DN_ENOTSUP = -2,    /* d_k, d_v outside {64, 128} or d_k != d_v, or no such form
+                           (see dn_kda_chunk_fwd, dn_chunk_fwd_fused) */
     DN_EWORKSPACE = -3, /* workspace NULL or smaller than dn_chunk_fwd_workspace() */
     DN_EHIP = -4        /* the HIP runtime reported an error at launch */
 } dn_status;
@@ -62,11 +63,12 @@ const char* dn_strerror(int status);
 int dn_version(void);
 
 /*
- * Workspace bytes that dn_chunk_fwd and dn_kda_chunk_fwd need for these sizes
- * (0 when T == 0; (size_t)0 also for invalid sizes, which the entry points
- * then reject). The workspace holds per-chunk intermediates of the UT/WY form
- * and is fully overwritten by every call; its contents between calls are
- * unspecified.
+ * Workspace bytes that dn_chunk_fwd, dn_chunk_fwd_fused and dn_kda_chunk_fwd
+ * need for these sizes (0 when T == 0; (size_t)0 also for invalid sizes, which
+ * the entry points then reject). The workspace holds one block of per-chunk
+ * intermediates of the UT/WY form per (head, chunk), then the hand-off words
+ * of the one-launch form. It needs no initialisation, its contents between
+ * calls are unspecified, and calls that overlap in time must not share it.
  */
 size_t dn_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int dtype);
 
@@ -92,6 +94,23 @@ int dn_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
                  const void* g, const float* S0, void* o, float* S_final,
                  int B, int H, int T, int dk, int dv, int dtype,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same prefill as dn_chunk_fwd, always as ONE kernel launch in which the
+ * chunk-parallel phase and the sequential scan run concurrently: prep
+ * workgroups produce the workspace blocks chunk by chunk while scan
+ * workgroups on the same XCD consume them (a block is handed over through
+ * 64-bit tags in the workspace, see the hand-off notes in chunk.hip). Same
+ * arguments, results bitwise equal to dn_chunk_fwd. Returns DN_ENOTSUP where
+ * this form does not exist: dtype other than bf16, or more heads than leave
+ * room for the prep workgroups (B*H above about 48 per 8 heads' worth of
+ * value tiles; dn_chunk_fwd then runs the two phases). dn_chunk_fwd itself
+ * uses this form for sequences of 64 chunks (4096 tokens) and more.
+ */
+int dn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* beta,
+                       const void* g, const float* S0, void* o, float* S_final,
+                       int B, int H, int T, int dk, int dv, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * KDA chunkwise prefill: as dn_chunk_fwd but g is REQUIRED and holds one

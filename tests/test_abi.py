@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = _lib.lib()
-    assert lib.dn_version() >= 1
+    assert lib.dn_version() >= 2   # workspace holds the one-launch hand-off words since 2
     for code in (0, -1, -2, -3, -4, 7):
         s = lib.dn_strerror(code)
         assert isinstance(s, bytes) and len(s) > 0
@@ -49,9 +49,14 @@ def test_workspace_size_function():
     ws = lib.dn_chunk_fwd_workspace
     assert ws(1, 1, 0, 64, 64, 0) == 0
     assert ws(1, 1, 64, 64, 64, 0) > 0
+    # one block per (head, chunk), then two 64-bit hand-off tags per block and
+    # an 8-byte error word, padded to 256 bytes
+    block = ws(1, 1, 128, 128, 128, 1) - ws(1, 1, 64, 128, 128, 1)
+    assert block > 0 and block % 256 == 0
+    assert ws(1, 1, 64, 128, 128, 1) == block + 256
     a = ws(4, 8, 2048, 128, 128, 1)
-    assert a == 32 * ws(1, 1, 2048, 128, 128, 1)
-    assert ws(1, 1, 65, 128, 128, 1) == 2 * ws(1, 1, 64, 128, 128, 1)
+    assert a == 32 * 32 * block + (32 * 32 * 16 + 8 + 255) // 256 * 256
+    assert ws(1, 1, 65, 128, 128, 1) == ws(1, 1, 128, 128, 128, 1)
     assert ws(1, 1, 64, 96, 96, 1) == 0     # unsupported head size
     assert ws(0, 1, 64, 64, 64, 1) == 0
     assert ws(1, 1, 64, 64, 64, 5) == 0     # unknown dtype
@@ -67,7 +72,7 @@ def _chunk(fn, **kw):
                                     args["ws_bytes"], args["stream"])
 
 
-@pytest.mark.parametrize("fn", ["dn_chunk_fwd", "dn_kda_chunk_fwd"])
+@pytest.mark.parametrize("fn", ["dn_chunk_fwd", "dn_chunk_fwd_fused", "dn_kda_chunk_fwd"])
 def test_chunk_validation(fn):
     E, N, W = _lib.DN_EINVAL, _lib.DN_ENOTSUP, _lib.DN_EWORKSPACE
     for name in ("q", "k", "v", "beta", "o"):
@@ -89,6 +94,9 @@ def test_chunk_validation(fn):
     if fn == "dn_kda_chunk_fwd":
         assert _chunk(fn, g=None) == E               # KDA needs its per-channel decay
         assert _chunk(fn, dtype=0, dk=128, dv=128) == N
+    if fn == "dn_chunk_fwd_fused":
+        assert _chunk(fn, dtype=0) == N              # the one-launch form is bf16 only
+        assert _chunk(fn, dtype=0, q=None) == E      # argument errors still come first
 
 
 def _rec(fn, **kw):

@@ -177,11 +177,13 @@ def test_decode_equals_one_token_prefill(kind):
 
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("T", [32 * 64 + 37, 48 * 64])
+@pytest.mark.parametrize("T", [32 * 64 + 37, 48 * 64, 64 * 64 + 5])
 def test_long_prefill(kind, dtype, T):
     """Sequences of 32 chunks and more, with a ragged last chunk: same results as
     the oracle with a start state, bitwise the same with the state updated in
-    place, and bitwise equal to calling the two phases one after the other."""
+    place, and bitwise equal to calling the two phases one after the other
+    (from 64 chunks on, chunk_fwd runs bf16 DeltaNet / Gated DeltaNet as one
+    launch)."""
     if not _supported(kind, dtype, 128, "chunk"):
         pytest.skip("fp32 KDA at d = 128 has no chunked form")
     dn = _dn()
@@ -207,3 +209,55 @@ def test_long_prefill(kind, dtype, T):
     assert eo <= tol and es <= tol
     assert torch.equal(o2, o) and torch.equal(Sip, S)
     assert torch.equal(o3, o) and torch.equal(S3, S)
+
+
+@pytest.mark.parametrize("kind", ["deltanet", "gated"])
+@pytest.mark.parametrize("BH", [(1, 2), (3, 5), (4, 8)])
+def test_fused_handoff(kind, BH):
+    """The one-launch prefill (prep and scan workgroups handing chunk blocks
+    over through tags in the workspace) on short sequences: bitwise equal to
+    the two phases, and
+    the tags show every block published by both of its wavefronts, from the
+    XCD its consumers run on (workgroup b on XCD b % 8, head h served by XCD
+    h % 8), with a new epoch per launch and the error word untouched."""
+    dn = _dn()
+    B, H = BH
+    T = 5 * 64 + 9
+    nch = (T + 63) // 64
+    say("fused hand-off", kind, B, H, T)
+    inp = make(kind, B, H, T, 128, "bf16", seed=29, s0_std=0.5)
+    d = to_dev(inp)
+    dt = d["q"].dtype
+    nbytes = dn.workspace_bytes(B, H, T, 128, 128, dt)
+    block = dn.workspace_bytes(1, 1, 128, 128, 128, dt) - dn.workspace_bytes(1, 1, 64, 128, 128, dt)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    o, S = dn.chunk_fwd_fused(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    tail = ws[B * H * nch * block:].cpu()
+    tags1 = tail[:B * H * nch * 16].view(torch.int64).view(B * H, nch, 2).clone()
+    err = int(tail[B * H * nch * 16:B * H * nch * 16 + 8].view(torch.int64)[0])
+    assert err == 0
+    assert torch.equal(tags1[:, :, 0], tags1[:, :, 1])
+    t = tags1[:, :, 0].numpy().astype(np.uint64)
+    low = t & np.uint64((1 << 56) - 1)
+    assert (low == low[0, 0]).all() and low[0, 0] != 0
+    # the XCD number sits XORed into bits 56..59 of the tag (over the epoch's
+    # own bits there), so tags of heads h and 0 differ there by h % 8
+    xcc = ((t >> np.uint64(56)) & np.uint64(15)) ^ ((t[0, 0] >> np.uint64(56)) & np.uint64(15))
+    for h in range(B * H):
+        assert (xcc[h] == np.uint64(h % 8)).all(), (h, xcc[h])
+
+    ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o3, S3 = torch.empty_like(o), torch.empty_like(S)
+    dn.chunk_prep(d["q"], d["k"], d["v"], d["beta"], d["g"], ws2)
+    dn.chunk_scan(d["q"], o3, ws2, d["S0"], S3)
+    o4, S4 = dn.chunk_fwd_fused(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    tags2 = ws[B * H * nch * block:].cpu()[:B * H * nch * 16].view(torch.int64).view(B * H, nch, 2)
+    assert not (tags2 == tags1).any()
+    assert torch.equal(o3, o) and torch.equal(S3, S)
+    assert torch.equal(o4, o) and torch.equal(S4, S)
+    o_ref, S_ref = oracle_prefill(inp)
+    eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
+    say("  err o %.3e  S %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
