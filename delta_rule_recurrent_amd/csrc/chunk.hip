@@ -132,6 +132,24 @@ __device__ __forceinline__ void tile_store(const TileRegs<E, D>& r, E* rows, int
     }
 }
 
+// Write a loaded tile into LDS as fp32 rows[64][ldr].
+template <typename E, int D>
+__device__ __forceinline__ void tile_store_f32(const TileRegs<E, D>& r, float* rows, int ldr,
+                                               int tid) {
+    typedef TileRegs<E, D> R;
+#pragma unroll
+    for (int it = 0; it < R::ITER; ++it) {
+        const int idx = tid + 256 * it;
+        if (idx >= 16 * R::NV) break;
+        const int tq = idx / R::NV, cv = idx % R::NV;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < R::VEC; ++e)
+                rows[(4 * tq + u) * ldr + cv * R::VEC + e] = to_f32(r.x[it][u][e]);
+    }
+}
+
 // KDA: fragment of a row-major [64][ld] token tile (rows = tokens, contraction
 // = key channels) with each value multiplied by exp(sgn * (G[row][c] - G[ref][c])).
 template <typename E>
@@ -233,7 +251,7 @@ void chunk_prep_kernel(const E* __restrict__ q,
     // loaded into registers while the current one is computed, and written to
     // LDS when it is done. Prefetches are unconditional (the item index is
     // clamped to the last item).
-    TileRegs<E, DK> rk, rq;
+    TileRegs<E, DK> rk, rq, rg;   // rg: KDA's per-channel log-decay
     TileRegs<E, DV> rv;
     float pb = 0.f, pg = 0.f;   // beta and log-decay of token `lane` (wave 0)
     auto fetch = [&](int it) {
@@ -243,6 +261,7 @@ void chunk_prep_kernel(const E* __restrict__ q,
         tile_load<E, DK>(rk, k + ftok * DK, fL, tid);
         tile_load<E, DK>(rq, q + ftok * DK, fL, tid);
         tile_load<E, DV>(rv, v + ftok * DV, fL, tid);
+        if (KDA) tile_load<E, DK>(rg, g + ftok * DK, fL, tid);
         if (w == 0) {
             const long tk = ftok + min(lane, fL - 1);
             pb = to_f32(beta[tk]);
@@ -283,22 +302,28 @@ void chunk_prep_kernel(const E* __restrict__ q,
             for (int ch = lane; ch < DK; ch += 64) gam[ch] = __expf(GC);
         }
     } else {
-        // one thread per key channel, sequential over the 64 tokens (tokens
-        // past the end of the sequence add nothing)
-        for (int ch = tid; ch < DK; ch += 256) {
-            float acc = 0.f;
-            for (int t = 0; t < CHUNK; ++t) {
-                if (t < L) acc += to_f32(g[(tok0 + t) * DK + ch]);
-                Gk[t * LDG + ch] = acc;
-            }
-            gam[ch] = __expf(acc);
-        }
+        // the log-decay tile (prefetched with K, Q, V; rows past the end of
+        // the sequence are zero) as fp32 rows, summed over tokens below
+        tile_store_f32<E, DK>(rg, Gk, LDG, tid);
     }
     tile_store<E, DK, true, true>(rk, Ks, LDK, KsT, LDT, tid);
     tile_store<E, DK, true, false>(rq, Qs, LDK, nullptr, 0, tid);
     tile_store<E, DV, false, true>(rv, nullptr, 0, VsT, LDT, tid);
     lds_barrier();
     fetch((int)min((long)item + gridDim.x, (long)nitems - 1));
+    if (KDA) {
+        // running sum over the chunk's tokens, in place, one thread per key channel
+        for (int ch = tid; ch < DK; ch += 256) {
+            float acc = 0.f;
+#pragma unroll 16
+            for (int t = 0; t < CHUNK; ++t) {
+                acc += Gk[t * LDG + ch];
+                Gk[t * LDG + ch] = acc;
+            }
+            gam[ch] = __expf(acc);
+        }
+        lds_barrier();
+    }
 
     // ---- 2. attn -> A-fragments, Q~ -> A-fragments; raw K K^T kept in registers
     // Wave w owns token tile w: rows i in [16w, 16w+16) of A and of attn.
