@@ -12,15 +12,15 @@ namespace dn {
 
 // ---------------------------------------------------------------------------
 // Decode step. HBM-bound: each fp32 state element is read once and written
-// once. One 256-thread workgroup per (sequence, head); thread t owns a column
-// quad (4 consecutive value columns, one 16-byte vector per row) on the rows
-// rg, rg + RG, rg + 2RG, ... so that a wavefront's load covers two whole
-// adjacent rows (1 KiB contiguous). The column sums p = S~^T k and r = S~^T q
-// are reduced across row groups with lane shuffles and one LDS exchange, and
-// the read-out uses o = S_new^T q = r + u (k . q), so the state is streamed
-// through registers exactly once.
+// once. NSPLIT 256-thread workgroups per (sequence, head), each over DV/NSPLIT
+// value columns; thread t owns a column quad (4 consecutive value columns, one
+// 16-byte vector per row) on the rows rg, rg + RG, rg + 2RG, ... The column
+// sums p = S~^T k and r = S~^T q are reduced across row groups with lane
+// shuffles and one LDS exchange, and the read-out uses
+// o = S_new^T q = r + u (k . q), so the state is streamed through registers
+// exactly once.
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV, int KIND>
+template <typename E, int DK, int DV, int KIND, int NSPLIT>
 __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ q,
                                                           const E* __restrict__ k,
                                                           const E* __restrict__ v,
@@ -28,17 +28,19 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ 
                                                           const E* __restrict__ g,
                                                           float* __restrict__ S,
                                                           E* __restrict__ o) {
-    constexpr int CQ = DV / 4;     // column quads per row
-    constexpr int RG = 256 / CQ;   // row groups
-    constexpr int RPT = DK / RG;   // rows per thread
+    constexpr int CW = DV / NSPLIT;   // value columns of this workgroup
+    constexpr int CQ = CW / 4;        // column quads per row
+    constexpr int RG = 256 / CQ;      // row groups
+    constexpr int RPT = DK / RG;      // rows per thread
     static_assert(DK % RG == 0 && CQ <= WAVE, "unsupported head size");
     typedef typename Vec4<E>::type V4;
 
-    const long bh = blockIdx.x;
+    const long bh = blockIdx.x / NSPLIT;
+    const int col0 = (int)(blockIdx.x % NSPLIT) * CW;
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
     const int cq = t % CQ, rg = t / CQ;
 
-    float* Sp = S + bh * DK * DV + 4 * cq;
+    float* Sp = S + bh * DK * DV + col0 + 4 * cq;
     f32x4 s[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const f32x4*>(Sp + (rg + RG * i) * DV);
@@ -51,7 +53,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ 
         sq[t] = to_f32(q[bh * DK + t]);
         if (KIND == KIND_KDA) sa[t] = __expf(to_f32(g[bh * DK + t]));
     }
-    const V4 vraw = *reinterpret_cast<const V4*>(v + bh * DV + 4 * cq);
+    const V4 vraw = *reinterpret_cast<const V4*>(v + bh * DV + col0 + 4 * cq);
     const float b = to_f32(beta[bh]);
     const float a = (KIND == KIND_GATED) ? __expf(to_f32(g[bh])) : 1.0f;
     __syncthreads();
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ 
         V4 ow;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ow[e] = from_f32<E>(ov[e]);
-        *reinterpret_cast<V4*>(o + bh * DV + 4 * cq) = ow;
+        *reinterpret_cast<V4*>(o + bh * DV + col0 + 4 * cq) = ow;
     }
 }
 
@@ -216,13 +218,18 @@ static hipError_t decode_t(int kind, const void* q, const void* k, const void* v
     const E *q_ = (const E*)q, *k_ = (const E*)k, *v_ = (const E*)v, *b_ = (const E*)beta,
             *g_ = (const E*)g;
     E* o_ = (E*)o;
-    dim3 grid(BH), block(256);
+    // four workgroups per state, one quarter of the value columns each (the
+    // column sums are independent per column): finer work units keep more of
+    // the state stream in flight per CU (measured 80.9 -> 78.6 us per step at
+    // 256 x 16 heads, d = 128)
+    constexpr int NS = 4;
+    dim3 grid((unsigned)((long)BH * NS)), block(256);
     if (kind == KIND_DELTANET)
-        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_DELTANET>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_);
+        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_DELTANET, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_);
     else if (kind == KIND_GATED)
-        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_GATED>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_);
+        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_GATED, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_);
     else
-        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_KDA>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_);
+        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_KDA, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_);
     return hipGetLastError();
 }
 
