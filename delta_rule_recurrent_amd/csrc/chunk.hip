@@ -152,18 +152,25 @@ __device__ __forceinline__ void tile_store_f32(const TileRegs<E, D>& r, float* r
 
 // KDA: fragment of a row-major [64][ld] token tile (rows = tokens, contraction
 // = key channels) with each value multiplied by exp(sgn * (G[row][c] - G[ref][c])).
+// The lane's two runs of 4 channels (4g .. 4g+3 and 16+4g .. 16+4g+3 of the
+// block) are read as vectors: two 4-element reads of M, four 16-byte reads of
+// G (row and reference row; ld, ldg, k0 keep them aligned).
 template <typename E>
 __device__ __forceinline__ typename Frag<E>::type frag_rows_decay(const E* M, int ld, const float* G,
                                                                   int ldg, int row0, int k0,
                                                                   int lane, int ref, float sgn) {
+    typedef typename Vec4<E>::type V4;
     const int g = lane >> 4, r = lane & 15;
     const int row = row0 + r;
     typename Frag<E>::type f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const int c = k0 + (j < 4 ? 4 * g + j : 16 + 4 * g + (j - 4));
-        const float e = __expf(sgn * (G[row * ldg + c] - G[ref * ldg + c]));
-        f[j] = from_f32<E>(to_f32(M[row * ld + c]) * e);
+    for (int h = 0; h < 2; ++h) {
+        const int c = k0 + 16 * h + 4 * g;
+        const V4 m = *reinterpret_cast<const V4*>(M + row * ld + c);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(G + row * ldg + c);
+        const f32x4 gf = *reinterpret_cast<const f32x4*>(G + ref * ldg + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[4 * h + j] = from_f32<E>(to_f32(m[j]) * __expf(sgn * (gr[j] - gf[j])));
     }
     return f;
 }
@@ -311,17 +318,29 @@ void chunk_prep_kernel(const E* __restrict__ q,
     tile_store<E, DV, false, true>(rv, nullptr, 0, VsT, LDT, tid);
     lds_barrier();
     fetch((int)min((long)item + gridDim.x, (long)nitems - 1));
-    if (KDA) {
-        // running sum over the chunk's tokens, in place, one thread per key channel
-        for (int ch = tid; ch < DK; ch += 256) {
-            float acc = 0.f;
-#pragma unroll 16
-            for (int t = 0; t < CHUNK; ++t) {
-                acc += Gk[t * LDG + ch];
-                Gk[t * LDG + ch] = acc;
-            }
-            gam[ch] = __expf(acc);
-        }
+    if constexpr (KDA) {
+        // running sum over the chunk's tokens, in place: 256 / DK threads per
+        // key channel, each over a run of consecutive tokens held in registers
+        // (all of its LDS reads in flight at once); the runs' totals are
+        // passed on through LDS
+        constexpr int SPL = 256 / DK, RUN = CHUNK / SPL;
+        static_assert(256 % DK == 0 && CHUNK % SPL == 0, "token runs");
+        __shared__ float gtot[SPL][DK];
+        const int ch = tid % DK, part = tid / DK;
+        float run[RUN];
+#pragma unroll
+        for (int t = 0; t < RUN; ++t) run[t] = Gk[(part * RUN + t) * LDG + ch];
+#pragma unroll
+        for (int t = 1; t < RUN; ++t) run[t] += run[t - 1];
+        gtot[part][ch] = run[RUN - 1];
+        lds_barrier();
+        float carry = 0.f;
+#pragma unroll
+        for (int p2 = 0; p2 < SPL - 1; ++p2)
+            if (p2 < part) carry += gtot[p2][ch];
+#pragma unroll
+        for (int t = 0; t < RUN; ++t) Gk[(part * RUN + t) * LDG + ch] = run[t] + carry;
+        if (part == SPL - 1) gam[ch] = __expf(run[RUN - 1] + carry);
         lds_barrier();
     }
 
@@ -383,9 +402,12 @@ void chunk_prep_kernel(const E* __restrict__ q,
                 F f;
                 const int row = 16 * w + n;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int cc = 32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + (j - 4));
-                    f[j] = from_f32<E>(to_f32(Qs[row * LDK + cc]) * __expf(Gk[row * LDG + cc]));
+                for (int h = 0; h < 2; ++h) {
+                    const int cc = 32 * kb + 16 * h + 4 * gq;
+                    const V4 m = *reinterpret_cast<const V4*>(Qs + row * LDK + cc);
+                    const f32x4 gr = *reinterpret_cast<const f32x4*>(Gk + row * LDG + cc);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) f[4 * h + j] = from_f32<E>(to_f32(m[j]) * __expf(gr[j]));
                 }
                 reinterpret_cast<F*>(Qf)[(w * (DK / 32) + kb) * 64 + lane] = f;
             }
@@ -412,13 +434,21 @@ void chunk_prep_kernel(const E* __restrict__ q,
             As[i * LDF + j] = val;
         }
     if (KDA) {
-        // X^T = (e^G K)^T; K^T -> K~^T = (e^{G_C - G} K)^T in place
-        for (int idx = tid; idx < DK * 64; idx += 256) {
-            const int ch = idx / 64, t = idx % 64;
-            const float kv = to_f32(KsT[ch * LDT + t]);
-            const float Gt = Gk[t * LDG + ch], GC = Gk[63 * LDG + ch];
-            XsT[ch * LDT + t] = from_f32<E>(kv * __expf(Gt));
-            KsT[ch * LDT + t] = from_f32<E>(kv * __expf(GC - Gt));
+        // X^T = (e^G K)^T; K^T -> K~^T = (e^{G_C - G} K)^T in place, four
+        // consecutive tokens of one key channel per thread and pass
+        for (int idx = tid; idx < DK * 16; idx += 256) {
+            const int ch = idx / 16, t4 = 4 * (idx % 16);
+            const V4 kv = *reinterpret_cast<const V4*>(KsT + ch * LDT + t4);
+            const float GC = Gk[63 * LDG + ch];
+            V4 xo, ko;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float Gt = Gk[(t4 + u) * LDG + ch];
+                xo[u] = from_f32<E>(to_f32(kv[u]) * __expf(Gt));
+                ko[u] = from_f32<E>(to_f32(kv[u]) * __expf(GC - Gt));
+            }
+            *reinterpret_cast<V4*>(XsT + ch * LDT + t4) = xo;
+            *reinterpret_cast<V4*>(KsT + ch * LDT + t4) = ko;
         }
     }
     lds_barrier();
