@@ -1080,14 +1080,14 @@ __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 // S = gamma S + K~^T U. S (fp32, MFMA accumulator layout) is updated in
 // place; the operands of chunk c+2 (`nxt`, from block `nblk`) are loaded in
 // parts along the way; the output tile leaves through LDS as 16-byte rows.
-template <typename E, int DK, int DV, int KIND, int BV>
+template <typename E, int DK, int DV, int KIND, int BV, bool PF>
 __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cur,
                                           ScanOps<E, DK, DV, BV, KIND>& nxt, const ChunkSrc<E>& nblk,
                                           f32x4 (&S)[DK / 64][BV / 16],
                                           typename Frag<E>::type (*Sx)[BV / 16][64],
                                           typename Frag<E>::type (*Ux)[BV / 16][64], E* ob, E* qs,
                                           E* __restrict__ o, long bh, int T, int t0, int vt,
-                                          int w, int lane) {
+                                          int w, int lane, const char* pfblk, float& pf) {
     typedef ScanOps<E, DK, DV, BV, KIND> Ops;
     typedef typename Ops::F F;
     typedef typename Ops::V4 V4;
@@ -1188,6 +1188,17 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cu
         const int t = t0 + 16 * w + row;
         const V16 val = *reinterpret_cast<const V16*>(&ob[row * LDO + col]);
         if (t < T) *reinterpret_cast<V16*>(o + ((long)bh * T + t) * DV + vt * BV + col) = val;
+    }
+    if constexpr (PF) {
+        // Pull a later chunk's block from HBM into L2: one 4-byte load per
+        // 128-byte line, the lines dealt out over the 4 NV wavefronts of the
+        // head's workgroups (lanes past the block's end load nothing). The
+        // value is never used; it is waited for only when the register comes
+        // round again, RING steps later, so the load never holds up a step.
+        asm volatile("" ::"v"(pf));
+        constexpr int NV = DV / BV;
+        pf = buf_load<float>(make_rsrc(pfblk, (unsigned)WsLayout<E, DK, DV>::BYTES),
+                             ((vt * 4 + w) + lane * 4 * NV) * 128);
     }
 }
 
@@ -1326,6 +1337,15 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
     }
     E* ob = lds.Ob[w];
     E* qs = lds.Qs[KIND == KIND_KDA ? 0 : w];
+    // KDA: L2 prefetch of the block RING + 1 chunks ahead (its operands are
+    // then loaded into registers two steps later). Measured at d = 128: 5 %
+    // off the KDA scan, nothing for the other kinds. Only where every block
+    // was written before the launch: a prefetched line that is written later
+    // could stay stale in this CU's L1.
+    constexpr bool PF = !SYNC && KIND == KIND_KDA;
+    auto pfb = [&](int cc) { return wsh + (long)min(cc, last) * Lw::BYTES; };
+    float pf0 = 0.f, pf1 = 0.f, pf2 = 0.f;
+    (void)pf2;
     if constexpr (RING == 2) {
         // operands of chunk c + 1 in flight while chunk c is processed
         Ops o0, o1;
@@ -1334,10 +1354,10 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), see below
         for (int c = 0; c < nchunks; c += 2) {
             ready(c + 1);
-            scan_step<E, DK, DV, KIND, BV>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane);
+            scan_step<E, DK, DV, KIND, BV, PF>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane, pfb(c + 3), pf0);
             if (c + 1 >= nchunks) break;
             ready(c + 2);
-            scan_step<E, DK, DV, KIND, BV>(o1, o0, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
+            scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane, pfb(c + 4), pf1);
         }
     } else {
         // operands of chunks c + 1 and c + 2 in flight while chunk c is processed
@@ -1353,13 +1373,13 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         for (int c = 0; c < nchunks; c += 3) {
             ready(c + 2);
-            scan_step<E, DK, DV, KIND, BV>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane);
+            scan_step<E, DK, DV, KIND, BV, PF>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane, pfb(c + 4), pf0);
             if (c + 1 >= nchunks) break;
             ready(c + 3);
-            scan_step<E, DK, DV, KIND, BV>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane);
+            scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane, pfb(c + 5), pf1);
             if (c + 2 >= nchunks) break;
             ready(c + 4);
-            scan_step<E, DK, DV, KIND, BV>(o2, o1, blk(c + 4), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 2) * CHUNK, vt, w, lane);
+            scan_step<E, DK, DV, KIND, BV, PF>(o2, o1, blk(c + 4), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 2) * CHUNK, vt, w, lane, pfb(c + 6), pf2);
         }
     }
 
