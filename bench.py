@@ -67,14 +67,14 @@ CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurren
 DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
                   "delta_rule_recurrent_amd/csrc/dn_launch.h")
 TRAFFIC = {
-    "chunk_prep2_kernel": {"fetch_kib": 29418.6, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
-                           "sha256": "db9ff28f671bfc3cae2d609a36ef3ed30eb3646a7b52b936da9c35da13109855"},
+    "chunk_prep2_kernel": {"fetch_kib": 29314.0, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
+                           "sha256": "6ce13b672766e99499ffba45d9c5b3ce06b2cd59cc18b5cdbec6ba979c506766"},
     "chunk_scan_kernel": {"fetch_kib": 37102.6, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
-                          "sha256": "db9ff28f671bfc3cae2d609a36ef3ed30eb3646a7b52b936da9c35da13109855"},
-    "chunk_fused_kernel": {"fetch_kib": 62001.6, "write_kib": 76630.5, "sources": CHUNK_SOURCES,
-                           "sha256": "db9ff28f671bfc3cae2d609a36ef3ed30eb3646a7b52b936da9c35da13109855"},
-    "decode_step_kernel": {"fetch_kib": 132752.1, "write_kib": 263168.0, "sources": DECODE_SOURCES,
-                           "sha256": "97909e8bd3d430aff64cf62dc77a70178c67b1102cee5d38ce5c9af2002a88fa"},
+                          "sha256": "6ce13b672766e99499ffba45d9c5b3ce06b2cd59cc18b5cdbec6ba979c506766"},
+    "chunk_fused_kernel": {"fetch_kib": 62003.6, "write_kib": 76633.9, "sources": CHUNK_SOURCES,
+                           "sha256": "6ce13b672766e99499ffba45d9c5b3ce06b2cd59cc18b5cdbec6ba979c506766"},
+    "decode_step_kernel": {"fetch_kib": 136303.3, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+                           "sha256": "df77ffcdf975415024e5a004bcb73c1a8db75523e965b8ea31d47ccd73b8d2f0"},
 }
 
 
