@@ -260,7 +260,11 @@ void chunk_prep_kernel(const E* __restrict__ q,
     // clamped to the last item).
     TileRegs<E, DK> rk, rq, rg;   // rg: KDA's per-channel log-decay
     TileRegs<E, DV> rv;
-    float pb = 0.f, pg = 0.f;   // beta and log-decay of token `lane` (wave 0)
+    // beta and log-decay of token `lane` (wave 0), kept as loaded: converting
+    // (or masking) them right after the load would make the wave wait for
+    // every prefetch load issued before them
+    E pbr{}, pgr{};
+    bool pin = false;   // token `lane` is inside the chunk
     auto fetch = [&](int it) {
         const int fc = it % nchunks;
         const long ftok = (long)(it / nchunks) * T + (long)fc * CHUNK;
@@ -271,9 +275,9 @@ void chunk_prep_kernel(const E* __restrict__ q,
         if (KDA) tile_load<E, DK>(rg, g + ftok * DK, fL, tid);
         if (w == 0) {
             const long tk = ftok + min(lane, fL - 1);
-            pb = to_f32(beta[tk]);
-            if (KIND == KIND_GATED) pg = to_f32(g[tk]);
-            if (lane >= fL) pb = pg = 0.f;
+            pbr = beta[tk];
+            if (KIND == KIND_GATED) pgr = g[tk];
+            pin = lane < fL;
         }
     };
     int item = blockIdx.x;
@@ -296,6 +300,8 @@ void chunk_prep_kernel(const E* __restrict__ q,
     const long tok0 = (long)bh * T + t0;
 
     // ---- 1. beta, log-decay and its running sum inside the chunk; stage tiles
+    const float pb = pin ? to_f32(pbr) : 0.f;
+    const float pg = KIND == KIND_GATED && pin ? to_f32(pgr) : 0.f;
     if (w == 0) bs[lane] = pb;
     if (!KDA) {
         if (w == 0) {
