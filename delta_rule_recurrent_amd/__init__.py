@@ -19,7 +19,8 @@ import torch
 from . import _lib
 from ._lib import DeltaNetError, lib
 
-__all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_prep", "chunk_scan", "recurrent_fwd",
+__all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_prep",
+           "chunk_scan", "recurrent_fwd",
            "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
            "DeltaNetError", "lib", "library_path"]
 
@@ -134,6 +135,41 @@ def kda_chunk_fwd(q, k, v, beta, g, S0=None, *, output_final_state=True, o=None,
     """Chunkwise (C=64) KDA prefill; g [B,H,T,dk] per-key-channel log-decay."""
     return _chunk("dn_kda_chunk_fwd", q, k, v, beta, g, S0, output_final_state, o, S_final,
                   workspace, stream, kda=True)
+
+
+def chunk_fwd_states(q, k, v, beta, g=None, S0=None, *, kda=False, o=None, S_final=None,
+                     S_chunks=None, workspace=None, stream=None):
+    """Chunkwise prefill that also returns the state at every chunk boundary.
+
+    kda=False: DeltaNet / Gated DeltaNet as chunk_fwd; kda=True: as
+    kda_chunk_fwd. Returns (o, S_final, S_chunks) with S_chunks fp32
+    [B,H,ceil(T/64),dk,dv]: entry c is the state after the first
+    min(64(c+1), T) tokens (the last equals S_final).
+    """
+    B, H, T, dk, dv, dev, dt = _prefill_args(q, k, v, beta, g, S0, kda)
+    n = (T + 63) // 64
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, T, dv), dt, dev)
+    if S_final is None:
+        S_final = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
+    if S_chunks is None:
+        S_chunks = torch.empty(B, H, n, dk, dv, dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("S_chunks", S_chunks, (B, H, n, dk, dv), torch.float32, dev)
+    need = int(lib().dn_chunk_fwd_workspace(B, H, T, dk, dv, _DT[dt]))
+    if workspace is None:
+        workspace = _alloc_workspace(need, dev)
+    st = lib().dn_chunk_fwd_states(int(kda), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                   _ptr(S0), _ptr(o), _ptr(S_final),
+                                   _ptr(S_chunks) if n > 0 else None, B, H, T, dk, dv, _DT[dt],
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream))
+    _lib.check("dn_chunk_fwd_states", st)
+    return o, S_final, S_chunks
 
 
 def chunk_prep(q, k, v, beta, g, workspace, *, kda=False, stream=None):

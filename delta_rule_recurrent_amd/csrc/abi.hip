@@ -158,6 +158,28 @@ int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* be
                         workspace, workspace_bytes, stream, dn::FWD_TWO);
 }
 
+int dn_chunk_fwd_states(int kda, const void* q, const void* k, const void* v, const void* beta,
+                        const void* g, const float* S0, void* o, float* S_final, float* S_chunks,
+                        int B, int H, int T, int dk, int dv, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    const int kind = chunk_kind(kda != 0, g);
+    int st = check_common(q, k, v, beta, g, kda != 0, S0, o, S_final, B, H, T, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    if (T > 0 && !S_chunks) return DN_EINVAL;
+    if (misaligned(S_chunks)) return DN_EINVAL;
+    if (kda && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
+    const long long BH = (long long)B * H;
+    if (T == 0) {
+        if (!S_final) return DN_OK;
+        return hip_status(dn::launch_state_copy(S0, S_final, BH * dk * dv, as_stream(stream)));
+    }
+    st = check_workspace(BH, T, dk, dv, dtype, workspace, workspace_bytes);
+    if (st != DN_OK) return st;
+    return hip_status(dn::launch_chunk_fwd_states(kind, dtype, q, k, v, beta, g, S0, o, S_final,
+                                                  S_chunks, workspace, (int)BH, T, dk, dv,
+                                                  as_stream(stream)));
+}
+
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,
                   const void* g, int B, int H, int T, int dk, int dv, int dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {

@@ -1282,13 +1282,14 @@ __device__ __forceinline__ u64* block_tags(char* ws, long BH, int nchunks) {
 // each is waited for (tags at `tags`, expected value `tag`) before its
 // operands are loaded. RING: 3 (two chunks prefetched) or 2 (one chunk; fewer
 // registers held, which leaves the fused launch's register budget room).
-template <typename E, int DK, int DV, int KIND, int BV, bool SYNC, int RING>
+template <typename E, int DK, int DV, int KIND, int BV, bool SYNC, int RING, bool EMIT = false>
 __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* __restrict__ q,
                                           const float* __restrict__ S0, E* __restrict__ o,
                                           float* __restrict__ S_final, int T, int nchunks,
                                           long bh, int vt, int w, int lane,
                                           ScanLds<E, DK, DV, KIND, BV>& lds, const u64* tags,
-                                          u64 tag, u64* err, u64 epoch) {
+                                          u64 tag, u64* err, u64 epoch,
+                                          float* __restrict__ S_bound = nullptr) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef ScanOps<E, DK, DV, BV, KIND> Ops;
     constexpr int NT = Ops::NT, MTW = Ops::MTW;
@@ -1312,6 +1313,23 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) S[m][nt] = zero4();
     }
+
+    // EMIT: the state after chunk cc, S_bound[bh][cc] (fp32 [DK][DV]); written
+    // at the end of the step, after its loads, like the output rows
+    auto emit = [&](int cc) {
+        if constexpr (EMIT) {
+            float* Sb = S_bound + ((long)bh * nchunks + cc) * DK * DV;
+#pragma unroll
+            for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int row = 16 * (w * MTW + m) + 4 * gq + e, col = vt * BV + 16 * nt + n;
+                        Sb[row * DV + col] = S[m][nt][e];
+                    }
+        }
+    };
 
     // The operands of the next RING - 1 chunks are in flight while chunk c is
     // processed (RING register sets in rotation). Prefetches are
@@ -1361,9 +1379,11 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
         for (int c = 0; c < nchunks; c += 2) {
             ready(c + 1);
             scan_step<E, DK, DV, KIND, BV, PF>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane, pfb(c + 3), pf0);
+            emit(c);
             if (c + 1 >= nchunks) break;
             ready(c + 2);
             scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane, pfb(c + 4), pf1);
+            emit(c + 1);
         }
     } else {
         // operands of chunks c + 1 and c + 2 in flight while chunk c is processed
@@ -1380,12 +1400,15 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
         for (int c = 0; c < nchunks; c += 3) {
             ready(c + 2);
             scan_step<E, DK, DV, KIND, BV, PF>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane, pfb(c + 4), pf0);
+            emit(c);
             if (c + 1 >= nchunks) break;
             ready(c + 3);
             scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane, pfb(c + 5), pf1);
+            emit(c + 1);
             if (c + 2 >= nchunks) break;
             ready(c + 4);
             scan_step<E, DK, DV, KIND, BV, PF>(o2, o1, blk(c + 4), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 2) * CHUNK, vt, w, lane, pfb(c + 6), pf2);
+            emit(c + 2);
         }
     }
 
@@ -1402,13 +1425,14 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
     }
 }
 
-template <typename E, int DK, int DV, int KIND, int BV>
+template <typename E, int DK, int DV, int KIND, int BV, bool EMIT>
 __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict__ ws,
                                                          const E* __restrict__ q,
                                                          const float* __restrict__ S0,
                                                          E* __restrict__ o,
                                                          float* __restrict__ S_final, int T,
-                                                         int nchunks, int BH) {
+                                                         int nchunks, int BH,
+                                                         float* __restrict__ S_bound) {
     constexpr int NV = DV / BV;
     // XCD-aware mapping: consecutive workgroups go to different XCDs
     // (round-robin over 8); the NV value tiles of one head share an XCD so
@@ -1418,9 +1442,9 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
     const long bh = (long)(slot / NV) * 8 + xcd;
     if (bh >= BH) return;
     __shared__ ScanLds<E, DK, DV, KIND, BV> lds;
-    scan_body<E, DK, DV, KIND, BV, false, 3>(ws, q, S0, o, S_final, T, nchunks, bh, vt,
-                                          (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63), lds,
-                                          nullptr, 0, nullptr, 0);
+    scan_body<E, DK, DV, KIND, BV, false, 3, EMIT>(ws, q, S0, o, S_final, T, nchunks, bh, vt,
+                                                (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63), lds,
+                                                nullptr, 0, nullptr, 0, S_bound);
 }
 
 // ---------------------------------------------------------------------------
@@ -1554,24 +1578,32 @@ static hipError_t prep_t(const void* q, const void* k, const void* v, const void
     return hipGetLastError();
 }
 
-template <typename E, int D, int KIND>
-static hipError_t scan_t(const void* q, const float* S0, void* o, float* S_final, const void* ws,
-                         int BH, int T, hipStream_t st) {
+template <typename E, int D, int KIND, bool EMIT>
+static hipError_t scan_launch(const void* q, const float* S0, void* o, float* S_final, const void* ws,
+                              int BH, int T, float* S_bound, hipStream_t st) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const long groups = ((long)BH + 7) / 8;
     // 32-column value tiles unless that leaves most of the 256 CUs idle
     if (scan_bv<D>(BH) == 32) {
         constexpr int BV = 32;
         const long nblk = groups * 8 * (D / BV);
-        hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
-                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH);
+        hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV, EMIT>), dim3((unsigned)nblk), dim3(256), 0,
+                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound);
     } else {
         constexpr int BV = 16;
         const long nblk = groups * 8 * (D / BV);
-        hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
-                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH);
+        hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV, EMIT>), dim3((unsigned)nblk), dim3(256), 0,
+                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound);
     }
     return hipGetLastError();
+}
+
+// S_bound: NULL, or the states at every chunk boundary, [BH][nchunks][D][D] fp32
+template <typename E, int D, int KIND>
+static hipError_t scan_t(const void* q, const float* S0, void* o, float* S_final, const void* ws,
+                         int BH, int T, hipStream_t st, float* S_bound = nullptr) {
+    if (S_bound) return scan_launch<E, D, KIND, true>(q, S0, o, S_final, ws, BH, T, S_bound, st);
+    return scan_launch<E, D, KIND, false>(q, S0, o, S_final, ws, BH, T, nullptr, st);
 }
 
 // A new 64-bit epoch per fused launch: a random per-process prefix and a
@@ -1627,10 +1659,11 @@ static hipError_t prep_kind(int kind, const void* q, const void* k, const void* 
 
 template <typename E, int D>
 static hipError_t scan_kind(int kind, const void* q, const float* S0, void* o, float* S_final,
-                            const void* ws, int BH, int T, hipStream_t st) {
+                            const void* ws, int BH, int T, hipStream_t st,
+                            float* S_bound = nullptr) {
     // DeltaNet and Gated DeltaNet share the scan (a unit decay is stored for DeltaNet)
-    if (kind == KIND_KDA) return scan_t<E, D, KIND_KDA>(q, S0, o, S_final, ws, BH, T, st);
-    return scan_t<E, D, KIND_GATED>(q, S0, o, S_final, ws, BH, T, st);
+    if (kind == KIND_KDA) return scan_t<E, D, KIND_KDA>(q, S0, o, S_final, ws, BH, T, st, S_bound);
+    return scan_t<E, D, KIND_GATED>(q, S0, o, S_final, ws, BH, T, st, S_bound);
 }
 
 hipError_t launch_chunk_prep(int kind, int dtype, const void* q, const void* k, const void* v,
@@ -1653,6 +1686,19 @@ hipError_t launch_chunk_scan(int kind, int dtype, const void* q, const float* S0
                          : scan_kind<bf16, 64>(kind, q, S0, o, S_final, ws, BH, T, st);
     return dk == 128 ? scan_kind<float, 128>(kind, q, S0, o, S_final, ws, BH, T, st)
                      : scan_kind<float, 64>(kind, q, S0, o, S_final, ws, BH, T, st);
+}
+
+hipError_t launch_chunk_fwd_states(int kind, int dtype, const void* q, const void* k,
+                                   const void* v, const void* beta, const void* g,
+                                   const float* S0, void* o, float* S_final, float* S_bound,
+                                   void* ws, int BH, int T, int dk, int dv, hipStream_t st) {
+    const hipError_t e = launch_chunk_prep(kind, dtype, q, k, v, beta, g, ws, BH, T, dk, dv, st);
+    if (e != hipSuccess) return e;
+    if (dtype == DT_BF16)
+        return dk == 128 ? scan_kind<bf16, 128>(kind, q, S0, o, S_final, ws, BH, T, st, S_bound)
+                         : scan_kind<bf16, 64>(kind, q, S0, o, S_final, ws, BH, T, st, S_bound);
+    return dk == 128 ? scan_kind<float, 128>(kind, q, S0, o, S_final, ws, BH, T, st, S_bound)
+                     : scan_kind<float, 64>(kind, q, S0, o, S_final, ws, BH, T, st, S_bound);
 }
 
 // One-launch prefill where it exists: bf16, DeltaNet or Gated DeltaNet, and

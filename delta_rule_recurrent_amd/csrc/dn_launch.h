@@ -42,6 +42,13 @@ hipError_t launch_chunk_fwd(int kind, int dtype, const void* q, const void* k, c
                             float* S_final, void* workspace, int BH, int T, int dk, int dv,
                             int mode, hipStream_t stream);
 
+// Two-phase prefill that also writes the state after every chunk:
+// S_bound [BH][ceil(T/64)][dk][dv] fp32.
+hipError_t launch_chunk_fwd_states(int kind, int dtype, const void* q, const void* k,
+                                   const void* v, const void* beta, const void* g,
+                                   const float* S0, void* o, float* S_final, float* S_bound,
+                                   void* ws, int BH, int T, int dk, int dv, hipStream_t stream);
+
 // Workspace bytes of the chunkwise prefill (per call).
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype);
 

@@ -124,6 +124,27 @@ int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* be
                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunkwise prefill that also returns the state at every chunk boundary, for
+ * prefix caching: an engine keeps the state after a shared prefix, at block
+ * boundaries, instead of per-position entries (page "28. Linear attention and
+ * Gated DeltaNet", section "The state a request carries").
+ *   kda      0: DeltaNet / Gated DeltaNet exactly as dn_chunk_fwd (g optional,
+ *            [B,H,T]); nonzero: KDA exactly as dn_kda_chunk_fwd (g required,
+ *            [B,H,T,dk]).
+ *   S_chunks [B,H,n,dk,dv] fp32 with n = ceil(T/64), 16-byte aligned: entry c
+ *            is the state after the first min(64(c+1), T) tokens, so the last
+ *            one equals S_final. Required when T > 0 (else DN_EINVAL).
+ * Every other argument, the workspace and the errors are as for dn_chunk_fwd
+ * (always the two-phase form). o and S_final are bitwise the same as
+ * dn_chunk_fwd's two-phase form gives.
+ */
+int dn_chunk_fwd_states(int kda, const void* q, const void* k, const void* v,
+                        const void* beta, const void* g, const float* S0, void* o,
+                        float* S_final, float* S_chunks, int B, int H, int T, int dk,
+                        int dv, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * The two phases of the chunkwise prefill, for callers that schedule them
  * separately (for example to overlap one request's chunk-parallel phase with
  * another's sequential phase, or to time them). On one stream,

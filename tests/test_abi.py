@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -97,6 +97,30 @@ def test_chunk_validation(fn):
     if fn == "dn_chunk_fwd_fused":
         assert _chunk(fn, dtype=0) == N              # the one-launch form is bf16 only
         assert _chunk(fn, dtype=0, q=None) == E      # argument errors still come first
+
+
+def _states(**kw):
+    args = dict(kda=0, q=P, k=P, v=P, beta=P, g=P, S0=P, o=P, S_final=P, S_chunks=P, B=1, H=1,
+                T=64, dk=64, dv=64, dtype=1, ws=WS, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return _lib.lib().dn_chunk_fwd_states(*[args[n] for n in (
+        "kda", "q", "k", "v", "beta", "g", "S0", "o", "S_final", "S_chunks", "B", "H", "T", "dk",
+        "dv", "dtype", "ws", "ws_bytes", "stream")])
+
+
+def test_boundary_states_validation():
+    E, N, W = _lib.DN_EINVAL, _lib.DN_ENOTSUP, _lib.DN_EWORKSPACE
+    assert _states(S_chunks=None) == E           # required whenever there is a chunk
+    assert _states(S_chunks=MIS) == E
+    assert _states(q=None) == E
+    assert _states(B=0) == E
+    assert _states(kda=1, g=None) == E           # KDA needs its per-channel decay
+    assert _states(kda=1, dtype=0, dk=128, dv=128) == N
+    assert _states(dk=96, dv=96) == N
+    assert _states(ws=None) == W
+    assert _states(ws_bytes=16) == W
+    # T == 0 with no S_final: nothing to do, no launch
+    assert _states(T=0, S_chunks=None, S_final=None) == _lib.DN_OK
 
 
 def _rec(fn, **kw):

@@ -261,3 +261,38 @@ def test_fused_handoff(kind, BH):
     eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
     say("  err o %.3e  S %.3e" % (eo, es))
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_boundary_states(kind, dtype, d):
+    """dn_chunk_fwd_states: the state after every chunk against the oracle run
+    chunk by chunk (each segment started from the oracle's state at the end of
+    the one before), on a ragged last chunk; o and S_final bitwise equal to the
+    plain prefill's, and the last boundary state equal to S_final."""
+    dn = _dn()
+    B, H, T = 2, 3, 5 * 64 + 9
+    n = (T + 63) // 64
+    say("boundary states", kind, dtype, d, T)
+    inp = make(kind, B, H, T, d, dtype, seed=41, s0_std=0.5)
+    dv = to_dev(inp)
+    args = (dv["q"], dv["k"], dv["v"], dv["beta"], dv["g"], dv["S0"])
+    o, S, Sc = dn.chunk_fwd_states(*args, kda=(kind == "kda"))
+    ref_fn = dn.kda_chunk_fwd if kind == "kda" else dn.chunk_fwd
+    o2, S2 = ref_fn(*args)
+    torch.cuda.synchronize()
+    assert Sc.shape == (B, H, n, d, d)
+    assert torch.equal(o, o2) and torch.equal(S, S2)
+    assert torch.equal(Sc[:, :, -1], S)
+    state = inp["S0"]
+    worst = 0.0
+    for c in range(n):
+        a, b = 64 * c, min(64 * (c + 1), T)
+        seg = {key: (inp[key][:, :, a:b] if inp[key] is not None else None)
+               for key in ("q", "k", "v", "beta", "g")}
+        seg["kind"] = inp["kind"]
+        _, state = oracle_prefill(seg, S0=state)
+        e = rel_err(Sc[:, :, c], state)
+        worst = max(worst, e)
+        assert e <= TOL[dtype], (c, e)
+    say("  worst boundary-state err %.3e" % worst)
