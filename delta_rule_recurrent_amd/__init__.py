@@ -19,8 +19,8 @@ import torch
 from . import _lib
 from ._lib import DeltaNetError, lib
 
-__all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_prep",
-           "chunk_scan", "recurrent_fwd",
+__all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_fwd_gqa",
+           "decode_step_gqa", "chunk_prep", "chunk_scan", "recurrent_fwd",
            "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
            "DeltaNetError", "lib", "library_path"]
 
@@ -170,6 +170,77 @@ def chunk_fwd_states(q, k, v, beta, g=None, S0=None, *, kda=False, o=None, S_fin
                                    _stream(stream))
     _lib.check("dn_chunk_fwd_states", st)
     return o, S_final, S_chunks
+
+
+def chunk_fwd_gqa(q, k, v, beta, g=None, S0=None, *, kda=False, output_final_state=True, o=None,
+                  S_final=None, workspace=None, stream=None):
+    """Chunkwise prefill with key heads shared by value heads.
+
+    q, k [B,Hk,T,dk]; v [B,Hv,T,dv] with Hv a multiple of Hk (key head j serves
+    value heads j*Hv/Hk .. (j+1)*Hv/Hk - 1); beta, g, S0 per value head. Equal
+    to chunk_fwd (kda_chunk_fwd) on q, k repeated over heads. Returns (o, S_final).
+    """
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [B,Hk,T,dk] and v [B,Hv,T,dv]")
+    B, Hk, T, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[3]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    _check_tensor("k", k, (B, Hk, T, dk), dt, dev)
+    _check_tensor("v", v, (B, Hv, T, dv), dt, dev)
+    _check_tensor("beta", beta, (B, Hv, T), dt, dev)
+    if kda:
+        _check_tensor("g", g, (B, Hv, T, dk), dt, dev)
+    elif g is not None:
+        _check_tensor("g", g, (B, Hv, T), dt, dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, Hv, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, Hv, T, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, Hv, T, dv), dt, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty(B, Hv, dk, dv, dtype=torch.float32, device=dev)
+    elif S_final is not None:
+        _check_tensor("S_final", S_final, (B, Hv, dk, dv), torch.float32, dev)
+    if workspace is None:
+        workspace = _alloc_workspace(int(lib().dn_chunk_fwd_workspace(B, Hv, T, dk, dv, _DT[dt])), dev)
+    st = lib().dn_chunk_fwd_gqa(int(kda), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                _ptr(S0), _ptr(o), _ptr(S_final), B, Hk, Hv, T, dk, dv, _DT[dt],
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _stream(stream))
+    _lib.check("dn_chunk_fwd_gqa", st)
+    return o, S_final
+
+
+def decode_step_gqa(q, k, v, beta, g, S, *, kda=False, o=None, stream=None):
+    """One decode step with key heads shared by value heads: q, k [B,Hk,dk];
+    v [B,Hv,dv]; beta [B,Hv]; g [B,Hv] (gated), [B,Hv,dk] (KDA) or None;
+    S [B,Hv,dk,dv] fp32 updated in place. Returns o [B,Hv,dv]."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q must be [B,Hk,dk] and v [B,Hv,dv]")
+    B, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    _check_tensor("k", k, (B, Hk, dk), dt, dev)
+    _check_tensor("v", v, (B, Hv, dv), dt, dev)
+    _check_tensor("beta", beta, (B, Hv), dt, dev)
+    if kda:
+        _check_tensor("g", g, (B, Hv, dk), dt, dev)
+    elif g is not None:
+        _check_tensor("g", g, (B, Hv), dt, dev)
+    _check_tensor("S", S, (B, Hv, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, Hv, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, Hv, dv), dt, dev)
+    st = lib().dn_decode_step_gqa(int(kda), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                  _ptr(S), _ptr(o), B, Hk, Hv, dk, dv, _DT[dt], _stream(stream))
+    _lib.check("dn_decode_step_gqa", st)
+    return o
 
 
 def chunk_prep(q, k, v, beta, g, workspace, *, kda=False, stream=None):

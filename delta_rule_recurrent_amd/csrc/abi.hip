@@ -59,7 +59,7 @@ int chunk_kind(bool kda, const void* g) {
 int chunk_common(int kind, const void* q, const void* k, const void* v, const void* beta,
                  const void* g, const float* S0, void* o, float* S_final, int B, int H, int T,
                  int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
-                 void* stream, int mode) {
+                 void* stream, int mode, dn::HeadMap hm = dn::HeadMap()) {
     int st = check_common(q, k, v, beta, g, kind == dn::KIND_KDA, S0, o, S_final, B, H, T, dk,
                           dv, dtype);
     if (st != DN_OK) return st;
@@ -74,7 +74,7 @@ int chunk_common(int kind, const void* q, const void* k, const void* v, const vo
     if (st != DN_OK) return st;
     const hipError_t e = dn::launch_chunk_fwd(kind, dtype, q, k, v, beta, g, S0, o, S_final,
                                               workspace, (int)BH, T, dk, dv, mode,
-                                              as_stream(stream));
+                                              as_stream(stream), hm);
     if (e == hipErrorNotSupported) return DN_ENOTSUP;
     return hip_status(e);
 }
@@ -96,13 +96,21 @@ int recurrent_common(int kind, const void* q, const void* k, const void* v, cons
 
 int decode_common(int kind, const void* q, const void* k, const void* v, const void* beta,
                   const void* g, float* S, void* o, int B, int H, int dk, int dv, int dtype,
-                  void* stream) {
+                  void* stream, dn::HeadMap hm = dn::HeadMap()) {
     if (!S) return DN_EINVAL;
     int st = check_common(q, k, v, beta, g, kind == dn::KIND_KDA, S, o, S, B, H, 1, dk, dv, dtype);
     if (st != DN_OK) return st;
     const long long BH = (long long)B * H;
     return hip_status(dn::launch_decode(kind, dtype, q, k, v, beta, g, S, o, (int)BH, dk, dv,
-                                        as_stream(stream)));
+                                        as_stream(stream), hm));
+}
+
+// Key heads shared by value heads: Hk >= 1 key heads, Hv a multiple of Hk.
+bool head_map(int Hk, int Hv, dn::HeadMap* hm) {
+    if (Hk < 1 || Hv < 1 || Hv % Hk != 0) return false;
+    hm->hv = Hv;
+    hm->g = Hv / Hk;
+    return true;
 }
 
 }  // namespace
@@ -178,6 +186,27 @@ int dn_chunk_fwd_states(int kda, const void* q, const void* k, const void* v, co
     return hip_status(dn::launch_chunk_fwd_states(kind, dtype, q, k, v, beta, g, S0, o, S_final,
                                                   S_chunks, workspace, (int)BH, T, dk, dv,
                                                   as_stream(stream)));
+}
+
+int dn_chunk_fwd_gqa(int kda, const void* q, const void* k, const void* v, const void* beta,
+                     const void* g, const float* S0, void* o, float* S_final, int B, int Hk,
+                     int Hv, int T, int dk, int dv, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    dn::HeadMap hm;
+    if (!head_map(Hk, Hv, &hm)) return DN_EINVAL;
+    const int kind = chunk_kind(kda != 0, g);
+    return chunk_common(kind, q, k, v, beta, g, S0, o, S_final, B, Hv, T, dk, dv, dtype,
+                        workspace, workspace_bytes, stream,
+                        kind == dn::KIND_KDA ? dn::FWD_TWO : dn::FWD_AUTO, hm);
+}
+
+int dn_decode_step_gqa(int kda, const void* q, const void* k, const void* v, const void* beta,
+                       const void* g, float* S, void* o, int B, int Hk, int Hv, int dk, int dv,
+                       int dtype, void* stream) {
+    dn::HeadMap hm;
+    if (!head_map(Hk, Hv, &hm)) return DN_EINVAL;
+    return decode_common(kda ? dn::KIND_KDA : (g ? dn::KIND_GATED : dn::KIND_DELTANET), q, k, v,
+                         beta, g, S, o, B, Hv, dk, dv, dtype, stream, hm);
 }
 
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,

@@ -230,7 +230,7 @@ void chunk_prep_kernel(const E* __restrict__ q,
                                                          const E* __restrict__ beta,
                                                          const E* __restrict__ g,
                                                          char* __restrict__ ws, int T,
-                                                         int nchunks, int nitems) {
+                                                         int nchunks, int nitems, HeadMap hm) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef PrepSmem<E, DK, DV, KIND> Sm;
     typedef typename Frag<E>::type F;
@@ -268,9 +268,10 @@ void chunk_prep_kernel(const E* __restrict__ q,
     auto fetch = [&](int it) {
         const int fc = it % nchunks;
         const long ftok = (long)(it / nchunks) * T + (long)fc * CHUNK;
+        const long fkey = hm.key(it / nchunks) * T + (long)fc * CHUNK;   // q, k row
         const int fL = min(CHUNK, T - fc * CHUNK);
-        tile_load<E, DK>(rk, k + ftok * DK, fL, tid);
-        tile_load<E, DK>(rq, q + ftok * DK, fL, tid);
+        tile_load<E, DK>(rk, k + fkey * DK, fL, tid);
+        tile_load<E, DK>(rq, q + fkey * DK, fL, tid);
         tile_load<E, DV>(rv, v + ftok * DV, fL, tid);
         if (KDA) tile_load<E, DK>(rg, g + ftok * DK, fL, tid);
         if (w == 0) {
@@ -693,8 +694,8 @@ template <typename E, int DK, int DV, int KIND>
 __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __restrict__ k,
                                            const E* __restrict__ v, const E* __restrict__ beta,
                                            const E* __restrict__ g, char* __restrict__ blk,
-                                           Prep2Lds<E, DK, DV>& lds, long bh, int c, int T, int w,
-                                           int lane) {
+                                           Prep2Lds<E, DK, DV>& lds, long bh, long bhk, int c, int T,
+                                           int w, int lane) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef Prep2Smem<E, DK, DV> Sm;
     typedef typename Frag<E>::type F;
@@ -713,6 +714,7 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
     const int t0 = c * CHUNK;
     const int L = min(CHUNK, T - t0);
     const long tok0 = bh * T + t0;
+    const long tokk = bhk * T + t0;   // q and k (key-head row)
 
     F* Wf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::W_OFF);
     F* Kf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::K_OFF);
@@ -733,13 +735,13 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[tt][kb] = frag_rows8_g<E>(k + tok0 * DK, DK, 16 * tt, 32 * kb, lane, L);
+        for (int kb = 0; kb < KB; ++kb) kf[tt][kb] = frag_rows8_g<E>(k + tokk * DK, DK, 16 * tt, 32 * kb, lane, L);
     F qa[4][KB], vf[4][VB];
     if (w == 1) {
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) qa[tt][kb] = frag_rows8_g<E>(q + tok0 * DK, DK, 16 * tt, 32 * kb, lane, L);
+            for (int kb = 0; kb < KB; ++kb) qa[tt][kb] = frag_rows8_g<E>(q + tokk * DK, DK, 16 * tt, 32 * kb, lane, L);
 #pragma unroll
         for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
@@ -940,12 +942,12 @@ __global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict
                                                              const E* __restrict__ beta,
                                                              const E* __restrict__ g,
                                                              char* __restrict__ ws, int T,
-                                                             int nchunks) {
+                                                             int nchunks, HeadMap hm) {
     __shared__ Prep2Lds<E, DK, DV> lds;
     const long item = blockIdx.x;
     prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV>::BYTES, lds,
-                                item / nchunks, (int)(item % nchunks), T, (int)(threadIdx.x >> 6),
-                                (int)(threadIdx.x & 63));
+                                item / nchunks, hm.key(item / nchunks), (int)(item % nchunks), T,
+                                (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
 }
 
 // ---------------------------------------------------------------------------
@@ -1288,7 +1290,7 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
                                           float* __restrict__ S_final, int T, int nchunks,
                                           long bh, int vt, int w, int lane,
                                           ScanLds<E, DK, DV, KIND, BV>& lds, const u64* tags,
-                                          u64 tag, u64* err, u64 epoch,
+                                          u64 tag, u64* err, u64 epoch, HeadMap hm,
                                           float* __restrict__ S_bound = nullptr) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef ScanOps<E, DK, DV, BV, KIND> Ops;
@@ -1337,10 +1339,11 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
     // straight-line code lets the compiler wait for exactly the set in use
     // instead of draining every load in flight.
     const char* wsh = ws + bh * nchunks * Lw::BYTES;
+    const long bhk = hm.key(bh);   // q rows of the key head
     const int last = nchunks - 1;
     auto blk = [&](int cc) {
         const int c2 = min(cc, last);
-        return ChunkSrc<E>{wsh + (long)c2 * Lw::BYTES, q + (bh * T + (long)c2 * CHUNK) * DK,
+        return ChunkSrc<E>{wsh + (long)c2 * Lw::BYTES, q + (bhk * T + (long)c2 * CHUNK) * DK,
                            min(CHUNK, T - c2 * CHUNK)};
     };
     // SYNC: the tags of the next block to be waited for are loaded one chunk
@@ -1432,7 +1435,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
                                                          E* __restrict__ o,
                                                          float* __restrict__ S_final, int T,
                                                          int nchunks, int BH,
-                                                         float* __restrict__ S_bound) {
+                                                         float* __restrict__ S_bound, HeadMap hm) {
     constexpr int NV = DV / BV;
     // XCD-aware mapping: consecutive workgroups go to different XCDs
     // (round-robin over 8); the NV value tiles of one head share an XCD so
@@ -1444,7 +1447,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
     __shared__ ScanLds<E, DK, DV, KIND, BV> lds;
     scan_body<E, DK, DV, KIND, BV, false, 3, EMIT>(ws, q, S0, o, S_final, T, nchunks, bh, vt,
                                                 (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63), lds,
-                                                nullptr, 0, nullptr, 0, S_bound);
+                                                nullptr, 0, nullptr, 0, hm, S_bound);
 }
 
 // ---------------------------------------------------------------------------
@@ -1477,7 +1480,8 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
                                                              const float* __restrict__ S0,
                                                              E* __restrict__ o,
                                                              float* __restrict__ S_final, int T,
-                                                             int nchunks, int BH, int NP, u64 epoch) {
+                                                             int nchunks, int BH, int NP, u64 epoch,
+                                                             HeadMap hm) {
     typedef WsLayout<E, DK, DV> Lw;
     constexpr int NV = DV / BV;
     __shared__ FusedLds<E, DK, DV, KIND, BV> lds;
@@ -1503,7 +1507,7 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
                 int ln;
                 asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
                 prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + (bh * nchunks + c) * Lw::BYTES,
-                                            lds.prep[unit], bh, c, T, wu, ln);
+                                            lds.prep[unit], bh, hm.key(bh), c, T, wu, ln);
                 publish(tags + 2 * (bh * nchunks + c) + wu, tag, ln);
             } else {
                 lds_barrier();   // the item's one barrier, passed with the other unit
@@ -1516,7 +1520,7 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
     if (i >= nh) return;
     const long bh = xcd + 8L * i;
     scan_body<E, DK, DV, KIND, BV, true, 2>(ws, q, S0, o, S_final, T, nchunks, bh, vt, w, lane, lds.scan,
-                                         tags + 2 * bh * nchunks, tag, err, epoch);
+                                         tags + 2 * bh * nchunks, tag, err, epoch, hm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1557,14 +1561,14 @@ static int scan_bv(int BH) {
 
 template <typename E, int D, int KIND>
 static hipError_t prep_t(const void* q, const void* k, const void* v, const void* beta,
-                         const void* g, void* ws, int BH, int T, hipStream_t st) {
+                         const void* g, void* ws, int BH, int T, hipStream_t st, HeadMap hm) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int nitems = nchunks * BH;
     // two wavefronts per chunk where their fragments fit in 256 registers
     if constexpr (KIND != KIND_KDA && (sizeof(E) == 2 || D == 64)) {
         hipLaunchKernelGGL((chunk_prep2_kernel<E, D, D, KIND>), dim3((unsigned)nitems), dim3(128), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
-                           (char*)ws, T, nchunks);
+                           (char*)ws, T, nchunks, hm);
         return hipGetLastError();
     }
     // persistent workgroups: as many as fit on the device at once (LDS bound)
@@ -1574,13 +1578,13 @@ static hipError_t prep_t(const void* q, const void* k, const void* v, const void
     const int grid = (int)(nitems < resident ? nitems : resident);
     hipLaunchKernelGGL((chunk_prep_kernel<E, D, D, KIND>), dim3((unsigned)grid), dim3(256), 0, st,
                        (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
-                       (char*)ws, T, nchunks, nitems);
+                       (char*)ws, T, nchunks, nitems, hm);
     return hipGetLastError();
 }
 
 template <typename E, int D, int KIND, bool EMIT>
 static hipError_t scan_launch(const void* q, const float* S0, void* o, float* S_final, const void* ws,
-                              int BH, int T, float* S_bound, hipStream_t st) {
+                              int BH, int T, float* S_bound, hipStream_t st, HeadMap hm) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const long groups = ((long)BH + 7) / 8;
     // 32-column value tiles unless that leaves most of the 256 CUs idle
@@ -1588,12 +1592,12 @@ static hipError_t scan_launch(const void* q, const float* S0, void* o, float* S_
         constexpr int BV = 32;
         const long nblk = groups * 8 * (D / BV);
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV, EMIT>), dim3((unsigned)nblk), dim3(256), 0,
-                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound);
+                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound, hm);
     } else {
         constexpr int BV = 16;
         const long nblk = groups * 8 * (D / BV);
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV, EMIT>), dim3((unsigned)nblk), dim3(256), 0,
-                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound);
+                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound, hm);
     }
     return hipGetLastError();
 }
@@ -1601,9 +1605,9 @@ static hipError_t scan_launch(const void* q, const float* S0, void* o, float* S_
 // S_bound: NULL, or the states at every chunk boundary, [BH][nchunks][D][D] fp32
 template <typename E, int D, int KIND>
 static hipError_t scan_t(const void* q, const float* S0, void* o, float* S_final, const void* ws,
-                         int BH, int T, hipStream_t st, float* S_bound = nullptr) {
-    if (S_bound) return scan_launch<E, D, KIND, true>(q, S0, o, S_final, ws, BH, T, S_bound, st);
-    return scan_launch<E, D, KIND, false>(q, S0, o, S_final, ws, BH, T, nullptr, st);
+                         int BH, int T, hipStream_t st, HeadMap hm, float* S_bound) {
+    if (S_bound) return scan_launch<E, D, KIND, true>(q, S0, o, S_final, ws, BH, T, S_bound, st, hm);
+    return scan_launch<E, D, KIND, false>(q, S0, o, S_final, ws, BH, T, nullptr, st, hm);
 }
 
 // A new 64-bit epoch per fused launch: a random per-process prefix and a
@@ -1622,7 +1626,7 @@ static u64 next_epoch() {
 template <typename E, int D, int KIND, int BV>
 static hipError_t fused_t(const void* q, const void* k, const void* v, const void* beta,
                           const void* g, const float* S0, void* o, float* S_final, void* ws, int BH,
-                          int T, hipStream_t st) {
+                          int T, hipStream_t st, HeadMap hm) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int per_xcd = 2 * device_cu_count() / 8;
     const int ns = (BH + 7) / 8 * (D / BV);   // scan workgroups of the busiest XCD
@@ -1642,63 +1646,64 @@ static hipError_t fused_t(const void* q, const void* k, const void* v, const voi
     if ((long)np > (items + 1) / 2) np = (int)((items + 1) / 2);
     hipLaunchKernelGGL((chunk_fused_kernel<E, D, D, KIND, BV>), dim3((unsigned)(8 * (np + ns))), dim3(256),
                        0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
-                       (char*)ws, S0, (E*)o, S_final, T, nchunks, BH, np, next_epoch());
+                       (char*)ws, S0, (E*)o, S_final, T, nchunks, BH, np, next_epoch(), hm);
     return hipGetLastError();
 }
 
 template <typename E, int D>
 static hipError_t prep_kind(int kind, const void* q, const void* k, const void* v,
                             const void* beta, const void* g, void* ws, int BH, int T,
-                            hipStream_t st) {
-    if (kind == KIND_DELTANET) return prep_t<E, D, KIND_DELTANET>(q, k, v, beta, g, ws, BH, T, st);
-    if (kind == KIND_GATED) return prep_t<E, D, KIND_GATED>(q, k, v, beta, g, ws, BH, T, st);
+                            hipStream_t st, HeadMap hm) {
+    if (kind == KIND_DELTANET) return prep_t<E, D, KIND_DELTANET>(q, k, v, beta, g, ws, BH, T, st, hm);
+    if (kind == KIND_GATED) return prep_t<E, D, KIND_GATED>(q, k, v, beta, g, ws, BH, T, st, hm);
     // fp32 KDA at d = 128 exceeds the prep kernel's LDS budget (rejected by the ABI layer)
     if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
-    else return prep_t<E, D, KIND_KDA>(q, k, v, beta, g, ws, BH, T, st);
+    else return prep_t<E, D, KIND_KDA>(q, k, v, beta, g, ws, BH, T, st, hm);
 }
 
 template <typename E, int D>
 static hipError_t scan_kind(int kind, const void* q, const float* S0, void* o, float* S_final,
-                            const void* ws, int BH, int T, hipStream_t st,
+                            const void* ws, int BH, int T, hipStream_t st, HeadMap hm,
                             float* S_bound = nullptr) {
     // DeltaNet and Gated DeltaNet share the scan (a unit decay is stored for DeltaNet)
-    if (kind == KIND_KDA) return scan_t<E, D, KIND_KDA>(q, S0, o, S_final, ws, BH, T, st, S_bound);
-    return scan_t<E, D, KIND_GATED>(q, S0, o, S_final, ws, BH, T, st, S_bound);
+    if (kind == KIND_KDA) return scan_t<E, D, KIND_KDA>(q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
+    return scan_t<E, D, KIND_GATED>(q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
 }
 
 hipError_t launch_chunk_prep(int kind, int dtype, const void* q, const void* k, const void* v,
                              const void* beta, const void* g, void* ws, int BH, int T, int dk,
-                             int dv, hipStream_t st) {
+                             int dv, hipStream_t st, HeadMap hm) {
     (void)dv;
     if (dtype == DT_BF16)
-        return dk == 128 ? prep_kind<bf16, 128>(kind, q, k, v, beta, g, ws, BH, T, st)
-                         : prep_kind<bf16, 64>(kind, q, k, v, beta, g, ws, BH, T, st);
-    return dk == 128 ? prep_kind<float, 128>(kind, q, k, v, beta, g, ws, BH, T, st)
-                     : prep_kind<float, 64>(kind, q, k, v, beta, g, ws, BH, T, st);
+        return dk == 128 ? prep_kind<bf16, 128>(kind, q, k, v, beta, g, ws, BH, T, st, hm)
+                         : prep_kind<bf16, 64>(kind, q, k, v, beta, g, ws, BH, T, st, hm);
+    return dk == 128 ? prep_kind<float, 128>(kind, q, k, v, beta, g, ws, BH, T, st, hm)
+                     : prep_kind<float, 64>(kind, q, k, v, beta, g, ws, BH, T, st, hm);
 }
 
 hipError_t launch_chunk_scan(int kind, int dtype, const void* q, const float* S0, void* o,
                              float* S_final, const void* ws, int BH, int T, int dk, int dv,
-                             hipStream_t st) {
+                             hipStream_t st, HeadMap hm) {
     (void)dv;
     if (dtype == DT_BF16)
-        return dk == 128 ? scan_kind<bf16, 128>(kind, q, S0, o, S_final, ws, BH, T, st)
-                         : scan_kind<bf16, 64>(kind, q, S0, o, S_final, ws, BH, T, st);
-    return dk == 128 ? scan_kind<float, 128>(kind, q, S0, o, S_final, ws, BH, T, st)
-                     : scan_kind<float, 64>(kind, q, S0, o, S_final, ws, BH, T, st);
+        return dk == 128 ? scan_kind<bf16, 128>(kind, q, S0, o, S_final, ws, BH, T, st, hm)
+                         : scan_kind<bf16, 64>(kind, q, S0, o, S_final, ws, BH, T, st, hm);
+    return dk == 128 ? scan_kind<float, 128>(kind, q, S0, o, S_final, ws, BH, T, st, hm)
+                     : scan_kind<float, 64>(kind, q, S0, o, S_final, ws, BH, T, st, hm);
 }
 
 hipError_t launch_chunk_fwd_states(int kind, int dtype, const void* q, const void* k,
                                    const void* v, const void* beta, const void* g,
                                    const float* S0, void* o, float* S_final, float* S_bound,
-                                   void* ws, int BH, int T, int dk, int dv, hipStream_t st) {
-    const hipError_t e = launch_chunk_prep(kind, dtype, q, k, v, beta, g, ws, BH, T, dk, dv, st);
+                                   void* ws, int BH, int T, int dk, int dv, hipStream_t st,
+                                   HeadMap hm) {
+    const hipError_t e = launch_chunk_prep(kind, dtype, q, k, v, beta, g, ws, BH, T, dk, dv, st, hm);
     if (e != hipSuccess) return e;
     if (dtype == DT_BF16)
-        return dk == 128 ? scan_kind<bf16, 128>(kind, q, S0, o, S_final, ws, BH, T, st, S_bound)
-                         : scan_kind<bf16, 64>(kind, q, S0, o, S_final, ws, BH, T, st, S_bound);
-    return dk == 128 ? scan_kind<float, 128>(kind, q, S0, o, S_final, ws, BH, T, st, S_bound)
-                     : scan_kind<float, 64>(kind, q, S0, o, S_final, ws, BH, T, st, S_bound);
+        return dk == 128 ? scan_kind<bf16, 128>(kind, q, S0, o, S_final, ws, BH, T, st, hm, S_bound)
+                         : scan_kind<bf16, 64>(kind, q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
+    return dk == 128 ? scan_kind<float, 128>(kind, q, S0, o, S_final, ws, BH, T, st, hm, S_bound)
+                     : scan_kind<float, 64>(kind, q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
 }
 
 // One-launch prefill where it exists: bf16, DeltaNet or Gated DeltaNet, and
@@ -1706,17 +1711,17 @@ hipError_t launch_chunk_fwd_states(int kind, int dtype, const void* q, const voi
 template <typename E, int D>
 static hipError_t fused_kind(int kind, const void* q, const void* k, const void* v, const void* beta,
                              const void* g, const float* S0, void* o, float* S_final, void* ws,
-                             int BH, int T, hipStream_t st) {
+                             int BH, int T, hipStream_t st, HeadMap hm) {
     if constexpr (sizeof(E) != 2) {
         return hipErrorNotSupported;
     } else {
         if (kind == KIND_KDA) return hipErrorNotSupported;
         const bool wide = scan_bv<D>(BH) == 32;
         if (kind == KIND_GATED)
-            return wide ? fused_t<E, D, KIND_GATED, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st)
-                        : fused_t<E, D, KIND_GATED, 16>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st);
-        return wide ? fused_t<E, D, KIND_DELTANET, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st)
-                    : fused_t<E, D, KIND_DELTANET, 16>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st);
+            return wide ? fused_t<E, D, KIND_GATED, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm)
+                        : fused_t<E, D, KIND_GATED, 16>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
+        return wide ? fused_t<E, D, KIND_DELTANET, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm)
+                    : fused_t<E, D, KIND_DELTANET, 16>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
     }
 }
 
@@ -1729,27 +1734,27 @@ constexpr int FUSED_MIN_CHUNKS = 64;
 template <typename E, int D>
 static hipError_t fwd_t(int kind, const void* q, const void* k, const void* v, const void* beta,
                         const void* g, const float* S0, void* o, float* S_final, void* ws, int BH,
-                        int T, int mode, hipStream_t st) {
+                        int T, int mode, hipStream_t st, HeadMap hm) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     if (mode == FWD_FUSED || (mode == FWD_AUTO && nchunks >= FUSED_MIN_CHUNKS)) {
-        const hipError_t e = fused_kind<E, D>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, st);
+        const hipError_t e = fused_kind<E, D>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
         if (e != hipErrorNotSupported || mode == FWD_FUSED) return e;
     }
-    hipError_t e = prep_kind<E, D>(kind, q, k, v, beta, g, ws, BH, T, st);
+    hipError_t e = prep_kind<E, D>(kind, q, k, v, beta, g, ws, BH, T, st, hm);
     if (e != hipSuccess) return e;
-    return scan_kind<E, D>(kind, q, S0, o, S_final, ws, BH, T, st);
+    return scan_kind<E, D>(kind, q, S0, o, S_final, ws, BH, T, st, hm);
 }
 
 hipError_t launch_chunk_fwd(int kind, int dtype, const void* q, const void* k, const void* v,
                             const void* beta, const void* g, const float* S0, void* o,
                             float* S_final, void* ws, int BH, int T, int dk, int dv, int mode,
-                            hipStream_t st) {
+                            hipStream_t st, HeadMap hm) {
     (void)dv;
     if (dtype == DT_BF16)
-        return dk == 128 ? fwd_t<bf16, 128>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st)
-                         : fwd_t<bf16, 64>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st);
-    return dk == 128 ? fwd_t<float, 128>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st)
-                     : fwd_t<float, 64>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st);
+        return dk == 128 ? fwd_t<bf16, 128>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st, hm)
+                         : fwd_t<bf16, 64>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st, hm);
+    return dk == 128 ? fwd_t<float, 128>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st, hm)
+                     : fwd_t<float, 64>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st, hm);
 }
 
 }  // namespace dn

@@ -27,7 +27,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ 
                                                           const E* __restrict__ beta,
                                                           const E* __restrict__ g,
                                                           float* __restrict__ S,
-                                                          E* __restrict__ o) {
+                                                          E* __restrict__ o, HeadMap hm) {
     constexpr int CW = DV / NSPLIT;   // value columns of this workgroup
     constexpr int CQ = CW / 4;        // column quads per row
     constexpr int RG = 256 / CQ;      // row groups
@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ 
     typedef typename Vec4<E>::type V4;
 
     const long bh = blockIdx.x / NSPLIT;
+    const long bk = hm.key(bh);   // q, k row (uniform: computed once, before any load)
     const int col0 = (int)(blockIdx.x % NSPLIT) * CW;
     const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
     const int cq = t % CQ, rg = t / CQ;
@@ -49,8 +50,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ 
     __shared__ f32x4 red_p[4][CQ], red_r[4][CQ];
     __shared__ float red_kq[4];
     if (t < DK) {
-        sk[t] = to_f32(k[bh * DK + t]);
-        sq[t] = to_f32(q[bh * DK + t]);
+        sk[t] = to_f32(k[bk * DK + t]);
+        sq[t] = to_f32(q[bk * DK + t]);
         if (KIND == KIND_KDA) sa[t] = __expf(to_f32(g[bh * DK + t]));
     }
     const V4 vraw = *reinterpret_cast<const V4*>(v + bh * DV + col0 + 4 * cq);
@@ -214,7 +215,7 @@ __global__ void state_copy_kernel(const float* __restrict__ S0, float* __restric
 // ---------------------------------------------------------------------------
 template <typename E, int D>
 static hipError_t decode_t(int kind, const void* q, const void* k, const void* v, const void* beta,
-                           const void* g, float* S, void* o, int BH, hipStream_t st) {
+                           const void* g, float* S, void* o, int BH, hipStream_t st, HeadMap hm) {
     const E *q_ = (const E*)q, *k_ = (const E*)k, *v_ = (const E*)v, *b_ = (const E*)beta,
             *g_ = (const E*)g;
     E* o_ = (E*)o;
@@ -225,23 +226,23 @@ static hipError_t decode_t(int kind, const void* q, const void* k, const void* v
     constexpr int NS = 4;
     dim3 grid((unsigned)((long)BH * NS)), block(256);
     if (kind == KIND_DELTANET)
-        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_DELTANET, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_);
+        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_DELTANET, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_, hm);
     else if (kind == KIND_GATED)
-        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_GATED, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_);
+        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_GATED, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_, hm);
     else
-        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_KDA, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_);
+        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_KDA, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_, hm);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(int kind, int dtype, const void* q, const void* k, const void* v,
                          const void* beta, const void* g, float* S, void* o, int BH, int dk,
-                         int dv, hipStream_t st) {
+                         int dv, hipStream_t st, HeadMap hm) {
     (void)dv;
     if (dtype == DT_BF16)
-        return dk == 128 ? decode_t<bf16, 128>(kind, q, k, v, beta, g, S, o, BH, st)
-                         : decode_t<bf16, 64>(kind, q, k, v, beta, g, S, o, BH, st);
-    return dk == 128 ? decode_t<float, 128>(kind, q, k, v, beta, g, S, o, BH, st)
-                     : decode_t<float, 64>(kind, q, k, v, beta, g, S, o, BH, st);
+        return dk == 128 ? decode_t<bf16, 128>(kind, q, k, v, beta, g, S, o, BH, st, hm)
+                         : decode_t<bf16, 64>(kind, q, k, v, beta, g, S, o, BH, st, hm);
+    return dk == 128 ? decode_t<float, 128>(kind, q, k, v, beta, g, S, o, BH, st, hm)
+                     : decode_t<float, 64>(kind, q, k, v, beta, g, S, o, BH, st, hm);
 }
 
 template <typename E, int D>

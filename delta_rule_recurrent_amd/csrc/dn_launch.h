@@ -12,10 +12,24 @@ enum DType { DT_F32 = 0, DT_BF16 = 1 };
 
 constexpr int CHUNK = 64;
 
+// Several value heads may share one key head (q and k repeated over the head
+// axis, each key head serving g consecutive value heads). Head rows bh run over
+// B x hv value heads; q and k are read at key-head row key(bh) of B x hv/g.
+// The default (g == 1) is one key head per value head.
+struct HeadMap {
+    int hv = 1;   // value heads per sequence
+    int g = 1;    // value heads per key head
+    // (head rows are below 2^24: 32-bit arithmetic)
+    __host__ __device__ long key(long bh) const {
+        const int r = (int)bh;
+        return g == 1 ? bh : (long)((r / hv) * (hv / g) + (r % hv) / g);
+    }
+};
+
 // One fused decode step for BH (sequence, head) states.
 hipError_t launch_decode(int kind, int dtype, const void* q, const void* k, const void* v,
                          const void* beta, const void* g, float* S, void* o, int BH, int dk,
-                         int dv, hipStream_t stream);
+                         int dv, hipStream_t stream, HeadMap hm = HeadMap());
 
 // Token-by-token recurrence over T tokens.
 hipError_t launch_recurrent(int kind, int dtype, const void* q, const void* k, const void* v,
@@ -25,12 +39,12 @@ hipError_t launch_recurrent(int kind, int dtype, const void* q, const void* k, c
 // Chunkwise prefill, phase 1: every chunk in parallel, intermediates -> workspace.
 hipError_t launch_chunk_prep(int kind, int dtype, const void* q, const void* k, const void* v,
                              const void* beta, const void* g, void* workspace, int BH, int T,
-                             int dk, int dv, hipStream_t stream);
+                             int dk, int dv, hipStream_t stream, HeadMap hm = HeadMap());
 
 // Chunkwise prefill, phase 2: sequential scan over the chunks of every head.
 hipError_t launch_chunk_scan(int kind, int dtype, const void* q, const float* S0, void* o,
                              float* S_final, const void* workspace, int BH, int T, int dk, int dv,
-                             hipStream_t stream);
+                             hipStream_t stream, HeadMap hm = HeadMap());
 
 // Whole chunkwise prefill. FWD_TWO: the two phases above in order.
 // FWD_FUSED: one launch (prep and scan workgroups together), or
@@ -40,14 +54,15 @@ enum FwdMode { FWD_TWO = 0, FWD_FUSED = 1, FWD_AUTO = 2 };
 hipError_t launch_chunk_fwd(int kind, int dtype, const void* q, const void* k, const void* v,
                             const void* beta, const void* g, const float* S0, void* o,
                             float* S_final, void* workspace, int BH, int T, int dk, int dv,
-                            int mode, hipStream_t stream);
+                            int mode, hipStream_t stream, HeadMap hm = HeadMap());
 
 // Two-phase prefill that also writes the state after every chunk:
 // S_bound [BH][ceil(T/64)][dk][dv] fp32.
 hipError_t launch_chunk_fwd_states(int kind, int dtype, const void* q, const void* k,
                                    const void* v, const void* beta, const void* g,
                                    const float* S0, void* o, float* S_final, float* S_bound,
-                                   void* ws, int BH, int T, int dk, int dv, hipStream_t stream);
+                                   void* ws, int BH, int T, int dk, int dv, hipStream_t stream,
+                                   HeadMap hm = HeadMap());
 
 // Workspace bytes of the chunkwise prefill (per call).
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype);

@@ -208,6 +208,31 @@ int dn_kda_decode_step(const void* q, const void* k, const void* v, const void* 
                        const void* g, float* S, void* o,
                        int B, int H, int dk, int dv, int dtype, void* stream);
 
+/*
+ * Several value heads sharing one key head. The gated layer on page "28.
+ * Linear attention and Gated DeltaNet" (section "The full layer")
+ * has more value heads than key heads and repeats q and k over the head axis
+ * (each key head serving Hv/Hk consecutive value heads) before the rule runs;
+ * these entry points read the shared q and k in place instead of a repeated
+ * copy. Results equal dn_chunk_fwd / dn_kda_chunk_fwd / dn_decode_step /
+ * dn_kda_decode_step on the repeated q and k, bitwise.
+ *   kda      0: DeltaNet (g NULL) or Gated DeltaNet; nonzero: KDA (g required)
+ *   q, k     [B,Hk,T,dk] (prefill) or [B,Hk,dk] (decode)
+ *   v, o     [B,Hv,T,dv] or [B,Hv,dv];  beta [B,Hv,T] or [B,Hv]
+ *   g        per value head: [B,Hv,T] / [B,Hv] (gated), [B,Hv,T,dk] / [B,Hv,dk] (KDA)
+ *   S0, S_final, S: [B,Hv,dk,dv] fp32
+ *   Hk >= 1 and Hv a multiple of Hk, else DN_EINVAL. The workspace is
+ *   dn_chunk_fwd_workspace(B, Hv, T, dk, dv, dtype). Every other rule is that
+ *   of the matching entry point above.
+ */
+int dn_chunk_fwd_gqa(int kda, const void* q, const void* k, const void* v,
+                     const void* beta, const void* g, const float* S0, void* o,
+                     float* S_final, int B, int Hk, int Hv, int T, int dk, int dv,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int dn_decode_step_gqa(int kda, const void* q, const void* k, const void* v,
+                       const void* beta, const void* g, float* S, void* o, int B,
+                       int Hk, int Hv, int dk, int dv, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

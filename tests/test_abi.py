@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -121,6 +121,41 @@ def test_boundary_states_validation():
     assert _states(ws_bytes=16) == W
     # T == 0 with no S_final: nothing to do, no launch
     assert _states(T=0, S_chunks=None, S_final=None) == _lib.DN_OK
+
+
+def _gqa(**kw):
+    args = dict(kda=0, q=P, k=P, v=P, beta=P, g=P, S0=P, o=P, S_final=P, B=1, Hk=2, Hv=6, T=64,
+                dk=64, dv=64, dtype=1, ws=WS, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return _lib.lib().dn_chunk_fwd_gqa(*[args[n] for n in (
+        "kda", "q", "k", "v", "beta", "g", "S0", "o", "S_final", "B", "Hk", "Hv", "T", "dk", "dv",
+        "dtype", "ws", "ws_bytes", "stream")])
+
+
+def _gqa_dec(**kw):
+    args = dict(kda=0, q=P, k=P, v=P, beta=P, g=P, S=P, o=P, B=1, Hk=2, Hv=6, dk=128, dv=128,
+                dtype=1, stream=None)
+    args.update(kw)
+    return _lib.lib().dn_decode_step_gqa(*[args[n] for n in (
+        "kda", "q", "k", "v", "beta", "g", "S", "o", "B", "Hk", "Hv", "dk", "dv", "dtype",
+        "stream")])
+
+
+def test_shared_key_heads_validation():
+    E, N, W = _lib.DN_EINVAL, _lib.DN_ENOTSUP, _lib.DN_EWORKSPACE
+    for fn in (_gqa, _gqa_dec):
+        assert fn(Hk=0) == E
+        assert fn(Hv=0) == E
+        assert fn(Hk=4, Hv=6) == E                 # value heads not a multiple of key heads
+        assert fn(Hk=3, Hv=2) == E
+        assert fn(q=None) == E
+        assert fn(B=0) == E
+        assert fn(kda=1, g=None) == E
+        assert fn(dk=96, dv=96) == N
+    assert _gqa(ws=None) == W
+    assert _gqa(ws_bytes=16) == W
+    assert _gqa(kda=1, dtype=0, dk=128, dv=128) == N
+    assert _gqa_dec(S=None) == E
 
 
 def _rec(fn, **kw):

@@ -296,3 +296,63 @@ def test_boundary_states(kind, dtype, d):
         worst = max(worst, e)
         assert e <= TOL[dtype], (c, e)
     say("  worst boundary-state err %.3e" % worst)
+
+
+def _gqa_inputs(kind, B, Hk, Hv, T, d, dtype, seed):
+    """q, k drawn for Hk key heads; v, beta, g and S0 for Hv value heads."""
+    kv = make(kind, B, Hk, T, d, dtype, seed=seed)
+    vv = make(kind, B, Hv, T, d, dtype, seed=seed + 1, s0_std=0.5)
+    inp = dict(vv)
+    inp["q"], inp["k"] = kv["q"], kv["k"]
+    rep = dict(inp)
+    rep["q"] = inp["q"].repeat_interleave(Hv // Hk, dim=1).contiguous()
+    rep["k"] = inp["k"].repeat_interleave(Hv // Hk, dim=1).contiguous()
+    return inp, rep
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("dtype,d,T,Hk,Hv", [("bf16", 128, 200, 2, 6), ("f32", 64, 137, 1, 3),
+                                             ("bf16", 128, 64 * 64 + 5, 1, 2)])
+def test_gqa_prefill(kind, dtype, d, T, Hk, Hv):
+    """Key heads shared by value heads: bitwise equal to the plain prefill on
+    q, k repeated over heads (the pages' repeat_interleave), and within the
+    bound of the oracle run on that repetition. T = 4101 takes the one-launch
+    form for the kinds that have it."""
+    if kind == "kda" and T > 1000:
+        pytest.skip("one long case per form is enough; KDA has only the two-phase form")
+    dn = _dn()
+    say("gqa prefill", kind, dtype, d, T, Hk, Hv)
+    inp, rep = _gqa_inputs(kind, 1 if T > 1000 else 2, Hk, Hv, T, d, dtype, seed=51)
+    di, dr = to_dev(inp), to_dev(rep)
+    o, S = dn.chunk_fwd_gqa(di["q"], di["k"], di["v"], di["beta"], di["g"], di["S0"],
+                            kda=(kind == "kda"))
+    fn = dn.kda_chunk_fwd if kind == "kda" else dn.chunk_fwd
+    o2, S2 = fn(dr["q"], dr["k"], dr["v"], dr["beta"], dr["g"], dr["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2)
+    o_ref, S_ref = oracle_prefill(rep)
+    eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
+    say("  err o %.3e  S %.3e" % (eo, es))
+    assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_gqa_decode(kind):
+    """One decode step with shared key heads equals the plain step on the
+    repetition, bitwise, and the oracle within the bound."""
+    dn = _dn()
+    B, Hk, Hv, d = 3, 2, 8, 128
+    inp, rep = _gqa_inputs(kind, B, Hk, Hv, 1, d, "bf16", seed=61)
+    di, dr = to_dev(inp), to_dev(rep)
+    one = lambda x: None if x is None else x[:, :, 0].contiguous()   # noqa: E731
+    S1, S2 = di["S0"].clone(), di["S0"].clone()
+    o1 = dn.decode_step_gqa(one(di["q"]), one(di["k"]), one(di["v"]), one(di["beta"]), one(di["g"]),
+                            S1, kda=(kind == "kda"))
+    fn = dn.kda_decode_step if kind == "kda" else dn.decode_step
+    o2 = fn(one(dr["q"]), one(dr["k"]), one(dr["v"]), one(dr["beta"]), one(dr["g"]), S2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    o_ref, S_ref = oracle_prefill(rep)
+    eo, es = rel_err(o1, o_ref[:, :, 0]), rel_err(S1, S_ref)
+    say("gqa decode", kind, "err o %.3e  S %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
