@@ -20,7 +20,7 @@ from . import _lib
 from ._lib import DeltaNetError, lib
 
 __all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_fwd_gqa",
-           "decode_step_gqa", "chunk_prep", "chunk_scan", "recurrent_fwd",
+           "decode_step_gqa", "chunk_fwd_varlen", "chunk_prep", "chunk_scan", "recurrent_fwd",
            "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
            "DeltaNetError", "lib", "library_path"]
 
@@ -241,6 +241,46 @@ def decode_step_gqa(q, k, v, beta, g, S, *, kda=False, o=None, stream=None):
                                   _ptr(S), _ptr(o), B, Hk, Hv, dk, dv, _DT[dt], _stream(stream))
     _lib.check("dn_decode_step_gqa", st)
     return o
+
+
+def chunk_fwd_varlen(q, k, v, beta, g, cu_seqlens, S0=None, *, kda=False, output_final_state=True,
+                     o=None, S_final=None, workspace=None, stream=None):
+    """Chunkwise prefill over packed sequences of different lengths.
+
+    q, k [1,H,T,dk], v [1,H,T,dv], beta [1,H,T], g [1,H,T] / [1,H,T,dk] (KDA) /
+    None: the sequences back to back; cu_seqlens int32 [N+1] on the device
+    (sequence n = tokens cu_seqlens[n] .. cu_seqlens[n+1]-1); S0 [N,H,dk,dv].
+    Returns (o [1,H,T,dv], S_final [N,H,dk,dv] fp32 or None).
+    """
+    B, H, T, dk, dv, dev, dt = _prefill_args(q, k, v, beta, g, None, kda)
+    if B != 1:
+        raise ValueError("packed sequences take B = 1 (q [1,H,T,dk])")
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or \
+            cu_seqlens.dtype != torch.int32 or cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens must be an int32 [N+1] tensor on %s" % dev)
+    N = cu_seqlens.numel() - 1
+    if N < 1:
+        raise ValueError("cu_seqlens needs at least two entries")
+    cu_seqlens = cu_seqlens.contiguous()
+    if S0 is not None:
+        _check_tensor("S0", S0, (N, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(1, H, T, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (1, H, T, dv), dt, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty(N, H, dk, dv, dtype=torch.float32, device=dev)
+    elif S_final is not None:
+        _check_tensor("S_final", S_final, (N, H, dk, dv), torch.float32, dev)
+    if workspace is None:
+        need = int(lib().dn_chunk_fwd_varlen_workspace(N, H, T, dk, dv, _DT[dt]))
+        workspace = _alloc_workspace(need, dev)
+    st = lib().dn_chunk_fwd_varlen(int(kda), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g),
+                                   _ptr(S0), _ptr(o), _ptr(S_final), _ptr(cu_seqlens), N, H, T, dk,
+                                   dv, _DT[dt], _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("dn_chunk_fwd_varlen", st)
+    return o, S_final
 
 
 def chunk_prep(q, k, v, beta, g, workspace, *, kda=False, stream=None):

@@ -209,6 +209,39 @@ int dn_decode_step_gqa(int kda, const void* q, const void* k, const void* v, con
                          beta, g, S, o, B, Hv, dk, dv, dtype, stream, hm);
 }
 
+size_t dn_chunk_fwd_varlen_workspace(int N, int H, int T, int dk, int dv, int dtype) {
+    if (N < 1 || H < 1 || T < 0) return 0;
+    if ((dk != 64 && dk != 128) || dk != dv) return 0;
+    if (dtype != DN_F32 && dtype != DN_BF16) return 0;
+    if (T == 0) return 0;
+    return dn::chunk_varlen_workspace_bytes(N, H, T, dk, dv, dtype);
+}
+
+int dn_chunk_fwd_varlen(int kda, const void* q, const void* k, const void* v, const void* beta,
+                        const void* g, const float* S0, void* o, float* S_final,
+                        const int* cu_seqlens, int N, int H, int T, int dk, int dv, int dtype,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (N < 1 || !cu_seqlens || misaligned(cu_seqlens, 4)) return DN_EINVAL;
+    int st = check_common(q, k, v, beta, g, kda != 0, S0, o, S_final, 1, H, T, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    if (kda && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
+    const long long rows = (long long)N * H;
+    const long long nc = ((long long)T + 63) / 64 + N;
+    if (rows > (1LL << 24) || nc * H > 0x7fffffffLL) return DN_EINVAL;
+    if (T == 0) {
+        if (!S_final) return DN_OK;
+        return hip_status(dn::launch_state_copy(S0, S_final, rows * dk * dv, as_stream(stream)));
+    }
+    const size_t need = dn::chunk_varlen_workspace_bytes(N, H, T, dk, dv, dtype);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return DN_EWORKSPACE;
+    const hipError_t e = dn::launch_chunk_fwd_varlen(chunk_kind(kda != 0, g), dtype, q, k, v, beta,
+                                                     g, S0, o, S_final, cu_seqlens, N, H, T, dk,
+                                                     dv, workspace, as_stream(stream));
+    if (e == hipErrorNotSupported) return DN_ENOTSUP;
+    return hip_status(e);
+}
+
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,
                   const void* g, int B, int H, int T, int dk, int dv, int dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {

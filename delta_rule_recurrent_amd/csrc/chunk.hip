@@ -86,7 +86,10 @@ struct TileRegs {
 // wait for exactly these loads later, with other memory operations in flight.
 template <typename E, int D>
 __device__ __forceinline__ void tile_load(TileRegs<E, D>& r, const E* __restrict__ src, int L,
-                                          int tid) {
+                                          int tid, int Lmask = -1) {
+    // rows are read at min(t, L - 1) (L >= 1) and kept where t < Lmask
+    // (Lmask defaults to L; an empty chunk passes L = 1, Lmask = 0)
+    if (Lmask < 0) Lmask = L;
     typedef TileRegs<E, D> R;
     typedef typename R::V16 V16;
 #pragma unroll
@@ -97,7 +100,7 @@ __device__ __forceinline__ void tile_load(TileRegs<E, D>& r, const E* __restrict
         for (int u = 0; u < 4; ++u) {
             const int t = 4 * tq + u;
             const V16 val = *reinterpret_cast<const V16*>(src + (long)min(t, L - 1) * D + cv * R::VEC);
-            r.x[it][u] = (t < L) ? val : V16{};
+            r.x[it][u] = (t < Lmask) ? val : V16{};
         }
     }
 }
@@ -222,7 +225,7 @@ struct PrepSmem {
 // ---------------------------------------------------------------------------
 // Two workgroups share a compute unit where the LDS allows it; the register
 // budget is capped accordingly.
-template <typename E, int DK, int DV, int KIND>
+template <typename E, int DK, int DV, int KIND, bool VARLEN = false>
 __global__ __launch_bounds__(256, (PrepSmem<E, DK, DV, KIND>::TOTAL + 1024) * 2 <= 163840 ? 2 : 1)
 void chunk_prep_kernel(const E* __restrict__ q,
                                                          const E* __restrict__ k,
@@ -230,7 +233,8 @@ void chunk_prep_kernel(const E* __restrict__ q,
                                                          const E* __restrict__ beta,
                                                          const E* __restrict__ g,
                                                          char* __restrict__ ws, int T,
-                                                         int nchunks, int nitems, HeadMap hm) {
+                                                         int nchunks, int nitems, HeadMap hm,
+                                                         const int2* __restrict__ ctab = nullptr) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef PrepSmem<E, DK, DV, KIND> Sm;
     typedef typename Frag<E>::type F;
@@ -267,15 +271,26 @@ void chunk_prep_kernel(const E* __restrict__ q,
     bool pin = false;   // token `lane` is inside the chunk
     auto fetch = [&](int it) {
         const int fc = it % nchunks;
-        const long ftok = (long)(it / nchunks) * T + (long)fc * CHUNK;
-        const long fkey = hm.key(it / nchunks) * T + (long)fc * CHUNK;   // q, k row
-        const int fL = min(CHUNK, T - fc * CHUNK);
-        tile_load<E, DK>(rk, k + fkey * DK, fL, tid);
-        tile_load<E, DK>(rq, q + fkey * DK, fL, tid);
-        tile_load<E, DV>(rv, v + ftok * DV, fL, tid);
-        if (KDA) tile_load<E, DK>(rg, g + ftok * DK, fL, tid);
+        long ftok, fkey;
+        int fL, fA;   // tokens of the chunk; fA >= 1 bounds the row addresses
+        if constexpr (VARLEN) {
+            // packed sequences: item = head * nchunks + global chunk, the chunk's
+            // first token and length from the chunk table (length 0: unused slot)
+            const int2 e = ctab[fc];
+            ftok = fkey = (long)(it / nchunks) * T + e.x;
+            fL = e.y;
+            fA = max(e.y, 1);
+        } else {
+            ftok = (long)(it / nchunks) * T + (long)fc * CHUNK;
+            fkey = hm.key(it / nchunks) * T + (long)fc * CHUNK;   // q, k row
+            fL = fA = min(CHUNK, T - fc * CHUNK);
+        }
+        tile_load<E, DK>(rk, k + fkey * DK, fA, tid, fL);
+        tile_load<E, DK>(rq, q + fkey * DK, fA, tid, fL);
+        tile_load<E, DV>(rv, v + ftok * DV, fA, tid, fL);
+        if (KDA) tile_load<E, DK>(rg, g + ftok * DK, fA, tid, fL);
         if (w == 0) {
-            const long tk = ftok + min(lane, fL - 1);
+            const long tk = ftok + min(lane, fA - 1);
             pbr = beta[tk];
             if (KIND == KIND_GATED) pgr = g[tk];
             pin = lane < fL;
@@ -694,7 +709,7 @@ template <typename E, int DK, int DV, int KIND>
 __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __restrict__ k,
                                            const E* __restrict__ v, const E* __restrict__ beta,
                                            const E* __restrict__ g, char* __restrict__ blk,
-                                           Prep2Lds<E, DK, DV>& lds, long bh, long bhk, int c, int T,
+                                           Prep2Lds<E, DK, DV>& lds, long tok0, long tokk, int L,
                                            int w, int lane) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef Prep2Smem<E, DK, DV> Sm;
@@ -711,10 +726,8 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
     F* Vl = reinterpret_cast<F*>(smem + Sm::AT_BYTES);
 
     const int gq = lane >> 4, n = lane & 15;
-    const int t0 = c * CHUNK;
-    const int L = min(CHUNK, T - t0);
-    const long tok0 = bh * T + t0;
-    const long tokk = bhk * T + t0;   // q and k (key-head row)
+    // tok0: the chunk's first token (value-head row), tokk: the same token in
+    // the q, k rows; L: tokens of the chunk (1..64)
 
     F* Wf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::W_OFF);
     F* Kf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::K_OFF);
@@ -945,9 +958,32 @@ __global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict
                                                              int nchunks, HeadMap hm) {
     __shared__ Prep2Lds<E, DK, DV> lds;
     const long item = blockIdx.x;
+    const long bh = item / nchunks;
+    const int t0 = (int)(item % nchunks) * CHUNK;
     prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV>::BYTES, lds,
-                                item / nchunks, hm.key(item / nchunks), (int)(item % nchunks), T,
+                                bh * T + t0, hm.key(bh) * T + t0, min(CHUNK, T - t0),
                                 (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
+}
+
+// Packed sequences of different lengths: item = head * nchunks + global chunk;
+// the chunk's first token and length come from the chunk table (slots past the
+// last chunk have length 0 and are skipped).
+template <typename E, int DK, int DV, int KIND>
+__global__ __launch_bounds__(128, 2) void chunk_prep2_varlen_kernel(const E* __restrict__ q,
+                                                                    const E* __restrict__ k,
+                                                                    const E* __restrict__ v,
+                                                                    const E* __restrict__ beta,
+                                                                    const E* __restrict__ g,
+                                                                    char* __restrict__ ws, int T,
+                                                                    int nchunks,
+                                                                    const int2* __restrict__ ctab) {
+    __shared__ Prep2Lds<E, DK, DV> lds;
+    const long item = blockIdx.x;
+    const int2 e = ctab[item % nchunks];
+    if (e.y == 0) return;
+    const long tok0 = (item / nchunks) * T + e.x;
+    prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV>::BYTES, lds,
+                                tok0, tok0, e.y, (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
 }
 
 // ---------------------------------------------------------------------------
@@ -1084,6 +1120,19 @@ __device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV, KIND>& x, const
 // load parts stay where they are placed in the step).
 __device__ __forceinline__ void sched_fence() { asm volatile("" ::: "memory"); }
 
+// One head row's sequence as the scan sees it: where its chunk blocks, q rows,
+// o rows and states are, and how long it is. For a batch of equal lengths
+// row bh holds tokens bh*T ..; for packed sequences of different lengths the
+// rows start at the sequence offsets.
+struct SeqView {
+    const char* wsh;   // the row's first chunk block (its chunks are consecutive)
+    long qrow;         // q row of the sequence's first token (key-head row for shared heads)
+    long orow;         // o row of the sequence's first token
+    long srow;         // index of the row's states in S0 / S_final / boundary states
+    int len;           // tokens (>= 1)
+    int nchunks;       // ceil(len / 64)
+};
+
 // One chunk of the scan for one workgroup: U = u - W S, O = Q~ S + attn U,
 // S = gamma S + K~^T U. S (fp32, MFMA accumulator layout) is updated in
 // place; the operands of chunk c+2 (`nxt`, from block `nblk`) are loaded in
@@ -1094,7 +1143,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cu
                                           f32x4 (&S)[DK / 64][BV / 16],
                                           typename Frag<E>::type (*Sx)[BV / 16][64],
                                           typename Frag<E>::type (*Ux)[BV / 16][64], E* ob, E* qs,
-                                          E* __restrict__ o, long bh, int T, int t0, int vt,
+                                          E* __restrict__ o, long orow, int len, int t0, int vt,
                                           int w, int lane, const char* pfblk, float& pf) {
     typedef ScanOps<E, DK, DV, BV, KIND> Ops;
     typedef typename Ops::F F;
@@ -1195,7 +1244,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cu
         const int row = p / PER_ROW, col = (p % PER_ROW) * VEC;
         const int t = t0 + 16 * w + row;
         const V16 val = *reinterpret_cast<const V16*>(&ob[row * LDO + col]);
-        if (t < T) *reinterpret_cast<V16*>(o + ((long)bh * T + t) * DV + vt * BV + col) = val;
+        if (t < len) *reinterpret_cast<V16*>(o + (orow + t) * DV + vt * BV + col) = val;
     }
     if constexpr (PF) {
         // Pull a later chunk's block from HBM into L2: one 4-byte load per
@@ -1285,12 +1334,11 @@ __device__ __forceinline__ u64* block_tags(char* ws, long BH, int nchunks) {
 // operands are loaded. RING: 3 (two chunks prefetched) or 2 (one chunk; fewer
 // registers held, which leaves the fused launch's register budget room).
 template <typename E, int DK, int DV, int KIND, int BV, bool SYNC, int RING, bool EMIT = false>
-__device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* __restrict__ q,
+__device__ __forceinline__ void scan_body(const SeqView& sv, const E* __restrict__ q,
                                           const float* __restrict__ S0, E* __restrict__ o,
-                                          float* __restrict__ S_final, int T, int nchunks,
-                                          long bh, int vt, int w, int lane,
+                                          float* __restrict__ S_final, int vt, int w, int lane,
                                           ScanLds<E, DK, DV, KIND, BV>& lds, const u64* tags,
-                                          u64 tag, u64* err, u64 epoch, HeadMap hm,
+                                          u64 tag, u64* err, u64 epoch,
                                           float* __restrict__ S_bound = nullptr) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef ScanOps<E, DK, DV, BV, KIND> Ops;
@@ -1307,7 +1355,7 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int row = 16 * (w * MTW + m) + 4 * gq + e, col = vt * BV + 16 * nt + n;
-                    S[m][nt][e] = S0[(bh * DK + row) * DV + col];
+                    S[m][nt][e] = S0[(sv.srow * DK + row) * DV + col];
                 }
     } else {
 #pragma unroll
@@ -1320,7 +1368,7 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
     // at the end of the step, after its loads, like the output rows
     auto emit = [&](int cc) {
         if constexpr (EMIT) {
-            float* Sb = S_bound + ((long)bh * nchunks + cc) * DK * DV;
+            float* Sb = S_bound + (sv.srow * sv.nchunks + cc) * DK * DV;
 #pragma unroll
             for (int m = 0; m < MTW; ++m)
 #pragma unroll
@@ -1338,13 +1386,13 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
     // unconditional (the chunk index is clamped to the last chunk):
     // straight-line code lets the compiler wait for exactly the set in use
     // instead of draining every load in flight.
-    const char* wsh = ws + bh * nchunks * Lw::BYTES;
-    const long bhk = hm.key(bh);   // q rows of the key head
+    const char* wsh = sv.wsh;
+    const int nchunks = sv.nchunks;
     const int last = nchunks - 1;
     auto blk = [&](int cc) {
         const int c2 = min(cc, last);
-        return ChunkSrc<E>{wsh + (long)c2 * Lw::BYTES, q + (bhk * T + (long)c2 * CHUNK) * DK,
-                           min(CHUNK, T - c2 * CHUNK)};
+        return ChunkSrc<E>{wsh + (long)c2 * Lw::BYTES, q + (sv.qrow + (long)c2 * CHUNK) * DK,
+                           min(CHUNK, sv.len - c2 * CHUNK)};
     };
     // SYNC: the tags of the next block to be waited for are loaded one chunk
     // step ahead, so a block that is already published costs no wait
@@ -1381,11 +1429,11 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), see below
         for (int c = 0; c < nchunks; c += 2) {
             ready(c + 1);
-            scan_step<E, DK, DV, KIND, BV, PF>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane, pfb(c + 3), pf0);
+            scan_step<E, DK, DV, KIND, BV, PF>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CHUNK, vt, w, lane, pfb(c + 3), pf0);
             emit(c);
             if (c + 1 >= nchunks) break;
             ready(c + 2);
-            scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane, pfb(c + 4), pf1);
+            scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 1) * CHUNK, vt, w, lane, pfb(c + 4), pf1);
             emit(c + 1);
         }
     } else {
@@ -1402,15 +1450,15 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         for (int c = 0; c < nchunks; c += 3) {
             ready(c + 2);
-            scan_step<E, DK, DV, KIND, BV, PF>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, c * CHUNK, vt, w, lane, pfb(c + 4), pf0);
+            scan_step<E, DK, DV, KIND, BV, PF>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CHUNK, vt, w, lane, pfb(c + 4), pf0);
             emit(c);
             if (c + 1 >= nchunks) break;
             ready(c + 3);
-            scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 1) * CHUNK, vt, w, lane, pfb(c + 5), pf1);
+            scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 1) * CHUNK, vt, w, lane, pfb(c + 5), pf1);
             emit(c + 1);
             if (c + 2 >= nchunks) break;
             ready(c + 4);
-            scan_step<E, DK, DV, KIND, BV, PF>(o2, o1, blk(c + 4), S, lds.Sx, lds.Ux, ob, qs, o, bh, T, (c + 2) * CHUNK, vt, w, lane, pfb(c + 6), pf2);
+            scan_step<E, DK, DV, KIND, BV, PF>(o2, o1, blk(c + 4), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 2) * CHUNK, vt, w, lane, pfb(c + 6), pf2);
             emit(c + 2);
         }
     }
@@ -1423,7 +1471,7 @@ __device__ __forceinline__ void scan_body(const char* __restrict__ ws, const E* 
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int row = 16 * (w * MTW + m) + 4 * gq + e, col = vt * BV + 16 * nt + n;
-                    S_final[(bh * DK + row) * DV + col] = S[m][nt][e];
+                    S_final[(sv.srow * DK + row) * DV + col] = S[m][nt][e];
                 }
     }
 }
@@ -1445,9 +1493,104 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
     const long bh = (long)(slot / NV) * 8 + xcd;
     if (bh >= BH) return;
     __shared__ ScanLds<E, DK, DV, KIND, BV> lds;
-    scan_body<E, DK, DV, KIND, BV, false, 3, EMIT>(ws, q, S0, o, S_final, T, nchunks, bh, vt,
-                                                (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63), lds,
-                                                nullptr, 0, nullptr, 0, hm, S_bound);
+    const SeqView sv{ws + bh * nchunks * WsLayout<E, DK, DV>::BYTES, hm.key(bh) * T, bh * T, bh, T,
+                     nchunks};
+    scan_body<E, DK, DV, KIND, BV, false, 3, EMIT>(sv, q, S0, o, S_final, vt, (int)(threadIdx.x >> 6),
+                                                (int)(threadIdx.x & 63), lds, nullptr, 0, nullptr, 0,
+                                                S_bound);
+}
+
+// The scan over packed sequences: one workgroup per (sequence n, head h, value
+// tile), state row n * H + h; the sequence's chunks are the global chunks
+// cs[n] .. cs[n+1] - 1 of head h. Sequence bounds are clamped to [0, T].
+template <typename E, int DK, int DV, int KIND, int BV>
+__global__ __launch_bounds__(256) void chunk_scan_varlen_kernel(const char* __restrict__ ws,
+                                                                const E* __restrict__ q,
+                                                                const float* __restrict__ S0,
+                                                                E* __restrict__ o,
+                                                                float* __restrict__ S_final, int T,
+                                                                int nchunks, int N, int H,
+                                                                const int* __restrict__ cu,
+                                                                const int* __restrict__ cs) {
+    constexpr int NV = DV / BV;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    const int vt = slot % NV;
+    const long bh = (long)(slot / NV) * 8 + xcd;
+    if (bh >= (long)N * H) return;
+    const int n = (int)(bh / H), h = (int)(bh % H);
+    const int start = min(max(cu[n], 0), T);
+    const int len = min(max(cu[n + 1], start), T) - start;
+    if (len == 0) {
+        // empty sequence: the state passes through
+        if (S_final)
+            for (int i = threadIdx.x; i < DK * BV; i += 256) {
+                const long at = (bh * DK + i / BV) * DV + vt * BV + i % BV;
+                S_final[at] = S0 ? S0[at] : 0.f;
+            }
+        return;
+    }
+    __shared__ ScanLds<E, DK, DV, KIND, BV> lds;
+    const long row = (long)h * T + start;
+    const SeqView sv{ws + ((long)h * nchunks + cs[n]) * WsLayout<E, DK, DV>::BYTES, row, row, bh,
+                     len, (len + CHUNK - 1) / CHUNK};
+    scan_body<E, DK, DV, KIND, BV, false, 3>(sv, q, S0, o, S_final, vt, (int)(threadIdx.x >> 6),
+                                          (int)(threadIdx.x & 63), lds, nullptr, 0, nullptr, 0);
+}
+
+// Chunk offsets of packed sequences (one workgroup): cs[n] = sum over m < n of
+// ceil(len_m / 64), n = 0..N, with len_m = cu[m+1] - cu[m] clamped to [0, T].
+__global__ __launch_bounds__(1024) void varlen_chunks_kernel(const int* __restrict__ cu, int N, int T,
+                                                             int* __restrict__ cs) {
+    __shared__ int part[1024];
+    const int t = threadIdx.x;
+    const int per = (N + 1023) / 1024;
+    const int m0 = min(t * per, N), m1 = min(m0 + per, N);
+    auto chunks = [&](int m) {
+        const int a = min(max(cu[m], 0), T);
+        const int b = min(max(cu[m + 1], a), T);
+        return (b - a + CHUNK - 1) / CHUNK;
+    };
+    int sum = 0;
+    for (int m = m0; m < m1; ++m) sum += chunks(m);
+    part[t] = sum;
+    __syncthreads();
+    // inclusive scan of the per-thread sums (Hillis-Steele over 1024 entries)
+    for (int off = 1; off < 1024; off <<= 1) {
+        const int x = t >= off ? part[t - off] : 0;
+        __syncthreads();
+        part[t] += x;
+        __syncthreads();
+    }
+    int run = part[t] - sum;   // exclusive prefix of this thread's range
+    for (int m = m0; m < m1; ++m) {
+        cs[m] = run;
+        run += chunks(m);
+    }
+    if (t == 1023) cs[N] = part[1023];
+}
+
+// Chunk table of packed sequences: entry gc (global chunk) = (first token of
+// the chunk in its head row, tokens in it); (0, 0) past the last chunk.
+__global__ __launch_bounds__(256) void varlen_table_kernel(const int* __restrict__ cu,
+                                                           const int* __restrict__ cs, int N, int T,
+                                                           int nchunks, int2* __restrict__ ctab) {
+    const int gc = blockIdx.x * 256 + threadIdx.x;
+    if (gc >= nchunks) return;
+    if (gc >= cs[N]) {
+        ctab[gc] = make_int2(0, 0);
+        return;
+    }
+    // the sequence n with cs[n] <= gc < cs[n + 1] (cs is nondecreasing)
+    int lo = 0, hi = N;   // invariant: cs[lo] <= gc < cs[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cs[mid] <= gc) lo = mid;
+        else hi = mid;
+    }
+    const int a = min(max(cu[lo], 0), T);
+    const int b = min(max(cu[lo + 1], a), T);
+    const int base = a + (gc - cs[lo]) * CHUNK;
+    ctab[gc] = make_int2(base, min(CHUNK, b - base));
 }
 
 // ---------------------------------------------------------------------------
@@ -1506,8 +1649,10 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
                 // registers across it
                 int ln;
                 asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+                const int t0 = c * CHUNK;
                 prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + (bh * nchunks + c) * Lw::BYTES,
-                                            lds.prep[unit], bh, hm.key(bh), c, T, wu, ln);
+                                            lds.prep[unit], bh * T + t0, hm.key(bh) * T + t0,
+                                            min(CHUNK, T - t0), wu, ln);
                 publish(tags + 2 * (bh * nchunks + c) + wu, tag, ln);
             } else {
                 lds_barrier();   // the item's one barrier, passed with the other unit
@@ -1519,8 +1664,9 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
     const int slot = s - NP, vt = slot % NV, i = slot / NV;
     if (i >= nh) return;
     const long bh = xcd + 8L * i;
-    scan_body<E, DK, DV, KIND, BV, true, 2>(ws, q, S0, o, S_final, T, nchunks, bh, vt, w, lane, lds.scan,
-                                         tags + 2 * bh * nchunks, tag, err, epoch, hm);
+    const SeqView sv{ws + bh * nchunks * Lw::BYTES, hm.key(bh) * T, bh * T, bh, T, nchunks};
+    scan_body<E, DK, DV, KIND, BV, true, 2>(sv, q, S0, o, S_final, vt, w, lane, lds.scan,
+                                         tags + 2 * bh * nchunks, tag, err, epoch);
 }
 
 // ---------------------------------------------------------------------------
@@ -1704,6 +1850,91 @@ hipError_t launch_chunk_fwd_states(int kind, int dtype, const void* q, const voi
                          : scan_kind<bf16, 64>(kind, q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
     return dk == 128 ? scan_kind<float, 128>(kind, q, S0, o, S_final, ws, BH, T, st, hm, S_bound)
                      : scan_kind<float, 64>(kind, q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
+}
+
+// Packed sequences: the chunk blocks [H][NC] with NC = ceil(T/64) + N (every
+// sequence boundary can split a chunk), then the chunk offsets cs[0..N] and
+// the chunk table ctab[NC] (first token, length).
+template <typename E, int D>
+static size_t varlen_ws_t(long long N, long long H, long long T) {
+    const long long nc = (T + CHUNK - 1) / CHUNK + N;
+    return (size_t)(H * nc * WsLayout<E, D, D>::BYTES + (4 * (N + 1) + 255) / 256 * 256 +
+                    (8 * nc + 255) / 256 * 256);
+}
+
+size_t chunk_varlen_workspace_bytes(long long N, long long H, long long T, int dk, int dv, int dtype) {
+    (void)dv;
+    if (dtype == DT_BF16) return dk == 128 ? varlen_ws_t<bf16, 128>(N, H, T) : varlen_ws_t<bf16, 64>(N, H, T);
+    return dk == 128 ? varlen_ws_t<float, 128>(N, H, T) : varlen_ws_t<float, 64>(N, H, T);
+}
+
+template <typename E, int D, int KIND, int BV>
+static hipError_t varlen_scan_t(const void* q, const float* S0, void* o, float* S_final,
+                                const void* ws, const int* cu, const int* cs, int N, int H, int T,
+                                int nc, hipStream_t st) {
+    const long rows = (long)N * H;
+    const long nblk = (rows + 7) / 8 * 8 * (D / BV);
+    hipLaunchKernelGGL((chunk_scan_varlen_kernel<E, D, D, KIND, BV>), dim3((unsigned)nblk), dim3(256), 0,
+                       st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nc, N, H, cu, cs);
+    return hipGetLastError();
+}
+
+template <typename E, int D, int KIND>
+static hipError_t varlen_kind_t(const void* q, const void* k, const void* v, const void* beta,
+                                const void* g, const float* S0, void* o, float* S_final,
+                                const int* cu, int N, int H, int T, void* ws, hipStream_t st) {
+    typedef WsLayout<E, D, D> Lw;
+    const int nc = (T + CHUNK - 1) / CHUNK + N;
+    char* tab = (char*)ws + (long)H * nc * Lw::BYTES;
+    int* cs = reinterpret_cast<int*>(tab);
+    int2* ctab = reinterpret_cast<int2*>(tab + (4L * (N + 1) + 255) / 256 * 256);
+    hipLaunchKernelGGL(varlen_chunks_kernel, dim3(1), dim3(1024), 0, st, cu, N, T, cs);
+    hipLaunchKernelGGL(varlen_table_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, st, cu,
+                       (const int*)cs, N, T, nc, ctab);
+    const long nitems = (long)H * nc;
+    if constexpr (KIND != KIND_KDA && (sizeof(E) == 2 || D == 64)) {
+        hipLaunchKernelGGL((chunk_prep2_varlen_kernel<E, D, D, KIND>), dim3((unsigned)nitems), dim3(128),
+                           0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
+                           (char*)ws, T, nc, (const int2*)ctab);
+    } else {
+        constexpr long lds = PrepSmem<E, D, D, KIND>::TOTAL + 1024;
+        constexpr int per_cu = (int)(163840 / lds) < 1 ? 1 : (int)(163840 / lds);
+        const long resident = (long)per_cu * device_cu_count();
+        const int grid = (int)(nitems < resident ? nitems : resident);
+        hipLaunchKernelGGL((chunk_prep_kernel<E, D, D, KIND, true>), dim3((unsigned)grid), dim3(256), 0,
+                           st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
+                           (char*)ws, T, nc, (int)nitems, HeadMap(), (const int2*)ctab);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    constexpr int SK = KIND == KIND_KDA ? KIND_KDA : KIND_GATED;   // DeltaNet shares the scan
+    if (scan_bv<D>(N * H) == 32)
+        return varlen_scan_t<E, D, SK, 32>(q, S0, o, S_final, ws, cu, cs, N, H, T, nc, st);
+    return varlen_scan_t<E, D, SK, 16>(q, S0, o, S_final, ws, cu, cs, N, H, T, nc, st);
+}
+
+template <typename E, int D>
+static hipError_t varlen_t(int kind, const void* q, const void* k, const void* v, const void* beta,
+                           const void* g, const float* S0, void* o, float* S_final, const int* cu,
+                           int N, int H, int T, void* ws, hipStream_t st) {
+    if (kind == KIND_DELTANET)
+        return varlen_kind_t<E, D, KIND_DELTANET>(q, k, v, beta, g, S0, o, S_final, cu, N, H, T, ws, st);
+    if (kind == KIND_GATED)
+        return varlen_kind_t<E, D, KIND_GATED>(q, k, v, beta, g, S0, o, S_final, cu, N, H, T, ws, st);
+    if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
+    else return varlen_kind_t<E, D, KIND_KDA>(q, k, v, beta, g, S0, o, S_final, cu, N, H, T, ws, st);
+}
+
+hipError_t launch_chunk_fwd_varlen(int kind, int dtype, const void* q, const void* k,
+                                   const void* v, const void* beta, const void* g,
+                                   const float* S0, void* o, float* S_final, const int* cu_seqlens,
+                                   int N, int H, int T, int dk, int dv, void* ws, hipStream_t st) {
+    (void)dv;
+    if (dtype == DT_BF16)
+        return dk == 128 ? varlen_t<bf16, 128>(kind, q, k, v, beta, g, S0, o, S_final, cu_seqlens, N, H, T, ws, st)
+                         : varlen_t<bf16, 64>(kind, q, k, v, beta, g, S0, o, S_final, cu_seqlens, N, H, T, ws, st);
+    return dk == 128 ? varlen_t<float, 128>(kind, q, k, v, beta, g, S0, o, S_final, cu_seqlens, N, H, T, ws, st)
+                     : varlen_t<float, 64>(kind, q, k, v, beta, g, S0, o, S_final, cu_seqlens, N, H, T, ws, st);
 }
 
 // One-launch prefill where it exists: bf16, DeltaNet or Gated DeltaNet, and

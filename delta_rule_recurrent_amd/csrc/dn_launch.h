@@ -64,6 +64,18 @@ hipError_t launch_chunk_fwd_states(int kind, int dtype, const void* q, const voi
                                    void* ws, int BH, int T, int dk, int dv, hipStream_t stream,
                                    HeadMap hm = HeadMap());
 
+// Chunkwise prefill over N packed sequences of different lengths: q, k, v, o
+// [H][T] rows holding the sequences back to back (sequence n at tokens
+// cu_seqlens[n] .. cu_seqlens[n+1], a device array of N + 1 ints), states
+// [N][H]. Always the two phases; the workspace also holds the chunk table.
+hipError_t launch_chunk_fwd_varlen(int kind, int dtype, const void* q, const void* k,
+                                   const void* v, const void* beta, const void* g,
+                                   const float* S0, void* o, float* S_final, const int* cu_seqlens,
+                                   int N, int H, int T, int dk, int dv, void* workspace,
+                                   hipStream_t stream);
+size_t chunk_varlen_workspace_bytes(long long N, long long H, long long T, int dk, int dv,
+                                    int dtype);
+
 // Workspace bytes of the chunkwise prefill (per call).
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype);
 

@@ -233,6 +233,34 @@ int dn_decode_step_gqa(int kda, const void* q, const void* k, const void* v,
                        const void* beta, const void* g, float* S, void* o, int B,
                        int Hk, int Hv, int dk, int dv, int dtype, void* stream);
 
+/*
+ * Chunkwise prefill over N packed sequences of different lengths, as a serving
+ * engine batches requests: one call, every sequence its own recurrence (the
+ * pages' model of a request: a state per sequence, page "28. Linear attention
+ * and Gated DeltaNet", section "The state a request carries").
+ *   kda         0: DeltaNet (g NULL) / Gated DeltaNet; nonzero: KDA (g required)
+ *   q, k        [1,H,T,dk], v and o [1,H,T,dv], beta [1,H,T], g [1,H,T] or
+ *               [1,H,T,dk]: the sequences back to back along T in every head
+ *   cu_seqlens  DEVICE array of N + 1 ints: sequence n holds tokens
+ *               cu_seqlens[n] .. cu_seqlens[n+1] - 1; expected cu_seqlens[0] = 0,
+ *               nondecreasing, cu_seqlens[N] = T (each bound is clamped to
+ *               [0, T] and to its predecessor, so no value reads out of bounds;
+ *               an empty sequence passes its state through)
+ *   S0, S_final [N,H,dk,dv] fp32 (S0 NULL => zeros; S_final NULL => not written)
+ *   workspace   at least dn_chunk_fwd_varlen_workspace(N,H,T,dk,dv,dtype) bytes,
+ *               256-byte aligned
+ * Each sequence's o and S_final are bitwise what dn_chunk_fwd / dn_kda_chunk_fwd
+ * (two-phase form) give for that sequence alone. N < 1, a NULL or misaligned
+ * cu_seqlens, and more than 2^24 (sequence, head) rows give DN_EINVAL; the
+ * other rules are those of dn_chunk_fwd.
+ */
+size_t dn_chunk_fwd_varlen_workspace(int N, int H, int T, int dk, int dv, int dtype);
+int dn_chunk_fwd_varlen(int kda, const void* q, const void* k, const void* v,
+                        const void* beta, const void* g, const float* S0, void* o,
+                        float* S_final, const int* cu_seqlens, int N, int H, int T, int dk,
+                        int dv, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -156,6 +156,38 @@ def test_shared_key_heads_validation():
     assert _gqa(ws_bytes=16) == W
     assert _gqa(kda=1, dtype=0, dk=128, dv=128) == N
     assert _gqa_dec(S=None) == E
+
+
+def _varlen(**kw):
+    args = dict(kda=0, q=P, k=P, v=P, beta=P, g=P, S0=P, o=P, S_final=P, cu=P, N=3, H=2, T=300,
+                dk=64, dv=64, dtype=1, ws=WS, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return _lib.lib().dn_chunk_fwd_varlen(*[args[n] for n in (
+        "kda", "q", "k", "v", "beta", "g", "S0", "o", "S_final", "cu", "N", "H", "T", "dk", "dv",
+        "dtype", "ws", "ws_bytes", "stream")])
+
+
+def test_varlen_workspace_and_validation():
+    lib = _lib.lib()
+    ws = lib.dn_chunk_fwd_varlen_workspace
+    block = lib.dn_chunk_fwd_workspace(1, 1, 128, 128, 128, 1) - lib.dn_chunk_fwd_workspace(1, 1, 64, 128, 128, 1)
+    # blocks for H x (ceil(T/64) + N) chunks, then N+1 chunk offsets and a
+    # table of 8 bytes per chunk, each padded to 256 bytes
+    assert ws(2, 1, 64, 128, 128, 1) == 3 * block + 256 + 256
+    assert ws(5, 4, 1000, 128, 128, 1) == 4 * 21 * block + 256 + 256
+    assert ws(0, 1, 64, 128, 128, 1) == 0 and ws(1, 1, 0, 128, 128, 1) == 0
+    E, N, W = _lib.DN_EINVAL, _lib.DN_ENOTSUP, _lib.DN_EWORKSPACE
+    assert _varlen(N=0) == E
+    assert _varlen(cu=None) == E
+    assert _varlen(cu=P + 2) == E              # int array: 4-byte alignment
+    assert _varlen(q=None) == E
+    assert _varlen(kda=1, g=None) == E
+    assert _varlen(kda=1, dtype=0, dk=128, dv=128) == N
+    assert _varlen(dk=96, dv=96) == N
+    assert _varlen(ws=None) == W
+    assert _varlen(ws_bytes=16) == W
+    assert _varlen(N=1 << 23, H=4) == E         # more than 2^24 (sequence, head) rows
+    assert _varlen(T=0, S_final=None) == _lib.DN_OK
 
 
 def _rec(fn, **kw):
