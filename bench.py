@@ -170,6 +170,7 @@ def main():
     # ---------------------------------------------------------- other workloads
     if not args.no_workloads:
         result["workloads"] = run_workloads(torch, dn, synthetic, to_dev, dev)
+        result["serving_forms"] = run_serving(torch, dn, synthetic, to_dev, dev)
 
     print(json.dumps(result), flush=True)
 
@@ -385,6 +386,82 @@ def run_workloads(torch, dn, synthetic, to_dev, dev):
         log("  %s %s %.4f ms" % (wname, form, ms))
         del x, wsw, ow, Sw
     return wl
+
+
+def run_serving(torch, dn, synthetic, to_dev, dev):
+    """The serving forms of the prefill at the headline's size (32 value heads'
+    worth of 2048 tokens at d = 128, bf16 Gated DeltaNet), each against the
+    plain call it generalises:
+      * chunk_fwd_states: every chunk-boundary state written (32 x 32 x 64 KiB);
+      * chunk_fwd_gqa: 4 key heads shared by 8 value heads per sequence;
+      * chunk_fwd_varlen: 8 heads over 8 sequences of 8192 tokens in all, with
+        lengths 63 .. 3008 (the same 65536 token-heads as the headline);
+    and decode_tokens (4 drafted tokens per sequence with a state snapshot after
+    each) at the decode workload's 256 x 16 states."""
+    out = {}
+    c = synthetic.CONFIGS["gdn_prefill_b4_h8_t2048_d128"]
+    B, H, T, d = c["B"], c["H"], c["T"], c["dk"]
+    x = to_dev(synthetic.make_config("gdn_prefill_b4_h8_t2048_d128"))
+    tok = B * H * T
+
+    def timed(name, run, extra=None):
+        for _ in range(3):
+            run()
+        ms = event_time_ms(torch, run, 20)
+        e = {"ms": round(ms, 4), "tokens_per_s": round(tok / (ms * 1e-3), 1)}
+        e.update(extra or {})
+        out[name] = e
+        log("  serving %s %.4f ms" % (name, ms))
+
+    ws = torch.empty(dn.workspace_bytes(B, H, T, d, d, torch.bfloat16), dtype=torch.uint8, device=dev)
+    o = torch.empty(B, H, T, d, dtype=torch.bfloat16, device=dev)
+    S = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)
+    timed("chunk_fwd", lambda: dn.chunk_fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], None,
+                                            o=o, S_final=S, workspace=ws))
+    Sc = torch.empty(B, H, (T + 63) // 64, d, d, dtype=torch.float32, device=dev)
+    timed("chunk_fwd_states", lambda: dn.chunk_fwd_states(x["q"], x["k"], x["v"], x["beta"], x["g"],
+                                                          None, o=o, S_final=S, S_chunks=Sc,
+                                                          workspace=ws),
+          {"boundary_state_bytes": Sc.numel() * 4})
+    qk = synthetic.make("gated", B, H // 2, T, d, d, dtype="bf16", seed=2001)
+    qg, kg = qk["q"].to(dev), qk["k"].to(dev)
+    timed("chunk_fwd_gqa", lambda: dn.chunk_fwd_gqa(qg, kg, x["v"], x["beta"], x["g"], None,
+                                                    o=o, S_final=S, workspace=ws),
+          {"key_heads": H // 2, "value_heads": H})
+    lens = [3008, 64, 1536, 520, 1024, 77, 1900, 63]
+    Tp = sum(lens)
+    cu = torch.tensor([0] + [sum(lens[:i + 1]) for i in range(len(lens))], dtype=torch.int32,
+                      device=dev)
+    xp = to_dev(synthetic.make("gated", 1, H, Tp, d, d, dtype="bf16", seed=2002))
+    wsp = torch.empty(int(dn.lib().dn_chunk_fwd_varlen_workspace(len(lens), H, Tp, d, d, 1)),
+                      dtype=torch.uint8, device=dev)
+    op = torch.empty(1, H, Tp, d, dtype=torch.bfloat16, device=dev)
+    Sp = torch.empty(len(lens), H, d, d, dtype=torch.float32, device=dev)
+    timed("chunk_fwd_varlen", lambda: dn.chunk_fwd_varlen(xp["q"], xp["k"], xp["v"], xp["beta"],
+                                                          xp["g"], cu, None, o=op, S_final=Sp,
+                                                          workspace=wsp),
+          {"sequence_lengths": lens, "heads": H})
+    del x, ws, o, S, Sc, qg, kg, xp, wsp, op, Sp
+    # speculative decode: 4 drafted tokens for the decode workload's 256 x 16
+    # states, the state after each kept (4 x 256 MiB of snapshots)
+    Bd, Hd, K = 256, 16, 4
+    xd = to_dev(synthetic.make("gated", Bd, Hd, K, d, d, dtype="bf16", seed=2003, s0_std=0.02))
+    Sd = xd["S0"].clone()
+    od = torch.empty(Bd, Hd, K, d, dtype=torch.bfloat16, device=dev)
+    snap = torch.empty(Bd, Hd, K, d, d, dtype=torch.float32, device=dev)
+    run = lambda: dn.decode_tokens(xd["q"], xd["k"], xd["v"], xd["beta"], xd["g"], Sd, o=od,
+                                   S_snap=snap)
+    for _ in range(2):
+        run()
+    ms = event_time_ms(torch, run, 5)
+    state = Bd * Hd * d * d * 4
+    moved = state * (2 + K)
+    out["decode_tokens"] = {"ms": round(ms, 4), "B": Bd, "H": Hd, "tokens_per_call": K,
+                            "state_bytes_moved": moved,
+                            "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
+    log("  serving decode_tokens %.4f ms" % ms)
+    del xd, Sd, od, snap
+    return out
 
 
 if __name__ == "__main__":

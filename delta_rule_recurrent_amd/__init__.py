@@ -20,7 +20,8 @@ from . import _lib
 from ._lib import DeltaNetError, lib
 
 __all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_fwd_gqa",
-           "decode_step_gqa", "chunk_fwd_varlen", "chunk_prep", "chunk_scan", "recurrent_fwd",
+           "decode_step_gqa", "chunk_fwd_varlen", "decode_tokens", "chunk_prep", "chunk_scan",
+           "recurrent_fwd",
            "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
            "DeltaNetError", "lib", "library_path"]
 
@@ -281,6 +282,30 @@ def chunk_fwd_varlen(q, k, v, beta, g, cu_seqlens, S0=None, *, kda=False, output
                                    workspace.numel() * workspace.element_size(), _stream(stream))
     _lib.check("dn_chunk_fwd_varlen", st)
     return o, S_final
+
+
+def decode_tokens(q, k, v, beta, g, S, *, kda=False, snapshots=True, o=None, S_snap=None,
+                  stream=None):
+    """K decode tokens per sequence in one call (speculative decoding).
+
+    q, k [B,H,K,dk]; v [B,H,K,dv]; beta [B,H,K]; g [B,H,K] / [B,H,K,dk] (KDA) /
+    None; S [B,H,dk,dv] fp32 updated in place. Returns (o [B,H,K,dv], S_snap
+    [B,H,K,dk,dv] with the state after each token, or None if not requested).
+    """
+    B, H, K, dk, dv, dev, dt = _prefill_args(q, k, v, beta, g, None, kda)
+    _check_tensor("S", S, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, H, K, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, K, dv), dt, dev)
+    if S_snap is None and snapshots:
+        S_snap = torch.empty(B, H, K, dk, dv, dtype=torch.float32, device=dev)
+    elif S_snap is not None:
+        _check_tensor("S_snap", S_snap, (B, H, K, dk, dv), torch.float32, dev)
+    st = lib().dn_decode_tokens(int(kda), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S),
+                                _ptr(o), _ptr(S_snap), B, H, K, dk, dv, _DT[dt], _stream(stream))
+    _lib.check("dn_decode_tokens", st)
+    return o, S_snap
 
 
 def chunk_prep(q, k, v, beta, g, workspace, *, kda=False, stream=None):

@@ -32,6 +32,7 @@ SIGNATURES = {
     "dn_decode_step_gqa": (_i, [_i] + [_vp] * 7 + [_i] * 6 + [_vp]),
     "dn_chunk_fwd_varlen_workspace": (_sz, [_i] * 6),
     "dn_chunk_fwd_varlen": (_i, [_i] + [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
+    "dn_decode_tokens": (_i, [_i] + [_vp] * 8 + [_i] * 6 + [_vp]),
     "dn_chunk_prep": (_i, [_i] + [_vp] * 5 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_chunk_scan": (_i, [_i] + [_vp] * 4 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_recurrent_fwd": (_i, _PREFILL + [_vp]),

@@ -242,6 +242,19 @@ int dn_chunk_fwd_varlen(int kda, const void* q, const void* k, const void* v, co
     return hip_status(e);
 }
 
+int dn_decode_tokens(int kda, const void* q, const void* k, const void* v, const void* beta,
+                     const void* g, float* S, void* o, float* S_snap, int B, int H, int K, int dk,
+                     int dv, int dtype, void* stream) {
+    if (!S || K < 1) return DN_EINVAL;
+    const int kind = chunk_kind(kda != 0, g);
+    int st = check_common(q, k, v, beta, g, kda != 0, S, o, S, B, H, K, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    if (misaligned(S_snap)) return DN_EINVAL;
+    const long long BH = (long long)B * H;
+    return hip_status(dn::launch_recurrent(kind, dtype, q, k, v, beta, g, S, o, S, (int)BH, K, dk,
+                                           dv, as_stream(stream), S_snap));
+}
+
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,
                   const void* g, int B, int H, int T, int dk, int dv, int dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {

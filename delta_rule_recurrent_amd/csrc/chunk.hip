@@ -1334,7 +1334,7 @@ __device__ __forceinline__ u64* block_tags(char* ws, long BH, int nchunks) {
 // operands are loaded. RING: 3 (two chunks prefetched) or 2 (one chunk; fewer
 // registers held, which leaves the fused launch's register budget room).
 template <typename E, int DK, int DV, int KIND, int BV, bool SYNC, int RING, bool EMIT = false>
-__device__ __forceinline__ void scan_body(const SeqView& sv, const E* __restrict__ q,
+__device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict__ q,
                                           const float* __restrict__ S0, E* __restrict__ o,
                                           float* __restrict__ S_final, int vt, int w, int lane,
                                           ScanLds<E, DK, DV, KIND, BV>& lds, const u64* tags,

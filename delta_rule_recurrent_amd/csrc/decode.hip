@@ -142,7 +142,7 @@ __device__ __forceinline__ void token_load(TokenIn<E, DK, KIND>& x, const E* __r
     }
 }
 
-template <typename E, int DK, int DV, int KIND>
+template <typename E, int DK, int DV, int KIND, bool SNAP = false>
 __global__ __launch_bounds__(64) void recurrent_kernel(const E* __restrict__ q,
                                                        const E* __restrict__ k,
                                                        const E* __restrict__ v,
@@ -150,7 +150,8 @@ __global__ __launch_bounds__(64) void recurrent_kernel(const E* __restrict__ q,
                                                        const E* __restrict__ g,
                                                        const float* __restrict__ S0,
                                                        E* __restrict__ o,
-                                                       float* __restrict__ S_final, int T) {
+                                                       float* __restrict__ S_final, int T,
+                                                       float* __restrict__ S_snap) {
     constexpr int NS = DV / WAVE;
     constexpr int KPL = DK / WAVE;
     constexpr int RING = 4;
@@ -194,6 +195,11 @@ __global__ __launch_bounds__(64) void recurrent_kernel(const E* __restrict__ q,
 #pragma unroll
                 for (int r = 0; r < DK; ++r) out += readlane_f(x.q[r / WAVE], r % WAVE) * s[r];
                 o[(bh * T + t) * DV + col] = from_f32<E>(out);
+                if constexpr (SNAP) {
+                    // the state after token t, [bh][t][DK][DV]
+#pragma unroll
+                    for (int r = 0; r < DK; ++r) S_snap[((bh * T + t) * DK + r) * DV + col] = s[r];
+                }
             }
             token_load<E, DK, DV, KIND>(ring[u], q, k, v, beta, g, bh, t + RING, T, col, lane);
         }
@@ -245,32 +251,40 @@ hipError_t launch_decode(int kind, int dtype, const void* q, const void* k, cons
                      : decode_t<float, 64>(kind, q, k, v, beta, g, S, o, BH, st, hm);
 }
 
+template <typename E, int D, bool SNAP>
+static hipError_t recurrent_launch(int kind, const E* q_, const E* k_, const E* v_, const E* b_,
+                                   const E* g_, const float* S0, E* o_, float* S_final, int BH,
+                                   int T, float* S_snap, hipStream_t st) {
+    dim3 grid((unsigned)BH * (D / WAVE)), block(WAVE);
+    if (kind == KIND_DELTANET)
+        hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_DELTANET, SNAP>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T, S_snap);
+    else if (kind == KIND_GATED)
+        hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_GATED, SNAP>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T, S_snap);
+    else
+        hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_KDA, SNAP>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T, S_snap);
+    return hipGetLastError();
+}
+
 template <typename E, int D>
 static hipError_t recurrent_t(int kind, const void* q, const void* k, const void* v,
                               const void* beta, const void* g, const float* S0, void* o,
-                              float* S_final, int BH, int T, hipStream_t st) {
+                              float* S_final, int BH, int T, hipStream_t st, float* S_snap) {
     const E *q_ = (const E*)q, *k_ = (const E*)k, *v_ = (const E*)v, *b_ = (const E*)beta,
             *g_ = (const E*)g;
-    E* o_ = (E*)o;
-    dim3 grid((unsigned)BH * (D / WAVE)), block(WAVE);
-    if (kind == KIND_DELTANET)
-        hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_DELTANET>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T);
-    else if (kind == KIND_GATED)
-        hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_GATED>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T);
-    else
-        hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_KDA>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T);
-    return hipGetLastError();
+    if (S_snap) return recurrent_launch<E, D, true>(kind, q_, k_, v_, b_, g_, S0, (E*)o, S_final, BH, T, S_snap, st);
+    return recurrent_launch<E, D, false>(kind, q_, k_, v_, b_, g_, S0, (E*)o, S_final, BH, T, nullptr, st);
 }
 
 hipError_t launch_recurrent(int kind, int dtype, const void* q, const void* k, const void* v,
                             const void* beta, const void* g, const float* S0, void* o,
-                            float* S_final, int BH, int T, int dk, int dv, hipStream_t st) {
+                            float* S_final, int BH, int T, int dk, int dv, hipStream_t st,
+                            float* S_snap) {
     (void)dv;
     if (dtype == DT_BF16)
-        return dk == 128 ? recurrent_t<bf16, 128>(kind, q, k, v, beta, g, S0, o, S_final, BH, T, st)
-                         : recurrent_t<bf16, 64>(kind, q, k, v, beta, g, S0, o, S_final, BH, T, st);
-    return dk == 128 ? recurrent_t<float, 128>(kind, q, k, v, beta, g, S0, o, S_final, BH, T, st)
-                     : recurrent_t<float, 64>(kind, q, k, v, beta, g, S0, o, S_final, BH, T, st);
+        return dk == 128 ? recurrent_t<bf16, 128>(kind, q, k, v, beta, g, S0, o, S_final, BH, T, st, S_snap)
+                         : recurrent_t<bf16, 64>(kind, q, k, v, beta, g, S0, o, S_final, BH, T, st, S_snap);
+    return dk == 128 ? recurrent_t<float, 128>(kind, q, k, v, beta, g, S0, o, S_final, BH, T, st, S_snap)
+                     : recurrent_t<float, 64>(kind, q, k, v, beta, g, S0, o, S_final, BH, T, st, S_snap);
 }
 
 hipError_t launch_state_copy(const float* S0, float* S_final, long long n, hipStream_t st) {

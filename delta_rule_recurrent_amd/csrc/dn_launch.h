@@ -31,10 +31,12 @@ hipError_t launch_decode(int kind, int dtype, const void* q, const void* k, cons
                          const void* beta, const void* g, float* S, void* o, int BH, int dk,
                          int dv, hipStream_t stream, HeadMap hm = HeadMap());
 
-// Token-by-token recurrence over T tokens.
+// Token-by-token recurrence over T tokens; S_snap (or NULL): the state after
+// every token, [BH][T][dk][dv] fp32.
 hipError_t launch_recurrent(int kind, int dtype, const void* q, const void* k, const void* v,
                             const void* beta, const void* g, const float* S0, void* o,
-                            float* S_final, int BH, int T, int dk, int dv, hipStream_t stream);
+                            float* S_final, int BH, int T, int dk, int dv, hipStream_t stream,
+                            float* S_snap = nullptr);
 
 // Chunkwise prefill, phase 1: every chunk in parallel, intermediates -> workspace.
 hipError_t launch_chunk_prep(int kind, int dtype, const void* q, const void* k, const void* v,

@@ -261,6 +261,25 @@ int dn_chunk_fwd_varlen(int kda, const void* q, const void* k, const void* v,
                         int dv, int dtype, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/*
+ * Multi-token decode for speculative decoding: K new tokens of every sequence
+ * in one call, with the state after each of them kept, so that an engine that
+ * accepts only the first j drafted tokens restores snapshot j - 1 instead of
+ * recomputing (a recurrent state cannot forget tokens once mixed in: page
+ * "28. Linear attention and Gated DeltaNet", section "The state a request
+ * carries"). The tokens run through the token-by-token recurrence.
+ *   kda      0: DeltaNet (g NULL) or Gated DeltaNet; nonzero: KDA (g required)
+ *   q, k     [B,H,K,dk]; v, o [B,H,K,dv]; beta [B,H,K]; g [B,H,K] or [B,H,K,dk]
+ *   S        [B,H,dk,dv] fp32, updated in place to the state after all K tokens
+ *   S_snap   [B,H,K,dk,dv] fp32 (16-byte aligned) or NULL: entry j is the state
+ *            after token j (the last equals the updated S)
+ * K >= 1. o and S are bitwise those of dn_recurrent_fwd / dn_kda_recurrent_fwd
+ * over the K tokens from S; errors as for dn_decode_step.
+ */
+int dn_decode_tokens(int kda, const void* q, const void* k, const void* v,
+                     const void* beta, const void* g, float* S, void* o, float* S_snap,
+                     int B, int H, int K, int dk, int dv, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

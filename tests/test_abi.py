@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -188,6 +188,26 @@ def test_varlen_workspace_and_validation():
     assert _varlen(ws_bytes=16) == W
     assert _varlen(N=1 << 23, H=4) == E         # more than 2^24 (sequence, head) rows
     assert _varlen(T=0, S_final=None) == _lib.DN_OK
+
+
+def _tokens(**kw):
+    args = dict(kda=0, q=P, k=P, v=P, beta=P, g=P, S=P, o=P, S_snap=P, B=1, H=1, K=4, dk=128,
+                dv=128, dtype=1, stream=None)
+    args.update(kw)
+    return _lib.lib().dn_decode_tokens(*[args[n] for n in (
+        "kda", "q", "k", "v", "beta", "g", "S", "o", "S_snap", "B", "H", "K", "dk", "dv", "dtype",
+        "stream")])
+
+
+def test_decode_tokens_validation():
+    E, N = _lib.DN_EINVAL, _lib.DN_ENOTSUP
+    assert _tokens(S=None) == E
+    assert _tokens(K=0) == E
+    assert _tokens(S_snap=MIS) == E
+    assert _tokens(q=None) == E
+    assert _tokens(kda=1, g=None) == E
+    assert _tokens(dk=96, dv=96) == N
+    assert _tokens(B=0) == E
 
 
 def _rec(fn, **kw):

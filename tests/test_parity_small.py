@@ -400,3 +400,33 @@ def test_varlen_prefill(kind, dtype, d):
         worst = max(worst, eo, es)
         assert eo <= TOL[dtype] and es <= TOL[dtype], (n, eo, es)
     say("  worst err %.3e" % worst)
+
+
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_decode_tokens_snapshots(kind, dtype, d):
+    """K tokens per sequence in one call: the snapshot after token j against the
+    oracle run over the first j + 1 tokens; o and the updated state bitwise
+    equal to the token-by-token prefill from the same start state."""
+    dn = _dn()
+    B, H, K = 3, 4, 5
+    say("decode tokens", kind, dtype, d, K)
+    inp = make(kind, B, H, K, d, dtype, seed=81, s0_std=0.5)
+    di = to_dev(inp)
+    S = di["S0"].clone()
+    o, snap = dn.decode_tokens(di["q"], di["k"], di["v"], di["beta"], di["g"], S,
+                               kda=(kind == "kda"))
+    fn = dn.kda_recurrent_fwd if kind == "kda" else dn.recurrent_fwd
+    o2, S2 = fn(di["q"], di["k"], di["v"], di["beta"], di["g"], di["S0"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(S, S2)
+    assert torch.equal(snap[:, :, -1], S)
+    for j in range(K):
+        seg = {key: (inp[key][:, :, :j + 1] if inp[key] is not None else None)
+               for key in ("q", "k", "v", "beta", "g")}
+        seg["kind"] = inp["kind"]
+        _, S_ref = oracle_prefill(seg, S0=inp["S0"])
+        e = rel_err(snap[:, :, j], S_ref)
+        assert e <= TOL[dtype], (j, e)
+    o_ref, _ = oracle_prefill(inp)
+    assert rel_err(o, o_ref) <= TOL[dtype]
