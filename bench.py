@@ -171,6 +171,7 @@ def main():
     if not args.no_workloads:
         result["workloads"] = run_workloads(torch, dn, synthetic, to_dev, dev)
         result["serving_forms"] = run_serving(torch, dn, synthetic, to_dev, dev)
+        result["layer"] = run_layer(torch, dn, synthetic, to_dev, dev)
 
     print(json.dumps(result), flush=True)
 
@@ -461,6 +462,75 @@ def run_serving(torch, dn, synthetic, to_dev, dev):
                             "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
     log("  serving decode_tokens %.4f ms" % ms)
     del xd, Sd, od, snap
+    return out
+
+
+def run_layer(torch, dn, synthetic, to_dev, dev):
+    """The gated layer's kernels around the rule, at the headline's size (B=4,
+    T=2048, 8 key and 8 value heads of d = 128, bf16) and at the decode
+    workload's 256 sequences x 16 heads for one token:
+      * prologue: convolution + SiLU with carried state, head split, L2 norm,
+        gates, and the new convolution state;
+      * epilogue: gated RMSNorm into token-major rows;
+      * layer: prologue -> rule (chunked prefill / decode step) -> epilogue,
+        i.e. the whole layer between its input and output projections.
+    Bytes are the algorithmic HBM bytes of each kernel (every input read once,
+    every output written once)."""
+    out = {}
+
+    def timed(name, run, nbytes, tokens, reps=20):
+        for _ in range(3):
+            run()
+        ms = event_time_ms(torch, run, reps)
+        e = {"ms": round(ms, 4), "tokens_per_s": round(tokens / (ms * 1e-3), 1)}
+        if nbytes:
+            e["bytes"] = nbytes
+            e["gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+            e["frac_of_8000_gbs"] = round(nbytes / (ms * 1e-3) / 8e12, 3)
+        out[name] = e
+        log("  layer %s %.4f ms" % (name, ms))
+
+    for tag, (B, T, Hk, Hv) in (("prefill_b4_t2048_h8", (4, 2048, 8, 8)),
+                                ("decode_b256_h16", (256, 1, 16, 16))):
+        d = 128
+        x = to_dev(synthetic.make_layer(B, T, Hk, Hv, d, "bf16", seed=3001))
+        C = (2 * Hk + Hv) * d
+        tok = B * T * Hv
+        q = torch.empty(B, Hk, T, d, dtype=torch.bfloat16, device=dev)
+        k = torch.empty_like(q)
+        v = torch.empty(B, Hv, T, d, dtype=torch.bfloat16, device=dev)
+        beta = torch.empty(B, Hv, T, dtype=torch.bfloat16, device=dev)
+        g = torch.empty_like(beta)
+        cst = x["conv_state"].clone()
+        act = B * T * C * 2 + 2 * B * T * Hv * 2   # qkv + (b, a), and as many written
+        pro_bytes = 2 * act + 2 * B * C * 3 * 2 + C * 4 * 2
+        prologue = lambda: dn.layer_prologue(x["qkv"], x["conv_w"], x["b"], x["a"], x["A_log"],
+                                             x["dt_bias"], Hk, Hv, conv_state=x["conv_state"],
+                                             conv_state_out=cst, out=(q, k, v, beta, g))
+        timed(tag + "_prologue", prologue, pro_bytes, tok)
+        o = torch.empty(B, Hv, T, d, dtype=torch.bfloat16, device=dev)
+        y = torch.empty(B, T, Hv * d, dtype=torch.bfloat16, device=dev)
+        epilogue = lambda: dn.layer_epilogue(o, x["z"], x["norm_w"], 1e-6, out=y)
+        o.normal_()
+        timed(tag + "_epilogue", epilogue, 3 * B * T * Hv * d * 2 + d * 2, tok)
+        S = torch.zeros(B, Hv, d, d, dtype=torch.float32, device=dev)
+        if T == 1:
+            def layer():
+                prologue()
+                dn.decode_step_gqa(q[:, :, 0], k[:, :, 0], v[:, :, 0], beta[:, :, 0], g[:, :, 0],
+                                   S, o=o[:, :, 0])
+                epilogue()
+        else:
+            ws = torch.empty(dn.workspace_bytes(B, Hv, T, d, d, torch.bfloat16), dtype=torch.uint8,
+                             device=dev)
+
+            def layer():
+                prologue()
+                dn.chunk_fwd_gqa(q, k, v, beta, g, None, o=o, S_final=S, workspace=ws)
+                epilogue()
+        timed(tag + "_layer", layer, 0, tok)
+        out[tag + "_layer"]["shape"] = {"B": B, "T": T, "key_heads": Hk, "value_heads": Hv, "d": d}
+        del x, q, k, v, beta, g, cst, o, y, S
     return out
 
 

@@ -20,7 +20,8 @@ from . import _lib
 from ._lib import DeltaNetError, lib
 
 __all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_fwd_gqa",
-           "decode_step_gqa", "chunk_fwd_varlen", "decode_tokens", "chunk_prep", "chunk_scan",
+           "decode_step_gqa", "chunk_fwd_varlen", "decode_tokens", "layer_prologue",
+           "layer_epilogue", "gated_deltanet_layer", "chunk_prep", "chunk_scan",
            "recurrent_fwd",
            "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
            "DeltaNetError", "lib", "library_path"]
@@ -306,6 +307,115 @@ def decode_tokens(q, k, v, beta, g, S, *, kda=False, snapshots=True, o=None, S_s
                                 _ptr(o), _ptr(S_snap), B, H, K, dk, dv, _DT[dt], _stream(stream))
     _lib.check("dn_decode_tokens", st)
     return o, S_snap
+
+
+def layer_prologue(qkv, conv_w, b, a, A_log, dt_bias, Hk, Hv, *, conv_state=None,
+                   conv_state_out=None, update_conv_state=True, out=None, stream=None):
+    """The gated layer's work before the rule, from the projected rows.
+
+    qkv [B,T,2*Hk*d + Hv*d] (q, k, v channels per token); conv_w [C,4];
+    b, a [B,T,Hv]; A_log, dt_bias [Hv] fp32 (a, A_log, dt_bias all None: no
+    decay gate, g is None). conv_state [B,C,3] or None (zeros). The new
+    convolution state goes to conv_state_out (default: a new tensor, or None
+    when update_conv_state is False); pass conv_state_out=conv_state to update
+    in place. ``out`` optionally gives (q, k, v, beta, g) to write into.
+    Returns (q [B,Hk,T,d], k, v [B,Hv,T,d], beta [B,Hv,T], g [B,Hv,T] or None,
+    new conv state or None).
+    """
+    if qkv.dim() != 3:
+        raise ValueError("qkv must be [B,T,C]")
+    B, T, C = qkv.shape
+    dev, dt = qkv.device, qkv.dtype
+    if dt not in _DT:
+        raise TypeError("qkv must be bfloat16 or float32")
+    if Hk < 1 or Hv < 1 or C % (2 * Hk + Hv):
+        raise ValueError("C = %d is not (2*Hk + Hv) * d for Hk=%d, Hv=%d" % (C, Hk, Hv))
+    d = C // (2 * Hk + Hv)
+    _check_tensor("qkv", qkv, (B, T, C), dt, dev)
+    _check_tensor("conv_w", conv_w, (C, 4), dt, dev)
+    _check_tensor("b", b, (B, T, Hv), dt, dev)
+    gated = a is not None
+    if gated:
+        _check_tensor("a", a, (B, T, Hv), dt, dev)
+        _check_tensor("A_log", A_log, (Hv,), torch.float32, dev)
+        _check_tensor("dt_bias", dt_bias, (Hv,), torch.float32, dev)
+    if conv_state is not None:
+        _check_tensor("conv_state", conv_state, (B, C, 3), dt, dev)
+    if conv_state_out is None and update_conv_state:
+        conv_state_out = torch.empty(B, C, 3, dtype=dt, device=dev)
+    elif conv_state_out is not None:
+        _check_tensor("conv_state_out", conv_state_out, (B, C, 3), dt, dev)
+    if out is None:
+        q = torch.empty(B, Hk, T, d, dtype=dt, device=dev)
+        k = torch.empty(B, Hk, T, d, dtype=dt, device=dev)
+        v = torch.empty(B, Hv, T, d, dtype=dt, device=dev)
+        beta = torch.empty(B, Hv, T, dtype=dt, device=dev)
+        g = torch.empty(B, Hv, T, dtype=dt, device=dev) if gated else None
+    else:
+        q, k, v, beta, g = out
+        _check_tensor("q", q, (B, Hk, T, d), dt, dev)
+        _check_tensor("k", k, (B, Hk, T, d), dt, dev)
+        _check_tensor("v", v, (B, Hv, T, d), dt, dev)
+        _check_tensor("beta", beta, (B, Hv, T), dt, dev)
+        if gated:
+            _check_tensor("g", g, (B, Hv, T), dt, dev)
+        else:
+            g = None
+    st = lib().dn_layer_prologue(_ptr(qkv), _ptr(conv_w), _ptr(conv_state), _ptr(conv_state_out),
+                                 _ptr(b), _ptr(a), _ptr(A_log), _ptr(dt_bias), _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(beta), _ptr(g), B, T, Hk, Hv, d, d, _DT[dt],
+                                 _stream(stream))
+    _lib.check("dn_layer_prologue", st)
+    return q, k, v, beta, g, conv_state_out
+
+
+def layer_epilogue(o, z, norm_w, eps=1e-6, *, out=None, stream=None):
+    """Gated RMSNorm after the rule: o [B,Hv,T,dv] (head-major read-out),
+    z [B,T,Hv*dv], norm_w [dv] -> out [B,T,Hv*dv] (token-major, ready for the
+    output projection)."""
+    if o.dim() != 4:
+        raise ValueError("o must be [B,Hv,T,dv]")
+    B, Hv, T, dv = o.shape
+    dev, dt = o.device, o.dtype
+    if dt not in _DT:
+        raise TypeError("o must be bfloat16 or float32")
+    _check_tensor("o", o, (B, Hv, T, dv), dt, dev)
+    _check_tensor("z", z, (B, T, Hv * dv), dt, dev)
+    _check_tensor("norm_w", norm_w, (dv,), dt, dev)
+    if out is None:
+        out = torch.empty(B, T, Hv * dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("out", out, (B, T, Hv * dv), dt, dev)
+    st = lib().dn_layer_epilogue(_ptr(o), _ptr(z), _ptr(norm_w), _ptr(out), B, Hv, T, dv,
+                                 float(eps), _DT[dt], _stream(stream))
+    _lib.check("dn_layer_epilogue", st)
+    return out
+
+
+def gated_deltanet_layer(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *,
+                         conv_state=None, S=None, eps=1e-6, workspace=None, stream=None):
+    """The gated layer between its input and output projections (page "28.
+    Linear attention and Gated DeltaNet", section "The full layer"): prologue,
+    the rule (the recurrent step for T == 1 with a carried state, the chunked
+    form otherwise), epilogue. The projections themselves are plain GEMMs and
+    stay with the caller: qkv, z, b, a are their outputs.
+
+    S [B,Hv,d,d] fp32 (or None: zeros) is the carried recurrent state; it is
+    updated in place when given. Returns (out [B,T,Hv*d], new conv state,
+    new recurrent state).
+    """
+    q, k, v, beta, g, cst = layer_prologue(qkv, conv_w, b, a, A_log, dt_bias, Hk, Hv,
+                                           conv_state=conv_state, stream=stream)
+    B, _, T, d = q.shape
+    if T == 1 and S is not None:
+        o = decode_step_gqa(q[:, :, 0], k[:, :, 0], v[:, :, 0], beta[:, :, 0],
+                            None if g is None else g[:, :, 0], S, stream=stream)
+        o = o.unsqueeze(2)
+        S_new = S
+    else:
+        o, S_new = chunk_fwd_gqa(q, k, v, beta, g, S, S_final=S, workspace=workspace,
+                                 stream=stream)
+    return layer_epilogue(o, z, norm_w, eps, stream=stream), cst, S_new
 
 
 def chunk_prep(q, k, v, beta, g, workspace, *, kda=False, stream=None):

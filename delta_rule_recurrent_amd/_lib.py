@@ -33,6 +33,8 @@ SIGNATURES = {
     "dn_chunk_fwd_varlen_workspace": (_sz, [_i] * 6),
     "dn_chunk_fwd_varlen": (_i, [_i] + [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_decode_tokens": (_i, [_i] + [_vp] * 8 + [_i] * 6 + [_vp]),
+    "dn_layer_prologue": (_i, [_vp] * 13 + [_i] * 7 + [_vp]),
+    "dn_layer_epilogue": (_i, [_vp] * 4 + [_i] * 4 + [ctypes.c_float, _i, _vp]),
     "dn_chunk_prep": (_i, [_i] + [_vp] * 5 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_chunk_scan": (_i, [_i] + [_vp] * 4 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_recurrent_fwd": (_i, _PREFILL + [_vp]),

@@ -255,6 +255,41 @@ int dn_decode_tokens(int kda, const void* q, const void* k, const void* v, const
                                            dv, as_stream(stream), S_snap));
 }
 
+int dn_layer_prologue(const void* qkv, const void* conv_w, const void* conv_state,
+                      void* conv_state_out, const void* b, const void* a, const float* A_log,
+                      const float* dt_bias, void* q, void* k, void* v, void* beta, void* g,
+                      int B, int T, int Hk, int Hv, int dk, int dv, int dtype, void* stream) {
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || Hv % Hk != 0) return DN_EINVAL;
+    if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+    if (B > 65535 || 2LL * Hk + Hv > 65535) return DN_EINVAL;
+    if (!conv_w) return DN_EINVAL;
+    if (T > 0 && (!qkv || !q || !k || !v || !b || !beta)) return DN_EINVAL;
+    if (g && (!a || !A_log || !dt_bias)) return DN_EINVAL;
+    const unsigned esz = dtype == DN_F32 ? 4u : 2u;
+    if (misaligned(qkv) || misaligned(conv_w) || misaligned(conv_state) ||
+        misaligned(conv_state_out) || misaligned(q) || misaligned(k) || misaligned(v) ||
+        misaligned(b, esz) || misaligned(a, esz) || misaligned(beta, esz) || misaligned(g, esz) ||
+        misaligned(A_log, 4) || misaligned(dt_bias, 4))
+        return DN_EINVAL;
+    if ((dk != 64 && dk != 128) || dk != dv) return DN_ENOTSUP;
+    return hip_status(dn::launch_layer_prologue(dtype, qkv, conv_w, conv_state, conv_state_out, b,
+                                                g ? a : nullptr, A_log, dt_bias, q, k, v, beta, g,
+                                                B, T, Hk, Hv, dk, as_stream(stream)));
+}
+
+int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* out, int B, int Hv,
+                      int T, int dv, float eps, int dtype, void* stream) {
+    if (B < 1 || Hv < 1 || T < 0 || !(eps >= 0.0f && eps < 3.0e38f)) return DN_EINVAL;
+    if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+    if (!norm_w) return DN_EINVAL;
+    if (T > 0 && (!o || !z || !out)) return DN_EINVAL;
+    if (misaligned(o) || misaligned(z) || misaligned(norm_w) || misaligned(out)) return DN_EINVAL;
+    if ((long long)B * Hv * T > (1LL << 37)) return DN_EINVAL;
+    if (dv != 64 && dv != 128) return DN_ENOTSUP;
+    return hip_status(dn::launch_layer_epilogue(dtype, o, z, norm_w, out, B, Hv, T, dv, eps,
+                                                as_stream(stream)));
+}
+
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,
                   const void* g, int B, int H, int T, int dk, int dv, int dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {

@@ -81,6 +81,21 @@ size_t chunk_varlen_workspace_bytes(long long N, long long H, long long T, int d
 // Workspace bytes of the chunkwise prefill (per call).
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype);
 
+// The gated layer around the rule (d = d_k = d_v). Prologue: causal
+// convolution + SiLU of the token-major q/k/v channel rows, head split,
+// L2 norm of q and k (q also scaled by d^-1/2), gates beta and g (g NULL: none);
+// then, when conv_state_out != NULL, the new convolution state (may alias
+// conv_state). Epilogue: gated RMSNorm of the head-major read-out into
+// token-major rows.
+hipError_t launch_layer_prologue(int dtype, const void* qkv, const void* conv_w,
+                                 const void* conv_state, void* conv_state_out, const void* b,
+                                 const void* a, const float* A_log, const float* dt_bias, void* q,
+                                 void* k, void* v, void* beta, void* g, int B, int T, int Hk,
+                                 int Hv, int d, hipStream_t st);
+hipError_t launch_layer_epilogue(int dtype, const void* o, const void* z, const void* norm_w,
+                                 void* out, int B, int Hv, int T, int d, float eps,
+                                 hipStream_t st);
+
 // S_final = S0 (or zeros when S0 == NULL), n floats; used when T == 0.
 hipError_t launch_state_copy(const float* S0, float* S_final, long long n, hipStream_t stream);
 

@@ -280,6 +280,59 @@ int dn_decode_tokens(int kda, const void* q, const void* k, const void* v,
                      const void* beta, const void* g, float* S, void* o, float* S_snap,
                      int B, int H, int K, int dk, int dv, int dtype, void* stream);
 
+/*
+ * The gated layer's work before the rule (page "28. Linear attention and
+ * Gated DeltaNet", section "The full layer", steps 2 to 5), in one pass over
+ * the projected rows: depthwise causal convolution of width 4 over time with
+ * carried history, SiLU, split into key and value heads, L2 normalisation of
+ * q and k (q then scaled by dk^-1/2), and the gates beta = sigmoid(b),
+ * g = -exp(A_log) * softplus(a + dt_bias). The outputs are exactly the
+ * head-major q, k, v, beta, g that dn_chunk_fwd_gqa / dn_decode_step_gqa take.
+ *   qkv         [B,T,C] (dtype), C = 2*Hk*dk + Hv*dv: per token, the q channels
+ *               of key heads 0..Hk-1, then k, then v of value heads 0..Hv-1
+ *   conv_w      [C,4] (dtype) filter taps per channel, tap 3 multiplies the
+ *               current token, tap 0 the token three steps back
+ *   conv_state  [B,C,3] (dtype) the three inputs before token 0, oldest first,
+ *               or NULL => zeros
+ *   conv_state_out [B,C,3] (dtype) or NULL => not written: the last three
+ *               inputs of (conv_state, qkv) per channel. May equal conv_state
+ *               (in-place update; it is written after every read of it); any
+ *               other overlap with an input is not allowed.
+ *   b, a        [B,T,Hv] (dtype) gate inputs; a is read only when g != NULL
+ *   A_log, dt_bias [Hv] fp32 (read only when g != NULL)
+ *   q, k        [B,Hk,T,dk] (dtype) out;  v [B,Hv,T,dv] (dtype) out
+ *   beta        [B,Hv,T] (dtype) out;     g [B,Hv,T] (dtype) out, or NULL for a
+ *               layer without decay (DeltaNet): then a, A_log, dt_bias unused
+ * Arithmetic is fp32 from the stored inputs, rounded once to dtype at each
+ * output. A norm below 1e-12 divides by 1e-12. dk == dv in {64, 128}
+ * (DN_ENOTSUP otherwise); Hk, Hv >= 1 with Hv a multiple of Hk, B <= 65535 and
+ * 2*Hk + Hv <= 65535 (DN_EINVAL otherwise). qkv, conv_w, the conv states, q, k,
+ * v must be 16-byte aligned; b, a, beta, g element-aligned. T == 0 writes only
+ * conv_state_out (a copy of conv_state, or zeros); the per-token tensors may be
+ * NULL then.
+ */
+int dn_layer_prologue(const void* qkv, const void* conv_w, const void* conv_state,
+                      void* conv_state_out, const void* b, const void* a, const float* A_log,
+                      const float* dt_bias, void* q, void* k, void* v, void* beta, void* g,
+                      int B, int T, int Hk, int Hv, int dk, int dv, int dtype, void* stream);
+
+/*
+ * The gated layer's work after the rule (same page and section, step 7):
+ * gated RMSNorm of every value head's read-out, written token-major for the
+ * output projection,
+ *   out[b,t,h*dv + c] = w[c] * n[b,h,t,c] * SiLU(z[b,t,h*dv + c]),
+ *   n = o / sqrt(mean_c(o^2) + eps) rounded to dtype (as the page rounds the
+ *   normalised value to the activation type before the products).
+ *   o      [B,Hv,T,dv] (dtype) the rule's read-out (o of dn_chunk_fwd_gqa)
+ *   z      [B,T,Hv*dv] (dtype) the output gate
+ *   norm_w [dv] (dtype) the weight vector, shared by all heads
+ *   out    [B,T,Hv*dv] (dtype), must not overlap o or z
+ * eps >= 0 and finite (the page uses 1e-6). dv in {64, 128} (DN_ENOTSUP
+ * otherwise); all four pointers 16-byte aligned; T == 0 does nothing.
+ */
+int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* out, int B, int Hv,
+                      int T, int dv, float eps, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

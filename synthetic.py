@@ -95,6 +95,43 @@ def make(kind: str, B: int, H: int, T: int, dk: int, dv: int, dtype: str = "bf16
     return out
 
 
+def make_layer(B: int, T: int, Hk: int, Hv: int, d: int, dtype: str = "bf16", seed: int = 0,
+               conv_state: bool = True, gated: bool = True) -> dict:
+    """Draw the inputs of the gated layer around the rule (the outputs of its
+    input projections plus its parameters; page "28. Linear attention and
+    Gated DeltaNet", section "The full layer"). Drawn on the CPU from one
+    generator, in this order:
+      * qkv [B,T,C] ~ N(0,1), C = (2*Hk + Hv)*d; z [B,T,Hv*d] ~ N(0,1);
+      * b, a [B,T,Hv] ~ N(0,1) (a None when not gated);
+      * conv_w [C,4] ~ U(-1/2, 1/2) (a depthwise filter of width 4 initialised
+        uniformly within 1/sqrt(fan-in));
+      * conv_state [B,C,3] ~ N(0,1) when requested;
+      * A_log = log(U(0.01, 16)) (the page's initialisation), dt_bias ~ N(1, 0.1^2)
+        (the page starts it at one; drawn around one so a dropped bias shows);
+      * norm_w [d] ~ U(0.5, 1.5) (the page starts it at one; drawn so that a
+        dropped weight shows).
+    Activations, filter, state and norm weight are rounded once to the storage
+    dtype; A_log and dt_bias stay fp32.
+    """
+    gen = torch.Generator().manual_seed(int(seed))
+    C = (2 * Hk + Hv) * d
+    qkv = torch.randn(B, T, C, generator=gen)
+    z = torch.randn(B, T, Hv * d, generator=gen)
+    b = torch.randn(B, T, Hv, generator=gen)
+    a = torch.randn(B, T, Hv, generator=gen)
+    conv_w = torch.rand(C, 4, generator=gen) - 0.5
+    cs = torch.randn(B, C, 3, generator=gen)
+    A_log = torch.log(torch.rand(Hv, generator=gen) * (16 - 0.01) + 0.01)
+    dt_bias = 1.0 + 0.1 * torch.randn(Hv, generator=gen)
+    norm_w = torch.rand(d, generator=gen) + 0.5
+    dt = DTYPES[dtype]
+    return dict(qkv=qkv.to(dt).contiguous(), z=z.to(dt).contiguous(), b=b.to(dt).contiguous(),
+                a=a.to(dt).contiguous() if gated else None, conv_w=conv_w.to(dt).contiguous(),
+                conv_state=cs.to(dt).contiguous() if conv_state else None,
+                A_log=A_log.float() if gated else None, dt_bias=dt_bias.float() if gated else None,
+                norm_w=norm_w.to(dt).contiguous(), B=B, T=T, Hk=Hk, Hv=Hv, d=d, dtype=dtype)
+
+
 def make_config(name: str, **overrides) -> dict:
     """Inputs of a named workload; keyword overrides (T, B, steps, ...) shrink it."""
     cfg = dict(CONFIGS[name])
@@ -111,4 +148,4 @@ def describe(name: str) -> str:
     return ", ".join("%s=%s" % (k, c[k]) for k in ("kind", "B", "H", "T", "dk", "dv", "dtype"))
 
 
-__all__ = ["CONFIGS", "make", "make_config", "nbytes", "describe"]
+__all__ = ["CONFIGS", "make", "make_layer", "make_config", "nbytes", "describe"]

@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -294,3 +294,59 @@ def test_phase_validation():
     assert _scan(S0=MIS) == E
     assert _scan(ws=None) == W
     assert _scan(dk=96, dv=96) == _lib.DN_ENOTSUP
+
+
+def _prologue(**kw):
+    args = dict(qkv=P, conv_w=P, conv_state=P, conv_state_out=P, b=P, a=P, A_log=P, dt_bias=P,
+                q=P, k=P, v=P, beta=P, g=P, B=1, T=64, Hk=1, Hv=2, dk=64, dv=64, dtype=1,
+                stream=None)
+    args.update(kw)
+    return _lib.lib().dn_layer_prologue(*[args[n] for n in (
+        "qkv", "conv_w", "conv_state", "conv_state_out", "b", "a", "A_log", "dt_bias", "q", "k",
+        "v", "beta", "g", "B", "T", "Hk", "Hv", "dk", "dv", "dtype", "stream")])
+
+
+def test_layer_prologue_validation():
+    E, N = _lib.DN_EINVAL, _lib.DN_ENOTSUP
+    assert _prologue(Hv=3, Hk=2) == E          # value heads not a multiple of key heads
+    assert _prologue(Hk=0) == E
+    assert _prologue(B=0) == E
+    assert _prologue(B=70000) == E
+    assert _prologue(T=-1) == E
+    assert _prologue(dtype=5) == E
+    assert _prologue(conv_w=None) == E
+    assert _prologue(qkv=None) == E
+    assert _prologue(beta=None) == E
+    assert _prologue(a=None) == E              # a decay gate needs a, A_log, dt_bias
+    assert _prologue(A_log=None) == E
+    assert _prologue(dt_bias=None) == E
+    assert _prologue(qkv=MIS) == E
+    assert _prologue(conv_w=MIS) == E
+    assert _prologue(conv_state_out=MIS) == E
+    assert _prologue(q=MIS) == E
+    assert _prologue(b=ODD) == E
+    assert _prologue(A_log=P + 2) == E
+    assert _prologue(dk=96, dv=96) == N
+    assert _prologue(dk=64, dv=128) == N
+
+
+def _epilogue(**kw):
+    args = dict(o=P, z=P, norm_w=P, out=P, B=1, Hv=2, T=64, dv=64, eps=1e-6, dtype=1, stream=None)
+    args.update(kw)
+    return _lib.lib().dn_layer_epilogue(*[args[n] for n in (
+        "o", "z", "norm_w", "out", "B", "Hv", "T", "dv", "eps", "dtype", "stream")])
+
+
+def test_layer_epilogue_validation():
+    E, N = _lib.DN_EINVAL, _lib.DN_ENOTSUP
+    assert _epilogue(o=None) == E
+    assert _epilogue(z=None) == E
+    assert _epilogue(norm_w=None) == E
+    assert _epilogue(out=MIS) == E
+    assert _epilogue(B=0) == E
+    assert _epilogue(T=-1) == E
+    assert _epilogue(eps=-1.0) == E
+    assert _epilogue(eps=float("nan")) == E
+    assert _epilogue(eps=float("inf")) == E
+    assert _epilogue(dtype=7) == E
+    assert _epilogue(dv=96) == N
