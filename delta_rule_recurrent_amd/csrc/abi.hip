@@ -284,7 +284,7 @@ int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* ou
     if (!norm_w) return DN_EINVAL;
     if (T > 0 && (!o || !z || !out)) return DN_EINVAL;
     if (misaligned(o) || misaligned(z) || misaligned(norm_w) || misaligned(out)) return DN_EINVAL;
-    if ((long long)B * Hv * T > (1LL << 37)) return DN_EINVAL;
+    if ((long long)B * Hv * T > (1LL << 35)) return DN_EINVAL;
     if (dv != 64 && dv != 128) return DN_ENOTSUP;
     return hip_status(dn::launch_layer_epilogue(dtype, o, z, norm_w, out, B, Hv, T, dv, eps,
                                                 as_stream(stream)));

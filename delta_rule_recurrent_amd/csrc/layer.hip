@@ -21,8 +21,9 @@ namespace dn {
 namespace {
 
 constexpr int LAYER_WG = 256;   // threads per workgroup of the layer kernels
-constexpr int RUN = 16;         // consecutive tokens one lane group convolves in registers
+constexpr int RUN = 8;          // consecutive tokens one lane group convolves in registers
 constexpr int CONV_K = 4;       // convolution width (its state: the last 3 inputs)
+constexpr int EPI_ROWS = 64;    // rows of the read-out per epilogue workgroup
 
 // Eight consecutive elements <-> fp32.
 __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
@@ -64,7 +65,14 @@ __device__ __forceinline__ void load_raw(const float* p, Raw8<float>& r) {
 __device__ __forceinline__ float elem(const Raw8<bf16>& r, int i) { return (float)r.v[i]; }
 __device__ __forceinline__ float elem(const Raw8<float>& r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
 
-__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+// SiLU with the hardware exp2 and reciprocal (each within 1 ulp): x / (1 + e^-x).
+// Large negative x gives e^-x = inf and a zero reciprocal, so the result is -0.
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
+// 1 / max(sqrt(s), 1e-12) for a sum of squares s >= 0, with the hardware rsqrt.
+__device__ __forceinline__ float inv_norm(float s) { return __builtin_amdgcn_rsqf(fmaxf(s, 1e-24f)); }
 
 // Sum over the `width` consecutive lanes that hold one row (width a power of two).
 template <int WIDTH>
@@ -84,7 +92,7 @@ __device__ __forceinline__ float row_sum(float s) {
 // ---------------------------------------------------------------------------
 template <typename E, int D>
 __global__ __launch_bounds__(LAYER_WG) void layer_prologue_kernel(
-    const E* __restrict__ qkv, const E* __restrict__ conv_w, const E* __restrict__ cstate,
+    const E* __restrict__ qkv, const E* __restrict__ conv_w, const E* cstate, E* cout,
     const E* __restrict__ bin, const E* __restrict__ ain, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, E* __restrict__ q, E* __restrict__ k, E* __restrict__ v,
     E* __restrict__ beta, E* __restrict__ g, int T, int Hk, int Hv) {
@@ -166,12 +174,38 @@ __global__ __launch_bounds__(LAYER_WG) void layer_prologue_kernel(
             h[2][i] = xi;
         }
         if (is_key) {
-            ss = row_sum<LPR>(ss);
-            const float sc = qs / fmaxf(sqrtf(ss), 1e-12f);
+            const float sc = qs * inv_norm(row_sum<LPR>(ss));
 #pragma unroll
             for (int i = 0; i < 8; ++i) y[i] *= sc;
         }
         if (t0 + r < T) store8(orow + (long)r * D, y);
+    }
+
+    // The new convolution state (the last three inputs of each channel) is
+    // written by the group of the first run, the only one that reads the old
+    // state, after its reads: an in-place update cannot race with them. For
+    // T < 3 the oldest entries come from the old state (input t < 0 is entry
+    // 3 + t), re-read here by the same lanes.
+    if (cout && t0 == 0) {
+        float nh[24];
+#pragma unroll
+        for (int j = 0; j < 3; ++j) {
+            const long tt = (long)T - 3 + j;
+            float rv[8];
+            if (tt >= 0) {
+                load8(qkv + ((long)b * T + tt) * C + c, rv);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    rv[i] = cstate ? to_f32(cstate[((long)b * C + c + i) * 3 + 3 + tt]) : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) nh[3 * i + j] = rv[i];
+        }
+        const long so = ((long)b * C + c) * 3;
+        store8(cout + so, *reinterpret_cast<const float(*)[8]>(nh));
+        store8(cout + so + 8, *reinterpret_cast<const float(*)[8]>(nh + 8));
+        store8(cout + so + 16, *reinterpret_cast<const float(*)[8]>(nh + 16));
     }
 
     if (s >= 2 * Hk) {
@@ -193,9 +227,101 @@ __global__ __launch_bounds__(LAYER_WG) void layer_prologue_kernel(
     }
 }
 
-// New convolution state: the last three entries of (old state, inputs) per
-// channel, [B][C][3]. One thread per (sequence, channel); it reads everything it
-// needs before writing, so the new state may overwrite the old one.
+// ---------------------------------------------------------------------------
+// Prologue of a single token (decode). One lane group per (sequence, segment):
+// the group reads its channels' three-entry history and the new input,
+// convolves, and writes the shifted history back (to conv_state_out, which may
+// be conv_state itself: every lane reads its own 24 entries before writing
+// them, and no other lane touches them). Grid ceil(B*(2*Hk + Hv) / GROUPS).
+// ---------------------------------------------------------------------------
+template <typename E, int D>
+__global__ __launch_bounds__(LAYER_WG) void layer_prologue_step_kernel(
+    const E* __restrict__ qkv, const E* __restrict__ conv_w, const E* cstate, E* cout,
+    const E* __restrict__ bin, const E* __restrict__ ain, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, E* __restrict__ q, E* __restrict__ k, E* __restrict__ v,
+    E* __restrict__ beta, E* __restrict__ g, int B, int Hk, int Hv) {
+    constexpr int LPR = D / 8;
+    constexpr int GROUPS = LAYER_WG / LPR;
+    constexpr float QSCALE = D == 64 ? 0.125f : 0.08838834764831845f;
+    const int NS = 2 * Hk + Hv;
+    const long gi = (long)blockIdx.x * GROUPS + threadIdx.x / LPR;
+    if (gi >= (long)B * NS) return;   // whole lane groups leave together
+    const int l = threadIdx.x % LPR;
+    const long b = gi / NS;
+    const int s = (int)(gi % NS);
+    const long C = (long)NS * D;
+    const long c = (long)s * D + l * 8;
+
+    Raw8<E> xr, w0, w1, w2, w3, h0, h1, h2;
+    load_raw(qkv + b * C + c, xr);
+    load_raw(conv_w + c * CONV_K, w0);
+    load_raw(conv_w + c * CONV_K + 8, w1);
+    load_raw(conv_w + c * CONV_K + 16, w2);
+    load_raw(conv_w + c * CONV_K + 24, w3);
+    const long so = (b * C + c) * 3;   // this lane's 24 history entries, channel-major
+    if (cstate) {
+        load_raw(cstate + so, h0);
+        load_raw(cstate + so + 8, h1);
+        load_raw(cstate + so + 16, h2);
+    }
+    float y[8], ss = 0.0f;
+    float hist[24];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        hist[i] = cstate ? elem(h0, i) : 0.0f;
+        hist[8 + i] = cstate ? elem(h1, i) : 0.0f;
+        hist[16 + i] = cstate ? elem(h2, i) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        // channel i: taps conv_w[c+i][0..3] are elements 4i..4i+3 of the 32 loaded
+        const Raw8<E>& wr = i < 2 ? w0 : i < 4 ? w1 : i < 6 ? w2 : w3;
+        const int o = (i % 2) * 4;
+        const float xi = elem(xr, i);
+        const float acc = elem(wr, o) * hist[3 * i] + elem(wr, o + 1) * hist[3 * i + 1] +
+                          elem(wr, o + 2) * hist[3 * i + 2] + elem(wr, o + 3) * xi;
+        y[i] = silu(acc);
+        ss += y[i] * y[i];
+    }
+    if (cout) {
+        float nh[24];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            nh[3 * i] = hist[3 * i + 1];
+            nh[3 * i + 1] = hist[3 * i + 2];
+            nh[3 * i + 2] = elem(xr, i);
+        }
+        // shifted history of stored values: exact in the storage type
+        store8(cout + so, *reinterpret_cast<const float(*)[8]>(nh));
+        store8(cout + so + 8, *reinterpret_cast<const float(*)[8]>(nh + 8));
+        store8(cout + so + 16, *reinterpret_cast<const float(*)[8]>(nh + 16));
+    }
+    E* out;
+    long row;
+    if (s < Hk) { out = q; row = b * Hk + s; }
+    else if (s < 2 * Hk) { out = k; row = b * Hk + s - Hk; }
+    else { out = v; row = b * Hv + s - 2 * Hk; }
+    if (s < 2 * Hk) {
+        const float sc = (s < Hk ? QSCALE : 1.0f) * inv_norm(row_sum<LPR>(ss));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] *= sc;
+    }
+    store8(out + row * D + l * 8, y);
+    if (s >= 2 * Hk && l == 0) {
+        const int hv = s - 2 * Hk;
+        const long i = b * Hv + hv;   // [B,1,Hv] in, [B,Hv,1] out: the same index
+        beta[i] = from_f32<E>(1.0f / (1.0f + __expf(-to_f32(bin[i]))));
+        if (g) {
+            const float z = to_f32(ain[i]) + dt_bias[hv];
+            g[i] = from_f32<E>(-__expf(A_log[hv]) * (fmaxf(z, 0.0f) + log1pf(__expf(-fabsf(z)))));
+        }
+    }
+}
+
+// New convolution state for an empty input (T == 0: the old state, or zeros),
+// [B][C][3]; written the same way for any T. One thread per (sequence,
+// channel); it reads everything it needs before writing, so the new state may
+// overwrite the old one.
 template <typename E>
 __global__ __launch_bounds__(LAYER_WG) void conv_state_kernel(const E* __restrict__ qkv,
                                                               const E* cstate, E* cout, int T,
@@ -215,7 +341,7 @@ __global__ __launch_bounds__(LAYER_WG) void conv_state_kernel(const E* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Epilogue. 64 rows of the head-major read-out o [B][Hv][T][D] per workgroup
+// Epilogue. EPI_ROWS rows of the head-major read-out o [B][Hv][T][D] per workgroup
 // (consecutive rows, so a wave reads a contiguous span); D/8 lanes per row.
 //   out[b][t][hv*D + c] = w[c] * round(o * rsqrt(mean(o^2) + eps)) * SiLU(z[b][t][hv*D + c])
 // with the normalised value rounded to the storage type before the products.
@@ -226,9 +352,9 @@ __global__ __launch_bounds__(LAYER_WG) void layer_epilogue_kernel(
     E* __restrict__ out, long rows, int T, int Hv, float eps) {
     constexpr int LPR = D / 8;
     constexpr int GROUPS = LAYER_WG / LPR;
-    constexpr int PER = 64 / GROUPS;
+    constexpr int PER = EPI_ROWS / GROUPS;
     const int grp = threadIdx.x / LPR, l = threadIdx.x % LPR;
-    const long base = (long)blockIdx.x * 64;
+    const long base = (long)blockIdx.x * EPI_ROWS;
     float wv[8];
     load8(nw + l * 8, wv);
 
@@ -268,18 +394,28 @@ hipError_t prologue_launch(const void* qkv, const void* conv_w, const void* csta
                            int B, int T, int Hk, int Hv, hipStream_t st) {
     const E* x = static_cast<const E*>(qkv);
     const long C = (long)(2 * Hk + Hv) * D;
+    if (T == 1) {
+        constexpr int GROUPS = LAYER_WG / (D / 8);
+        const long groups = (long)B * (2 * Hk + Hv);
+        layer_prologue_step_kernel<E, D><<<(unsigned)((groups + GROUPS - 1) / GROUPS), LAYER_WG, 0,
+                                           st>>>(
+            x, static_cast<const E*>(conv_w), static_cast<const E*>(cstate),
+            static_cast<E*>(cstate_out), static_cast<const E*>(b), static_cast<const E*>(a), A_log,
+            dt_bias, static_cast<E*>(q), static_cast<E*>(k), static_cast<E*>(v),
+            static_cast<E*>(beta), static_cast<E*>(g), B, Hk, Hv);
+        return hipGetLastError();
+    }
     if (T > 0) {
         constexpr int TILE = (LAYER_WG / (D / 8)) * RUN;
         const dim3 grid((unsigned)((T + TILE - 1) / TILE), (unsigned)(2 * Hk + Hv), (unsigned)B);
         layer_prologue_kernel<E, D><<<grid, LAYER_WG, 0, st>>>(
             x, static_cast<const E*>(conv_w), static_cast<const E*>(cstate),
-            static_cast<const E*>(b), static_cast<const E*>(a), A_log, dt_bias,
+            static_cast<E*>(cstate_out), static_cast<const E*>(b), static_cast<const E*>(a), A_log, dt_bias,
             static_cast<E*>(q), static_cast<E*>(k), static_cast<E*>(v), static_cast<E*>(beta),
             static_cast<E*>(g), T, Hk, Hv);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        return hipGetLastError();
     }
-    if (cstate_out) {
+    if (cstate_out) {   // T == 0: the state passes through (or becomes zeros)
         const long n = (long)B * C;
         conv_state_kernel<E><<<(unsigned)((n + LAYER_WG - 1) / LAYER_WG), LAYER_WG, 0, st>>>(
             x, static_cast<const E*>(cstate), static_cast<E*>(cstate_out), T, C, n);
@@ -293,7 +429,7 @@ hipError_t epilogue_launch(const void* o, const void* z, const void* w, void* ou
                            int T, float eps, hipStream_t st) {
     const long rows = (long)B * Hv * T;
     if (rows == 0) return hipSuccess;
-    layer_epilogue_kernel<E, D><<<(unsigned)((rows + 63) / 64), LAYER_WG, 0, st>>>(
+    layer_epilogue_kernel<E, D><<<(unsigned)((rows + EPI_ROWS - 1) / EPI_ROWS), LAYER_WG, 0, st>>>(
         static_cast<const E*>(o), static_cast<const E*>(z), static_cast<const E*>(w),
         static_cast<E*>(out), rows, T, Hv, eps);
     return hipGetLastError();
