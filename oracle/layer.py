@@ -64,15 +64,21 @@ def l2norm(x, eps=1e-12):
     return x / np.maximum(n, eps)
 
 
-def gates(b, a, A_log, dt_bias):
-    """b, a [B,T,Hv]; A_log, dt_bias [Hv] -> (beta, g) [B,Hv,T]."""
+def gates(b, a, A_log, dt_bias, allow_neg_eigval=False):
+    """b, a [B,T,Hv]; A_log, dt_bias [Hv] -> (beta, g) [B,Hv,T].
+
+    allow_neg_eigval doubles the write strength to 2 sigmoid(b) in (0, 2), so
+    that I - beta k k^T can reach eigenvalue 1 - beta < 0 along k (page
+    "DeltaNet: Memory That Edits", section "The reflection hiding in the delta
+    rule")."""
     b, a, A_log, dt_bias = _f64(b), _f64(a), _f64(A_log), _f64(dt_bias)
-    beta = sigmoid(b)
+    beta = sigmoid(b) * (2.0 if allow_neg_eigval else 1.0)
     g = -np.exp(A_log) * softplus(a + dt_bias)
     return np.transpose(beta, (0, 2, 1)), np.transpose(g, (0, 2, 1))
 
 
-def prologue(qkv, conv_w, conv_state, b, a, A_log, dt_bias, Hk, Hv, dk, dv):
+def prologue(qkv, conv_w, conv_state, b, a, A_log, dt_bias, Hk, Hv, dk, dv,
+             allow_neg_eigval=False):
     """Returns q, k [B,Hk,T,dk], v [B,Hv,T,dv], beta, g [B,Hv,T], new conv state."""
     y, st = causal_conv1d(qkv, conv_w, conv_state)
     B, T, _ = y.shape
@@ -82,7 +88,7 @@ def prologue(qkv, conv_w, conv_state, b, a, A_log, dt_bias, Hk, Hv, dk, dv):
     v = y[:, :, 2 * ks:].reshape(B, T, Hv, dv).transpose(0, 2, 1, 3)
     q = l2norm(q) * dk ** -0.5
     k = l2norm(k)
-    beta, g = gates(b, a, A_log, dt_bias)
+    beta, g = gates(b, a, A_log, dt_bias, allow_neg_eigval)
     return q, k, v, beta, g, st
 
 

@@ -128,3 +128,24 @@ def test_prologue_splits_heads():
     y = L.silu(qkv)
     assert np.allclose(v, y[:, :, 2 * Hk * dk:].reshape(B, T, Hv, dv).transpose(0, 2, 1, 3))
     assert beta.shape == (B, Hv, T) and g.shape == (B, Hv, T) and st.shape == (B, C, 3)
+
+
+def test_gates_allow_neg_eigval():
+    """The flag doubles beta to 2 sigmoid(b) in (0, 2) and leaves g alone; at
+    large b the transition I - beta k k^T then has eigenvalue near -1 along k
+    (a reflection; page "DeltaNet: Memory That Edits", section "The reflection
+    hiding in the delta rule"), where the plain gate stops near 0."""
+    r = np.random.default_rng(11)
+    b, a = r.standard_normal((2, 7, 3)), r.standard_normal((2, 7, 3))
+    A_log, dt_bias = np.log(r.uniform(0.01, 16, 3)), np.ones(3)
+    b1, g1 = L.gates(b, a, A_log, dt_bias)
+    b2, g2 = L.gates(b, a, A_log, dt_bias, allow_neg_eigval=True)
+    assert np.array_equal(b2, 2 * b1) and np.array_equal(g1, g2)
+    assert (b2 > 0).all() and (b2 < 2).all()
+    k = r.standard_normal(8)
+    k /= np.linalg.norm(k)
+    big = np.full((1, 1, 1), 30.0)
+    for flag, along in ((False, 0.0), (True, -1.0)):
+        beta = L.gates(big, big, np.zeros(1), np.zeros(1), allow_neg_eigval=flag)[0][0, 0, 0]
+        ev = np.sort(np.linalg.eigvalsh(np.eye(8) - beta * np.outer(k, k)))
+        assert abs(ev[0] - along) < 1e-9 and np.allclose(ev[1:], 1.0)
