@@ -21,7 +21,8 @@ from ._lib import DeltaNetError, lib
 
 __all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_fwd_gqa",
            "decode_step_gqa", "chunk_fwd_varlen", "decode_tokens", "layer_prologue",
-           "layer_epilogue", "gated_deltanet_layer", "chunk_prep", "chunk_scan",
+           "layer_epilogue", "gated_deltanet_layer", "ssm_chunk_fwd", "ssm_recurrent_fwd",
+           "ssm_decode_step", "chunk_prep", "chunk_scan",
            "recurrent_fwd",
            "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
            "DeltaNetError", "lib", "library_path"]
@@ -310,7 +311,8 @@ def decode_tokens(q, k, v, beta, g, S, *, kda=False, snapshots=True, o=None, S_s
 
 
 def layer_prologue(qkv, conv_w, b, a, A_log, dt_bias, Hk, Hv, *, conv_state=None,
-                   conv_state_out=None, update_conv_state=True, out=None, stream=None):
+                   conv_state_out=None, update_conv_state=True, allow_neg_eigval=False, out=None,
+                   stream=None):
     """The gated layer's work before the rule, from the projected rows.
 
     qkv [B,T,2*Hk*d + Hv*d] (q, k, v channels per token); conv_w [C,4];
@@ -318,7 +320,8 @@ def layer_prologue(qkv, conv_w, b, a, A_log, dt_bias, Hk, Hv, *, conv_state=None
     decay gate, g is None). conv_state [B,C,3] or None (zeros). The new
     convolution state goes to conv_state_out (default: a new tensor, or None
     when update_conv_state is False); pass conv_state_out=conv_state to update
-    in place. ``out`` optionally gives (q, k, v, beta, g) to write into.
+    in place. allow_neg_eigval: beta = 2 sigmoid(b) in (0, 2) (the reflection
+    range). ``out`` optionally gives (q, k, v, beta, g) to write into.
     Returns (q [B,Hk,T,d], k, v [B,Hv,T,d], beta [B,Hv,T], g [B,Hv,T] or None,
     new conv state or None).
     """
@@ -363,8 +366,8 @@ def layer_prologue(qkv, conv_w, b, a, A_log, dt_bias, Hk, Hv, *, conv_state=None
             g = None
     st = lib().dn_layer_prologue(_ptr(qkv), _ptr(conv_w), _ptr(conv_state), _ptr(conv_state_out),
                                  _ptr(b), _ptr(a), _ptr(A_log), _ptr(dt_bias), _ptr(q), _ptr(k),
-                                 _ptr(v), _ptr(beta), _ptr(g), B, T, Hk, Hv, d, d, _DT[dt],
-                                 _stream(stream))
+                                 _ptr(v), _ptr(beta), _ptr(g), int(bool(allow_neg_eigval)), B, T,
+                                 Hk, Hv, d, d, _DT[dt], _stream(stream))
     _lib.check("dn_layer_prologue", st)
     return q, k, v, beta, g, conv_state_out
 
@@ -393,7 +396,8 @@ def layer_epilogue(o, z, norm_w, eps=1e-6, *, out=None, stream=None):
 
 
 def gated_deltanet_layer(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *,
-                         conv_state=None, S=None, eps=1e-6, workspace=None, stream=None):
+                         conv_state=None, S=None, eps=1e-6, allow_neg_eigval=False,
+                         workspace=None, stream=None):
     """The gated layer between its input and output projections (page "28.
     Linear attention and Gated DeltaNet", section "The full layer"): prologue,
     the rule (the recurrent step for T == 1 with a carried state, the chunked
@@ -405,7 +409,8 @@ def gated_deltanet_layer(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *
     new recurrent state).
     """
     q, k, v, beta, g, cst = layer_prologue(qkv, conv_w, b, a, A_log, dt_bias, Hk, Hv,
-                                           conv_state=conv_state, stream=stream)
+                                           conv_state=conv_state,
+                                           allow_neg_eigval=allow_neg_eigval, stream=stream)
     B, _, T, d = q.shape
     if T == 1 and S is not None:
         o = decode_step_gqa(q[:, :, 0], k[:, :, 0], v[:, :, 0], beta[:, :, 0],
@@ -416,6 +421,82 @@ def gated_deltanet_layer(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *
         o, S_new = chunk_fwd_gqa(q, k, v, beta, g, S, S_final=S, workspace=workspace,
                                  stream=stream)
     return layer_epilogue(o, z, norm_w, eps, stream=stream), cst, S_new
+
+
+def _ssm_args(q, k, v, g, S0):
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,T,dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    _check_tensor("q", q, (B, H, T, dk), dt, dev)
+    _check_tensor("k", k, (B, H, T, dk), dt, dev)
+    _check_tensor("v", v, (B, H, T, dv), dt, dev)
+    _check_tensor("g", g, (B, H, T), dt, dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    return B, H, T, dk, dv, dev, dt
+
+
+def ssm_chunk_fwd(q, k, v, g, S0=None, *, output_final_state=True, o=None, S_final=None,
+                  workspace=None, stream=None):
+    """Chunked selective state-space recurrence S = exp(g) S + k v^T,
+    o = S^T q (Gated DeltaNet without the correction term; no beta).
+    q, k [B,H,T,dk]; v [B,H,T,dv]; g [B,H,T] (zeros: plain causal linear
+    attention). Returns (o, S_final)."""
+    B, H, T, dk, dv, dev, dt = _ssm_args(q, k, v, g, S0)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, T, dv), dt, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    elif S_final is not None:
+        _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
+    if workspace is None:
+        workspace = _alloc_workspace(workspace_bytes(B, H, T, dk, dv, dt), dev)
+    st = lib().dn_ssm_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0), _ptr(o),
+                                _ptr(S_final), B, H, T, dk, dv, _DT[dt], _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("dn_ssm_chunk_fwd", st)
+    return o, S_final
+
+
+def ssm_recurrent_fwd(q, k, v, g, S0=None, *, output_final_state=True, stream=None):
+    """Token-by-token form of ssm_chunk_fwd. Returns (o, S_final)."""
+    B, H, T, dk, dv, dev, dt = _ssm_args(q, k, v, g, S0)
+    o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    S_final = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev) if output_final_state else None
+    st = lib().dn_ssm_recurrent_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S0), _ptr(o),
+                                    _ptr(S_final), B, H, T, dk, dv, _DT[dt], _stream(stream))
+    _lib.check("dn_ssm_recurrent_fwd", st)
+    return o, S_final
+
+
+def ssm_decode_step(q, k, v, g, S, *, o=None, stream=None):
+    """One token of the selective state-space recurrence: q, k [B,H,dk];
+    v [B,H,dv]; g [B,H]; S [B,H,dk,dv] fp32 updated in place. Returns o [B,H,dv]."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    _check_tensor("k", k, (B, H, dk), dt, dev)
+    _check_tensor("v", v, (B, H, dv), dt, dev)
+    _check_tensor("g", g, (B, H), dt, dev)
+    _check_tensor("S", S, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, H, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, dv), dt, dev)
+    st = lib().dn_ssm_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S), _ptr(o), B, H, dk,
+                                  dv, _DT[dt], _stream(stream))
+    _lib.check("dn_ssm_decode_step", st)
+    return o
 
 
 def chunk_prep(q, k, v, beta, g, workspace, *, kda=False, stream=None):

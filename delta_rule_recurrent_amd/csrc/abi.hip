@@ -258,7 +258,8 @@ int dn_decode_tokens(int kda, const void* q, const void* k, const void* v, const
 int dn_layer_prologue(const void* qkv, const void* conv_w, const void* conv_state,
                       void* conv_state_out, const void* b, const void* a, const float* A_log,
                       const float* dt_bias, void* q, void* k, void* v, void* beta, void* g,
-                      int B, int T, int Hk, int Hv, int dk, int dv, int dtype, void* stream) {
+                      int allow_neg_eigval, int B, int T, int Hk, int Hv, int dk, int dv,
+                      int dtype, void* stream) {
     if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || Hv % Hk != 0) return DN_EINVAL;
     if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
     if (B > 65535 || 2LL * Hk + Hv > 65535) return DN_EINVAL;
@@ -274,7 +275,8 @@ int dn_layer_prologue(const void* qkv, const void* conv_w, const void* conv_stat
     if ((dk != 64 && dk != 128) || dk != dv) return DN_ENOTSUP;
     return hip_status(dn::launch_layer_prologue(dtype, qkv, conv_w, conv_state, conv_state_out, b,
                                                 g ? a : nullptr, A_log, dt_bias, q, k, v, beta, g,
-                                                B, T, Hk, Hv, dk, as_stream(stream)));
+                                                allow_neg_eigval ? 2.0f : 1.0f, B, T, Hk, Hv, dk,
+                                                as_stream(stream)));
 }
 
 int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* out, int B, int Hv,
@@ -288,6 +290,32 @@ int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* ou
     if (dv != 64 && dv != 128) return DN_ENOTSUP;
     return hip_status(dn::launch_layer_epilogue(dtype, o, z, norm_w, out, B, Hv, T, dv, eps,
                                                 as_stream(stream)));
+}
+
+int dn_ssm_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                     const float* S0, void* o, float* S_final, int B, int H, int T, int dk, int dv,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (T > 0 && !g) return DN_EINVAL;
+    // (g stands in for beta in the shared checks: the state-space kind has none)
+    const int st = check_common(q, k, v, g, g, false, S0, o, S_final, B, H, T, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    if (dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
+    return chunk_common(dn::KIND_SSM, q, k, v, g, g, S0, o, S_final, B, H, T, dk, dv, dtype,
+                        workspace, workspace_bytes, stream, dn::FWD_TWO);
+}
+
+int dn_ssm_recurrent_fwd(const void* q, const void* k, const void* v, const void* g,
+                         const float* S0, void* o, float* S_final, int B, int H, int T, int dk,
+                         int dv, int dtype, void* stream) {
+    if (T > 0 && !g) return DN_EINVAL;
+    return recurrent_common(dn::KIND_SSM, q, k, v, g, g, S0, o, S_final, B, H, T, dk, dv, dtype,
+                            stream);
+}
+
+int dn_ssm_decode_step(const void* q, const void* k, const void* v, const void* g, float* S,
+                       void* o, int B, int H, int dk, int dv, int dtype, void* stream) {
+    if (!g) return DN_EINVAL;
+    return decode_common(dn::KIND_SSM, q, k, v, g, g, S, o, B, H, dk, dv, dtype, stream);
 }
 
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,

@@ -742,8 +742,8 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
     //         channels, in the 8-consecutive-channel order; both wavefronts),
     //         then (wavefront 1) Q and V in the same order
     const long tk = tok0 + min(lane, L - 1);
-    const E braw = beta[tk];
-    const E graw = KIND == KIND_GATED ? g[tk] : E{};
+    const E braw = KIND == KIND_SSM ? E{} : beta[tk];
+    const E graw = (KIND == KIND_GATED || KIND == KIND_SSM) ? g[tk] : E{};
     F kf[4][KB];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -768,9 +768,12 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
     float* sK = tab[w][2];
     float* bs = tab[w][3];
     {
-        float bv = to_f32(braw), gv = to_f32(graw);
+        // the state-space kind has no write strength and no correction: beta = 1
+        // (so u = V) and a zero beta e^G table (so W = 0)
+        float bv = KIND == KIND_SSM ? 1.f : to_f32(braw), gv = to_f32(graw);
         if (lane >= L) bv = gv = 0.f;
         const float eGC = token_tables(bv, gv, lane, Gs, sX, sK, bs, w == 0 ? eg : nullptr);
+        if (KIND == KIND_SSM) sX[lane] = 0.f;
         if (w == 0)
             for (int ch = lane; ch < DK; ch += 64) gam[ch] = eGC;
     }
@@ -782,9 +785,11 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
         for (int it = 0; it < 4; ++it)
 #pragma unroll
             for (int jt = 0; jt <= it; ++jt) {
-                f32x4 s = zero4();
+                f32x4 s = zero4();   // (state-space kind: A = 0, so T = I)
+                if constexpr (KIND != KIND_SSM) {
 #pragma unroll
-                for (int kb = 0; kb < KB; ++kb) s = mma(kf[it][kb], kf[jt][kb], s);
+                    for (int kb = 0; kb < KB; ++kb) s = mma(kf[it][kb], kf[jt][kb], s);
+                }
                 const int j = 16 * jt + n;
                 const float Gj = Gs[j];
                 const f32x4 Gi = *reinterpret_cast<const f32x4*>(Gs + 16 * it + 4 * gq);
@@ -1802,6 +1807,11 @@ static hipError_t prep_kind(int kind, const void* q, const void* k, const void* 
                             hipStream_t st, HeadMap hm) {
     if (kind == KIND_DELTANET) return prep_t<E, D, KIND_DELTANET>(q, k, v, beta, g, ws, BH, T, st, hm);
     if (kind == KIND_GATED) return prep_t<E, D, KIND_GATED>(q, k, v, beta, g, ws, BH, T, st, hm);
+    if (kind == KIND_SSM) {
+        // only the two-wavefront prep has the state-space kind (not fp32 at d = 128)
+        if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
+        else return prep_t<E, D, KIND_SSM>(q, k, v, beta, g, ws, BH, T, st, hm);
+    }
     // fp32 KDA at d = 128 exceeds the prep kernel's LDS budget (rejected by the ABI layer)
     if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
     else return prep_t<E, D, KIND_KDA>(q, k, v, beta, g, ws, BH, T, st, hm);
@@ -1917,6 +1927,7 @@ template <typename E, int D>
 static hipError_t varlen_t(int kind, const void* q, const void* k, const void* v, const void* beta,
                            const void* g, const float* S0, void* o, float* S_final, const int* cu,
                            int N, int H, int T, void* ws, hipStream_t st) {
+    if (kind == KIND_SSM) return hipErrorNotSupported;
     if (kind == KIND_DELTANET)
         return varlen_kind_t<E, D, KIND_DELTANET>(q, k, v, beta, g, S0, o, S_final, cu, N, H, T, ws, st);
     if (kind == KIND_GATED)
@@ -1946,7 +1957,7 @@ static hipError_t fused_kind(int kind, const void* q, const void* k, const void*
     if constexpr (sizeof(E) != 2) {
         return hipErrorNotSupported;
     } else {
-        if (kind == KIND_KDA) return hipErrorNotSupported;
+        if (kind == KIND_KDA || kind == KIND_SSM) return hipErrorNotSupported;
         const bool wide = scan_bv<D>(BH) == 32;
         if (kind == KIND_GATED)
             return wide ? fused_t<E, D, KIND_GATED, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm)

@@ -4,7 +4,9 @@
 // One token: S~ = Diag(alpha) S; p = S~^T k; u = beta (v - p); S = S~ + k u^T;
 // o = S^T q (page "28. Linear attention and Gated DeltaNet", section "The
 // recurrent form"; page "A walk through of the DeltaNet family of linear
-// attention variants", fused recurrent KDA).
+// attention variants", fused recurrent KDA). The selective state-space kind
+// drops the correction: u = v, S = alpha S + k v^T (page 28, section "Forget:
+// decay").
 #include "dn_device.h"
 #include "dn_launch.h"
 
@@ -55,8 +57,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ 
         if (KIND == KIND_KDA) sa[t] = __expf(to_f32(g[bh * DK + t]));
     }
     const V4 vraw = *reinterpret_cast<const V4*>(v + bh * DV + col0 + 4 * cq);
-    const float b = to_f32(beta[bh]);
-    const float a = (KIND == KIND_GATED) ? __expf(to_f32(g[bh])) : 1.0f;
+    const float b = KIND == KIND_SSM ? 1.0f : to_f32(beta[bh]);
+    const float a = (KIND == KIND_GATED || KIND == KIND_SSM) ? __expf(to_f32(g[bh])) : 1.0f;
     __syncthreads();
 
     f32x4 p = zero4(), r = zero4();
@@ -65,7 +67,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ 
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + RG * i;
         if (KIND == KIND_KDA) s[i] *= sa[row];
-        else if (KIND == KIND_GATED) s[i] *= a;
+        else if (KIND == KIND_GATED || KIND == KIND_SSM) s[i] *= a;
         p += sk[row] * s[i];
         r += sq[row] * s[i];
         kq += sk[row] * sq[row];
@@ -93,7 +95,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(const E* __restrict__ 
     f32x4 vv;
 #pragma unroll
     for (int e = 0; e < 4; ++e) vv[e] = to_f32(vraw[e]);
-    const f32x4 u = b * (vv - p);
+    const f32x4 u = KIND == KIND_SSM ? vv : b * (vv - p);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int row = rg + RG * i;
@@ -137,8 +139,8 @@ __device__ __forceinline__ void token_load(TokenIn<E, DK, KIND>& x, const E* __r
             x.a[m] = (KIND == KIND_KDA) ? to_f32(g[tok * DK + lane + WAVE * m]) : 0.f;
         }
         x.v = to_f32(v[tok * DV + col]);
-        x.b = to_f32(beta[tok]);
-        x.ga = (KIND == KIND_GATED) ? to_f32(g[tok]) : 0.f;
+        x.b = KIND == KIND_SSM ? 1.f : to_f32(beta[tok]);
+        x.ga = (KIND == KIND_GATED || KIND == KIND_SSM) ? to_f32(g[tok]) : 0.f;
     }
 }
 
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(const E* __restrict__ q,
             const int t = t0 + u;
             if (t < T) {
                 TokenIn<E, DK, KIND>& x = ring[u];
-                if (KIND == KIND_GATED) {
+                if (KIND == KIND_GATED || KIND == KIND_SSM) {
                     const float a = __expf(x.ga);
 #pragma unroll
                     for (int r = 0; r < DK; ++r) s[r] *= a;
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(64) void recurrent_kernel(const E* __restrict__ q,
                 float p = 0.f;
 #pragma unroll
                 for (int r = 0; r < DK; ++r) p += readlane_f(x.k[r / WAVE], r % WAVE) * s[r];
-                const float uu = x.b * (x.v - p);
+                const float uu = KIND == KIND_SSM ? x.v : x.b * (x.v - p);
 #pragma unroll
                 for (int r = 0; r < DK; ++r) s[r] += readlane_f(x.k[r / WAVE], r % WAVE) * uu;
                 float out = 0.f;
@@ -235,6 +237,8 @@ static hipError_t decode_t(int kind, const void* q, const void* k, const void* v
         hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_DELTANET, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_, hm);
     else if (kind == KIND_GATED)
         hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_GATED, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_, hm);
+    else if (kind == KIND_SSM)
+        hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_SSM, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_, hm);
     else
         hipLaunchKernelGGL((decode_step_kernel<E, D, D, KIND_KDA, NS>), grid, block, 0, st, q_, k_, v_, b_, g_, S, o_, hm);
     return hipGetLastError();
@@ -260,6 +264,8 @@ static hipError_t recurrent_launch(int kind, const E* q_, const E* k_, const E* 
         hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_DELTANET, SNAP>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T, S_snap);
     else if (kind == KIND_GATED)
         hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_GATED, SNAP>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T, S_snap);
+    else if (kind == KIND_SSM)
+        hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_SSM, SNAP>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T, S_snap);
     else
         hipLaunchKernelGGL((recurrent_kernel<E, D, D, KIND_KDA, SNAP>), grid, block, 0, st, q_, k_, v_, b_, g_, S0, o_, S_final, T, S_snap);
     return hipGetLastError();

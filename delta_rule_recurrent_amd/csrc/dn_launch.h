@@ -7,7 +7,9 @@
 
 namespace dn {
 
-enum Kind { KIND_DELTANET = 0, KIND_GATED = 1, KIND_KDA = 2 };
+// KIND_SSM: the selective state-space recurrence S = alpha S + k v^T (Gated
+// DeltaNet without the correction term: no beta, u = v).
+enum Kind { KIND_DELTANET = 0, KIND_GATED = 1, KIND_KDA = 2, KIND_SSM = 3 };
 enum DType { DT_F32 = 0, DT_BF16 = 1 };
 
 constexpr int CHUNK = 64;
@@ -83,15 +85,16 @@ size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtyp
 
 // The gated layer around the rule (d = d_k = d_v). Prologue: causal
 // convolution + SiLU of the token-major q/k/v channel rows, head split,
-// L2 norm of q and k (q also scaled by d^-1/2), gates beta and g (g NULL: none);
+// L2 norm of q and k (q also scaled by d^-1/2), gates beta = beta_scale *
+// sigmoid(b) and g (g NULL: none);
 // then, when conv_state_out != NULL, the new convolution state (may alias
 // conv_state). Epilogue: gated RMSNorm of the head-major read-out into
 // token-major rows.
 hipError_t launch_layer_prologue(int dtype, const void* qkv, const void* conv_w,
                                  const void* conv_state, void* conv_state_out, const void* b,
                                  const void* a, const float* A_log, const float* dt_bias, void* q,
-                                 void* k, void* v, void* beta, void* g, int B, int T, int Hk,
-                                 int Hv, int d, hipStream_t st);
+                                 void* k, void* v, void* beta, void* g, float beta_scale, int B,
+                                 int T, int Hk, int Hv, int d, hipStream_t st);
 hipError_t launch_layer_epilogue(int dtype, const void* o, const void* z, const void* norm_w,
                                  void* out, int B, int Hv, int T, int d, float eps,
                                  hipStream_t st);

@@ -95,7 +95,7 @@ __global__ __launch_bounds__(LAYER_WG) void layer_prologue_kernel(
     const E* __restrict__ qkv, const E* __restrict__ conv_w, const E* cstate, E* cout,
     const E* __restrict__ bin, const E* __restrict__ ain, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, E* __restrict__ q, E* __restrict__ k, E* __restrict__ v,
-    E* __restrict__ beta, E* __restrict__ g, int T, int Hk, int Hv) {
+    E* __restrict__ beta, E* __restrict__ g, float bscale, int T, int Hk, int Hv) {
     constexpr int LPR = D / 8;
     constexpr int GROUPS = LAYER_WG / LPR;
     constexpr float QSCALE = D == 64 ? 0.125f : 0.08838834764831845f;   // D^-1/2
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(LAYER_WG) void layer_prologue_kernel(
             if (t >= T) break;
             const long src = ((long)b * T + t) * Hv + hv;
             const long dst = ((long)b * Hv + hv) * T + t;
-            beta[dst] = from_f32<E>(1.0f / (1.0f + __expf(-to_f32(bin[src]))));
+            beta[dst] = from_f32<E>(bscale / (1.0f + __expf(-to_f32(bin[src]))));
             if (g) {
                 const float z = to_f32(ain[src]) + bias;
                 const float sp = fmaxf(z, 0.0f) + log1pf(__expf(-fabsf(z)));   // softplus
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(LAYER_WG) void layer_prologue_step_kernel(
     const E* __restrict__ qkv, const E* __restrict__ conv_w, const E* cstate, E* cout,
     const E* __restrict__ bin, const E* __restrict__ ain, const float* __restrict__ A_log,
     const float* __restrict__ dt_bias, E* __restrict__ q, E* __restrict__ k, E* __restrict__ v,
-    E* __restrict__ beta, E* __restrict__ g, int B, int Hk, int Hv) {
+    E* __restrict__ beta, E* __restrict__ g, float bscale, int B, int Hk, int Hv) {
     constexpr int LPR = D / 8;
     constexpr int GROUPS = LAYER_WG / LPR;
     constexpr float QSCALE = D == 64 ? 0.125f : 0.08838834764831845f;
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(LAYER_WG) void layer_prologue_step_kernel(
     if (s >= 2 * Hk && l == 0) {
         const int hv = s - 2 * Hk;
         const long i = b * Hv + hv;   // [B,1,Hv] in, [B,Hv,1] out: the same index
-        beta[i] = from_f32<E>(1.0f / (1.0f + __expf(-to_f32(bin[i]))));
+        beta[i] = from_f32<E>(bscale / (1.0f + __expf(-to_f32(bin[i]))));
         if (g) {
             const float z = to_f32(ain[i]) + dt_bias[hv];
             g[i] = from_f32<E>(-__expf(A_log[hv]) * (fmaxf(z, 0.0f) + log1pf(__expf(-fabsf(z)))));
@@ -391,7 +391,7 @@ template <typename E, int D>
 hipError_t prologue_launch(const void* qkv, const void* conv_w, const void* cstate,
                            void* cstate_out, const void* b, const void* a, const float* A_log,
                            const float* dt_bias, void* q, void* k, void* v, void* beta, void* g,
-                           int B, int T, int Hk, int Hv, hipStream_t st) {
+                           float bs, int B, int T, int Hk, int Hv, hipStream_t st) {
     const E* x = static_cast<const E*>(qkv);
     const long C = (long)(2 * Hk + Hv) * D;
     if (T == 1) {
@@ -402,7 +402,7 @@ hipError_t prologue_launch(const void* qkv, const void* conv_w, const void* csta
             x, static_cast<const E*>(conv_w), static_cast<const E*>(cstate),
             static_cast<E*>(cstate_out), static_cast<const E*>(b), static_cast<const E*>(a), A_log,
             dt_bias, static_cast<E*>(q), static_cast<E*>(k), static_cast<E*>(v),
-            static_cast<E*>(beta), static_cast<E*>(g), B, Hk, Hv);
+            static_cast<E*>(beta), static_cast<E*>(g), bs, B, Hk, Hv);
         return hipGetLastError();
     }
     if (T > 0) {
@@ -412,7 +412,7 @@ hipError_t prologue_launch(const void* qkv, const void* conv_w, const void* csta
             x, static_cast<const E*>(conv_w), static_cast<const E*>(cstate),
             static_cast<E*>(cstate_out), static_cast<const E*>(b), static_cast<const E*>(a), A_log, dt_bias,
             static_cast<E*>(q), static_cast<E*>(k), static_cast<E*>(v), static_cast<E*>(beta),
-            static_cast<E*>(g), T, Hk, Hv);
+            static_cast<E*>(g), bs, T, Hk, Hv);
         return hipGetLastError();
     }
     if (cstate_out) {   // T == 0: the state passes through (or becomes zeros)
@@ -440,18 +440,18 @@ hipError_t epilogue_launch(const void* o, const void* z, const void* w, void* ou
 hipError_t launch_layer_prologue(int dtype, const void* qkv, const void* conv_w,
                                  const void* conv_state, void* conv_state_out, const void* b,
                                  const void* a, const float* A_log, const float* dt_bias, void* q,
-                                 void* k, void* v, void* beta, void* g, int B, int T, int Hk,
-                                 int Hv, int d, hipStream_t st) {
+                                 void* k, void* v, void* beta, void* g, float bs, int B, int T,
+                                 int Hk, int Hv, int d, hipStream_t st) {
     if (dtype == DT_BF16) {
         return d == 64 ? prologue_launch<bf16, 64>(qkv, conv_w, conv_state, conv_state_out, b, a,
-                                                   A_log, dt_bias, q, k, v, beta, g, B, T, Hk, Hv, st)
+                                                   A_log, dt_bias, q, k, v, beta, g, bs, B, T, Hk, Hv, st)
                        : prologue_launch<bf16, 128>(qkv, conv_w, conv_state, conv_state_out, b, a,
-                                                    A_log, dt_bias, q, k, v, beta, g, B, T, Hk, Hv, st);
+                                                    A_log, dt_bias, q, k, v, beta, g, bs, B, T, Hk, Hv, st);
     }
     return d == 64 ? prologue_launch<float, 64>(qkv, conv_w, conv_state, conv_state_out, b, a,
-                                                A_log, dt_bias, q, k, v, beta, g, B, T, Hk, Hv, st)
+                                                A_log, dt_bias, q, k, v, beta, g, bs, B, T, Hk, Hv, st)
                    : prologue_launch<float, 128>(qkv, conv_w, conv_state, conv_state_out, b, a,
-                                                 A_log, dt_bias, q, k, v, beta, g, B, T, Hk, Hv, st);
+                                                 A_log, dt_bias, q, k, v, beta, g, bs, B, T, Hk, Hv, st);
 }
 
 hipError_t launch_layer_epilogue(int dtype, const void* o, const void* z, const void* norm_w,

@@ -303,6 +303,10 @@ int dn_decode_tokens(int kda, const void* q, const void* k, const void* v,
  *   q, k        [B,Hk,T,dk] (dtype) out;  v [B,Hv,T,dv] (dtype) out
  *   beta        [B,Hv,T] (dtype) out;     g [B,Hv,T] (dtype) out, or NULL for a
  *               layer without decay (DeltaNet): then a, A_log, dt_bias unused
+ *   allow_neg_eigval  nonzero: beta = 2 sigmoid(b) in (0, 2), so the transition
+ *               I - beta k k^T may have the negative eigenvalue 1 - beta along k
+ *               (page "DeltaNet: Memory That Edits", section "The reflection
+ *               hiding in the delta rule"); the rule's kernels never clamp beta
  * Arithmetic is fp32 from the stored inputs, rounded once to dtype at each
  * output. A norm below 1e-12 divides by 1e-12. dk == dv in {64, 128}
  * (DN_ENOTSUP otherwise); Hk, Hv >= 1 with Hv a multiple of Hk, B <= 65535 and
@@ -314,7 +318,8 @@ int dn_decode_tokens(int kda, const void* q, const void* k, const void* v,
 int dn_layer_prologue(const void* qkv, const void* conv_w, const void* conv_state,
                       void* conv_state_out, const void* b, const void* a, const float* A_log,
                       const float* dt_bias, void* q, void* k, void* v, void* beta, void* g,
-                      int B, int T, int Hk, int Hv, int dk, int dv, int dtype, void* stream);
+                      int allow_neg_eigval, int B, int T, int Hk, int Hv, int dk, int dv,
+                      int dtype, void* stream);
 
 /*
  * The gated layer's work after the rule (same page and section, step 7):
@@ -332,6 +337,28 @@ int dn_layer_prologue(const void* qkv, const void* conv_w, const void* conv_stat
  */
 int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* out, int B, int Hv,
                       int T, int dv, float eps, int dtype, void* stream);
+
+/*
+ * Selective state-space recurrence (decayed linear attention, the form behind
+ * RetNet, GLA and Mamba-2): S_t = alpha_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t,
+ * alpha_t = exp(g_t) with one log-decay per head and token. This is Gated
+ * DeltaNet with the correction term removed (page "28. Linear attention and
+ * Gated DeltaNet", sections "Forget: decay" and "Stretch exercises", item 4),
+ * and it runs on the same chunk machinery with the UT solve reduced to the
+ * identity. There is no beta. Arguments as for dn_chunk_fwd / dn_recurrent_fwd
+ * / dn_decode_step without beta, and g is REQUIRED (pass zeros for plain
+ * causal linear attention). The chunked form uses dn_chunk_fwd_workspace()
+ * bytes and is not provided for fp32 at d = 128 (DN_ENOTSUP; the recurrent
+ * form covers it). Each returns DN_EINVAL when g is NULL.
+ */
+int dn_ssm_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
+                     const float* S0, void* o, float* S_final, int B, int H, int T, int dk, int dv,
+                     int dtype, void* workspace, size_t workspace_bytes, void* stream);
+int dn_ssm_recurrent_fwd(const void* q, const void* k, const void* v, const void* g,
+                         const float* S0, void* o, float* S_final, int B, int H, int T, int dk,
+                         int dv, int dtype, void* stream);
+int dn_ssm_decode_step(const void* q, const void* k, const void* v, const void* g, float* S,
+                       void* o, int B, int H, int dk, int dv, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 20, names
+    assert len(names) == 23, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -298,12 +298,12 @@ def test_phase_validation():
 
 def _prologue(**kw):
     args = dict(qkv=P, conv_w=P, conv_state=P, conv_state_out=P, b=P, a=P, A_log=P, dt_bias=P,
-                q=P, k=P, v=P, beta=P, g=P, B=1, T=64, Hk=1, Hv=2, dk=64, dv=64, dtype=1,
+                q=P, k=P, v=P, beta=P, g=P, neg=0, B=1, T=64, Hk=1, Hv=2, dk=64, dv=64, dtype=1,
                 stream=None)
     args.update(kw)
     return _lib.lib().dn_layer_prologue(*[args[n] for n in (
         "qkv", "conv_w", "conv_state", "conv_state_out", "b", "a", "A_log", "dt_bias", "q", "k",
-        "v", "beta", "g", "B", "T", "Hk", "Hv", "dk", "dv", "dtype", "stream")])
+        "v", "beta", "g", "neg", "B", "T", "Hk", "Hv", "dk", "dv", "dtype", "stream")])
 
 
 def test_layer_prologue_validation():
@@ -350,3 +350,35 @@ def test_layer_epilogue_validation():
     assert _epilogue(eps=float("inf")) == E
     assert _epilogue(dtype=7) == E
     assert _epilogue(dv=96) == N
+
+
+def _ssm(fn, **kw):
+    args = dict(q=P, k=P, v=P, g=P, S0=P, o=P, S_final=P, S=P, B=1, H=1, T=64, dk=64, dv=64,
+                dtype=1, ws=WS, wsb=1 << 30, stream=None)
+    args.update(kw)
+    names = {"dn_ssm_chunk_fwd": ("q", "k", "v", "g", "S0", "o", "S_final", "B", "H", "T", "dk",
+                                  "dv", "dtype", "ws", "wsb", "stream"),
+             "dn_ssm_recurrent_fwd": ("q", "k", "v", "g", "S0", "o", "S_final", "B", "H", "T",
+                                      "dk", "dv", "dtype", "stream"),
+             "dn_ssm_decode_step": ("q", "k", "v", "g", "S", "o", "B", "H", "dk", "dv", "dtype",
+                                    "stream")}[fn]
+    return getattr(_lib.lib(), fn)(*[args[n] for n in names])
+
+
+@pytest.mark.parametrize("fn", ["dn_ssm_chunk_fwd", "dn_ssm_recurrent_fwd", "dn_ssm_decode_step"])
+def test_ssm_validation(fn):
+    E, N = _lib.DN_EINVAL, _lib.DN_ENOTSUP
+    assert _ssm(fn, g=None) == E          # the decay is required
+    assert _ssm(fn, q=None) == E
+    assert _ssm(fn, o=None) == E
+    assert _ssm(fn, B=0) == E
+    assert _ssm(fn, v=MIS) == E
+    assert _ssm(fn, g=ODD) == E
+    assert _ssm(fn, dk=96, dv=96) == N
+    assert _ssm(fn, dtype=3) == E
+    if fn == "dn_ssm_chunk_fwd":
+        assert _ssm(fn, dtype=0, dk=128, dv=128) == N   # fp32 at d = 128: recurrent form only
+        assert _ssm(fn, ws=None) == _lib.DN_EWORKSPACE
+        assert _ssm(fn, wsb=16) == _lib.DN_EWORKSPACE
+    if fn == "dn_ssm_decode_step":
+        assert _ssm(fn, S=None) == E

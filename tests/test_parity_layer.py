@@ -35,11 +35,12 @@ def _dn():
     return dn
 
 
-def _prologue_ref(x):
+def _prologue_ref(x, neg=False):
     return ol.prologue(x["qkv"], x["conv_w"], x["conv_state"], x["b"], x["a"] if x["a"] is not None
                        else torch.zeros_like(x["b"]), x["A_log"] if x["A_log"] is not None
                        else torch.zeros(x["Hv"]), x["dt_bias"] if x["dt_bias"] is not None
-                       else torch.zeros(x["Hv"]), x["Hk"], x["Hv"], x["d"], x["d"])
+                       else torch.zeros(x["Hv"]), x["Hk"], x["Hv"], x["d"], x["d"],
+                       allow_neg_eigval=neg)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
@@ -49,6 +50,7 @@ def test_prologue_matches_oracle(dtype, d, T):
     dn = _dn()
     with_state = T % 2 == 1
     gated = T != 64
+    neg = T in (1, 5, 517)   # beta = 2 sigmoid(b): the reflection range
     Hk, Hv = (1, 2) if d == 128 else (2, 4)
     say("prologue", dtype, d, T, "state" if with_state else "zeros", "gated" if gated else "ungated")
     x = synthetic.make_layer(2, T, Hk, Hv, d, dtype, seed=T * 3 + d, conv_state=with_state,
@@ -56,9 +58,9 @@ def test_prologue_matches_oracle(dtype, d, T):
     dx = to_dev(x)
     q, k, v, beta, g, cst = dn.layer_prologue(dx["qkv"], dx["conv_w"], dx["b"], dx["a"],
                                               dx["A_log"], dx["dt_bias"], Hk, Hv,
-                                              conv_state=dx["conv_state"])
+                                              conv_state=dx["conv_state"], allow_neg_eigval=neg)
     torch.cuda.synchronize()
-    rq, rk, rv, rbeta, rg, rst = _prologue_ref(x)
+    rq, rk, rv, rbeta, rg, rst = _prologue_ref(x, neg)
     tol = TOL[dtype]
     for name, gpu, ref in (("q", q, rq), ("k", k, rk), ("v", v, rv), ("beta", beta, rbeta)):
         e = rel_err(gpu, ref)
