@@ -67,14 +67,14 @@ CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurren
 DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
                   "delta_rule_recurrent_amd/csrc/dn_launch.h")
 TRAFFIC = {
-    "chunk_prep2_kernel": {"fetch_kib": 29314.0, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
-                           "sha256": "6ce13b672766e99499ffba45d9c5b3ce06b2cd59cc18b5cdbec6ba979c506766"},
-    "chunk_scan_kernel": {"fetch_kib": 37102.6, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
-                          "sha256": "6ce13b672766e99499ffba45d9c5b3ce06b2cd59cc18b5cdbec6ba979c506766"},
-    "chunk_fused_kernel": {"fetch_kib": 62003.6, "write_kib": 76633.9, "sources": CHUNK_SOURCES,
-                           "sha256": "6ce13b672766e99499ffba45d9c5b3ce06b2cd59cc18b5cdbec6ba979c506766"},
-    "decode_step_kernel": {"fetch_kib": 136303.3, "write_kib": 263168.0, "sources": DECODE_SOURCES,
-                           "sha256": "df77ffcdf975415024e5a004bcb73c1a8db75523e965b8ea31d47ccd73b8d2f0"},
+    "chunk_prep2_kernel": {"fetch_kib": 28801.4, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
+                           "sha256": "af53d26046e5e8fff2029345e3613e7351f084349518391f92a9d9ba812f408b"},
+    "chunk_scan_kernel": {"fetch_kib": 37107.1, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
+                          "sha256": "af53d26046e5e8fff2029345e3613e7351f084349518391f92a9d9ba812f408b"},
+    "chunk_fused_kernel": {"fetch_kib": 62001.0, "write_kib": 76660.3, "sources": CHUNK_SOURCES,
+                           "sha256": "af53d26046e5e8fff2029345e3613e7351f084349518391f92a9d9ba812f408b"},
+    "decode_step_kernel": {"fetch_kib": 136310.2, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+                           "sha256": "173b2dff07f3bce9abcbc61a2891e5c7866065d1acb681d60a8e35a29c762992"},
 }
 
 
@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the headline prefill (for profiling the other kernels alone)")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="only time the gated layer's prologue / epilogue kernels (for profiling them)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (three times) and exit: "
                          "the reference kernel for scaling memory-traffic counters")
@@ -156,6 +158,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n * 4, "copies": 3}), flush=True)
+        return
+
+    if args.layer_only:
+        print(json.dumps({"layer": run_layer(torch, dn, synthetic, to_dev, dev)}), flush=True)
         return
 
     # ------------------------------------------------------------------ prefill
@@ -398,7 +404,9 @@ def run_serving(torch, dn, synthetic, to_dev, dev):
       * chunk_fwd_varlen: 8 heads over 8 sequences of 8192 tokens in all, with
         lengths 63 .. 3008 (the same 65536 token-heads as the headline);
     and decode_tokens (4 drafted tokens per sequence with a state snapshot after
-    each) at the decode workload's 256 x 16 states."""
+    each) at the decode workload's 256 x 16 states; and the selective
+    state-space kind (ssm_chunk_fwd at the headline size, ssm_decode_step at
+    256 x 16 states)."""
     out = {}
     c = synthetic.CONFIGS["gdn_prefill_b4_h8_t2048_d128"]
     B, H, T, d = c["B"], c["H"], c["T"], c["dk"]
@@ -442,6 +450,9 @@ def run_serving(torch, dn, synthetic, to_dev, dev):
                                                           xp["g"], cu, None, o=op, S_final=Sp,
                                                           workspace=wsp),
           {"sequence_lengths": lens, "heads": H})
+    # the selective state-space kind (no beta, no correction) on the same inputs
+    timed("ssm_chunk_fwd", lambda: dn.ssm_chunk_fwd(x["q"], x["k"], x["v"], x["g"], None, o=o,
+                                                    S_final=S, workspace=ws))
     del x, ws, o, S, Sc, qg, kg, xp, wsp, op, Sp
     # speculative decode: 4 drafted tokens for the decode workload's 256 x 16
     # states, the state after each kept (4 x 256 MiB of snapshots)
@@ -461,7 +472,16 @@ def run_serving(torch, dn, synthetic, to_dev, dev):
                             "state_bytes_moved": moved,
                             "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
     log("  serving decode_tokens %.4f ms" % ms)
-    del xd, Sd, od, snap
+    od1 = torch.empty(Bd, Hd, d, dtype=torch.bfloat16, device=dev)
+    q1, k1, v1, g1 = (xd[n][:, :, 0].contiguous() for n in ("q", "k", "v", "g"))
+    run = lambda: dn.ssm_decode_step(q1, k1, v1, g1, Sd, o=od1)
+    for _ in range(2):
+        run()
+    ms = event_time_ms(torch, run, 20)
+    out["ssm_decode_step"] = {"ms": round(ms, 4), "B": Bd, "H": Hd, "state_bytes_moved": 2 * state,
+                              "gbs": round(2 * state / (ms * 1e-3) / 1e9, 1)}
+    log("  serving ssm_decode_step %.4f ms" % ms)
+    del xd, Sd, od, snap, od1
     return out
 
 
