@@ -910,20 +910,24 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
 
         // ---- 4. W = T diag(beta e^G) K: W^T tiles (rows = key channels) for each
         //         token tile, stacked over channel tiles = A-fragments of W
+        //         (the state-space kind has W = 0, which its scan does not read:
+        //         not written)
+        if constexpr (KIND != KIND_SSM) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-            F tf[2];
+            for (int tt = 0; tt < 4; ++tt) {
+                F tf[2];
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) tf[kt] = frag_rows<E>(Tw, LDT, 16 * tt, 32 * kt, lane);
-            f32x4 wt[CT];
+                for (int kt = 0; kt < 2; ++kt) tf[kt] = frag_rows<E>(Tw, LDT, 16 * tt, 32 * kt, lane);
+                f32x4 wt[CT];
 #pragma unroll
-            for (int mt = 0; mt < CT; ++mt) {
-                wt[mt] = zero4();
+                for (int mt = 0; mt < CT; ++mt) {
+                    wt[mt] = zero4();
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) wt[mt] = mma(xf[mt][kt], tf[kt], wt[mt]);
+                    for (int kt = 0; kt < 2; ++kt) wt[mt] = mma(xf[mt][kt], tf[kt], wt[mt]);
+                }
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) Wf[(tt * KB + kb) * 64 + lane] = frag_from_tiles<E>(wt[2 * kb], wt[2 * kb + 1]);
             }
-#pragma unroll
-            for (int kb = 0; kb < KB; ++kb) Wf[(tt * KB + kb) * 64 + lane] = frag_from_tiles<E>(wt[2 * kb], wt[2 * kb + 1]);
         }
         return;
     }
@@ -1070,9 +1074,12 @@ __device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV, KIND>& x, 
     constexpr int ES = (int)sizeof(E);
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(src.blk, (unsigned)Lw::BYTES);
     if (PART == 0) {
+        // (the state-space kind has no W: its prep does not write it)
+        if (KIND != KIND_SSM) {
 #pragma unroll
-        for (int kb = 0; kb < O::KB; ++kb)
-            x.w[kb] = buf_load<F>(rb, (int)(Lw::W_OFF * ES) + ((w * O::KB + kb) * 64 + lane) * FB);
+            for (int kb = 0; kb < O::KB; ++kb)
+                x.w[kb] = buf_load<F>(rb, (int)(Lw::W_OFF * ES) + ((w * O::KB + kb) * 64 + lane) * FB);
+        }
     } else if (PART == 1) {
         if (KIND == KIND_KDA) {
 #pragma unroll
@@ -1199,7 +1206,8 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cu
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const F sb = Sx[kb][nt][lane];
-            U[nt] = mma(cur.w[kb], sb, U[nt]);
+            // state-space kind: W = 0, so U = u without the product (bitwise the same)
+            if constexpr (KIND != KIND_SSM) U[nt] = mma(cur.w[kb], sb, U[nt]);
             O[nt] = mma(qf[kb], sb, O[nt]);
         }
         // Gated / DeltaNet: (e^G Q) S = e^G (Q S), per token row
@@ -1821,8 +1829,13 @@ template <typename E, int D>
 static hipError_t scan_kind(int kind, const void* q, const float* S0, void* o, float* S_final,
                             const void* ws, int BH, int T, hipStream_t st, HeadMap hm,
                             float* S_bound = nullptr) {
-    // DeltaNet and Gated DeltaNet share the scan (a unit decay is stored for DeltaNet)
+    // DeltaNet and Gated DeltaNet share the scan (a unit decay is stored for
+    // DeltaNet); the state-space kind drops its W S product
     if (kind == KIND_KDA) return scan_t<E, D, KIND_KDA>(q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
+    if (kind == KIND_SSM) {
+        if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
+        else return scan_t<E, D, KIND_SSM>(q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
+    }
     return scan_t<E, D, KIND_GATED>(q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
 }
 
