@@ -406,7 +406,7 @@ def run_serving(torch, dn, synthetic, to_dev, dev):
     and decode_tokens (4 drafted tokens per sequence with a state snapshot after
     each) at the decode workload's 256 x 16 states; and the selective
     state-space kind (ssm_chunk_fwd at the headline size, ssm_decode_step at
-    256 x 16 states)."""
+    256 x 16 states) and the generalized delta rule's decode step (256 x 16)."""
     out = {}
     c = synthetic.CONFIGS["gdn_prefill_b4_h8_t2048_d128"]
     B, H, T, d = c["B"], c["H"], c["T"], c["dk"]
@@ -481,7 +481,17 @@ def run_serving(torch, dn, synthetic, to_dev, dev):
     out["ssm_decode_step"] = {"ms": round(ms, 4), "B": Bd, "H": Hd, "state_bytes_moved": 2 * state,
                               "gbs": round(2 * state / (ms * 1e-3) / 1e9, 1)}
     log("  serving ssm_decode_step %.4f ms" % ms)
-    del xd, Sd, od, snap, od1
+    # generalized delta rule, one token for the same 256 x 16 states
+    xg = to_dev(synthetic.make_gdr(Bd, Hd, 1, d, "bf16", seed=2004))
+    gin = [xg[n][:, :, 0].contiguous() for n in ("q", "kw", "v", "kr", "a", "g")]
+    run = lambda: dn.gdr_decode_step(*gin, Sd, o=od1)
+    for _ in range(2):
+        run()
+    ms = event_time_ms(torch, run, 20)
+    out["gdr_decode_step"] = {"ms": round(ms, 4), "B": Bd, "H": Hd, "state_bytes_moved": 2 * state,
+                              "gbs": round(2 * state / (ms * 1e-3) / 1e9, 1)}
+    log("  serving gdr_decode_step %.4f ms" % ms)
+    del xd, Sd, od, snap, od1, xg, gin
     return out
 
 

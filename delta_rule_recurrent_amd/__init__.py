@@ -22,7 +22,7 @@ from ._lib import DeltaNetError, lib
 __all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_fwd_gqa",
            "decode_step_gqa", "chunk_fwd_varlen", "decode_tokens", "layer_prologue",
            "layer_epilogue", "gated_deltanet_layer", "ssm_chunk_fwd", "ssm_recurrent_fwd",
-           "ssm_decode_step", "chunk_prep", "chunk_scan",
+           "ssm_decode_step", "gdr_recurrent_fwd", "gdr_decode_step", "chunk_prep", "chunk_scan",
            "recurrent_fwd",
            "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
            "DeltaNetError", "lib", "library_path"]
@@ -496,6 +496,63 @@ def ssm_decode_step(q, k, v, g, S, *, o=None, stream=None):
     st = lib().dn_ssm_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(S), _ptr(o), B, H, dk,
                                   dv, _DT[dt], _stream(stream))
     _lib.check("dn_ssm_decode_step", st)
+    return o
+
+
+def gdr_recurrent_fwd(q, kw, v, kr, a, g, S0=None, *, output_final_state=True, o=None,
+                      S_final=None, stream=None):
+    """Generalized delta rule, token by token:
+    S = (diag(exp g) - (a * kr) kr^T) S + kw v^T, o = S^T q.
+    q, kw (write key), kr (removal key), a (removal rate), g (log-decay)
+    [B,H,T,dk]; v [B,H,T,dv]; S0 [B,H,dk,dv] fp32 or None. Returns (o, S_final)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,T,dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    for name, t in (("kw", kw), ("kr", kr), ("a", a), ("g", g)):
+        _check_tensor(name, t, (B, H, T, dk), dt, dev)
+    _check_tensor("v", v, (B, H, T, dv), dt, dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, T, dv), dt, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    elif S_final is not None:
+        _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
+    st = lib().dn_gdr_recurrent_fwd(_ptr(q), _ptr(kw), _ptr(v), _ptr(kr), _ptr(a), _ptr(g),
+                                    _ptr(S0), _ptr(o), _ptr(S_final), B, H, T, dk, dv, _DT[dt],
+                                    _stream(stream))
+    _lib.check("dn_gdr_recurrent_fwd", st)
+    return o, S_final
+
+
+def gdr_decode_step(q, kw, v, kr, a, g, S, *, o=None, stream=None):
+    """One token of the generalized delta rule: q, kw, kr, a, g [B,H,dk];
+    v [B,H,dv]; S [B,H,dk,dv] fp32 updated in place. Returns o [B,H,dv]."""
+    if q.dim() != 3:
+        raise ValueError("q must be [B,H,dk]")
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    for name, t in (("kw", kw), ("kr", kr), ("a", a), ("g", g)):
+        _check_tensor(name, t, (B, H, dk), dt, dev)
+    _check_tensor("v", v, (B, H, dv), dt, dev)
+    _check_tensor("S", S, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, H, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, dv), dt, dev)
+    st = lib().dn_gdr_decode_step(_ptr(q), _ptr(kw), _ptr(v), _ptr(kr), _ptr(a), _ptr(g), _ptr(S),
+                                  _ptr(o), B, H, dk, dv, _DT[dt], _stream(stream))
+    _lib.check("dn_gdr_decode_step", st)
     return o
 
 

@@ -318,6 +318,48 @@ int dn_ssm_decode_step(const void* q, const void* k, const void* v, const void* 
     return decode_common(dn::KIND_SSM, q, k, v, g, g, S, o, B, H, dk, dv, dtype, stream);
 }
 
+// The generalized rule reads every tensor element by element: element
+// alignment for the activations, 4 bytes for the states.
+static int gdr_check(const void* q, const void* kw, const void* v, const void* kr, const void* a,
+                     const void* g, const void* S0, const void* o, const void* S_final, int B,
+                     int H, int T, int dk, int dv, int dtype) {
+    if (B < 1 || H < 1 || T < 0) return DN_EINVAL;
+    if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+    if (T > 0 && (!q || !kw || !v || !kr || !a || !g || !o)) return DN_EINVAL;
+    const unsigned esz = dtype == DN_F32 ? 4u : 2u;
+    if (misaligned(q, esz) || misaligned(kw, esz) || misaligned(v, esz) || misaligned(kr, esz) ||
+        misaligned(a, esz) || misaligned(g, esz) || misaligned(o, esz) || misaligned(S0, 4) ||
+        misaligned(S_final, 4))
+        return DN_EINVAL;
+    if ((dk != 64 && dk != 128) || dk != dv) return DN_ENOTSUP;
+    if ((long long)B * H * (dk / 64) > 0x7fffffffLL) return DN_EINVAL;
+    return DN_OK;
+}
+
+int dn_gdr_recurrent_fwd(const void* q, const void* kw, const void* v, const void* kr,
+                         const void* a, const void* g, const float* S0, void* o, float* S_final,
+                         int B, int H, int T, int dk, int dv, int dtype, void* stream) {
+    const int st = gdr_check(q, kw, v, kr, a, g, S0, o, S_final, B, H, T, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    const long long BH = (long long)B * H;
+    if (T == 0) {
+        if (!S_final) return DN_OK;
+        return hip_status(dn::launch_state_copy(S0, S_final, BH * dk * dv, as_stream(stream)));
+    }
+    return hip_status(dn::launch_gdr_recurrent(dtype, q, kw, v, kr, a, g, S0, o, S_final, (int)BH,
+                                               T, dk, as_stream(stream)));
+}
+
+int dn_gdr_decode_step(const void* q, const void* kw, const void* v, const void* kr,
+                       const void* a, const void* g, float* S, void* o, int B, int H, int dk,
+                       int dv, int dtype, void* stream) {
+    if (!S) return DN_EINVAL;
+    const int st = gdr_check(q, kw, v, kr, a, g, S, o, S, B, H, 1, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    return hip_status(dn::launch_gdr_recurrent(dtype, q, kw, v, kr, a, g, S, o, S, B * H, 1, dk,
+                                               as_stream(stream)));
+}
+
 int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const void* beta,
                   const void* g, int B, int H, int T, int dk, int dv, int dtype, void* workspace,
                   size_t workspace_bytes, void* stream) {

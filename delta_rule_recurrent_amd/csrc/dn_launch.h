@@ -99,6 +99,13 @@ hipError_t launch_layer_epilogue(int dtype, const void* o, const void* z, const 
                                  void* out, int B, int Hv, int T, int d, float eps,
                                  hipStream_t st);
 
+// Generalized delta rule, token by token: S = (diag(exp g) - (a * kr) kr^T) S
+// + kw v^T, o = S^T q; q, kw, kr, a, g [BH][T][d], v, o [BH][T][d]. S0 and
+// S_final may be the same buffer (the decode step is T = 1 in place).
+hipError_t launch_gdr_recurrent(int dtype, const void* q, const void* kw, const void* v,
+                                const void* kr, const void* a, const void* g, const float* S0,
+                                void* o, float* S_final, int BH, int T, int d, hipStream_t st);
+
 // S_final = S0 (or zeros when S0 == NULL), n floats; used when T == 0.
 hipError_t launch_state_copy(const float* S0, float* S_final, long long n, hipStream_t stream);
 

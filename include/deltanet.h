@@ -360,6 +360,33 @@ int dn_ssm_recurrent_fwd(const void* q, const void* k, const void* v, const void
 int dn_ssm_decode_step(const void* q, const void* k, const void* v, const void* g, float* S,
                        void* o, int B, int H, int dk, int dv, int dtype, void* stream);
 
+/*
+ * The generalized delta rule (page "DeltaNet: Memory That Edits", section "The
+ * generalized delta rule"): the roles the delta rule ties together are
+ * separated,
+ *     S_t = (diag(w_t) - (a_t * kr_t) kr_t^T) S_{t-1} + kw_t v_t^T,  o_t = S_t^T q_t,
+ * with w_t = exp(g_t) a per-key-channel decay, kr_t the removal key, kw_t the
+ * write key and a_t a per-key-channel removal rate: a diagonal-plus-low-rank
+ * key-space transition (page "A walk through of the DeltaNet family of linear
+ * attention variants"). kr = k, kw = beta k, a = beta, g = 0 is DeltaNet; the
+ * removal term uses the state before the decay, as the transition is written.
+ * Token by token (one wavefront per head and 64 value columns); the chunked
+ * form is not provided.
+ *   q, kw, kr, a, g  [B,H,T,dk] (dtype);  v, o  [B,H,T,dv] (dtype)
+ *   S0, S_final      [B,H,dk,dv] fp32 (S0 NULL => zeros; S_final NULL => not
+ *                    written; S_final == S0 allowed)
+ * dn_gdr_decode_step is one token ([B,H,dk] / [B,H,dv] inputs) with S updated
+ * in place. dk == dv in {64, 128}. Every tensor is read element by element:
+ * the activations need the alignment of their element type, the states 4
+ * bytes. Errors as for dn_recurrent_fwd.
+ */
+int dn_gdr_recurrent_fwd(const void* q, const void* kw, const void* v, const void* kr,
+                         const void* a, const void* g, const float* S0, void* o, float* S_final,
+                         int B, int H, int T, int dk, int dv, int dtype, void* stream);
+int dn_gdr_decode_step(const void* q, const void* kw, const void* v, const void* kr,
+                       const void* a, const void* g, float* S, void* o, int B, int H, int dk,
+                       int dv, int dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

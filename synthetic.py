@@ -132,6 +132,33 @@ def make_layer(B: int, T: int, Hk: int, Hv: int, d: int, dtype: str = "bf16", se
                 norm_w=norm_w.to(dt).contiguous(), B=B, T=T, Hk=Hk, Hv=Hv, d=d, dtype=dtype)
 
 
+def make_gdr(B: int, H: int, T: int, d: int, dtype: str = "bf16", seed: int = 0,
+             s0_std: float | None = None) -> dict:
+    """Draw inputs of the generalized delta rule (separate removal and write
+    keys, per-channel removal rate and decay; page "DeltaNet: Memory That
+    Edits", section "The generalized delta rule"), in this order from one
+    generator: q, write key, removal key, v ~ N(0,1); write-strength logits,
+    rate logits, decay logits ~ N(0,1); then S0 ~ N(0, s0_std^2). q and both
+    keys are L2-normalised (q also scaled by d^-1/2); the write key is scaled
+    by sigmoid of its logit (one per token), the rate a = sigmoid(logit) per
+    channel, g = -softplus(logit) per channel. Rounded once to the dtype."""
+    gen = torch.Generator().manual_seed(int(seed))
+    q = torch.randn(B, H, T, d, generator=gen)
+    kw = torch.randn(B, H, T, d, generator=gen)
+    kr = torch.randn(B, H, T, d, generator=gen)
+    v = torch.randn(B, H, T, d, generator=gen)
+    bw = torch.randn(B, H, T, generator=gen)
+    ar = torch.randn(B, H, T, d, generator=gen)
+    gl = torch.randn(B, H, T, d, generator=gen)
+    S0 = None if s0_std is None else torch.randn(B, H, d, d, generator=gen) * float(s0_std)
+    dt = DTYPES[dtype]
+    out = dict(q=_unit(q) * d ** -0.5, kw=_unit(kw) * torch.sigmoid(bw)[..., None], kr=_unit(kr),
+               v=v, a=torch.sigmoid(ar), g=-torch.nn.functional.softplus(gl))
+    out = {k: t.to(dt).contiguous() for k, t in out.items()}
+    out["S0"] = None if S0 is None else S0.float().contiguous()
+    return out
+
+
 def make_config(name: str, **overrides) -> dict:
     """Inputs of a named workload; keyword overrides (T, B, steps, ...) shrink it."""
     cfg = dict(CONFIGS[name])
@@ -148,4 +175,4 @@ def describe(name: str) -> str:
     return ", ".join("%s=%s" % (k, c[k]) for k in ("kind", "B", "H", "T", "dk", "dv", "dtype"))
 
 
-__all__ = ["CONFIGS", "make", "make_layer", "make_config", "nbytes", "describe"]
+__all__ = ["CONFIGS", "make", "make_layer", "make_gdr", "make_config", "nbytes", "describe"]

@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 25, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -382,3 +382,32 @@ def test_ssm_validation(fn):
         assert _ssm(fn, wsb=16) == _lib.DN_EWORKSPACE
     if fn == "dn_ssm_decode_step":
         assert _ssm(fn, S=None) == E
+
+
+def _gdr(fn, **kw):
+    args = dict(q=P, kw=P, v=P, kr=P, a=P, g=P, S0=P, o=P, S_final=P, S=P, B=1, H=1, T=64, dk=64,
+                dv=64, dtype=1, stream=None)
+    args.update(kw)
+    names = {"dn_gdr_recurrent_fwd": ("q", "kw", "v", "kr", "a", "g", "S0", "o", "S_final", "B",
+                                      "H", "T", "dk", "dv", "dtype", "stream"),
+             "dn_gdr_decode_step": ("q", "kw", "v", "kr", "a", "g", "S", "o", "B", "H", "dk", "dv",
+                                    "dtype", "stream")}[fn]
+    return getattr(_lib.lib(), fn)(*[args[n] for n in names])
+
+
+@pytest.mark.parametrize("fn", ["dn_gdr_recurrent_fwd", "dn_gdr_decode_step"])
+def test_gdr_validation(fn):
+    E, N = _lib.DN_EINVAL, _lib.DN_ENOTSUP
+    for name in ("q", "kw", "v", "kr", "a", "g", "o"):
+        assert _gdr(fn, **{name: None}) == E, name
+    assert _gdr(fn, kr=ODD) == E
+    assert _gdr(fn, B=0) == E
+    assert _gdr(fn, dtype=2) == E
+    assert _gdr(fn, dk=96, dv=96) == N
+    assert _gdr(fn, dk=64, dv=128) == N
+    if fn == "dn_gdr_decode_step":
+        assert _gdr(fn, S=None) == E
+        assert _gdr(fn, S=P + 2) == E
+    else:
+        assert _gdr(fn, T=-1) == E
+        assert _gdr(fn, S0=P + 2) == E

@@ -1,0 +1,81 @@
+"""GPU generalized delta rule (through the C ABI) versus its fp64 oracle.
+
+S_t = (diag(exp g_t) - (a_t * kr_t) kr_t^T) S_{t-1} + kw_t v_t^T, o_t = S_t^T q_t
+(oracle/gdr.py), token by token and as single-token decode steps, on seeded
+inputs (``synthetic.make_gdr``) with T in {1, 5, 64, 130}, both head sizes,
+both dtypes and a non-zero start state; the tie to DeltaNet against the GPU
+DeltaNet recurrence; the in-place state update. Bound: max|gpu - ref| /
+max|ref| <= 1e-4 (fp32), 2e-2 (bf16).
+"""
+import pytest
+import torch
+
+import synthetic
+from gpu_util import TOL, rel_err, say, to_dev
+from oracle import gdr as ogdr
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import delta_rule_recurrent_amd as dn  # noqa: F401  (loads libdeltanet.so)
+
+
+def _dn():
+    import delta_rule_recurrent_amd as dn
+    return dn
+
+
+NAMES = ("q", "kw", "v", "kr", "a", "g")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("T", [1, 5, 64, 130])
+def test_gdr_matches_oracle(dtype, d, T):
+    dn = _dn()
+    say("gdr", dtype, d, T)
+    x = synthetic.make_gdr(2, 3, T, d, dtype, seed=700 + T + d, s0_std=0.5)
+    dx = to_dev(x)
+    o, S = dn.gdr_recurrent_fwd(*(dx[n] for n in NAMES), dx["S0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = ogdr.recurrent(*(x[n] for n in NAMES), x["S0"])
+    eo, eS = rel_err(o, o_ref), rel_err(S, S_ref)
+    say("  o err %.3g, S err %.3g" % (eo, eS))
+    assert eo <= TOL[dtype] and eS <= TOL[dtype], (eo, eS)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_gdr_decode_steps_in_place(dtype, d):
+    """Four single-token steps on one state buffer, against the oracle over
+    the four tokens."""
+    dn = _dn()
+    say("gdr decode", dtype, d)
+    x = synthetic.make_gdr(3, 2, 4, d, dtype, seed=760 + d, s0_std=0.5)
+    dx = to_dev(x)
+    S = dx["S0"].clone()
+    outs = [dn.gdr_decode_step(*(dx[n][:, :, t].contiguous() for n in NAMES), S) for t in range(4)]
+    torch.cuda.synchronize()
+    o_ref, S_ref = ogdr.recurrent(*(x[n] for n in NAMES), x["S0"])
+    assert rel_err(torch.stack(outs, dim=2), o_ref) <= TOL[dtype]
+    assert rel_err(S, S_ref) <= TOL[dtype]
+
+
+def test_gdr_tied_equals_deltanet_on_gpu():
+    """kr = k, kw = beta k, a = beta, g = 0 is DeltaNet: the two GPU paths agree
+    to fp32 rounding (fp32 inputs)."""
+    dn = _dn()
+    inp = synthetic.make("deltanet", 2, 2, 90, 64, 64, dtype="f32", seed=81, s0_std=0.5)
+    d = to_dev(inp)
+    k, beta = d["k"], d["beta"]
+    o1, S1 = dn.gdr_recurrent_fwd(d["q"], (beta[..., None] * k).contiguous(), d["v"], k,
+                                  (beta[..., None] * torch.ones_like(k)).contiguous(),
+                                  torch.zeros_like(k), d["S0"])
+    o2, S2 = dn.recurrent_fwd(d["q"], k, d["v"], beta, None, d["S0"])
+    torch.cuda.synchronize()
+    assert rel_err(o1, o2.double().cpu().numpy()) <= 1e-5
+    assert rel_err(S1, S2.double().cpu().numpy()) <= 1e-5
