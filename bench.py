@@ -67,14 +67,14 @@ CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurren
 DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
                   "delta_rule_recurrent_amd/csrc/dn_launch.h")
 TRAFFIC = {
-    "chunk_prep2_kernel": {"fetch_kib": 28801.4, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
-                           "sha256": "af53d26046e5e8fff2029345e3613e7351f084349518391f92a9d9ba812f408b"},
-    "chunk_scan_kernel": {"fetch_kib": 37107.1, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
-                          "sha256": "af53d26046e5e8fff2029345e3613e7351f084349518391f92a9d9ba812f408b"},
-    "chunk_fused_kernel": {"fetch_kib": 62001.0, "write_kib": 76660.3, "sources": CHUNK_SOURCES,
-                           "sha256": "af53d26046e5e8fff2029345e3613e7351f084349518391f92a9d9ba812f408b"},
-    "decode_step_kernel": {"fetch_kib": 136310.2, "write_kib": 263168.0, "sources": DECODE_SOURCES,
-                           "sha256": "173b2dff07f3bce9abcbc61a2891e5c7866065d1acb681d60a8e35a29c762992"},
+    "chunk_prep2_kernel": {"fetch_kib": 29262.9, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
+                           "sha256": "dd56f4f6f16f042dfbadb4b974e9db43abe5ffddd2a7ec2858fa12bd53c31ed5"},
+    "chunk_scan_kernel": {"fetch_kib": 37103.1, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
+                          "sha256": "dd56f4f6f16f042dfbadb4b974e9db43abe5ffddd2a7ec2858fa12bd53c31ed5"},
+    "chunk_fused_kernel": {"fetch_kib": 62018.5, "write_kib": 76652.9, "sources": CHUNK_SOURCES,
+                           "sha256": "dd56f4f6f16f042dfbadb4b974e9db43abe5ffddd2a7ec2858fa12bd53c31ed5"},
+    "decode_step_kernel": {"fetch_kib": 136309.6, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+                           "sha256": "74f4a1e0ef92f2aee9dbd9ed668d70f9e1ee2e41e77559b6eb24fa94dbbaac1a"},
 }
 
 
