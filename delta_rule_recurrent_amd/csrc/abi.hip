@@ -318,8 +318,8 @@ int dn_ssm_decode_step(const void* q, const void* k, const void* v, const void* 
     return decode_common(dn::KIND_SSM, q, k, v, g, g, S, o, B, H, dk, dv, dtype, stream);
 }
 
-// The generalized rule reads every tensor element by element: element
-// alignment for the activations, 4 bytes for the states.
+// The generalized rule's single-token kernel reads the states, v and o as
+// 16-byte vectors; the other per-token tensors are read element by element.
 static int gdr_check(const void* q, const void* kw, const void* v, const void* kr, const void* a,
                      const void* g, const void* S0, const void* o, const void* S_final, int B,
                      int H, int T, int dk, int dv, int dtype) {
@@ -327,9 +327,9 @@ static int gdr_check(const void* q, const void* kw, const void* v, const void* k
     if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
     if (T > 0 && (!q || !kw || !v || !kr || !a || !g || !o)) return DN_EINVAL;
     const unsigned esz = dtype == DN_F32 ? 4u : 2u;
-    if (misaligned(q, esz) || misaligned(kw, esz) || misaligned(v, esz) || misaligned(kr, esz) ||
-        misaligned(a, esz) || misaligned(g, esz) || misaligned(o, esz) || misaligned(S0, 4) ||
-        misaligned(S_final, 4))
+    if (misaligned(q, esz) || misaligned(kw, esz) || misaligned(v) || misaligned(kr, esz) ||
+        misaligned(a, esz) || misaligned(g, esz) || misaligned(o) || misaligned(S0) ||
+        misaligned(S_final))
         return DN_EINVAL;
     if ((dk != 64 && dk != 128) || dk != dv) return DN_ENOTSUP;
     if ((long long)B * H * (dk / 64) > 0x7fffffffLL) return DN_EINVAL;

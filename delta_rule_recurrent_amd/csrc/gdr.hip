@@ -12,7 +12,8 @@
 // update is local to the column: p_j = kr . S[:, j] (before the decay), then
 // S[:, j] = w * S[:, j] - (a * kr) p_j + kw v_j and o_j = q . S[:, j]. The
 // per-channel vectors of a token are spread over the lanes and broadcast with
-// readlane; the next four tokens' inputs are kept in flight.
+// readlane; the next four tokens' inputs are kept in flight. A single token
+// takes gdr_step_kernel below, which streams the state once.
 #include "dn_device.h"
 #include "dn_launch.h"
 
@@ -103,10 +104,123 @@ __global__ __launch_bounds__(WAVE) void gdr_recurrent_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// One token (decode). HBM-bound, so every state element is read once and
+// written once: NSPLIT 256-thread workgroups per (sequence, head), each over
+// DV/NSPLIT value columns; thread t owns a column quad on rows rg, rg + RG, ...
+// The read-out is formed from the old state,
+//     o = (q * w)^T S - (q . (a * kr)) p + (q . kw) v,   p = kr^T S,
+// so the column sums p and (q * w)^T S and the two scalars are reduced across
+// row groups (lane shuffles, then one LDS exchange) before the update is
+// written. S0 NULL reads zeros; S_final NULL writes nothing; S_final == S0 is
+// safe (each thread reads its elements before writing them).
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV, int NSPLIT>
+__global__ __launch_bounds__(256) void gdr_step_kernel(
+    const E* __restrict__ q, const E* __restrict__ kw, const E* __restrict__ v,
+    const E* __restrict__ kr, const E* __restrict__ a, const E* __restrict__ g, const float* S0,
+    E* __restrict__ o, float* S_final) {
+    constexpr int CW = DV / NSPLIT;   // value columns of this workgroup
+    constexpr int CQ = CW / 4;        // column quads per row
+    constexpr int RG = 256 / CQ;      // row groups
+    constexpr int RPT = DK / RG;      // rows per thread
+    static_assert(DK % RG == 0 && CQ <= WAVE, "unsupported head size");
+    typedef typename Vec4<E>::type V4;
+
+    const long bh = blockIdx.x / NSPLIT;
+    const int col0 = (int)(blockIdx.x % NSPLIT) * CW;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    const int cq = t % CQ, rg = t / CQ;
+    const long base = bh * DK * DV + col0 + 4 * cq;
+
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = S0 ? *reinterpret_cast<const f32x4*>(S0 + base + (rg + RG * i) * DV) : zero4();
+
+    __shared__ float skr[DK], sak[DK], sw[DK], skw[DK], sq[DK], sqw[DK];
+    __shared__ f32x4 red_p[4][CQ], red_r[4][CQ];
+    __shared__ float red_s[4][2];
+    if (t < DK) {
+        const long i = bh * DK + t;
+        const float r_ = to_f32(kr[i]), w_ = __expf(to_f32(g[i])), q_ = to_f32(q[i]);
+        skr[t] = r_;
+        sak[t] = to_f32(a[i]) * r_;
+        sw[t] = w_;
+        skw[t] = to_f32(kw[i]);
+        sq[t] = q_;
+        sqw[t] = q_ * w_;
+    }
+    const V4 vraw = *reinterpret_cast<const V4*>(v + bh * DV + col0 + 4 * cq);
+    __syncthreads();
+
+    f32x4 p = zero4(), r = zero4();
+    float qak = 0.f, qkw = 0.f;   // q . (a * kr) and q . kw over this thread's rows
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        p += skr[row] * s[i];
+        r += sqw[row] * s[i];
+        qak += sq[row] * sak[row];
+        qkw += sq[row] * skw[row];
+    }
+    // Row groups inside one wavefront differ in lane bits >= log2(CQ).
+#pragma unroll
+    for (int off = CQ; off < WAVE; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p[e] += __shfl_xor(p[e], off, WAVE);
+            r[e] += __shfl_xor(r[e], off, WAVE);
+        }
+        qak += __shfl_xor(qak, off, WAVE);
+        qkw += __shfl_xor(qkw, off, WAVE);
+    }
+    if (lane < CQ) {
+        red_p[w][lane] = p;
+        red_r[w][lane] = r;
+    }
+    if (lane == 0) {
+        red_s[w][0] = qak;
+        red_s[w][1] = qkw;
+    }
+    __syncthreads();
+    p = red_p[0][cq] + red_p[1][cq] + red_p[2][cq] + red_p[3][cq];
+    r = red_r[0][cq] + red_r[1][cq] + red_r[2][cq] + red_r[3][cq];
+    qak = red_s[0][0] + red_s[1][0] + red_s[2][0] + red_s[3][0];
+    qkw = red_s[0][1] + red_s[1][1] + red_s[2][1] + red_s[3][1];
+
+    f32x4 vv;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vv[e] = to_f32(vraw[e]);
+    if (S_final) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int row = rg + RG * i;
+            *reinterpret_cast<f32x4*>(S_final + base + row * DV) =
+                sw[row] * s[i] - sak[row] * p + skw[row] * vv;
+        }
+    }
+    if (rg == 0) {
+        const f32x4 ov = r - qak * p + qkw * vv;
+        V4 ow;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ow[e] = from_f32<E>(ov[e]);
+        *reinterpret_cast<V4*>(o + bh * DV + col0 + 4 * cq) = ow;
+    }
+}
+
 template <typename E, int D>
 hipError_t gdr_t(const void* q, const void* kw, const void* v, const void* kr, const void* a,
                  const void* g, const float* S0, void* o, float* S_final, int BH, int T,
                  hipStream_t st) {
+    if (T == 1) {
+        // four workgroups per state, a quarter of the value columns each
+        constexpr int NS = 4;
+        gdr_step_kernel<E, D, D, NS><<<(unsigned)((long)BH * NS), 256, 0, st>>>(
+            (const E*)q, (const E*)kw, (const E*)v, (const E*)kr, (const E*)a, (const E*)g, S0,
+            (E*)o, S_final);
+        return hipGetLastError();
+    }
     const long blocks = (long)BH * (D / WAVE);
     gdr_recurrent_kernel<E, D, D><<<(unsigned)blocks, WAVE, 0, st>>>(
         (const E*)q, (const E*)kw, (const E*)v, (const E*)kr, (const E*)a, (const E*)g, S0, (E*)o,

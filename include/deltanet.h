@@ -370,15 +370,16 @@ int dn_ssm_decode_step(const void* q, const void* k, const void* v, const void* 
  * key-space transition (page "A walk through of the DeltaNet family of linear
  * attention variants"). kr = k, kw = beta k, a = beta, g = 0 is DeltaNet; the
  * removal term uses the state before the decay, as the transition is written.
- * Token by token (one wavefront per head and 64 value columns); the chunked
- * form is not provided.
+ * Token by token (one wavefront per head and 64 value columns); a single
+ * token (T == 1, and the decode step) streams each state once instead. The
+ * chunked form is not provided.
  *   q, kw, kr, a, g  [B,H,T,dk] (dtype);  v, o  [B,H,T,dv] (dtype)
  *   S0, S_final      [B,H,dk,dv] fp32 (S0 NULL => zeros; S_final NULL => not
  *                    written; S_final == S0 allowed)
  * dn_gdr_decode_step is one token ([B,H,dk] / [B,H,dv] inputs) with S updated
- * in place. dk == dv in {64, 128}. Every tensor is read element by element:
- * the activations need the alignment of their element type, the states 4
- * bytes. Errors as for dn_recurrent_fwd.
+ * in place. dk == dv in {64, 128}. v, o and the states must be 16-byte
+ * aligned; q, kw, kr, a, g only element-aligned. Errors as for
+ * dn_recurrent_fwd.
  */
 int dn_gdr_recurrent_fwd(const void* q, const void* kw, const void* v, const void* kr,
                          const void* a, const void* g, const float* S0, void* o, float* S_final,

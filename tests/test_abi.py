@@ -401,13 +401,15 @@ def test_gdr_validation(fn):
     for name in ("q", "kw", "v", "kr", "a", "g", "o"):
         assert _gdr(fn, **{name: None}) == E, name
     assert _gdr(fn, kr=ODD) == E
+    assert _gdr(fn, v=MIS) == E      # v, o and the states are read as 16-byte vectors
+    assert _gdr(fn, o=MIS) == E
     assert _gdr(fn, B=0) == E
     assert _gdr(fn, dtype=2) == E
     assert _gdr(fn, dk=96, dv=96) == N
     assert _gdr(fn, dk=64, dv=128) == N
     if fn == "dn_gdr_decode_step":
         assert _gdr(fn, S=None) == E
-        assert _gdr(fn, S=P + 2) == E
+        assert _gdr(fn, S=MIS) == E
     else:
         assert _gdr(fn, T=-1) == E
-        assert _gdr(fn, S0=P + 2) == E
+        assert _gdr(fn, S0=MIS) == E

@@ -79,3 +79,19 @@ def test_gdr_tied_equals_deltanet_on_gpu():
     torch.cuda.synchronize()
     assert rel_err(o1, o2.double().cpu().numpy()) <= 1e-5
     assert rel_err(S1, S2.double().cpu().numpy()) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gdr_decode_strong_decay(dtype):
+    """Decays that underflow to zero in some channels (g = -200): those rows of
+    the state drop out, nothing becomes NaN."""
+    dn = _dn()
+    x = synthetic.make_gdr(4, 2, 1, 128, dtype, seed=91, s0_std=0.5)
+    x["g"][..., ::3] = -200.0
+    dx = to_dev(x)
+    S = dx["S0"].clone()
+    o = dn.gdr_decode_step(*(dx[n][:, :, 0].contiguous() for n in NAMES), S)
+    torch.cuda.synchronize()
+    o_ref, S_ref = ogdr.recurrent(*(x[n] for n in NAMES), x["S0"])
+    assert rel_err(o, o_ref[:, :, 0]) <= TOL[dtype]
+    assert rel_err(S, S_ref) <= TOL[dtype]
