@@ -69,3 +69,37 @@ def test_separate_keys_differ_from_tied():
     o1, _ = gdr.recurrent(q, beta[..., None] * k, v, kr, beta[..., None] * ones, np.zeros_like(k), S0)
     o2, _ = oracle.recurrent(q, k, v, beta, None, S0, kind=oracle.DELTANET)
     assert not np.allclose(o1, o2)
+
+
+@pytest.mark.parametrize("C", [1, 3, 8, 16, 40])
+def test_chunk_form_equals_recurrence(C):
+    """The chunked form (its derivation is in oracle/gdr.chunk_maps) against the
+    token-by-token recurrence, with separate keys, per-channel decay and rate,
+    a start state and a ragged last chunk."""
+    r = np.random.default_rng(50 + C)
+    B, H, T, dk, dv = 1, 2, 37, 8, 5
+    q = r.standard_normal((B, H, T, dk))
+    kw = r.standard_normal((B, H, T, dk)) * 0.5
+    kr = r.standard_normal((B, H, T, dk))
+    kr /= np.linalg.norm(kr, axis=-1, keepdims=True)
+    a = 1.0 / (1.0 + np.exp(-r.standard_normal((B, H, T, dk))))
+    g = -np.log1p(np.exp(r.standard_normal((B, H, T, dk))))
+    v = r.standard_normal((B, H, T, dv))
+    S0 = r.standard_normal((B, H, dk, dv))
+    o1, S1 = gdr.recurrent(q, kw, v, kr, a, g, S0)
+    o2, S2 = gdr.chunk(q, kw, v, kr, a, g, S0, C=C)
+    assert np.allclose(o1, o2, rtol=1e-9, atol=1e-10)
+    assert np.allclose(S1, S2, rtol=1e-9, atol=1e-10)
+
+
+def test_chunk_form_strong_decay_is_finite():
+    """Decays summing to -1000 inside a chunk: every factor of the chunked form
+    has a non-positive exponent, so nothing overflows."""
+    r = np.random.default_rng(77)
+    B, H, T, d = 1, 1, 20, 4
+    q, kw, kr, v = (r.standard_normal((B, H, T, d)) for _ in range(4))
+    a = np.full((B, H, T, d), 0.5)
+    g = np.full((B, H, T, d), -50.0)
+    o1, S1 = gdr.recurrent(q, kw, v, kr, a, g, None)
+    o2, S2 = gdr.chunk(q, kw, v, kr, a, g, None, C=16)
+    assert np.isfinite(o2).all() and np.allclose(o1, o2, rtol=1e-9, atol=1e-12)
