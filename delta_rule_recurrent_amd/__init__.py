@@ -22,7 +22,7 @@ from ._lib import DeltaNetError, lib
 __all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_fwd_gqa",
            "decode_step_gqa", "chunk_fwd_varlen", "decode_tokens", "layer_prologue",
            "layer_epilogue", "gated_deltanet_layer", "ssm_chunk_fwd", "ssm_recurrent_fwd",
-           "ssm_decode_step", "gdr_recurrent_fwd", "gdr_decode_step", "chunk_prep", "chunk_scan",
+           "ssm_decode_step", "gdr_recurrent_fwd", "gdr_chunk_fwd", "gdr_decode_step", "chunk_prep", "chunk_scan",
            "recurrent_fwd",
            "kda_recurrent_fwd", "decode_step", "kda_decode_step", "workspace_bytes",
            "DeltaNetError", "lib", "library_path"]
@@ -529,6 +529,41 @@ def gdr_recurrent_fwd(q, kw, v, kr, a, g, S0=None, *, output_final_state=True, o
                                     _ptr(S0), _ptr(o), _ptr(S_final), B, H, T, dk, dv, _DT[dt],
                                     _stream(stream))
     _lib.check("dn_gdr_recurrent_fwd", st)
+    return o, S_final
+
+
+def gdr_chunk_fwd(q, kw, v, kr, a, g, S0=None, *, output_final_state=True, o=None,
+                  S_final=None, workspace=None, stream=None):
+    """Chunked form of gdr_recurrent_fwd (64-token chunks reduced to affine maps
+    of the state, fp32 arithmetic). Same arguments; ``workspace`` (uint8, at
+    least dn_gdr_chunk_workspace bytes) is allocated when not given.
+    Returns (o, S_final)."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B,H,T,dk]")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    if dt not in _DT:
+        raise TypeError("q must be bfloat16 or float32")
+    for name, t in (("kw", kw), ("kr", kr), ("a", a), ("g", g)):
+        _check_tensor(name, t, (B, H, T, dk), dt, dev)
+    _check_tensor("v", v, (B, H, T, dv), dt, dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, H, dk, dv), torch.float32, dev)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, T, dv), dt, dev)
+    if S_final is None and output_final_state:
+        S_final = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    elif S_final is not None:
+        _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
+    if workspace is None:
+        workspace = _alloc_workspace(int(lib().dn_gdr_chunk_workspace(B, H, T, dk, dv, _DT[dt])), dev)
+    st = lib().dn_gdr_chunk_fwd(_ptr(q), _ptr(kw), _ptr(v), _ptr(kr), _ptr(a), _ptr(g), _ptr(S0),
+                                _ptr(o), _ptr(S_final), B, H, T, dk, dv, _DT[dt], _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("dn_gdr_chunk_fwd", st)
     return o, S_final
 
 

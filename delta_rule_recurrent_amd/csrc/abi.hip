@@ -7,6 +7,15 @@
 #include "../../include/deltanet.h"
 #include "dn_launch.h"
 
+namespace dn {
+// the chunked generalized delta rule (gdr_chunk.hip)
+size_t gdr_chunk_workspace_bytes(long long BH, long long T, int d);
+hipError_t launch_gdr_chunk(int dtype, const void* q, const void* kw, const void* v,
+                            const void* kr, const void* a, const void* g, const float* S0,
+                            void* o, float* S_final, void* ws, int BH, int T, int d,
+                            hipStream_t st);
+}  // namespace dn
+
 namespace {
 
 constexpr int kVersion = 2;
@@ -348,6 +357,32 @@ int dn_gdr_recurrent_fwd(const void* q, const void* kw, const void* v, const voi
     }
     return hip_status(dn::launch_gdr_recurrent(dtype, q, kw, v, kr, a, g, S0, o, S_final, (int)BH,
                                                T, dk, as_stream(stream)));
+}
+
+size_t dn_gdr_chunk_workspace(int B, int H, int T, int dk, int dv, int dtype) {
+    if (B < 1 || H < 1 || T < 1) return 0;
+    if ((dk != 64 && dk != 128) || dk != dv) return 0;
+    if (dtype != DN_F32 && dtype != DN_BF16) return 0;
+    return dn::gdr_chunk_workspace_bytes((long long)B * H, T, dk);
+}
+
+int dn_gdr_chunk_fwd(const void* q, const void* kw, const void* v, const void* kr, const void* a,
+                     const void* g, const float* S0, void* o, float* S_final, int B, int H, int T,
+                     int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    const int st = gdr_check(q, kw, v, kr, a, g, S0, o, S_final, B, H, T, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    const long long BH = (long long)B * H;
+    if (T == 0) {
+        if (!S_final) return DN_OK;
+        return hip_status(dn::launch_state_copy(S0, S_final, BH * dk * dv, as_stream(stream)));
+    }
+    // every chunk is one workgroup of the map kernels, four of the products
+    if (BH * ((T + 63) / 64) > (1LL << 28)) return DN_EINVAL;
+    const size_t need = dn::gdr_chunk_workspace_bytes(BH, T, dk);
+    if (!workspace || workspace_bytes < need || misaligned(workspace, 256)) return DN_EWORKSPACE;
+    return hip_status(dn::launch_gdr_chunk(dtype, q, kw, v, kr, a, g, S0, o, S_final, workspace,
+                                           (int)BH, T, dk, as_stream(stream)));
 }
 
 int dn_gdr_decode_step(const void* q, const void* kw, const void* v, const void* kr,

@@ -372,7 +372,7 @@ int dn_ssm_decode_step(const void* q, const void* k, const void* v, const void* 
  * removal term uses the state before the decay, as the transition is written.
  * Token by token (one wavefront per head and 64 value columns); a single
  * token (T == 1, and the decode step) streams each state once instead. The
- * chunked form is not provided.
+ * chunked form is dn_gdr_chunk_fwd below.
  *   q, kw, kr, a, g  [B,H,T,dk] (dtype);  v, o  [B,H,T,dv] (dtype)
  *   S0, S_final      [B,H,dk,dv] fp32 (S0 NULL => zeros; S_final NULL => not
  *                    written; S_final == S0 allowed)
@@ -387,6 +387,25 @@ int dn_gdr_recurrent_fwd(const void* q, const void* kw, const void* v, const voi
 int dn_gdr_decode_step(const void* q, const void* kw, const void* v, const void* kr,
                        const void* a, const void* g, float* S, void* o, int B, int H, int dk,
                        int dv, int dtype, void* stream);
+
+/*
+ * Chunked form of the generalized delta rule (derived here; the pages give
+ * none): every 64-token chunk is reduced to an affine map S <- P S + Sh with
+ * read-outs O = Qp S + Oh, where the chunk's removal read-outs solve a unit
+ * lower-triangular system whose entries carry the per-channel decay inside
+ * their contraction (all exponents <= 0); the maps are then applied chunk
+ * after chunk. Arithmetic is fp32 throughout. Same tensors and rules as
+ * dn_gdr_recurrent_fwd, plus a workspace of at least
+ * dn_gdr_chunk_workspace(B,H,T,dk,dv,dtype) bytes (256-byte aligned; 528 KiB
+ * per (head, chunk) at d = 128; contents unspecified between calls;
+ * DN_EWORKSPACE if missing or short). The result equals the token-by-token
+ * form up to rounding.
+ */
+size_t dn_gdr_chunk_workspace(int B, int H, int T, int dk, int dv, int dtype);
+int dn_gdr_chunk_fwd(const void* q, const void* kw, const void* v, const void* kr, const void* a,
+                     const void* g, const float* S0, void* o, float* S_final, int B, int H, int T,
+                     int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 #ifdef __cplusplus
 }

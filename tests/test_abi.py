@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 27, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -413,3 +413,29 @@ def test_gdr_validation(fn):
     else:
         assert _gdr(fn, T=-1) == E
         assert _gdr(fn, S0=MIS) == E
+
+
+def test_gdr_chunk_workspace_and_validation():
+    lib = _lib.lib()
+    ws = lib.dn_gdr_chunk_workspace
+    assert ws(1, 1, 0, 64, 64, 1) == 0
+    assert ws(1, 1, 64, 96, 96, 1) == 0
+    one = ws(1, 1, 64, 128, 128, 1)
+    assert one > 0 and one % 256 == 0
+    assert ws(2, 3, 65, 128, 128, 1) == 2 * 3 * 2 * one      # per (head, chunk)
+    args = dict(q=P, kw=P, v=P, kr=P, a=P, g=P, S0=P, o=P, S_final=P, B=1, H=1, T=64, dk=64,
+                dv=64, dtype=1, ws=WS, wsb=1 << 30, stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.dn_gdr_chunk_fwd(*[a[n] for n in ("q", "kw", "v", "kr", "a", "g", "S0", "o",
+                                                       "S_final", "B", "H", "T", "dk", "dv",
+                                                       "dtype", "ws", "wsb", "stream")])
+    E, W = _lib.DN_EINVAL, _lib.DN_EWORKSPACE
+    assert call(kr=None) == E
+    assert call(v=MIS) == E
+    assert call(dk=96, dv=96) == _lib.DN_ENOTSUP
+    assert call(ws=None) == W
+    assert call(wsb=16) == W
+    assert call(ws=WS + 128) == W
