@@ -453,6 +453,15 @@ def run_serving(torch, dn, synthetic, to_dev, dev):
     # the selective state-space kind (no beta, no correction) on the same inputs
     timed("ssm_chunk_fwd", lambda: dn.ssm_chunk_fwd(x["q"], x["k"], x["v"], x["g"], None, o=o,
                                                     S_final=S, workspace=ws))
+    # the generalized delta rule at the same size, chunked (fp32 maps) and token by token
+    xg = to_dev(synthetic.make_gdr(B, H, T, d, "bf16", seed=2005))
+    gargs = [xg[n] for n in ("q", "kw", "v", "kr", "a", "g")]
+    wsg = torch.empty(int(dn.lib().dn_gdr_chunk_workspace(B, H, T, d, d, 1)), dtype=torch.uint8,
+                      device=dev)
+    timed("gdr_chunk_fwd", lambda: dn.gdr_chunk_fwd(*gargs, None, o=o, S_final=S, workspace=wsg),
+          {"workspace_bytes": wsg.numel()})
+    timed("gdr_recurrent_fwd", lambda: dn.gdr_recurrent_fwd(*gargs, None))
+    del xg, gargs, wsg
     del x, ws, o, S, Sc, qg, kg, xp, wsp, op, Sp
     # speculative decode: 4 drafted tokens for the decode workload's 256 x 16
     # states, the state after each kept (4 x 256 MiB of snapshots)

@@ -54,7 +54,10 @@ struct GdrWs {
     static constexpr long FLOATS = OH + GC * D;  // a multiple of 64 floats (256 bytes)
 };
 
-// ---- 1. elementwise: G, R^, L~, Kw~, V, Q^ (into the Qp slot), P = diag(e^{G_C})
+// ---- 1. elementwise: G, R^, L~, Kw~, V, Q^ (into the Qp slot), P = diag(e^{G_C}).
+//         g is staged in LDS and summed there over tokens (one thread per
+//         channel); every other output is then written by all threads, rows
+//         of consecutive channels, reading the running sums from LDS.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
                                                        const E* __restrict__ kw,
@@ -64,6 +67,7 @@ __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
                                                        const E* __restrict__ g,
                                                        float* __restrict__ ws, int T, int nchunks) {
     typedef GdrWs<D> Ws;
+    __shared__ float sG[GC][D + 1];
     const long item = blockIdx.x;
     const long bh = item / nchunks;
     const int c = (int)(item % nchunks);
@@ -71,35 +75,36 @@ __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
     float* w = ws + item * Ws::FLOATS;
     const long row0 = bh * T + (long)c * GC;
     const int tid = threadIdx.x;
+    for (int e = tid; e < GC * D; e += 256) {
+        const int t = e / D, ch = e % D;
+        sG[t][ch] = t < L ? to_f32(g[(row0 + t) * D + ch]) : 0.f;
+    }
+    __syncthreads();
     if (tid < D) {
-        const int ch = tid;
         float Gr = 0.f;
         for (int t = 0; t < GC; ++t) {
-            const bool in = t < L;
-            const long i = (row0 + t) * D + ch;
-            const float gt = in ? to_f32(g[i]) : 0.f;
-            const float krt = in ? to_f32(kr[i]) : 0.f;
-            w[Ws::R + t * D + ch] = krt * __expf(Gr);   // e^{G_{t-1}}
-            Gr += gt;
-            w[Ws::G + t * D + ch] = Gr;
-            w[Ws::V + t * D + ch] = in ? to_f32(v[i]) : 0.f;   // d_v == d_k
+            Gr += sG[t][tid];
+            sG[t][tid] = Gr;
         }
-        const float GCh = Gr;
-        for (int t = 0; t < GC; ++t) {
-            const bool in = t < L;
-            const long i = (row0 + t) * D + ch;
-            const float Gt = w[Ws::G + t * D + ch];
-            const float dec = __expf(GCh - Gt);
-            w[Ws::L + t * D + ch] = in ? to_f32(a[i]) * to_f32(kr[i]) * dec : 0.f;
-            w[Ws::K + t * D + ch] = in ? to_f32(kw[i]) * dec : 0.f;
-            w[Ws::QP + t * D + ch] = in ? to_f32(q[i]) * __expf(Gt) : 0.f;
-        }
-        w[Ws::P + (long)ch * D + ch] = __expf(GCh);
     }
-    // off-diagonal of P
+    __syncthreads();
+    for (int e = tid; e < GC * D; e += 256) {
+        const int t = e / D, ch = e % D;
+        const bool in = t < L;
+        const long i = (row0 + t) * D + ch;
+        const float Gt = sG[t][ch], Gm = t > 0 ? sG[t - 1][ch] : 0.f, GCh = sG[GC - 1][ch];
+        const float dec = __expf(GCh - Gt);
+        const float krv = in ? to_f32(kr[i]) : 0.f;
+        w[Ws::G + e] = Gt;
+        w[Ws::R + e] = krv * __expf(Gm);
+        w[Ws::V + e] = in ? to_f32(v[i]) : 0.f;   // d_v == d_k
+        w[Ws::L + e] = in ? to_f32(a[i]) * krv * dec : 0.f;
+        w[Ws::K + e] = in ? to_f32(kw[i]) * dec : 0.f;
+        w[Ws::QP + e] = in ? to_f32(q[i]) * __expf(Gt) : 0.f;
+    }
     for (int e = tid; e < D * D; e += 256) {
         const int r = e / D, cc = e % D;
-        if (r != cc) w[Ws::P + e] = 0.f;
+        w[Ws::P + e] = r == cc ? __expf(sG[GC - 1][r]) : 0.f;
     }
 }
 
@@ -144,19 +149,22 @@ __global__ __launch_bounds__(256) void gdr_pairs_kernel(const E* __restrict__ q,
         for (int ch = 0; ch < CB; ++ch) {
             const float Gs = sG[s][ch], Gm = s > 0 ? sG[s - 1][ch] : 0.f;
             const float krs = sKr[s][ch], qs = sQ[s][ch];
+            // e^{G_s - G_j} = e^{G_{s-1} - G_j} e^{g_s}: one exponential per pair
+            const float egq = __expf(Gs - Gm) * qs;
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
                 const int j = jg + 4 * jj;
-                const float Gj = sG[j][ch];
+                const float lj = sL[j][ch], kj = sKw[j][ch];
                 if (j < s) {
-                    const float e1 = __expf(Gm - Gj) * krs;
-                    m[jj] += e1 * sL[j][ch];
-                    n[jj] += e1 * sKw[j][ch];
-                }
-                if (j <= s) {
-                    const float e2 = __expf(Gs - Gj) * qs;
-                    ak[jj] += e2 * sKw[j][ch];
-                    al[jj] += e2 * sL[j][ch];
+                    const float e = __expf(Gm - sG[j][ch]);
+                    const float e1 = e * krs, e2 = e * egq;
+                    m[jj] += e1 * lj;
+                    n[jj] += e1 * kj;
+                    ak[jj] += e2 * kj;
+                    al[jj] += e2 * lj;
+                } else if (j == s) {
+                    ak[jj] += qs * kj;
+                    al[jj] += qs * lj;
                 }
             }
         }
@@ -244,7 +252,9 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
 }
 
 // ---- 5. the scan: one workgroup per (head, 32 value columns) applies the maps
-//         chunk after chunk, S (D x 32, fp32) in LDS.
+//         chunk after chunk, S (D x 32, fp32) in LDS; each thread reads its rows
+//         of P and Qp from memory (cached), which measured faster than staging
+//         whole chunks in LDS (the LDS reads of S then bound the step).
 template <typename E, int D>
 __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __restrict__ ws,
                                                              const float* S0, E* __restrict__ o,
@@ -299,6 +309,7 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
     }
 }
 
+// (every product contracts over the chunk's 64 tokens: K == GC)
 template <int D>
 hipError_t gemm(float* ws, long items, int M, int N, int K, long offA, int lda, int transA,
                 long offB, int ldb, long offC, int ldc, float alpha, float beta, hipStream_t st) {
