@@ -129,3 +129,32 @@ def test_gdr_chunk_strong_decay_and_in_place():
     o_ref, S_ref = ogdr.recurrent(*(x[n] for n in NAMES), x["S0"])
     assert rel_err(o, o_ref) <= TOL["f32"]
     assert rel_err(S, S_ref) <= TOL["f32"]
+
+
+def test_gdr_chunk_long_sequence():
+    """70 chunks and a ragged tail (4489 tokens) at d = 128, bf16, with a start
+    state: the chunk maps chained 70 times stay within the bound of the
+    oracle's recurrence."""
+    dn = _dn()
+    say("gdr chunk long")
+    x = synthetic.make_gdr(1, 2, 64 * 70 + 9, 128, "bf16", seed=820, s0_std=0.5)
+    dx = to_dev(x)
+    o, S = dn.gdr_chunk_fwd(*(dx[n] for n in NAMES), dx["S0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = ogdr.recurrent(*(x[n] for n in NAMES), x["S0"])
+    eo, eS = rel_err(o, o_ref), rel_err(S, S_ref)
+    say("  o err %.3g, S err %.3g" % (eo, eS))
+    assert eo <= TOL["bf16"] and eS <= TOL["bf16"], (eo, eS)
+
+
+def test_gdr_chunk_many_heads():
+    """40 (sequence, head) rows of 3 chunks: the grid and workspace indexing
+    over many heads, against the token-by-token GPU form (fp32, 1e-4)."""
+    dn = _dn()
+    x = synthetic.make_gdr(5, 8, 150, 64, "f32", seed=830, s0_std=0.5)
+    dx = to_dev(x)
+    o1, S1 = dn.gdr_chunk_fwd(*(dx[n] for n in NAMES), dx["S0"])
+    o2, S2 = dn.gdr_recurrent_fwd(*(dx[n] for n in NAMES), dx["S0"])
+    torch.cuda.synchronize()
+    assert rel_err(o1, o2.double().cpu().numpy()) <= 1e-4
+    assert rel_err(S1, S2.double().cpu().numpy()) <= 1e-4
