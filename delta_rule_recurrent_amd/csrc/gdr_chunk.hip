@@ -199,16 +199,19 @@ __global__ __launch_bounds__(WAVE) void gdr_tinv_kernel(float* __restrict__ ws) 
 }
 
 // ---- 4. batched fp32 product inside every chunk's workspace:
-//         C = alpha op(A) B + beta C, op(A) = A or A^T; A (M x K after op), B
-//         (K x N), C (M x N), all row-major with the given leading dimensions.
-//         64 x 64 output tile per workgroup, 4 x 4 outputs per thread, the
-//         contraction in steps of 16 through LDS. M, N multiples of 64 and K
-//         of 16 (checked by the caller).
+//         C = alpha op(A) B + beta C, op(A) = A or A^T; op(A) (M x 64), B
+//         (64 x N), C (M x N), row-major with the given leading dimensions.
+//         Every product here contracts over the 64 tokens of a chunk. A
+//         workgroup stages its op(A) rows and B columns (64 x 64 each) in LDS
+//         and computes a 64 x 64 tile on the fp32 matrix cores: wave w the rows
+//         16w .. 16w + 15, four 16-column tiles. M and N are multiples of 64.
 __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, long stride, int tm,
-                                                       int tn, int K, long offA, int lda,
-                                                       int transA, long offB, int ldb, long offC,
-                                                       int ldc, float alpha, float beta) {
-    __shared__ float As[16][64 + 4], Bs[16][64 + 4];
+                                                       int tn, long offA, int lda, int transA,
+                                                       long offB, int ldb, long offC, int ldc,
+                                                       float alpha, float beta) {
+    constexpr int KK = GC;
+    __shared__ __align__(16) float As[64][KK + 4];   // op(A) rows: As[m][k]
+    __shared__ float Bs[KK][64 + 1];                 // Bs[k][n]
     // block = (chunk item, output tile row, output tile column)
     const long tiles = (long)tm * tn;
     const long item = blockIdx.x / tiles;
@@ -218,94 +221,161 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
     const float* B = w + offB;
     float* Cm = w + offC;
     const int m0 = (tile / tn) * 64, n0 = (tile % tn) * 64;
-    const int tid = threadIdx.x, tr = tid / 16, tc = tid % 16;
-    float acc[4][4] = {};
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        __syncthreads();
-        for (int e = tid; e < 16 * 64; e += 256) {
-            const int kk = e / 64, mm = e % 64;
-            As[kk][mm] = transA ? A[(long)(k0 + kk) * lda + m0 + mm] : A[(long)(m0 + mm) * lda + k0 + kk];
-            Bs[kk][mm] = B[(long)(k0 + kk) * ldb + n0 + mm];
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
+    const int gq = lane >> 4, r = lane & 15;
+    // 16 bytes per load (every offset and leading dimension is a multiple of 4 floats)
+    for (int e = tid; e < KK * 16; e += 256) {
+        const int hi = e / 16, lo = (e % 16) * 4;
+        const f32x4 bv = *reinterpret_cast<const f32x4*>(B + (long)hi * ldb + n0 + lo);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) Bs[hi][lo + u] = bv[u];
+        if (transA) {
+            // A^T: columns m0 + lo .. of A are rows of op(A)
+            const f32x4 av = *reinterpret_cast<const f32x4*>(A + (long)hi * lda + m0 + lo);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) As[lo + u][hi] = av[u];
+        } else {
+            *reinterpret_cast<f32x4*>(&As[hi][lo]) =
+                *reinterpret_cast<const f32x4*>(A + (long)(m0 + hi) * lda + lo);
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    f32x4 acc[4];
 #pragma unroll
-        for (int kk = 0; kk < 16; ++kk) {
-            float av[4], bv[4];
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = zero4();
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                av[i] = As[kk][tr * 4 + i];
-                bv[i] = Bs[kk][tc * 4 + i];
-            }
+    for (int kb = 0; kb < KK / 32; ++kb) {
+        f32x8 af;   // row 16 wv + r at contraction indices 4gq .. 4gq + 3, 16 + 4gq .. 16 + 4gq + 3
+        const f32x4 lo4 = *reinterpret_cast<const f32x4*>(&As[16 * wv + r][32 * kb + 4 * gq]);
+        const f32x4 hi4 = *reinterpret_cast<const f32x4*>(&As[16 * wv + r][32 * kb + 16 + 4 * gq]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 4; ++j) { af[j] = lo4[j]; af[4 + j] = hi4[j]; }
 #pragma unroll
-                for (int jn = 0; jn < 4; ++jn) acc[i][jn] += av[i] * bv[jn];
+        for (int ct = 0; ct < 4; ++ct) {
+            f32x8 bf;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                bf[j] = Bs[32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + j - 4)][16 * ct + r];
+            acc[ct] = mma(af, bf, acc[ct]);
         }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-        for (int jn = 0; jn < 4; ++jn) {
-            float* dst = Cm + (long)(m0 + tr * 4 + i) * ldc + n0 + tc * 4 + jn;
-            *dst = alpha * acc[i][jn] + (beta != 0.f ? beta * *dst : 0.f);
+        for (int i = 0; i < 4; ++i) {
+            float* dst = Cm + (long)(m0 + 16 * wv + 4 * gq + i) * ldc + n0 + 16 * ct + r;
+            *dst = alpha * acc[ct][i] + (beta != 0.f ? beta * *dst : 0.f);
         }
 }
 
-// ---- 5. the scan: one workgroup per (head, 32 value columns) applies the maps
-//         chunk after chunk, S (D x 32, fp32) in LDS; each thread reads its rows
-//         of P and Qp from memory (cached), which measured faster than staging
-//         whole chunks in LDS (the LDS reads of S then bound the step).
+// ---- 5. the scan: one workgroup (four wavefronts) per (head, 32 value
+//         columns) applies the maps chunk after chunk on the fp32 matrix cores
+//         (the fragment convention of dn_device.h). Wave w owns S rows
+//         32w .. 32w + 31 (d = 128; 16w .. 16w + 15 at d = 64) and read-out rows
+//         16w .. 16w + 15 as 16 x 16 accumulator tiles. Per chunk: the A-fragments
+//         of P and Qp are loaded straight from the workspace (they do not depend
+//         on S), S goes through LDS once to become B-fragments, and
+//         S <- P S + Sh, O = Qp S + Oh accumulate from the Sh and Oh tiles.
 template <typename E, int D>
 __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __restrict__ ws,
                                                              const float* S0, E* __restrict__ o,
                                                              float* S_final, int T, int nchunks) {
     typedef GdrWs<D> Ws;
-    constexpr int NB = 32;                 // value columns per workgroup
-    constexpr int SPT = D * NB / 256;      // state outputs per thread
-    constexpr int OPT = GC * NB / 256;     // read-out outputs per thread
+    constexpr int NB = 32;          // value columns per workgroup (two 16-column tiles)
+    constexpr int RTW = D / 64;     // 16-row tiles of S per wavefront
+    constexpr int KB = D / 32;      // 32-wide blocks of the contraction over key channels
     __shared__ float sS[D][NB + 1];
     const long bh = blockIdx.x / (D / NB);
     const int n0 = (int)(blockIdx.x % (D / NB)) * NB;
-    const int tid = threadIdx.x;
-    for (int e = tid; e < D * NB; e += 256) {
-        const int r = e / NB, cc = e % NB;
-        sS[r][cc] = S0 ? S0[(bh * D + r) * D + n0 + cc] : 0.f;
-    }
-    // thread -> state row ks, columns kn .. kn + SPT - 1; read-out row to, columns on .. on + OPT - 1
-    const int ks = tid / (NB / SPT), kn = (tid % (NB / SPT)) * SPT;
-    const int to = tid / (NB / OPT), on = (tid % (NB / OPT)) * OPT;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
+    const int gq = lane >> 4, r = lane & 15;
+
+    f32x4 S[RTW][2];
+#pragma unroll
+    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const long row = 16 * (RTW * w + rt) + 4 * gq + i;
+                S[rt][ct][i] = S0 ? S0[(bh * D + row) * D + n0 + 16 * ct + r] : 0.f;
+            }
+
     for (int c = 0; c < nchunks; ++c) {
-        const float* w = ws + (bh * nchunks + c) * Ws::FLOATS;
+        const float* wc = ws + (bh * nchunks + c) * Ws::FLOATS;
         const int L = min(GC, T - c * GC);
-        __syncthreads();   // S of the previous chunk is in LDS
-        float so[SPT], oo[OPT];
+        // A-fragments: lane (gq, r) holds row r of the tile at contraction
+        // indices 4gq .. 4gq + 3 and 16 + 4gq .. 16 + 4gq + 3 of each 32-block
+        f32x8 pa[RTW][KB], qa[KB];
 #pragma unroll
-        for (int i = 0; i < SPT; ++i) so[i] = w[Ws::SH + (long)ks * D + n0 + kn + i];
+        for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
-        for (int i = 0; i < OPT; ++i) oo[i] = w[Ws::OH + to * D + n0 + on + i];
-        for (int m = 0; m < D; ++m) {
-            const float p = w[Ws::P + (long)ks * D + m];
-            const float qp = w[Ws::QP + to * D + m];
+            for (int rt = 0; rt < RTW; ++rt) {
+                const float* src = wc + Ws::P + (long)(16 * (RTW * w + rt) + r) * D + 32 * kb + 4 * gq;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
 #pragma unroll
-            for (int i = 0; i < SPT; ++i) so[i] += p * sS[m][kn + i];
+                for (int j = 0; j < 4; ++j) { pa[rt][kb][j] = lo[j]; pa[rt][kb][4 + j] = hi[j]; }
+            }
+            const float* src = wc + Ws::QP + (long)(16 * w + r) * D + 32 * kb + 4 * gq;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
 #pragma unroll
-            for (int i = 0; i < OPT; ++i) oo[i] += qp * sS[m][on + i];
+            for (int j = 0; j < 4; ++j) { qa[kb][j] = lo[j]; qa[kb][4 + j] = hi[j]; }
         }
-        if (to < L) {
+        f32x4 sn[RTW][2], oa[2];
 #pragma unroll
-            for (int i = 0; i < OPT; ++i)
-                o[(bh * T + (long)c * GC + to) * D + n0 + on + i] = from_f32<E>(oo[i]);
+        for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+                    sn[rt][ct][i] = wc[Ws::SH + (long)(16 * (RTW * w + rt) + 4 * gq + i) * D + n0 + 16 * ct + r];
+                oa[ct][i] = wc[Ws::OH + (long)(16 * w + 4 * gq + i) * D + n0 + 16 * ct + r];
+            }
         }
-        __syncthreads();   // every read of the old S is done
+        __syncthreads();   // every B-fragment read of the previous S is done
 #pragma unroll
-        for (int i = 0; i < SPT; ++i) sS[ks][kn + i] = so[i];
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sS[16 * (RTW * w + rt) + 4 * gq + i][16 * ct + r] = S[rt][ct][i];
+        __syncthreads();
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+                f32x8 sb;   // B-fragment: column r of the tile at the same contraction indices
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    sb[j] = sS[32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + j - 4)][16 * ct + r];
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt) sn[rt][ct] = mma(pa[rt][kb], sb, sn[rt][ct]);
+                oa[ct] = mma(qa[kb], sb, oa[ct]);
+            }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * w + 4 * gq + i;
+                if (t < L) o[(bh * T + (long)c * GC + t) * D + n0 + 16 * ct + r] = from_f32<E>(oa[ct][i]);
+            }
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) S[rt][ct] = sn[rt][ct];
     }
-    __syncthreads();
     if (S_final) {
-        for (int e = tid; e < D * NB; e += 256) {
-            const int r = e / NB, cc = e % NB;
-            S_final[(bh * D + r) * D + n0 + cc] = sS[r][cc];
-        }
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const long row = 16 * (RTW * w + rt) + 4 * gq + i;
+                    S_final[(bh * D + row) * D + n0 + 16 * ct + r] = S[rt][ct][i];
+                }
     }
 }
 
@@ -313,8 +383,9 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 template <int D>
 hipError_t gemm(float* ws, long items, int M, int N, int K, long offA, int lda, int transA,
                 long offB, int ldb, long offC, int ldc, float alpha, float beta, hipStream_t st) {
+    if (K != GC || M % 64 || N % 64) return hipErrorInvalidValue;
     const int tm = M / 64, tn = N / 64;
-    gdr_gemm_kernel<<<(unsigned)(items * tm * tn), 256, 0, st>>>(ws, GdrWs<D>::FLOATS, tm, tn, K,
+    gdr_gemm_kernel<<<(unsigned)(items * tm * tn), 256, 0, st>>>(ws, GdrWs<D>::FLOATS, tm, tn,
                                                                  offA, lda, transA, offB, ldb,
                                                                  offC, ldc, alpha, beta);
     return hipGetLastError();
