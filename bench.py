@@ -456,12 +456,32 @@ def run_serving(torch, dn, synthetic, to_dev, dev):
     # the generalized delta rule at the same size, chunked (fp32 maps) and token by token
     xg = to_dev(synthetic.make_gdr(B, H, T, d, "bf16", seed=2005))
     gargs = [xg[n] for n in ("q", "kw", "v", "kr", "a", "g")]
-    wsg = torch.empty(int(dn.lib().dn_gdr_chunk_workspace(B, H, T, d, d, 1)), dtype=torch.uint8,
+    wsg = torch.empty(int(dn.lib().dn_gdr_chunk_workspace(B, H, T, d, d, 1, 64)), dtype=torch.uint8,
                       device=dev)
     timed("gdr_chunk_fwd", lambda: dn.gdr_chunk_fwd(*gargs, None, o=o, S_final=S, workspace=wsg),
           {"workspace_bytes": wsg.numel()})
     timed("gdr_recurrent_fwd", lambda: dn.gdr_recurrent_fwd(*gargs, None))
     del xg, gargs, wsg
+    # chunk-length sweep of the chunked generalized rule at T = 4096 (16 heads,
+    # d = 128): the per-chunk triangular work grows with the length, the number
+    # of sequential chunk steps falls with it
+    Bs_, Hs_, Ts_ = 1, 16, 4096
+    xs = to_dev(synthetic.make_gdr(Bs_, Hs_, Ts_, d, "bf16", seed=2006))
+    sargs = [xs[n] for n in ("q", "kw", "v", "kr", "a", "g")]
+    os_ = torch.empty(Bs_, Hs_, Ts_, d, dtype=torch.bfloat16, device=dev)
+    Ss_ = torch.empty(Bs_, Hs_, d, d, dtype=torch.float32, device=dev)
+    sweep = {}
+    for ch in (16, 32, 64):
+        wss = torch.empty(int(dn.lib().dn_gdr_chunk_workspace(Bs_, Hs_, Ts_, d, d, 1, ch)),
+                          dtype=torch.uint8, device=dev)
+        run = lambda: dn.gdr_chunk_fwd(*sargs, None, chunk=ch, o=os_, S_final=Ss_, workspace=wss)
+        for _ in range(2):
+            run()
+        sweep[str(ch)] = round(event_time_ms(torch, run, 5), 4)
+        del wss
+    out["gdr_chunk_length_sweep_ms"] = {"B": Bs_, "H": Hs_, "T": Ts_, "d": d, "ms_by_chunk": sweep}
+    log("  serving gdr chunk sweep %s" % sweep)
+    del xs, sargs, os_, Ss_
     del x, ws, o, S, Sc, qg, kg, xp, wsp, op, Sp
     # speculative decode: 4 drafted tokens for the decode workload's 256 x 16
     # states, the state after each kept (4 x 256 MiB of snapshots)

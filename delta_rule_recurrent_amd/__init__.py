@@ -532,12 +532,12 @@ def gdr_recurrent_fwd(q, kw, v, kr, a, g, S0=None, *, output_final_state=True, o
     return o, S_final
 
 
-def gdr_chunk_fwd(q, kw, v, kr, a, g, S0=None, *, output_final_state=True, o=None,
+def gdr_chunk_fwd(q, kw, v, kr, a, g, S0=None, *, chunk=64, output_final_state=True, o=None,
                   S_final=None, workspace=None, stream=None):
-    """Chunked form of gdr_recurrent_fwd (64-token chunks reduced to affine maps
-    of the state, fp32 arithmetic). Same arguments; ``workspace`` (uint8, at
-    least dn_gdr_chunk_workspace bytes) is allocated when not given.
-    Returns (o, S_final)."""
+    """Chunked form of gdr_recurrent_fwd (chunks of ``chunk`` = 16, 32 or 64
+    tokens reduced to affine maps of the state, fp32 arithmetic). Same
+    arguments; ``workspace`` (uint8, at least dn_gdr_chunk_workspace bytes) is
+    allocated when not given. Returns (o, S_final)."""
     if q.dim() != 4:
         raise ValueError("q must be [B,H,T,dk]")
     B, H, T, dk = q.shape
@@ -559,9 +559,11 @@ def gdr_chunk_fwd(q, kw, v, kr, a, g, S0=None, *, output_final_state=True, o=Non
     elif S_final is not None:
         _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
     if workspace is None:
-        workspace = _alloc_workspace(int(lib().dn_gdr_chunk_workspace(B, H, T, dk, dv, _DT[dt])), dev)
+        workspace = _alloc_workspace(
+            int(lib().dn_gdr_chunk_workspace(B, H, T, dk, dv, _DT[dt], int(chunk))), dev)
     st = lib().dn_gdr_chunk_fwd(_ptr(q), _ptr(kw), _ptr(v), _ptr(kr), _ptr(a), _ptr(g), _ptr(S0),
-                                _ptr(o), _ptr(S_final), B, H, T, dk, dv, _DT[dt], _ptr(workspace),
+                                _ptr(o), _ptr(S_final), B, H, T, dk, dv, _DT[dt], int(chunk),
+                                _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), _stream(stream))
     _lib.check("dn_gdr_chunk_fwd", st)
     return o, S_final

@@ -40,8 +40,8 @@ SIGNATURES = {
     "dn_layer_epilogue": (_i, [_vp] * 4 + [_i] * 4 + [ctypes.c_float, _i, _vp]),
     "dn_gdr_recurrent_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_vp]),
     "dn_gdr_decode_step": (_i, [_vp] * 8 + [_i] * 5 + [_vp]),
-    "dn_gdr_chunk_workspace": (_sz, [_i] * 6),
-    "dn_gdr_chunk_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
+    "dn_gdr_chunk_workspace": (_sz, [_i] * 7),
+    "dn_gdr_chunk_fwd": (_i, [_vp] * 9 + [_i] * 7 + [_vp, _sz, _vp]),
     "dn_chunk_prep": (_i, [_i] + [_vp] * 5 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_chunk_scan": (_i, [_i] + [_vp] * 4 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_recurrent_fwd": (_i, _PREFILL + [_vp]),

@@ -9,10 +9,10 @@
 
 namespace dn {
 // the chunked generalized delta rule (gdr_chunk.hip)
-size_t gdr_chunk_workspace_bytes(long long BH, long long T, int d);
+size_t gdr_chunk_workspace_bytes(long long BH, long long T, int d, int chunk);
 hipError_t launch_gdr_chunk(int dtype, const void* q, const void* kw, const void* v,
                             const void* kr, const void* a, const void* g, const float* S0,
-                            void* o, float* S_final, void* ws, int BH, int T, int d,
+                            void* o, float* S_final, void* ws, int BH, int T, int d, int chunk,
                             hipStream_t st);
 }  // namespace dn
 
@@ -359,30 +359,33 @@ int dn_gdr_recurrent_fwd(const void* q, const void* kw, const void* v, const voi
                                                T, dk, as_stream(stream)));
 }
 
-size_t dn_gdr_chunk_workspace(int B, int H, int T, int dk, int dv, int dtype) {
-    if (B < 1 || H < 1 || T < 1) return 0;
+static bool gdr_chunk_size_ok(int chunk) { return chunk == 16 || chunk == 32 || chunk == 64; }
+
+size_t dn_gdr_chunk_workspace(int B, int H, int T, int dk, int dv, int dtype, int chunk) {
+    if (B < 1 || H < 1 || T < 1 || !gdr_chunk_size_ok(chunk)) return 0;
     if ((dk != 64 && dk != 128) || dk != dv) return 0;
     if (dtype != DN_F32 && dtype != DN_BF16) return 0;
-    return dn::gdr_chunk_workspace_bytes((long long)B * H, T, dk);
+    return dn::gdr_chunk_workspace_bytes((long long)B * H, T, dk, chunk);
 }
 
 int dn_gdr_chunk_fwd(const void* q, const void* kw, const void* v, const void* kr, const void* a,
                      const void* g, const float* S0, void* o, float* S_final, int B, int H, int T,
-                     int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+                     int dk, int dv, int dtype, int chunk, void* workspace,
+                     size_t workspace_bytes, void* stream) {
     const int st = gdr_check(q, kw, v, kr, a, g, S0, o, S_final, B, H, T, dk, dv, dtype);
     if (st != DN_OK) return st;
+    if (!gdr_chunk_size_ok(chunk)) return DN_ENOTSUP;
     const long long BH = (long long)B * H;
     if (T == 0) {
         if (!S_final) return DN_OK;
         return hip_status(dn::launch_state_copy(S0, S_final, BH * dk * dv, as_stream(stream)));
     }
     // every chunk is one workgroup of the map kernels, four of the products
-    if (BH * ((T + 63) / 64) > (1LL << 28)) return DN_EINVAL;
-    const size_t need = dn::gdr_chunk_workspace_bytes(BH, T, dk);
+    if (BH * ((T + chunk - 1) / chunk) > (1LL << 28)) return DN_EINVAL;
+    const size_t need = dn::gdr_chunk_workspace_bytes(BH, T, dk, chunk);
     if (!workspace || workspace_bytes < need || misaligned(workspace, 256)) return DN_EWORKSPACE;
     return hip_status(dn::launch_gdr_chunk(dtype, q, kw, v, kr, a, g, S0, o, S_final, workspace,
-                                           (int)BH, T, dk, as_stream(stream)));
+                                           (int)BH, T, dk, chunk, as_stream(stream)));
 }
 
 int dn_gdr_decode_step(const void* q, const void* kw, const void* v, const void* kr,

@@ -3,7 +3,7 @@
 // The transition S_t = (diag(w_t) - (a_t * kr_t) kr_t^T) S_{t-1} + kw_t v_t^T
 // (page "DeltaNet: Memory That Edits", section "The generalized delta rule";
 // the pages give no chunked form, so it is derived here). Within a chunk of
-// C = 64 tokens, with G_t the running sum of g = log w (G_{-1} = 0) and
+// C tokens (16, 32 or 64), with G_t the running sum of g = log w (G_{-1} = 0) and
 // l = a * kr, the removal read-outs z_s = kr_s^T S_{s-1} obey the unit
 // lower-triangular system
 //     (I + M) Z = R^ S_0 + N V,
@@ -29,36 +29,38 @@
 namespace dn {
 namespace {
 
-constexpr int GC = 64;   // chunk length
+// Chunk lengths this path is built for (template parameter C below).
+constexpr bool gdr_chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
 
-// Per-chunk workspace, in floats, for head size D.
-template <int D>
+// Per-chunk workspace, in floats, for head size D and chunk length C.
+template <int D, int C>
 struct GdrWs {
     static constexpr long G = 0;                 // running log-decay [C][D]
-    static constexpr long R = G + GC * D;        // R^ = kr e^{G_{s-1}}
-    static constexpr long L = R + GC * D;        // L~ = a kr e^{G_C - G}
-    static constexpr long K = L + GC * D;        // Kw~ = kw e^{G_C - G}
-    static constexpr long V = K + GC * D;        // v (zero-padded)
-    static constexpr long W = V + GC * D;        // Wz = T R^
-    static constexpr long NV = W + GC * D;       // N V
-    static constexpr long U = NV + GC * D;       // uz = T N V
-    static constexpr long M = U + GC * D;        // M [C][C]
-    static constexpr long N = M + GC * GC;       // N
-    static constexpr long AK = N + GC * GC;      // A_kw
-    static constexpr long AL = AK + GC * GC;     // A_l
-    static constexpr long T = AL + GC * GC;      // (I + M)^-1
-    static constexpr long P = T + GC * GC;       // P [D][D]
+    static constexpr long R = G + C * D;         // R^ = kr e^{G_{s-1}}
+    static constexpr long L = R + C * D;         // L~ = a kr e^{G_C - G}
+    static constexpr long K = L + C * D;         // Kw~ = kw e^{G_C - G}
+    static constexpr long V = K + C * D;         // v (zero-padded)
+    static constexpr long W = V + C * D;         // Wz = T R^
+    static constexpr long NV = W + C * D;        // N V
+    static constexpr long U = NV + C * D;        // uz = T N V
+    static constexpr long M = U + C * D;         // M [C][C]
+    static constexpr long N = M + C * C;         // N
+    static constexpr long AK = N + C * C;        // A_kw
+    static constexpr long AL = AK + C * C;       // A_l
+    static constexpr long T = AL + C * C;        // (I + M)^-1
+    static constexpr long P = T + C * C;         // P [D][D]
     static constexpr long SH = P + (long)D * D;  // Sh [D][D]
     static constexpr long QP = SH + (long)D * D; // Qp [C][D] (Q^ until the product)
-    static constexpr long OH = QP + GC * D;      // Oh [C][D]
-    static constexpr long FLOATS = OH + GC * D;  // a multiple of 64 floats (256 bytes)
+    static constexpr long OH = QP + C * D;       // Oh [C][D]
+    static constexpr long FLOATS = OH + C * D;   // a multiple of 64 floats (256 bytes)
+    static_assert(FLOATS % 64 == 0, "256-byte blocks");
 };
 
 // ---- 1. elementwise: G, R^, L~, Kw~, V, Q^ (into the Qp slot), P = diag(e^{G_C}).
 //         g is staged in LDS and summed there over tokens (one thread per
 //         channel); every other output is then written by all threads, rows
 //         of consecutive channels, reading the running sums from LDS.
-template <typename E, int D>
+template <typename E, int D, int C>
 __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
                                                        const E* __restrict__ kw,
                                                        const E* __restrict__ v,
@@ -66,33 +68,33 @@ __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
                                                        const E* __restrict__ a,
                                                        const E* __restrict__ g,
                                                        float* __restrict__ ws, int T, int nchunks) {
-    typedef GdrWs<D> Ws;
-    __shared__ float sG[GC][D + 1];
+    typedef GdrWs<D, C> Ws;
+    __shared__ float sG[C][D + 1];
     const long item = blockIdx.x;
     const long bh = item / nchunks;
     const int c = (int)(item % nchunks);
-    const int L = min(GC, T - c * GC);
+    const int L = min(C, T - c * C);
     float* w = ws + item * Ws::FLOATS;
-    const long row0 = bh * T + (long)c * GC;
+    const long row0 = bh * T + (long)c * C;
     const int tid = threadIdx.x;
-    for (int e = tid; e < GC * D; e += 256) {
+    for (int e = tid; e < C * D; e += 256) {
         const int t = e / D, ch = e % D;
         sG[t][ch] = t < L ? to_f32(g[(row0 + t) * D + ch]) : 0.f;
     }
     __syncthreads();
     if (tid < D) {
         float Gr = 0.f;
-        for (int t = 0; t < GC; ++t) {
+        for (int t = 0; t < C; ++t) {
             Gr += sG[t][tid];
             sG[t][tid] = Gr;
         }
     }
     __syncthreads();
-    for (int e = tid; e < GC * D; e += 256) {
+    for (int e = tid; e < C * D; e += 256) {
         const int t = e / D, ch = e % D;
         const bool in = t < L;
         const long i = (row0 + t) * D + ch;
-        const float Gt = sG[t][ch], Gm = t > 0 ? sG[t - 1][ch] : 0.f, GCh = sG[GC - 1][ch];
+        const float Gt = sG[t][ch], Gm = t > 0 ? sG[t - 1][ch] : 0.f, GCh = sG[C - 1][ch];
         const float dec = __expf(GCh - Gt);
         const float krv = in ? to_f32(kr[i]) : 0.f;
         w[Ws::G + e] = Gt;
@@ -104,37 +106,39 @@ __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
     }
     for (int e = tid; e < D * D; e += 256) {
         const int r = e / D, cc = e % D;
-        w[Ws::P + e] = r == cc ? __expf(sG[GC - 1][r]) : 0.f;
+        w[Ws::P + e] = r == cc ? __expf(sG[C - 1][r]) : 0.f;
     }
 }
 
 // ---- 2. the decay-weighted contractions M, N (j < s) and A_kw, A_l (j <= s),
-//         over the key channels in blocks of 32 staged in LDS. Thread: row s =
-//         tid / 4, columns j = tid % 4 + 4 jj.
-template <typename E, int D>
+//         over the key channels in blocks of 32 staged in LDS. Thread: row
+//         s = tid / TPR, columns j = tid % TPR + TPR jj (TPR = 256 / C threads
+//         per row, C / TPR columns each).
+template <typename E, int D, int C>
 __global__ __launch_bounds__(256) void gdr_pairs_kernel(const E* __restrict__ q,
                                                         const E* __restrict__ kw,
                                                         const E* __restrict__ kr,
                                                         const E* __restrict__ a,
                                                         float* __restrict__ ws, int T, int nchunks) {
-    typedef GdrWs<D> Ws;
+    typedef GdrWs<D, C> Ws;
     constexpr int CB = 32, LD = CB + 1;
-    __shared__ float sG[GC][LD], sKr[GC][LD], sL[GC][LD], sKw[GC][LD], sQ[GC][LD];
+    __shared__ float sG[C][LD], sKr[C][LD], sL[C][LD], sKw[C][LD], sQ[C][LD];
     const long item = blockIdx.x;
     const long bh = item / nchunks;
     const int c = (int)(item % nchunks);
-    const int L = min(GC, T - c * GC);
+    const int L = min(C, T - c * C);
     float* w = ws + item * Ws::FLOATS;
-    const long row0 = bh * T + (long)c * GC;
+    const long row0 = bh * T + (long)c * C;
     const int tid = threadIdx.x;
-    const int s = tid >> 2, jg = tid & 3;
-    float m[16], n[16], ak[16], al[16];
+    constexpr int TPR = 256 / C, CPT = C / TPR;
+    const int s = tid / TPR, jg = tid % TPR;
+    float m[CPT], n[CPT], ak[CPT], al[CPT];
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) m[jj] = n[jj] = ak[jj] = al[jj] = 0.f;
+    for (int jj = 0; jj < CPT; ++jj) m[jj] = n[jj] = ak[jj] = al[jj] = 0.f;
 
     for (int c0 = 0; c0 < D; c0 += CB) {
         __syncthreads();   // the previous block's reads are done
-        for (int e = tid; e < GC * CB; e += 256) {
+        for (int e = tid; e < C * CB; e += 256) {
             const int t = e / CB, ch = e % CB;
             const bool in = t < L;
             const long i = (row0 + t) * D + c0 + ch;
@@ -152,8 +156,8 @@ __global__ __launch_bounds__(256) void gdr_pairs_kernel(const E* __restrict__ q,
             // e^{G_s - G_j} = e^{G_{s-1} - G_j} e^{g_s}: one exponential per pair
             const float egq = __expf(Gs - Gm) * qs;
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int j = jg + 4 * jj;
+            for (int jj = 0; jj < CPT; ++jj) {
+                const int j = jg + TPR * jj;
                 const float lj = sL[j][ch], kj = sKw[j][ch];
                 if (j < s) {
                     const float e = __expf(Gm - sG[j][ch]);
@@ -170,48 +174,50 @@ __global__ __launch_bounds__(256) void gdr_pairs_kernel(const E* __restrict__ q,
         }
     }
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-        const int j = jg + 4 * jj;
-        w[Ws::M + s * GC + j] = m[jj];
-        w[Ws::N + s * GC + j] = n[jj];
-        w[Ws::AK + s * GC + j] = ak[jj];
-        w[Ws::AL + s * GC + j] = al[jj];
+    for (int jj = 0; jj < CPT; ++jj) {
+        const int j = jg + TPR * jj;
+        w[Ws::M + s * C + j] = m[jj];
+        w[Ws::N + s * C + j] = n[jj];
+        w[Ws::AK + s * C + j] = ak[jj];
+        w[Ws::AL + s * C + j] = al[jj];
     }
 }
 
 // ---- 3. T = (I + M)^-1 by forward substitution; lane j computes column j:
 //         T_ij = [i == j] - sum_{m < i} M_im T_mj (M strictly lower, so T_ij = 0 for i < j).
-template <int D>
+template <int D, int C>
 __global__ __launch_bounds__(WAVE) void gdr_tinv_kernel(float* __restrict__ ws) {
-    typedef GdrWs<D> Ws;
-    __shared__ float sM[GC][GC + 1];
-    __shared__ float sT[GC][GC + 1];
+    typedef GdrWs<D, C> Ws;
+    __shared__ float sM[C][C + 1];
+    __shared__ float sT[C][C + 1];
     float* w = ws + (long)blockIdx.x * Ws::FLOATS;
     const int j = threadIdx.x;
-    for (int i = 0; i < GC; ++i) sM[i][j] = w[Ws::M + i * GC + j];
+    for (int i = 0; i < C; ++i) sM[i][j] = w[Ws::M + i * C + j];
     __syncthreads();
-    for (int i = 0; i < GC; ++i) {
+    for (int i = 0; i < C; ++i) {
         float acc = 0.f;
         for (int m = 0; m < i; ++m) acc += sM[i][m] * sT[m][j];
         sT[i][j] = (i == j ? 1.f : 0.f) - acc;
     }
-    for (int i = 0; i < GC; ++i) w[Ws::T + i * GC + j] = sT[i][j];
+    for (int i = 0; i < C; ++i) w[Ws::T + i * C + j] = sT[i][j];
 }
 
 // ---- 4. batched fp32 product inside every chunk's workspace:
-//         C = alpha op(A) B + beta C, op(A) = A or A^T; op(A) (M x 64), B
-//         (64 x N), C (M x N), row-major with the given leading dimensions.
-//         Every product here contracts over the 64 tokens of a chunk. A
-//         workgroup stages its op(A) rows and B columns (64 x 64 each) in LDS
-//         and computes a 64 x 64 tile on the fp32 matrix cores: wave w the rows
-//         16w .. 16w + 15, four 16-column tiles. M and N are multiples of 64.
-__global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, long stride, int tm,
-                                                       int tn, long offA, int lda, int transA,
-                                                       long offB, int ldb, long offC, int ldc,
-                                                       float alpha, float beta) {
-    constexpr int KK = GC;
-    __shared__ __align__(16) float As[64][KK + 4];   // op(A) rows: As[m][k]
-    __shared__ float Bs[KK][64 + 1];                 // Bs[k][n]
+//         C = alpha op(A) B + beta C, op(A) = A or A^T; op(A) (M x KK), B
+//         (KK x N), C (M x N), row-major with the given leading dimensions.
+//         Every product here contracts over the KK tokens of a chunk. A
+//         workgroup stages its op(A) rows and B columns in LDS (the contraction
+//         zero-padded to a multiple of 32) and computes a 64 x 64 tile on the
+//         fp32 matrix cores: wave w the rows 16w .. 16w + 15 (when they exist:
+//         M is a multiple of 16), four 16-column tiles. N is a multiple of 64.
+template <int KK>
+__global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, long stride, int M,
+                                                       int tm, int tn, long offA, int lda,
+                                                       int transA, long offB, int ldb, long offC,
+                                                       int ldc, float alpha, float beta) {
+    constexpr int KP = (KK + 31) / 32 * 32;
+    __shared__ __align__(16) float As[64][KP + 4];   // op(A) rows: As[m][k]
+    __shared__ float Bs[KP][64 + 1];                 // Bs[k][n]
     // block = (chunk item, output tile row, output tile column)
     const long tiles = (long)tm * tn;
     const long item = blockIdx.x / tiles;
@@ -221,30 +227,40 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
     const float* B = w + offB;
     float* Cm = w + offC;
     const int m0 = (tile / tn) * 64, n0 = (tile % tn) * 64;
+    const int rows = min(64, M - m0);
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
     const int gq = lane >> 4, r = lane & 15;
-    // 16 bytes per load (every offset and leading dimension is a multiple of 4 floats)
-    for (int e = tid; e < KK * 16; e += 256) {
-        const int hi = e / 16, lo = (e % 16) * 4;
-        const f32x4 bv = *reinterpret_cast<const f32x4*>(B + (long)hi * ldb + n0 + lo);
+    // 16 bytes per load (every offset and leading dimension is a multiple of 4
+    // floats); rows and contraction indices past the operands read as zero
+    for (int e = tid; e < KP * 16; e += 256) {
+        const int k = e / 16, c4 = (e % 16) * 4;
+        f32x4 bv = zero4();
+        if (k < KK) bv = *reinterpret_cast<const f32x4*>(B + (long)k * ldb + n0 + c4);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) Bs[hi][lo + u] = bv[u];
+        for (int u = 0; u < 4; ++u) Bs[k][c4 + u] = bv[u];
         if (transA) {
-            // A^T: columns m0 + lo .. of A are rows of op(A)
-            const f32x4 av = *reinterpret_cast<const f32x4*>(A + (long)hi * lda + m0 + lo);
+            // A^T: A is KK x M; columns m0 + c4 .. of A are rows of op(A)
+            f32x4 av = zero4();
+            if (k < KK && c4 < rows) av = *reinterpret_cast<const f32x4*>(A + (long)k * lda + m0 + c4);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) As[lo + u][hi] = av[u];
-        } else {
-            *reinterpret_cast<f32x4*>(&As[hi][lo]) =
-                *reinterpret_cast<const f32x4*>(A + (long)(m0 + hi) * lda + lo);
+            for (int u = 0; u < 4; ++u) As[c4 + u][k] = av[u];
+        }
+    }
+    if (!transA) {
+        for (int e = tid; e < 64 * (KP / 4); e += 256) {
+            const int mr = e / (KP / 4), k4 = (e % (KP / 4)) * 4;
+            f32x4 av = zero4();
+            if (mr < rows && k4 < KK) av = *reinterpret_cast<const f32x4*>(A + (long)(m0 + mr) * lda + k4);
+            *reinterpret_cast<f32x4*>(&As[mr][k4]) = av;
         }
     }
     __syncthreads();
+    if (16 * wv >= rows) return;   // (no barrier follows)
     f32x4 acc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) acc[ct] = zero4();
 #pragma unroll
-    for (int kb = 0; kb < KK / 32; ++kb) {
+    for (int kb = 0; kb < KP / 32; ++kb) {
         f32x8 af;   // row 16 wv + r at contraction indices 4gq .. 4gq + 3, 16 + 4gq .. 16 + 4gq + 3
         const f32x4 lo4 = *reinterpret_cast<const f32x4*>(&As[16 * wv + r][32 * kb + 4 * gq]);
         const f32x4 hi4 = *reinterpret_cast<const f32x4*>(&As[16 * wv + r][32 * kb + 16 + 4 * gq]);
@@ -272,15 +288,15 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
 //         columns) applies the maps chunk after chunk on the fp32 matrix cores
 //         (the fragment convention of dn_device.h). Wave w owns S rows
 //         32w .. 32w + 31 (d = 128; 16w .. 16w + 15 at d = 64) and read-out rows
-//         16w .. 16w + 15 as 16 x 16 accumulator tiles. Per chunk: the A-fragments
+//         16w .. 16w + 15 (those below C) as 16 x 16 accumulator tiles. Per chunk: the A-fragments
 //         of P and Qp are loaded straight from the workspace (they do not depend
 //         on S), S goes through LDS once to become B-fragments, and
 //         S <- P S + Sh, O = Qp S + Oh accumulate from the Sh and Oh tiles.
-template <typename E, int D>
+template <typename E, int D, int C>
 __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __restrict__ ws,
                                                              const float* S0, E* __restrict__ o,
                                                              float* S_final, int T, int nchunks) {
-    typedef GdrWs<D> Ws;
+    typedef GdrWs<D, C> Ws;
     constexpr int NB = 32;          // value columns per workgroup (two 16-column tiles)
     constexpr int RTW = D / 64;     // 16-row tiles of S per wavefront
     constexpr int KB = D / 32;      // 32-wide blocks of the contraction over key channels
@@ -289,6 +305,7 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
     const int n0 = (int)(blockIdx.x % (D / NB)) * NB;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int gq = lane >> 4, r = lane & 15;
+    const bool ORW = 16 * w < C;   // this wavefront holds read-out rows
 
     f32x4 S[RTW][2];
 #pragma unroll
@@ -303,7 +320,7 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 
     for (int c = 0; c < nchunks; ++c) {
         const float* wc = ws + (bh * nchunks + c) * Ws::FLOATS;
-        const int L = min(GC, T - c * GC);
+        const int L = min(C, T - c * C);
         // A-fragments: lane (gq, r) holds row r of the tile at contraction
         // indices 4gq .. 4gq + 3 and 16 + 4gq .. 16 + 4gq + 3 of each 32-block
         f32x8 pa[RTW][KB], qa[KB];
@@ -317,7 +334,9 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 #pragma unroll
                 for (int j = 0; j < 4; ++j) { pa[rt][kb][j] = lo[j]; pa[rt][kb][4 + j] = hi[j]; }
             }
-            const float* src = wc + Ws::QP + (long)(16 * w + r) * D + 32 * kb + 4 * gq;
+            // (read-out rows exist for the first C / 16 wavefronts; the others
+            // read row 0, whose products they never store)
+            const float* src = wc + Ws::QP + (long)(ORW ? 16 * w + r : 0) * D + 32 * kb + 4 * gq;
             const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
             const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
 #pragma unroll
@@ -331,7 +350,7 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 #pragma unroll
                 for (int rt = 0; rt < RTW; ++rt)
                     sn[rt][ct][i] = wc[Ws::SH + (long)(16 * (RTW * w + rt) + 4 * gq + i) * D + n0 + 16 * ct + r];
-                oa[ct][i] = wc[Ws::OH + (long)(16 * w + 4 * gq + i) * D + n0 + 16 * ct + r];
+                oa[ct][i] = ORW ? wc[Ws::OH + (long)(16 * w + 4 * gq + i) * D + n0 + 16 * ct + r] : 0.f;
             }
         }
         __syncthreads();   // every B-fragment read of the previous S is done
@@ -359,7 +378,7 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int t = 16 * w + 4 * gq + i;
-                if (t < L) o[(bh * T + (long)c * GC + t) * D + n0 + 16 * ct + r] = from_f32<E>(oa[ct][i]);
+                if (ORW && t < L) o[(bh * T + (long)c * C + t) * D + n0 + 16 * ct + r] = from_f32<E>(oa[ct][i]);
             }
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
@@ -379,69 +398,84 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
     }
 }
 
-// (every product contracts over the chunk's 64 tokens: K == GC)
-template <int D>
-hipError_t gemm(float* ws, long items, int M, int N, int K, long offA, int lda, int transA,
-                long offB, int ldb, long offC, int ldc, float alpha, float beta, hipStream_t st) {
-    if (K != GC || M % 64 || N % 64) return hipErrorInvalidValue;
-    const int tm = M / 64, tn = N / 64;
-    gdr_gemm_kernel<<<(unsigned)(items * tm * tn), 256, 0, st>>>(ws, GdrWs<D>::FLOATS, tm, tn,
-                                                                 offA, lda, transA, offB, ldb,
-                                                                 offC, ldc, alpha, beta);
+template <int D, int C>
+hipError_t gemm(float* ws, long items, int M, int N, long offA, int lda, int transA, long offB,
+                int ldb, long offC, int ldc, float alpha, float beta, hipStream_t st) {
+    if (M % 16 || N % 64) return hipErrorInvalidValue;
+    const int tm = (M + 63) / 64, tn = N / 64;
+    gdr_gemm_kernel<C><<<(unsigned)(items * tm * tn), 256, 0, st>>>(ws, GdrWs<D, C>::FLOATS, M, tm,
+                                                                    tn, offA, lda, transA, offB,
+                                                                    ldb, offC, ldc, alpha, beta);
     return hipGetLastError();
 }
 
-template <typename E, int D>
+template <typename E, int D, int C>
 hipError_t gdr_chunk_t(const void* q, const void* kw, const void* v, const void* kr,
                        const void* a, const void* g, const float* S0, void* o, float* S_final,
                        void* wsv, int BH, int T, hipStream_t st) {
-    typedef GdrWs<D> Ws;
-    const int nchunks = (T + GC - 1) / GC;
+    typedef GdrWs<D, C> Ws;
+    const int nchunks = (T + C - 1) / C;
     const long items = (long)BH * nchunks;
     float* ws = static_cast<float*>(wsv);
     hipError_t e;
-    gdr_elem_kernel<E, D><<<(unsigned)items, 256, 0, st>>>(
+    gdr_elem_kernel<E, D, C><<<(unsigned)items, 256, 0, st>>>(
         (const E*)q, (const E*)kw, (const E*)v, (const E*)kr, (const E*)a, (const E*)g, ws, T, nchunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    gdr_pairs_kernel<E, D><<<(unsigned)items, 256, 0, st>>>((const E*)q, (const E*)kw, (const E*)kr,
-                                                            (const E*)a, ws, T, nchunks);
+    gdr_pairs_kernel<E, D, C><<<(unsigned)items, 256, 0, st>>>((const E*)q, (const E*)kw, (const E*)kr,
+                                                               (const E*)a, ws, T, nchunks);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    gdr_tinv_kernel<D><<<(unsigned)items, WAVE, 0, st>>>(ws);
+    gdr_tinv_kernel<D, C><<<(unsigned)items, C, 0, st>>>(ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // Wz = T R^, NV = N V, uz = T NV                       (C x D each)
-    if ((e = gemm<D>(ws, items, GC, D, GC, Ws::T, GC, 0, Ws::R, D, Ws::W, D, 1.f, 0.f, st))) return e;
-    if ((e = gemm<D>(ws, items, GC, D, GC, Ws::N, GC, 0, Ws::V, D, Ws::NV, D, 1.f, 0.f, st))) return e;
-    if ((e = gemm<D>(ws, items, GC, D, GC, Ws::T, GC, 0, Ws::NV, D, Ws::U, D, 1.f, 0.f, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, Ws::T, C, 0, Ws::R, D, Ws::W, D, 1.f, 0.f, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, Ws::N, C, 0, Ws::V, D, Ws::NV, D, 1.f, 0.f, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, Ws::T, C, 0, Ws::NV, D, Ws::U, D, 1.f, 0.f, st))) return e;
     // P = diag(e^{G_C}) - L~^T Wz;  Sh = Kw~^T V - L~^T uz  (D x D)
-    if ((e = gemm<D>(ws, items, D, D, GC, Ws::L, D, 1, Ws::W, D, Ws::P, D, -1.f, 1.f, st))) return e;
-    if ((e = gemm<D>(ws, items, D, D, GC, Ws::K, D, 1, Ws::V, D, Ws::SH, D, 1.f, 0.f, st))) return e;
-    if ((e = gemm<D>(ws, items, D, D, GC, Ws::L, D, 1, Ws::U, D, Ws::SH, D, -1.f, 1.f, st))) return e;
+    if ((e = gemm<D, C>(ws, items, D, D, Ws::L, D, 1, Ws::W, D, Ws::P, D, -1.f, 1.f, st))) return e;
+    if ((e = gemm<D, C>(ws, items, D, D, Ws::K, D, 1, Ws::V, D, Ws::SH, D, 1.f, 0.f, st))) return e;
+    if ((e = gemm<D, C>(ws, items, D, D, Ws::L, D, 1, Ws::U, D, Ws::SH, D, -1.f, 1.f, st))) return e;
     // Qp = Q^ - A_l Wz;  Oh = A_kw V - A_l uz               (C x D)
-    if ((e = gemm<D>(ws, items, GC, D, GC, Ws::AL, GC, 0, Ws::W, D, Ws::QP, D, -1.f, 1.f, st))) return e;
-    if ((e = gemm<D>(ws, items, GC, D, GC, Ws::AK, GC, 0, Ws::V, D, Ws::OH, D, 1.f, 0.f, st))) return e;
-    if ((e = gemm<D>(ws, items, GC, D, GC, Ws::AL, GC, 0, Ws::U, D, Ws::OH, D, -1.f, 1.f, st))) return e;
-    gdr_chunk_scan_kernel<E, D><<<(unsigned)((long)BH * (D / 32)), 256, 0, st>>>(
+    if ((e = gemm<D, C>(ws, items, C, D, Ws::AL, C, 0, Ws::W, D, Ws::QP, D, -1.f, 1.f, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, Ws::AK, C, 0, Ws::V, D, Ws::OH, D, 1.f, 0.f, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, Ws::AL, C, 0, Ws::U, D, Ws::OH, D, -1.f, 1.f, st))) return e;
+    gdr_chunk_scan_kernel<E, D, C><<<(unsigned)((long)BH * (D / 32)), 256, 0, st>>>(
         ws, S0, (E*)o, S_final, T, nchunks);
     return hipGetLastError();
 }
 
+template <typename E, int D>
+hipError_t gdr_chunk_c(int chunk, const void* q, const void* kw, const void* v, const void* kr,
+                       const void* a, const void* g, const float* S0, void* o, float* S_final,
+                       void* ws, int BH, int T, hipStream_t st) {
+    if (chunk == 16) return gdr_chunk_t<E, D, 16>(q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st);
+    if (chunk == 32) return gdr_chunk_t<E, D, 32>(q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st);
+    return gdr_chunk_t<E, D, 64>(q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st);
+}
+
+template <int D>
+long ws_floats(int chunk) {
+    return chunk == 16 ? GdrWs<D, 16>::FLOATS : chunk == 32 ? GdrWs<D, 32>::FLOATS : GdrWs<D, 64>::FLOATS;
+}
+
 }  // namespace
 
-size_t gdr_chunk_workspace_bytes(long long BH, long long T, int d) {
-    const long long nchunks = (T + GC - 1) / GC;
-    const long long per = d == 128 ? GdrWs<128>::FLOATS : GdrWs<64>::FLOATS;
+size_t gdr_chunk_workspace_bytes(long long BH, long long T, int d, int chunk) {
+    if (!gdr_chunk_ok(chunk)) return 0;
+    const long long nchunks = (T + chunk - 1) / chunk;
+    const long long per = d == 128 ? ws_floats<128>(chunk) : ws_floats<64>(chunk);
     return (size_t)(BH * nchunks * per * 4);
 }
 
 hipError_t launch_gdr_chunk(int dtype, const void* q, const void* kw, const void* v,
                             const void* kr, const void* a, const void* g, const float* S0,
-                            void* o, float* S_final, void* ws, int BH, int T, int d,
+                            void* o, float* S_final, void* ws, int BH, int T, int d, int chunk,
                             hipStream_t st) {
+    if (!gdr_chunk_ok(chunk)) return hipErrorNotSupported;
     if (dtype == DT_BF16)
-        return d == 128 ? gdr_chunk_t<bf16, 128>(q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st)
-                        : gdr_chunk_t<bf16, 64>(q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st);
-    return d == 128 ? gdr_chunk_t<float, 128>(q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st)
-                    : gdr_chunk_t<float, 64>(q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st);
+        return d == 128 ? gdr_chunk_c<bf16, 128>(chunk, q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st)
+                        : gdr_chunk_c<bf16, 64>(chunk, q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st);
+    return d == 128 ? gdr_chunk_c<float, 128>(chunk, q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st)
+                    : gdr_chunk_c<float, 64>(chunk, q, kw, v, kr, a, g, S0, o, S_final, ws, BH, T, st);
 }
 
 }  // namespace dn

@@ -390,22 +390,25 @@ int dn_gdr_decode_step(const void* q, const void* kw, const void* v, const void*
 
 /*
  * Chunked form of the generalized delta rule (derived here; the pages give
- * none): every 64-token chunk is reduced to an affine map S <- P S + Sh with
+ * none): every chunk of `chunk` tokens (16, 32 or 64; DN_ENOTSUP otherwise)
+ * is reduced to an affine map S <- P S + Sh with
  * read-outs O = Qp S + Oh, where the chunk's removal read-outs solve a unit
  * lower-triangular system whose entries carry the per-channel decay inside
  * their contraction (all exponents <= 0); the maps are then applied chunk
  * after chunk. Arithmetic is fp32 throughout. Same tensors and rules as
  * dn_gdr_recurrent_fwd, plus a workspace of at least
- * dn_gdr_chunk_workspace(B,H,T,dk,dv,dtype) bytes (256-byte aligned; 528 KiB
- * per (head, chunk) at d = 128; contents unspecified between calls;
- * DN_EWORKSPACE if missing or short). The result equals the token-by-token
- * form up to rounding.
+ * dn_gdr_chunk_workspace(B,H,T,dk,dv,dtype,chunk) bytes (256-byte aligned;
+ * 528 KiB per (head, 64-token chunk) at d = 128; contents unspecified between
+ * calls; DN_EWORKSPACE if missing or short). The chunk length trades the
+ * per-chunk triangular work (quadratic in the length) against the number of
+ * sequential chunk steps; the result equals the token-by-token form up to
+ * rounding for every length.
  */
-size_t dn_gdr_chunk_workspace(int B, int H, int T, int dk, int dv, int dtype);
+size_t dn_gdr_chunk_workspace(int B, int H, int T, int dk, int dv, int dtype, int chunk);
 int dn_gdr_chunk_fwd(const void* q, const void* kw, const void* v, const void* kr, const void* a,
                      const void* g, const float* S0, void* o, float* S_final, int B, int H, int T,
-                     int dk, int dv, int dtype, void* workspace, size_t workspace_bytes,
-                     void* stream);
+                     int dk, int dv, int dtype, int chunk, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

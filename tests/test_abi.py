@@ -418,24 +418,28 @@ def test_gdr_validation(fn):
 def test_gdr_chunk_workspace_and_validation():
     lib = _lib.lib()
     ws = lib.dn_gdr_chunk_workspace
-    assert ws(1, 1, 0, 64, 64, 1) == 0
-    assert ws(1, 1, 64, 96, 96, 1) == 0
-    one = ws(1, 1, 64, 128, 128, 1)
+    assert ws(1, 1, 0, 64, 64, 1, 64) == 0
+    assert ws(1, 1, 64, 96, 96, 1, 64) == 0
+    assert ws(1, 1, 64, 128, 128, 1, 48) == 0                # chunk lengths 16, 32, 64 only
+    one = ws(1, 1, 64, 128, 128, 1, 64)
     assert one > 0 and one % 256 == 0
-    assert ws(2, 3, 65, 128, 128, 1) == 2 * 3 * 2 * one      # per (head, chunk)
+    assert ws(2, 3, 65, 128, 128, 1, 64) == 2 * 3 * 2 * one  # per (head, chunk)
+    assert ws(1, 1, 64, 128, 128, 1, 16) % 256 == 0
+    assert ws(1, 1, 65, 128, 128, 1, 16) == 5 * ws(1, 1, 16, 128, 128, 1, 16)
     args = dict(q=P, kw=P, v=P, kr=P, a=P, g=P, S0=P, o=P, S_final=P, B=1, H=1, T=64, dk=64,
-                dv=64, dtype=1, ws=WS, wsb=1 << 30, stream=None)
+                dv=64, dtype=1, chunk=64, ws=WS, wsb=1 << 30, stream=None)
 
     def call(**kw):
         a = dict(args)
         a.update(kw)
         return lib.dn_gdr_chunk_fwd(*[a[n] for n in ("q", "kw", "v", "kr", "a", "g", "S0", "o",
                                                        "S_final", "B", "H", "T", "dk", "dv",
-                                                       "dtype", "ws", "wsb", "stream")])
+                                                       "dtype", "chunk", "ws", "wsb", "stream")])
     E, W = _lib.DN_EINVAL, _lib.DN_EWORKSPACE
     assert call(kr=None) == E
     assert call(v=MIS) == E
     assert call(dk=96, dv=96) == _lib.DN_ENOTSUP
+    assert call(chunk=128) == _lib.DN_ENOTSUP
     assert call(ws=None) == W
     assert call(wsb=16) == W
     assert call(ws=WS + 128) == W

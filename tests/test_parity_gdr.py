@@ -158,3 +158,18 @@ def test_gdr_chunk_many_heads():
     torch.cuda.synchronize()
     assert rel_err(o1, o2.double().cpu().numpy()) <= 1e-4
     assert rel_err(S1, S2.double().cpu().numpy()) <= 1e-4
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+@pytest.mark.parametrize("dtype,d,T", [("f32", 64, 37), ("bf16", 128, 130), ("f32", 128, 100)])
+def test_gdr_chunk_lengths(chunk, dtype, d, T):
+    """Chunks of 16 and 32 tokens (ragged last chunk) against the oracle's
+    recurrence; the chunk length changes only the rounding."""
+    dn = _dn()
+    say("gdr chunk length", chunk, dtype, d, T)
+    x = synthetic.make_gdr(2, 2, T, d, dtype, seed=840 + chunk + T, s0_std=0.5)
+    dx = to_dev(x)
+    o, S = dn.gdr_chunk_fwd(*(dx[n] for n in NAMES), dx["S0"], chunk=chunk)
+    torch.cuda.synchronize()
+    o_ref, S_ref = ogdr.recurrent(*(x[n] for n in NAMES), x["S0"])
+    assert rel_err(o, o_ref) <= TOL[dtype] and rel_err(S, S_ref) <= TOL[dtype]
