@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the headline prefill (for profiling the other kernels alone)")
+    ap.add_argument("--serving-only", action="store_true",
+                    help="only time the serving forms and variants (for profiling their kernels)")
     ap.add_argument("--layer-only", action="store_true",
                     help="only time the gated layer's prologue / epilogue kernels (for profiling them)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -158,6 +160,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_each_way": n * 4, "copies": 3}), flush=True)
+        return
+
+    if args.serving_only:
+        print(json.dumps({"serving_forms": run_serving(torch, dn, synthetic, to_dev, dev)}), flush=True)
         return
 
     if args.layer_only:
