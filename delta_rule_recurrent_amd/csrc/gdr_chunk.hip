@@ -110,10 +110,24 @@ __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
     }
 }
 
-// ---- 2. the decay-weighted contractions M, N (j < s) and A_kw, A_l (j <= s),
-//         over the key channels in blocks of 32 staged in LDS. Thread: row
-//         s = tid / TPR, columns j = tid % TPR + TPR jj (TPR = 256 / C threads
-//         per row, C / TPR columns each).
+// ---- 2. the decay-weighted contractions M, N (j < s) and A_kw, A_l (j <= s).
+//         Tokens fall into sub-blocks of 16. For s in sub-block I and j in an
+//         earlier sub-block J, with b = 16 I - 1 (the token before sub-block I)
+//         and e = 16 J + 15 (the last token of sub-block J), the decay factors
+//         split per channel into three with exponents <= 0:
+//             e^{G_{s-1} - G_j} = e^{G_{s-1} - G_b} e^{G_b - G_e} e^{G_e - G_j}
+//         (and the same with G_s for the read-out forms). The first depends on
+//         the row only, the last on the column only and the middle on (I, J), so
+//         these 16 x 16 blocks are products of scaled rows over the channels, run
+//         on the fp32 matrix cores: wave w computes one of the four outputs for
+//         every pair of sub-blocks. Pairs inside one sub-block keep one
+//         exponential per pair and channel on the VALU (a factor through a fixed
+//         token could overflow there): thread (sl, jl) of the 16 x 16 grid takes
+//         the pair (sl, jl) of the first half of the diagonal blocks when jl < sl
+//         and the mirrored pair (15 - sl, 15 - jl) of the second half when jl > sl.
+//         The entries j == s (no decay) are dot products per token, summed by the
+//         threads that stage the token. The channels are staged in LDS in blocks
+//         of 16, the next block's inputs loaded while this one is used.
 template <typename E, int D, int C>
 __global__ __launch_bounds__(256) void gdr_pairs_kernel(const E* __restrict__ q,
                                                         const E* __restrict__ kw,
@@ -121,65 +135,214 @@ __global__ __launch_bounds__(256) void gdr_pairs_kernel(const E* __restrict__ q,
                                                         const E* __restrict__ a,
                                                         float* __restrict__ ws, int T, int nchunks) {
     typedef GdrWs<D, C> Ws;
-    constexpr int CB = 32, LD = CB + 1;
-    __shared__ float sG[C][LD], sKr[C][LD], sL[C][LD], sKw[C][LD], sQ[C][LD];
+    typedef typename Vec4<E>::type V4;
+    constexpr int SB = 16, NSB = C / SB, NPAIR = NSB * (NSB - 1) / 2;
+    constexpr int CB = 16, LD = CB + 4;          // channels per block; row stride (16-byte aligned)
+    constexpr int NDIR = (NSB + 1) / 2;          // diagonal blocks taken by the direct pairs
+    constexpr int NLD = C * CB / 4;              // four-channel groups per block
+    static_assert(NLD <= 256, "one group per thread");
+    __shared__ __align__(16) float sG[C][LD], sKr[C][LD], sL[C][LD], sKw[C][LD];
+    __shared__ __align__(16) float sQg[C][LD], sRm[C][LD], sQm[C][LD], sLc[C][LD], sKc[C][LD];
+    __shared__ __align__(16) float sDk[NPAIR > 0 ? NPAIR : 1][CB];
+
     const long item = blockIdx.x;
     const long bh = item / nchunks;
     const int c = (int)(item % nchunks);
     const int L = min(C, T - c * C);
     float* w = ws + item * Ws::FLOATS;
     const long row0 = bh * T + (long)c * C;
-    const int tid = threadIdx.x;
-    constexpr int TPR = 256 / C, CPT = C / TPR;
-    const int s = tid / TPR, jg = tid % TPR;
-    float m[CPT], n[CPT], ak[CPT], al[CPT];
-#pragma unroll
-    for (int jj = 0; jj < CPT; ++jj) m[jj] = n[jj] = ak[jj] = al[jj] = 0.f;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
 
+    // staging role: token lt, channels lc .. lc + 3 of the block
+    const int lt = tid / (CB / 4), lc = 4 * (tid % (CB / 4));
+    const bool lin = tid < NLD && lt < L;
+    const long gi = (row0 + lt) * D + lc;
+    V4 rq, rkw, rkr, ra;
+    f32x4 rg;
+    auto fetch = [&](int c0) {
+        if (tid < NLD) {
+            rg = *reinterpret_cast<const f32x4*>(w + Ws::G + lt * D + c0 + lc);
+            if (lin) {
+                rq = *reinterpret_cast<const V4*>(q + gi + c0);
+                rkw = *reinterpret_cast<const V4*>(kw + gi + c0);
+                rkr = *reinterpret_cast<const V4*>(kr + gi + c0);
+                ra = *reinterpret_cast<const V4*>(a + gi + c0);
+            }
+        }
+    };
+
+    // VALU role
+    const int sl = tid / SB, jl = tid % SB;
+    const bool dgl = sl == jl, mir = jl > sl;
+    int prow[NDIR], pcol[NDIR], prm[NDIR];
+    bool pok[NDIR];
+#pragma unroll
+    for (int v = 0; v < NDIR; ++v) {
+        int I = mir ? NDIR + v : v;
+        pok[v] = !dgl && I < NSB;
+        I = min(I, NSB - 1);
+        prow[v] = SB * I + (mir ? SB - 1 - sl : sl);
+        pcol[v] = SB * I + (mir ? SB - 1 - jl : jl);
+        prm[v] = max(prow[v] - 1, 0);
+    }
+    float m[NDIR], n[NDIR], ak[NDIR], al[NDIR];
+#pragma unroll
+    for (int v = 0; v < NDIR; ++v) m[v] = n[v] = ak[v] = al[v] = 0.f;
+    float dak = 0.f, dal = 0.f;   // A_kw[lt][lt], A_l[lt][lt] (staging role)
+
+    // matrix-core role: wave wv computes M (0), N (1), A_kw (2) or A_l (3)
+    const int fr = lane & 15, fg = lane >> 4;
+    const float(*Aop)[LD] = wv < 2 ? sRm : sQm;
+    const float(*Bop)[LD] = (wv == 0 || wv == 3) ? sLc : sKc;
+    f32x4 acc[NPAIR > 0 ? NPAIR : 1];
+#pragma unroll
+    for (int p = 0; p < NPAIR; ++p) acc[p] = zero4();
+
+    fetch(0);
     for (int c0 = 0; c0 < D; c0 += CB) {
-        __syncthreads();   // the previous block's reads are done
-        for (int e = tid; e < C * CB; e += 256) {
-            const int t = e / CB, ch = e % CB;
-            const bool in = t < L;
-            const long i = (row0 + t) * D + c0 + ch;
-            sG[t][ch] = w[Ws::G + t * D + c0 + ch];
-            const float krv = in ? to_f32(kr[i]) : 0.f;
-            sKr[t][ch] = krv;
-            sL[t][ch] = in ? to_f32(a[i]) * krv : 0.f;
-            sKw[t][ch] = in ? to_f32(kw[i]) : 0.f;
-            sQ[t][ch] = in ? to_f32(q[i]) : 0.f;
+        __syncthreads();   // the previous block's readers are done
+        f32x4 xq = zero4(), xkw = zero4(), xkr = zero4(), xl = zero4();
+        if (tid < NLD) {
+            if (lin) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xq[i] = to_f32(rq[i]);
+                    xkw[i] = to_f32(rkw[i]);
+                    xkr[i] = to_f32(rkr[i]);
+                    xl[i] = to_f32(ra[i]) * xkr[i];
+                }
+            }
+            *reinterpret_cast<f32x4*>(&sG[lt][lc]) = rg;
+            *reinterpret_cast<f32x4*>(&sKw[lt][lc]) = xkw;
+            *reinterpret_cast<f32x4*>(&sKr[lt][lc]) = xkr;
+            *reinterpret_cast<f32x4*>(&sL[lt][lc]) = xl;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                dak += xq[i] * xkw[i];
+                dal += xq[i] * xl[i];
+            }
+        }
+        if (c0 + CB < D) fetch(c0 + CB);
+        __syncthreads();
+        // scaled rows (exponents <= 0): q e^{g}, and the factors through the sub-block ends
+        if (tid < NLD) {
+            const int I = lt / SB;
+            const f32x4 Gt = *reinterpret_cast<const f32x4*>(&sG[lt][lc]);
+            const f32x4 Gm = lt > 0 ? *reinterpret_cast<const f32x4*>(&sG[lt - 1][lc]) : zero4();
+            const f32x4 Gb = I > 0 ? *reinterpret_cast<const f32x4*>(&sG[SB * I - 1][lc]) : zero4();
+            const f32x4 Ge = *reinterpret_cast<const f32x4*>(&sG[SB * I + SB - 1][lc]);
+            f32x4 qg, rm, qm, lcv, kcv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                qg[i] = xq[i] * __expf(Gt[i] - Gm[i]);
+                rm[i] = xkr[i] * __expf(Gm[i] - Gb[i]);
+                qm[i] = xq[i] * __expf(Gt[i] - Gb[i]);
+                const float dec = __expf(Ge[i] - Gt[i]);
+                lcv[i] = xl[i] * dec;
+                kcv[i] = xkw[i] * dec;
+            }
+            *reinterpret_cast<f32x4*>(&sQg[lt][lc]) = qg;
+            *reinterpret_cast<f32x4*>(&sRm[lt][lc]) = rm;
+            *reinterpret_cast<f32x4*>(&sQm[lt][lc]) = qm;
+            *reinterpret_cast<f32x4*>(&sLc[lt][lc]) = lcv;
+            *reinterpret_cast<f32x4*>(&sKc[lt][lc]) = kcv;
+        }
+        if (NPAIR > 0 && tid < NPAIR * CB) {
+            // e^{G_b - G_e} of the pair of sub-blocks (I, J), J < I
+            const int p = tid / CB, ch = tid % CB;
+            int I = 1, J = p;
+            while (J >= I) {
+                J -= I;
+                ++I;
+            }
+            sDk[p][ch] = __expf(sG[SB * I - 1][ch] - sG[SB * J + SB - 1][ch]);
         }
         __syncthreads();
-        for (int ch = 0; ch < CB; ++ch) {
-            const float Gs = sG[s][ch], Gm = s > 0 ? sG[s - 1][ch] : 0.f;
-            const float krs = sKr[s][ch], qs = sQ[s][ch];
-            // e^{G_s - G_j} = e^{G_{s-1} - G_j} e^{g_s}: one exponential per pair
-            const float egq = __expf(Gs - Gm) * qs;
+
+        // pairs inside a sub-block
+#pragma unroll 1
+        for (int c4 = 0; c4 < CB; c4 += 4) {
 #pragma unroll
-            for (int jj = 0; jj < CPT; ++jj) {
-                const int j = jg + TPR * jj;
-                const float lj = sL[j][ch], kj = sKw[j][ch];
-                if (j < s) {
-                    const float e = __expf(Gm - sG[j][ch]);
-                    const float e1 = e * krs, e2 = e * egq;
-                    m[jj] += e1 * lj;
-                    n[jj] += e1 * kj;
-                    ak[jj] += e2 * kj;
-                    al[jj] += e2 * lj;
-                } else if (j == s) {
-                    ak[jj] += qs * kj;
-                    al[jj] += qs * lj;
+            for (int v = 0; v < NDIR; ++v) {
+                const f32x4 gm = *reinterpret_cast<const f32x4*>(&sG[prm[v]][c4]);
+                const f32x4 gj = *reinterpret_cast<const f32x4*>(&sG[pcol[v]][c4]);
+                const f32x4 xr = *reinterpret_cast<const f32x4*>(&sKr[prow[v]][c4]);
+                const f32x4 xg = *reinterpret_cast<const f32x4*>(&sQg[prow[v]][c4]);
+                const f32x4 xl = *reinterpret_cast<const f32x4*>(&sL[pcol[v]][c4]);
+                const f32x4 xk = *reinterpret_cast<const f32x4*>(&sKw[pcol[v]][c4]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float e = __expf(gm[i] - gj[i]);
+                    const float e1 = e * xr[i], e2 = e * xg[i];
+                    m[v] += e1 * xl[i];
+                    n[v] += e1 * xk[i];
+                    ak[v] += e2 * xk[i];
+                    al[v] += e2 * xl[i];
                 }
             }
         }
-    }
+        // pairs across sub-blocks: lane (fg, fr) supplies channel 4 fg + i of
+        // row fr to the i-th 16 x 16 x 4 product
 #pragma unroll
-    for (int jj = 0; jj < CPT; ++jj) {
-        const int j = jg + TPR * jj;
-        w[Ws::M + s * C + j] = m[jj];
-        w[Ws::N + s * C + j] = n[jj];
-        w[Ws::AK + s * C + j] = ak[jj];
-        w[Ws::AL + s * C + j] = al[jj];
+        for (int p = 0, I = 1, J = 0; p < NPAIR; ++p) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(&Aop[SB * I + fr][4 * fg]);
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bop[SB * J + fr][4 * fg]) *
+                             *reinterpret_cast<const f32x4*>(&sDk[p][4 * fg]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                acc[p] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[i], bv[i], acc[p], 0, 0, 0);
+            if (++J == I) {
+                J = 0;
+                ++I;
+            }
+        }
+    }
+
+    float* const out[4] = {w + Ws::M, w + Ws::N, w + Ws::AK, w + Ws::AL};
+    // diagonal blocks (every entry written: values below the diagonal, zeros above)
+#pragma unroll
+    for (int v = 0; v < NDIR; ++v) {
+        if (pok[v]) {
+            const int at = prow[v] * C + pcol[v];
+            out[0][at] = m[v];
+            out[1][at] = n[v];
+            out[2][at] = ak[v];
+            out[3][at] = al[v];
+        }
+    }
+    if (mir) {
+#pragma unroll
+        for (int I = 0; I < NSB; ++I) {
+            const int at = (SB * I + sl) * C + SB * I + jl;
+            out[0][at] = out[1][at] = out[2][at] = out[3][at] = 0.f;
+        }
+    }
+    // the entries j == s: the four staging threads of token lt hold a quarter
+    // of its channels each (adjacent lanes)
+#pragma unroll
+    for (int off = 1; off < CB / 4; off <<= 1) {
+        dak += __shfl_xor(dak, off, WAVE);
+        dal += __shfl_xor(dal, off, WAVE);
+    }
+    if (tid < NLD && lc == 0) {
+        const int at = lt * (C + 1);
+        out[0][at] = out[1][at] = 0.f;
+        out[2][at] = dak;
+        out[3][at] = dal;
+    }
+    // blocks across sub-blocks: the product below the diagonal, zeros above
+    float* const o = w + (wv == 0 ? Ws::M : wv == 1 ? Ws::N : wv == 2 ? Ws::AK : Ws::AL);
+#pragma unroll
+    for (int p = 0, I = 1, J = 0; p < NPAIR; ++p) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[(SB * I + 4 * fg + i) * C + SB * J + fr] = acc[p][i];
+            o[(SB * J + 4 * fg + i) * C + SB * I + fr] = 0.f;
+        }
+        if (++J == I) {
+            J = 0;
+            ++I;
+        }
     }
 }
 
