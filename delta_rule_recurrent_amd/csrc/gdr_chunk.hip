@@ -56,7 +56,7 @@ struct GdrWs {
     static_assert(FLOATS % 64 == 0, "256-byte blocks");
 };
 
-// ---- 1. elementwise: G, R^, L~, Kw~, V, Q^ (into the Qp slot), P = diag(e^{G_C}).
+// ---- 1. elementwise: G, R^, L~, Kw~, V, Q^ (into the Qp slot).
 //         g is staged in LDS and summed there over tokens (one thread per
 //         channel); every other output is then written by all threads, rows
 //         of consecutive channels, reading the running sums from LDS.
@@ -103,10 +103,6 @@ __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
         w[Ws::L + e] = in ? to_f32(a[i]) * krv * dec : 0.f;
         w[Ws::K + e] = in ? to_f32(kw[i]) * dec : 0.f;
         w[Ws::QP + e] = in ? to_f32(q[i]) * __expf(Gt) : 0.f;
-    }
-    for (int e = tid; e < D * D; e += 256) {
-        const int r = e / D, cc = e % D;
-        w[Ws::P + e] = r == cc ? __expf(sG[C - 1][r]) : 0.f;
     }
 }
 
@@ -366,18 +362,28 @@ __global__ __launch_bounds__(WAVE) void gdr_tinv_kernel(float* __restrict__ ws) 
 }
 
 // ---- 4. batched fp32 product inside every chunk's workspace:
-//         C = alpha op(A) B + beta C, op(A) = A or A^T; op(A) (M x KK), B
-//         (KK x N), C (M x N), row-major with the given leading dimensions.
-//         Every product here contracts over the KK tokens of a chunk. A
-//         workgroup stages its op(A) rows and B columns in LDS (the contraction
-//         zero-padded to a multiple of 32) and computes a 64 x 64 tile on the
+//         C = sum over one or two terms of alpha op(A) B  (+ beta C)  (+ diag(e^x)),
+//         op(A) = A or A^T; op(A) (M x KK), B (KK x N), C (M x N), row-major
+//         with the given leading dimensions; x (optional) is a length-M vector
+//         whose exponentials are added on the diagonal. Every product here
+//         contracts over the KK tokens of a chunk. A workgroup stages each
+//         term's op(A) rows (times alpha) and B columns in LDS (the contraction
+//         zero-padded to a multiple of 32) and accumulates a 64 x 64 tile on the
 //         fp32 matrix cores: wave w the rows 16w .. 16w + 15 (when they exist:
 //         M is a multiple of 16), four 16-column tiles. N is a multiple of 64.
+struct GemmTerm {
+    long offA;
+    int lda, transA;
+    long offB;
+    int ldb;
+    float alpha;
+};
+
 template <int KK>
 __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, long stride, int M,
-                                                       int tm, int tn, long offA, int lda,
-                                                       int transA, long offB, int ldb, long offC,
-                                                       int ldc, float alpha, float beta) {
+                                                       int tm, int tn, GemmTerm t0, GemmTerm t1,
+                                                       int nterms, long offC, int ldc, float beta,
+                                                       long offDiag) {
     constexpr int KP = (KK + 31) / 32 * 32;
     __shared__ __align__(16) float As[64][KP + 4];   // op(A) rows: As[m][k]
     __shared__ float Bs[KP][64 + 1];                 // Bs[k][n]
@@ -386,64 +392,81 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
     const long item = blockIdx.x / tiles;
     const int tile = (int)(blockIdx.x % tiles);
     float* w = ws + item * stride;
-    const float* A = w + offA;
-    const float* B = w + offB;
     float* Cm = w + offC;
     const int m0 = (tile / tn) * 64, n0 = (tile % tn) * 64;
     const int rows = min(64, M - m0);
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), wv = tid / WAVE;
     const int gq = lane >> 4, r = lane & 15;
-    // 16 bytes per load (every offset and leading dimension is a multiple of 4
-    // floats); rows and contraction indices past the operands read as zero
-    for (int e = tid; e < KP * 16; e += 256) {
-        const int k = e / 16, c4 = (e % 16) * 4;
-        f32x4 bv = zero4();
-        if (k < KK) bv = *reinterpret_cast<const f32x4*>(B + (long)k * ldb + n0 + c4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) Bs[k][c4 + u] = bv[u];
-        if (transA) {
-            // A^T: A is KK x M; columns m0 + c4 .. of A are rows of op(A)
-            f32x4 av = zero4();
-            if (k < KK && c4 < rows) av = *reinterpret_cast<const f32x4*>(A + (long)k * lda + m0 + c4);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) As[c4 + u][k] = av[u];
-        }
-    }
-    if (!transA) {
-        for (int e = tid; e < 64 * (KP / 4); e += 256) {
-            const int mr = e / (KP / 4), k4 = (e % (KP / 4)) * 4;
-            f32x4 av = zero4();
-            if (mr < rows && k4 < KK) av = *reinterpret_cast<const f32x4*>(A + (long)(m0 + mr) * lda + k4);
-            *reinterpret_cast<f32x4*>(&As[mr][k4]) = av;
-        }
-    }
-    __syncthreads();
-    if (16 * wv >= rows) return;   // (no barrier follows)
+    const bool active = 16 * wv < rows;
     f32x4 acc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) acc[ct] = zero4();
+
+    for (int term = 0; term < nterms; ++term) {
+        const GemmTerm t = term == 0 ? t0 : t1;
+        const float* A = w + t.offA;
+        const float* B = w + t.offB;
+        if (term > 0) __syncthreads();   // the previous term's readers are done
+        // 16 bytes per load (every offset and leading dimension is a multiple of
+        // 4 floats); rows and contraction indices past the operands read as zero
+        for (int e = tid; e < KP * 16; e += 256) {
+            const int k = e / 16, c4 = (e % 16) * 4;
+            f32x4 bv = zero4();
+            if (k < KK) bv = *reinterpret_cast<const f32x4*>(B + (long)k * t.ldb + n0 + c4);
 #pragma unroll
-    for (int kb = 0; kb < KP / 32; ++kb) {
-        f32x8 af;   // row 16 wv + r at contraction indices 4gq .. 4gq + 3, 16 + 4gq .. 16 + 4gq + 3
-        const f32x4 lo4 = *reinterpret_cast<const f32x4*>(&As[16 * wv + r][32 * kb + 4 * gq]);
-        const f32x4 hi4 = *reinterpret_cast<const f32x4*>(&As[16 * wv + r][32 * kb + 16 + 4 * gq]);
+            for (int u = 0; u < 4; ++u) Bs[k][c4 + u] = bv[u];
+            if (t.transA) {
+                // A^T: A is KK x M; columns m0 + c4 .. of A are rows of op(A)
+                f32x4 av = zero4();
+                if (k < KK && c4 < rows)
+                    av = *reinterpret_cast<const f32x4*>(A + (long)k * t.lda + m0 + c4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { af[j] = lo4[j]; af[4 + j] = hi4[j]; }
+                for (int u = 0; u < 4; ++u) As[c4 + u][k] = t.alpha * av[u];
+            }
+        }
+        if (!t.transA) {
+            for (int e = tid; e < 64 * (KP / 4); e += 256) {
+                const int mr = e / (KP / 4), k4 = (e % (KP / 4)) * 4;
+                f32x4 av = zero4();
+                if (mr < rows && k4 < KK)
+                    av = *reinterpret_cast<const f32x4*>(A + (long)(m0 + mr) * t.lda + k4);
+                *reinterpret_cast<f32x4*>(&As[mr][k4]) = t.alpha * av;
+            }
+        }
+        __syncthreads();
+        if (active) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-            f32x8 bf;
+            for (int kb = 0; kb < KP / 32; ++kb) {
+                f32x8 af;   // row 16 wv + r at contraction indices 4gq .. 4gq + 3, 16 + 4gq .. 16 + 4gq + 3
+                const f32x4 lo4 = *reinterpret_cast<const f32x4*>(&As[16 * wv + r][32 * kb + 4 * gq]);
+                const f32x4 hi4 = *reinterpret_cast<const f32x4*>(&As[16 * wv + r][32 * kb + 16 + 4 * gq]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                bf[j] = Bs[32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + j - 4)][16 * ct + r];
-            acc[ct] = mma(af, bf, acc[ct]);
+                for (int j = 0; j < 4; ++j) {
+                    af[j] = lo4[j];
+                    af[4 + j] = hi4[j];
+                }
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct) {
+                    f32x8 bf;
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        bf[j] = Bs[32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + j - 4)][16 * ct + r];
+                    acc[ct] = mma(af, bf, acc[ct]);
+                }
+            }
         }
     }
+    if (!active) return;
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float* dst = Cm + (long)(m0 + 16 * wv + 4 * gq + i) * ldc + n0 + 16 * ct + r;
-            *dst = alpha * acc[ct][i] + (beta != 0.f ? beta * *dst : 0.f);
+            const int row = m0 + 16 * wv + 4 * gq + i, col = n0 + 16 * ct + r;
+            float* dst = Cm + (long)row * ldc + col;
+            float val = acc[ct][i];
+            if (beta != 0.f) val += beta * *dst;
+            if (offDiag >= 0 && row == col) val += __expf(w[offDiag + row]);
+            *dst = val;
         }
 }
 
@@ -562,13 +585,12 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 }
 
 template <int D, int C>
-hipError_t gemm(float* ws, long items, int M, int N, long offA, int lda, int transA, long offB,
-                int ldb, long offC, int ldc, float alpha, float beta, hipStream_t st) {
+hipError_t gemm(float* ws, long items, int M, int N, GemmTerm t0, const GemmTerm* t1, long offC,
+                int ldc, float beta, long offDiag, hipStream_t st) {
     if (M % 16 || N % 64) return hipErrorInvalidValue;
     const int tm = (M + 63) / 64, tn = N / 64;
-    gdr_gemm_kernel<C><<<(unsigned)(items * tm * tn), 256, 0, st>>>(ws, GdrWs<D, C>::FLOATS, M, tm,
-                                                                    tn, offA, lda, transA, offB,
-                                                                    ldb, offC, ldc, alpha, beta);
+    gdr_gemm_kernel<C><<<(unsigned)(items * tm * tn), 256, 0, st>>>(
+        ws, GdrWs<D, C>::FLOATS, M, tm, tn, t0, t1 ? *t1 : t0, t1 ? 2 : 1, offC, ldc, beta, offDiag);
     return hipGetLastError();
 }
 
@@ -590,17 +612,22 @@ hipError_t gdr_chunk_t(const void* q, const void* kw, const void* v, const void*
     gdr_tinv_kernel<D, C><<<(unsigned)items, C, 0, st>>>(ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // Wz = T R^, NV = N V, uz = T NV                       (C x D each)
-    if ((e = gemm<D, C>(ws, items, C, D, Ws::T, C, 0, Ws::R, D, Ws::W, D, 1.f, 0.f, st))) return e;
-    if ((e = gemm<D, C>(ws, items, C, D, Ws::N, C, 0, Ws::V, D, Ws::NV, D, 1.f, 0.f, st))) return e;
-    if ((e = gemm<D, C>(ws, items, C, D, Ws::T, C, 0, Ws::NV, D, Ws::U, D, 1.f, 0.f, st))) return e;
+    const GemmTerm tWz{Ws::T, C, 0, Ws::R, D, 1.f}, tNV{Ws::N, C, 0, Ws::V, D, 1.f};
+    const GemmTerm tuz{Ws::T, C, 0, Ws::NV, D, 1.f};
+    if ((e = gemm<D, C>(ws, items, C, D, tWz, nullptr, Ws::W, D, 0.f, -1, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, tNV, nullptr, Ws::NV, D, 0.f, -1, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, tuz, nullptr, Ws::U, D, 0.f, -1, st))) return e;
     // P = diag(e^{G_C}) - L~^T Wz;  Sh = Kw~^T V - L~^T uz  (D x D)
-    if ((e = gemm<D, C>(ws, items, D, D, Ws::L, D, 1, Ws::W, D, Ws::P, D, -1.f, 1.f, st))) return e;
-    if ((e = gemm<D, C>(ws, items, D, D, Ws::K, D, 1, Ws::V, D, Ws::SH, D, 1.f, 0.f, st))) return e;
-    if ((e = gemm<D, C>(ws, items, D, D, Ws::L, D, 1, Ws::U, D, Ws::SH, D, -1.f, 1.f, st))) return e;
-    // Qp = Q^ - A_l Wz;  Oh = A_kw V - A_l uz               (C x D)
-    if ((e = gemm<D, C>(ws, items, C, D, Ws::AL, C, 0, Ws::W, D, Ws::QP, D, -1.f, 1.f, st))) return e;
-    if ((e = gemm<D, C>(ws, items, C, D, Ws::AK, C, 0, Ws::V, D, Ws::OH, D, 1.f, 0.f, st))) return e;
-    if ((e = gemm<D, C>(ws, items, C, D, Ws::AL, C, 0, Ws::U, D, Ws::OH, D, -1.f, 1.f, st))) return e;
+    const GemmTerm tP{Ws::L, D, 1, Ws::W, D, -1.f};
+    const GemmTerm tSh0{Ws::K, D, 1, Ws::V, D, 1.f}, tSh1{Ws::L, D, 1, Ws::U, D, -1.f};
+    if ((e = gemm<D, C>(ws, items, D, D, tP, nullptr, Ws::P, D, 0.f, Ws::G + (long)(C - 1) * D, st)))
+        return e;
+    if ((e = gemm<D, C>(ws, items, D, D, tSh0, &tSh1, Ws::SH, D, 0.f, -1, st))) return e;
+    // Qp = Q^ - A_l Wz (Q^ already in place);  Oh = A_kw V - A_l uz   (C x D)
+    const GemmTerm tQp{Ws::AL, C, 0, Ws::W, D, -1.f};
+    const GemmTerm tOh0{Ws::AK, C, 0, Ws::V, D, 1.f}, tOh1{Ws::AL, C, 0, Ws::U, D, -1.f};
+    if ((e = gemm<D, C>(ws, items, C, D, tQp, nullptr, Ws::QP, D, 1.f, -1, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, tOh0, &tOh1, Ws::OH, D, 0.f, -1, st))) return e;
     gdr_chunk_scan_kernel<E, D, C><<<(unsigned)((long)BH * (D / 32)), 256, 0, st>>>(
         ws, S0, (E*)o, S_final, T, nchunks);
     return hipGetLastError();
