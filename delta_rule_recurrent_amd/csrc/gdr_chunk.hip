@@ -470,117 +470,163 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
         }
 }
 
-// ---- 5. the scan: one workgroup (four wavefronts) per (head, 32 value
+// ---- 5. the scan: one workgroup (four wavefronts) per (head, 16 value
 //         columns) applies the maps chunk after chunk on the fp32 matrix cores
 //         (the fragment convention of dn_device.h). Wave w owns S rows
 //         32w .. 32w + 31 (d = 128; 16w .. 16w + 15 at d = 64) and read-out rows
 //         16w .. 16w + 15 (those below C) as 16 x 16 accumulator tiles. Per chunk: the A-fragments
 //         of P and Qp are loaded straight from the workspace (they do not depend
-//         on S), S goes through LDS once to become B-fragments, and
-//         S <- P S + Sh, O = Qp S + Oh accumulate from the Sh and Oh tiles.
+//         on S), one chunk ahead; S goes through LDS once to become B-fragments,
+//         and S <- P S + Sh, O = Qp S + Oh accumulate from the Sh and Oh tiles.
+//         When the number of heads is a multiple of 8, the column tiles of a head
+//         run on one XCD (workgroup b is dealt to XCD b mod 8) and share its L2.
+template <int D, int C>
+struct GdrScanOps {
+    static constexpr int RTW = D / 64;   // 16-row tiles of S per wavefront
+    static constexpr int KB = D / 32;    // 32-wide blocks of the contraction over key channels
+    f32x8 pa[RTW][KB], qa[KB];           // A-fragments of P and Qp
+    f32x4 sh[RTW], oh;                   // this wavefront's tiles of Sh and Oh
+};
+
+template <int D, int C>
+__device__ __forceinline__ void gdr_scan_load(GdrScanOps<D, C>& x, const float* __restrict__ wc,
+                                              int n0, int w, int gq, int r, bool orw) {
+    typedef GdrWs<D, C> Ws;
+    typedef GdrScanOps<D, C> O;
+    // lane (gq, r) holds row r of the tile at contraction indices 4gq .. 4gq + 3
+    // and 16 + 4gq .. 16 + 4gq + 3 of each 32-block
+#pragma unroll
+    for (int kb = 0; kb < O::KB; ++kb) {
+#pragma unroll
+        for (int rt = 0; rt < O::RTW; ++rt) {
+            const float* src = wc + Ws::P + (long)(16 * (O::RTW * w + rt) + r) * D + 32 * kb + 4 * gq;
+            const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                x.pa[rt][kb][j] = lo[j];
+                x.pa[rt][kb][4 + j] = hi[j];
+            }
+        }
+        // (read-out rows exist for the first C / 16 wavefronts; the others
+        // read row 0, whose products they never store)
+        const float* src = wc + Ws::QP + (long)(orw ? 16 * w + r : 0) * D + 32 * kb + 4 * gq;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x.qa[kb][j] = lo[j];
+            x.qa[kb][4 + j] = hi[j];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int rt = 0; rt < O::RTW; ++rt)
+            x.sh[rt][i] = wc[Ws::SH + (long)(16 * (O::RTW * w + rt) + 4 * gq + i) * D + n0 + r];
+        x.oh[i] = wc[Ws::OH + (long)((orw ? 16 * w : 0) + 4 * gq + i) * D + n0 + r];
+    }
+}
+
+// One element stored through a buffer resource (0x00020000: the gfx9 word for
+// untyped 32-bit-element buffers). The hardware drops a store whose byte
+// offset is at or past the resource's size, so a store that must not happen
+// needs no branch; with every store unconditional the compiler knows how many
+// are in flight and can wait for the loads issued before them alone.
+template <typename E>
+__device__ __forceinline__ void store_ranged(E* base, unsigned bytes, unsigned voff, float x) {
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+    if constexpr (sizeof(E) == 2) {
+        const E h = from_f32<E>(x);
+        unsigned short u;
+        __builtin_memcpy(&u, &h, 2);
+        __builtin_amdgcn_raw_buffer_store_b16(u, rs, (int)voff, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), rs, (int)voff, 0, 0);
+    }
+}
+
 template <typename E, int D, int C>
 __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __restrict__ ws,
                                                              const float* S0, E* __restrict__ o,
                                                              float* S_final, int T, int nchunks) {
     typedef GdrWs<D, C> Ws;
-    constexpr int NB = 32;          // value columns per workgroup (two 16-column tiles)
-    constexpr int RTW = D / 64;     // 16-row tiles of S per wavefront
-    constexpr int KB = D / 32;      // 32-wide blocks of the contraction over key channels
-    __shared__ float sS[D][NB + 1];
-    const long bh = blockIdx.x / (D / NB);
-    const int n0 = (int)(blockIdx.x % (D / NB)) * NB;
+    typedef GdrScanOps<D, C> O;
+    constexpr int NT = D / 16;      // 16-column tiles per head
+    constexpr int RTW = O::RTW, KB = O::KB;
+    __shared__ float sS[D][16 + 1];
+    const long b = blockIdx.x, heads = gridDim.x / NT;
+    long bh;
+    int vt;
+    if (heads % 8 == 0) {
+        bh = b % 8 + 8 * ((b / 8) / NT);
+        vt = (int)((b / 8) % NT);
+    } else {
+        bh = b / NT;
+        vt = (int)(b % NT);
+    }
+    const int n0 = 16 * vt;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = tid / WAVE;
     const int gq = lane >> 4, r = lane & 15;
     const bool ORW = 16 * w < C;   // this wavefront holds read-out rows
 
-    f32x4 S[RTW][2];
+    f32x4 S[RTW];
 #pragma unroll
     for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const long row = 16 * (RTW * w + rt) + 4 * gq + i;
-                S[rt][ct][i] = S0 ? S0[(bh * D + row) * D + n0 + 16 * ct + r] : 0.f;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const long row = 16 * (RTW * w + rt) + 4 * gq + i;
+            S[rt][i] = S0 ? S0[(bh * D + row) * D + n0 + r] : 0.f;
+        }
 
+    const float* wh = ws + bh * nchunks * Ws::FLOATS;
+    // The operands of chunk c + 1 load while chunk c is applied. They are
+    // copied into the working set at the top of the next step, so the
+    // products only ever read registers whose loads have been waited for.
+    O cur, nxt;
+    gdr_scan_load<D, C>(nxt, wh, n0, w, gq, r, ORW);
     for (int c = 0; c < nchunks; ++c) {
-        const float* wc = ws + (bh * nchunks + c) * Ws::FLOATS;
+        cur = nxt;
+        if (c + 1 < nchunks) gdr_scan_load<D, C>(nxt, wh + (long)(c + 1) * Ws::FLOATS, n0, w, gq, r, ORW);
         const int L = min(C, T - c * C);
-        // A-fragments: lane (gq, r) holds row r of the tile at contraction
-        // indices 4gq .. 4gq + 3 and 16 + 4gq .. 16 + 4gq + 3 of each 32-block
-        f32x8 pa[RTW][KB], qa[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-            for (int rt = 0; rt < RTW; ++rt) {
-                const float* src = wc + Ws::P + (long)(16 * (RTW * w + rt) + r) * D + 32 * kb + 4 * gq;
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) { pa[rt][kb][j] = lo[j]; pa[rt][kb][4 + j] = hi[j]; }
-            }
-            // (read-out rows exist for the first C / 16 wavefronts; the others
-            // read row 0, whose products they never store)
-            const float* src = wc + Ws::QP + (long)(ORW ? 16 * w + r : 0) * D + 32 * kb + 4 * gq;
-            const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { qa[kb][j] = lo[j]; qa[kb][4 + j] = hi[j]; }
-        }
-        f32x4 sn[RTW][2], oa[2];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                for (int rt = 0; rt < RTW; ++rt)
-                    sn[rt][ct][i] = wc[Ws::SH + (long)(16 * (RTW * w + rt) + 4 * gq + i) * D + n0 + 16 * ct + r];
-                oa[ct][i] = ORW ? wc[Ws::OH + (long)(16 * w + 4 * gq + i) * D + n0 + 16 * ct + r] : 0.f;
-            }
-        }
         __syncthreads();   // every B-fragment read of the previous S is done
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sS[16 * (RTW * w + rt) + 4 * gq + i][16 * ct + r] = S[rt][ct][i];
+            for (int i = 0; i < 4; ++i) sS[16 * (RTW * w + rt) + 4 * gq + i][r] = S[rt][i];
         __syncthreads();
+        f32x4 sn[RTW], oa = cur.oh;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int rt = 0; rt < RTW; ++rt) sn[rt] = cur.sh[rt];
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                f32x8 sb;   // B-fragment: column r of the tile at the same contraction indices
+        for (int kb = 0; kb < KB; ++kb) {
+            f32x8 sb;   // B-fragment: column r of the tile at the same contraction indices
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    sb[j] = sS[32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + j - 4)][16 * ct + r];
+            for (int j = 0; j < 8; ++j) sb[j] = sS[32 * kb + (j < 4 ? 4 * gq + j : 16 + 4 * gq + j - 4)][r];
 #pragma unroll
-                for (int rt = 0; rt < RTW; ++rt) sn[rt][ct] = mma(pa[rt][kb], sb, sn[rt][ct]);
-                oa[ct] = mma(qa[kb], sb, oa[ct]);
-            }
+            for (int rt = 0; rt < RTW; ++rt) sn[rt] = mma(cur.pa[rt][kb], sb, sn[rt]);
+            oa = mma(cur.qa[kb], sb, oa);
+        }
+        // rows t >= L of the last chunk, and the rows of wavefronts without
+        // read-out rows, fall outside the resource and are not written
+        E* const oc = o + (bh * T + (long)c * C) * D;
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * w + 4 * gq + i;
+            const unsigned off = ORW ? (unsigned)((t * D + n0 + r) * (int)sizeof(E)) : 0x40000000u;
+            store_ranged<E>(oc, (unsigned)(L * D * (int)sizeof(E)), off, oa[i]);
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * w + 4 * gq + i;
-                if (ORW && t < L) o[(bh * T + (long)c * C + t) * D + n0 + 16 * ct + r] = from_f32<E>(oa[ct][i]);
-            }
-#pragma unroll
-        for (int rt = 0; rt < RTW; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) S[rt][ct] = sn[rt][ct];
+        for (int rt = 0; rt < RTW; ++rt) S[rt] = sn[rt];
     }
     if (S_final) {
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const long row = 16 * (RTW * w + rt) + 4 * gq + i;
-                    S_final[(bh * D + row) * D + n0 + 16 * ct + r] = S[rt][ct][i];
-                }
+            for (int i = 0; i < 4; ++i) {
+                const long row = 16 * (RTW * w + rt) + 4 * gq + i;
+                S_final[(bh * D + row) * D + n0 + r] = S[rt][i];
+            }
     }
 }
 
@@ -628,7 +674,7 @@ hipError_t gdr_chunk_t(const void* q, const void* kw, const void* v, const void*
     const GemmTerm tOh0{Ws::AK, C, 0, Ws::V, D, 1.f}, tOh1{Ws::AL, C, 0, Ws::U, D, -1.f};
     if ((e = gemm<D, C>(ws, items, C, D, tQp, nullptr, Ws::QP, D, 1.f, -1, st))) return e;
     if ((e = gemm<D, C>(ws, items, C, D, tOh0, &tOh1, Ws::OH, D, 0.f, -1, st))) return e;
-    gdr_chunk_scan_kernel<E, D, C><<<(unsigned)((long)BH * (D / 32)), 256, 0, st>>>(
+    gdr_chunk_scan_kernel<E, D, C><<<(unsigned)((long)BH * (D / 16)), 256, 0, st>>>(
         ws, S0, (E*)o, S_final, T, nchunks);
     return hipGetLastError();
 }
