@@ -41,8 +41,7 @@ struct GdrWs {
     static constexpr long K = L + C * D;         // Kw~ = kw e^{G_C - G}
     static constexpr long V = K + C * D;         // v (zero-padded)
     static constexpr long W = V + C * D;         // Wz = T R^
-    static constexpr long NV = W + C * D;        // N V
-    static constexpr long U = NV + C * D;        // uz = T N V
+    static constexpr long U = W + C * D;         // uz = T N V
     static constexpr long M = U + C * D;         // M [C][C]
     static constexpr long N = M + C * C;         // N
     static constexpr long AK = N + C * C;        // A_kw
@@ -56,10 +55,12 @@ struct GdrWs {
     static_assert(FLOATS % 64 == 0, "256-byte blocks");
 };
 
-// ---- 1. elementwise: G, R^, L~, Kw~, V, Q^ (into the Qp slot).
-//         g is staged in LDS and summed there over tokens (one thread per
-//         channel); every other output is then written by all threads, rows
-//         of consecutive channels, reading the running sums from LDS.
+// ---- 1. elementwise: G, R^, L~, Kw~, V, Q^ (into the Qp slot). A thread
+//         owns NG groups of four consecutive channels of one token and issues
+//         every input load of its groups before the first is used. g is staged
+//         in LDS and summed there over tokens (one thread per channel, the sum
+//         in a register); the outputs are then written as 16-byte vectors,
+//         reading the running sums from LDS.
 template <typename E, int D, int C>
 __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
                                                        const E* __restrict__ kw,
@@ -69,7 +70,11 @@ __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
                                                        const E* __restrict__ g,
                                                        float* __restrict__ ws, int T, int nchunks) {
     typedef GdrWs<D, C> Ws;
-    __shared__ float sG[C][D + 1];
+    typedef typename Vec4<E>::type V4;
+    constexpr int G4 = D / 4;              // four-channel groups per token
+    constexpr int NG = C * G4 / 256;       // groups per thread
+    static_assert(C * G4 % 256 == 0, "whole groups per thread");
+    __shared__ __align__(16) float sG[C][D + 4];
     const long item = blockIdx.x;
     const long bh = item / nchunks;
     const int c = (int)(item % nchunks);
@@ -77,32 +82,64 @@ __global__ __launch_bounds__(256) void gdr_elem_kernel(const E* __restrict__ q,
     float* w = ws + item * Ws::FLOATS;
     const long row0 = bh * T + (long)c * C;
     const int tid = threadIdx.x;
-    for (int e = tid; e < C * D; e += 256) {
-        const int t = e / D, ch = e % D;
-        sG[t][ch] = t < L ? to_f32(g[(row0 + t) * D + ch]) : 0.f;
+
+    V4 xg[NG], xq[NG], xkw[NG], xkr[NG], xa[NG], xv[NG];
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+        const int gi = tid + 256 * k, t = gi / G4, ch = (gi % G4) * 4;
+        xg[k] = xq[k] = xkw[k] = xkr[k] = xa[k] = xv[k] = V4{};
+        if (t < L) {
+            const long i = (row0 + t) * D + ch;
+            xg[k] = *reinterpret_cast<const V4*>(g + i);
+            xq[k] = *reinterpret_cast<const V4*>(q + i);
+            xkw[k] = *reinterpret_cast<const V4*>(kw + i);
+            xkr[k] = *reinterpret_cast<const V4*>(kr + i);
+            xa[k] = *reinterpret_cast<const V4*>(a + i);
+            xv[k] = *reinterpret_cast<const V4*>(v + i);   // d_v == d_k
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+        const int gi = tid + 256 * k, t = gi / G4, ch = (gi % G4) * 4;
+        f32x4 x;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) x[u] = to_f32(xg[k][u]);
+        *reinterpret_cast<f32x4*>(&sG[t][ch]) = x;
     }
     __syncthreads();
     if (tid < D) {
         float Gr = 0.f;
+#pragma unroll 8
         for (int t = 0; t < C; ++t) {
             Gr += sG[t][tid];
             sG[t][tid] = Gr;
         }
     }
     __syncthreads();
-    for (int e = tid; e < C * D; e += 256) {
-        const int t = e / D, ch = e % D;
-        const bool in = t < L;
-        const long i = (row0 + t) * D + ch;
-        const float Gt = sG[t][ch], Gm = t > 0 ? sG[t - 1][ch] : 0.f, GCh = sG[C - 1][ch];
-        const float dec = __expf(GCh - Gt);
-        const float krv = in ? to_f32(kr[i]) : 0.f;
-        w[Ws::G + e] = Gt;
-        w[Ws::R + e] = krv * __expf(Gm);
-        w[Ws::V + e] = in ? to_f32(v[i]) : 0.f;   // d_v == d_k
-        w[Ws::L + e] = in ? to_f32(a[i]) * krv * dec : 0.f;
-        w[Ws::K + e] = in ? to_f32(kw[i]) * dec : 0.f;
-        w[Ws::QP + e] = in ? to_f32(q[i]) * __expf(Gt) : 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k) {
+        const int gi = tid + 256 * k, t = gi / G4, ch = (gi % G4) * 4;
+        const long e = (long)t * D + ch;
+        const f32x4 Gt = *reinterpret_cast<const f32x4*>(&sG[t][ch]);
+        const f32x4 Gm = t > 0 ? *reinterpret_cast<const f32x4*>(&sG[t - 1][ch]) : zero4();
+        const f32x4 GC = *reinterpret_cast<const f32x4*>(&sG[C - 1][ch]);
+        f32x4 oR, oV, oL, oK, oQ;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float dec = __expf(GC[u] - Gt[u]);
+            const float krv = to_f32(xkr[k][u]);
+            oR[u] = krv * __expf(Gm[u]);
+            oV[u] = to_f32(xv[k][u]);
+            oL[u] = to_f32(xa[k][u]) * krv * dec;
+            oK[u] = to_f32(xkw[k][u]) * dec;
+            oQ[u] = to_f32(xq[k][u]) * __expf(Gt[u]);
+        }
+        *reinterpret_cast<f32x4*>(w + Ws::G + e) = Gt;
+        *reinterpret_cast<f32x4*>(w + Ws::R + e) = oR;
+        *reinterpret_cast<f32x4*>(w + Ws::V + e) = oV;
+        *reinterpret_cast<f32x4*>(w + Ws::L + e) = oL;
+        *reinterpret_cast<f32x4*>(w + Ws::K + e) = oK;
+        *reinterpret_cast<f32x4*>(w + Ws::QP + e) = oQ;
     }
 }
 
@@ -365,7 +402,9 @@ __global__ __launch_bounds__(WAVE) void gdr_tinv_kernel(float* __restrict__ ws) 
 //         C = sum over one or two terms of alpha op(A) B  (+ beta C)  (+ diag(e^x)),
 //         op(A) = A or A^T; op(A) (M x KK), B (KK x N), C (M x N), row-major
 //         with the given leading dimensions; x (optional) is a length-M vector
-//         whose exponentials are added on the diagonal. Every product here
+//         whose exponentials are added on the diagonal. With `chain`, the
+//         second term's B is the first term's result (M == KK <= 64: the
+//         workgroup holds all its rows), kept in LDS. Every product here
 //         contracts over the KK tokens of a chunk. A workgroup stages each
 //         term's op(A) rows (times alpha) and B columns in LDS (the contraction
 //         zero-padded to a multiple of 32) and accumulates a 64 x 64 tile on the
@@ -382,8 +421,8 @@ struct GemmTerm {
 template <int KK>
 __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, long stride, int M,
                                                        int tm, int tn, GemmTerm t0, GemmTerm t1,
-                                                       int nterms, long offC, int ldc, float beta,
-                                                       long offDiag) {
+                                                       int nterms, int chain, long offC, int ldc,
+                                                       float beta, long offDiag) {
     constexpr int KP = (KK + 31) / 32 * 32;
     __shared__ __align__(16) float As[64][KP + 4];   // op(A) rows: As[m][k]
     __shared__ float Bs[KP][64 + 1];                 // Bs[k][n]
@@ -406,15 +445,30 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
         const GemmTerm t = term == 0 ? t0 : t1;
         const float* A = w + t.offA;
         const float* B = w + t.offB;
+        const bool fromAcc = chain && term == 1;
         if (term > 0) __syncthreads();   // the previous term's readers are done
+        if (fromAcc) {
+            // B = the first term's result: rows 16 wv + 4 gq + i (< M = KK), the
+            // other rows keep the zeros staged with the first term
+            if (active) {
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Bs[16 * wv + 4 * gq + i][16 * ct + r] = acc[ct][i];
+            }
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) acc[ct] = zero4();
+        }
         // 16 bytes per load (every offset and leading dimension is a multiple of
         // 4 floats); rows and contraction indices past the operands read as zero
         for (int e = tid; e < KP * 16; e += 256) {
             const int k = e / 16, c4 = (e % 16) * 4;
-            f32x4 bv = zero4();
-            if (k < KK) bv = *reinterpret_cast<const f32x4*>(B + (long)k * t.ldb + n0 + c4);
+            if (!fromAcc) {
+                f32x4 bv = zero4();
+                if (k < KK) bv = *reinterpret_cast<const f32x4*>(B + (long)k * t.ldb + n0 + c4);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) Bs[k][c4 + u] = bv[u];
+                for (int u = 0; u < 4; ++u) Bs[k][c4 + u] = bv[u];
+            }
             if (t.transA) {
                 // A^T: A is KK x M; columns m0 + c4 .. of A are rows of op(A)
                 f32x4 av = zero4();
@@ -632,11 +686,13 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 
 template <int D, int C>
 hipError_t gemm(float* ws, long items, int M, int N, GemmTerm t0, const GemmTerm* t1, long offC,
-                int ldc, float beta, long offDiag, hipStream_t st) {
+                int ldc, float beta, long offDiag, hipStream_t st, bool chain = false) {
     if (M % 16 || N % 64) return hipErrorInvalidValue;
+    if (chain && (!t1 || M != C || M > 64)) return hipErrorInvalidValue;
     const int tm = (M + 63) / 64, tn = N / 64;
     gdr_gemm_kernel<C><<<(unsigned)(items * tm * tn), 256, 0, st>>>(
-        ws, GdrWs<D, C>::FLOATS, M, tm, tn, t0, t1 ? *t1 : t0, t1 ? 2 : 1, offC, ldc, beta, offDiag);
+        ws, GdrWs<D, C>::FLOATS, M, tm, tn, t0, t1 ? *t1 : t0, t1 ? 2 : 1, chain ? 1 : 0, offC, ldc,
+        beta, offDiag);
     return hipGetLastError();
 }
 
@@ -657,12 +713,11 @@ hipError_t gdr_chunk_t(const void* q, const void* kw, const void* v, const void*
     if ((e = hipGetLastError()) != hipSuccess) return e;
     gdr_tinv_kernel<D, C><<<(unsigned)items, C, 0, st>>>(ws);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    // Wz = T R^, NV = N V, uz = T NV                       (C x D each)
+    // Wz = T R^, uz = T (N V)                             (C x D each)
     const GemmTerm tWz{Ws::T, C, 0, Ws::R, D, 1.f}, tNV{Ws::N, C, 0, Ws::V, D, 1.f};
-    const GemmTerm tuz{Ws::T, C, 0, Ws::NV, D, 1.f};
+    const GemmTerm tuz{Ws::T, C, 0, 0, 0, 1.f};   // B: the result of tNV
     if ((e = gemm<D, C>(ws, items, C, D, tWz, nullptr, Ws::W, D, 0.f, -1, st))) return e;
-    if ((e = gemm<D, C>(ws, items, C, D, tNV, nullptr, Ws::NV, D, 0.f, -1, st))) return e;
-    if ((e = gemm<D, C>(ws, items, C, D, tuz, nullptr, Ws::U, D, 0.f, -1, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, tNV, &tuz, Ws::U, D, 0.f, -1, st, true))) return e;
     // P = diag(e^{G_C}) - L~^T Wz;  Sh = Kw~^T V - L~^T uz  (D x D)
     const GemmTerm tP{Ws::L, D, 1, Ws::W, D, -1.f};
     const GemmTerm tSh0{Ws::K, D, 1, Ws::V, D, 1.f}, tSh1{Ws::L, D, 1, Ws::U, D, -1.f};
