@@ -18,11 +18,10 @@
 // <= 0. A short last chunk is padded with zero inputs and g = 0, which leaves
 // every formula exact (padded tokens contribute nothing and decay nothing).
 //
-// This path is built for plain correctness and a bounded cost, not speed: the
-// per-chunk maps are computed by a few simple kernels over a per-chunk fp32
+// The per-chunk maps are computed by a few kernels over a per-chunk fp32
 // workspace (an elementwise pass, the four decay-weighted contractions, the
-// triangular inverse, then tiled fp32 products), and a scan applies the maps
-// chunk after chunk.
+// triangular inverse, then tiled products on the fp32 matrix cores), and a
+// scan applies the maps chunk after chunk, also on the matrix cores.
 #include "dn_device.h"
 #include "dn_launch.h"
 

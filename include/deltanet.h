@@ -398,7 +398,7 @@ int dn_gdr_decode_step(const void* q, const void* kw, const void* v, const void*
  * after chunk. Arithmetic is fp32 throughout. Same tensors and rules as
  * dn_gdr_recurrent_fwd, plus a workspace of at least
  * dn_gdr_chunk_workspace(B,H,T,dk,dv,dtype,chunk) bytes (256-byte aligned;
- * 528 KiB per (head, 64-token chunk) at d = 128; contents unspecified between
+ * 496 KiB per (head, 64-token chunk) at d = 128; contents unspecified between
  * calls; DN_EWORKSPACE if missing or short). The chunk length trades the
  * per-chunk triangular work (quadratic in the length) against the number of
  * sequential chunk steps; the result equals the token-by-token form up to
