@@ -115,15 +115,18 @@ def test_gdr_chunk_matches_oracle(dtype, d, T):
     assert eo <= TOL[dtype] and eS <= TOL[dtype], (eo, eS)
 
 
-def test_gdr_chunk_strong_decay_and_in_place():
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_gdr_chunk_strong_decay_and_in_place(chunk):
     """Decays of -30 per token in a third of the channels (sums far below the
-    fp32 exponent range inside a chunk) stay finite; S_final == S0 in place."""
+    fp32 exponent range inside a chunk, and across its 16-token sub-blocks)
+    stay finite; S_final == S0 in place."""
     dn = _dn()
+    say("gdr chunk strong decay", chunk)
     x = synthetic.make_gdr(1, 2, 150, 64, "f32", seed=812, s0_std=0.5)
     x["g"][..., ::3] = -30.0
     dx = to_dev(x)
     S = dx["S0"].clone()
-    o, S2 = dn.gdr_chunk_fwd(*(dx[n] for n in NAMES), S, S_final=S)
+    o, S2 = dn.gdr_chunk_fwd(*(dx[n] for n in NAMES), S, S_final=S, chunk=chunk)
     torch.cuda.synchronize()
     assert S2 is S
     o_ref, S_ref = ogdr.recurrent(*(x[n] for n in NAMES), x["S0"])
@@ -147,17 +150,39 @@ def test_gdr_chunk_long_sequence():
     assert eo <= TOL["bf16"] and eS <= TOL["bf16"], (eo, eS)
 
 
-def test_gdr_chunk_many_heads():
-    """40 (sequence, head) rows of 3 chunks: the grid and workspace indexing
-    over many heads, against the token-by-token GPU form (fp32, 1e-4)."""
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_gdr_chunk_many_heads(chunk):
+    """40 (sequence, head) rows (a multiple of 8: the scan groups a head's
+    column tiles on one XCD) of a ragged 150 tokens: the grid and workspace
+    indexing over many heads, against the token-by-token GPU form (fp32, 1e-4)."""
     dn = _dn()
+    say("gdr chunk many heads", chunk)
     x = synthetic.make_gdr(5, 8, 150, 64, "f32", seed=830, s0_std=0.5)
     dx = to_dev(x)
-    o1, S1 = dn.gdr_chunk_fwd(*(dx[n] for n in NAMES), dx["S0"])
+    o1, S1 = dn.gdr_chunk_fwd(*(dx[n] for n in NAMES), dx["S0"], chunk=chunk)
     o2, S2 = dn.gdr_recurrent_fwd(*(dx[n] for n in NAMES), dx["S0"])
     torch.cuda.synchronize()
     assert rel_err(o1, o2.double().cpu().numpy()) <= 1e-4
     assert rel_err(S1, S2.double().cpu().numpy()) <= 1e-4
+
+
+def test_gdr_chunk_timed_size():
+    """The size the chunked form is timed at (4 x 8 x 2048 tokens, d = 128,
+    bf16 inputs; 32 heads: the scan's XCD grouping) against the token-by-token
+    GPU form on the same inputs: the final states, both fp32, within 1e-4;
+    the read-outs, both rounded to bf16, within the bf16 bound."""
+    dn = _dn()
+    say("gdr chunk timed size")
+    x = synthetic.make_gdr(4, 8, 2048, 128, "bf16", seed=2005)
+    dx = to_dev(x)
+    o1, S1 = dn.gdr_chunk_fwd(*(dx[n] for n in NAMES), None)
+    o2, S2 = dn.gdr_recurrent_fwd(*(dx[n] for n in NAMES), None)
+    torch.cuda.synchronize()
+    eo = rel_err(o1, o2.double().cpu().numpy())
+    eS = rel_err(S1, S2.double().cpu().numpy())
+    say("  o err %.3g, S err %.3g" % (eo, eS))
+    assert eS <= 1e-4, eS
+    assert eo <= TOL["bf16"], eo
 
 
 @pytest.mark.parametrize("chunk", [16, 32])
