@@ -47,9 +47,9 @@ struct GdrWs {
     static constexpr long AL = AK + C * C;       // A_l
     static constexpr long T = AL + C * C;        // (I + M)^-1
     static constexpr long P = T + C * C;         // P [D][D]
-    static constexpr long SH = P + (long)D * D;  // Sh [D][D]
+    static constexpr long SH = P + (long)D * D;  // Sh [D][D] (fragment order, see the products)
     static constexpr long QP = SH + (long)D * D; // Qp [C][D] (Q^ until the product)
-    static constexpr long OH = QP + C * D;       // Oh [C][D]
+    static constexpr long OH = QP + C * D;       // Oh [C][D] (fragment order)
     static constexpr long FLOATS = OH + C * D;   // a multiple of 64 floats (256 bytes)
     static_assert(FLOATS % 64 == 0, "256-byte blocks");
 };
@@ -403,7 +403,10 @@ __global__ __launch_bounds__(WAVE) void gdr_tinv_kernel(float* __restrict__ ws) 
 //         with the given leading dimensions; x (optional) is a length-M vector
 //         whose exponentials are added on the diagonal. With `chain`, the
 //         second term's B is the first term's result (M == KK <= 64: the
-//         workgroup holds all its rows), kept in LDS. Every product here
+//         workgroup holds all its rows), kept in LDS. With `tiled`, C is
+//         written in fragment order for the scan: 16 x 16 tiles of 256 floats,
+//         tiles row-major, and in a tile lane (g, n) holds rows 4g .. 4g + 3 of
+//         column n (ldc = N; beta 0, no diagonal). Every product here
 //         contracts over the KK tokens of a chunk. A workgroup stages each
 //         term's op(A) rows (times alpha) and B columns in LDS (the contraction
 //         zero-padded to a multiple of 32) and accumulates a 64 x 64 tile on the
@@ -421,7 +424,7 @@ template <int KK>
 __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, long stride, int M,
                                                        int tm, int tn, GemmTerm t0, GemmTerm t1,
                                                        int nterms, int chain, long offC, int ldc,
-                                                       float beta, long offDiag) {
+                                                       int tiled, float beta, long offDiag) {
     constexpr int KP = (KK + 31) / 32 * 32;
     __shared__ __align__(16) float As[64][KP + 4];   // op(A) rows: As[m][k]
     __shared__ float Bs[KP][64 + 1];                 // Bs[k][n]
@@ -510,6 +513,14 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
         }
     }
     if (!active) return;
+    if (tiled) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            const long tile = (long)((m0 >> 4) + wv) * (ldc >> 4) + (n0 >> 4) + ct;
+            *reinterpret_cast<f32x4*>(Cm + tile * 256 + (gq * 16 + r) * 4) = acc[ct];
+        }
+        return;
+    }
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -529,7 +540,7 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
 //         32w .. 32w + 31 (d = 128; 16w .. 16w + 15 at d = 64) and read-out rows
 //         16w .. 16w + 15 (those below C) as 16 x 16 accumulator tiles. Per chunk: the A-fragments
 //         of P and Qp are loaded straight from the workspace (they do not depend
-//         on S), one chunk ahead; S goes through LDS once to become B-fragments,
+//         on S), two chunks ahead; S goes through LDS once to become B-fragments,
 //         and S <- P S + Sh, O = Qp S + Oh accumulate from the Sh and Oh tiles.
 //         When the number of heads is a multiple of 8, the column tiles of a head
 //         run on one XCD (workgroup b is dealt to XCD b mod 8) and share its L2.
@@ -543,7 +554,7 @@ struct GdrScanOps {
 
 template <int D, int C>
 __device__ __forceinline__ void gdr_scan_load(GdrScanOps<D, C>& x, const float* __restrict__ wc,
-                                              int n0, int w, int gq, int r, bool orw) {
+                                              int vt, int w, int gq, int r, bool orw) {
     typedef GdrWs<D, C> Ws;
     typedef GdrScanOps<D, C> O;
     // lane (gq, r) holds row r of the tile at contraction indices 4gq .. 4gq + 3
@@ -572,13 +583,12 @@ __device__ __forceinline__ void gdr_scan_load(GdrScanOps<D, C>& x, const float* 
             x.qa[kb][4 + j] = hi[j];
         }
     }
+    // Sh and Oh are stored in fragment order: one 16-byte load per tile
+    const int fo = (gq * 16 + r) * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int rt = 0; rt < O::RTW; ++rt)
-            x.sh[rt][i] = wc[Ws::SH + (long)(16 * (O::RTW * w + rt) + 4 * gq + i) * D + n0 + r];
-        x.oh[i] = wc[Ws::OH + (long)((orw ? 16 * w : 0) + 4 * gq + i) * D + n0 + r];
-    }
+    for (int rt = 0; rt < O::RTW; ++rt)
+        x.sh[rt] = *reinterpret_cast<const f32x4*>(wc + Ws::SH + ((long)(O::RTW * w + rt) * (D / 16) + vt) * 256 + fo);
+    x.oh = *reinterpret_cast<const f32x4*>(wc + Ws::OH + ((long)(orw ? w : 0) * (D / 16) + vt) * 256 + fo);
 }
 
 // One element stored through a buffer resource (0x00020000: the gfx9 word for
@@ -633,15 +643,12 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
         }
 
     const float* wh = ws + bh * nchunks * Ws::FLOATS;
-    // The operands of chunk c + 1 load while chunk c is applied. They are
-    // copied into the working set at the top of the next step, so the
-    // products only ever read registers whose loads have been waited for.
-    O cur, nxt;
-    gdr_scan_load<D, C>(nxt, wh, n0, w, gq, r, ORW);
-    for (int c = 0; c < nchunks; ++c) {
-        cur = nxt;
-        if (c + 1 < nchunks) gdr_scan_load<D, C>(nxt, wh + (long)(c + 1) * Ws::FLOATS, n0, w, gq, r, ORW);
-        const int L = min(C, T - c * C);
+    // Three register sets rotate: the maps of chunk c + 2 load while chunk c is
+    // applied. The steps are unrolled by three with no exit between them; the
+    // steps past the last chunk load that chunk again, store nothing and keep S.
+    auto step = [&](int c, const O& cur) {
+        const bool valid = c < nchunks;
+        const int L = valid ? min(C, T - c * C) : 0;
         __syncthreads();   // every B-fragment read of the previous S is done
 #pragma unroll
         for (int rt = 0; rt < RTW; ++rt)
@@ -660,8 +667,8 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
             for (int rt = 0; rt < RTW; ++rt) sn[rt] = mma(cur.pa[rt][kb], sb, sn[rt]);
             oa = mma(cur.qa[kb], sb, oa);
         }
-        // rows t >= L of the last chunk, and the rows of wavefronts without
-        // read-out rows, fall outside the resource and are not written
+        // rows t >= L of the last chunk, the rows of wavefronts without read-out
+        // rows and every row of a step past the end fall outside the resource
         E* const oc = o + (bh * T + (long)c * C) * D;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -670,7 +677,22 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
             store_ranged<E>(oc, (unsigned)(L * D * (int)sizeof(E)), off, oa[i]);
         }
 #pragma unroll
-        for (int rt = 0; rt < RTW; ++rt) S[rt] = sn[rt];
+        for (int rt = 0; rt < RTW; ++rt) S[rt] = valid ? sn[rt] : S[rt];
+    };
+    const int last = nchunks - 1;
+    auto load = [&](O& x, int c) {
+        gdr_scan_load<D, C>(x, wh + (long)min(c, last) * Ws::FLOATS, vt, w, gq, r, ORW);
+    };
+    O s0, s1, s2;
+    load(s0, 0);
+    load(s1, 1);
+    for (int c = 0; c < nchunks; c += 3) {
+        load(s2, c + 2);
+        step(c, s0);
+        load(s0, c + 3);
+        step(c + 1, s1);
+        load(s1, c + 4);
+        step(c + 2, s2);
     }
     if (S_final) {
 #pragma unroll
@@ -685,13 +707,15 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 
 template <int D, int C>
 hipError_t gemm(float* ws, long items, int M, int N, GemmTerm t0, const GemmTerm* t1, long offC,
-                int ldc, float beta, long offDiag, hipStream_t st, bool chain = false) {
+                int ldc, float beta, long offDiag, hipStream_t st, bool chain = false,
+                bool tiled = false) {
     if (M % 16 || N % 64) return hipErrorInvalidValue;
     if (chain && (!t1 || M != C || M > 64)) return hipErrorInvalidValue;
+    if (tiled && (ldc != N || beta != 0.f || offDiag >= 0)) return hipErrorInvalidValue;
     const int tm = (M + 63) / 64, tn = N / 64;
     gdr_gemm_kernel<C><<<(unsigned)(items * tm * tn), 256, 0, st>>>(
         ws, GdrWs<D, C>::FLOATS, M, tm, tn, t0, t1 ? *t1 : t0, t1 ? 2 : 1, chain ? 1 : 0, offC, ldc,
-        beta, offDiag);
+        tiled ? 1 : 0, beta, offDiag);
     return hipGetLastError();
 }
 
@@ -722,12 +746,12 @@ hipError_t gdr_chunk_t(const void* q, const void* kw, const void* v, const void*
     const GemmTerm tSh0{Ws::K, D, 1, Ws::V, D, 1.f}, tSh1{Ws::L, D, 1, Ws::U, D, -1.f};
     if ((e = gemm<D, C>(ws, items, D, D, tP, nullptr, Ws::P, D, 0.f, Ws::G + (long)(C - 1) * D, st)))
         return e;
-    if ((e = gemm<D, C>(ws, items, D, D, tSh0, &tSh1, Ws::SH, D, 0.f, -1, st))) return e;
+    if ((e = gemm<D, C>(ws, items, D, D, tSh0, &tSh1, Ws::SH, D, 0.f, -1, st, false, true))) return e;
     // Qp = Q^ - A_l Wz (Q^ already in place);  Oh = A_kw V - A_l uz   (C x D)
     const GemmTerm tQp{Ws::AL, C, 0, Ws::W, D, -1.f};
     const GemmTerm tOh0{Ws::AK, C, 0, Ws::V, D, 1.f}, tOh1{Ws::AL, C, 0, Ws::U, D, -1.f};
     if ((e = gemm<D, C>(ws, items, C, D, tQp, nullptr, Ws::QP, D, 1.f, -1, st))) return e;
-    if ((e = gemm<D, C>(ws, items, C, D, tOh0, &tOh1, Ws::OH, D, 0.f, -1, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, tOh0, &tOh1, Ws::OH, D, 0.f, -1, st, false, true))) return e;
     gdr_chunk_scan_kernel<E, D, C><<<(unsigned)((long)BH * (D / 16)), 256, 0, st>>>(
         ws, S0, (E*)o, S_final, T, nchunks);
     return hipGetLastError();
