@@ -724,6 +724,7 @@ hipError_t gdr_chunk_t(const void* q, const void* kw, const void* v, const void*
                        const void* a, const void* g, const float* S0, void* o, float* S_final,
                        void* wsv, int BH, int T, hipStream_t st) {
     typedef GdrWs<D, C> Ws;
+    if (T <= 0 || BH <= 0) return hipErrorInvalidValue;   // the scan assumes at least one chunk
     const int nchunks = (T + C - 1) / C;
     const long items = (long)BH * nchunks;
     float* ws = static_cast<float*>(wsv);
