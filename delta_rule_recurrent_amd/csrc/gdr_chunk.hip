@@ -380,21 +380,36 @@ __global__ __launch_bounds__(256) void gdr_pairs_kernel(const E* __restrict__ q,
 
 // ---- 3. T = (I + M)^-1 by forward substitution; lane j computes column j:
 //         T_ij = [i == j] - sum_{m < i} M_im T_mj (M strictly lower, so T_ij = 0 for i < j).
+//         The column stays in registers (both loops unrolled); row i of M is read
+//         from LDS as 16-byte vectors, the same address in every lane, and the
+//         sum is split over four accumulators.
 template <int D, int C>
 __global__ __launch_bounds__(WAVE) void gdr_tinv_kernel(float* __restrict__ ws) {
     typedef GdrWs<D, C> Ws;
-    __shared__ float sM[C][C + 1];
-    __shared__ float sT[C][C + 1];
+    __shared__ __align__(16) float sM[C][C + 4];
     float* w = ws + (long)blockIdx.x * Ws::FLOATS;
     const int j = threadIdx.x;
-    for (int i = 0; i < C; ++i) sM[i][j] = w[Ws::M + i * C + j];
-    __syncthreads();
-    for (int i = 0; i < C; ++i) {
-        float acc = 0.f;
-        for (int m = 0; m < i; ++m) acc += sM[i][m] * sT[m][j];
-        sT[i][j] = (i == j ? 1.f : 0.f) - acc;
+    if (j < C) {
+        for (int i = 0; i < C; ++i) sM[i][j] = w[Ws::M + i * C + j];
     }
-    for (int i = 0; i < C; ++i) w[Ws::T + i * C + j] = sT[i][j];
+    __syncthreads();
+    if (j >= C) return;
+    float t[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m4 = 0; m4 < (i & ~3); m4 += 4) {
+            const f32x4 mv = *reinterpret_cast<const f32x4*>(&sM[i][m4]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc[u] += mv[u] * t[m4 + u];
+        }
+#pragma unroll
+        for (int m = i & ~3; m < i; ++m) acc[m & 3] += sM[i][m] * t[m];
+        t[i] = (i == j ? 1.f : 0.f) - ((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    }
+#pragma unroll
+    for (int i = 0; i < C; ++i) w[Ws::T + i * C + j] = t[i];
 }
 
 // ---- 4. batched fp32 product inside every chunk's workspace:
