@@ -46,7 +46,7 @@ struct GdrWs {
     static constexpr long AK = N + C * C;        // A_kw
     static constexpr long AL = AK + C * C;       // A_l
     static constexpr long T = AL + C * C;        // (I + M)^-1
-    static constexpr long P = T + C * C;         // P [D][D]
+    static constexpr long P = T + C * C;         // P [D][D] (A-fragment order, see the products)
     static constexpr long SH = P + (long)D * D;  // Sh [D][D] (fragment order, see the products)
     static constexpr long QP = SH + (long)D * D; // Qp [C][D] (Q^ until the product)
     static constexpr long OH = QP + C * D;       // Oh [C][D] (fragment order)
@@ -418,10 +418,14 @@ __global__ __launch_bounds__(WAVE) void gdr_tinv_kernel(float* __restrict__ ws) 
 //         with the given leading dimensions; x (optional) is a length-M vector
 //         whose exponentials are added on the diagonal. With `chain`, the
 //         second term's B is the first term's result (M == KK <= 64: the
-//         workgroup holds all its rows), kept in LDS. With `tiled`, C is
-//         written in fragment order for the scan: 16 x 16 tiles of 256 floats,
+//         workgroup holds all its rows), kept in LDS. With `tiled` = 1, C is
+//         written in the scan's accumulator order: 16 x 16 tiles of 256 floats,
 //         tiles row-major, and in a tile lane (g, n) holds rows 4g .. 4g + 3 of
-//         column n (ldc = N; beta 0, no diagonal). Every product here
+//         column n (ldc = N; beta 0, no diagonal). With `tiled` = 2, C is written
+//         in the scan's A-fragment order: blocks of 16 rows x 32 columns (512
+//         floats, blocks row-major), in a block first the columns 4g .. 4g + 3 of
+//         row r at (16 g + r) * 4, then the columns 16 + 4g .. at 256 + the same
+//         (ldc = N; beta 0). Every product here
 //         contracts over the KK tokens of a chunk. A workgroup stages each
 //         term's op(A) rows (times alpha) and B columns in LDS (the contraction
 //         zero-padded to a multiple of 32) and accumulates a 64 x 64 tile on the
@@ -528,6 +532,21 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
         }
     }
     if (!active) return;
+    if (tiled == 2) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = m0 + 16 * wv + 4 * gq + i, col = n0 + 16 * ct + r;
+                float val = acc[ct][i];
+                if (offDiag >= 0 && row == col) val += __expf(w[offDiag + row]);
+                const int c = col & 31;
+                const long off = ((long)(row >> 4) * (ldc >> 5) + (col >> 5)) * 512 + (c >> 4) * 256 +
+                                 (((c & 15) >> 2) * 16 + (row & 15)) * 4 + (c & 3);
+                Cm[off] = val;
+            }
+        return;
+    }
     if (tiled) {
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
@@ -578,9 +597,10 @@ __device__ __forceinline__ void gdr_scan_load(GdrScanOps<D, C>& x, const float* 
     for (int kb = 0; kb < O::KB; ++kb) {
 #pragma unroll
         for (int rt = 0; rt < O::RTW; ++rt) {
-            const float* src = wc + Ws::P + (long)(16 * (O::RTW * w + rt) + r) * D + 32 * kb + 4 * gq;
+            // P is stored in A-fragment order: 1 KiB of lo values, then 1 KiB of hi
+            const float* src = wc + Ws::P + ((long)(O::RTW * w + rt) * (D / 32) + kb) * 512 + (gq * 16 + r) * 4;
             const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+            const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 256);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 x.pa[rt][kb][j] = lo[j];
@@ -723,14 +743,14 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 template <int D, int C>
 hipError_t gemm(float* ws, long items, int M, int N, GemmTerm t0, const GemmTerm* t1, long offC,
                 int ldc, float beta, long offDiag, hipStream_t st, bool chain = false,
-                bool tiled = false) {
+                int tiled = 0) {
     if (M % 16 || N % 64) return hipErrorInvalidValue;
     if (chain && (!t1 || M != C || M > 64)) return hipErrorInvalidValue;
-    if (tiled && (ldc != N || beta != 0.f || offDiag >= 0)) return hipErrorInvalidValue;
+    if (tiled && (ldc != N || beta != 0.f || (tiled == 1 && offDiag >= 0))) return hipErrorInvalidValue;
     const int tm = (M + 63) / 64, tn = N / 64;
     gdr_gemm_kernel<C><<<(unsigned)(items * tm * tn), 256, 0, st>>>(
         ws, GdrWs<D, C>::FLOATS, M, tm, tn, t0, t1 ? *t1 : t0, t1 ? 2 : 1, chain ? 1 : 0, offC, ldc,
-        tiled ? 1 : 0, beta, offDiag);
+        tiled, beta, offDiag);
     return hipGetLastError();
 }
 
@@ -760,14 +780,15 @@ hipError_t gdr_chunk_t(const void* q, const void* kw, const void* v, const void*
     // P = diag(e^{G_C}) - L~^T Wz;  Sh = Kw~^T V - L~^T uz  (D x D)
     const GemmTerm tP{Ws::L, D, 1, Ws::W, D, -1.f};
     const GemmTerm tSh0{Ws::K, D, 1, Ws::V, D, 1.f}, tSh1{Ws::L, D, 1, Ws::U, D, -1.f};
-    if ((e = gemm<D, C>(ws, items, D, D, tP, nullptr, Ws::P, D, 0.f, Ws::G + (long)(C - 1) * D, st)))
+    if ((e = gemm<D, C>(ws, items, D, D, tP, nullptr, Ws::P, D, 0.f, Ws::G + (long)(C - 1) * D, st,
+                        false, 2)))
         return e;
-    if ((e = gemm<D, C>(ws, items, D, D, tSh0, &tSh1, Ws::SH, D, 0.f, -1, st, false, true))) return e;
+    if ((e = gemm<D, C>(ws, items, D, D, tSh0, &tSh1, Ws::SH, D, 0.f, -1, st, false, 1))) return e;
     // Qp = Q^ - A_l Wz (Q^ already in place);  Oh = A_kw V - A_l uz   (C x D)
     const GemmTerm tQp{Ws::AL, C, 0, Ws::W, D, -1.f};
     const GemmTerm tOh0{Ws::AK, C, 0, Ws::V, D, 1.f}, tOh1{Ws::AL, C, 0, Ws::U, D, -1.f};
     if ((e = gemm<D, C>(ws, items, C, D, tQp, nullptr, Ws::QP, D, 1.f, -1, st))) return e;
-    if ((e = gemm<D, C>(ws, items, C, D, tOh0, &tOh1, Ws::OH, D, 0.f, -1, st, false, true))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, tOh0, &tOh1, Ws::OH, D, 0.f, -1, st, false, 1))) return e;
     gdr_chunk_scan_kernel<E, D, C><<<(unsigned)((long)BH * (D / 16)), 256, 0, st>>>(
         ws, S0, (E*)o, S_final, T, nchunks);
     return hipGetLastError();
