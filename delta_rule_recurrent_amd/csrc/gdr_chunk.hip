@@ -35,7 +35,7 @@ constexpr bool gdr_chunk_ok(int c) { return c == 16 || c == 32 || c == 64; }
 template <int D, int C>
 struct GdrWs {
     static constexpr long G = 0;                 // running log-decay [C][D]
-    static constexpr long R = G + C * D;         // R^ = kr e^{G_{s-1}}
+    static constexpr long R = G + C * D;         // R^ = kr e^{G_{s-1}}; then Qp (A-fragment order)
     static constexpr long L = R + C * D;         // L~ = a kr e^{G_C - G}
     static constexpr long K = L + C * D;         // Kw~ = kw e^{G_C - G}
     static constexpr long V = K + C * D;         // v (zero-padded)
@@ -48,7 +48,7 @@ struct GdrWs {
     static constexpr long T = AL + C * C;        // (I + M)^-1
     static constexpr long P = T + C * C;         // P [D][D] (A-fragment order, see the products)
     static constexpr long SH = P + (long)D * D;  // Sh [D][D] (fragment order, see the products)
-    static constexpr long QP = SH + (long)D * D; // Qp [C][D] (Q^ until the product)
+    static constexpr long QP = SH + (long)D * D; // Q^ = q e^{G} [C][D]
     static constexpr long OH = QP + C * D;       // Oh [C][D] (fragment order)
     static constexpr long FLOATS = OH + C * D;   // a multiple of 64 floats (256 bytes)
     static_assert(FLOATS % 64 == 0, "256-byte blocks");
@@ -425,7 +425,8 @@ __global__ __launch_bounds__(WAVE) void gdr_tinv_kernel(float* __restrict__ ws) 
 //         in the scan's A-fragment order: blocks of 16 rows x 32 columns (512
 //         floats, blocks row-major), in a block first the columns 4g .. 4g + 3 of
 //         row r at (16 g + r) * 4, then the columns 16 + 4g .. at 256 + the same
-//         (ldc = N; beta 0). Every product here
+//         (ldc = N). The beta term reads C row-major at offBeta when that is
+//         given (a different slot), else C itself. Every product here
 //         contracts over the KK tokens of a chunk. A workgroup stages each
 //         term's op(A) rows (times alpha) and B columns in LDS (the contraction
 //         zero-padded to a multiple of 32) and accumulates a 64 x 64 tile on the
@@ -443,7 +444,8 @@ template <int KK>
 __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, long stride, int M,
                                                        int tm, int tn, GemmTerm t0, GemmTerm t1,
                                                        int nterms, int chain, long offC, int ldc,
-                                                       int tiled, float beta, long offDiag) {
+                                                       int tiled, float beta, long offDiag,
+                                                       long offBeta) {
     constexpr int KP = (KK + 31) / 32 * 32;
     __shared__ __align__(16) float As[64][KP + 4];   // op(A) rows: As[m][k]
     __shared__ float Bs[KP][64 + 1];                 // Bs[k][n]
@@ -539,6 +541,7 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
             for (int i = 0; i < 4; ++i) {
                 const int row = m0 + 16 * wv + 4 * gq + i, col = n0 + 16 * ct + r;
                 float val = acc[ct][i];
+                if (beta != 0.f) val += beta * w[offBeta + (long)row * ldc + col];
                 if (offDiag >= 0 && row == col) val += __expf(w[offDiag + row]);
                 const int c = col & 31;
                 const long off = ((long)(row >> 4) * (ldc >> 5) + (col >> 5)) * 512 + (c >> 4) * 256 +
@@ -562,7 +565,7 @@ __global__ __launch_bounds__(256) void gdr_gemm_kernel(float* __restrict__ ws, l
             const int row = m0 + 16 * wv + 4 * gq + i, col = n0 + 16 * ct + r;
             float* dst = Cm + (long)row * ldc + col;
             float val = acc[ct][i];
-            if (beta != 0.f) val += beta * *dst;
+            if (beta != 0.f) val += beta * (offBeta >= 0 ? w[offBeta + (long)row * ldc + col] : *dst);
             if (offDiag >= 0 && row == col) val += __expf(w[offDiag + row]);
             *dst = val;
         }
@@ -607,11 +610,12 @@ __device__ __forceinline__ void gdr_scan_load(GdrScanOps<D, C>& x, const float* 
                 x.pa[rt][kb][4 + j] = hi[j];
             }
         }
-        // (read-out rows exist for the first C / 16 wavefronts; the others
-        // read row 0, whose products they never store)
-        const float* src = wc + Ws::QP + (long)(orw ? 16 * w + r : 0) * D + 32 * kb + 4 * gq;
+        // Qp in A-fragment order in the slot of R^ (read-out rows exist for the
+        // first C / 16 wavefronts; the others read rows 0 .. 15, whose products
+        // they never store)
+        const float* src = wc + Ws::R + ((long)(orw ? w : 0) * (D / 32) + kb) * 512 + (gq * 16 + r) * 4;
         const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 16);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 256);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             x.qa[kb][j] = lo[j];
@@ -743,14 +747,15 @@ __global__ __launch_bounds__(256) void gdr_chunk_scan_kernel(const float* __rest
 template <int D, int C>
 hipError_t gemm(float* ws, long items, int M, int N, GemmTerm t0, const GemmTerm* t1, long offC,
                 int ldc, float beta, long offDiag, hipStream_t st, bool chain = false,
-                int tiled = 0) {
+                int tiled = 0, long offBeta = -1) {
     if (M % 16 || N % 64) return hipErrorInvalidValue;
     if (chain && (!t1 || M != C || M > 64)) return hipErrorInvalidValue;
-    if (tiled && (ldc != N || beta != 0.f || (tiled == 1 && offDiag >= 0))) return hipErrorInvalidValue;
+    if (tiled && (ldc != N || (tiled == 1 && (beta != 0.f || offDiag >= 0)))) return hipErrorInvalidValue;
+    if (tiled == 2 && beta != 0.f && offBeta < 0) return hipErrorInvalidValue;   // in place would race
     const int tm = (M + 63) / 64, tn = N / 64;
     gdr_gemm_kernel<C><<<(unsigned)(items * tm * tn), 256, 0, st>>>(
         ws, GdrWs<D, C>::FLOATS, M, tm, tn, t0, t1 ? *t1 : t0, t1 ? 2 : 1, chain ? 1 : 0, offC, ldc,
-        tiled, beta, offDiag);
+        tiled, beta, offDiag, offBeta);
     return hipGetLastError();
 }
 
@@ -784,10 +789,11 @@ hipError_t gdr_chunk_t(const void* q, const void* kw, const void* v, const void*
                         false, 2)))
         return e;
     if ((e = gemm<D, C>(ws, items, D, D, tSh0, &tSh1, Ws::SH, D, 0.f, -1, st, false, 1))) return e;
-    // Qp = Q^ - A_l Wz (Q^ already in place);  Oh = A_kw V - A_l uz   (C x D)
+    // Qp = Q^ - A_l Wz, in the scan's fragment order into the slot of R^ (no
+    // longer needed once Wz is formed);  Oh = A_kw V - A_l uz   (C x D)
     const GemmTerm tQp{Ws::AL, C, 0, Ws::W, D, -1.f};
     const GemmTerm tOh0{Ws::AK, C, 0, Ws::V, D, 1.f}, tOh1{Ws::AL, C, 0, Ws::U, D, -1.f};
-    if ((e = gemm<D, C>(ws, items, C, D, tQp, nullptr, Ws::QP, D, 1.f, -1, st))) return e;
+    if ((e = gemm<D, C>(ws, items, C, D, tQp, nullptr, Ws::R, D, 1.f, -1, st, false, 2, Ws::QP))) return e;
     if ((e = gemm<D, C>(ws, items, C, D, tOh0, &tOh1, Ws::OH, D, 0.f, -1, st, false, 1))) return e;
     gdr_chunk_scan_kernel<E, D, C><<<(unsigned)((long)BH * (D / 16)), 256, 0, st>>>(
         ws, S0, (E*)o, S_final, T, nchunks);
