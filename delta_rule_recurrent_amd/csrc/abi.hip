@@ -374,6 +374,12 @@ int dn_gdr_chunk_fwd(const void* q, const void* kw, const void* v, const void* k
                      size_t workspace_bytes, void* stream) {
     const int st = gdr_check(q, kw, v, kr, a, g, S0, o, S_final, B, H, T, dk, dv, dtype);
     if (st != DN_OK) return st;
+    // the chunked form's kernels read q, kw, kr, a and g as vectors of four
+    // elements (8 bytes for bf16, 16 for fp32)
+    const unsigned vsz = dtype == DN_F32 ? 16u : 8u;
+    if (misaligned(q, vsz) || misaligned(kw, vsz) || misaligned(kr, vsz) || misaligned(a, vsz) ||
+        misaligned(g, vsz))
+        return DN_EINVAL;
     if (!gdr_chunk_size_ok(chunk)) return DN_ENOTSUP;
     const long long BH = (long long)B * H;
     if (T == 0) {

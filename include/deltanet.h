@@ -396,7 +396,9 @@ int dn_gdr_decode_step(const void* q, const void* kw, const void* v, const void*
  * lower-triangular system whose entries carry the per-channel decay inside
  * their contraction (all exponents <= 0); the maps are then applied chunk
  * after chunk. Arithmetic is fp32 throughout. Same tensors and rules as
- * dn_gdr_recurrent_fwd, plus a workspace of at least
+ * dn_gdr_recurrent_fwd, except that q, kw, kr, a and g are read as vectors of
+ * four elements and must be aligned to 8 bytes (bf16) or 16 bytes (fp32)
+ * (DN_EINVAL otherwise), plus a workspace of at least
  * dn_gdr_chunk_workspace(B,H,T,dk,dv,dtype,chunk) bytes (256-byte aligned;
  * 496 KiB per (head, 64-token chunk) at d = 128; contents unspecified between
  * calls; DN_EWORKSPACE if missing or short). The chunk length trades the

@@ -443,3 +443,9 @@ def test_gdr_chunk_workspace_and_validation():
     assert call(ws=None) == W
     assert call(wsb=16) == W
     assert call(ws=WS + 128) == W
+    # the chunked form reads q, kw, kr, a and g as 4-element vectors: 8-byte
+    # alignment for bf16, 16-byte for fp32 (an element-aligned pointer is not enough)
+    for name in ("q", "kw", "kr", "a", "g"):
+        assert call(**{name: P + 2}) == E, name               # bf16: 2-byte aligned only
+        assert call(**{name: P + 4, "dtype": 0}) == E, name   # fp32: 4-byte aligned only
+        assert call(**{name: MIS, "dtype": 0}) == E, name     # fp32: 8-byte aligned only
