@@ -154,7 +154,8 @@ __device__ __forceinline__ void tile_store_f32(const TileRegs<E, D>& r, float* r
 }
 
 // KDA: fragment of a row-major [64][ld] token tile (rows = tokens, contraction
-// = key channels) with each value multiplied by exp(sgn * (G[row][c] - G[ref][c])).
+// = key channels) with each value multiplied by exp(sgn * (G[row][c] - G[ref][c]))
+// (callers choose ref and sgn so that the exponent is <= 0).
 // The lane's two runs of 4 channels (4g .. 4g+3 and 16+4g .. 16+4g+3 of the
 // block) are read as vectors: two 4-element reads of M, four 16-byte reads of
 // G (row and reference row; ld, ldg, k0 keep them aligned).
@@ -177,6 +178,47 @@ __device__ __forceinline__ typename Frag<E>::type frag_rows_decay(const E* M, in
     }
     return f;
 }
+
+// KDA, pairs inside one 16-token tile: the fragment of level lv (1..4) of a
+// binary split of the tile's tokens. At level lv the tile is cut into groups of
+// 2^lv tokens; a pair (i > j) belongs to the one level at which i and j share
+// a group but lie in different halves of it. With r the last token of the
+// group's lower half, the decay of such a pair factors exactly as
+//     exp(G_i - G_j) = exp(G_i - G_r) * exp(G_r - G_j),
+// both exponents <= 0. UPPER: rows of the upper halves scaled by
+// exp(G_row - G_r) (the other rows zero); otherwise rows of the lower halves
+// scaled by exp(G_r - G_row). A product of the two gives the level's pairs
+// exactly; its other entries (pairs of different groups) are finite and
+// discarded by the caller.
+template <typename E, bool UPPER>
+__device__ __forceinline__ typename Frag<E>::type frag_rows_level(const E* M, int ld, const float* G,
+                                                                  int ldg, int row0, int k0,
+                                                                  int lane, int lv) {
+    typedef typename Vec4<E>::type V4;
+    const int g = lane >> 4, r = lane & 15;
+    const int sz = 1 << lv, half = sz >> 1;
+    const bool in = UPPER ? ((r & (sz - 1)) >= half) : ((r & (sz - 1)) < half);
+    const int row = row0 + r;
+    const int ref = row0 + (r & ~(sz - 1)) + half - 1;
+    typename Frag<E>::type f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = k0 + 16 * h + 4 * g;
+        const V4 m = *reinterpret_cast<const V4*>(M + row * ld + c);
+        const f32x4 gr = *reinterpret_cast<const f32x4*>(G + row * ldg + c);
+        const f32x4 gf = *reinterpret_cast<const f32x4*>(G + ref * ldg + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float x = UPPER ? gr[j] - gf[j] : gf[j] - gr[j];
+            f[4 * h + j] = from_f32<E>(to_f32(m[j]) * __expf(in ? x : -INFINITY));
+        }
+    }
+    return f;
+}
+
+// The level (1..4) of the binary split that holds the pair of local token
+// indices a > b of one 16-token tile: the highest bit in which they differ.
+__device__ __forceinline__ int pair_level(int a, int b) { return 32 - __clz(a ^ b); }
 
 // fp32 16x16x16 product on the matrix cores, acc += X * Y, with X a 16x16
 // block of a row-major fp32 LDS matrix and Y a 16x16 D-tile held in
@@ -368,22 +410,20 @@ void chunk_prep_kernel(const E* __restrict__ q,
 
     // ---- 2. attn -> A-fragments, Q~ -> A-fragments; raw K K^T kept in registers
     // Wave w owns token tile w: rows i in [16w, 16w+16) of A and of attn.
-    // KDA: the decay exp(G_ic - G_jc) sits inside the contraction, so both
-    // operands are scaled around a reference token ref of the row tile:
-    // k_i exp(G_i - G_ref) and k_j exp(G_ref - G_j). With ref in the middle of
-    // the tile every factor is bounded by the decay over at most 8 tokens.
+    // KDA: the decay exp(G_ic - G_jc) sits inside the contraction, so it is
+    // split between the two operands at a token r with j <= r < i:
+    // k_i exp(G_i - G_r) and k_j exp(G_r - G_j). Every factor is a decay
+    // (exponent <= 0), so nothing overflows whatever the decay's strength:
+    // tiles before the row tile split at their last token, pairs inside the
+    // row tile by the levels of a binary split of its 16 tokens.
     f32x4 sa[4];
     {
         F ka[DK / 32], qa[DK / 32];
-        const int ref = 16 * w + 8;
+        if (!KDA) {
 #pragma unroll
-        for (int kb = 0; kb < DK / 32; ++kb) {
-            if (!KDA) {
+            for (int kb = 0; kb < DK / 32; ++kb) {
                 ka[kb] = frag_rows<E>(Ks, LDK, 16 * w, 32 * kb, lane);
                 qa[kb] = frag_rows<E>(Qs, LDK, 16 * w, 32 * kb, lane);
-            } else {
-                ka[kb] = frag_rows_decay<E>(Ks, LDK, Gk, LDG, 16 * w, 32 * kb, lane, ref, 1.f);
-                qa[kb] = frag_rows_decay<E>(Qs, LDK, Gk, LDG, 16 * w, 32 * kb, lane, ref, 1.f);
             }
         }
         f32x4 at[4];
@@ -391,13 +431,58 @@ void chunk_prep_kernel(const E* __restrict__ q,
         for (int jt = 0; jt < 4; ++jt) {
             sa[jt] = zero4();
             at[jt] = zero4();
-            if (jt <= w) {
+            if (!KDA && jt <= w) {
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
-                    const F kj = KDA ? frag_rows_decay<E>(Ks, LDK, Gk, LDG, 16 * jt, 32 * kb, lane, ref, -1.f)
-                                     : frag_rows<E>(Ks, LDK, 16 * jt, 32 * kb, lane);
+                    const F kj = frag_rows<E>(Ks, LDK, 16 * jt, 32 * kb, lane);
                     sa[jt] = mma(ka[kb], kj, sa[jt]);  // (K K^T)[i][j]
                     at[jt] = mma(kj, qa[kb], at[jt]);  // (K Q^T)[j][i] = attn^T
+                }
+            } else if (KDA && jt < w) {
+                // KDA, tile jt before the row tile: split the decay at the last
+                // token e of tile jt, exp(G_i - G_j) = exp(G_i - G_e) exp(G_e - G_j),
+                // both exponents <= 0 (i > e >= j)
+                const int ref = 16 * jt + 15;
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb) {
+                    const F ki = frag_rows_decay<E>(Ks, LDK, Gk, LDG, 16 * w, 32 * kb, lane, ref, 1.f);
+                    const F qi = frag_rows_decay<E>(Qs, LDK, Gk, LDG, 16 * w, 32 * kb, lane, ref, 1.f);
+                    const F kj = frag_rows_decay<E>(Ks, LDK, Gk, LDG, 16 * jt, 32 * kb, lane, ref, -1.f);
+                    sa[jt] = mma(ki, kj, sa[jt]);
+                    at[jt] = mma(kj, qi, at[jt]);
+                }
+            } else if (KDA && jt == w) {
+                // KDA, pairs inside the row tile: one product per level of the
+                // binary split (frag_rows_level), each entry taken from the level
+                // of its pair; the diagonal of attn (decay exp(0) = 1) unscaled
+                f32x4 ls[4], lt[4], dg = zero4();
+#pragma unroll
+                for (int lv = 1; lv <= 4; ++lv) {
+                    ls[lv - 1] = zero4();
+                    lt[lv - 1] = zero4();
+#pragma unroll
+                    for (int kb = 0; kb < DK / 32; ++kb) {
+                        const F ki = frag_rows_level<E, true>(Ks, LDK, Gk, LDG, 16 * w, 32 * kb, lane, lv);
+                        const F qi = frag_rows_level<E, true>(Qs, LDK, Gk, LDG, 16 * w, 32 * kb, lane, lv);
+                        const F kj = frag_rows_level<E, false>(Ks, LDK, Gk, LDG, 16 * w, 32 * kb, lane, lv);
+                        ls[lv - 1] = mma(ki, kj, ls[lv - 1]);
+                        lt[lv - 1] = mma(kj, qi, lt[lv - 1]);
+                    }
+                }
+#pragma unroll
+                for (int kb = 0; kb < DK / 32; ++kb)
+                    dg = mma(frag_rows<E>(Ks, LDK, 16 * w, 32 * kb, lane),
+                             frag_rows<E>(Qs, LDK, 16 * w, 32 * kb, lane), dg);
+                auto pick = [&](const f32x4* L, int lv, int e) {
+                    return lv == 1 ? L[0][e] : lv == 2 ? L[1][e] : lv == 3 ? L[2][e] : L[3][e];
+                };
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int a = 4 * gq + e;   // D-tile row (local token)
+                    // K K^T: row i = a, column j = n
+                    sa[jt][e] = a > n ? pick(ls, pair_level(a, n), e) : 0.f;
+                    // attn^T: row j = a, column i = n
+                    at[jt][e] = n > a ? pick(lt, pair_level(n, a), e) : (n == a ? dg[e] : 0.f);
                 }
             }
             // attn^T tile: rows j = 16jt + 4gq + e, column i = 16w + n (causal, incl. diagonal)

@@ -73,6 +73,36 @@ def test_kda_prefill_b2_h16_t8192():
     assert eo <= tol and es <= tol
 
 
+def test_kda_prefill_b2_h16_t8192_strong_decay():
+    """The KDA workload's size (2 x 16 x 8192, d = 128, bf16) with the decay
+    sixteen times stronger (g = -16 softplus(N(0,1)) per channel), in the
+    bench's launch configuration: every output finite, and five sampled heads
+    against the oracle run on those heads alone."""
+    import delta_rule_recurrent_amd as dn
+
+    B, H, T, d = 2, 16, 8192, 128
+    say("generating kda strong decay")
+    inp = synthetic.make("kda", B, H, T, d, d, dtype="bf16", seed=1004, decay_scale=16.0)
+    dv = to_dev(inp)
+    o = torch.empty(B, H, T, d, dtype=torch.bfloat16, device="cuda")
+    S = torch.empty(B, H, d, d, dtype=torch.float32, device="cuda")
+    ws = torch.empty(dn.workspace_bytes(B, H, T, d, d, torch.bfloat16), dtype=torch.uint8,
+                     device="cuda")
+    dn.kda_chunk_fwd(dv["q"], dv["k"], dv["v"], dv["beta"], dv["g"], None, o=o, S_final=S,
+                     workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(S).all()
+    bi, hi = [0, 0, 1, 1, 1], [0, 9, 3, 12, 15]
+    sub = {n: inp[n][bi, hi][None] for n in ("q", "k", "v", "beta", "g")}
+    say("oracle on 5 sampled heads")
+    o_ref, S_ref = oracle.recurrent(sub["q"], sub["k"], sub["v"], sub["beta"], sub["g"], None,
+                                    kind=oracle.KDA)
+    eo = rel_err(o[bi, hi][None], o_ref)
+    es = rel_err(S[bi, hi][None], S_ref)
+    say("  kda strong decay: err o %.3e  S %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
 def test_gdn_decode_b256_h16_1000_steps():
     import delta_rule_recurrent_amd as dn
 

@@ -86,6 +86,27 @@ def test_prefill_stress(kind, dtype, variant):
         assert eo <= TOL[dtype] and es <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 64), ("bf16", 128)])
+@pytest.mark.parametrize("T", [37, 300])
+def test_kda_strong_decay(dtype, d, T):
+    """KDA with per-channel log-decay g = -16 softplus(N(0,1)) (the scale the
+    full layer's gate -exp(A_log) softplus(a + dt_bias) reaches with A_log up
+    to log 16): the decay summed over a few tokens is far below the fp32
+    exponent range, so every decay factor of the chunked form must stay a
+    decay (no overflow, no inf * 0). Chunked and recurrent forms against the
+    oracle, with a start state."""
+    inp = make("kda", 1, 3, T, d, dtype, seed=500 + T + d, s0_std=0.5, decay_scale=16.0)
+    g = inp["g"].float()
+    assert float(g.min()) < -40.0          # several tokens' worth exceeds exp's range
+    o_ref, S_ref = oracle_prefill(inp)
+    for form in ("chunk", "recurrent"):
+        say("case kda strong decay", form, dtype, d, T)
+        o, S = _prefill(form, "kda", inp)
+        eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
+        say("  err o %.3e  S %.3e" % (eo, es))
+        assert eo <= TOL[dtype] and es <= TOL[dtype]
+
+
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
