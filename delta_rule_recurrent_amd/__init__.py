@@ -133,6 +133,16 @@ def chunk_fwd_fused(q, k, v, beta, g=None, S0=None, *, output_final_state=True, 
                   workspace, stream, kda=False)
 
 
+def chunk_fwd_handoff_status(workspace, B, H, T, dk, dv, dtype, stream=None):
+    """Status of the latest one-launch prefill that used `workspace` with these
+    sizes: DN_OK, or DN_EHANDOFF when a hand-off wait gave up and the call's
+    results were recomputed by the two phases (correct either way).
+    Synchronizes the stream."""
+    return int(lib().dn_chunk_fwd_handoff_status(_ptr(workspace),
+                                                 workspace.numel() * workspace.element_size(),
+                                                 B, H, T, dk, dv, _DT[dtype], _stream(stream)))
+
+
 def kda_chunk_fwd(q, k, v, beta, g, S0=None, *, output_final_state=True, o=None, S_final=None,
                   workspace=None, stream=None):
     """Chunkwise (C=64) KDA prefill; g [B,H,T,dk] per-key-channel log-decay."""

@@ -18,7 +18,7 @@ hipError_t launch_gdr_chunk(int dtype, const void* q, const void* kw, const void
 
 namespace {
 
-constexpr int kVersion = 2;
+constexpr int kVersion = 3;
 
 bool misaligned(const void* p, unsigned a = 16) {
     return (reinterpret_cast<uintptr_t>(p) & (uintptr_t)(a - 1)) != 0;
@@ -134,6 +134,8 @@ const char* dn_strerror(int status) {
                                 "no chunked fp32 KDA at d = 128; dn_chunk_fwd_fused: no one-launch form)";
         case DN_EWORKSPACE: return "workspace missing, misaligned or smaller than dn_chunk_fwd_workspace()";
         case DN_EHIP: return "HIP runtime error at kernel launch";
+        case DN_EHANDOFF: return "the latest one-launch prefill on this workspace had a hand-off wait give up; "
+                                 "its results were recomputed by the two phases (they are correct)";
         default: return "unknown status";
     }
 }
@@ -153,6 +155,24 @@ int dn_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, 
                  int dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return chunk_common(g ? dn::KIND_GATED : dn::KIND_DELTANET, q, k, v, beta, g, S0, o, S_final,
                         B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream, dn::FWD_AUTO);
+}
+
+int dn_chunk_fwd_handoff_status(const void* workspace, size_t workspace_bytes, int B, int H, int T,
+                                int dk, int dv, int dtype, void* stream) {
+    if (B < 1 || H < 1 || T < 0) return DN_EINVAL;
+    if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+    if ((dk != 64 && dk != 128) || dk != dv) return DN_ENOTSUP;
+    const long long BH = (long long)B * H;
+    if (T == 0) return DN_OK;
+    const int st = check_workspace(BH, T, dk, dv, dtype, workspace, workspace_bytes);
+    if (st != DN_OK) return st;
+    unsigned long long w[2] = {0, 0};
+    const char* at = static_cast<const char*>(workspace) + dn::chunk_handoff_offset(BH, T, dk, dtype);
+    if (hipMemcpyAsync(w, at, sizeof(w), hipMemcpyDeviceToHost, as_stream(stream)) != hipSuccess) return DN_EHIP;
+    if (hipStreamSynchronize(as_stream(stream)) != hipSuccess) return DN_EHIP;
+    // the error word holds the epoch of a failed launch; the word after it the
+    // epoch of the latest one-launch call
+    return (w[1] != 0 && w[0] == w[1]) ? DN_EHANDOFF : DN_OK;
 }
 
 int dn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* beta,

@@ -32,6 +32,7 @@
 //                      to the scan workgroups of the same XCD as they finish
 //                      (long sequences, bf16).
 #include <atomic>
+#include <cstdlib>
 #include <random>
 
 #include "dn_device.h"
@@ -819,7 +820,12 @@ __global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict
                                                              const E* __restrict__ beta,
                                                              const E* __restrict__ g,
                                                              char* __restrict__ ws, int T,
-                                                             int nchunks, HeadMap hm) {
+                                                             int nchunks, HeadMap hm,
+                                                             const unsigned long long* guard,
+                                                             unsigned long long gval) {
+    // guard != NULL: recomputation after a one-launch call, done only if that
+    // launch's hand-off failed (its error word holds gval)
+    if (guard && __hip_atomic_load(guard, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gval) return;
     __shared__ Prep2Lds<E, DK, DV> lds;
     const long item = blockIdx.x;
     const long bh = item / nchunks;
@@ -1118,9 +1124,13 @@ struct ScanLds {
 // invalidation is needed: the consumer has not read the block's lines before
 // (the vector L1 starts every launch empty), so it cannot hold stale copies.
 // A tag left over from an earlier launch never matches (the epoch is new for
-// every launch). Waits are bounded: after about a second a wavefront marks
-// the launch as failed (it writes the epoch into an error word after the tags)
-// and stops waiting; the others stop waiting once they see that.
+// every launch). Waits are bounded: after `spin` polls (about a second at the
+// default) a wavefront marks the launch as failed (it writes the epoch into
+// an error word after the tags) and stops waiting; the others stop waiting
+// once they see that. A failed launch's results are then recomputed by the
+// two phases (kernels enqueued after it that do nothing unless the error word
+// holds that launch's epoch), so the call's results are correct either way;
+// dn_chunk_fwd_handoff_status reports that it happened.
 // ---------------------------------------------------------------------------
 typedef unsigned long long u64;
 constexpr int SPIN_LIMIT = 1 << 20;
@@ -1144,9 +1154,9 @@ __device__ __forceinline__ void publish(u64* f, u64 tag, int lane) {
 // Consumer: (a, b) are the block's two tags as loaded earlier; poll until both
 // equal `tag` (or give up, see above).
 __device__ __forceinline__ void wait_block(const u64* f, u64 a, u64 b, u64 tag, u64* err, u64 epoch,
-                                        int lane) {
+                                        int spin, int lane) {
     if (a == tag && b == tag) return;
-    for (int i = 0; i < SPIN_LIMIT; ++i) {
+    for (int i = 0; i < spin; ++i) {
         __builtin_amdgcn_s_sleep(8);
         a = flag_load(f);
         b = flag_load(f + 1);
@@ -1157,7 +1167,8 @@ __device__ __forceinline__ void wait_block(const u64* f, u64 a, u64 b, u64 tag, 
 }
 
 // Where the hand-off tags live: after the BH * nchunks workspace blocks, two
-// 64-bit tags per block, then the error word.
+// 64-bit tags per block, then the error word and the epoch of the last
+// one-launch call (see ws_bytes_t for the rest of the tail).
 template <typename E, int DK, int DV>
 __device__ __forceinline__ u64* block_tags(char* ws, long BH, int nchunks) {
     return reinterpret_cast<u64*>(ws + BH * nchunks * WsLayout<E, DK, DV>::BYTES);
@@ -1173,7 +1184,7 @@ __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict_
                                           const float* __restrict__ S0, E* __restrict__ o,
                                           float* __restrict__ S_final, int vt, int w, int lane,
                                           ScanLds<E, DK, DV, KIND, BV>& lds, const u64* tags,
-                                          u64 tag, u64* err, u64 epoch,
+                                          u64 tag, u64* err, u64 epoch, int spin,
                                           float* __restrict__ S_bound = nullptr) {
     typedef WsLayout<E, DK, DV> Lw;
     typedef ScanOps<E, DK, DV, BV, KIND> Ops;
@@ -1235,7 +1246,7 @@ __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict_
     auto tags_of = [&](int cc) { return tags + 2 * min(cc, last); };
     auto ready = [&](int cc) {
         if (SYNC) {
-            wait_block(tags_of(cc), ta, tb, tag, err, epoch, lane);
+            wait_block(tags_of(cc), ta, tb, tag, err, epoch, spin, lane);
             sched_fence();
             ta = flag_load(tags_of(cc + 1));
             tb = flag_load(tags_of(cc + 1) + 1);
@@ -1318,7 +1329,11 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
                                                          E* __restrict__ o,
                                                          float* __restrict__ S_final, int T,
                                                          int nchunks, int BH,
-                                                         float* __restrict__ S_bound, HeadMap hm) {
+                                                         float* __restrict__ S_bound, HeadMap hm,
+                                                         const unsigned long long* guard,
+                                                         unsigned long long gval) {
+    // guard: as in chunk_prep2_kernel
+    if (guard && __hip_atomic_load(guard, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gval) return;
     constexpr int NV = DV / BV;
     // XCD-aware mapping: consecutive workgroups go to different XCDs
     // (round-robin over 8); the NV value tiles of one head share an XCD so
@@ -1331,7 +1346,7 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
     const SeqView sv{ws + bh * nchunks * WsLayout<E, DK, DV>::BYTES, hm.key(bh) * T, bh * T, bh, T,
                      nchunks};
     scan_body<E, DK, DV, KIND, BV, false, 3, EMIT>(sv, q, S0, o, S_final, vt, (int)(threadIdx.x >> 6),
-                                                (int)(threadIdx.x & 63), lds, nullptr, 0, nullptr, 0,
+                                                (int)(threadIdx.x & 63), lds, nullptr, 0, nullptr, 0, 0,
                                                 S_bound);
 }
 
@@ -1369,7 +1384,7 @@ __global__ __launch_bounds__(256) void chunk_scan_varlen_kernel(const char* __re
     const SeqView sv{ws + ((long)h * nchunks + cs[n]) * WsLayout<E, DK, DV>::BYTES, row, row, bh,
                      len, (len + CHUNK - 1) / CHUNK};
     scan_body<E, DK, DV, KIND, BV, false, 3>(sv, q, S0, o, S_final, vt, (int)(threadIdx.x >> 6),
-                                          (int)(threadIdx.x & 63), lds, nullptr, 0, nullptr, 0);
+                                          (int)(threadIdx.x & 63), lds, nullptr, 0, nullptr, 0, 0);
 }
 
 // Chunk offsets of packed sequences (one workgroup): cs[n] = sum over m < n of
@@ -1459,7 +1474,7 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
                                                              E* __restrict__ o,
                                                              float* __restrict__ S_final, int T,
                                                              int nchunks, int BH, int NP, u64 epoch,
-                                                             HeadMap hm) {
+                                                             int spin, HeadMap hm) {
     typedef WsLayout<E, DK, DV> Lw;
     constexpr int NV = DV / BV;
     __shared__ FusedLds<E, DK, DV, KIND, BV> lds;
@@ -1469,6 +1484,10 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
     u64* tags = block_tags<E, DK, DV>(ws, BH, nchunks);
     u64* err = tags + 2L * BH * nchunks;
     const u64 tag = xcc_tag(epoch);
+    // the epoch of the latest one-launch call on this workspace, for the
+    // status query (the word after the error word)
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        __hip_atomic_store(err + 1, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
     if (s < NP) {
         const int unit = w >> 1, wu = w & 1;
@@ -1501,7 +1520,7 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
     const long bh = xcd + 8L * i;
     const SeqView sv{ws + bh * nchunks * Lw::BYTES, hm.key(bh) * T, bh * T, bh, T, nchunks};
     scan_body<E, DK, DV, KIND, BV, true, 2>(sv, q, S0, o, S_final, vt, w, lane, lds.scan,
-                                         tags + 2 * bh * nchunks, tag, err, epoch);
+                                         tags + 2 * bh * nchunks, tag, err, epoch, spin);
 }
 
 // ---------------------------------------------------------------------------
@@ -1520,11 +1539,21 @@ static int device_cu_count() {
     return n;
 }
 
-// The chunk blocks, then the hand-off tags of the fused launch (two 64-bit
-// words per block) and its error word, padded to 256 bytes.
+// The chunk blocks, then the words of the one-launch form: two 64-bit
+// hand-off tags per block, the error word and the latest epoch (padded to 256
+// bytes), then a copy of the start state [BH][D][D] fp32 (the one-launch
+// form may overwrite S0 in place before a failed hand-off is recomputed).
+template <typename E, int D>
+static long long ws_tail_off(long long BH, long long nchunks) {
+    return BH * nchunks * WsLayout<E, D, D>::BYTES;
+}
+template <typename E, int D>
+static long long ws_s0copy_off(long long BH, long long nchunks) {
+    return ws_tail_off<E, D>(BH, nchunks) + (BH * nchunks * 16 + 16 + 255) / 256 * 256;
+}
 template <typename E, int D>
 static size_t ws_bytes_t(long long BH, long long nchunks) {
-    return (size_t)(BH * nchunks * WsLayout<E, D, D>::BYTES + (BH * nchunks * 16 + 8 + 255) / 256 * 256);
+    return (size_t)(ws_s0copy_off<E, D>(BH, nchunks) + BH * D * D * 4);
 }
 
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype) {
@@ -1549,7 +1578,7 @@ static hipError_t prep_t(const void* q, const void* k, const void* v, const void
     if constexpr (KIND != KIND_KDA && (sizeof(E) == 2 || D == 64)) {
         hipLaunchKernelGGL((chunk_prep2_kernel<E, D, D, KIND>), dim3((unsigned)nitems), dim3(128), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
-                           (char*)ws, T, nchunks, hm);
+                           (char*)ws, T, nchunks, hm, (const u64*)nullptr, 0ull);
         return hipGetLastError();
     }
     // persistent workgroups: as many as fit on the device at once (LDS bound)
@@ -1565,7 +1594,8 @@ static hipError_t prep_t(const void* q, const void* k, const void* v, const void
 
 template <typename E, int D, int KIND, bool EMIT>
 static hipError_t scan_launch(const void* q, const float* S0, void* o, float* S_final, const void* ws,
-                              int BH, int T, float* S_bound, hipStream_t st, HeadMap hm) {
+                              int BH, int T, float* S_bound, hipStream_t st, HeadMap hm,
+                              const u64* guard = nullptr, u64 gval = 0) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const long groups = ((long)BH + 7) / 8;
     // 32-column value tiles unless that leaves most of the 256 CUs idle
@@ -1573,12 +1603,14 @@ static hipError_t scan_launch(const void* q, const float* S0, void* o, float* S_
         constexpr int BV = 32;
         const long nblk = groups * 8 * (D / BV);
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV, EMIT>), dim3((unsigned)nblk), dim3(256), 0,
-                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound, hm);
+                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound, hm,
+                           guard, gval);
     } else {
         constexpr int BV = 16;
         const long nblk = groups * 8 * (D / BV);
         hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND, BV, EMIT>), dim3((unsigned)nblk), dim3(256), 0,
-                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound, hm);
+                           st, (const char*)ws, (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, S_bound, hm,
+                           guard, gval);
     }
     return hipGetLastError();
 }
@@ -1589,6 +1621,17 @@ static hipError_t scan_t(const void* q, const float* S0, void* o, float* S_final
                          int BH, int T, hipStream_t st, HeadMap hm, float* S_bound) {
     if (S_bound) return scan_launch<E, D, KIND, true>(q, S0, o, S_final, ws, BH, T, S_bound, st, hm);
     return scan_launch<E, D, KIND, false>(q, S0, o, S_final, ws, BH, T, nullptr, st, hm);
+}
+
+// Polls a hand-off wait makes before it gives up: SPIN_LIMIT, or the value of
+// the environment variable DN_HANDOFF_SPIN_LIMIT (a small value forces the
+// recomputation path, for testing it).
+static int handoff_spin_limit() {
+    const char* s = getenv("DN_HANDOFF_SPIN_LIMIT");
+    if (!s || !*s) return SPIN_LIMIT;
+    char* end = nullptr;
+    const long v = strtol(s, &end, 10);
+    return (end && *end == 0 && v >= 0 && v <= SPIN_LIMIT) ? (int)v : SPIN_LIMIT;
 }
 
 // A new 64-bit epoch per fused launch: a random per-process prefix and a
@@ -1625,10 +1668,40 @@ static hipError_t fused_t(const void* q, const void* k, const void* v, const voi
     const int cus_per_xcd = device_cu_count() / 8;
     if (cus_per_xcd - ns >= 8) np = min(cus_per_xcd - ns, 6 * ((BH + 7) / 8));
     if ((long)np > (items + 1) / 2) np = (int)((items + 1) / 2);
+    char* wsc = static_cast<char*>(ws);
+    const u64* err = reinterpret_cast<const u64*>(wsc + ws_tail_off<E, D>(BH, nchunks)) + 2L * BH * nchunks;
+    // the start state as it is now: an in-place call overwrites S0 before a
+    // failed hand-off could be recomputed
+    float* s0c = nullptr;
+    if (S0) {
+        s0c = reinterpret_cast<float*>(wsc + ws_s0copy_off<E, D>(BH, nchunks));
+        const hipError_t e = launch_state_copy(S0, s0c, (long long)BH * D * D, st);
+        if (e != hipSuccess) return e;
+    }
+    const u64 epoch = next_epoch();
     hipLaunchKernelGGL((chunk_fused_kernel<E, D, D, KIND, BV>), dim3((unsigned)(8 * (np + ns))), dim3(256),
                        0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
-                       (char*)ws, S0, (E*)o, S_final, T, nchunks, BH, np, next_epoch(), hm);
-    return hipGetLastError();
+                       (char*)ws, S0, (E*)o, S_final, T, nchunks, BH, np, epoch, handoff_spin_limit(), hm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // the two phases, which return at once unless this launch's hand-off
+    // failed (its error word holds the epoch): then they recompute the call
+    hipLaunchKernelGGL((chunk_prep2_kernel<E, D, D, KIND>), dim3((unsigned)((long)BH * nchunks)), dim3(128), 0,
+                       st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g, (char*)ws, T,
+                       nchunks, hm, err, epoch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return scan_launch<E, D, KIND, false>(q, s0c, o, S_final, ws, BH, T, nullptr, st, hm, err, epoch);
+}
+
+// Byte offset of the one-launch form's error word (followed by the latest
+// epoch) in the workspace.
+size_t chunk_handoff_offset(long long BH, long long T, int dk, int dtype) {
+    const long long nchunks = (T + CHUNK - 1) / CHUNK;
+    long long tail;
+    if (dtype == DT_BF16) tail = dk == 128 ? ws_tail_off<bf16, 128>(BH, nchunks) : ws_tail_off<bf16, 64>(BH, nchunks);
+    else tail = dk == 128 ? ws_tail_off<float, 128>(BH, nchunks) : ws_tail_off<float, 64>(BH, nchunks);
+    return (size_t)(tail + BH * nchunks * 16);
 }
 
 template <typename E, int D>

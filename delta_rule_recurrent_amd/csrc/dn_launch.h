@@ -80,6 +80,10 @@ hipError_t launch_chunk_fwd_varlen(int kind, int dtype, const void* q, const voi
 size_t chunk_varlen_workspace_bytes(long long N, long long H, long long T, int dk, int dv,
                                     int dtype);
 
+// Byte offset, in the prefill's workspace, of the one-launch form's error word
+// and (next) the epoch of the latest one-launch call on that workspace.
+size_t chunk_handoff_offset(long long BH, long long T, int dk, int dtype);
+
 // Workspace bytes of the chunkwise prefill (per call).
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype);
 

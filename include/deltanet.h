@@ -51,7 +51,9 @@ typedef enum dn_status {
     DN_ENOTSUP = -2,    /* d_k, d_v outside {64, 128} or d_k != d_v, or no such form
                            (see dn_kda_chunk_fwd, dn_chunk_fwd_fused) */
     DN_EWORKSPACE = -3, /* workspace NULL or smaller than dn_chunk_fwd_workspace() */
-    DN_EHIP = -4        /* the HIP runtime reported an error at launch */
+    DN_EHIP = -4,       /* the HIP runtime reported an error at launch */
+    DN_EHANDOFF = -5    /* dn_chunk_fwd_handoff_status only: the latest one-launch
+                           prefill on the workspace was recomputed (see there) */
 } dn_status;
 
 typedef enum dn_dtype { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
@@ -67,8 +69,10 @@ int dn_version(void);
  * need for these sizes (0 when T == 0; (size_t)0 also for invalid sizes, which
  * the entry points then reject). The workspace holds one block of per-chunk
  * intermediates of the UT/WY form per (head, chunk), then the hand-off words
- * of the one-launch form. It needs no initialisation, its contents between
- * calls are unspecified, and calls that overlap in time must not share it.
+ * of the one-launch form and a copy of the start state. It needs no
+ * initialisation, its contents between calls are unspecified (apart from what
+ * dn_chunk_fwd_handoff_status reads), and calls that overlap in time must not
+ * share it.
  */
 size_t dn_chunk_fwd_workspace(int B, int H, int T, int dk, int dv, int dtype);
 
@@ -106,11 +110,33 @@ int dn_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
  * room for the prep workgroups (B*H above about 48 per 8 heads' worth of
  * value tiles; dn_chunk_fwd then runs the two phases). dn_chunk_fwd itself
  * uses this form for sequences of 64 chunks (4096 tokens) and more.
+ *
+ * The hand-off relies on two measured facts of the hardware, not guaranteed
+ * by any API: workgroup b of a launch runs on XCD b mod 8, and workgroups
+ * start in index order. Every wait for a block is bounded; a wait that gives
+ * up marks the launch as failed in the workspace. The call also enqueues the
+ * two phases behind the launch, guarded on the device: they return at once
+ * unless that launch failed, in which case they recompute o and S_final
+ * (from a copy of S0 taken before the launch, so in-place calls are covered).
+ * The results are therefore correct either way; dn_chunk_fwd_handoff_status
+ * tells whether the recomputation ran.
  */
 int dn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* beta,
                        const void* g, const float* S0, void* o, float* S_final,
                        int B, int H, int T, int dk, int dv, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Whether the latest one-launch prefill (dn_chunk_fwd_fused, or dn_chunk_fwd
+ * taking that form) that used `workspace` with these sizes had a hand-off
+ * wait give up: DN_EHANDOFF if so (its results were recomputed by the two
+ * phases and are correct), DN_OK if not or if no one-launch call used the
+ * workspace. Reads 16 bytes of the workspace after synchronizing `stream`
+ * (blocking the host). DN_EINVAL / DN_ENOTSUP / DN_EWORKSPACE as for
+ * dn_chunk_fwd; DN_EHIP if the copy fails.
+ */
+int dn_chunk_fwd_handoff_status(const void* workspace, size_t workspace_bytes, int B, int H, int T,
+                                int dk, int dv, int dtype, void* stream);
 
 /*
  * KDA chunkwise prefill: as dn_chunk_fwd but g is REQUIRED and holds one

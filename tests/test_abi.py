@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -38,8 +38,8 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strerror():
     lib = _lib.lib()
-    assert lib.dn_version() >= 2   # workspace holds the one-launch hand-off words since 2
-    for code in (0, -1, -2, -3, -4, 7):
+    assert lib.dn_version() >= 3   # workspace holds the start-state copy since 3
+    for code in (0, -1, -2, -3, -4, -5, 7):
         s = lib.dn_strerror(code)
         assert isinstance(s, bytes) and len(s) > 0
 
@@ -49,13 +49,15 @@ def test_workspace_size_function():
     ws = lib.dn_chunk_fwd_workspace
     assert ws(1, 1, 0, 64, 64, 0) == 0
     assert ws(1, 1, 64, 64, 64, 0) > 0
-    # one block per (head, chunk), then two 64-bit hand-off tags per block and
-    # an 8-byte error word, padded to 256 bytes
+    # one block per (head, chunk), then two 64-bit hand-off tags per block, an
+    # error word and the latest epoch (padded to 256 bytes), then a copy of
+    # the fp32 start state per head
+    state = 128 * 128 * 4
     block = ws(1, 1, 128, 128, 128, 1) - ws(1, 1, 64, 128, 128, 1)
     assert block > 0 and block % 256 == 0
-    assert ws(1, 1, 64, 128, 128, 1) == block + 256
+    assert ws(1, 1, 64, 128, 128, 1) == block + 256 + state
     a = ws(4, 8, 2048, 128, 128, 1)
-    assert a == 32 * 32 * block + (32 * 32 * 16 + 8 + 255) // 256 * 256
+    assert a == 32 * 32 * block + (32 * 32 * 16 + 16 + 255) // 256 * 256 + 32 * state
     assert ws(1, 1, 65, 128, 128, 1) == ws(1, 1, 128, 128, 128, 1)
     assert ws(1, 1, 64, 96, 96, 1) == 0     # unsupported head size
     assert ws(0, 1, 64, 64, 64, 1) == 0
@@ -449,3 +451,20 @@ def test_gdr_chunk_workspace_and_validation():
         assert call(**{name: P + 2}) == E, name               # bf16: 2-byte aligned only
         assert call(**{name: P + 4, "dtype": 0}) == E, name   # fp32: 4-byte aligned only
         assert call(**{name: MIS, "dtype": 0}) == E, name     # fp32: 8-byte aligned only
+
+
+def test_handoff_status_validation():
+    """The status query of the one-launch form validates like the prefill
+    (no GPU is touched on these paths)."""
+    lib = _lib.lib()
+    fn = lib.dn_chunk_fwd_handoff_status
+    need = lib.dn_chunk_fwd_workspace(1, 2, 4096, 128, 128, 1)
+    E, N, W = _lib.DN_EINVAL, _lib.DN_ENOTSUP, _lib.DN_EWORKSPACE
+    assert fn(WS, need, 0, 2, 4096, 128, 128, 1, None) == E
+    assert fn(WS, need, 1, 2, -1, 128, 128, 1, None) == E
+    assert fn(WS, need, 1, 2, 4096, 128, 128, 7, None) == E
+    assert fn(WS, need, 1, 2, 4096, 96, 96, 1, None) == N
+    assert fn(None, need, 1, 2, 4096, 128, 128, 1, None) == W
+    assert fn(WS, need - 1, 1, 2, 4096, 128, 128, 1, None) == W
+    assert fn(WS + 128, need, 1, 2, 4096, 128, 128, 1, None) == W
+    assert fn(None, 0, 1, 2, 0, 128, 128, 1, None) == _lib.DN_OK   # T == 0: nothing ran

@@ -256,8 +256,9 @@ def test_fused_handoff(kind, BH):
     torch.cuda.synchronize()
     tail = ws[B * H * nch * block:].cpu()
     tags1 = tail[:B * H * nch * 16].view(torch.int64).view(B * H, nch, 2).clone()
-    err = int(tail[B * H * nch * 16:B * H * nch * 16 + 8].view(torch.int64)[0])
-    assert err == 0
+    err, last = (int(x) for x in tail[B * H * nch * 16:B * H * nch * 16 + 16].view(torch.int64))
+    assert err == 0 and last != 0
+    assert dn.chunk_fwd_handoff_status(ws, B, H, T, 128, 128, dt) == 0
     assert torch.equal(tags1[:, :, 0], tags1[:, :, 1])
     t = tags1[:, :, 0].numpy().astype(np.uint64)
     low = t & np.uint64((1 << 56) - 1)
@@ -267,6 +268,8 @@ def test_fused_handoff(kind, BH):
     xcc = ((t >> np.uint64(56)) & np.uint64(15)) ^ ((t[0, 0] >> np.uint64(56)) & np.uint64(15))
     for h in range(B * H):
         assert (xcc[h] == np.uint64(h % 8)).all(), (h, xcc[h])
+    # the latest-epoch word is the epoch the tags carry (below the XCD bits)
+    assert np.uint64(last & ((1 << 56) - 1)) == low[0, 0]
 
     ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     o3, S3 = torch.empty_like(o), torch.empty_like(S)
@@ -282,6 +285,51 @@ def test_fused_handoff(kind, BH):
     eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
     say("  err o %.3e  S %.3e" % (eo, es))
     assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_fused_handoff_failure_recomputed(in_place, monkeypatch):
+    """The one-launch form with its hand-off waits cut to zero polls (set from
+    the host through DN_HANDOFF_SPIN_LIMIT; every kernel still ends normally):
+    waits give up on blocks not yet published, the launch marks itself
+    failed, and the two phases enqueued behind it recompute the call. The
+    status query reports DN_EHANDOFF, and o and S_final are bitwise the
+    two-phase prefill's, also when S_final is S0 (updated in place). A
+    following call with the default limit reports DN_OK."""
+    dn = _dn()
+    B, H, T = 1, 4, 80 * 64 + 11
+    nch = (T + 63) // 64
+    say("fused hand-off failure", in_place, B, H, T)
+    inp = make("gated", B, H, T, 128, "bf16", seed=31, s0_std=0.5)
+    d = to_dev(inp)
+    dt = d["q"].dtype
+    ws = torch.empty(dn.workspace_bytes(B, H, T, 128, 128, dt), dtype=torch.uint8, device="cuda")
+    # the reference: the two phases on their own workspace
+    ws2 = torch.empty_like(ws)
+    o2, S2 = torch.empty(B, H, T, 128, dtype=dt, device="cuda"), torch.empty_like(d["S0"])
+    dn.chunk_prep(d["q"], d["k"], d["v"], d["beta"], d["g"], ws2)
+    dn.chunk_scan(d["q"], o2, ws2, d["S0"], S2)
+    monkeypatch.setenv("DN_HANDOFF_SPIN_LIMIT", "0")
+    if in_place:
+        S = d["S0"].clone()
+        o, S1 = dn.chunk_fwd_fused(d["q"], d["k"], d["v"], d["beta"], d["g"], S, S_final=S,
+                                   workspace=ws)
+        assert S1 is S
+    else:
+        o, S1 = dn.chunk_fwd_fused(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"], workspace=ws)
+    st = dn.chunk_fwd_handoff_status(ws, B, H, T, 128, 128, dt)
+    assert st == _lib_status("DN_EHANDOFF"), st
+    assert torch.equal(o, o2) and torch.equal(S1, S2)
+    monkeypatch.delenv("DN_HANDOFF_SPIN_LIMIT")
+    o3, S3 = dn.chunk_fwd_fused(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"], workspace=ws)
+    assert dn.chunk_fwd_handoff_status(ws, B, H, T, 128, 128, dt) == 0
+    assert torch.equal(o3, o2) and torch.equal(S3, S2)
+    assert nch >= 64
+
+
+def _lib_status(name):
+    from delta_rule_recurrent_amd import _lib
+    return getattr(_lib, name)
 
 
 @pytest.mark.parametrize("kind", KINDS)
