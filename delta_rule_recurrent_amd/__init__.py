@@ -133,6 +133,26 @@ def chunk_fwd_fused(q, k, v, beta, g=None, S0=None, *, output_final_state=True, 
                   workspace, stream, kda=False)
 
 
+def chunk_fwd_noalloc(q, k, v, beta, g=None, S0=None, *, o=None, S_final=None, stream=None):
+    """chunk_fwd without a workspace (dn_chunk_fwd_noalloc: the library's
+    built-in 128 MiB scratch per GPU). o and S_final are allocated here unless
+    given; pass them to keep the whole call allocation-free. Calls that
+    overlap in time on one GPU race."""
+    B, H, T, dk, dv, dev, dt = _prefill_args(q, k, v, beta, g, S0, False)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, T, dv), dt, dev)
+    if S_final is None:
+        S_final = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
+    st = lib().dn_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o),
+                                    _ptr(S_final), B, H, T, dk, dv, _DT[dt], _stream(stream))
+    _lib.check("dn_chunk_fwd_noalloc", st)
+    return o, S_final
+
+
 def chunk_fwd_handoff_status(workspace, B, H, T, dk, dv, dtype, stream=None):
     """Status of the latest one-launch prefill that used `workspace` with these
     sizes: DN_OK, or DN_EHANDOFF when a hand-off wait gave up and the call's

@@ -14,7 +14,7 @@ from . import build as _build
 
 LIB_PATH = _build.LIB
 
-DN_OK, DN_EINVAL, DN_ENOTSUP, DN_EWORKSPACE, DN_EHIP, DN_EHANDOFF = 0, -1, -2, -3, -4, -5
+DN_OK, DN_EINVAL, DN_ENOTSUP, DN_EWORKSPACE, DN_EHIP, DN_EHANDOFF, DN_ESCRATCH = 0, -1, -2, -3, -4, -5, -6
 DN_F32, DN_BF16 = 0, 1
 
 # Every symbol include/deltanet.h declares, with its ctypes signature.
@@ -27,6 +27,7 @@ SIGNATURES = {
     "dn_chunk_fwd": (_i, _PREFILL + [_vp, _sz, _vp]),
     "dn_chunk_fwd_fused": (_i, _PREFILL + [_vp, _sz, _vp]),
     "dn_chunk_fwd_handoff_status": (_i, [_vp, _sz] + [_i] * 6 + [_vp]),
+    "dn_chunk_fwd_noalloc": (_i, _PREFILL + [_vp]),
     "dn_kda_chunk_fwd": (_i, _PREFILL + [_vp, _sz, _vp]),
     "dn_chunk_fwd_states": (_i, [_i] + [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_chunk_fwd_gqa": (_i, [_i] + [_vp] * 8 + [_i] * 7 + [_vp, _sz, _vp]),

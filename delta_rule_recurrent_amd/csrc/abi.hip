@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/deltanet.h"
 #include "dn_launch.h"
 
@@ -122,6 +124,32 @@ bool head_map(int Hk, int Hv, dn::HeadMap* hm) {
     return true;
 }
 
+// Scratch of dn_chunk_fwd_noalloc: a device array of the library itself, so
+// that the call allocates nothing. Each GPU the library runs on holds its own
+// copy until the process ends. In host code `scratch` is a host-side stand-in,
+// not a device address: its address on a device comes from
+// hipGetSymbolAddress, once per device, and only that address is ever passed
+// to kernels.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // address of `scratch` on each device
+
+int scratch_address(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DN_EHIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return DN_EHIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,6 +162,8 @@ const char* dn_strerror(int status) {
                                 "no chunked fp32 KDA at d = 128; dn_chunk_fwd_fused: no one-launch form)";
         case DN_EWORKSPACE: return "workspace missing, misaligned or smaller than dn_chunk_fwd_workspace()";
         case DN_EHIP: return "HIP runtime error at kernel launch";
+        case DN_ESCRATCH: return "sizes need more scratch than dn_chunk_fwd_noalloc's built-in 128 MiB "
+                                 "(use dn_chunk_fwd with a workspace)";
         case DN_EHANDOFF: return "the latest one-launch prefill on this workspace had a hand-off wait give up; "
                                  "its results were recomputed by the two phases (they are correct)";
         default: return "unknown status";
@@ -155,6 +185,24 @@ int dn_chunk_fwd(const void* q, const void* k, const void* v, const void* beta, 
                  int dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return chunk_common(g ? dn::KIND_GATED : dn::KIND_DELTANET, q, k, v, beta, g, S0, o, S_final,
                         B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream, dn::FWD_AUTO);
+}
+
+int dn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* beta,
+                         const void* g, const float* S0, void* o, float* S_final, int B, int H,
+                         int T, int dk, int dv, int dtype, void* stream) {
+    // every argument is checked before the first HIP call
+    const int st = check_common(q, k, v, beta, g, false, S0, o, S_final, B, H, T, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    const int kind = g ? dn::KIND_GATED : dn::KIND_DELTANET;
+    if (T == 0)   // no workspace involved
+        return chunk_common(kind, q, k, v, beta, g, S0, o, S_final, B, H, T, dk, dv, dtype, nullptr, 0,
+                            stream, dn::FWD_AUTO);
+    if (dn::chunk_workspace_bytes((long long)B * H, T, dk, dv, dtype) > kScratchBytes) return DN_ESCRATCH;
+    void* ws = nullptr;
+    const int sa = scratch_address(&ws);
+    if (sa != DN_OK) return sa;
+    return chunk_common(kind, q, k, v, beta, g, S0, o, S_final, B, H, T, dk, dv, dtype, ws, kScratchBytes,
+                        stream, dn::FWD_AUTO);
 }
 
 int dn_chunk_fwd_handoff_status(const void* workspace, size_t workspace_bytes, int B, int H, int T,

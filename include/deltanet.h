@@ -52,8 +52,10 @@ typedef enum dn_status {
                            (see dn_kda_chunk_fwd, dn_chunk_fwd_fused) */
     DN_EWORKSPACE = -3, /* workspace NULL or smaller than dn_chunk_fwd_workspace() */
     DN_EHIP = -4,       /* the HIP runtime reported an error at launch */
-    DN_EHANDOFF = -5    /* dn_chunk_fwd_handoff_status only: the latest one-launch
+    DN_EHANDOFF = -5,   /* dn_chunk_fwd_handoff_status only: the latest one-launch
                            prefill on the workspace was recomputed (see there) */
+    DN_ESCRATCH = -6    /* dn_chunk_fwd_noalloc only: the sizes need more scratch
+                           than its built-in array */
 } dn_status;
 
 typedef enum dn_dtype { DN_F32 = 0, DN_BF16 = 1 } dn_dtype;
@@ -125,6 +127,24 @@ int dn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* 
                        const void* g, const float* S0, void* o, float* S_final,
                        int B, int H, int T, int dk, int dv, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * dn_chunk_fwd without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments (minus the workspace), same results as
+ * dn_chunk_fwd, which it calls. Its scratch is a 128 MiB device array built
+ * into the library, one per GPU the library runs on, held until the process
+ * ends (bf16 at d = 128 that covers about 1,700 (head, 64-token chunk) pairs,
+ * e.g. 4 x 8 heads of 2,048 tokens); sizes whose dn_chunk_fwd_workspace()
+ * exceeds it return DN_ESCRATCH before any HIP call. The call allocates
+ * nothing and frees nothing. Every call on one GPU uses that GPU's array and
+ * leaves its contents behind (nothing in it needs clearing between calls):
+ * calls that overlap in time on one GPU race, so run them on one stream or
+ * serialize them.
+ */
+int dn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* beta,
+                         const void* g, const float* S0, void* o, float* S_final,
+                         int B, int H, int T, int dk, int dv, int dtype, void* stream);
 
 /*
  * Whether the latest one-launch prefill (dn_chunk_fwd_fused, or dn_chunk_fwd

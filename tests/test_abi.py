@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 28, names
+    assert len(names) == 29, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol():
 def test_version_and_strerror():
     lib = _lib.lib()
     assert lib.dn_version() >= 3   # workspace holds the start-state copy since 3
-    for code in (0, -1, -2, -3, -4, -5, 7):
+    for code in (0, -1, -2, -3, -4, -5, -6, 7):
         s = lib.dn_strerror(code)
         assert isinstance(s, bytes) and len(s) > 0
 
@@ -468,3 +468,26 @@ def test_handoff_status_validation():
     assert fn(WS, need - 1, 1, 2, 4096, 128, 128, 1, None) == W
     assert fn(WS + 128, need, 1, 2, 4096, 128, 128, 1, None) == W
     assert fn(None, 0, 1, 2, 0, 128, 128, 1, None) == _lib.DN_OK   # T == 0: nothing ran
+
+
+def test_noalloc_validation():
+    """dn_chunk_fwd_noalloc checks its arguments like dn_chunk_fwd, and rejects
+    sizes beyond its built-in scratch, all before any HIP call."""
+    lib = _lib.lib()
+    fn = lib.dn_chunk_fwd_noalloc
+
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, beta=P, g=P, S0=P, o=P, S_final=P, B=1, H=1, T=64, dk=128, dv=128,
+                 dtype=1, stream=None)
+        a.update(kw)
+        return fn(*[a[n] for n in ("q", "k", "v", "beta", "g", "S0", "o", "S_final", "B", "H", "T",
+                                   "dk", "dv", "dtype", "stream")])
+    assert call(q=None) == _lib.DN_EINVAL
+    assert call(o=MIS) == _lib.DN_EINVAL
+    assert call(B=0) == _lib.DN_EINVAL
+    assert call(dk=96, dv=96) == _lib.DN_ENOTSUP
+    # 128 MiB of scratch: 4 x 8 heads of 2048 tokens fit (about 75 MiB at
+    # bf16, d = 128), 4 x 32 heads of 8192 tokens do not
+    assert lib.dn_chunk_fwd_workspace(4, 8, 2048, 128, 128, 1) <= 128 << 20
+    assert call(B=4, H=32, T=8192) == _lib.DN_ESCRATCH
+    assert call(B=1, H=1, T=1 << 20, dtype=0) == _lib.DN_ESCRATCH
