@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdeltanet.so")
-SOURCES = ["abi.hip", "decode.hip", "chunk.hip", "layer.hip", "gdr.hip", "gdr_chunk.hip"]
+SOURCES = ["abi.hip", "decode.hip", "chunk.hip", "chunk_kda.hip", "layer.hip", "gdr.hip", "gdr_chunk.hip"]
 ARCH = os.environ.get("DN_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

@@ -74,8 +74,6 @@ int chunk_common(int kind, const void* q, const void* k, const void* v, const vo
     int st = check_common(q, k, v, beta, g, kind == dn::KIND_KDA, S0, o, S_final, B, H, T, dk,
                           dv, dtype);
     if (st != DN_OK) return st;
-    // fp32 KDA at d = 128 does not fit the prep kernel's LDS budget
-    if (kind == dn::KIND_KDA && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
     const long long BH = (long long)B * H;
     if (T == 0) {
         if (!S_final) return DN_OK;
@@ -159,7 +157,7 @@ const char* dn_strerror(int status) {
         case DN_OK: return "success";
         case DN_EINVAL: return "invalid argument (NULL or misaligned pointer, bad size or dtype)";
         case DN_ENOTSUP: return "unsupported configuration (d_k, d_v must be equal and in {64, 128}; "
-                                "no chunked fp32 KDA at d = 128; dn_chunk_fwd_fused: no one-launch form)";
+                                "dn_chunk_fwd_fused: no one-launch form)";
         case DN_EWORKSPACE: return "workspace missing, misaligned or smaller than dn_chunk_fwd_workspace()";
         case DN_EHIP: return "HIP runtime error at kernel launch";
         case DN_ESCRATCH: return "sizes need more scratch than dn_chunk_fwd_noalloc's built-in 128 MiB "
@@ -252,7 +250,6 @@ int dn_chunk_fwd_states(int kda, const void* q, const void* k, const void* v, co
     if (st != DN_OK) return st;
     if (T > 0 && !S_chunks) return DN_EINVAL;
     if (misaligned(S_chunks)) return DN_EINVAL;
-    if (kda && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
     const long long BH = (long long)B * H;
     if (T == 0) {
         if (!S_final) return DN_OK;
@@ -301,7 +298,6 @@ int dn_chunk_fwd_varlen(int kda, const void* q, const void* k, const void* v, co
     if (N < 1 || !cu_seqlens || misaligned(cu_seqlens, 4)) return DN_EINVAL;
     int st = check_common(q, k, v, beta, g, kda != 0, S0, o, S_final, 1, H, T, dk, dv, dtype);
     if (st != DN_OK) return st;
-    if (kda && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
     const long long rows = (long long)N * H;
     const long long nc = ((long long)T + 63) / 64 + N;
     if (rows > (1LL << 24) || nc * H > 0x7fffffffLL) return DN_EINVAL;
@@ -376,7 +372,6 @@ int dn_ssm_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
     // (g stands in for beta in the shared checks: the state-space kind has none)
     const int st = check_common(q, k, v, g, g, false, S0, o, S_final, B, H, T, dk, dv, dtype);
     if (st != DN_OK) return st;
-    if (dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
     return chunk_common(dn::KIND_SSM, q, k, v, g, g, S0, o, S_final, B, H, T, dk, dv, dtype,
                         workspace, workspace_bytes, stream, dn::FWD_TWO);
 }
@@ -478,7 +473,6 @@ int dn_chunk_prep(int kda, const void* q, const void* k, const void* v, const vo
     // o is not touched by this phase: q stands in for it in the shared checks
     int st = check_common(q, k, v, beta, g, kda != 0, nullptr, q, nullptr, B, H, T, dk, dv, dtype);
     if (st != DN_OK) return st;
-    if (kda && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
     if (T == 0) return DN_OK;
     const long long BH = (long long)B * H;
     st = check_workspace(BH, T, dk, dv, dtype, workspace, workspace_bytes);
@@ -493,7 +487,6 @@ int dn_chunk_scan(int kda, const void* q, const float* S0, void* o, float* S_fin
     // k, v and beta are not read by this phase: q stands in for them
     int st = check_common(q, q, q, q, nullptr, false, S0, o, S_final, B, H, T, dk, dv, dtype);
     if (st != DN_OK) return st;
-    if (kda && dtype == DN_F32 && dk == 128) return DN_ENOTSUP;
     const long long BH = (long long)B * H;
     if (T == 0) {
         if (!S_final) return DN_OK;

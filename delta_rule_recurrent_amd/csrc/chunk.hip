@@ -17,7 +17,7 @@
 //   chunk_prep_kernel  one workgroup per (head, chunk), all chunks in parallel:
 //                      G, A (MFMA), T (forward substitution in LDS), W, u
 //                      (MFMA), the masked decayed Q K^T and the decay-scaled
-//                      Q and K^T; everything the sequential part needs is
+//                      K^T (fp32 at d = 128); everything the sequential part needs is
 //                      written to the workspace in the exact per-lane MFMA
 //                      fragment order the scan loads (one coalesced 16-byte
 //                      load per lane per fragment).
@@ -31,6 +31,8 @@
 //   chunk_fused_kernel both in one launch: prep workgroups hand chunk blocks
 //                      to the scan workgroups of the same XCD as they finish
 //                      (long sequences, bf16).
+// KDA's prep (per-channel decay) is in chunk_kda.hip; it writes the same
+// workspace blocks, which the scan here reads.
 #include <atomic>
 #include <cstdlib>
 #include <random>
@@ -41,49 +43,19 @@
 
 namespace dn {
 
-// ---------------------------------------------------------------------------
-// Workspace layout of one (head, chunk) block. Fragment arrays are
-// [tile][k-block][lane][8] elements of E (see the fragment convention in
-// dn_device.h); D-tile arrays are [tile][tile][lane][4].
-//   W   [4 token tiles][DK/32][64][8]      W = T (beta e^G K)          A-fragments
-//   Qt  [4 token tiles][DK/32][64][8]      Q~ = e^G * Q (KDA only)     A-fragments
-//   Kt  [DK/16 chan tiles][2][64][8]       K~^T = (e^{G_C - G} K)^T    A-fragments
-//   At  [4 token tiles][2][64][8]          attn = tril(Q K^T D)         A-fragments
-//   Uu  [DV/16 col tiles][4 token tiles][64][4]  u = T (beta V)         D-tiles
-//                                          (a 16-column slice is contiguous)
-//   gam [DK] float                         e^{G_C} per key channel (Gated: all equal)
-//   eg  [64] float                         e^{G_t} per token (Gated / DeltaNet: the
-//                                          scan reads Q itself and scales Q S by it)
-// ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
-struct WsLayout {
-    static constexpr long W_OFF = 0;
-    static constexpr long Q_OFF = W_OFF + 4L * (DK / 32) * 64 * 8;
-    static constexpr long K_OFF = Q_OFF + 4L * (DK / 32) * 64 * 8;
-    static constexpr long A_OFF = K_OFF + (DK / 16) * 2L * 64 * 8;
-    static constexpr long U_OFF = A_OFF + 4L * 2 * 64 * 8;
-    static constexpr long E_END = U_OFF + 4L * (DV / 16) * 64 * 4;
-    static constexpr long GAM_BYTE_OFF = (E_END * (long)sizeof(E) + 255) / 256 * 256;
-    static constexpr long EG_BYTE_OFF = GAM_BYTE_OFF + DK * 4L;
-    static constexpr long BYTES = (EG_BYTE_OFF + 64 * 4L + 255) / 256 * 256;
-};
-
 // LDS carve-up of the prep kernel (bytes). Regions X and Y are reused as the
 // work moves on (each switch is separated by a workgroup barrier):
 //   X : K rows     -> fp32 T (diagonal 16x16 inverses)          -> T' = T diag(beta e^G)
 //   Y : Q rows     -> fp32 system matrix A                      -> T'' = T diag(beta)
-//   KT: K^T (token index contiguous; KDA: becomes K~^T in place)
+//   KT: K^T (token index contiguous)
 //   VT: V^T
-//   XT: KDA only, (e^G K)^T
-//   GK: KDA only, fp32 running log-decay per (token, key channel)
 template <typename E, int DK, int DV, int KIND>
 struct PrepSmem {
+    static_assert(KIND != KIND_KDA, "KDA has its own prep kernel");
     static constexpr int KP = 16 / sizeof(E);  // row padding: one 16-byte vector
     static constexpr int LDK = DK + KP;        // [64][DK] tiles
     static constexpr int LDT = 64 + KP;        // [D][64] tiles
     static constexpr int LDF = 68;             // fp32 64x64 matrices
-    static constexpr bool KDA = (KIND == KIND_KDA);
-    static constexpr int LDG = DK + 4;
     static constexpr long cmax(long a, long b) { return a > b ? a : b; }
     static constexpr long SZ_X = cmax(cmax(64L * LDK * sizeof(E), 64L * LDF * 4), 64L * LDT * sizeof(E));
     static constexpr long SZ_Y = SZ_X;
@@ -91,13 +63,13 @@ struct PrepSmem {
     static constexpr long OFF_Y = OFF_X + SZ_X;
     static constexpr long OFF_KT = OFF_Y + SZ_Y;
     static constexpr long OFF_VT = OFF_KT + (long)DK * LDT * sizeof(E);
-    static constexpr long OFF_XT = OFF_VT + (long)DV * LDT * sizeof(E);
-    static constexpr long OFF_GK = OFF_XT + (KDA ? (long)DK * LDT * sizeof(E) : 0);
-    static constexpr long TOTAL = OFF_GK + (KDA ? 64L * LDG * 4 : 0);
+    static constexpr long TOTAL = OFF_VT + (long)DV * LDT * sizeof(E);
 };
 
 // ---------------------------------------------------------------------------
-// Prep kernel: one workgroup (4 wavefronts) per (head, chunk).
+// Prep kernel: one workgroup (4 wavefronts) per (head, chunk); DeltaNet, Gated
+// DeltaNet and the state-space kind in fp32 at d = 128, where the two-wavefront
+// prep's fragments do not fit its registers.
 // ---------------------------------------------------------------------------
 // Two workgroups share a compute unit where the LDS allows it; the register
 // budget is capped accordingly.
@@ -115,8 +87,7 @@ void chunk_prep_kernel(const E* __restrict__ q,
     typedef PrepSmem<E, DK, DV, KIND> Sm;
     typedef typename Frag<E>::type F;
     typedef typename Vec4<E>::type V4;
-    constexpr int LDK = Sm::LDK, LDT = Sm::LDT, LDF = Sm::LDF, LDG = Sm::LDG;
-    constexpr bool KDA = Sm::KDA;
+    constexpr int LDK = Sm::LDK, LDT = Sm::LDT, LDF = Sm::LDF;
 
     __shared__ __align__(16) char smem[Sm::TOTAL];
     __shared__ float Gs[64], eG[64], eGC[64], bs[64];
@@ -128,8 +99,6 @@ void chunk_prep_kernel(const E* __restrict__ q,
     E* Tpp = reinterpret_cast<E*>(smem + Sm::OFF_Y);
     E* KsT = reinterpret_cast<E*>(smem + Sm::OFF_KT);
     E* VsT = reinterpret_cast<E*>(smem + Sm::OFF_VT);
-    E* XsT = reinterpret_cast<E*>(smem + Sm::OFF_XT);
-    float* Gk = reinterpret_cast<float*>(smem + Sm::OFF_GK);
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int gq = lane >> 4, n = lane & 15;
@@ -138,7 +107,7 @@ void chunk_prep_kernel(const E* __restrict__ q,
     // loaded into registers while the current one is computed, and written to
     // LDS when it is done. Prefetches are unconditional (the item index is
     // clamped to the last item).
-    TileRegs<E, DK> rk, rq, rg;   // rg: KDA's per-channel log-decay
+    TileRegs<E, DK> rk, rq;
     TileRegs<E, DV> rv;
     // beta and log-decay of token `lane` (wave 0), kept as loaded: converting
     // (or masking) them right after the load would make the wave wait for
@@ -164,11 +133,10 @@ void chunk_prep_kernel(const E* __restrict__ q,
         tile_load<E, DK>(rk, k + fkey * DK, fA, tid, fL);
         tile_load<E, DK>(rq, q + fkey * DK, fA, tid, fL);
         tile_load<E, DV>(rv, v + ftok * DV, fA, tid, fL);
-        if (KDA) tile_load<E, DK>(rg, g + ftok * DK, fA, tid, fL);
         if (w == 0) {
             const long tk = ftok + min(lane, fA - 1);
-            pbr = beta[tk];
-            if (KIND == KIND_GATED) pgr = g[tk];
+            if (KIND != KIND_SSM) pbr = beta[tk];
+            if (KIND == KIND_GATED || KIND == KIND_SSM) pgr = g[tk];
             pin = lane < fL;
         }
     };
@@ -182,7 +150,6 @@ void chunk_prep_kernel(const E* __restrict__ q,
 
     char* blk = ws + ((long)bh * nchunks + c) * Lw::BYTES;
     E* Wf = reinterpret_cast<E*>(blk) + Lw::W_OFF;
-    E* Qf = reinterpret_cast<E*>(blk) + Lw::Q_OFF;
     E* Kf = reinterpret_cast<E*>(blk) + Lw::K_OFF;
     E* Af = reinterpret_cast<E*>(blk) + Lw::A_OFF;
     E* Uf = reinterpret_cast<E*>(blk) + Lw::U_OFF;
@@ -192,175 +159,67 @@ void chunk_prep_kernel(const E* __restrict__ q,
     const long tok0 = (long)bh * T + t0;
 
     // ---- 1. beta, log-decay and its running sum inside the chunk; stage tiles
-    const float pb = pin ? to_f32(pbr) : 0.f;
-    const float pg = KIND == KIND_GATED && pin ? to_f32(pgr) : 0.f;
+    // the state-space kind has no write strength and no correction: beta = 1
+    // (u = V) and A = 0 (T = I); the W it gets is never read by its scan
+    const float pb = pin ? (KIND == KIND_SSM ? 1.f : to_f32(pbr)) : 0.f;
+    const float pg = (KIND == KIND_GATED || KIND == KIND_SSM) && pin ? to_f32(pgr) : 0.f;
     if (w == 0) bs[lane] = pb;
-    if (!KDA) {
-        if (w == 0) {
-            const float G = wave_inclusive_sum(pg, lane);
-            const float GC = readlane_f(G, 63);
-            Gs[lane] = G;
-            eG[lane] = __expf(G);
-            eGC[lane] = __expf(GC - G);
-            // the chunk decay, replicated per key channel so that the scan reads
-            // it like KDA's (vector loads; no scalar load on its critical path)
-            for (int ch = lane; ch < DK; ch += 64) gam[ch] = __expf(GC);
-        }
-    } else {
-        // the log-decay tile (prefetched with K, Q, V; rows past the end of
-        // the sequence are zero) as fp32 rows, summed over tokens below
-        tile_store_f32<E, DK>(rg, Gk, LDG, tid);
+    if (w == 0) {
+        const float G = wave_inclusive_sum(pg, lane);
+        const float GC = readlane_f(G, 63);
+        Gs[lane] = G;
+        eG[lane] = __expf(G);
+        eGC[lane] = __expf(GC - G);
+        // the chunk decay, replicated per key channel so that the scan reads
+        // it like KDA's (vector loads; no scalar load on its critical path)
+        for (int ch = lane; ch < DK; ch += 64) gam[ch] = __expf(GC);
     }
     tile_store<E, DK, true, true>(rk, Ks, LDK, KsT, LDT, tid);
     tile_store<E, DK, true, false>(rq, Qs, LDK, nullptr, 0, tid);
     tile_store<E, DV, false, true>(rv, nullptr, 0, VsT, LDT, tid);
     lds_barrier();
     fetch((int)min((long)item + gridDim.x, (long)nitems - 1));
-    if constexpr (KDA) {
-        // running sum over the chunk's tokens, in place: 256 / DK threads per
-        // key channel, each over a run of consecutive tokens held in registers
-        // (all of its LDS reads in flight at once); the runs' totals are
-        // passed on through LDS
-        constexpr int SPL = 256 / DK, RUN = CHUNK / SPL;
-        static_assert(256 % DK == 0 && CHUNK % SPL == 0, "token runs");
-        __shared__ float gtot[SPL][DK];
-        const int ch = tid % DK, part = tid / DK;
-        float run[RUN];
-#pragma unroll
-        for (int t = 0; t < RUN; ++t) run[t] = Gk[(part * RUN + t) * LDG + ch];
-#pragma unroll
-        for (int t = 1; t < RUN; ++t) run[t] += run[t - 1];
-        gtot[part][ch] = run[RUN - 1];
-        lds_barrier();
-        float carry = 0.f;
-#pragma unroll
-        for (int p2 = 0; p2 < SPL - 1; ++p2)
-            if (p2 < part) carry += gtot[p2][ch];
-#pragma unroll
-        for (int t = 0; t < RUN; ++t) Gk[(part * RUN + t) * LDG + ch] = run[t] + carry;
-        if (part == SPL - 1) gam[ch] = __expf(run[RUN - 1] + carry);
-        lds_barrier();
-    }
-
-    // ---- 2. attn -> A-fragments, Q~ -> A-fragments; raw K K^T kept in registers
+    // ---- 2. attn -> A-fragments; raw K K^T kept in registers
     // Wave w owns token tile w: rows i in [16w, 16w+16) of A and of attn.
-    // KDA: the decay exp(G_ic - G_jc) sits inside the contraction, so it is
-    // split between the two operands at a token r with j <= r < i:
-    // k_i exp(G_i - G_r) and k_j exp(G_r - G_j). Every factor is a decay
-    // (exponent <= 0), so nothing overflows whatever the decay's strength:
-    // tiles before the row tile split at their last token, pairs inside the
-    // row tile by the levels of a binary split of its 16 tokens.
     f32x4 sa[4];
     {
         F ka[DK / 32], qa[DK / 32];
-        if (!KDA) {
 #pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                ka[kb] = frag_rows<E>(Ks, LDK, 16 * w, 32 * kb, lane);
-                qa[kb] = frag_rows<E>(Qs, LDK, 16 * w, 32 * kb, lane);
-            }
+        for (int kb = 0; kb < DK / 32; ++kb) {
+            ka[kb] = frag_rows<E>(Ks, LDK, 16 * w, 32 * kb, lane);
+            qa[kb] = frag_rows<E>(Qs, LDK, 16 * w, 32 * kb, lane);
         }
         f32x4 at[4];
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
             sa[jt] = zero4();
             at[jt] = zero4();
-            if (!KDA && jt <= w) {
+            if (jt <= w) {
 #pragma unroll
                 for (int kb = 0; kb < DK / 32; ++kb) {
                     const F kj = frag_rows<E>(Ks, LDK, 16 * jt, 32 * kb, lane);
-                    sa[jt] = mma(ka[kb], kj, sa[jt]);  // (K K^T)[i][j]
+                    if (KIND != KIND_SSM) sa[jt] = mma(ka[kb], kj, sa[jt]);  // (K K^T)[i][j]
                     at[jt] = mma(kj, qa[kb], at[jt]);  // (K Q^T)[j][i] = attn^T
-                }
-            } else if (KDA && jt < w) {
-                // KDA, tile jt before the row tile: split the decay at the last
-                // token e of tile jt, exp(G_i - G_j) = exp(G_i - G_e) exp(G_e - G_j),
-                // both exponents <= 0 (i > e >= j)
-                const int ref = 16 * jt + 15;
-#pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb) {
-                    const F ki = frag_rows_decay<E>(Ks, LDK, Gk, LDG, 16 * w, 32 * kb, lane, ref, 1.f);
-                    const F qi = frag_rows_decay<E>(Qs, LDK, Gk, LDG, 16 * w, 32 * kb, lane, ref, 1.f);
-                    const F kj = frag_rows_decay<E>(Ks, LDK, Gk, LDG, 16 * jt, 32 * kb, lane, ref, -1.f);
-                    sa[jt] = mma(ki, kj, sa[jt]);
-                    at[jt] = mma(kj, qi, at[jt]);
-                }
-            } else if (KDA && jt == w) {
-                // KDA, pairs inside the row tile: one product per level of the
-                // binary split (frag_rows_level), each entry taken from the level
-                // of its pair; the diagonal of attn (decay exp(0) = 1) unscaled
-                f32x4 ls[4], lt[4], dg = zero4();
-#pragma unroll
-                for (int lv = 1; lv <= 4; ++lv) {
-                    ls[lv - 1] = zero4();
-                    lt[lv - 1] = zero4();
-#pragma unroll
-                    for (int kb = 0; kb < DK / 32; ++kb) {
-                        const F ki = frag_rows_level<E, true>(Ks, LDK, Gk, LDG, 16 * w, 32 * kb, lane, lv);
-                        const F qi = frag_rows_level<E, true>(Qs, LDK, Gk, LDG, 16 * w, 32 * kb, lane, lv);
-                        const F kj = frag_rows_level<E, false>(Ks, LDK, Gk, LDG, 16 * w, 32 * kb, lane, lv);
-                        ls[lv - 1] = mma(ki, kj, ls[lv - 1]);
-                        lt[lv - 1] = mma(kj, qi, lt[lv - 1]);
-                    }
-                }
-#pragma unroll
-                for (int kb = 0; kb < DK / 32; ++kb)
-                    dg = mma(frag_rows<E>(Ks, LDK, 16 * w, 32 * kb, lane),
-                             frag_rows<E>(Qs, LDK, 16 * w, 32 * kb, lane), dg);
-                auto pick = [&](const f32x4* L, int lv, int e) {
-                    return lv == 1 ? L[0][e] : lv == 2 ? L[1][e] : lv == 3 ? L[2][e] : L[3][e];
-                };
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int a = 4 * gq + e;   // D-tile row (local token)
-                    // K K^T: row i = a, column j = n
-                    sa[jt][e] = a > n ? pick(ls, pair_level(a, n), e) : 0.f;
-                    // attn^T: row j = a, column i = n
-                    at[jt][e] = n > a ? pick(lt, pair_level(n, a), e) : (n == a ? dg[e] : 0.f);
                 }
             }
             // attn^T tile: rows j = 16jt + 4gq + e, column i = 16w + n (causal, incl. diagonal)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 16 * jt + 4 * gq + e, i = 16 * w + n;
-                float val = 0.f;
-                if (i >= j) val = KDA ? at[jt][e] : __expf(Gs[i] - Gs[j]) * at[jt][e];
-                at[jt][e] = val;
+                at[jt][e] = i >= j ? __expf(Gs[i] - Gs[j]) * at[jt][e] : 0.f;
             }
         }
         // attn^T computed with rows = j lands directly as A-fragments of attn (rows i)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
             reinterpret_cast<F*>(Af)[(w * 2 + kb) * 64 + lane] = frag_from_tiles<E>(at[2 * kb], at[2 * kb + 1]);
-        // KDA: Q~ = e^G * Q (one factor per token and key channel), A-fragments
-        // of token tile w in fragment order. Otherwise the scan reads Q itself
-        // and applies the per-token factor e^G (stored per token) to Q S.
-        if (!KDA) {
-            if (w == 0) eg[lane] = eG[lane];
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < DK / 32; ++kb) {
-                F f;
-                const int row = 16 * w + n;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int cc = 32 * kb + 16 * h + 4 * gq;
-                    const V4 m = *reinterpret_cast<const V4*>(Qs + row * LDK + cc);
-                    const f32x4 gr = *reinterpret_cast<const f32x4*>(Gk + row * LDG + cc);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) f[4 * h + j] = from_f32<E>(to_f32(m[j]) * __expf(gr[j]));
-                }
-                reinterpret_cast<F*>(Qf)[(w * (DK / 32) + kb) * 64 + lane] = f;
-            }
-        }
+        // the scan reads Q itself and applies the per-token factor e^G to Q S
+        if (w == 0) eg[lane] = eG[lane];
     }
-    if (!KDA) {
-        // K~^T = (e^{G_C - G} K)^T, A-fragments with rows = key channels
-        for (int p = w; p < (DK / 16) * 2; p += 4) {
-            const int mt = p >> 1, kb = p & 1;
-            reinterpret_cast<F*>(Kf)[p * 64 + lane] =
-                frag_rows_scaled<E>(KsT, LDT, 16 * mt, 32 * kb, lane, 1.f, eGC);
-        }
+    // K~^T = (e^{G_C - G} K)^T, A-fragments with rows = key channels
+    for (int p = w; p < (DK / 16) * 2; p += 4) {
+        const int mt = p >> 1, kb = p & 1;
+        reinterpret_cast<F*>(Kf)[p * 64 + lane] = frag_rows_scaled<E>(KsT, LDT, 16 * mt, 32 * kb, lane, 1.f, eGC);
     }
     lds_barrier();  // K and Q rows are dead from here on
 
@@ -371,27 +230,9 @@ void chunk_prep_kernel(const E* __restrict__ q,
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * w + 4 * gq + e, j = 16 * jt + n;
             float val = 0.f;
-            if (i > j) val = KDA ? bs[i] * sa[jt][e] : bs[i] * __expf(Gs[i] - Gs[j]) * sa[jt][e];
+            if (i > j) val = bs[i] * __expf(Gs[i] - Gs[j]) * sa[jt][e];
             As[i * LDF + j] = val;
         }
-    if (KDA) {
-        // X^T = (e^G K)^T; K^T -> K~^T = (e^{G_C - G} K)^T in place, four
-        // consecutive tokens of one key channel per thread and pass
-        for (int idx = tid; idx < DK * 16; idx += 256) {
-            const int ch = idx / 16, t4 = 4 * (idx % 16);
-            const V4 kv = *reinterpret_cast<const V4*>(KsT + ch * LDT + t4);
-            const float GC = Gk[63 * LDG + ch];
-            V4 xo, ko;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float Gt = Gk[(t4 + u) * LDG + ch];
-                xo[u] = from_f32<E>(to_f32(kv[u]) * __expf(Gt));
-                ko[u] = from_f32<E>(to_f32(kv[u]) * __expf(GC - Gt));
-            }
-            *reinterpret_cast<V4*>(XsT + ch * LDT + t4) = xo;
-            *reinterpret_cast<V4*>(KsT + ch * LDT + t4) = ko;
-        }
-    }
     lds_barrier();
 
     // ---- 3. UT transform T = (I + A)^-1, blocked over 16x16 tiles ------------
@@ -413,12 +254,6 @@ void chunk_prep_kernel(const E* __restrict__ q,
         if (gq == 0) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) Tf[(b0 + i) * LDF + b0 + j] = tc[i];
-        }
-    }
-    if (KDA) {
-        for (int p = w; p < (DK / 16) * 2; p += 4) {
-            const int mt = p >> 1, kb = p & 1;
-            reinterpret_cast<F*>(Kf)[p * 64 + lane] = frag_rows<E>(KsT, LDT, 16 * mt, 32 * kb, lane);
         }
     }
     lds_barrier();
@@ -451,23 +286,23 @@ void chunk_prep_kernel(const E* __restrict__ q,
     {
         const int j = 16 * w + n;
         const float sb = bs[j];
-        const float sbg = KDA ? 0.f : bs[j] * eG[j];
+        const float sbg = bs[j] * eG[j];
 #pragma unroll
         for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int i = 16 * I + 4 * gq + e;
-                if (!KDA) Tp[i * LDT + j] = from_f32<E>(tcol[I][e] * sbg);
+                Tp[i * LDT + j] = from_f32<E>(tcol[I][e] * sbg);
                 Tpp[i * LDT + j] = from_f32<E>(tcol[I][e] * sb);
             }
     }
     lds_barrier();
 
     // ---- 4. W^T = X^T T'^T, computed transposed so it lands as A-fragments of W
-    //         (Gated / DeltaNet: X = K, T' = T diag(beta e^G); KDA: X = e^G K, T' = T diag(beta))
+    //         (X = K, T' = T diag(beta e^G))
     {
-        const E* XT = KDA ? XsT : KsT;
-        const E* TT = KDA ? Tpp : Tp;
+        const E* XT = KsT;
+        const E* TT = Tp;
         f32x4 wt[DK / 16];
 #pragma unroll
         for (int mt = 0; mt < DK / 16; ++mt) {
@@ -820,12 +655,7 @@ __global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict
                                                              const E* __restrict__ beta,
                                                              const E* __restrict__ g,
                                                              char* __restrict__ ws, int T,
-                                                             int nchunks, HeadMap hm,
-                                                             const unsigned long long* guard,
-                                                             unsigned long long gval) {
-    // guard != NULL: recomputation after a one-launch call, done only if that
-    // launch's hand-off failed (its error word holds gval)
-    if (guard && __hip_atomic_load(guard, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gval) return;
+                                                             int nchunks, HeadMap hm) {
     __shared__ Prep2Lds<E, DK, DV> lds;
     const long item = blockIdx.x;
     const long bh = item / nchunks;
@@ -833,6 +663,32 @@ __global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict
     prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV>::BYTES, lds,
                                 bh * T + t0, hm.key(bh) * T + t0, min(CHUNK, T - t0),
                                 (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
+}
+
+// The same prep as the recomputation after a one-launch call: it runs only if
+// that launch's hand-off failed (its error word holds gval). Launched with few
+// workgroups that take the items in turn, so that the usual case (nothing to
+// do) costs one round of workgroups.
+template <typename E, int DK, int DV, int KIND>
+__global__ __launch_bounds__(128, 2) void chunk_prep2_redo_kernel(const E* __restrict__ q,
+                                                                  const E* __restrict__ k,
+                                                                  const E* __restrict__ v,
+                                                                  const E* __restrict__ beta,
+                                                                  const E* __restrict__ g,
+                                                                  char* __restrict__ ws, int T,
+                                                                  int nchunks, long nitems, HeadMap hm,
+                                                                  const unsigned long long* guard,
+                                                                  unsigned long long gval) {
+    if (__hip_atomic_load(guard, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gval) return;
+    __shared__ Prep2Lds<E, DK, DV> lds;
+    for (long item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const long bh = item / nchunks;
+        const int t0 = (int)(item % nchunks) * CHUNK;
+        prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV>::BYTES, lds,
+                                    bh * T + t0, hm.key(bh) * T + t0, min(CHUNK, T - t0),
+                                    (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
+        if (item + gridDim.x < nitems) lds_barrier();   // both wavefronts are done with the LDS
+    }
 }
 
 // Packed sequences of different lengths: item = head * nchunks + global chunk;
@@ -1332,7 +1188,8 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
                                                          float* __restrict__ S_bound, HeadMap hm,
                                                          const unsigned long long* guard,
                                                          unsigned long long gval) {
-    // guard: as in chunk_prep2_kernel
+    // guard != NULL: recomputation after a one-launch call, done only if that
+    // launch's hand-off failed (its error word holds gval)
     if (guard && __hip_atomic_load(guard, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gval) return;
     constexpr int NV = DV / BV;
     // XCD-aware mapping: consecutive workgroups go to different XCDs
@@ -1574,22 +1431,25 @@ static hipError_t prep_t(const void* q, const void* k, const void* v, const void
                          const void* g, void* ws, int BH, int T, hipStream_t st, HeadMap hm) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
     const int nitems = nchunks * BH;
-    // two wavefronts per chunk where their fragments fit in 256 registers
-    if constexpr (KIND != KIND_KDA && (sizeof(E) == 2 || D == 64)) {
+    if constexpr (KIND == KIND_KDA) {
+        return launch_kda_prep<E, D>(q, k, v, beta, g, ws, nitems, T, nchunks, hm, nullptr, st);
+    } else if constexpr (sizeof(E) == 2 || D == 64) {
+        // two wavefronts per chunk where their fragments fit in 256 registers
         hipLaunchKernelGGL((chunk_prep2_kernel<E, D, D, KIND>), dim3((unsigned)nitems), dim3(128), 0, st,
                            (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
-                           (char*)ws, T, nchunks, hm, (const u64*)nullptr, 0ull);
+                           (char*)ws, T, nchunks, hm);
+        return hipGetLastError();
+    } else {
+        // persistent workgroups: as many as fit on the device at once (LDS bound)
+        constexpr long lds = PrepSmem<E, D, D, KIND>::TOTAL + 1024;
+        constexpr int per_cu = (int)(163840 / lds) < 1 ? 1 : (int)(163840 / lds);
+        const long resident = (long)per_cu * device_cu_count();
+        const int grid = (int)(nitems < resident ? nitems : resident);
+        hipLaunchKernelGGL((chunk_prep_kernel<E, D, D, KIND>), dim3((unsigned)grid), dim3(256), 0, st,
+                           (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
+                           (char*)ws, T, nchunks, nitems, hm);
         return hipGetLastError();
     }
-    // persistent workgroups: as many as fit on the device at once (LDS bound)
-    constexpr long lds = PrepSmem<E, D, D, KIND>::TOTAL + 1024;
-    constexpr int per_cu = (int)(163840 / lds) < 1 ? 1 : (int)(163840 / lds);
-    const long resident = (long)per_cu * device_cu_count();
-    const int grid = (int)(nitems < resident ? nitems : resident);
-    hipLaunchKernelGGL((chunk_prep_kernel<E, D, D, KIND>), dim3((unsigned)grid), dim3(256), 0, st,
-                       (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
-                       (char*)ws, T, nchunks, nitems, hm);
-    return hipGetLastError();
 }
 
 template <typename E, int D, int KIND, bool EMIT>
@@ -1686,9 +1546,11 @@ static hipError_t fused_t(const void* q, const void* k, const void* v, const voi
     if (e != hipSuccess) return e;
     // the two phases, which return at once unless this launch's hand-off
     // failed (its error word holds the epoch): then they recompute the call
-    hipLaunchKernelGGL((chunk_prep2_kernel<E, D, D, KIND>), dim3((unsigned)((long)BH * nchunks)), dim3(128), 0,
+    const long pitems = (long)BH * nchunks;
+    const long pgrid = min(pitems, 4L * device_cu_count());
+    hipLaunchKernelGGL((chunk_prep2_redo_kernel<E, D, D, KIND>), dim3((unsigned)pgrid), dim3(128), 0,
                        st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g, (char*)ws, T,
-                       nchunks, hm, err, epoch);
+                       nchunks, pitems, hm, err, epoch);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return scan_launch<E, D, KIND, false>(q, s0c, o, S_final, ws, BH, T, nullptr, st, hm, err, epoch);
@@ -1710,14 +1572,8 @@ static hipError_t prep_kind(int kind, const void* q, const void* k, const void* 
                             hipStream_t st, HeadMap hm) {
     if (kind == KIND_DELTANET) return prep_t<E, D, KIND_DELTANET>(q, k, v, beta, g, ws, BH, T, st, hm);
     if (kind == KIND_GATED) return prep_t<E, D, KIND_GATED>(q, k, v, beta, g, ws, BH, T, st, hm);
-    if (kind == KIND_SSM) {
-        // only the two-wavefront prep has the state-space kind (not fp32 at d = 128)
-        if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
-        else return prep_t<E, D, KIND_SSM>(q, k, v, beta, g, ws, BH, T, st, hm);
-    }
-    // fp32 KDA at d = 128 exceeds the prep kernel's LDS budget (rejected by the ABI layer)
-    if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
-    else return prep_t<E, D, KIND_KDA>(q, k, v, beta, g, ws, BH, T, st, hm);
+    if (kind == KIND_SSM) return prep_t<E, D, KIND_SSM>(q, k, v, beta, g, ws, BH, T, st, hm);
+    return prep_t<E, D, KIND_KDA>(q, k, v, beta, g, ws, BH, T, st, hm);
 }
 
 template <typename E, int D>
@@ -1727,10 +1583,7 @@ static hipError_t scan_kind(int kind, const void* q, const float* S0, void* o, f
     // DeltaNet and Gated DeltaNet share the scan (a unit decay is stored for
     // DeltaNet); the state-space kind drops its W S product
     if (kind == KIND_KDA) return scan_t<E, D, KIND_KDA>(q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
-    if (kind == KIND_SSM) {
-        if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
-        else return scan_t<E, D, KIND_SSM>(q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
-    }
+    if (kind == KIND_SSM) return scan_t<E, D, KIND_SSM>(q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
     return scan_t<E, D, KIND_GATED>(q, S0, o, S_final, ws, BH, T, st, hm, S_bound);
 }
 
@@ -1810,7 +1663,10 @@ static hipError_t varlen_kind_t(const void* q, const void* k, const void* v, con
     hipLaunchKernelGGL(varlen_table_kernel, dim3((unsigned)((nc + 255) / 256)), dim3(256), 0, st, cu,
                        (const int*)cs, N, T, nc, ctab);
     const long nitems = (long)H * nc;
-    if constexpr (KIND != KIND_KDA && (sizeof(E) == 2 || D == 64)) {
+    if constexpr (KIND == KIND_KDA) {
+        const hipError_t e = launch_kda_prep<E, D>(q, k, v, beta, g, ws, nitems, T, nc, HeadMap(), ctab, st);
+        if (e != hipSuccess) return e;
+    } else if constexpr (KIND != KIND_KDA && (sizeof(E) == 2 || D == 64)) {
         hipLaunchKernelGGL((chunk_prep2_varlen_kernel<E, D, D, KIND>), dim3((unsigned)nitems), dim3(128),
                            0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g,
                            (char*)ws, T, nc, (const int2*)ctab);
@@ -1840,8 +1696,7 @@ static hipError_t varlen_t(int kind, const void* q, const void* k, const void* v
         return varlen_kind_t<E, D, KIND_DELTANET>(q, k, v, beta, g, S0, o, S_final, cu, N, H, T, ws, st);
     if (kind == KIND_GATED)
         return varlen_kind_t<E, D, KIND_GATED>(q, k, v, beta, g, S0, o, S_final, cu, N, H, T, ws, st);
-    if constexpr (sizeof(E) == 4 && D == 128) return hipErrorNotSupported;
-    else return varlen_kind_t<E, D, KIND_KDA>(q, k, v, beta, g, S0, o, S_final, cu, N, H, T, ws, st);
+    return varlen_kind_t<E, D, KIND_KDA>(q, k, v, beta, g, S0, o, S_final, cu, N, H, T, ws, st);
 }
 
 hipError_t launch_chunk_fwd_varlen(int kind, int dtype, const void* q, const void* k,

@@ -1,12 +1,40 @@
 // dn_chunk.h -- device helpers of the chunkwise kernels (gfx950): token tiles
-// staged through registers, operand fragments read from row-major tiles (with
-// the decay factors of the per-channel kind), small fp32 products on the matrix
-// cores, and range-checked buffer loads.
+// staged through registers, operand fragments read from row-major tiles and
+// from global memory, small fp32 products on the matrix cores, and
+// range-checked buffer loads.
 #pragma once
 
 #include "dn_device.h"
+#include "dn_launch.h"
 
 namespace dn {
+
+// ---------------------------------------------------------------------------
+// Workspace layout of one (head, chunk) block. Fragment arrays are
+// [tile][k-block][lane][8] elements of E (see the fragment convention in
+// dn_device.h); D-tile arrays are [tile][tile][lane][4].
+//   W   [4 token tiles][DK/32][64][8]      W = T (beta e^G K)          A-fragments
+//   Qt  [4 token tiles][DK/32][64][8]      Q~ = e^G * Q (KDA only)     A-fragments
+//   Kt  [DK/16 chan tiles][2][64][8]       K~^T = (e^{G_C - G} K)^T    A-fragments
+//   At  [4 token tiles][2][64][8]          attn = tril(Q K^T D)         A-fragments
+//   Uu  [DV/16 col tiles][4 token tiles][64][4]  u = T (beta V)         D-tiles
+//                                          (a 16-column slice is contiguous)
+//   gam [DK] float                         e^{G_C} per key channel (Gated: all equal)
+//   eg  [64] float                         e^{G_t} per token (Gated / DeltaNet: the
+//                                          scan reads Q itself and scales Q S by it)
+// ---------------------------------------------------------------------------
+template <typename E, int DK, int DV>
+struct WsLayout {
+    static constexpr long W_OFF = 0;
+    static constexpr long Q_OFF = W_OFF + 4L * (DK / 32) * 64 * 8;
+    static constexpr long K_OFF = Q_OFF + 4L * (DK / 32) * 64 * 8;
+    static constexpr long A_OFF = K_OFF + (DK / 16) * 2L * 64 * 8;
+    static constexpr long U_OFF = A_OFF + 4L * 2 * 64 * 8;
+    static constexpr long E_END = U_OFF + 4L * (DV / 16) * 64 * 4;
+    static constexpr long GAM_BYTE_OFF = (E_END * (long)sizeof(E) + 255) / 256 * 256;
+    static constexpr long EG_BYTE_OFF = GAM_BYTE_OFF + DK * 4L;
+    static constexpr long BYTES = (EG_BYTE_OFF + 64 * 4L + 255) / 256 * 256;
+};
 
 template <typename E> struct Vec16;
 template <> struct Vec16<bf16> { typedef bf16x8 type; };
@@ -77,89 +105,9 @@ __device__ __forceinline__ void tile_store(const TileRegs<E, D>& r, E* rows, int
     }
 }
 
-// Write a loaded tile into LDS as fp32 rows[64][ldr].
-template <typename E, int D>
-__device__ __forceinline__ void tile_store_f32(const TileRegs<E, D>& r, float* rows, int ldr,
-                                               int tid) {
-    typedef TileRegs<E, D> R;
-#pragma unroll
-    for (int it = 0; it < R::ITER; ++it) {
-        const int idx = tid + 256 * it;
-        if (idx >= 16 * R::NV) break;
-        const int tq = idx / R::NV, cv = idx % R::NV;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int e = 0; e < R::VEC; ++e)
-                rows[(4 * tq + u) * ldr + cv * R::VEC + e] = to_f32(r.x[it][u][e]);
-    }
-}
-
-// KDA: fragment of a row-major [64][ld] token tile (rows = tokens, contraction
-// = key channels) with each value multiplied by exp(sgn * (G[row][c] - G[ref][c]))
-// (callers choose ref and sgn so that the exponent is <= 0).
-// The lane's two runs of 4 channels (4g .. 4g+3 and 16+4g .. 16+4g+3 of the
-// block) are read as vectors: two 4-element reads of M, four 16-byte reads of
-// G (row and reference row; ld, ldg, k0 keep them aligned).
-template <typename E>
-__device__ __forceinline__ typename Frag<E>::type frag_rows_decay(const E* M, int ld, const float* G,
-                                                                  int ldg, int row0, int k0,
-                                                                  int lane, int ref, float sgn) {
-    typedef typename Vec4<E>::type V4;
-    const int g = lane >> 4, r = lane & 15;
-    const int row = row0 + r;
-    typename Frag<E>::type f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int c = k0 + 16 * h + 4 * g;
-        const V4 m = *reinterpret_cast<const V4*>(M + row * ld + c);
-        const f32x4 gr = *reinterpret_cast<const f32x4*>(G + row * ldg + c);
-        const f32x4 gf = *reinterpret_cast<const f32x4*>(G + ref * ldg + c);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) f[4 * h + j] = from_f32<E>(to_f32(m[j]) * __expf(sgn * (gr[j] - gf[j])));
-    }
-    return f;
-}
-
-// KDA, pairs inside one 16-token tile: the fragment of level lv (1..4) of a
-// binary split of the tile's tokens. At level lv the tile is cut into groups of
-// 2^lv tokens; a pair (i > j) belongs to the one level at which i and j share
-// a group but lie in different halves of it. With r the last token of the
-// group's lower half, the decay of such a pair factors exactly as
-//     exp(G_i - G_j) = exp(G_i - G_r) * exp(G_r - G_j),
-// both exponents <= 0. UPPER: rows of the upper halves scaled by
-// exp(G_row - G_r) (the other rows zero); otherwise rows of the lower halves
-// scaled by exp(G_r - G_row). A product of the two gives the level's pairs
-// exactly; its other entries (pairs of different groups) are finite and
-// discarded by the caller.
-template <typename E, bool UPPER>
-__device__ __forceinline__ typename Frag<E>::type frag_rows_level(const E* M, int ld, const float* G,
-                                                                  int ldg, int row0, int k0,
-                                                                  int lane, int lv) {
-    typedef typename Vec4<E>::type V4;
-    const int g = lane >> 4, r = lane & 15;
-    const int sz = 1 << lv, half = sz >> 1;
-    const bool in = UPPER ? ((r & (sz - 1)) >= half) : ((r & (sz - 1)) < half);
-    const int row = row0 + r;
-    const int ref = row0 + (r & ~(sz - 1)) + half - 1;
-    typename Frag<E>::type f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int c = k0 + 16 * h + 4 * g;
-        const V4 m = *reinterpret_cast<const V4*>(M + row * ld + c);
-        const f32x4 gr = *reinterpret_cast<const f32x4*>(G + row * ldg + c);
-        const f32x4 gf = *reinterpret_cast<const f32x4*>(G + ref * ldg + c);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const float x = UPPER ? gr[j] - gf[j] : gf[j] - gr[j];
-            f[4 * h + j] = from_f32<E>(to_f32(m[j]) * __expf(in ? x : -INFINITY));
-        }
-    }
-    return f;
-}
-
-// The level (1..4) of the binary split that holds the pair of local token
-// indices a > b of one 16-token tile: the highest bit in which they differ.
+// The level of the binary split of a chunk's tokens that holds the pair of
+// token indices a > b: one plus the highest bit in which they differ (1..4 for
+// a pair inside one 16-token tile).
 __device__ __forceinline__ int pair_level(int a, int b) { return 32 - __clz(a ^ b); }
 
 // fp32 16x16x16 product on the matrix cores, acc += X * Y, with X a 16x16

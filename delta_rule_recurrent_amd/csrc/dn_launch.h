@@ -87,6 +87,15 @@ size_t chunk_handoff_offset(long long BH, long long T, int dk, int dtype);
 // Workspace bytes of the chunkwise prefill (per call).
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype);
 
+// KDA's chunk-parallel phase (chunk_kda.hip): nitems = head rows x nchunks
+// (head, chunk) blocks of the workspace; with ctab (int2 per chunk: first token,
+// length; length 0 = unused slot) the rows hold packed sequences.
+// E is the element type (float or the device bf16), D = d_k = d_v.
+template <typename E, int D>
+hipError_t launch_kda_prep(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                           void* ws, long nitems, int T, int nchunks, HeadMap hm, const void* ctab,
+                           hipStream_t st);
+
 // The gated layer around the rule (d = d_k = d_v). Prologue: causal
 // convolution + SiLU of the token-major q/k/v channel rows, head split,
 // L2 norm of q and k (q also scaled by d^-1/2), gates beta = beta_scale *

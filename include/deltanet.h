@@ -49,7 +49,7 @@ typedef enum dn_status {
     DN_EINVAL = -1,     /* a required pointer is NULL or misaligned, B/H < 1, T < 0,
                            an unknown dtype, or more than 2^24 heads / 2^31-1 chunks */
     DN_ENOTSUP = -2,    /* d_k, d_v outside {64, 128} or d_k != d_v, or no such form
-                           (see dn_kda_chunk_fwd, dn_chunk_fwd_fused) */
+                           (see dn_chunk_fwd_fused) */
     DN_EWORKSPACE = -3, /* workspace NULL or smaller than dn_chunk_fwd_workspace() */
     DN_EHIP = -4,       /* the HIP runtime reported an error at launch */
     DN_EHANDOFF = -5,   /* dn_chunk_fwd_handoff_status only: the latest one-launch
@@ -394,8 +394,7 @@ int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* ou
  * identity. There is no beta. Arguments as for dn_chunk_fwd / dn_recurrent_fwd
  * / dn_decode_step without beta, and g is REQUIRED (pass zeros for plain
  * causal linear attention). The chunked form uses dn_chunk_fwd_workspace()
- * bytes and is not provided for fp32 at d = 128 (DN_ENOTSUP; the recurrent
- * form covers it). Each returns DN_EINVAL when g is NULL.
+ * bytes. Each returns DN_EINVAL when g is NULL.
  */
 int dn_ssm_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                      const float* S0, void* o, float* S_final, int B, int H, int T, int dk, int dv,

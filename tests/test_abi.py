@@ -95,7 +95,6 @@ def test_chunk_validation(fn):
     assert _chunk(fn, B=1 << 20, H=1 << 10) == E   # heads beyond the grid limit
     if fn == "dn_kda_chunk_fwd":
         assert _chunk(fn, g=None) == E               # KDA needs its per-channel decay
-        assert _chunk(fn, dtype=0, dk=128, dv=128) == N
     if fn == "dn_chunk_fwd_fused":
         assert _chunk(fn, dtype=0) == N              # the one-launch form is bf16 only
         assert _chunk(fn, dtype=0, q=None) == E      # argument errors still come first
@@ -117,7 +116,6 @@ def test_boundary_states_validation():
     assert _states(q=None) == E
     assert _states(B=0) == E
     assert _states(kda=1, g=None) == E           # KDA needs its per-channel decay
-    assert _states(kda=1, dtype=0, dk=128, dv=128) == N
     assert _states(dk=96, dv=96) == N
     assert _states(ws=None) == W
     assert _states(ws_bytes=16) == W
@@ -156,7 +154,6 @@ def test_shared_key_heads_validation():
         assert fn(dk=96, dv=96) == N
     assert _gqa(ws=None) == W
     assert _gqa(ws_bytes=16) == W
-    assert _gqa(kda=1, dtype=0, dk=128, dv=128) == N
     assert _gqa_dec(S=None) == E
 
 
@@ -184,7 +181,6 @@ def test_varlen_workspace_and_validation():
     assert _varlen(cu=P + 2) == E              # int array: 4-byte alignment
     assert _varlen(q=None) == E
     assert _varlen(kda=1, g=None) == E
-    assert _varlen(kda=1, dtype=0, dk=128, dv=128) == N
     assert _varlen(dk=96, dv=96) == N
     assert _varlen(ws=None) == W
     assert _varlen(ws_bytes=16) == W
@@ -289,7 +285,6 @@ def test_phase_validation():
     assert _prep(kda=1, g=None) == E
     assert _prep(ws=None) == W
     assert _prep(wsb=8) == W
-    assert _prep(kda=1, dtype=0, dk=128, dv=128) == _lib.DN_ENOTSUP
     assert _scan(o=None) == E
     assert _scan(q=None) == E
     assert _scan(q=ODD) == E
@@ -379,7 +374,6 @@ def test_ssm_validation(fn):
     assert _ssm(fn, dk=96, dv=96) == N
     assert _ssm(fn, dtype=3) == E
     if fn == "dn_ssm_chunk_fwd":
-        assert _ssm(fn, dtype=0, dk=128, dv=128) == N   # fp32 at d = 128: recurrent form only
         assert _ssm(fn, ws=None) == _lib.DN_EWORKSPACE
         assert _ssm(fn, wsb=16) == _lib.DN_EWORKSPACE
     if fn == "dn_ssm_decode_step":

@@ -42,18 +42,12 @@ def _prefill(form, kind, inp):
     return o, S
 
 
-def _supported(kind, dtype, d, form):
-    return not (form == "chunk" and kind == "kda" and dtype == "f32" and d == 128)
-
-
 @pytest.mark.parametrize("form", ["chunk", "recurrent"])
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("T", [1, 16, 37, 64, 65, 200])
 def test_prefill_matches_oracle(form, kind, dtype, d, T):
-    if not _supported(kind, dtype, d, form):
-        pytest.skip("fp32 KDA chunk at d=128 is not provided (LDS budget); recurrent form covers it")
     say("case", form, kind, dtype, d, T)
     inp = make(kind, 2, 3, T, d, dtype, seed=T * 7 + d, s0_std=0.5)
     o, S = _prefill(form, kind, inp)
@@ -183,8 +177,6 @@ def test_decode_equals_one_token_prefill(kind):
     dn = _dn()
     inp = to_dev(make(kind, 4, 4, 1, 128, "f32", seed=21, s0_std=0.5))
     fn = dn.kda_chunk_fwd if kind == "kda" else dn.chunk_fwd
-    if kind == "kda":
-        fn = dn.kda_recurrent_fwd      # fp32 KDA chunk at d=128 is not provided
     o_p, S_p = fn(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], inp["S0"])
     S = inp["S0"].clone()
     dec = dn.kda_decode_step if kind == "kda" else dn.decode_step
@@ -205,8 +197,6 @@ def test_long_prefill(kind, dtype, T):
     place, and bitwise equal to calling the two phases one after the other
     (from 64 chunks on, chunk_fwd runs bf16 DeltaNet / Gated DeltaNet as one
     launch)."""
-    if not _supported(kind, dtype, 128, "chunk"):
-        pytest.skip("fp32 KDA at d = 128 has no chunked form")
     dn = _dn()
     say("long prefill", kind, dtype, T)
     inp = make(kind, 1, 2, T, 128, dtype, seed=23, s0_std=0.5)

@@ -39,8 +39,6 @@ def _inputs(T, d, dtype, seed, decay=1.0):
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("T", [1, 37, 64, 65, 200])
 def test_ssm_matches_oracle(form, dtype, d, T):
-    if form == "chunk" and dtype == "f32" and d == 128:
-        pytest.skip("fp32 chunked form at d=128 is not provided; the recurrent form covers it")
     dn = _dn()
     say("ssm", form, dtype, d, T)
     x = _inputs(T, d, dtype, seed=300 + T + d)
