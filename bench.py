@@ -6,12 +6,17 @@ A step is one chunkwise Gated DeltaNet prefill of the workload
 B=4, H=8, T=2048, d_k=d_v=128, bf16 (seeded synthetic inputs resident in HBM),
 i.e. dn_chunk_fwd = the chunk-parallel UT/WY phase followed by the sequential
 inter-chunk scan. The JSON line reports whole-job token-heads/s (B*H*T per
-second) as `value`, the roofline of the dominant kernel (timed live with HIP
-events on the stream it runs on), the fp64 CPU oracle timed on this host as
-`cpu_baseline`, and, under `decode`, the fused decode step of
-B=256 x H=16, d=128 (1000 steps, fp32 state updated in place) in state-HBM GB/s
-against the HBM peak. The other workloads (long-context prefill, KDA prefill,
-the fp32 DeltaNet recurrent and chunked forms) are timed under `workloads`.
+second) as `value` (K steps back to back between two synchronisations), the
+median step and the median cold step (MALL and L2s flushed before each call),
+the roofline of the dominant kernel (timed live with HIP events on the stream
+it runs on), the fp64 CPU oracle timed on this host as `cpu_baseline`, and the
+parity of the timed outputs against it. `long_context` holds the same record
+for the largest single-GPU workload, B=1, H=16, T=65536 (the one-launch form).
+`decode` holds the fused decode step of B=256 x H=16, d=128 (1000 steps, fp32
+state updated in place) in state-HBM GB/s against the HBM peak. The other
+workloads (KDA prefill, the fp32 DeltaNet recurrent and chunked forms) are timed
+under `workloads`, the serving forms and variants under `serving_forms`, and
+the gated layer's kernels around the rule under `layer`.
 """
 from __future__ import annotations
 
@@ -56,25 +61,33 @@ def log(*a):
 
 
 # HBM traffic per launch from rocprofv3 counter runs (FETCH_SIZE and WRITE_SIZE in
-# KiB per dispatch, each in a run of its own) on the workloads timed here. A plain
-# device copy of 512 MiB reads FETCH_SIZE = 262,158 KiB and WRITE_SIZE = 524,288 KiB,
-# so FETCH_SIZE is scaled by 2.0 and WRITE_SIZE by 1.0. Each entry carries the
-# SHA-256 of the kernel sources it was taken on; when they have changed since,
-# the figure no longer describes the kernel and is reported as null.
+# KiB per dispatch, each in a run of its own, averaged over the dispatches of the
+# kernel at the workload's grid size) on the workloads timed here:
+#   rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --no-cpu
+#       --no-workloads --steps 5 --warmup 2 --cold-reps 2 --decode-steps 20
+# A plain device copy of 512 MiB (bench.py --copy-mib 512) reads FETCH_SIZE =
+# 262,159 KiB and WRITE_SIZE = 524,288 KiB, so FETCH_SIZE is scaled by 2.0 and
+# WRITE_SIZE by 1.0. Each entry carries the SHA-256 of the kernel sources it was
+# taken on; when they have changed since, the figure no longer describes the
+# kernel and is reported as null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
-CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
-                 "delta_rule_recurrent_amd/csrc/dn_launch.h")
+CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurrent_amd/csrc/dn_chunk.h",
+                 "delta_rule_recurrent_amd/csrc/dn_device.h", "delta_rule_recurrent_amd/csrc/dn_launch.h")
 DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
                   "delta_rule_recurrent_amd/csrc/dn_launch.h")
 TRAFFIC = {
-    "chunk_prep2_kernel": {"fetch_kib": 29262.9, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
-                           "sha256": "dd56f4f6f16f042dfbadb4b974e9db43abe5ffddd2a7ec2858fa12bd53c31ed5"},
-    "chunk_scan_kernel": {"fetch_kib": 37103.1, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
-                          "sha256": "dd56f4f6f16f042dfbadb4b974e9db43abe5ffddd2a7ec2858fa12bd53c31ed5"},
-    "chunk_fused_kernel": {"fetch_kib": 62018.5, "write_kib": 76652.9, "sources": CHUNK_SOURCES,
-                           "sha256": "dd56f4f6f16f042dfbadb4b974e9db43abe5ffddd2a7ec2858fa12bd53c31ed5"},
-    "decode_step_kernel": {"fetch_kib": 136309.6, "write_kib": 263168.0, "sources": DECODE_SOURCES,
-                           "sha256": "74f4a1e0ef92f2aee9dbd9ed668d70f9e1ee2e41e77559b6eb24fa94dbbaac1a"},
+    # B=4 H=8 T=2048 d=128 (grid 1024 x 128 threads; 3554 / 3894 dispatches)
+    "chunk_prep2_kernel": {"fetch_kib": 29899.8, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
+                           "sha256": "d993e92e185f361e75cdc60abe80ec5f4606cd94d48aa1ab2e316a736b0915d6"},
+    # B=4 H=8 T=2048 d=128 (grid 256 x 256 threads; 3554 / 3894 dispatches)
+    "chunk_scan_kernel": {"fetch_kib": 37107.5, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
+                          "sha256": "d993e92e185f361e75cdc60abe80ec5f4606cd94d48aa1ab2e316a736b0915d6"},
+    # B=1 H=16 T=65536 d=128 (grid 224 x 256 threads; 714 / 734 dispatches)
+    "chunk_fused_kernel": {"fetch_kib": 980238.1, "write_kib": 1193988.0, "sources": CHUNK_SOURCES,
+                           "sha256": "d993e92e185f361e75cdc60abe80ec5f4606cd94d48aa1ab2e316a736b0915d6"},
+    # B=256 H=16 d=128, one token (311 dispatches each)
+    "decode_step_kernel": {"fetch_kib": 136307.8, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+                           "sha256": "09de62aed945e212144a0bc31bcc3dc4e0cafaa31057c40c0c6285a057b47873"},
 }
 
 
@@ -111,6 +124,90 @@ def event_time_ms(torch, fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def call_times_ms(torch, fn, reps, flush=None):
+    """Durations in ms of `reps` calls of fn, each between its own pair of HIP
+    events on the current stream (the stream every entry point here launches
+    on). Warm (flush None): the calls run back to back. Cold: before each call,
+    outside its events, `flush` (a copy through two 512 MiB buffers, twice the
+    256 MB MALL) evicts what the earlier calls left in the MALL and the L2s."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for e0, e1 in evs:
+        if flush is not None:
+            flush()
+        e0.record()
+        fn()
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def launch_means_ms(torch, fn, groups, per_group):
+    """Mean duration of one fn() (one kernel launch) in each of `groups` groups of
+    `per_group` launches back to back between one pair of HIP events on the
+    current stream, after one untimed launch. Back to back, the launches run
+    one after the other with no gap, so a group's mean matches the per-dispatch
+    average of a kernel trace (events around single launches would add each
+    launch's start-up latency)."""
+    fn()
+    out = []
+    for _ in range(groups):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(per_group):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / per_group)
+    return out
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def make_flush(torch, dev):
+    a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    return lambda: b.copy_(a)
+
+
+def settle(torch, step, seconds):
+    """Untimed calls, after the warmup steps, until `seconds` of wall time have
+    passed: the timed region then starts with the GPU's clocks already up (a
+    few warmup steps of tens of microseconds leave it at its idle clocks).
+    Returns the number of calls."""
+    t0, n = time.perf_counter(), 0
+    while True:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+        n += 20
+        if time.perf_counter() - t0 >= seconds:
+            return n
+
+
+def timed_steps(torch, step, steps):
+    """The contract's timing: `steps` calls back to back between a barrier and a
+    device synchronisation on both sides, one HIP event before each call and one
+    after the last. Returns (mean ms per call over the whole bracket, median of
+    the per-call event intervals, wall seconds)."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(steps):
+        evs[i].record()
+        step()
+    evs[steps].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return evs[0].elapsed_time(evs[steps]) / steps, median(per), t_wall
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +221,12 @@ def main():
     ap.add_argument("--no-decode", action="store_true", help="skip the decode workload")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the headline prefill (for profiling the other kernels alone)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long-context prefill (B=1, H=16, T=65536)")
+    ap.add_argument("--settle", type=float, default=1.0,
+                    help="seconds of untimed calls after the warmup steps of each prefill workload")
+    ap.add_argument("--cold-reps", type=int, default=10,
+                    help="calls timed after a flush of the MALL and L2s (0: none)")
     ap.add_argument("--serving-only", action="store_true",
                     help="only time the serving forms and variants (for profiling their kernels)")
     ap.add_argument("--layer-only", action="store_true",
@@ -170,10 +273,18 @@ def main():
         print(json.dumps({"layer": run_layer(torch, dn, synthetic, to_dev, dev)}), flush=True)
         return
 
+    flush = make_flush(torch, dev) if args.cold_reps else None
+
     # ------------------------------------------------------------------ prefill
     result = {}
     if not args.no_prefill:
-        result = run_prefill(args, torch, np, dn, synthetic, to_dev, dev)
+        result = run_prefill(args, torch, np, dn, synthetic, to_dev, dev,
+                             "gdn_prefill_b4_h8_t2048_d128", flush)
+    if not args.no_long:
+        # the largest single-GPU workload, with its own roofline and CPU baseline
+        result["long_context"] = run_prefill(args, torch, np, dn, synthetic, to_dev, dev,
+                                             "gdn_prefill_b1_h16_t65536_d128", flush)
+    del flush
 
     # ------------------------------------------------------------------- decode
     if not args.no_decode:
@@ -188,10 +299,73 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def run_prefill(args, torch, np, dn, synthetic, to_dev, dev):
-    name = "gdn_prefill_b4_h8_t2048_d128"
+def cpu_oracle(args, np, inp_cpu, o, S_final, label):
+    """The fp64 oracle on the whole workload, repeated until args.cpu_seconds of
+    wall time have passed, and the parity of the timed GPU outputs against it."""
+    import oracle
+
+    nthreads = len(os.sched_getaffinity(0))
+    log("cpu oracle on %d threads (%s)" % (nthreads, label))
+    reps, t = 0, 0.0
+    while reps == 0 or t < args.cpu_seconds:
+        t0 = time.perf_counter()
+        o_ref, S_ref = oracle.recurrent(inp_cpu["q"], inp_cpu["k"], inp_cpu["v"],
+                                        inp_cpu["beta"], inp_cpu["g"], None, nthreads=nthreads)
+        t += time.perf_counter() - t0
+        reps += 1
+    tokens = int(np.prod(inp_cpu["q"].shape[:3]))
+    base = {
+        "value": round(tokens * reps / t, 1), "unit": "tokens/s",
+        "cores": oracle.max_threads(nthreads), "kind": "oracle",
+        "sample": "the whole workload (%s; fp64 token-by-token recurrence) run %d times back "
+                  "to back, %.2f s in total" % (label, reps, t),
+    }
+    og = o.float().cpu().double().numpy()
+    sg = S_final.cpu().double().numpy()
+    parity = {
+        "o": float(np.abs(og - o_ref).max() / np.abs(o_ref).max()),
+        "S_final": float(np.abs(sg - S_ref).max() / np.abs(S_ref).max()),
+        "bound": 2e-2, "metric": "max|gpu-ref|/max|ref|",
+    }
+    log("cpu oracle %.2f s, parity %s" % (t, parity))
+    return base, parity
+
+
+def kernel_entry(ms_list, flop, per_group):
+    """ms: mean launch duration over all groups; median_ms: median of the groups' means."""
+    ms = sum(ms_list) / len(ms_list)
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 5), "median_ms": round(median(ms_list), 5), "flop": flop,
+            "launches": len(ms_list) * per_group,
+            "timing": "%d groups of %d launches back to back" % (len(ms_list), per_group),
+            "tflops": round(tf, 2), "frac_mfma": round(tf / PEAK_BF16_TFLOPS, 4)}
+
+
+def roofline_block(name, e):
+    return {
+        "kernel": name, "bound": "mfma",
+        "achieved": e["tflops"], "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": e["frac_mfma"],
+        "traffic": traffic_bytes(name),
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
+        "algorithmic_flop_per_launch": e["flop"],
+        "avg_launch_ms": e["ms"],
+    }
+
+
+def run_prefill(args, torch, np, dn, synthetic, to_dev, dev, name, flush):
+    """One chunked Gated DeltaNet prefill workload: the contract's K-step timing,
+    warm and cold medians, the dominant kernel's roofline from live event timing,
+    and the CPU oracle beside it with the parity of the timed outputs.
+
+    At 32 chunks per sequence dn_chunk_fwd runs the two phases (chunk_prep2 then
+    chunk_scan), each timed alone back to back on the same stream; from 64
+    chunks on it runs the one-launch form, whose call is chunk_fused_kernel plus
+    two recomputation launches that return at once when the hand-off succeeded
+    (about 2 us together), so the call's duration stands for the kernel's."""
     cfg = synthetic.CONFIGS[name]
     B, H, T, d = cfg["B"], cfg["H"], cfg["T"], cfg["dk"]
+    nchunks = (T + C - 1) // C
     log("generating", name)
     inp_cpu = synthetic.make_config(name)
     inp = to_dev(inp_cpu)
@@ -203,108 +377,72 @@ def run_prefill(args, torch, np, dn, synthetic, to_dev, dev):
         dn.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], None, o=o,
                      S_final=S_final, workspace=ws)
 
+    steps = args.steps if nchunks < 64 else max(5, args.steps // 4)
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    nsettle = settle(torch, step, args.settle)
+    ms_step, med_step, t_wall = timed_steps(torch, step, steps)
+    cold = call_times_ms(torch, step, args.cold_reps, flush=flush)
     tokens = B * H * T
     value = tokens / (ms_step * 1e-3)
-    log("prefill %.4f ms/step  %.3e token-heads/s (wall %.3f s for %d steps)"
-        % (ms_step, value, t_wall, args.steps))
+    log("%s %.4f ms/step (median %.4f, cold median %.4f)  %.3e token-heads/s (wall %.3f s, %d steps)"
+        % (name, ms_step, med_step, median(cold), value, t_wall, steps))
 
-    # live per-kernel timing (same stream, events around back-to-back launches
-    # of each kernel alone): at 32 chunks per sequence the step is the two
-    # phase kernels; the one-launch form (prep and scan workgroups together,
-    # used from 64 chunks on) is timed beside them on the same inputs
-    prep_ms = event_time_ms(torch, lambda: dn.chunk_prep(inp["q"], inp["k"], inp["v"], inp["beta"],
-                                                         inp["g"], ws), args.steps)
-    scan_ms = event_time_ms(torch, lambda: dn.chunk_scan(inp["q"], o, ws, None, S_final),
-                            args.steps)
-    fused_ms = event_time_ms(torch, lambda: dn.chunk_fwd_fused(
-        inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], None, o=o, S_final=S_final,
-        workspace=ws), args.steps)
-    kern = {
-        "chunk_prep2_kernel": dict(ms=prep_ms, flop=flops_prep(d) * tokens),
-        "chunk_scan_kernel": dict(ms=scan_ms, flop=flops_scan(d) * tokens),
-    }
-    alt = {"chunk_fused_kernel": dict(ms=fused_ms, flop=(flops_prep(d) + flops_scan(d)) * tokens)}
-    for k_, v_ in list(kern.items()) + list(alt.items()):
-        v_["tflops"] = v_["flop"] / (v_["ms"] * 1e-3) / 1e12
-        v_["frac_mfma"] = v_["tflops"] / PEAK_BF16_TFLOPS
-        log("  %s %.4f ms  %.1f TFLOP/s (%.1f%% of bf16 MFMA peak)"
-            % (k_, v_["ms"], v_["tflops"], 100 * v_["frac_mfma"]))
+    groups, per = (5, 20) if nchunks < 64 else (5, 4)
+    if nchunks < 64:
+        kern = {
+            "chunk_prep2_kernel": kernel_entry(launch_means_ms(torch, lambda: dn.chunk_prep(
+                inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], ws), groups, per),
+                flops_prep(d) * tokens, per),
+            "chunk_scan_kernel": kernel_entry(launch_means_ms(torch, lambda: dn.chunk_scan(
+                inp["q"], o, ws, None, S_final), groups, per), flops_scan(d) * tokens, per),
+        }
+    else:
+        kern = {
+            "chunk_fused_kernel": kernel_entry(launch_means_ms(torch, lambda: dn.chunk_fwd_fused(
+                inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], None, o=o, S_final=S_final,
+                workspace=ws), groups, per), (flops_prep(d) + flops_scan(d)) * tokens, per),
+        }
+        # DN_OK unless a hand-off wait of the latest call gave up (its results
+        # were then recomputed by the two phases, and the time includes that)
+        kern["chunk_fused_kernel"]["handoff_status"] = dn.chunk_fwd_handoff_status(
+            ws, B, H, T, d, d, torch.bfloat16)
+    for k_, v_ in kern.items():
+        log("  %s %.4f ms (median %.4f)  %.1f TFLOP/s (%.2f%% of bf16 MFMA peak)"
+            % (k_, v_["ms"], v_["median_ms"], v_["tflops"], 100 * v_["frac_mfma"]))
     dom = max(kern, key=lambda k_: kern[k_]["ms"])
     total_flop = (flops_prep(d) + flops_scan(d)) * tokens
-    path_tflops = total_flop / (ms_step * 1e-3) / 1e12
-    roofline = {
-        "kernel": dom,
-        "bound": "mfma",
-        "achieved": round(kern[dom]["tflops"], 2),
-        "peak": PEAK_BF16_TFLOPS,
-        "unit": "TFLOP/s",
-        "frac": round(kern[dom]["frac_mfma"], 4),
-        "traffic": traffic_bytes(dom),
-        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE x1.0)",
-        "algorithmic_flop_per_launch": kern[dom]["flop"],
-        "avg_launch_ms": round(kern[dom]["ms"], 5),
-    }
-
-    # parity of the benchmarked output and the CPU baseline (fp64 oracle, same inputs)
+    nbytes = bytes_prefill(B, H, T, d)
+    path = lambda ms: {"ms": round(ms, 5),
+                       "tflops": round(total_flop / (ms * 1e-3) / 1e12, 2),
+                       "frac_mfma": round(total_flop / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                       "gbs_algorithmic": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                       "frac_hbm": round(nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "settle": {"seconds": args.settle, "calls": nsettle,
+                   "what": "untimed calls after the warmup steps, before the timed region"},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": name, "B": B, "H": H, "T": T, "d_k": d, "d_v": d, "chunk": C,
-                   "variant": "gated_deltanet", "S0": "zeros"},
-        "roofline": roofline,
-        "prefill_path": {
-            "tflops": round(path_tflops, 2), "frac_mfma": round(path_tflops / PEAK_BF16_TFLOPS, 4),
-            "gbs_algorithmic": round(bytes_prefill(B, H, T, d) / (ms_step * 1e-3) / 1e9, 1),
-            "frac_hbm": round(bytes_prefill(B, H, T, d) / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-            "kernels": {k_: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
-                             for kk, vv in v_.items()} for k_, v_ in kern.items()},
-            "one_launch_form": {k_: {kk: (round(vv, 5) if isinstance(vv, float) else vv)
-                                     for kk, vv in v_.items()} for k_, v_ in alt.items()},
+                   "variant": "gated_deltanet", "S0": "zeros",
+                   "form": "two-phase" if nchunks < 64 else "one-launch"},
+        "timing": {
+            "mean_ms": round(ms_step, 5), "median_ms": round(med_step, 5),
+            "cold_median_ms": round(median(cold), 5), "cold_reps": len(cold),
+            "cold": "a copy of 512 MiB between two buffers (1 GiB of HBM traffic, four times the "
+                    "256 MB MALL) before each cold call, outside its events",
+            "warm_path": path(med_step), "cold_path": path(median(cold)),
+            "algorithmic_flop": total_flop, "algorithmic_bytes": nbytes,
         },
+        "roofline": roofline_block(dom, kern[dom]),
+        "kernels": kern,
     }
-
     if not args.no_cpu:
-        import oracle
-
-        nthreads = len(os.sched_getaffinity(0))
-        log("cpu oracle on %d threads" % nthreads)
-        # the whole workload, repeated until about 10 s of CPU time have passed
-        reps, t = 0, 0.0
-        while reps == 0 or t < args.cpu_seconds:
-            t0 = time.perf_counter()
-            o_ref, S_ref = oracle.recurrent(inp_cpu["q"], inp_cpu["k"], inp_cpu["v"],
-                                            inp_cpu["beta"], inp_cpu["g"], None, nthreads=nthreads)
-            t += time.perf_counter() - t0
-            reps += 1
-        result["cpu_baseline"] = {
-            "value": round(tokens * reps / t, 1), "unit": "tokens/s",
-            "cores": oracle.max_threads(nthreads), "kind": "oracle",
-            "sample": "the whole workload (B=4, H=8, T=2048, d=128; fp64 token-by-token "
-                      "recurrence) run %d times back to back, %.2f s in total" % (reps, t),
-        }
-        og = o.float().cpu().double().numpy()
-        sg = S_final.cpu().double().numpy()
-        result["parity"] = {
-            "o": float(np.abs(og - o_ref).max() / np.abs(o_ref).max()),
-            "S_final": float(np.abs(sg - S_ref).max() / np.abs(S_ref).max()),
-            "bound": 2e-2, "metric": "max|gpu-ref|/max|ref|",
-        }
-        log("cpu oracle %.2f s, parity %s" % (t, result["parity"]))
-
+        label = "B=%d, H=%d, T=%d, d=%d" % (B, H, T, d)
+        result["cpu_baseline"], result["parity"] = cpu_oracle(args, np, inp_cpu, o, S_final, label)
+    del inp, ws, o, S_final, inp_cpu
     return result
 
 
@@ -328,7 +466,7 @@ def run_decode(args, torch, dn, synthetic, to_dev):
         dstep(s)
     torch.cuda.synchronize()
     runs = []
-    for _ in range(3):
+    for _ in range(5):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for s in range(nsteps):
@@ -336,7 +474,7 @@ def run_decode(args, torch, dn, synthetic, to_dev):
         e1.record()
         torch.cuda.synchronize()
         runs.append(e0.elapsed_time(e1))
-    loop_ms = sorted(runs)[1]
+    loop_ms = median(runs)
     per_launch = event_time_ms(torch, lambda: dstep(0), 200)
     bps = decode_bytes_per_step(Bd, Hd, dd)
     gbs_loop = bps * nsteps / (loop_ms * 1e-3) / 1e9
@@ -345,6 +483,7 @@ def run_decode(args, torch, dn, synthetic, to_dev):
         % (loop_ms * 1000 / nsteps, gbs_loop, gbs_kernel))
     return {
         "workload": name_d, "B": Bd, "H": Hd, "d": dd, "steps": nsteps,
+        "runs_ms": [round(r, 4) for r in runs], "run": "median of 5 runs of the steps back to back",
         "ms_per_1000_steps": round(loop_ms * 1000.0 / nsteps, 3),
         "us_per_step": round(loop_ms * 1000.0 / nsteps, 2),
         "token_heads_per_s": round(Bd * Hd * nsteps / (loop_ms * 1e-3), 1),
@@ -363,8 +502,7 @@ def run_decode(args, torch, dn, synthetic, to_dev):
 
 def run_workloads(torch, dn, synthetic, to_dev, dev):
     wl = {}
-    for wname, form in (("gdn_prefill_b1_h16_t65536_d128", "chunk"),
-                        ("kda_prefill_b2_h16_t8192_d128", "chunk"),
+    for wname, form in (("kda_prefill_b2_h16_t8192_d128", "chunk"),
                         ("deltanet_fp32_t512_d64", "chunk"),
                         ("deltanet_fp32_t512_d64", "recurrent")):
         c = synthetic.CONFIGS[wname]
