@@ -626,6 +626,25 @@ def run_serving(torch, dn, synthetic, to_dev, dev):
     out["gdr_chunk_length_sweep_ms"] = {"B": Bs_, "H": Hs_, "T": Ts_, "d": d, "ms_by_chunk": sweep}
     log("  serving gdr chunk sweep %s" % sweep)
     del xs, sargs, os_, Ss_
+    # the same sweep on the Gated DeltaNet prefill itself (two launches, chunk
+    # lengths 32, 64, 128) at the same size
+    xg2 = to_dev(synthetic.make("gated", Bs_, Hs_, Ts_, d, d, dtype="bf16", seed=2007))
+    og2 = torch.empty(Bs_, Hs_, Ts_, d, dtype=torch.bfloat16, device=dev)
+    Sg2 = torch.empty(Bs_, Hs_, d, d, dtype=torch.float32, device=dev)
+    gsweep = {}
+    for ch in (32, 64, 128):
+        wsl = torch.empty(int(dn.lib().dn_chunk_fwd_len_workspace(Bs_, Hs_, Ts_, d, d, 1, ch)), dtype=torch.uint8,
+                          device=dev)
+        run = lambda: dn.chunk_fwd_len(xg2["q"], xg2["k"], xg2["v"], xg2["beta"], xg2["g"], None, chunk=ch,
+                                       o=og2, S_final=Sg2, workspace=wsl)
+        for _ in range(3):
+            run()
+        gsweep[str(ch)] = round(event_time_ms(torch, run, 20), 4)
+        del wsl
+    out["gdn_chunk_length_sweep_ms"] = {"B": Bs_, "H": Hs_, "T": Ts_, "d": d, "ms_by_chunk": gsweep,
+                                        "form": "two launches (prep, scan)"}
+    log("  serving gdn chunk sweep %s" % gsweep)
+    del xg2, og2, Sg2
     del x, ws, o, S, Sc, qg, kg, xp, wsp, op, Sp
     # speculative decode: 4 drafted tokens for the decode workload's 256 x 16
     # states, the state after each kept (4 x 256 MiB of snapshots)

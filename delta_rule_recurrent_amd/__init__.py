@@ -19,7 +19,7 @@ import torch
 from . import _lib
 from ._lib import DeltaNetError, lib
 
-__all__ = ["chunk_fwd", "chunk_fwd_fused", "kda_chunk_fwd", "chunk_fwd_states", "chunk_fwd_gqa",
+__all__ = ["chunk_fwd", "chunk_fwd_fused", "chunk_fwd_len", "chunk_fwd_noalloc", "chunk_fwd_handoff_status", "kda_chunk_fwd", "chunk_fwd_states", "chunk_fwd_gqa",
            "decode_step_gqa", "chunk_fwd_varlen", "decode_tokens", "layer_prologue",
            "layer_epilogue", "gated_deltanet_layer", "ssm_chunk_fwd", "ssm_recurrent_fwd",
            "ssm_decode_step", "gdr_recurrent_fwd", "gdr_chunk_fwd", "gdr_decode_step", "chunk_prep", "chunk_scan",
@@ -131,6 +131,30 @@ def chunk_fwd_fused(q, k, v, beta, g=None, S0=None, *, output_final_state=True, 
     where no one-launch form exists."""
     return _chunk("dn_chunk_fwd_fused", q, k, v, beta, g, S0, output_final_state, o, S_final,
                   workspace, stream, kda=False)
+
+
+def chunk_fwd_len(q, k, v, beta, g=None, S0=None, *, chunk=64, o=None, S_final=None,
+                  workspace=None, stream=None):
+    """chunk_fwd in its two-launch form with chunks of `chunk` tokens (32, 64 or
+    128; bf16; 128 needs d = 128). chunk=64 is bitwise chunk_fwd's two
+    launches. Returns (o, S_final)."""
+    B, H, T, dk, dv, dev, dt = _prefill_args(q, k, v, beta, g, S0, False)
+    if o is None:
+        o = torch.empty(B, H, T, dv, dtype=dt, device=dev)
+    else:
+        _check_tensor("o", o, (B, H, T, dv), dt, dev)
+    if S_final is None:
+        S_final = torch.empty(B, H, dk, dv, dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("S_final", S_final, (B, H, dk, dv), torch.float32, dev)
+    if workspace is None:
+        need = int(lib().dn_chunk_fwd_len_workspace(B, H, T, dk, dv, _DT[dt], chunk))
+        workspace = _alloc_workspace(need, dev)
+    st = lib().dn_chunk_fwd_len(_ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(g), _ptr(S0), _ptr(o),
+                                _ptr(S_final), B, H, T, dk, dv, _DT[dt], chunk, _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("dn_chunk_fwd_len", st)
+    return o, S_final
 
 
 def chunk_fwd_noalloc(q, k, v, beta, g=None, S0=None, *, o=None, S_final=None, stream=None):

@@ -29,6 +29,8 @@ SIGNATURES = {
     "dn_chunk_fwd_handoff_status": (_i, [_vp, _sz] + [_i] * 6 + [_vp]),
     "dn_chunk_fwd_noalloc": (_i, _PREFILL + [_vp]),
     "dn_kda_chunk_fwd": (_i, _PREFILL + [_vp, _sz, _vp]),
+    "dn_chunk_fwd_len_workspace": (_sz, [_i] * 7),
+    "dn_chunk_fwd_len": (_i, _PREFILL + [_i, _vp, _sz, _vp]),
     "dn_chunk_fwd_states": (_i, [_i] + [_vp] * 9 + [_i] * 6 + [_vp, _sz, _vp]),
     "dn_chunk_fwd_gqa": (_i, [_i] + [_vp] * 8 + [_i] * 7 + [_vp, _sz, _vp]),
     "dn_decode_step_gqa": (_i, [_i] + [_vp] * 7 + [_i] * 6 + [_vp]),

@@ -233,6 +233,33 @@ int dn_chunk_fwd_fused(const void* q, const void* k, const void* v, const void* 
                         B, H, T, dk, dv, dtype, workspace, workspace_bytes, stream, dn::FWD_FUSED);
 }
 
+size_t dn_chunk_fwd_len_workspace(int B, int H, int T, int dk, int dv, int dtype, int chunk) {
+    if (B < 1 || H < 1 || T < 1 || dk != dv) return 0;
+    if ((dk != 64 && dk != 128) || !dn::chunk_len_supported(chunk, dk, dtype)) return 0;
+    return dn::chunk_len_workspace_bytes((long long)B * H, T, dk, chunk);
+}
+
+int dn_chunk_fwd_len(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                     const float* S0, void* o, float* S_final, int B, int H, int T, int dk, int dv,
+                     int dtype, int chunk, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_common(q, k, v, beta, g, false, S0, o, S_final, B, H, T, dk, dv, dtype);
+    if (st != DN_OK) return st;
+    if (!dn::chunk_len_supported(chunk, dk, dtype)) return DN_ENOTSUP;
+    const long long BH = (long long)B * H;
+    if (T == 0) {
+        if (!S_final) return DN_OK;
+        return hip_status(dn::launch_state_copy(S0, S_final, BH * dk * dv, as_stream(stream)));
+    }
+    const size_t need = dn::chunk_len_workspace_bytes(BH, T, dk, chunk);
+    if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return DN_EWORKSPACE;
+    const hipError_t e = dn::launch_chunk_fwd_len(g ? dn::KIND_GATED : dn::KIND_DELTANET, dtype, chunk, q, k, v,
+                                                  beta, g, S0, o, S_final, workspace, (int)BH, T, dk,
+                                                  as_stream(stream));
+    if (e == hipErrorNotSupported) return DN_ENOTSUP;
+    return hip_status(e);
+}
+
 int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
                      const void* g, const float* S0, void* o, float* S_final, int B, int H,
                      int T, int dk, int dv, int dtype, void* workspace,

@@ -358,67 +358,84 @@ void chunk_prep_kernel(const E* __restrict__ q,
 //  * Each scaled T is rounded once to the operand type.
 
 
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, int CH = CHUNK>
 struct Prep2Smem {
-    static constexpr int LDF = 68;                     // fp32 64x64: A, then T's diagonal blocks
-    static constexpr int LDT = 64 + 16 / sizeof(E);    // T diag(.) in the operand type (two)
-    static constexpr long AT_BYTES = 64L * LDF * 4 > 2 * 64L * LDT * (long)sizeof(E)
-                                         ? 64L * LDF * 4
-                                         : 2 * 64L * LDT * (long)sizeof(E);
-    // V as B-fragments (contraction over tokens), [DV/16 value tiles][2][64 lanes]
-    static constexpr long V_BYTES = (DV / 16) * 2L * 64 * 8 * sizeof(E);
+    static constexpr int LDF = CH + 4;                 // fp32 CH x CH: A, then T's diagonal blocks
+    static constexpr int LDT = CH + 16 / sizeof(E);    // T diag(.) in the operand type (two)
+    static constexpr long AT_BYTES = (long)CH * LDF * 4 > 2L * CH * LDT * (long)sizeof(E)
+                                         ? (long)CH * LDF * 4
+                                         : 2L * CH * LDT * (long)sizeof(E);
+    // V as B-fragments (contraction over tokens), [DV/16 value tiles][CH/32][64 lanes]
+    static constexpr long V_BYTES = (DV / 16) * (CH / 32) * 64L * 8 * sizeof(E);
     static constexpr long BYTES = AT_BYTES + V_BYTES;
 };
 
-// Per-token tables of one chunk in LDS: running log-decay G, beta e^G,
-// e^{G_C - G} and beta of token `lane`; returns e^{G_C}.
-__device__ __forceinline__ float token_tables(float bv, float gv, int lane, float* Gs, float* sX,
-                                              float* sK, float* bs, float* eG) {
-    const float G = wave_inclusive_sum(gv, lane);
-    const float GC = readlane_f(G, 63);
-    const float e = __expf(G);
-    Gs[lane] = G;
-    sX[lane] = bv * e;
-    sK[lane] = __expf(GC - G);
-    bs[lane] = bv;
-    if (eG) eG[lane] = e;
+// Per-token tables of one chunk of CH tokens in LDS: running log-decay G,
+// beta e^G, e^{G_C - G} and beta; lane l holds tokens l, l + 64, ... (bv, gv
+// zero past the chunk's end). Returns e^{G_C}.
+template <int CH>
+__device__ __forceinline__ float token_tables(const float (&bv)[(CH + 63) / 64], const float (&gv)[(CH + 63) / 64],
+                                              int lane, float* Gs, float* sX, float* sK, float* bs, float* eG) {
+    constexpr int TH = (CH + 63) / 64;
+    float G[TH];
+#pragma unroll
+    for (int h = 0; h < TH; ++h) {
+        G[h] = wave_inclusive_sum(gv[h], lane);
+        if (h > 0) G[h] += readlane_f(G[h - 1], 63);
+    }
+    const float GC = readlane_f(G[TH - 1], CH >= 64 ? 63 : CH - 1);
+#pragma unroll
+    for (int h = 0; h < TH; ++h) {
+        const int t = 64 * h + lane;
+        if (CH >= 64 || t < CH) {
+            const float e = __expf(G[h]);
+            Gs[t] = G[h];
+            sX[t] = bv[h] * e;
+            sK[t] = __expf(GC - G[h]);
+            bs[t] = bv[h];
+            if (eG) eG[t] = e;
+        }
+    }
     return __expf(GC);
 }
 
 // LDS of one two-wavefront prep unit.
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, int CH = CHUNK>
 struct Prep2Lds {
-    __align__(16) char smem[Prep2Smem<E, DK, DV>::BYTES];
+    __align__(16) char smem[Prep2Smem<E, DK, DV, CH>::BYTES];
     // per wavefront: running log-decay, beta e^G, e^{G_C - G}, beta of each token
-    __align__(16) float tab[2][4][64];
+    __align__(16) float tab[2][4][CH];
 };
 
-// One (head bh, chunk c) item on two wavefronts (w = 0, 1 of the unit), its
-// results written to the workspace block `blk`. Each of the two wavefronts
-// passes exactly one workgroup barrier.
-template <typename E, int DK, int DV, int KIND>
+// One (head bh, chunk c) item of CH tokens (32, 64 or 128) on two wavefronts
+// (w = 0, 1 of the unit), its results written to the workspace block `blk`.
+// Each of the two wavefronts passes exactly one workgroup barrier.
+template <typename E, int DK, int DV, int KIND, int CH = CHUNK>
 __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __restrict__ k,
                                            const E* __restrict__ v, const E* __restrict__ beta,
                                            const E* __restrict__ g, char* __restrict__ blk,
-                                           Prep2Lds<E, DK, DV>& lds, long tok0, long tokk, int L,
+                                           Prep2Lds<E, DK, DV, CH>& lds, long tok0, long tokk, int L,
                                            int w, int lane) {
-    typedef WsLayout<E, DK, DV> Lw;
-    typedef Prep2Smem<E, DK, DV> Sm;
+    typedef WsLayout<E, DK, DV, CH> Lw;
+    typedef Prep2Smem<E, DK, DV, CH> Sm;
     typedef typename Frag<E>::type F;
     typedef typename Vec4<E>::type V4;
     constexpr int KB = DK / 32, CT = DK / 16, VB = DV / 32, VT = DV / 16;
+    constexpr int NT = CH / 16, CB = CH / 32, TH = (CH + 63) / 64;
     constexpr int LDF = Sm::LDF, LDT = Sm::LDT;
+    // past 64 tokens, V's fragments are loaded after attn (register room)
+    constexpr bool LATE_V = CH > 64;
 
     char* smem = lds.smem;
-    float(*tab)[4][64] = lds.tab;
+    float(*tab)[4][CH] = lds.tab;
     float* As = reinterpret_cast<float*>(smem);   // A, then T's diagonal blocks in place
     E* Tw = reinterpret_cast<E*>(smem);           // T diag(beta e^G), once the inverse is done
-    E* Tu = Tw + 64 * LDT;                        // T diag(beta)
+    E* Tu = Tw + CH * LDT;                        // T diag(beta)
     F* Vl = reinterpret_cast<F*>(smem + Sm::AT_BYTES);
 
     const int gq = lane >> 4, n = lane & 15;
     // tok0: the chunk's first token (value-head row), tokk: the same token in
-    // the q, k rows; L: tokens of the chunk (1..64)
+    // the q, k rows; L: tokens of the chunk (1..CH)
 
     F* Wf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::W_OFF);
     F* Kf = reinterpret_cast<F*>(reinterpret_cast<E*>(blk) + Lw::K_OFF);
@@ -428,28 +445,34 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
     float* eg = reinterpret_cast<float*>(blk + Lw::EG_BYTE_OFF);
 
     // ---- 1. every load of this wavefront is issued up front, so that a single
-    //         memory latency covers them: beta and the log-decay of token
-    //         `lane`, then the K fragments (rows = tokens, contraction = key
-    //         channels, in the 8-consecutive-channel order; both wavefronts),
-    //         then (wavefront 1) Q and V in the same order
-    const long tk = tok0 + min(lane, L - 1);
-    const E braw = KIND == KIND_SSM ? E{} : beta[tk];
-    const E graw = (KIND == KIND_GATED || KIND == KIND_SSM) ? g[tk] : E{};
-    F kf[4][KB];
+    //         memory latency covers them: beta and the log-decay of tokens
+    //         `lane` (+ 64), then the K fragments (rows = tokens, contraction =
+    //         key channels, in the 8-consecutive-channel order; both
+    //         wavefronts), then (wavefront 1) Q and V in the same order
+    E braw[TH], graw[TH];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int h = 0; h < TH; ++h) {
+        const long tk = tok0 + min(64 * h + lane, L - 1);
+        braw[h] = KIND == KIND_SSM ? E{} : beta[tk];
+        graw[h] = (KIND == KIND_GATED || KIND == KIND_SSM) ? g[tk] : E{};
+    }
+    F kf[NT][KB];
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) kf[tt][kb] = frag_rows8_g<E>(k + tokk * DK, DK, 16 * tt, 32 * kb, lane, L);
-    F qa[4][KB], vf[4][VB];
+    F qa[NT][KB], vf[NT][VB];
     if (w == 1) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) qa[tt][kb] = frag_rows8_g<E>(q + tokk * DK, DK, 16 * tt, 32 * kb, lane, L);
+        if (!LATE_V) {
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
+            for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int kb = 0; kb < VB; ++kb) vf[tt][kb] = frag_rows8_g<E>(v + tok0 * DV, DV, 16 * tt, 32 * kb, lane, L);
+                for (int kb = 0; kb < VB; ++kb) vf[tt][kb] = frag_rows8_g<E>(v + tok0 * DV, DV, 16 * tt, 32 * kb, lane, L);
+        }
     }
 
     // per-token tables (each wavefront its own copy; wave 0 stores the per-token
@@ -461,10 +484,19 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
     {
         // the state-space kind has no write strength and no correction: beta = 1
         // (so u = V) and a zero beta e^G table (so W = 0)
-        float bv = KIND == KIND_SSM ? 1.f : to_f32(braw), gv = to_f32(graw);
-        if (lane >= L) bv = gv = 0.f;
-        const float eGC = token_tables(bv, gv, lane, Gs, sX, sK, bs, w == 0 ? eg : nullptr);
-        if (KIND == KIND_SSM) sX[lane] = 0.f;
+        float bv[TH], gv[TH];
+#pragma unroll
+        for (int h = 0; h < TH; ++h) {
+            bv[h] = KIND == KIND_SSM ? 1.f : to_f32(braw[h]);
+            gv[h] = to_f32(graw[h]);
+            if (64 * h + lane >= L) bv[h] = gv[h] = 0.f;
+        }
+        const float eGC = token_tables<CH>(bv, gv, lane, Gs, sX, sK, bs, w == 0 ? eg : nullptr);
+        if (KIND == KIND_SSM) {
+#pragma unroll
+            for (int h = 0; h < TH; ++h)
+                if (CH >= 64 || 64 * h + lane < CH) sX[64 * h + lane] = 0.f;
+        }
         if (w == 0)
             for (int ch = lane; ch < DK; ch += 64) gam[ch] = eGC;
     }
@@ -473,7 +505,7 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
         lds_fence();   // tables written
         // ---- 2. A = strict_tril(beta_i K K^T exp(G_i - G_j)) into LDS (fp32)
 #pragma unroll
-        for (int it = 0; it < 4; ++it)
+        for (int it = 0; it < NT; ++it)
 #pragma unroll
             for (int jt = 0; jt <= it; ++jt) {
                 f32x4 s = zero4();   // (state-space kind: A = 0, so T = I)
@@ -495,34 +527,39 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
         lds_fence();   // A is written
 
         // ---- 3. UT transform T = (I + A)^-1, blocked over 16x16 tiles
-        // 3a: diagonal blocks by forward substitution, lane (block gq, column n):
-        //     T_jj = 1, T_ij = -sum_{j <= m < i} A_im T_mj; written over the block of A
-        {
-            const int b0 = 16 * gq, j = n;
-            float tc[16];
+        // 3a: diagonal blocks by forward substitution, lane (block 4p + gq,
+        //     column n): T_jj = 1, T_ij = -sum_{j <= m < i} A_im T_mj; written
+        //     over the block of A
 #pragma unroll
-            for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
+        for (int pass = 0; pass < (NT + 3) / 4; ++pass) {
+            const int blkd = 4 * pass + gq;
+            if (NT % 4 == 0 || blkd < NT) {
+                const int b0 = 16 * blkd, j = n;
+                float tc[16];
 #pragma unroll
-            for (int i = 1; i < 16; ++i) {
-                float acc = 0.f;
+                for (int i = 0; i < 16; ++i) tc[i] = (i == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < i; ++m) acc += As[(b0 + i) * LDF + b0 + m] * tc[m];
-                tc[i] = (i > j) ? -acc : tc[i];
+                for (int i = 1; i < 16; ++i) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int m = 0; m < i; ++m) acc += As[(b0 + i) * LDF + b0 + m] * tc[m];
+                    tc[i] = (i > j) ? -acc : tc[i];
+                }
+                lds_fence();
+#pragma unroll
+                for (int i = 0; i < 16; ++i) As[(b0 + i) * LDF + b0 + j] = tc[i];
             }
-            lds_fence();
-#pragma unroll
-            for (int i = 0; i < 16; ++i) As[(b0 + i) * LDF + b0 + j] = tc[i];
         }
         lds_fence();
         // 3b: T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ on the matrix cores (fp32),
         //     the column tiles J interleaved
-        f32x4 tm[4][4];
+        f32x4 tm[NT][NT];
 #pragma unroll
-        for (int J = 0; J < 4; ++J)
+        for (int J = 0; J < NT; ++J)
 #pragma unroll
             for (int e = 0; e < 4; ++e) tm[J][J][e] = As[(16 * J + 4 * gq + e) * LDF + 16 * J + n];
 #pragma unroll
-        for (int I = 1; I < 4; ++I) {
+        for (int I = 1; I < NT; ++I) {
 #pragma unroll
             for (int J = 0; J < I; ++J) {
                 f32x4 R = zero4();
@@ -535,10 +572,10 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
         // T diag(beta e^G) and T diag(beta) (lower triangular) in the operand
         // type, over the fp32 region; lane (gq, n) holds column 16J + n of tile (I, J)
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
+        for (int J = 0; J < NT; ++J) {
             const float cx = sX[16 * J + n], cb = bs[16 * J + n];
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
+            for (int I = 0; I < NT; ++I)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int o = (16 * I + 4 * gq + e) * LDT + 16 * J + n;
@@ -551,10 +588,10 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
         //          (rows j) stacked over two j tiles
         lds_fence();   // tables written
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-            f32x4 at[4];
+        for (int it = 0; it < NT; ++it) {
+            f32x4 at[NT];
 #pragma unroll
-            for (int jt = 0; jt < 4; ++jt) {
+            for (int jt = 0; jt < NT; ++jt) {
                 at[jt] = zero4();
                 if (jt <= it) {
 #pragma unroll
@@ -571,7 +608,13 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
                 }
             }
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) Af[(it * 2 + kb) * 64 + lane] = frag_from_tiles<E>(at[2 * kb], at[2 * kb + 1]);
+            for (int kb = 0; kb < CB; ++kb) Af[(it * CB + kb) * 64 + lane] = frag_from_tiles<E>(at[2 * kb], at[2 * kb + 1]);
+        }
+        if (LATE_V) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int kb = 0; kb < VB; ++kb) vf[tt][kb] = frag_rows8_g<E>(v + tok0 * DV, DV, 16 * tt, 32 * kb, lane, L);
         }
         // K and V with tokens as the contraction index (D = K I): K as
         // B-fragments (kept for W = T diag(beta e^G) K), K~^T = (e^{G_C - G} K)^T
@@ -579,22 +622,22 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
         const F id0 = ident8_frag<E>(0, lane), id1 = ident8_frag<E>(1, lane);
 #pragma unroll
         for (int nt = 0; nt < VT; ++nt) {
-            f32x4 d[4];
+            f32x4 d[NT];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) d[tt] = mma(vf[tt][nt >> 1], (nt & 1) ? id1 : id0, zero4());
+            for (int tt = 0; tt < NT; ++tt) d[tt] = mma(vf[tt][nt >> 1], (nt & 1) ? id1 : id0, zero4());
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) Vl[(nt * 2 + kt) * 64 + lane] = frag_from_tiles<E>(d[2 * kt], d[2 * kt + 1]);
+            for (int kt = 0; kt < CB; ++kt) Vl[(nt * CB + kt) * 64 + lane] = frag_from_tiles<E>(d[2 * kt], d[2 * kt + 1]);
         }
-        F xf[CT][2];
+        F xf[CT][CB];
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
-            f32x4 d[4];
+            f32x4 d[NT];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) d[tt] = mma(kf[tt][ct >> 1], (ct & 1) ? id1 : id0, zero4());
+            for (int tt = 0; tt < NT; ++tt) d[tt] = mma(kf[tt][ct >> 1], (ct & 1) ? id1 : id0, zero4());
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
+            for (int kt = 0; kt < CB; ++kt) {
                 xf[ct][kt] = frag_from_tiles<E>(d[2 * kt], d[2 * kt + 1]);
-                Kf[(ct * 2 + kt) * 64 + lane] = frag_from_tiles_rs<E>(d[2 * kt], d[2 * kt + 1], sK, 32 * kt, lane);
+                Kf[(ct * CB + kt) * 64 + lane] = frag_from_tiles_rs<E>(d[2 * kt], d[2 * kt + 1], sK, 32 * kt, lane);
             }
         }
         lds_barrier();   // T diag(.) and V are in LDS
@@ -605,16 +648,16 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
         //         not written)
         if constexpr (KIND != KIND_SSM) {
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                F tf[2];
+            for (int tt = 0; tt < NT; ++tt) {
+                F tf[CB];
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt) tf[kt] = frag_rows<E>(Tw, LDT, 16 * tt, 32 * kt, lane);
+                for (int kt = 0; kt < CB; ++kt) tf[kt] = frag_rows<E>(Tw, LDT, 16 * tt, 32 * kt, lane);
                 f32x4 wt[CT];
 #pragma unroll
                 for (int mt = 0; mt < CT; ++mt) {
                     wt[mt] = zero4();
 #pragma unroll
-                    for (int kt = 0; kt < 2; ++kt) wt[mt] = mma(xf[mt][kt], tf[kt], wt[mt]);
+                    for (int kt = 0; kt < CB; ++kt) wt[mt] = mma(xf[mt][kt], tf[kt], wt[mt]);
                 }
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb) Wf[(tt * KB + kb) * 64 + lane] = frag_from_tiles<E>(wt[2 * kb], wt[2 * kb + 1]);
@@ -625,44 +668,46 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
     lds_barrier();   // (wavefront 0) T diag(.) and V are in LDS
 
     // ---- 5. u = T diag(beta) V as D-tiles (rows = tokens), value tile by value tile
-    F tu[4][2];
+    F tu[NT][CB];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) tu[tt][kt] = frag_rows<E>(Tu, LDT, 16 * tt, 32 * kt, lane);
+        for (int kt = 0; kt < CB; ++kt) tu[tt][kt] = frag_rows<E>(Tu, LDT, 16 * tt, 32 * kt, lane);
 #pragma unroll
     for (int nt = 0; nt < VT; ++nt) {
-        F vb[2];
+        F vb[CB];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) vb[kt] = Vl[(nt * 2 + kt) * 64 + lane];
+        for (int kt = 0; kt < CB; ++kt) vb[kt] = Vl[(nt * CB + kt) * 64 + lane];
 #pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
+        for (int tt = 0; tt < NT; ++tt) {
             f32x4 acc = zero4();
 #pragma unroll
-            for (int kt = 0; kt < 2; ++kt) acc = mma(tu[tt][kt], vb[kt], acc);
+            for (int kt = 0; kt < CB; ++kt) acc = mma(tu[tt][kt], vb[kt], acc);
             V4 u4;
 #pragma unroll
             for (int e = 0; e < 4; ++e) u4[e] = from_f32<E>(acc[e]);
-            Uf[(nt * 4 + tt) * 64 + lane] = u4;
+            Uf[(nt * NT + tt) * 64 + lane] = u4;
         }
     }
 }
 
-template <typename E, int DK, int DV, int KIND>
-__global__ __launch_bounds__(128, 2) void chunk_prep2_kernel(const E* __restrict__ q,
-                                                             const E* __restrict__ k,
-                                                             const E* __restrict__ v,
-                                                             const E* __restrict__ beta,
-                                                             const E* __restrict__ g,
-                                                             char* __restrict__ ws, int T,
-                                                             int nchunks, HeadMap hm) {
-    __shared__ Prep2Lds<E, DK, DV> lds;
+// Chunks of CH tokens (64 unless stated); past 64 the fragments need the whole
+// register file, one unit per SIMD pair.
+template <typename E, int DK, int DV, int KIND, int CH = CHUNK>
+__global__ __launch_bounds__(128, CH > 64 ? 1 : 2) void chunk_prep2_kernel(const E* __restrict__ q,
+                                                                           const E* __restrict__ k,
+                                                                           const E* __restrict__ v,
+                                                                           const E* __restrict__ beta,
+                                                                           const E* __restrict__ g,
+                                                                           char* __restrict__ ws, int T,
+                                                                           int nchunks, HeadMap hm) {
+    __shared__ Prep2Lds<E, DK, DV, CH> lds;
     const long item = blockIdx.x;
     const long bh = item / nchunks;
-    const int t0 = (int)(item % nchunks) * CHUNK;
-    prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV>::BYTES, lds,
-                                bh * T + t0, hm.key(bh) * T + t0, min(CHUNK, T - t0),
-                                (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
+    const int t0 = (int)(item % nchunks) * CH;
+    prep2_item<E, DK, DV, KIND, CH>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV, CH>::BYTES, lds,
+                                    bh * T + t0, hm.key(bh) * T + t0, min(CH, T - t0),
+                                    (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
 }
 
 // The same prep as the recomputation after a one-launch call: it runs only if
@@ -715,18 +760,23 @@ __global__ __launch_bounds__(128, 2) void chunk_prep2_varlen_kernel(const E* __r
 // ---------------------------------------------------------------------------
 // Scan kernel
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV, int BV, int KIND>
+// One wavefront per 16-token tile of a CH-token chunk (NW = CH / 16); each owns
+// DK / NW key rows of the state (MTW tiles of 16).
+template <typename E, int DK, int DV, int BV, int KIND, int CH = CHUNK>
 struct ScanOps {
     typedef typename Frag<E>::type F;
     typedef typename Vec4<E>::type V4;
-    static constexpr int KB = DK / 32;   // contraction blocks over key channels
-    static constexpr int MTW = DK / 64;  // key-channel tiles per wave
-    static constexpr int NT = BV / 16;   // value tiles (16 columns) per workgroup
+    static constexpr int NW = CH / 16;          // wavefronts = token tiles
+    static constexpr int CB = CH / 32;          // contraction blocks over tokens
+    static constexpr int KB = DK / 32;          // contraction blocks over key channels
+    static constexpr int MTW = DK / (16 * NW);  // key-channel tiles per wave
+    static_assert(MTW >= 1 && MTW * 16 * NW == DK, "key rows split evenly over the wavefronts");
+    static constexpr int NT = BV / 16;          // value tiles (16 columns) per workgroup
     typedef typename Vec16<E>::type V16;
     // Gated / DeltaNet: the wave's 16 rows of Q as loaded (row-major, 16 bytes
     // per lane per load); KDA: Q~ as A-fragments from the workspace
     static constexpr int QR = 16 * DK * (int)sizeof(E) / (64 * 16);
-    F w[KB], q[KB], a[2], k[MTW][2];
+    F w[KB], q[KB], a[CB], k[MTW][CB];
     V16 qr[QR];
     V4 u[NT];
     // chunk decay: KDA per key channel of the wave's rows (D-tile order),
@@ -747,11 +797,11 @@ struct ChunkSrc {
 // coalesced load per lane per fragment). The parts are issued at different
 // points of the previous-but-one chunk's step, so the wave never stalls on a
 // burst of loads waiting for the memory pipeline to accept them.
-template <int PART, int KIND, typename E, int DK, int DV, int BV>
-__device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV, KIND>& x, const ChunkSrc<E>& src,
+template <int PART, int KIND, typename E, int DK, int DV, int BV, int CH>
+__device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV, KIND, CH>& x, const ChunkSrc<E>& src,
                                                int vt, int w, int lane) {
-    typedef WsLayout<E, DK, DV> Lw;
-    typedef ScanOps<E, DK, DV, BV, KIND> O;
+    typedef WsLayout<E, DK, DV, CH> Lw;
+    typedef ScanOps<E, DK, DV, BV, KIND, CH> O;
     typedef typename O::F F;
     typedef typename O::V4 V4;
     constexpr int FB = (int)sizeof(F);    // bytes of one fragment per lane
@@ -780,18 +830,18 @@ __device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV, KIND>& x, 
         }
     } else if (PART == 2) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-            x.a[kb] = buf_load<F>(rb, (int)(Lw::A_OFF * ES) + ((w * 2 + kb) * 64 + lane) * FB);
+        for (int kb = 0; kb < O::CB; ++kb)
+            x.a[kb] = buf_load<F>(rb, (int)(Lw::A_OFF * ES) + ((w * O::CB + kb) * 64 + lane) * FB);
 #pragma unroll
         for (int m = 0; m < O::MTW; ++m)
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                x.k[m][kb] = buf_load<F>(rb, (int)(Lw::K_OFF * ES) + (((w * O::MTW + m) * 2 + kb) * 64 + lane) * FB);
+            for (int kb = 0; kb < O::CB; ++kb)
+                x.k[m][kb] = buf_load<F>(rb, (int)(Lw::K_OFF * ES) + (((w * O::MTW + m) * O::CB + kb) * 64 + lane) * FB);
     } else {
         const int gq = lane >> 4;
 #pragma unroll
         for (int nt = 0; nt < O::NT; ++nt)
-            x.u[nt] = buf_load<V4>(rb, (int)(Lw::U_OFF * ES) + (((vt * O::NT + nt) * 4 + w) * 64 + lane) * (int)sizeof(V4));
+            x.u[nt] = buf_load<V4>(rb, (int)(Lw::U_OFF * ES) + (((vt * O::NT + nt) * O::NW + w) * 64 + lane) * (int)sizeof(V4));
         if (KIND == KIND_KDA) {
 #pragma unroll
             for (int m = 0; m < O::MTW; ++m)
@@ -803,8 +853,8 @@ __device__ __forceinline__ void scan_load_part(ScanOps<E, DK, DV, BV, KIND>& x, 
     }
 }
 
-template <int KIND, typename E, int DK, int DV, int BV>
-__device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV, KIND>& x, const ChunkSrc<E>& src, int vt,
+template <int KIND, typename E, int DK, int DV, int BV, int CH>
+__device__ __forceinline__ void scan_load(ScanOps<E, DK, DV, BV, KIND, CH>& x, const ChunkSrc<E>& src, int vt,
                                           int w, int lane) {
     scan_load_part<0, KIND>(x, src, vt, w, lane);
     scan_load_part<1, KIND>(x, src, vt, w, lane);
@@ -833,19 +883,19 @@ struct SeqView {
 // S = gamma S + K~^T U. S (fp32, MFMA accumulator layout) is updated in
 // place; the operands of chunk c+2 (`nxt`, from block `nblk`) are loaded in
 // parts along the way; the output tile leaves through LDS as 16-byte rows.
-template <typename E, int DK, int DV, int KIND, int BV, bool PF>
-__device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cur,
-                                          ScanOps<E, DK, DV, BV, KIND>& nxt, const ChunkSrc<E>& nblk,
-                                          f32x4 (&S)[DK / 64][BV / 16],
+template <typename E, int DK, int DV, int KIND, int BV, bool PF, int CH = CHUNK>
+__device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND, CH>& cur,
+                                          ScanOps<E, DK, DV, BV, KIND, CH>& nxt, const ChunkSrc<E>& nblk,
+                                          f32x4 (&S)[ScanOps<E, DK, DV, BV, KIND, CH>::MTW][BV / 16],
                                           typename Frag<E>::type (*Sx)[BV / 16][64],
                                           typename Frag<E>::type (*Ux)[BV / 16][64], E* ob, E* qs,
                                           E* __restrict__ o, long orow, int len, int t0, int vt,
                                           int w, int lane, const char* pfblk, float& pf) {
-    typedef ScanOps<E, DK, DV, BV, KIND> Ops;
+    typedef ScanOps<E, DK, DV, BV, KIND, CH> Ops;
     typedef typename Ops::F F;
     typedef typename Ops::V4 V4;
     typedef typename Vec16<E>::type V16;
-    constexpr int NT = Ops::NT, KB = Ops::KB, MTW = Ops::MTW;
+    constexpr int NT = Ops::NT, KB = Ops::KB, MTW = Ops::MTW, CB = Ops::CB;
     constexpr int LDO = BV + 16 / sizeof(E);   // output staging row (padded)
     const int gq = lane >> 4, n = lane & 15;
 
@@ -862,12 +912,14 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cu
     }
 
     // state -> B-fragments of the contraction over key channels; key-channel
-    // block kb covers the tiles 2kb, 2kb+1, i.e. wave kb (d = 128) or the waves
-    // 2kb, 2kb+1 (d = 64, one tile each, half a fragment each)
+    // block kb covers the key tiles 2kb, 2kb+1: two tiles of one wave (MTW even)
+    // or one tile each of the waves 2kb, 2kb+1 (MTW = 1, half a fragment each)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        if (MTW == 2) {
-            Sx[w][nt][lane] = frag_from_tiles<E>(S[0][nt], S[MTW - 1][nt]);
+        if (MTW >= 2) {
+#pragma unroll
+            for (int m = 0; m < MTW; m += 2)
+                Sx[(w * MTW + m) >> 1][nt][lane] = frag_from_tiles<E>(S[m][nt], S[m + 1][nt]);
         } else {
             V4 h;
 #pragma unroll
@@ -921,7 +973,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cu
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < CB; ++kb) {
             const F ub = Ux[kb][nt][lane];
             O[nt] = mma(cur.a[kb], ub, O[nt]);
 #pragma unroll
@@ -951,22 +1003,22 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND>& cu
         // round again, RING steps later, so the load never holds up a step.
         asm volatile("" ::"v"(pf));
         constexpr int NV = DV / BV;
-        pf = buf_load<float>(make_rsrc(pfblk, (unsigned)WsLayout<E, DK, DV>::BYTES),
-                             ((vt * 4 + w) + lane * 4 * NV) * 128);
+        pf = buf_load<float>(make_rsrc(pfblk, (unsigned)WsLayout<E, DK, DV, CH>::BYTES),
+                             ((vt * Ops::NW + w) + lane * Ops::NW * NV) * 128);
     }
 }
 
 // LDS of one scan workgroup.
-template <typename E, int DK, int DV, int KIND, int BV>
+template <typename E, int DK, int DV, int KIND, int BV, int CH = CHUNK>
 struct ScanLds {
     typedef typename Frag<E>::type F;
-    static constexpr int KB = DK / 32, NT = BV / 16;
+    static constexpr int KB = DK / 32, NT = BV / 16, NW = CH / 16, CB = CH / 32;
     static constexpr int LDO = BV + 16 / sizeof(E);   // output staging row (padded)
     static constexpr int LDQ = DK + 16 / sizeof(E);   // Q row (padded)
     F Sx[KB][NT][64];   // state as B-fragments (contraction over key channels)
-    F Ux[2][NT][64];    // U as B-fragments (contraction over tokens)
-    __align__(16) E Ob[4][16 * LDO];                              // per-wave output staging
-    __align__(16) E Qs[KIND == KIND_KDA ? 1 : 4][16 * LDQ];      // per-wave Q rows
+    F Ux[CB][NT][64];   // U as B-fragments (contraction over tokens)
+    __align__(16) E Ob[NW][16 * LDO];                              // per-wave output staging
+    __align__(16) E Qs[KIND == KIND_KDA ? 1 : NW][16 * LDQ];      // per-wave Q rows
 };
 
 // ---------------------------------------------------------------------------
@@ -1035,15 +1087,15 @@ __device__ __forceinline__ u64* block_tags(char* ws, long BH, int nchunks) {
 // each is waited for (tags at `tags`, expected value `tag`) before its
 // operands are loaded. RING: 3 (two chunks prefetched) or 2 (one chunk; fewer
 // registers held, which leaves the fused launch's register budget room).
-template <typename E, int DK, int DV, int KIND, int BV, bool SYNC, int RING, bool EMIT = false>
+template <typename E, int DK, int DV, int KIND, int BV, bool SYNC, int RING, bool EMIT = false, int CH = CHUNK>
 __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict__ q,
                                           const float* __restrict__ S0, E* __restrict__ o,
                                           float* __restrict__ S_final, int vt, int w, int lane,
-                                          ScanLds<E, DK, DV, KIND, BV>& lds, const u64* tags,
+                                          ScanLds<E, DK, DV, KIND, BV, CH>& lds, const u64* tags,
                                           u64 tag, u64* err, u64 epoch, int spin,
                                           float* __restrict__ S_bound = nullptr) {
-    typedef WsLayout<E, DK, DV> Lw;
-    typedef ScanOps<E, DK, DV, BV, KIND> Ops;
+    typedef WsLayout<E, DK, DV, CH> Lw;
+    typedef ScanOps<E, DK, DV, BV, KIND, CH> Ops;
     constexpr int NT = Ops::NT, MTW = Ops::MTW;
     const int gq = lane >> 4, n = lane & 15;
 
@@ -1093,8 +1145,8 @@ __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict_
     const int last = nchunks - 1;
     auto blk = [&](int cc) {
         const int c2 = min(cc, last);
-        return ChunkSrc<E>{wsh + (long)c2 * Lw::BYTES, q + (sv.qrow + (long)c2 * CHUNK) * DK,
-                           min(CHUNK, sv.len - c2 * CHUNK)};
+        return ChunkSrc<E>{wsh + (long)c2 * Lw::BYTES, q + (sv.qrow + (long)c2 * CH) * DK,
+                           min(CH, sv.len - c2 * CH)};
     };
     // SYNC: the tags of the next block to be waited for are loaded one chunk
     // step ahead, so a block that is already published costs no wait
@@ -1131,11 +1183,11 @@ __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict_
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), see below
         for (int c = 0; c < nchunks; c += 2) {
             ready(c + 1);
-            scan_step<E, DK, DV, KIND, BV, PF>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CHUNK, vt, w, lane, pfb(c + 3), pf0);
+            scan_step<E, DK, DV, KIND, BV, PF, CH>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CH, vt, w, lane, pfb(c + 3), pf0);
             emit(c);
             if (c + 1 >= nchunks) break;
             ready(c + 2);
-            scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 1) * CHUNK, vt, w, lane, pfb(c + 4), pf1);
+            scan_step<E, DK, DV, KIND, BV, PF, CH>(o1, o0, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 1) * CH, vt, w, lane, pfb(c + 4), pf1);
             emit(c + 1);
         }
     } else {
@@ -1152,15 +1204,15 @@ __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict_
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
         for (int c = 0; c < nchunks; c += 3) {
             ready(c + 2);
-            scan_step<E, DK, DV, KIND, BV, PF>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CHUNK, vt, w, lane, pfb(c + 4), pf0);
+            scan_step<E, DK, DV, KIND, BV, PF, CH>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CH, vt, w, lane, pfb(c + 4), pf0);
             emit(c);
             if (c + 1 >= nchunks) break;
             ready(c + 3);
-            scan_step<E, DK, DV, KIND, BV, PF>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 1) * CHUNK, vt, w, lane, pfb(c + 5), pf1);
+            scan_step<E, DK, DV, KIND, BV, PF, CH>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 1) * CH, vt, w, lane, pfb(c + 5), pf1);
             emit(c + 1);
             if (c + 2 >= nchunks) break;
             ready(c + 4);
-            scan_step<E, DK, DV, KIND, BV, PF>(o2, o1, blk(c + 4), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 2) * CHUNK, vt, w, lane, pfb(c + 6), pf2);
+            scan_step<E, DK, DV, KIND, BV, PF, CH>(o2, o1, blk(c + 4), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 2) * CH, vt, w, lane, pfb(c + 6), pf2);
             emit(c + 2);
         }
     }
@@ -1178,8 +1230,8 @@ __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict_
     }
 }
 
-template <typename E, int DK, int DV, int KIND, int BV, bool EMIT>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict__ ws,
+template <typename E, int DK, int DV, int KIND, int BV, bool EMIT, int CH = CHUNK>
+__global__ __launch_bounds__(4 * CH) void chunk_scan_kernel(const char* __restrict__ ws,
                                                          const E* __restrict__ q,
                                                          const float* __restrict__ S0,
                                                          E* __restrict__ o,
@@ -1199,12 +1251,12 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(const char* __restrict_
     const int vt = slot % NV;
     const long bh = (long)(slot / NV) * 8 + xcd;
     if (bh >= BH) return;
-    __shared__ ScanLds<E, DK, DV, KIND, BV> lds;
-    const SeqView sv{ws + bh * nchunks * WsLayout<E, DK, DV>::BYTES, hm.key(bh) * T, bh * T, bh, T,
+    __shared__ ScanLds<E, DK, DV, KIND, BV, CH> lds;
+    const SeqView sv{ws + bh * nchunks * WsLayout<E, DK, DV, CH>::BYTES, hm.key(bh) * T, bh * T, bh, T,
                      nchunks};
-    scan_body<E, DK, DV, KIND, BV, false, 3, EMIT>(sv, q, S0, o, S_final, vt, (int)(threadIdx.x >> 6),
-                                                (int)(threadIdx.x & 63), lds, nullptr, 0, nullptr, 0, 0,
-                                                S_bound);
+    scan_body<E, DK, DV, KIND, BV, false, 3, EMIT, CH>(sv, q, S0, o, S_final, vt, (int)(threadIdx.x >> 6),
+                                                    (int)(threadIdx.x & 63), lds, nullptr, 0, nullptr, 0, 0,
+                                                    S_bound);
 }
 
 // The scan over packed sequences: one workgroup per (sequence n, head h, value
@@ -1554,6 +1606,79 @@ static hipError_t fused_t(const void* q, const void* k, const void* v, const voi
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return scan_launch<E, D, KIND, false>(q, s0c, o, S_final, ws, BH, T, nullptr, st, hm, err, epoch);
+}
+
+// Two-phase prefill with chunks of CH tokens (32, 64 or 128): the prep and the
+// scan above instantiated for that length (CH = 64 is dn_chunk_fwd's two-phase
+// form). Blocks of WsLayout<E, D, D, CH>::BYTES, one per (head, chunk), and
+// nothing after them.
+template <typename E, int D, int KIND, int CH>
+static hipError_t fwd_ch_t(const void* q, const void* k, const void* v, const void* beta,
+                           const void* g, const float* S0, void* o, float* S_final, void* ws, int BH,
+                           int T, hipStream_t st, HeadMap hm) {
+    const int nchunks = (T + CH - 1) / CH;
+    hipLaunchKernelGGL((chunk_prep2_kernel<E, D, D, KIND, CH>), dim3((unsigned)((long)BH * nchunks)), dim3(128),
+                       0, st, (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g, (char*)ws, T,
+                       nchunks, hm);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long groups = ((long)BH + 7) / 8;
+    // DeltaNet shares the Gated DeltaNet scan (its prep stores a unit decay)
+    if (scan_bv<D>(BH) == 32) {
+        constexpr int BV = 32;
+        hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND_GATED, BV, false, CH>),
+                           dim3((unsigned)(groups * 8 * (D / BV))), dim3(4 * CH), 0, st, (const char*)ws,
+                           (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, (float*)nullptr, hm,
+                           (const u64*)nullptr, 0ull);
+    } else {
+        constexpr int BV = 16;
+        hipLaunchKernelGGL((chunk_scan_kernel<E, D, D, KIND_GATED, BV, false, CH>),
+                           dim3((unsigned)(groups * 8 * (D / BV))), dim3(4 * CH), 0, st, (const char*)ws,
+                           (const E*)q, S0, (E*)o, S_final, T, nchunks, BH, (float*)nullptr, hm,
+                           (const u64*)nullptr, 0ull);
+    }
+    return hipGetLastError();
+}
+
+template <int D, int KIND>
+static hipError_t fwd_ch_len(int chunk, const void* q, const void* k, const void* v, const void* beta,
+                             const void* g, const float* S0, void* o, float* S_final, void* ws, int BH, int T,
+                             hipStream_t st, HeadMap hm) {
+    if (chunk == 32) return fwd_ch_t<bf16, D, KIND, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
+    if (chunk == 64) return fwd_ch_t<bf16, D, KIND, 64>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
+    if constexpr (D == 128) {
+        if (chunk == 128) return fwd_ch_t<bf16, D, KIND, 128>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
+    }
+    return hipErrorNotSupported;
+}
+
+bool chunk_len_supported(int chunk, int dk, int dtype) {
+    return dtype == DT_BF16 && (chunk == 32 || chunk == 64 || (chunk == 128 && dk == 128));
+}
+
+size_t chunk_len_workspace_bytes(long long BH, long long T, int dk, int chunk) {
+    const long long nchunks = (T + chunk - 1) / chunk;
+    long long blk = 0;
+    if (dk == 128) {
+        blk = chunk == 32 ? WsLayout<bf16, 128, 128, 32>::BYTES
+            : chunk == 64 ? WsLayout<bf16, 128, 128, 64>::BYTES : WsLayout<bf16, 128, 128, 128>::BYTES;
+    } else {
+        blk = chunk == 32 ? WsLayout<bf16, 64, 64, 32>::BYTES : WsLayout<bf16, 64, 64, 64>::BYTES;
+    }
+    return (size_t)(BH * nchunks * blk);
+}
+
+hipError_t launch_chunk_fwd_len(int kind, int dtype, int chunk, const void* q, const void* k, const void* v,
+                                const void* beta, const void* g, const float* S0, void* o, float* S_final,
+                                void* ws, int BH, int T, int dk, hipStream_t st) {
+    if (!chunk_len_supported(chunk, dk, dtype) || (kind != KIND_GATED && kind != KIND_DELTANET))
+        return hipErrorNotSupported;
+    const HeadMap hm;
+    if (dk == 128)
+        return kind == KIND_GATED ? fwd_ch_len<128, KIND_GATED>(chunk, q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm)
+                                  : fwd_ch_len<128, KIND_DELTANET>(chunk, q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
+    return kind == KIND_GATED ? fwd_ch_len<64, KIND_GATED>(chunk, q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm)
+                              : fwd_ch_len<64, KIND_DELTANET>(chunk, q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
 }
 
 // Byte offset of the one-launch form's error word (followed by the latest

@@ -10,30 +10,32 @@
 namespace dn {
 
 // ---------------------------------------------------------------------------
-// Workspace layout of one (head, chunk) block. Fragment arrays are
-// [tile][k-block][lane][8] elements of E (see the fragment convention in
-// dn_device.h); D-tile arrays are [tile][tile][lane][4].
-//   W   [4 token tiles][DK/32][64][8]      W = T (beta e^G K)          A-fragments
-//   Qt  [4 token tiles][DK/32][64][8]      Q~ = e^G * Q (KDA only)     A-fragments
-//   Kt  [DK/16 chan tiles][2][64][8]       K~^T = (e^{G_C - G} K)^T    A-fragments
-//   At  [4 token tiles][2][64][8]          attn = tril(Q K^T D)         A-fragments
-//   Uu  [DV/16 col tiles][4 token tiles][64][4]  u = T (beta V)         D-tiles
+// Workspace layout of one (head, chunk) block, for a chunk of CH tokens (64
+// unless stated; NT = CH / 16 token tiles, CB = CH / 32 token blocks).
+// Fragment arrays are [tile][k-block][lane][8] elements of E (see the fragment
+// convention in dn_device.h); D-tile arrays are [tile][tile][lane][4].
+//   W   [NT token tiles][DK/32][64][8]     W = T (beta e^G K)          A-fragments
+//   Qt  [NT token tiles][DK/32][64][8]     Q~ = e^G * Q (KDA only)     A-fragments
+//   Kt  [DK/16 chan tiles][CB][64][8]      K~^T = (e^{G_C - G} K)^T    A-fragments
+//   At  [NT token tiles][CB][64][8]        attn = tril(Q K^T D)         A-fragments
+//   Uu  [DV/16 col tiles][NT token tiles][64][4]  u = T (beta V)        D-tiles
 //                                          (a 16-column slice is contiguous)
 //   gam [DK] float                         e^{G_C} per key channel (Gated: all equal)
-//   eg  [64] float                         e^{G_t} per token (Gated / DeltaNet: the
+//   eg  [CH] float                         e^{G_t} per token (Gated / DeltaNet: the
 //                                          scan reads Q itself and scales Q S by it)
 // ---------------------------------------------------------------------------
-template <typename E, int DK, int DV>
+template <typename E, int DK, int DV, int CH = CHUNK>
 struct WsLayout {
+    static constexpr long NT = CH / 16, CB = CH / 32;
     static constexpr long W_OFF = 0;
-    static constexpr long Q_OFF = W_OFF + 4L * (DK / 32) * 64 * 8;
-    static constexpr long K_OFF = Q_OFF + 4L * (DK / 32) * 64 * 8;
-    static constexpr long A_OFF = K_OFF + (DK / 16) * 2L * 64 * 8;
-    static constexpr long U_OFF = A_OFF + 4L * 2 * 64 * 8;
-    static constexpr long E_END = U_OFF + 4L * (DV / 16) * 64 * 4;
+    static constexpr long Q_OFF = W_OFF + NT * (DK / 32) * 64 * 8;
+    static constexpr long K_OFF = Q_OFF + NT * (DK / 32) * 64 * 8;
+    static constexpr long A_OFF = K_OFF + (DK / 16) * CB * 64 * 8;
+    static constexpr long U_OFF = A_OFF + NT * CB * 64 * 8;
+    static constexpr long E_END = U_OFF + NT * (DV / 16) * 64 * 4;
     static constexpr long GAM_BYTE_OFF = (E_END * (long)sizeof(E) + 255) / 256 * 256;
     static constexpr long EG_BYTE_OFF = GAM_BYTE_OFF + DK * 4L;
-    static constexpr long BYTES = (EG_BYTE_OFF + 64 * 4L + 255) / 256 * 256;
+    static constexpr long BYTES = (EG_BYTE_OFF + CH * 4L + 255) / 256 * 256;
 };
 
 template <typename E> struct Vec16;

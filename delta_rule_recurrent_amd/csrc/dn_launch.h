@@ -87,6 +87,15 @@ size_t chunk_handoff_offset(long long BH, long long T, int dk, int dtype);
 // Workspace bytes of the chunkwise prefill (per call).
 size_t chunk_workspace_bytes(long long BH, long long T, int dk, int dv, int dtype);
 
+// Two-phase DeltaNet / Gated DeltaNet prefill with chunks of `chunk` tokens
+// (32, 64 or 128; bf16; 128 needs dk = 128); its workspace is BH x
+// ceil(T/chunk) blocks. hipErrorNotSupported outside that.
+bool chunk_len_supported(int chunk, int dk, int dtype);
+size_t chunk_len_workspace_bytes(long long BH, long long T, int dk, int chunk);
+hipError_t launch_chunk_fwd_len(int kind, int dtype, int chunk, const void* q, const void* k, const void* v,
+                                const void* beta, const void* g, const float* S0, void* o, float* S_final,
+                                void* ws, int BH, int T, int dk, hipStream_t st);
+
 // KDA's chunk-parallel phase (chunk_kda.hip): nitems = head rows x nchunks
 // (head, chunk) blocks of the workspace; with ctab (int2 per chunk: first token,
 // length; length 0 = unused slot) the rows hold packed sequences.

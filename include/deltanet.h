@@ -159,6 +159,23 @@ int dn_chunk_fwd_handoff_status(const void* workspace, size_t workspace_bytes, i
                                 int dk, int dv, int dtype, void* stream);
 
 /*
+ * The chunkwise prefill with a chosen chunk length (page "28. Linear attention
+ * and Gated DeltaNet", section "Stretch exercises", item 2: the trade between
+ * the work inside a chunk and the number of sequential chunk steps). As
+ * dn_chunk_fwd in its two-launch form (DeltaNet with g NULL, Gated DeltaNet
+ * otherwise) with chunks of `chunk` tokens: 32, 64 (then bitwise equal to
+ * dn_chunk_fwd's two launches) or 128. Supported for bf16 only, at
+ * dk = dv = 64 (chunk 32 or 64) and 128 (32, 64, 128); DN_ENOTSUP otherwise.
+ * The workspace (dn_chunk_fwd_len_workspace bytes, 256-byte aligned, owned by
+ * the caller) holds one block per (head, chunk); contents unspecified
+ * between calls. Other arguments, layouts and errors as dn_chunk_fwd.
+ */
+size_t dn_chunk_fwd_len_workspace(int B, int H, int T, int dk, int dv, int dtype, int chunk);
+int dn_chunk_fwd_len(const void* q, const void* k, const void* v, const void* beta, const void* g,
+                     const float* S0, void* o, float* S_final, int B, int H, int T, int dk, int dv,
+                     int dtype, int chunk, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * KDA chunkwise prefill: as dn_chunk_fwd but g is REQUIRED and holds one
  * log-decay per key channel, g [B,H,T,dk] (page "A walk through of the
  * DeltaNet family of linear attention variants", KDA section). Uses the same

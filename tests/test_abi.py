@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 29, names
+    assert len(names) == 31, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -485,3 +485,42 @@ def test_noalloc_validation():
     assert lib.dn_chunk_fwd_workspace(4, 8, 2048, 128, 128, 1) <= 128 << 20
     assert call(B=4, H=32, T=8192) == _lib.DN_ESCRATCH
     assert call(B=1, H=1, T=1 << 20, dtype=0) == _lib.DN_ESCRATCH
+
+
+def test_chunk_len_validation():
+    """dn_chunk_fwd_len: chunk lengths 32, 64, 128 (128 only at d = 128), bf16
+    only; the workspace size is one block per (head, chunk) of the length;
+    every check before any HIP call."""
+    lib = _lib.lib()
+    wsf = lib.dn_chunk_fwd_len_workspace
+    fn = lib.dn_chunk_fwd_len
+
+    def call(**kw):
+        a = dict(q=P, k=P, v=P, beta=P, g=P, S0=P, o=P, S_final=P, B=1, H=1, T=64, dk=128, dv=128,
+                 dtype=1, chunk=32, ws=WS, wsb=1 << 30, stream=None)
+        a.update(kw)
+        return fn(*[a[n] for n in ("q", "k", "v", "beta", "g", "S0", "o", "S_final", "B", "H", "T",
+                                   "dk", "dv", "dtype", "chunk", "ws", "wsb", "stream")])
+    # the block of a chunk length, through the size function
+    for chunk in (32, 64, 128):
+        one = wsf(1, 1, chunk, 128, 128, 1, chunk)
+        assert one > 0 and one % 256 == 0
+        assert wsf(2, 3, 5 * chunk + 1, 128, 128, 1, chunk) == 2 * 3 * 6 * one
+    # at 64 the block is the one dn_chunk_fwd uses (its tail aside)
+    state = 128 * 128 * 4
+    assert wsf(1, 1, 64, 128, 128, 1, 64) == lib.dn_chunk_fwd_workspace(1, 1, 64, 128, 128, 1) - 256 - state
+    assert wsf(1, 1, 64, 64, 64, 1, 128) == 0       # 128-token chunks need d = 128
+    assert wsf(1, 1, 64, 128, 128, 0, 64) == 0      # bf16 only
+    assert wsf(1, 1, 64, 128, 128, 1, 48) == 0
+    assert wsf(1, 1, 0, 128, 128, 1, 64) == 0
+    N, E, W = _lib.DN_ENOTSUP, _lib.DN_EINVAL, _lib.DN_EWORKSPACE
+    assert call(chunk=48) == N
+    assert call(chunk=128, dk=64, dv=64) == N
+    assert call(dtype=0) == N
+    assert call(q=None) == E
+    assert call(o=MIS) == E
+    assert call(B=0) == E
+    assert call(dk=96, dv=96) == N
+    assert call(ws=None) == W
+    assert call(wsb=16) == W
+    assert call(ws=WS + 16) == W
