@@ -76,18 +76,18 @@ CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurren
 DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
                   "delta_rule_recurrent_amd/csrc/dn_launch.h")
 TRAFFIC = {
-    # B=4 H=8 T=2048 d=128 (grid 1024 x 128 threads; 3554 / 3894 dispatches)
-    "chunk_prep2_kernel": {"fetch_kib": 29899.8, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
-                           "sha256": "d993e92e185f361e75cdc60abe80ec5f4606cd94d48aa1ab2e316a736b0915d6"},
-    # B=4 H=8 T=2048 d=128 (grid 256 x 256 threads; 3554 / 3894 dispatches)
+    # B=4 H=8 T=2048 d=128 (grid 1024 x 128 threads; 3910 / 4010 dispatches)
+    "chunk_prep2_kernel": {"fetch_kib": 29109.2, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
+                           "sha256": "e255237613ea2dfcb01805cd0bf81ab8c77948ef2c6fa95c5e58f59b42f2dcc0"},
+    # B=4 H=8 T=2048 d=128 (grid 256 x 256 threads; 3910 / 4010 dispatches)
     "chunk_scan_kernel": {"fetch_kib": 37107.5, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
-                          "sha256": "d993e92e185f361e75cdc60abe80ec5f4606cd94d48aa1ab2e316a736b0915d6"},
-    # B=1 H=16 T=65536 d=128 (grid 224 x 256 threads; 714 / 734 dispatches)
-    "chunk_fused_kernel": {"fetch_kib": 980238.1, "write_kib": 1193988.0, "sources": CHUNK_SOURCES,
-                           "sha256": "d993e92e185f361e75cdc60abe80ec5f4606cd94d48aa1ab2e316a736b0915d6"},
+                          "sha256": "e255237613ea2dfcb01805cd0bf81ab8c77948ef2c6fa95c5e58f59b42f2dcc0"},
+    # B=1 H=16 T=65536 d=128 (grid 224 x 256 threads; 770 / 790 dispatches)
+    "chunk_fused_kernel": {"fetch_kib": 982206.7, "write_kib": 1193986.3, "sources": CHUNK_SOURCES,
+                           "sha256": "e255237613ea2dfcb01805cd0bf81ab8c77948ef2c6fa95c5e58f59b42f2dcc0"},
     # B=256 H=16 d=128, one token (311 dispatches each)
-    "decode_step_kernel": {"fetch_kib": 136307.8, "write_kib": 263168.0, "sources": DECODE_SOURCES,
-                           "sha256": "09de62aed945e212144a0bc31bcc3dc4e0cafaa31057c40c0c6285a057b47873"},
+    "decode_step_kernel": {"fetch_kib": 136307.5, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+                           "sha256": "827188831a721cb9d51c314c05a6e14c4a6d5eb4033c2119767958926a8feec6"},
 }
 
 
