@@ -211,7 +211,8 @@ def timed_steps(torch, step, steps):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=100,
+                    help="timed steps of the headline prefill (the long-context one takes a fifth)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
@@ -377,7 +378,7 @@ def run_prefill(args, torch, np, dn, synthetic, to_dev, dev, name, flush):
         dn.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["beta"], inp["g"], None, o=o,
                      S_final=S_final, workspace=ws)
 
-    steps = args.steps if nchunks < 64 else max(5, args.steps // 4)
+    steps = args.steps if nchunks < 64 else max(5, args.steps // 5)
     for _ in range(args.warmup):
         step()
     nsettle = settle(torch, step, args.settle)
@@ -523,16 +524,19 @@ def run_workloads(torch, dn, synthetic, to_dev, dev):
             run = lambda: dn.recurrent_fwd(x["q"], x["k"], x["v"], x["beta"], x["g"], None)
         for _ in range(3):
             run()
-        reps = 5 if Tw >= 8192 else 20
-        ms = event_time_ms(torch, run, reps)
+        # median of groups of launches back to back (50 calls in all)
+        ms = median(launch_means_ms(torch, run, 5, 10))
         tok = Bw * Hw * Tw
         entry = {"form": form, "ms": round(ms, 4), "tokens_per_s": round(tok / (ms * 1e-3), 1)}
         if form == "chunk":
             tf = (flops_prep(dw) + flops_scan(dw)) * tok / (ms * 1e-3) / 1e12
             entry["tflops"] = round(tf, 2)
             entry["frac_mfma"] = round(tf / (PEAK_BF16_TFLOPS if dt == torch.bfloat16 else 157.3), 4)
-            entry["gbs_algorithmic"] = round(bytes_prefill(Bw, Hw, Tw, dw, 2 if dt == torch.bfloat16 else 4)
-                                             / (ms * 1e-3) / 1e9, 1)
+            nb = bytes_prefill(Bw, Hw, Tw, dw, 2 if dt == torch.bfloat16 else 4)
+            if kda:
+                nb += Bw * Hw * Tw * (dw - 1) * (2 if dt == torch.bfloat16 else 4)   # g per key channel
+            entry["gbs_algorithmic"] = round(nb / (ms * 1e-3) / 1e9, 1)
+            entry["frac_hbm"] = round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         wl["%s/%s" % (wname, form)] = entry
         log("  %s %s %.4f ms" % (wname, form, ms))
         del x, wsw, ow, Sw

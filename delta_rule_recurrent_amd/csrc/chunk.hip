@@ -953,10 +953,14 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND, CH>
     scan_load_part<1, KIND>(nxt, nblk, vt, w, lane);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
+        // (an opaque copy: keeps the compiler from converting this operand
+        // steps early, which would make it wait for the newest loads)
+        V4 uc = cur.u[nt];
+        asm volatile("" : "+v"(uc));
         V4 h;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            U[nt][e] = to_f32(cur.u[nt][e]) - U[nt][e];
+            U[nt][e] = to_f32(uc[e]) - U[nt][e];
             h[e] = from_f32<E>(U[nt][e]);
         }
         reinterpret_cast<V4*>(&Ux[w >> 1][nt][lane])[w & 1] = h;
@@ -985,15 +989,24 @@ __device__ __forceinline__ void scan_step(const ScanOps<E, DK, DV, BV, KIND, CH>
     }
     sched_fence();
     scan_load_part<3, KIND>(nxt, nblk, vt, w, lane);
-    // 16 rows x BV columns: BV*sizeof(E) bytes per row, 16 bytes per lane
+    // 16 rows x BV columns: BV*sizeof(E) bytes per row, 16 bytes per lane.
+    // Stored through a resource that ends at the sequence's last row, so rows
+    // past it (and lanes past the tile, sent out of range) are dropped by the
+    // hardware: the stores are unconditional, which lets the compiler count
+    // them when it waits for the next step's operands (a store inside a
+    // branch made it wait for every memory operation in flight instead).
     constexpr int PER_ROW = BV * sizeof(E) / 16;
     constexpr int VEC = 16 / sizeof(E);
+    constexpr int NST = (16 * PER_ROW + 63) / 64;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + (orow + t0) * DV, (unsigned)(min(len - t0, CH) * DV * (int)sizeof(E)));
 #pragma unroll
-    for (int p = lane; p < 16 * PER_ROW; p += 64) {
-        const int row = p / PER_ROW, col = (p % PER_ROW) * VEC;
-        const int t = t0 + 16 * w + row;
+    for (int i = 0; i < NST; ++i) {
+        const int p = lane + 64 * i;
+        const bool in = (16 * PER_ROW) % 64 == 0 || p < 16 * PER_ROW;
+        const int pp = in ? p : 0;
+        const int row = pp / PER_ROW, col = (pp % PER_ROW) * VEC;
         const V16 val = *reinterpret_cast<const V16*>(&ob[row * LDO + col]);
-        if (t < len) *reinterpret_cast<V16*>(o + (orow + t) * DV + vt * BV + col) = val;
+        buf_store16(ro, in ? ((16 * w + row) * DV + vt * BV + col) * (int)sizeof(E) : 0x40000000, val);
     }
     if constexpr (PF) {
         // Pull a later chunk's block from HBM into L2: one 4-byte load per
@@ -1175,20 +1188,30 @@ __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict_
     auto pfb = [&](int cc) { return wsh + (long)min(cc, last) * Lw::BYTES; };
     float pf0 = 0.f, pf1 = 0.f, pf2 = 0.f;
     (void)pf2;
+    // The loops run whole rounds of RING steps with no exit inside (an exit
+    // between steps let the compiler sink the next operands' loads past it,
+    // to just before their use); the last nchunks mod RING steps follow the
+    // loop, with the operands the loop's last round loaded.
     if constexpr (RING == 2) {
         // operands of chunk c + 1 in flight while chunk c is processed
         Ops o0, o1;
         ready(0);
         scan_load<KIND>(o0, blk(0), vt, w, lane);
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0), see below
-        for (int c = 0; c < nchunks; c += 2) {
+        const int cend = nchunks & ~1;
+        int c = 0;
+        for (; c < cend; c += 2) {
             ready(c + 1);
             scan_step<E, DK, DV, KIND, BV, PF, CH>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CH, vt, w, lane, pfb(c + 3), pf0);
             emit(c);
-            if (c + 1 >= nchunks) break;
             ready(c + 2);
             scan_step<E, DK, DV, KIND, BV, PF, CH>(o1, o0, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 1) * CH, vt, w, lane, pfb(c + 4), pf1);
             emit(c + 1);
+        }
+        if (c < nchunks) {
+            ready(c + 1);
+            scan_step<E, DK, DV, KIND, BV, PF, CH>(o0, o1, blk(c + 1), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CH, vt, w, lane, pfb(c + 3), pf0);
+            emit(c);
         }
     } else {
         // operands of chunks c + 1 and c + 2 in flight while chunk c is processed
@@ -1202,18 +1225,28 @@ __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict_
         // compiler waits in it for the set each step uses rather than (on the
         // strength of the entry path) for nearly everything in flight.
         __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
-        for (int c = 0; c < nchunks; c += 3) {
+        const int cend = nchunks - nchunks % 3;
+        int c = 0;
+        for (; c < cend; c += 3) {
             ready(c + 2);
             scan_step<E, DK, DV, KIND, BV, PF, CH>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CH, vt, w, lane, pfb(c + 4), pf0);
             emit(c);
-            if (c + 1 >= nchunks) break;
             ready(c + 3);
             scan_step<E, DK, DV, KIND, BV, PF, CH>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 1) * CH, vt, w, lane, pfb(c + 5), pf1);
             emit(c + 1);
-            if (c + 2 >= nchunks) break;
             ready(c + 4);
             scan_step<E, DK, DV, KIND, BV, PF, CH>(o2, o1, blk(c + 4), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 2) * CH, vt, w, lane, pfb(c + 6), pf2);
             emit(c + 2);
+        }
+        if (c < nchunks) {
+            ready(c + 2);
+            scan_step<E, DK, DV, KIND, BV, PF, CH>(o0, o2, blk(c + 2), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, c * CH, vt, w, lane, pfb(c + 4), pf0);
+            emit(c);
+            if (c + 1 < nchunks) {
+                ready(c + 3);
+                scan_step<E, DK, DV, KIND, BV, PF, CH>(o1, o0, blk(c + 3), S, lds.Sx, lds.Ux, ob, qs, o, sv.orow, sv.len, (c + 1) * CH, vt, w, lane, pfb(c + 5), pf1);
+                emit(c + 1);
+            }
         }
     }
 

@@ -223,6 +223,15 @@ __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int voff) {
     }
     return out;
 }
+// Raw 16-byte buffer store: dropped (no write, no fault) when the offset is
+// at or past the resource's byte count.
+template <typename T>
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, int voff, const T& v) {
+    static_assert(sizeof(T) == 16, "16 bytes");
+    i32x4 x;
+    __builtin_memcpy(&x, &v, 16);
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, 0, 0);
+}
 
 
 }  // namespace dn
