@@ -265,7 +265,7 @@ int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* be
                      int T, int dk, int dv, int dtype, void* workspace,
                      size_t workspace_bytes, void* stream) {
     return chunk_common(dn::KIND_KDA, q, k, v, beta, g, S0, o, S_final, B, H, T, dk, dv, dtype,
-                        workspace, workspace_bytes, stream, dn::FWD_TWO);
+                        workspace, workspace_bytes, stream, dn::FWD_AUTO);
 }
 
 int dn_chunk_fwd_states(int kda, const void* q, const void* k, const void* v, const void* beta,

@@ -40,6 +40,7 @@
 #include "dn_device.h"
 #include "dn_launch.h"
 #include "dn_chunk.h"
+#include "dn_kda_prep.h"
 
 namespace dn {
 
@@ -729,9 +730,14 @@ __global__ __launch_bounds__(128, 2) void chunk_prep2_redo_kernel(const E* __res
     for (long item = blockIdx.x; item < nitems; item += gridDim.x) {
         const long bh = item / nchunks;
         const int t0 = (int)(item % nchunks) * CHUNK;
+        // a lane index the compiler cannot see to be the same in every
+        // iteration (see chunk_fused_kernel): without it the item's
+        // lane-dependent offsets were held across iterations and spilled
+        int ln;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"((int)(threadIdx.x & 63)));
         prep2_item<E, DK, DV, KIND>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV>::BYTES, lds,
                                     bh * T + t0, hm.key(bh) * T + t0, min(CHUNK, T - t0),
-                                    (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
+                                    (int)(threadIdx.x >> 6), ln);
         if (item + gridDim.x < nitems) lds_barrier();   // both wavefronts are done with the LDS
     }
 }
@@ -1466,6 +1472,105 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
 }
 
 // ---------------------------------------------------------------------------
+// Fused prefill for KDA: the same hand-off as above, with the four-wavefront
+// KDA prep as the prep workgroups.
+// ---------------------------------------------------------------------------
+// On each XCD the first NP workgroups each take the XCD's (chunk, head)
+// items in chunk-major order, one item at a time on all four wavefronts;
+// after an item every wavefront waits for its stores, and once all four
+// have passed a barrier one of them publishes the block's two tags. The
+// workgroups after them scan the XCD's heads exactly as in chunk_fused_kernel.
+// KDA's prep is bound by the SIMDs' issue (exponentials), so the prep gets
+// every workgroup slot the scan leaves free, and the scan takes wide value
+// tiles (fewer scan workgroups).
+template <typename E, int D, int BV>
+union FusedKdaLds {
+    KdaPrepLds<E, D, D> prep;
+    ScanLds<E, D, D, KIND_KDA, BV> scan;
+};
+
+template <typename E, int D, int BV>
+__global__ __launch_bounds__(256, 2) void chunk_fused_kda_kernel(const E* __restrict__ q,
+                                                                 const E* __restrict__ k,
+                                                                 const E* __restrict__ v,
+                                                                 const E* __restrict__ beta,
+                                                                 const E* __restrict__ g,
+                                                                 char* __restrict__ ws,
+                                                                 const float* __restrict__ S0,
+                                                                 E* __restrict__ o,
+                                                                 float* __restrict__ S_final, int T,
+                                                                 int nchunks, int BH, int NP, u64 epoch,
+                                                                 int spin, HeadMap hm) {
+    typedef WsLayout<E, D, D> Lw;
+    constexpr int NV = D / BV;
+    __shared__ FusedKdaLds<E, D, BV> lds;
+    const int xcd = blockIdx.x & 7, s = blockIdx.x >> 3;
+    const int nh = xcd < BH ? (BH - 1 - xcd) / 8 + 1 : 0;   // heads xcd, xcd + 8, ...
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    u64* tags = block_tags<E, D, D>(ws, BH, nchunks);
+    u64* err = tags + 2L * BH * nchunks;
+    const u64 tag = xcc_tag(epoch);
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        __hip_atomic_store(err + 1, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    if (s < NP) {
+        const long total = (long)nh * nchunks;
+        for (long m = s; m < total; m += NP) {
+            const int c = (int)(m / nh);
+            const long bh = xcd + 8L * (m % nh);
+            int ln;   // (see chunk_fused_kernel)
+            asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+            const int t0 = c * CHUNK;
+            kda_prep4_item<E, D, D>(q, k, v, beta, g, ws + (bh * nchunks + c) * Lw::BYTES, lds.prep, bh * T + t0,
+                                    hm.key(bh) * T + t0, min(CHUNK, T - t0), w, ln);
+            // every wavefront's stores to the block have completed before the
+            // barrier; the tags follow it (the barrier also keeps the next
+            // item's LDS writes behind this item's reads)
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            lds_barrier();
+            if (w == 0 && ln == 0) {
+                __hip_atomic_store(tags + 2 * (bh * nchunks + c), tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(tags + 2 * (bh * nchunks + c) + 1, tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+        }
+        return;
+    }
+    const int slot = s - NP, vt = slot % NV, i = slot / NV;
+    if (i >= nh) return;
+    const long bh = xcd + 8L * i;
+    const SeqView sv{ws + bh * nchunks * Lw::BYTES, hm.key(bh) * T, bh * T, bh, T, nchunks};
+    scan_body<E, D, D, KIND_KDA, BV, true, 2>(sv, q, S0, o, S_final, vt, w, lane, lds.scan,
+                                           tags + 2 * bh * nchunks, tag, err, epoch, spin);
+}
+
+// KDA's prep as the recomputation after a one-launch call: it runs only if
+// that launch's hand-off failed (its error word holds gval); few workgroups
+// take the items in turn.
+template <typename E, int D>
+__global__ __launch_bounds__(256, 2) void chunk_prep_kda_redo_kernel(const E* __restrict__ q,
+                                                                     const E* __restrict__ k,
+                                                                     const E* __restrict__ v,
+                                                                     const E* __restrict__ beta,
+                                                                     const E* __restrict__ g,
+                                                                     char* __restrict__ ws, int T, int nchunks,
+                                                                     long nitems, HeadMap hm,
+                                                                     const unsigned long long* guard,
+                                                                     unsigned long long gval) {
+    if (__hip_atomic_load(guard, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != gval) return;
+    __shared__ KdaPrepLds<E, D, D> lds;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (long item = blockIdx.x; item < nitems; item += gridDim.x) {
+        const long bh = item / nchunks;
+        const int t0 = (int)(item % nchunks) * CHUNK;
+        int ln;   // (see chunk_fused_kernel)
+        asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
+        kda_prep4_item<E, D, D>(q, k, v, beta, g, ws + item * WsLayout<E, D, D>::BYTES, lds, bh * T + t0,
+                                hm.key(bh) * T + t0, min(CHUNK, T - t0), w, ln);
+        if (item + gridDim.x < nitems) lds_barrier();   // every wavefront is done with the LDS
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 // Compute units of the current device (queried once per device).
@@ -1639,6 +1744,44 @@ static hipError_t fused_t(const void* q, const void* k, const void* v, const voi
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return scan_launch<E, D, KIND, false>(q, s0c, o, S_final, ws, BH, T, nullptr, st, hm, err, epoch);
+}
+
+// KDA's one-launch form: the prep (bound by the SIMDs' issue) takes every
+// workgroup slot the scan leaves free, two per CU (its LDS allows no more),
+// and the scan takes value tiles of BV columns.
+template <typename E, int D, int BV>
+static hipError_t fused_kda_t(const void* q, const void* k, const void* v, const void* beta,
+                              const void* g, const float* S0, void* o, float* S_final, void* ws, int BH,
+                              int T, hipStream_t st, HeadMap hm) {
+    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    const int per_xcd = 2 * device_cu_count() / 8;
+    const int ns = (BH + 7) / 8 * (D / BV);   // scan workgroups of the busiest XCD
+    const long items = (long)(BH + 7) / 8 * nchunks;
+    int np = per_xcd - ns;
+    if (np < 16) return hipErrorNotSupported;
+    if ((long)np > items) np = (int)items;
+    char* wsc = static_cast<char*>(ws);
+    const u64* err = reinterpret_cast<const u64*>(wsc + ws_tail_off<E, D>(BH, nchunks)) + 2L * BH * nchunks;
+    float* s0c = nullptr;
+    if (S0) {
+        s0c = reinterpret_cast<float*>(wsc + ws_s0copy_off<E, D>(BH, nchunks));
+        const hipError_t e = launch_state_copy(S0, s0c, (long long)BH * D * D, st);
+        if (e != hipSuccess) return e;
+    }
+    const u64 epoch = next_epoch();
+    hipLaunchKernelGGL((chunk_fused_kda_kernel<E, D, BV>), dim3((unsigned)(8 * (np + ns))), dim3(256), 0, st,
+                       (const E*)q, (const E*)k, (const E*)v, (const E*)beta, (const E*)g, (char*)ws, S0, (E*)o,
+                       S_final, T, nchunks, BH, np, epoch, handoff_spin_limit(), hm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long pitems = (long)BH * nchunks;
+    const long pgrid = min(pitems, 2L * device_cu_count());
+    hipLaunchKernelGGL((chunk_prep_kda_redo_kernel<E, D>), dim3((unsigned)pgrid), dim3(256), 0, st, (const E*)q,
+                       (const E*)k, (const E*)v, (const E*)beta, (const E*)g, (char*)ws, T, nchunks, pitems, hm, err,
+                       epoch);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return scan_launch<E, D, KIND_KDA, false>(q, s0c, o, S_final, ws, BH, T, nullptr, st, hm, err, epoch);
 }
 
 // Two-phase prefill with chunks of CH tokens (32, 64 or 128): the prep and the
@@ -1878,7 +2021,16 @@ static hipError_t fused_kind(int kind, const void* q, const void* k, const void*
     if constexpr (sizeof(E) != 2) {
         return hipErrorNotSupported;
     } else {
-        if (kind == KIND_KDA || kind == KIND_SSM) return hipErrorNotSupported;
+        if (kind == KIND_SSM) return hipErrorNotSupported;
+        if (kind == KIND_KDA) {
+            // sixteen scan workgroups per XCD where the heads allow it: 16-column
+            // tiles for up to two heads per XCD, 32 columns above (measured at
+            // d = 128: 1x16x16384 373 us with 16 columns against 405 with 32;
+            // 2x16x8192 243 us with 32 columns against 305 with 16 and 290 with 64)
+            if ((BH + 7) / 8 * (D / 16) <= 16)
+                return fused_kda_t<E, D, 16>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
+            return fused_kda_t<E, D, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
+        }
         const bool wide = scan_bv<D>(BH) == 32;
         if (kind == KIND_GATED)
             return wide ? fused_t<E, D, KIND_GATED, 32>(q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm)

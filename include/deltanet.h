@@ -148,7 +148,7 @@ int dn_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void
 
 /*
  * Whether the latest one-launch prefill (dn_chunk_fwd_fused, or dn_chunk_fwd
- * taking that form) that used `workspace` with these sizes had a hand-off
+ * or dn_kda_chunk_fwd taking that form) that used `workspace` with these sizes had a hand-off
  * wait give up: DN_EHANDOFF if so (its results were recomputed by the two
  * phases and are correct), DN_OK if not or if no one-launch call used the
  * workspace. Reads 16 bytes of the workspace after synchronizing `stream`
@@ -179,7 +179,11 @@ int dn_chunk_fwd_len(const void* q, const void* k, const void* v, const void* be
  * KDA chunkwise prefill: as dn_chunk_fwd but g is REQUIRED and holds one
  * log-decay per key channel, g [B,H,T,dk] (page "A walk through of the
  * DeltaNet family of linear attention variants", KDA section). Uses the same
- * workspace size function.
+ * workspace size function. Like dn_chunk_fwd it takes the one-launch form for
+ * bf16 sequences of 64 chunks and more where the heads leave room for the
+ * prep workgroups (the prep of a chunk on four wavefronts, then the same
+ * hand-off, the same guarded recomputation and the same status query,
+ * dn_chunk_fwd_handoff_status); results are bitwise those of the two phases.
  */
 int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
                      const void* g, const float* S0, void* o, float* S_final,

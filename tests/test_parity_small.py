@@ -195,7 +195,7 @@ def test_long_prefill(kind, dtype, T):
     """Sequences of 32 chunks and more, with a ragged last chunk: same results as
     the oracle with a start state, bitwise the same with the state updated in
     place, and bitwise equal to calling the two phases one after the other
-    (from 64 chunks on, chunk_fwd runs bf16 DeltaNet / Gated DeltaNet as one
+    (from 64 chunks on, chunk_fwd and kda_chunk_fwd run bf16 inputs as one
     launch)."""
     dn = _dn()
     say("long prefill", kind, dtype, T)
@@ -315,6 +315,85 @@ def test_fused_handoff_failure_recomputed(in_place, monkeypatch):
     assert dn.chunk_fwd_handoff_status(ws, B, H, T, 128, 128, dt) == 0
     assert torch.equal(o3, o2) and torch.equal(S3, S2)
     assert nch >= 64
+
+
+@pytest.mark.parametrize("BH", [(1, 2), (3, 5)])
+def test_kda_fused_handoff(BH):
+    """KDA's one-launch prefill (from 64 chunks on; four-wavefront prep
+    workgroups publish each block once all four wavefronts' stores are done):
+    bitwise equal to the two phases, every block's two tags carry the launch
+    epoch and the XCD of the head (h % 8), the error word is untouched, and the
+    results match the oracle."""
+    dn = _dn()
+    B, H = BH
+    T = 64 * 64 + 9
+    nch = (T + 63) // 64
+    say("kda fused hand-off", B, H, T)
+    inp = make("kda", B, H, T, 128, "bf16", seed=37, s0_std=0.5)
+    d = to_dev(inp)
+    dt = d["q"].dtype
+    nbytes = dn.workspace_bytes(B, H, T, 128, 128, dt)
+    block = dn.workspace_bytes(1, 1, 128, 128, 128, dt) - dn.workspace_bytes(1, 1, 64, 128, 128, dt)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    o, S = dn.kda_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"], workspace=ws)
+    torch.cuda.synchronize()
+    tail = ws[B * H * nch * block:].cpu()
+    tags = tail[:B * H * nch * 16].view(torch.int64).view(B * H, nch, 2).clone()
+    err, last = (int(x) for x in tail[B * H * nch * 16:B * H * nch * 16 + 16].view(torch.int64))
+    assert err == 0 and last != 0
+    assert dn.chunk_fwd_handoff_status(ws, B, H, T, 128, 128, dt) == 0
+    assert torch.equal(tags[:, :, 0], tags[:, :, 1])
+    t = tags[:, :, 0].numpy().astype(np.uint64)
+    low = t & np.uint64((1 << 56) - 1)
+    assert (low == low[0, 0]).all() and low[0, 0] != 0
+    assert np.uint64(last & ((1 << 56) - 1)) == low[0, 0]
+    xcc = ((t >> np.uint64(56)) & np.uint64(15)) ^ ((t[0, 0] >> np.uint64(56)) & np.uint64(15))
+    for h in range(B * H):
+        assert (xcc[h] == np.uint64(h % 8)).all(), (h, xcc[h])
+    ws2 = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o2, S2 = torch.empty_like(o), torch.empty_like(S)
+    dn.chunk_prep(d["q"], d["k"], d["v"], d["beta"], d["g"], ws2, kda=True)
+    dn.chunk_scan(d["q"], o2, ws2, d["S0"], S2, kda=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(S2, S)
+    o_ref, S_ref = oracle_prefill(inp)
+    eo, es = rel_err(o, o_ref), rel_err(S, S_ref)
+    say("  err o %.3e  S %.3e" % (eo, es))
+    assert eo <= TOL["bf16"] and es <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("in_place", [False, True])
+def test_kda_fused_handoff_failure_recomputed(in_place, monkeypatch):
+    """KDA's one-launch form with its hand-off waits cut to zero polls (from
+    the host; every kernel still ends normally): the launch marks itself
+    failed, the guarded two phases behind it recompute the call (bitwise the
+    two-phase results, also with the state updated in place), the status
+    query reports DN_EHANDOFF, and the next call with the default limit DN_OK."""
+    dn = _dn()
+    B, H, T = 1, 4, 66 * 64 + 21
+    say("kda fused hand-off failure", in_place, B, H, T)
+    inp = make("kda", B, H, T, 128, "bf16", seed=41, s0_std=0.5)
+    d = to_dev(inp)
+    dt = d["q"].dtype
+    ws = torch.empty(dn.workspace_bytes(B, H, T, 128, 128, dt), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty_like(ws)
+    o2, S2 = torch.empty(B, H, T, 128, dtype=dt, device="cuda"), torch.empty_like(d["S0"])
+    dn.chunk_prep(d["q"], d["k"], d["v"], d["beta"], d["g"], ws2, kda=True)
+    dn.chunk_scan(d["q"], o2, ws2, d["S0"], S2, kda=True)
+    monkeypatch.setenv("DN_HANDOFF_SPIN_LIMIT", "0")
+    if in_place:
+        S = d["S0"].clone()
+        o, S1 = dn.kda_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], S, S_final=S, workspace=ws)
+        assert S1 is S
+    else:
+        o, S1 = dn.kda_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"], workspace=ws)
+    st = dn.chunk_fwd_handoff_status(ws, B, H, T, 128, 128, dt)
+    assert st == _lib_status("DN_EHANDOFF"), st
+    assert torch.equal(o, o2) and torch.equal(S1, S2)
+    monkeypatch.delenv("DN_HANDOFF_SPIN_LIMIT")
+    o3, S3 = dn.kda_chunk_fwd(d["q"], d["k"], d["v"], d["beta"], d["g"], d["S0"], workspace=ws)
+    assert dn.chunk_fwd_handoff_status(ws, B, H, T, 128, 128, dt) == 0
+    assert torch.equal(o3, o2) and torch.equal(S3, S2)
 
 
 def _lib_status(name):
