@@ -1707,16 +1707,14 @@ static hipError_t fused_t(const void* q, const void* k, const void* v, const voi
     const long items = (long)(BH + 7) / 8 * nchunks;
     int np = per_xcd - ns;
     if (np < 16) return hipErrorNotSupported;
-    // Few heads: the XCD's scan workgroups and a few prep workgroups fit one
-    // to a CU (the hardware deals out one workgroup per CU before it doubles
-    // up), so no scan shares its CU with a prep. Six prep workgroups (twelve
-    // items in flight) per head keep just ahead of the scan at d = 128: the
-    // blocks are then read soon after they are written, and the prep traffic
-    // is spread thin. Measured with 16 heads of 65536 tokens: 1.05 ms against
-    // 1.37 ms with every slot filled (and 1.20 ms with 8, 1.44 ms with 4 prep
-    // workgroups per head).
-    const int cus_per_xcd = device_cu_count() / 8;
-    if (cus_per_xcd - ns >= 8) np = min(cus_per_xcd - ns, 6 * ((BH + 7) / 8));
+    // Seven prep workgroups (fourteen items in flight) per head keep just
+    // ahead of the scan at d = 128: the blocks are then read soon after they
+    // are written, and the prep traffic is spread thin. With up to two heads
+    // per XCD they fit beside the scan workgroups one to a CU (the hardware
+    // deals out one workgroup per CU before it doubles up). Measured with 16
+    // heads of 65536 tokens: 0.88 ms with 7, against 1.17 ms with 5 and 8 and
+    // 1.00 ms with 6 prep workgroups per head.
+    np = min(np, 7 * ((BH + 7) / 8));
     if ((long)np > (items + 1) / 2) np = (int)((items + 1) / 2);
     char* wsc = static_cast<char*>(ws);
     const u64* err = reinterpret_cast<const u64*>(wsc + ws_tail_off<E, D>(BH, nchunks)) + 2L * BH * nchunks;
@@ -2040,18 +2038,28 @@ static hipError_t fused_kind(int kind, const void* q, const void* k, const void*
     }
 }
 
-// The one-launch form pays about one prep item's latency (some 10 us) before
-// the scan can start, against the whole prep phase and the gap between two
-// launches saved. Measured at d = 128 with 16 to 32 heads: level with the two
-// launches at 32 chunks per sequence, 8 to 14 % faster from 64 chunks on.
-constexpr int FUSED_MIN_CHUNKS = 64;
+// Where the one-launch form beats the two launches (dn_chunk_fwd and
+// dn_kda_chunk_fwd without a choice). It pays about one prep item's latency
+// before the scan can start and shares the CUs between the two roles; it saves
+// the prep phase's own time and reads the blocks from L2. Measured at d = 128
+// (bf16), one launch against two, Gated DeltaNet: 1.04-1.09x at 64 chunks per
+// sequence and at 128 chunks with 8 heads, 0.94-0.96x at 128 chunks with 16-32
+// heads, 0.72x at 256 chunks with 16 heads, 0.63-0.72x at 1,024 chunks with
+// 4-16 heads. KDA (whose prep is bound by the SIMDs' issue): 0.79-0.93x from
+// 64 chunks on with 8-32 heads, 1.03x with 64 heads, and 1.08-1.15x at 1,024
+// chunks with 4-8 heads (the scan chain, slower beside the prep, then sets
+// the time).
+static bool fused_preferred(int kind, int BH, int nchunks) {
+    if (kind == KIND_KDA) return nchunks >= 64 && BH <= 32 && (nchunks <= 512 || BH >= 16);
+    return nchunks >= 512 || (nchunks >= 128 && BH >= 16);
+}
 
 template <typename E, int D>
 static hipError_t fwd_t(int kind, const void* q, const void* k, const void* v, const void* beta,
                         const void* g, const float* S0, void* o, float* S_final, void* ws, int BH,
                         int T, int mode, hipStream_t st, HeadMap hm) {
     const int nchunks = (T + CHUNK - 1) / CHUNK;
-    if (mode == FWD_FUSED || (mode == FWD_AUTO && nchunks >= FUSED_MIN_CHUNKS)) {
+    if (mode == FWD_FUSED || (mode == FWD_AUTO && fused_preferred(kind, BH, nchunks))) {
         const hipError_t e = fused_kind<E, D>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, st, hm);
         if (e != hipErrorNotSupported || mode == FWD_FUSED) return e;
     }

@@ -111,7 +111,8 @@ int dn_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
  * this form does not exist: dtype other than bf16, or more heads than leave
  * room for the prep workgroups (B*H above about 48 per 8 heads' worth of
  * value tiles; dn_chunk_fwd then runs the two phases). dn_chunk_fwd itself
- * uses this form for sequences of 64 chunks (4096 tokens) and more.
+ * uses this form for long sequences, where it is the faster one: from 128
+ * chunks (8,192 tokens) with 16 heads or more, from 512 chunks with fewer.
  *
  * The hand-off relies on two measured facts of the hardware, not guaranteed
  * by any API: workgroup b of a launch runs on XCD b mod 8, and workgroups
@@ -179,11 +180,12 @@ int dn_chunk_fwd_len(const void* q, const void* k, const void* v, const void* be
  * KDA chunkwise prefill: as dn_chunk_fwd but g is REQUIRED and holds one
  * log-decay per key channel, g [B,H,T,dk] (page "A walk through of the
  * DeltaNet family of linear attention variants", KDA section). Uses the same
- * workspace size function. Like dn_chunk_fwd it takes the one-launch form for
- * bf16 sequences of 64 chunks and more where the heads leave room for the
- * prep workgroups (the prep of a chunk on four wavefronts, then the same
- * hand-off, the same guarded recomputation and the same status query,
- * dn_chunk_fwd_handoff_status); results are bitwise those of the two phases.
+ * workspace size function. Like dn_chunk_fwd it takes a one-launch form for
+ * bf16 where that is the faster one: from 64 chunks (4,096 tokens) with up to
+ * 32 heads, past 512 chunks only with 16 heads or more (the prep of a chunk
+ * on four wavefronts, then the same hand-off, the same guarded recomputation
+ * and the same status query, dn_chunk_fwd_handoff_status); results are
+ * bitwise those of the two phases.
  */
 int dn_kda_chunk_fwd(const void* q, const void* k, const void* v, const void* beta,
                      const void* g, const float* S0, void* o, float* S_final,

@@ -195,8 +195,7 @@ def test_long_prefill(kind, dtype, T):
     """Sequences of 32 chunks and more, with a ragged last chunk: same results as
     the oracle with a start state, bitwise the same with the state updated in
     place, and bitwise equal to calling the two phases one after the other
-    (from 64 chunks on, chunk_fwd and kda_chunk_fwd run bf16 inputs as one
-    launch)."""
+    (kda_chunk_fwd runs bf16 inputs of 64 chunks and more as one launch)."""
     dn = _dn()
     say("long prefill", kind, dtype, T)
     inp = make(kind, 1, 2, T, 128, dtype, seed=23, s0_std=0.5)
@@ -319,7 +318,7 @@ def test_fused_handoff_failure_recomputed(in_place, monkeypatch):
 
 @pytest.mark.parametrize("BH", [(1, 2), (3, 5)])
 def test_kda_fused_handoff(BH):
-    """KDA's one-launch prefill (from 64 chunks on; four-wavefront prep
+    """KDA's one-launch prefill (kda_chunk_fwd from 64 chunks on; four-wavefront prep
     workgroups publish each block once all four wavefronts' stores are done):
     bitwise equal to the two phases, every block's two tags carry the launch
     epoch and the XCD of the head (h % 8), the error word is untouched, and the
