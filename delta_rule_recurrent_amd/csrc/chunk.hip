@@ -1105,7 +1105,8 @@ __device__ __forceinline__ u64* block_tags(char* ws, long BH, int nchunks) {
 // SYNC: the chunk blocks are produced concurrently in the same launch and
 // each is waited for (tags at `tags`, expected value `tag`) before its
 // operands are loaded. RING: 3 (two chunks prefetched) or 2 (one chunk; fewer
-// registers held, which leaves the fused launch's register budget room).
+// registers held; the Gated DeltaNet one-launch form, where three measured no
+// faster).
 template <typename E, int DK, int DV, int KIND, int BV, bool SYNC, int RING, bool EMIT = false, int CH = CHUNK>
 __device__ __forceinline__ void scan_body(const SeqView sv, const E* __restrict__ q,
                                           const float* __restrict__ S0, E* __restrict__ o,
@@ -1482,7 +1483,11 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kernel(const E* __restrict
 // workgroups after them scan the XCD's heads exactly as in chunk_fused_kernel.
 // KDA's prep is bound by the SIMDs' issue (exponentials), so the prep gets
 // every workgroup slot the scan leaves free, and the scan takes wide value
-// tiles (fewer scan workgroups).
+// tiles (fewer scan workgroups). The scan keeps two chunks of operands in
+// flight, as in the two-phase form (2-3 % faster than one here; the
+// matrix-core accumulators in vector registers leave room for both roles).
+// Measured at 2x16x8192: 243 us with every free slot taken by the prep,
+// against 260 us with 40 prep workgroups per XCD and 292 us with 32.
 template <typename E, int D, int BV>
 union FusedKdaLds {
     KdaPrepLds<E, D, D> prep;
@@ -1539,7 +1544,7 @@ __global__ __launch_bounds__(256, 2) void chunk_fused_kda_kernel(const E* __rest
     if (i >= nh) return;
     const long bh = xcd + 8L * i;
     const SeqView sv{ws + bh * nchunks * Lw::BYTES, hm.key(bh) * T, bh * T, bh, T, nchunks};
-    scan_body<E, D, D, KIND_KDA, BV, true, 2>(sv, q, S0, o, S_final, vt, w, lane, lds.scan,
+    scan_body<E, D, D, KIND_KDA, BV, true, 3>(sv, q, S0, o, S_final, vt, w, lane, lds.scan,
                                            tags + 2 * bh * nchunks, tag, err, epoch, spin);
 }
 
