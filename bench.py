@@ -72,21 +72,27 @@ def log(*a):
 # kernel and is reported as null.
 FETCH_SCALE, WRITE_SCALE = 2.0, 1.0
 CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurrent_amd/csrc/dn_chunk.h",
-                 "delta_rule_recurrent_amd/csrc/dn_device.h", "delta_rule_recurrent_amd/csrc/dn_launch.h")
+                 "delta_rule_recurrent_amd/csrc/dn_device.h", "delta_rule_recurrent_amd/csrc/dn_launch.h",
+                 "delta_rule_recurrent_amd/csrc/dn_kda_prep.h", "delta_rule_recurrent_amd/build.py")
 DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
                   "delta_rule_recurrent_amd/csrc/dn_launch.h")
 TRAFFIC = {
-    # B=4 H=8 T=2048 d=128 (grid 1024 x 128 threads; 3910 / 4010 dispatches)
-    "chunk_prep2_kernel": {"fetch_kib": 29109.2, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
-                           "sha256": "e255237613ea2dfcb01805cd0bf81ab8c77948ef2c6fa95c5e58f59b42f2dcc0"},
-    # B=4 H=8 T=2048 d=128 (grid 256 x 256 threads; 3910 / 4010 dispatches)
-    "chunk_scan_kernel": {"fetch_kib": 37107.5, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
-                          "sha256": "e255237613ea2dfcb01805cd0bf81ab8c77948ef2c6fa95c5e58f59b42f2dcc0"},
-    # B=1 H=16 T=65536 d=128 (grid 224 x 256 threads; 770 / 790 dispatches)
-    "chunk_fused_kernel": {"fetch_kib": 982206.7, "write_kib": 1193986.3, "sources": CHUNK_SOURCES,
-                           "sha256": "e255237613ea2dfcb01805cd0bf81ab8c77948ef2c6fa95c5e58f59b42f2dcc0"},
+    # B=4 H=8 T=2048 d=128 (grid 1024 x 128 threads; 3670 / 4170 dispatches)
+    "chunk_prep2_kernel": {"fetch_kib": 28547.4, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
+                           "sha256": "3450d50feaf0e2bd72627671cb49c44521298bb5df4843bed615d30fcef4d491"},
+    # B=4 H=8 T=2048 d=128 (grid 256 x 256 threads; 3670 / 4170 dispatches)
+    "chunk_scan_kernel": {"fetch_kib": 37109.5, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
+                          "sha256": "3450d50feaf0e2bd72627671cb49c44521298bb5df4843bed615d30fcef4d491"},
+    # B=1 H=16 T=65536 d=128 (grid 240 x 256 threads; 830 / 830 dispatches)
+    "chunk_fused_kernel": {"fetch_kib": 987845.4, "write_kib": 1193989.6, "sources": CHUNK_SOURCES,
+                           "sha256": "3450d50feaf0e2bd72627671cb49c44521298bb5df4843bed615d30fcef4d491"},
+    # KDA B=2 H=16 T=8192 d=128 (grid 512 x 256 threads; 54 / 54 dispatches), from
+    #   rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --no-cpu
+    #       --no-prefill --no-long --no-decode
+    "chunk_fused_kda_kernel": {"fetch_kib": 283274.3, "write_kib": 367137.8, "sources": CHUNK_SOURCES,
+                               "sha256": "3450d50feaf0e2bd72627671cb49c44521298bb5df4843bed615d30fcef4d491"},
     # B=256 H=16 d=128, one token (311 dispatches each)
-    "decode_step_kernel": {"fetch_kib": 136307.5, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+    "decode_step_kernel": {"fetch_kib": 136307.9, "write_kib": 263168.0, "sources": DECODE_SOURCES,
                            "sha256": "827188831a721cb9d51c314c05a6e14c4a6d5eb4033c2119767958926a8feec6"},
 }
 
@@ -537,6 +543,14 @@ def run_workloads(torch, dn, synthetic, to_dev, dev):
                 nb += Bw * Hw * Tw * (dw - 1) * (2 if dt == torch.bfloat16 else 4)   # g per key channel
             entry["gbs_algorithmic"] = round(nb / (ms * 1e-3) / 1e9, 1)
             entry["frac_hbm"] = round(nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            if kda and dt == torch.bfloat16:
+                # the one-launch form (the call's two guarded recomputation
+                # launches return at once); counter traffic against the
+                # compulsory bytes
+                tb = traffic_bytes("chunk_fused_kda_kernel")
+                entry["kernel"] = "chunk_fused_kda_kernel"
+                entry["traffic"] = tb
+                entry["traffic_vs_compulsory"] = round(tb / nb, 2) if tb else None
         wl["%s/%s" % (wname, form)] = entry
         log("  %s %s %.4f ms" % (wname, form, ms))
         del x, wsw, ow, Sw
