@@ -297,8 +297,7 @@ int dn_chunk_fwd_gqa(int kda, const void* q, const void* k, const void* v, const
     if (!head_map(Hk, Hv, &hm)) return DN_EINVAL;
     const int kind = chunk_kind(kda != 0, g);
     return chunk_common(kind, q, k, v, beta, g, S0, o, S_final, B, Hv, T, dk, dv, dtype,
-                        workspace, workspace_bytes, stream,
-                        kind == dn::KIND_KDA ? dn::FWD_TWO : dn::FWD_AUTO, hm);
+                        workspace, workspace_bytes, stream, dn::FWD_AUTO, hm);
 }
 
 int dn_decode_step_gqa(int kda, const void* q, const void* k, const void* v, const void* beta,

@@ -449,14 +449,12 @@ def _gqa_inputs(kind, B, Hk, Hv, T, d, dtype, seed):
 
 @pytest.mark.parametrize("kind", KINDS)
 @pytest.mark.parametrize("dtype,d,T,Hk,Hv", [("bf16", 128, 200, 2, 6), ("f32", 64, 137, 1, 3),
-                                             ("bf16", 128, 64 * 64 + 5, 1, 2)])
+                                             ("bf16", 128, 128 * 64 + 5, 4, 16)])
 def test_gqa_prefill(kind, dtype, d, T, Hk, Hv):
     """Key heads shared by value heads: bitwise equal to the plain prefill on
     q, k repeated over heads (the pages' repeat_interleave), and within the
-    bound of the oracle run on that repetition. T = 4101 takes the one-launch
-    form for the kinds that have it."""
-    if kind == "kda" and T > 1000:
-        pytest.skip("one long case per form is enough; KDA has only the two-phase form")
+    bound of the oracle run on that repetition. 16 value heads of 129 chunks
+    take the one-launch form (every kind has it at bf16)."""
     dn = _dn()
     say("gqa prefill", kind, dtype, d, T, Hk, Hv)
     inp, rep = _gqa_inputs(kind, 1 if T > 1000 else 2, Hk, Hv, T, d, dtype, seed=51)
