@@ -85,17 +85,20 @@ __device__ __forceinline__ void g_row8(const float* G, int ldg, int row, int c, 
     }
 }
 
-// Level fragments of one row: the factor exp2(sg (G_row - G_ref)) applied to
-// the row's key (zk) and, with Q, query (zq) values; sg = +1 in the upper half
-// of the row's group, -1 in the lower half (the exponent is then <= 0).
+// Level fragments of one row: the decay between the row's token and the
+// reference token, exp2(-|G_row - G_ref|), applied to the row's key (zk) and,
+// with Q, query (zq) values. G never increases along the chunk (every
+// log-decay is <= 0), so this is exp2(G_row - G_ref) in the upper half of the
+// row's group and exp2(G_ref - G_row) in the lower half; the sign costs no
+// instruction (the exponential's source modifiers).
 template <typename E, bool Q>
 __device__ __forceinline__ void level_frags(const typename Frag<E>::type& kx,
                                             const typename Frag<E>::type& qx, const float (&gi)[8],
-                                            const float (&gr)[8], float sg,
+                                            const float (&gr)[8],
                                             typename Frag<E>::type& zk, typename Frag<E>::type& zq) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const float f = exp2_raw(sg * (gi[j] - gr[j]));
+        const float f = exp2_raw(-fabsf(gi[j] - gr[j]));
         zk[j] = from_f32<E>(to_f32(kx[j]) * f);
         if (Q) zq[j] = from_f32<E>(to_f32(qx[j]) * f);
     }
@@ -155,7 +158,7 @@ __device__ __forceinline__ void kda_intra(const KQSlice<E> (&sl)[2], int t0, con
                 float gr[8];
                 g_row8(G, LDG, ref, c, gr);
                 F zk, zq;
-                level_frags<E, true>(sl[h].k[kb], sl[h].q[kb], gi, gr, (n & (sz - 1)) >= half ? 1.f : -1.f, zk, zq);
+                level_frags<E, true>(sl[h].k[kb], sl[h].q[kb], gi, gr, zk, zq);
                 sA[lv - 1] = mma(zk, zk, sA[lv - 1]);   // (Z Z^T)[i][j]
                 sT[lv - 1] = mma(zk, zq, sT[lv - 1]);   // (Z Zq^T)[j][i] = attn^T
             }
@@ -203,8 +206,8 @@ __device__ __forceinline__ void kda_cross(KQSlice<E> (&sl)[2], const E* __restri
                 const int tt = 2 * pp + h;
                 float gi[8];
                 g_row8(G, LDG, 16 * tt + n, c, gi);
-                level_frags<E, true>(x.k[tt], x.q[tt], gi, g5, h ? 1.f : -1.f, z5k[h], z5q[h]);
-                level_frags<E, true>(x.k[tt], x.q[tt], gi, g6, pp ? 1.f : -1.f, z6k[h], z6q[h]);
+                level_frags<E, true>(x.k[tt], x.q[tt], gi, g5, z5k[h], z5q[h]);
+                level_frags<E, true>(x.k[tt], x.q[tt], gi, g6, z6k[h], z6q[h]);
             }
             if (pp == 0) {
                 // level 5: tiles (1, 0)
