@@ -14,6 +14,8 @@
 // epilogue reads the head-major read-out and z and writes token-major rows for the
 // output projection. Arithmetic is fp32 with one rounding to the storage type at
 // each output.
+#include <type_traits>
+
 #include "dn_device.h"
 #include "dn_launch.h"
 
@@ -23,7 +25,7 @@ namespace {
 constexpr int LAYER_WG = 256;   // threads per workgroup of the layer kernels
 constexpr int RUN = 8;          // consecutive tokens one lane group convolves in registers
 constexpr int CONV_K = 4;       // convolution width (its state: the last 3 inputs)
-constexpr int EPI_ROWS = 64;    // rows of the read-out per epilogue workgroup
+constexpr int EPI_ROWS = 32;    // rows of the output per epilogue workgroup
 
 // Eight consecutive elements <-> fp32.
 __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
@@ -64,22 +66,25 @@ __device__ __forceinline__ void load_raw(const float* p, Raw8<float>& r) {
 }
 __device__ __forceinline__ float elem(const Raw8<bf16>& r, int i) { return (float)r.v[i]; }
 __device__ __forceinline__ float elem(const Raw8<float>& r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
-
-// SiLU with the hardware exp2 and reciprocal (each within 1 ulp): x / (1 + e^-x).
-// Large negative x gives e^-x = inf and a zero reciprocal, so the result is -0.
-__device__ __forceinline__ float silu(float x) {
-    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+__device__ __forceinline__ void set_elem(Raw8<bf16>& r, int i, bf16 x) { r.v[i] = x; }
+__device__ __forceinline__ void set_elem(Raw8<float>& r, int i, float x) {
+    if (i < 4) r.a[i] = x;
+    else r.b[i - 4] = x;
 }
 
-// 1 / max(sqrt(s), 1e-12) for a sum of squares s >= 0, with the hardware rsqrt.
-__device__ __forceinline__ float inv_norm(float s) { return __builtin_amdgcn_rsqf(fmaxf(s, 1e-24f)); }
-
-// Sum over the `width` consecutive lanes that hold one row (width a power of two).
-template <int WIDTH>
-__device__ __forceinline__ float row_sum(float s) {
-#pragma unroll
-    for (int m = WIDTH / 2; m >= 1; m /= 2) s += __shfl_xor(s, m, WAVE);
-    return s;
+// bf16 pairs: channel i of two rows as one 32-bit word (the earlier row in the
+// low half), picked with a byte permute; and the fp32 dot product of two pairs
+// plus an accumulator (products of bf16 values are exact in fp32).
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ unsigned pair_of(const Raw8<bf16>& early, const Raw8<bf16>& late, int i) {
+    const unsigned a = __builtin_bit_cast(u32x4, early.v)[i / 2];
+    const unsigned b = __builtin_bit_cast(u32x4, late.v)[i / 2];
+    return __builtin_amdgcn_perm(b, a, (i & 1) ? 0x07060302u : 0x05040100u);
+}
+__device__ __forceinline__ float dot2(unsigned x, unsigned w, float acc) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, w),
+                                           acc, false);
 }
 
 // ---------------------------------------------------------------------------
@@ -106,47 +111,19 @@ __global__ __launch_bounds__(LAYER_WG) void layer_prologue_kernel(
     const long C = (long)(2 * Hk + Hv) * D;
     const long c = (long)s * D + l * 8;   // first of this lane's eight channels
 
-    // Filter taps of the eight channels: conv_w [C][4], 32 consecutive elements.
-    float w[8][CONV_K];
-    {
-        float a[8], bb[8], cc[8], dd[8];
-        load8(conv_w + c * CONV_K, a);
-        load8(conv_w + c * CONV_K + 8, bb);
-        load8(conv_w + c * CONV_K + 16, cc);
-        load8(conv_w + c * CONV_K + 24, dd);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float* src = i < 2 ? a : i < 4 ? bb : i < 6 ? cc : dd;
-            const int o = (i % 2) * 4;
-#pragma unroll
-            for (int j = 0; j < CONV_K; ++j) w[i][j] = src[o + j];
-        }
-    }
-
     // The three inputs before t0: earlier rows of qkv, else the carried state
     // [B][C][3] (oldest first: input t < 0 is state entry 3 + t), else zeros.
-    float h[3][8];
+    Raw8<E> hr[3];
 #pragma unroll
     for (int j = 0; j < 3; ++j) {
         const long tt = t0 - 3 + j;
         if (tt >= 0) {
-            load8(qkv + ((long)b * T + tt) * C + c, h[j]);
-        } else if (cstate) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) h[j][i] = to_f32(cstate[((long)b * C + c + i) * 3 + 3 + tt]);
+            load_raw(qkv + ((long)b * T + tt) * C + c, hr[j]);
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) h[j][i] = 0.0f;
+            for (int i = 0; i < 8; ++i)
+                set_elem(hr[j], i, cstate ? cstate[((long)b * C + c + i) * 3 + 3 + tt] : from_f32<E>(0.0f));
         }
-    }
-
-    // All RUN rows are loaded up front (rows past the end re-read the last one);
-    // only the stores are predicated.
-    Raw8<E> x[RUN];
-#pragma unroll
-    for (int r = 0; r < RUN; ++r) {
-        const long tt = t0 + r < T ? t0 + r : (long)T - 1;
-        load_raw(qkv + ((long)b * T + tt) * C + c, x[r]);
     }
 
     E* out;
@@ -159,27 +136,97 @@ __global__ __launch_bounds__(LAYER_WG) void layer_prologue_kernel(
     const bool is_key = s < 2 * Hk;
     const float qs = s < Hk ? QSCALE : 1.0f;
 
+    // All RUN rows are loaded up front, each a fixed stride after the first. A
+    // run that reaches past the end (only the last one of a sequence) re-reads
+    // its last row for the missing ones and predicates its stores; every other
+    // run takes the same code without the checks.
+    const E* xrow = qkv + ((long)b * T + t0) * C + c;
+    auto run = [&](auto whole) {
+        constexpr bool WHOLE = decltype(whole)::value;
+        const int last = WHOLE ? RUN - 1 : (int)(T - 1 - t0);
+        Raw8<E> x[RUN];
 #pragma unroll
-    for (int r = 0; r < RUN; ++r) {
-        float y[8];
-        float ss = 0.0f;
+        for (int r = 0; r < RUN; ++r) load_raw(xrow + (long)(WHOLE ? r : min(r, last)) * C, x[r]);
+        // SiLU, the key heads' norm and scale, the store of one output row.
+        auto finish = [&](int r, float (&y)[8]) {
+            float ss = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float xi = elem(x[r], i);
-            const float acc = w[i][0] * h[0][i] + w[i][1] * h[1][i] + w[i][2] * h[2][i] + w[i][3] * xi;
-            y[i] = silu(acc);
-            ss += y[i] * y[i];
-            h[0][i] = h[1][i];
-            h[1][i] = h[2][i];
-            h[2][i] = xi;
+            for (int i = 0; i < 8; ++i) {
+                y[i] = silu(y[i]);
+                ss += y[i] * y[i];
+            }
+            if (is_key) {
+                const float sc = qs * inv_norm(row_sum<LPR>(ss));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] *= sc;
+            }
+            if (WHOLE || r <= last) store8(orow + r * D, y);
+        };
+        if constexpr (sizeof(E) == 2) {
+            // conv_w [C][4]: the taps of channel i are 32-bit words 2i (taps 0, 1)
+            // and 2i + 1 (taps 2, 3) of the lane's 64 bytes; the inputs go in as
+            // pairs of consecutive tokens, so each output is two pair products.
+            Raw8<E> wr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) load_raw(conv_w + c * CONV_K + 8 * j, wr[j]);
+            unsigned w01[8], w23[8], p2[8], p1[8];   // pairs (t-3, t-2) and (t-2, t-1)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const u32x4 wd = __builtin_bit_cast(u32x4, wr[i / 2].v);
+                w01[i] = wd[2 * (i % 2)];
+                w23[i] = wd[2 * (i % 2) + 1];
+                p2[i] = pair_of(hr[0], hr[1], i);
+                p1[i] = pair_of(hr[1], hr[2], i);
+            }
+#pragma unroll
+            for (int r = 0; r < RUN; ++r) {
+                float y[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const unsigned p0 = pair_of(r == 0 ? hr[2] : x[r - 1], x[r], i);   // (t-1, t)
+                    y[i] = dot2(p0, w23[i], dot2(p2[i], w01[i], 0.0f));
+                    p2[i] = p1[i];
+                    p1[i] = p0;
+                }
+                finish(r, y);
+            }
+        } else {
+            float w[8][CONV_K], h[3][8];
+            {
+                float a[8], bb[8], cc[8], dd[8];
+                load8(conv_w + c * CONV_K, a);
+                load8(conv_w + c * CONV_K + 8, bb);
+                load8(conv_w + c * CONV_K + 16, cc);
+                load8(conv_w + c * CONV_K + 24, dd);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float* src = i < 2 ? a : i < 4 ? bb : i < 6 ? cc : dd;
+                    const int o = (i % 2) * 4;
+#pragma unroll
+                    for (int j = 0; j < CONV_K; ++j) w[i][j] = src[o + j];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 3; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) h[j][i] = elem(hr[j], i);
+#pragma unroll
+            for (int r = 0; r < RUN; ++r) {
+                float y[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float xi = elem(x[r], i);
+                    y[i] = w[i][0] * h[0][i] + w[i][1] * h[1][i] + w[i][2] * h[2][i] + w[i][3] * xi;
+                    h[0][i] = h[1][i];
+                    h[1][i] = h[2][i];
+                    h[2][i] = xi;
+                }
+                finish(r, y);
+            }
         }
-        if (is_key) {
-            const float sc = qs * inv_norm(row_sum<LPR>(ss));
-#pragma unroll
-            for (int i = 0; i < 8; ++i) y[i] *= sc;
-        }
-        if (t0 + r < T) store8(orow + (long)r * D, y);
-    }
+    };
+    if (t0 + RUN <= T) run(std::true_type{});
+    else run(std::false_type{});
 
     // The new convolution state (the last three inputs of each channel) is
     // written by the group of the first run, the only one that reads the old
@@ -341,8 +388,10 @@ __global__ __launch_bounds__(LAYER_WG) void conv_state_kernel(const E* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Epilogue. EPI_ROWS rows of the head-major read-out o [B][Hv][T][D] per workgroup
-// (consecutive rows, so a wave reads a contiguous span); D/8 lanes per row.
+// Epilogue. EPI_ROWS consecutive rows of the token-major output out [B][T][Hv][D]
+// per workgroup, D/8 lanes per row: a wave reads z and writes out as contiguous
+// spans, and reads the head-major read-out o [B][Hv][T][D] one head row at a time
+// (the layout that measured fastest: two of the three streams are contiguous).
 //   out[b][t][hv*D + c] = w[c] * round(o * rsqrt(mean(o^2) + eps)) * SiLU(z[b][t][hv*D + c])
 // with the normalised value rounded to the storage type before the products.
 // ---------------------------------------------------------------------------
@@ -364,10 +413,10 @@ __global__ __launch_bounds__(LAYER_WG) void layer_epilogue_kernel(
     for (int p = 0; p < PER; ++p) {
         long row = base + p * GROUPS + grp;
         if (row >= rows) row = rows - 1;
-        const long bh = row / T, t = row % T;
-        const long bb = bh / Hv, hv = bh % Hv;
-        zoff[p] = ((bb * T + t) * Hv + hv) * D + l * 8;
-        load_raw(o + row * D + l * 8, ov[p]);
+        const long bt = row / Hv, hv = row % Hv;
+        const long bb = bt / T, t = bt % T;
+        zoff[p] = row * D + l * 8;
+        load_raw(o + ((bb * Hv + hv) * T + t) * D + l * 8, ov[p]);
         load_raw(z + zoff[p], zv[p]);
     }
 #pragma unroll
