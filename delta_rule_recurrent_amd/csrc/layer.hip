@@ -87,6 +87,35 @@ __device__ __forceinline__ float dot2(unsigned x, unsigned w, float acc) {
                                            acc, false);
 }
 
+// SiLU with the hardware exp2 and reciprocal (each within 1 ulp): x / (1 + e^-x).
+// Large negative x gives e^-x = inf and a zero reciprocal, so the result is -0.
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
+
+// 1 / max(sqrt(s), 1e-12) for a sum of squares s >= 0, with the hardware rsqrt.
+__device__ __forceinline__ float inv_norm(float s) { return __builtin_amdgcn_rsqf(fmaxf(s, 1e-24f)); }
+
+// Sum over the `WIDTH` consecutive lanes that hold one row (8 or 16, aligned), with
+// data-parallel-primitive moves inside a row of 16 lanes: swap neighbours, swap
+// pairs (each quad then holds its sum), mirror within eight lanes, mirror within
+// sixteen. The additions pair up as in a butterfly, so every lane of the row ends
+// with the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float s) {
+    return s + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), CTRL,
+                                                                  0xF, 0xF, false));
+}
+template <int WIDTH>
+__device__ __forceinline__ float row_sum(float s) {
+    static_assert(WIDTH == 8 || WIDTH == 16, "rows of 8 or 16 lanes");
+    s = dpp_add<0xB1>(s);    // quad_perm [1,0,3,2]
+    s = dpp_add<0x4E>(s);    // quad_perm [2,3,0,1]
+    s = dpp_add<0x141>(s);   // row_half_mirror
+    if (WIDTH == 16) s = dpp_add<0x140>(s);   // row_mirror
+    return s;
+}
+
 // ---------------------------------------------------------------------------
 // Prologue. Grid (ceil(T / (GROUPS*RUN)), 2*Hk + Hv, B), 256 threads. Block y
 // picks one head-sized channel segment (q head, k head or v head); D/8 lanes
