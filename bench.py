@@ -765,20 +765,26 @@ def run_layer(torch, dn, synthetic, to_dev, dev):
         o.normal_()
         timed(tag + "_epilogue", epilogue, 3 * B * T * Hv * d * 2 + d * 2, tok)
         S = torch.zeros(B, Hv, d, d, dtype=torch.float32, device=dev)
+        # the rule is likewise checked once through the binding and then timed as
+        # a bare C-ABI call, so that the layer's figure is the GPU's time and not
+        # the host's (three binding calls per layer at decode size outlast it)
         if T == 1:
-            def layer():
-                prologue()
-                dn.decode_step_gqa(q[:, :, 0], k[:, :, 0], v[:, :, 0], beta[:, :, 0], g[:, :, 0],
-                                   S, o=o[:, :, 0])
-                epilogue()
+            dn.decode_step_gqa(q[:, :, 0], k[:, :, 0], v[:, :, 0], beta[:, :, 0], g[:, :, 0], S,
+                               o=o[:, :, 0])
+            rule_args = (0, P(q), P(k), P(v), P(beta), P(g), P(S), P(o), B, Hk, Hv, d, d, 1, st)
+            rule = lambda: lib.dn_decode_step_gqa(*rule_args)   # noqa: E731
         else:
             ws = torch.empty(dn.workspace_bytes(B, Hv, T, d, d, torch.bfloat16), dtype=torch.uint8,
                              device=dev)
+            dn.chunk_fwd_gqa(q, k, v, beta, g, None, o=o, S_final=S, workspace=ws)
+            rule_args = (0, P(q), P(k), P(v), P(beta), P(g), None, P(o), P(S), B, Hk, Hv, T, d, d, 1,
+                         P(ws), ws.numel(), st)
+            rule = lambda: lib.dn_chunk_fwd_gqa(*rule_args)   # noqa: E731
 
-            def layer():
-                prologue()
-                dn.chunk_fwd_gqa(q, k, v, beta, g, None, o=o, S_final=S, workspace=ws)
-                epilogue()
+        def layer():
+            prologue()
+            assert rule() == 0
+            epilogue()
         timed(tag + "_layer", layer, 0, tok)
         out[tag + "_layer"]["shape"] = {"B": B, "T": T, "key_heads": Hk, "value_heads": Hv, "d": d}
         del x, q, k, v, beta, g, cst, o, y, S
