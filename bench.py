@@ -787,6 +787,25 @@ def run_layer(torch, dn, synthetic, to_dev, dev):
             epilogue()
         timed(tag + "_layer", layer, 0, tok)
         out[tag + "_layer"]["shape"] = {"B": B, "T": T, "key_heads": Hk, "value_heads": Hv, "d": d}
+        if T == 1:
+            # the same layer step as one kernel (dn_layer_decode_step): checked
+            # once through the binding, then timed as a bare C-ABI call
+            cst2 = torch.empty_like(cst)
+            dn.layer_decode_step(x["qkv"], x["z"], x["b"], x["a"], x["conv_w"], x["A_log"],
+                                 x["dt_bias"], x["norm_w"], Hk, Hv, S, conv_state=x["conv_state"],
+                                 conv_state_out=cst2, out=y)
+            fused_args = (P(x["qkv"]), P(x["conv_w"]), P(x["conv_state"]), P(cst2), P(x["b"]),
+                          P(x["a"]), P(x["A_log"]), P(x["dt_bias"]), P(x["z"]), P(x["norm_w"]), 1e-6,
+                          P(S), P(y), 0, B, Hk, Hv, d, 1, st)
+            fused = lambda: lib.dn_layer_decode_step(*fused_args)   # noqa: E731
+            fused_bytes = (2 * B * Hv * d * d * 4 + pro_bytes - (2 * B * Hk + B * Hv) * d * 2
+                           - 2 * B * Hv * 2 + 2 * B * Hv * d * 2)
+            timed(tag + "_layer_one_kernel", lambda: fused() == 0 or None, fused_bytes, tok)
+            out[tag + "_layer_one_kernel"]["what"] = (
+                "dn_layer_decode_step: prologue, decode step and gated RMSNorm in one kernel; "
+                "bytes: the state read and written once, qkv, b, a, z, conv_w, norm_w read, the "
+                "two conv histories, out written")
+            del cst2
         del x, q, k, v, beta, g, cst, o, y, S
     return out
 

@@ -449,6 +449,53 @@ def layer_epilogue(o, z, norm_w, eps=1e-6, *, out=None, stream=None):
     return out
 
 
+def layer_decode_step(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, S, *, conv_state=None,
+                      conv_state_out=None, eps=1e-6, allow_neg_eigval=False, out=None,
+                      stream=None):
+    """The whole gated layer for one token per sequence in one kernel:
+    prologue, decode step (S [B,Hv,d,d] fp32 updated in place) and epilogue.
+
+    qkv [B,1,C], z [B,1,Hv*d], b, a [B,1,Hv] (a, A_log, dt_bias None: no decay
+    gate); conv_state [B,C,3] or None (zeros). The new convolution state goes
+    to conv_state_out (default: a new tensor; conv_state itself is allowed when
+    Hk == Hv). Returns (out [B,1,Hv*d], new conv state).
+    """
+    if qkv.dim() != 3 or qkv.shape[1] != 1:
+        raise ValueError("qkv must be [B,1,C]")
+    B, _, C = qkv.shape
+    dev, dt = qkv.device, qkv.dtype
+    if dt not in _DT:
+        raise TypeError("qkv must be bfloat16 or float32")
+    if Hk < 1 or Hv < 1 or C % (2 * Hk + Hv):
+        raise ValueError("C = %d is not (2*Hk + Hv) * d for Hk=%d, Hv=%d" % (C, Hk, Hv))
+    d = C // (2 * Hk + Hv)
+    _check_tensor("conv_w", conv_w, (C, 4), dt, dev)
+    _check_tensor("b", b, (B, 1, Hv), dt, dev)
+    if a is not None:
+        _check_tensor("a", a, (B, 1, Hv), dt, dev)
+        _check_tensor("A_log", A_log, (Hv,), torch.float32, dev)
+        _check_tensor("dt_bias", dt_bias, (Hv,), torch.float32, dev)
+    _check_tensor("z", z, (B, 1, Hv * d), dt, dev)
+    _check_tensor("norm_w", norm_w, (d,), dt, dev)
+    _check_tensor("S", S, (B, Hv, d, d), torch.float32, dev)
+    if conv_state is not None:
+        _check_tensor("conv_state", conv_state, (B, C, 3), dt, dev)
+    if conv_state_out is None:
+        conv_state_out = torch.empty(B, C, 3, dtype=dt, device=dev)
+    else:
+        _check_tensor("conv_state_out", conv_state_out, (B, C, 3), dt, dev)
+    if out is None:
+        out = torch.empty(B, 1, Hv * d, dtype=dt, device=dev)
+    else:
+        _check_tensor("out", out, (B, 1, Hv * d), dt, dev)
+    st = lib().dn_layer_decode_step(_ptr(qkv), _ptr(conv_w), _ptr(conv_state), _ptr(conv_state_out),
+                                    _ptr(b), _ptr(a), _ptr(A_log), _ptr(dt_bias), _ptr(z),
+                                    _ptr(norm_w), float(eps), _ptr(S), _ptr(out),
+                                    int(bool(allow_neg_eigval)), B, Hk, Hv, d, _DT[dt], _stream(stream))
+    _lib.check("dn_layer_decode_step", st)
+    return out, conv_state_out
+
+
 def gated_deltanet_layer(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *,
                          conv_state=None, S=None, eps=1e-6, allow_neg_eigval=False,
                          workspace=None, stream=None):
@@ -459,21 +506,20 @@ def gated_deltanet_layer(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *
     stay with the caller: qkv, z, b, a are their outputs.
 
     S [B,Hv,d,d] fp32 (or None: zeros) is the carried recurrent state; it is
-    updated in place when given. Returns (out [B,T,Hv*d], new conv state,
+    updated in place when given. One token with a carried state runs as the
+    single-kernel layer step (layer_decode_step). Returns (out [B,T,Hv*d], new conv state,
     new recurrent state).
     """
+    if qkv.dim() == 3 and qkv.shape[1] == 1 and S is not None:
+        # one token with a carried state: the single-kernel layer step
+        out, cst = layer_decode_step(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, S,
+                                     conv_state=conv_state, eps=eps,
+                                     allow_neg_eigval=allow_neg_eigval, stream=stream)
+        return out, cst, S
     q, k, v, beta, g, cst = layer_prologue(qkv, conv_w, b, a, A_log, dt_bias, Hk, Hv,
                                            conv_state=conv_state,
                                            allow_neg_eigval=allow_neg_eigval, stream=stream)
-    B, _, T, d = q.shape
-    if T == 1 and S is not None:
-        o = decode_step_gqa(q[:, :, 0], k[:, :, 0], v[:, :, 0], beta[:, :, 0],
-                            None if g is None else g[:, :, 0], S, stream=stream)
-        o = o.unsqueeze(2)
-        S_new = S
-    else:
-        o, S_new = chunk_fwd_gqa(q, k, v, beta, g, S, S_final=S, workspace=workspace,
-                                 stream=stream)
+    o, S_new = chunk_fwd_gqa(q, k, v, beta, g, S, S_final=S, workspace=workspace, stream=stream)
     return layer_epilogue(o, z, norm_w, eps, stream=stream), cst, S_new
 
 

@@ -391,6 +391,37 @@ int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* ou
                                                 as_stream(stream)));
 }
 
+int dn_layer_decode_step(const void* qkv, const void* conv_w, const void* conv_state,
+                         void* conv_state_out, const void* b, const void* a, const float* A_log,
+                         const float* dt_bias, const void* z, const void* norm_w, float eps, float* S,
+                         void* out, int allow_neg_eigval, int B, int Hk, int Hv, int d, int dtype,
+                         void* stream) {
+    if (B < 1 || Hk < 1 || Hv < 1 || Hv % Hk != 0 || !(eps >= 0.0f && eps < 3.0e38f)) return DN_EINVAL;
+    if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+    if ((long long)B * Hv > 0x7fffffffLL) return DN_EINVAL;
+    if (!qkv || !conv_w || !b || !z || !norm_w || !S || !out) return DN_EINVAL;
+    if (a && (!A_log || !dt_bias)) return DN_EINVAL;
+    const unsigned esz = dtype == DN_F32 ? 4u : 2u;
+    if (misaligned(qkv) || misaligned(conv_w) || misaligned(conv_state) || misaligned(conv_state_out) ||
+        misaligned(z) || misaligned(norm_w) || misaligned(S) || misaligned(out) || misaligned(b, esz) ||
+        misaligned(a, esz) || misaligned(A_log, 4) || misaligned(dt_bias, 4))
+        return DN_EINVAL;
+    if (d != 64 && d != 128) return DN_ENOTSUP;
+    // the new convolution history in place only where no other workgroup
+    // reads a channel's old entries (one value head per key head); otherwise
+    // the two histories must not overlap at all
+    if (conv_state && conv_state_out && conv_state != conv_state_out) {
+        const long long bytes = (long long)B * (2LL * Hk + Hv) * d * 3 * esz;
+        const char* x0 = static_cast<const char*>(conv_state);
+        const char* y0 = static_cast<const char*>(conv_state_out);
+        if (x0 < y0 + bytes && y0 < x0 + bytes) return DN_EINVAL;
+    }
+    if (conv_state && conv_state == conv_state_out && Hk != Hv) return DN_EINVAL;
+    return hip_status(dn::launch_layer_decode(dtype, qkv, conv_w, conv_state, conv_state_out, b, a, A_log,
+                                              dt_bias, z, norm_w, eps, S, out, allow_neg_eigval ? 2.0f : 1.0f,
+                                              B, Hk, Hv, d, as_stream(stream)));
+}
+
 int dn_ssm_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                      const float* S0, void* o, float* S_final, int B, int H, int T, int dk, int dv,
                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {

@@ -121,6 +121,16 @@ hipError_t launch_layer_epilogue(int dtype, const void* o, const void* z, const 
                                  void* out, int B, int Hv, int T, int d, float eps,
                                  hipStream_t st);
 
+// The whole layer for one token per sequence in one kernel (one workgroup per
+// (sequence, value head)): the prologue's steps in the load stage, the decode
+// step on S [B][Hv][d][d] in place, the gated RMSNorm in the store stage;
+// a == NULL: no decay gate (DeltaNet). conv_state_out may alias conv_state
+// only when Hk == Hv.
+hipError_t launch_layer_decode(int dtype, const void* qkv, const void* conv_w, const void* conv_state,
+                               void* conv_state_out, const void* b, const void* a, const float* A_log,
+                               const float* dt_bias, const void* z, const void* norm_w, float eps, float* S,
+                               void* out, float beta_scale, int B, int Hk, int Hv, int d, hipStream_t st);
+
 // Generalized delta rule, token by token: S = (diag(exp g) - (a * kr) kr^T) S
 // + kw v^T, o = S^T q; q, kw, kr, a, g [BH][T][d], v, o [BH][T][d]. S0 and
 // S_final may be the same buffer (the decode step is T = 1 in place).

@@ -394,6 +394,210 @@ __global__ __launch_bounds__(LAYER_WG) void layer_prologue_step_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The whole layer for one token (decode) in one kernel: the prologue in the
+// rule's load stage, the gated RMSNorm in its store stage (page "28. Linear
+// attention and Gated DeltaNet", section "The full layer", steps 2-7, with the
+// recurrent step of section "The recurrent form"). One 256-thread workgroup
+// per (sequence b, value head h) holds the whole D x D state of its head, so
+// the RMS over the head's D read-out columns needs no exchange between
+// workgroups (splitting a state over four workgroups, as the decode step
+// does, needs such an exchange: through agent-coherent stores, loads and an
+// arrival count it made the step slower, not faster).
+//  * Load stage. Wavefront 0 requests the token's inputs first, then every
+//    thread its share of the state (thread t: column quad t % (D/4), rows
+//    t / (D/4) + RG i); loads complete in order, so wavefront 0 forms q, k
+//    (key head h / (Hv/Hk)) and v while the state is in flight, exactly as
+//    the single-token prologue does: D/8 lanes per segment, eight channels
+//    each, the convolution with the carried history, SiLU, the L2 norms as
+//    lane sums (q also scaled by D^-1/2), each rounded to the storage type;
+//    one lane forms beta and g. They go to LDS for the whole workgroup.
+//  * The rule: S~ = alpha S, p = S~^T k, u = beta (v - p), S = S~ + k u^T,
+//    o = S^T q = S~^T q + u (k . q), as in the decode step (the state is read
+//    and written once).
+//  * Store stage. The threads of row group 0 hold o for their column quads;
+//    o is rounded to the storage type (as the rule's output would be), its
+//    RMS over the D columns is a lane sum over those threads, and
+//    out = w * round(o * rsqrt(mean(o^2) + eps)) * SiLU(z).
+// The new convolution history of this token goes to cout: v channels by every
+// workgroup, the q and k channels of a key head by the first value head of
+// its group only (one writer per channel). Every lane reads its own entries
+// before writing them, so cout may be cstate itself when each key head serves
+// one value head (with shared key heads other workgroups still read them).
+// ---------------------------------------------------------------------------
+template <typename E, int D, bool GATED>
+__global__ __launch_bounds__(LAYER_WG) void layer_decode_kernel(
+    const E* __restrict__ qkv, const E* __restrict__ conv_w, const E* cstate, E* cout,
+    const E* __restrict__ bin, const E* __restrict__ ain, const float* __restrict__ A_log,
+    const float* __restrict__ dt_bias, const E* __restrict__ z, const E* __restrict__ nw,
+    float* __restrict__ S, E* __restrict__ out, float bscale, float eps, int Hk, int Hv) {
+    constexpr int LPR = D / 8;            // lanes per channel segment
+    constexpr int CQ = D / 4;             // column quads per state row
+    constexpr int RG = LAYER_WG / CQ;     // row groups
+    constexpr int RPT = D / RG;           // rows per thread
+    constexpr float QSCALE = D == 64 ? 0.125f : 0.08838834764831845f;   // D^-1/2
+    static_assert(D % RG == 0 && CQ <= WAVE && 3 * LPR < WAVE, "unsupported head size");
+    typedef typename Vec4<E>::type V4;
+
+    const long bh = blockIdx.x;
+    const long b = bh / Hv;
+    const int h = (int)(bh % Hv);
+    const int grp = Hv / Hk, hk = h / grp;
+    const int t = threadIdx.x, lane = t & (WAVE - 1), w = t / WAVE;
+    const int cq = t % CQ, rg = t / CQ;
+    const long C = (long)(2 * Hk + Hv) * D;
+
+    const int seg = lane / LPR, l = lane % LPR;   // wavefront 0: 0 q, 1 k, 2 v
+    const bool pro = w == 0 && seg < 3;
+    const long c = (seg < 2 ? (long)(seg * Hk + hk) * D : (long)(2 * Hk + h) * D) + l * 8;
+    const long so = (b * C + c) * 3;   // this lane's 24 history entries, channel-major
+    Raw8<E> xr, w0, w1, w2, w3, h0, h1, h2;
+    if (pro) {
+        load_raw(qkv + b * C + c, xr);
+        load_raw(conv_w + c * CONV_K, w0);
+        load_raw(conv_w + c * CONV_K + 8, w1);
+        load_raw(conv_w + c * CONV_K + 16, w2);
+        load_raw(conv_w + c * CONV_K + 24, w3);
+        if (cstate) {
+            load_raw(cstate + so, h0);
+            load_raw(cstate + so + 8, h1);
+            load_raw(cstate + so + 16, h2);
+        }
+    }
+    const bool gl = w == 0 && lane == WAVE - 1;   // the lane that forms the gates
+    float bin_v = 0.f, ain_v = 0.f, alog_v = 0.f;
+    if (gl) {
+        bin_v = to_f32(bin[b * Hv + h]);
+        if (GATED) {
+            ain_v = to_f32(ain[b * Hv + h]) + dt_bias[h];
+            alog_v = A_log[h];
+        }
+    }
+    // the store stage's z and norm weights (row group 0: lanes 0 .. CQ-1 of
+    // wavefront 0)
+    const long oc = (b * Hv + h) * D + 4 * cq;   // [B][Hv*D]: the same as [B][1][Hv*D]
+    V4 zv, wv;
+    if (rg == 0) {
+        zv = *reinterpret_cast<const V4*>(z + oc);
+        wv = *reinterpret_cast<const V4*>(nw + 4 * cq);
+    }
+
+    float* Sp = S + bh * D * D + 4 * cq;
+    f32x4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const f32x4*>(Sp + (rg + RG * i) * D);
+
+    __shared__ float sq[D], sk[D], sv[D], sgate[2];
+    __shared__ f32x4 red_p[4][CQ], red_r[4][CQ];
+    __shared__ float red_kq[4];
+
+    if (pro) {
+        float y[8], ss = 0.0f, hist[24];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            hist[i] = cstate ? elem(h0, i) : 0.0f;
+            hist[8 + i] = cstate ? elem(h1, i) : 0.0f;
+            hist[16 + i] = cstate ? elem(h2, i) : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const Raw8<E>& wr = i < 2 ? w0 : i < 4 ? w1 : i < 6 ? w2 : w3;
+            const int o = (i % 2) * 4;
+            const float xi = elem(xr, i);
+            const float acc = elem(wr, o) * hist[3 * i] + elem(wr, o + 1) * hist[3 * i + 1] +
+                              elem(wr, o + 2) * hist[3 * i + 2] + elem(wr, o + 3) * xi;
+            y[i] = silu(acc);
+            ss += y[i] * y[i];
+        }
+        if (cout && (seg == 2 || h % grp == 0)) {
+            float nh[24];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                nh[3 * i] = hist[3 * i + 1];
+                nh[3 * i + 1] = hist[3 * i + 2];
+                nh[3 * i + 2] = elem(xr, i);
+            }
+            store8(cout + so, *reinterpret_cast<const float(*)[8]>(nh));
+            store8(cout + so + 8, *reinterpret_cast<const float(*)[8]>(nh + 8));
+            store8(cout + so + 16, *reinterpret_cast<const float(*)[8]>(nh + 16));
+        }
+        // the lane sum runs in every lane of the segment (rows of LPR lanes)
+        const float tot = row_sum<LPR>(ss);
+        const float sc = seg == 0 ? QSCALE * inv_norm(tot) : seg == 1 ? inv_norm(tot) : 1.0f;
+        float* dst = seg == 0 ? sq : seg == 1 ? sk : sv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dst[l * 8 + i] = to_f32(from_f32<E>(y[i] * sc));
+    } else if (gl) {
+        sgate[0] = to_f32(from_f32<E>(bscale / (1.0f + __expf(-bin_v))));
+        if (GATED)
+            sgate[1] = to_f32(from_f32<E>(-__expf(alog_v) * (fmaxf(ain_v, 0.0f) + log1pf(__expf(-fabsf(ain_v))))));
+    }
+    __syncthreads();
+
+    const float beta = sgate[0];
+    const float alpha = GATED ? __expf(sgate[1]) : 1.0f;
+    f32x4 p = zero4(), r = zero4();
+    float kq = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        if (GATED) s[i] *= alpha;
+        p += sk[row] * s[i];
+        r += sq[row] * s[i];
+        kq += sk[row] * sq[row];
+    }
+    // row groups inside one wavefront differ in lane bits >= log2(CQ)
+#pragma unroll
+    for (int off = CQ; off < WAVE; off <<= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            p[e] += __shfl_xor(p[e], off, WAVE);
+            r[e] += __shfl_xor(r[e], off, WAVE);
+        }
+        kq += __shfl_xor(kq, off, WAVE);
+    }
+    if (lane < CQ) {
+        red_p[w][lane] = p;
+        red_r[w][lane] = r;
+    }
+    if (lane == 0) red_kq[w] = kq;
+    __syncthreads();
+    p = red_p[0][cq] + red_p[1][cq] + red_p[2][cq] + red_p[3][cq];
+    r = red_r[0][cq] + red_r[1][cq] + red_r[2][cq] + red_r[3][cq];
+    kq = red_kq[0] + red_kq[1] + red_kq[2] + red_kq[3];
+
+    f32x4 u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = beta * (sv[4 * cq + e] - p[e]);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int row = rg + RG * i;
+        s[i] += sk[row] * u;
+        *reinterpret_cast<f32x4*>(Sp + row * D) = s[i];
+    }
+    if (rg == 0) {
+        // row group 0 is lanes 0 .. CQ-1 of wavefront 0: the read-out of the
+        // head's D columns, four per lane
+        const f32x4 ov = r + u * kq;
+        float on[4], ss = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            on[e] = to_f32(from_f32<E>(ov[e]));
+            ss += on[e] * on[e];
+        }
+#pragma unroll
+        for (int off = 1; off < CQ; off <<= 1) ss += __shfl_xor(ss, off, CQ);
+        const float rr = rsqrtf(ss * (1.0f / D) + eps);
+        V4 res;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float nrm = to_f32(from_f32<E>(on[e] * rr));
+            res[e] = from_f32<E>(to_f32(wv[e]) * nrm * silu(to_f32(zv[e])));
+        }
+        *reinterpret_cast<V4*>(out + oc) = res;
+    }
+}
+
 // New convolution state for an empty input (T == 0: the old state, or zeros),
 // [B][C][3]; written the same way for any T. One thread per (sequence,
 // channel); it reads everything it needs before writing, so the new state may
@@ -513,6 +717,26 @@ hipError_t epilogue_launch(const void* o, const void* z, const void* w, void* ou
     return hipGetLastError();
 }
 
+template <typename E, int D>
+hipError_t decode_layer_launch(const void* qkv, const void* conv_w, const void* cstate, void* cout,
+                               const void* b, const void* a, const float* A_log, const float* dt_bias,
+                               const void* z, const void* nw, float* S, void* out, float bs, float eps,
+                               int B, int Hk, int Hv, hipStream_t st) {
+    const unsigned grid = (unsigned)((long)B * Hv);
+    if (a) {
+        layer_decode_kernel<E, D, true><<<grid, LAYER_WG, 0, st>>>(
+            static_cast<const E*>(qkv), static_cast<const E*>(conv_w), static_cast<const E*>(cstate),
+            static_cast<E*>(cout), static_cast<const E*>(b), static_cast<const E*>(a), A_log, dt_bias,
+            static_cast<const E*>(z), static_cast<const E*>(nw), S, static_cast<E*>(out), bs, eps, Hk, Hv);
+    } else {
+        layer_decode_kernel<E, D, false><<<grid, LAYER_WG, 0, st>>>(
+            static_cast<const E*>(qkv), static_cast<const E*>(conv_w), static_cast<const E*>(cstate),
+            static_cast<E*>(cout), static_cast<const E*>(b), nullptr, nullptr, nullptr,
+            static_cast<const E*>(z), static_cast<const E*>(nw), S, static_cast<E*>(out), bs, eps, Hk, Hv);
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_layer_prologue(int dtype, const void* qkv, const void* conv_w,
@@ -541,6 +765,22 @@ hipError_t launch_layer_epilogue(int dtype, const void* o, const void* z, const 
     }
     return d == 64 ? epilogue_launch<float, 64>(o, z, norm_w, out, B, Hv, T, eps, st)
                    : epilogue_launch<float, 128>(o, z, norm_w, out, B, Hv, T, eps, st);
+}
+
+hipError_t launch_layer_decode(int dtype, const void* qkv, const void* conv_w, const void* conv_state,
+                               void* conv_state_out, const void* b, const void* a, const float* A_log,
+                               const float* dt_bias, const void* z, const void* norm_w, float eps, float* S,
+                               void* out, float bs, int B, int Hk, int Hv, int d, hipStream_t st) {
+    if (dtype == DT_BF16) {
+        return d == 64 ? decode_layer_launch<bf16, 64>(qkv, conv_w, conv_state, conv_state_out, b, a, A_log,
+                                                       dt_bias, z, norm_w, S, out, bs, eps, B, Hk, Hv, st)
+                       : decode_layer_launch<bf16, 128>(qkv, conv_w, conv_state, conv_state_out, b, a, A_log,
+                                                        dt_bias, z, norm_w, S, out, bs, eps, B, Hk, Hv, st);
+    }
+    return d == 64 ? decode_layer_launch<float, 64>(qkv, conv_w, conv_state, conv_state_out, b, a, A_log,
+                                                    dt_bias, z, norm_w, S, out, bs, eps, B, Hk, Hv, st)
+                   : decode_layer_launch<float, 128>(qkv, conv_w, conv_state, conv_state_out, b, a, A_log,
+                                                     dt_bias, z, norm_w, S, out, bs, eps, B, Hk, Hv, st);
 }
 
 }  // namespace dn

@@ -408,6 +408,35 @@ int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* ou
                       int T, int dv, float eps, int dtype, void* stream);
 
 /*
+ * The whole gated layer between its projections for ONE token per sequence
+ * (decode), in a single kernel (page "28. Linear attention and Gated
+ * DeltaNet", section "The full layer", steps 2-7, around the recurrent step
+ * of section "The recurrent form"): exactly the work of dn_layer_prologue
+ * (T = 1), dn_decode_step_gqa and dn_layer_epilogue in order, with q, k, v,
+ * beta, g and o kept on chip. One workgroup per (sequence, value head).
+ *   qkv, b, a, conv_w, conv_state, conv_state_out, A_log, dt_bias, allow_neg_eigval
+ *               as in dn_layer_prologue with T = 1 (qkv [B,1,C], b and a
+ *               [B,1,Hv]); a == NULL selects no decay gate (DeltaNet; A_log
+ *               and dt_bias unused)
+ *   z, norm_w, eps, out  as in dn_layer_epilogue with T = 1 (z, out [B,1,Hv*d])
+ *   S           [B,Hv,d,d] fp32, the recurrent state, updated in place
+ * d = dk = dv in {64, 128} (DN_ENOTSUP otherwise); Hv a multiple of Hk. The
+ * intermediate values are those of the three separate calls: q, k, v, beta
+ * and g rounded to dtype, and o rounded to dtype before its norm (the
+ * reductions may add in another order: the results agree to rounding, not
+ * bit for bit). conv_state_out may be conv_state itself only when Hk == Hv
+ * (with shared key heads other workgroups still read a key head's history);
+ * any other overlap between the two is DN_EINVAL. The state must not overlap
+ * any other argument. Alignment: qkv, conv_w, the conv states, z, norm_w, S,
+ * out 16 bytes; b, a element; A_log, dt_bias 4 bytes.
+ */
+int dn_layer_decode_step(const void* qkv, const void* conv_w, const void* conv_state,
+                         void* conv_state_out, const void* b, const void* a, const float* A_log,
+                         const float* dt_bias, const void* z, const void* norm_w, float eps, float* S,
+                         void* out, int allow_neg_eigval, int B, int Hk, int Hv, int d, int dtype,
+                         void* stream);
+
+/*
  * Selective state-space recurrence (decayed linear attention, the form behind
  * RetNet, GLA and Mamba-2): S_t = alpha_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t,
  * alpha_t = exp(g_t) with one log-decay per head and token. This is Gated

@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 31, names
+    assert len(names) == 32, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -347,6 +347,39 @@ def test_layer_epilogue_validation():
     assert _epilogue(eps=float("inf")) == E
     assert _epilogue(dtype=7) == E
     assert _epilogue(dv=96) == N
+
+
+def _layer_decode(**kw):
+    args = dict(qkv=P, conv_w=P, conv_state=P, conv_state_out=P + 0x100000, b=P, a=P, A_log=P,
+                dt_bias=P, z=P, norm_w=P, eps=1e-6, S=P, out=P, neg=0, B=2, Hk=1, Hv=2, d=128,
+                dtype=1, stream=None)
+    args.update(kw)
+    return _lib.lib().dn_layer_decode_step(*[args[n] for n in (
+        "qkv", "conv_w", "conv_state", "conv_state_out", "b", "a", "A_log", "dt_bias", "z", "norm_w",
+        "eps", "S", "out", "neg", "B", "Hk", "Hv", "d", "dtype", "stream")])
+
+
+def test_layer_decode_validation():
+    E, N = _lib.DN_EINVAL, _lib.DN_ENOTSUP
+    assert _layer_decode(Hv=3, Hk=2) == E      # value heads not a multiple of key heads
+    assert _layer_decode(B=0) == E
+    assert _layer_decode(Hk=0) == E
+    assert _layer_decode(dtype=4) == E
+    assert _layer_decode(eps=-1.0) == E
+    assert _layer_decode(eps=float("nan")) == E
+    for name in ("qkv", "conv_w", "b", "z", "norm_w", "S", "out"):
+        assert _layer_decode(**{name: None}) == E, name
+    assert _layer_decode(A_log=None) == E      # a decay gate needs A_log and dt_bias
+    assert _layer_decode(dt_bias=None) == E
+    for name in ("qkv", "conv_w", "conv_state", "conv_state_out", "z", "norm_w", "S", "out"):
+        assert _layer_decode(**{name: MIS}) == E, name
+    assert _layer_decode(b=ODD) == E
+    assert _layer_decode(A_log=P + 2) == E
+    assert _layer_decode(d=96) == N
+    # the history in place only with one value head per key head; no partial overlap
+    assert _layer_decode(conv_state_out=P) == E
+    assert _layer_decode(conv_state_out=P + 16) == E
+    assert _layer_decode(Hk=2, Hv=2, conv_state_out=P + 16) == E
 
 
 def _ssm(fn, **kw):
