@@ -787,6 +787,24 @@ def run_layer(torch, dn, synthetic, to_dev, dev):
             epilogue()
         timed(tag + "_layer", layer, 0, tok)
         out[tag + "_layer"]["shape"] = {"B": B, "T": T, "key_heads": Hk, "value_heads": Hv, "d": d}
+        if T > 1:
+            # the same layer with the prologue inside the prefill's prep
+            # (dn_layer_prefill): checked once through the binding, then timed as
+            # a bare C-ABI call
+            lws = dn.layer_prefill_workspace(B, T, Hk, Hv, d, torch.bfloat16, dev)
+            cst3 = torch.empty_like(cst)
+            dn.layer_prefill(x["qkv"], x["z"], x["b"], x["a"], x["conv_w"], x["A_log"], x["dt_bias"],
+                             x["norm_w"], Hk, Hv, conv_state=x["conv_state"], conv_state_out=cst3,
+                             S_final=S, out=y, workspace=lws)
+            lp_args = (P(x["qkv"]), P(x["conv_w"]), P(x["conv_state"]), P(cst3), P(x["b"]), P(x["a"]),
+                       P(x["A_log"]), P(x["dt_bias"]), P(x["z"]), P(x["norm_w"]), 1e-6, None, P(S),
+                       P(y), 0, B, T, Hk, Hv, d, 1, P(lws), lws.numel(), st)
+            lp = lambda: lib.dn_layer_prefill(*lp_args)   # noqa: E731
+            timed(tag + "_layer_prologue_in_prep", lp, 0, tok)
+            out[tag + "_layer_prologue_in_prep"]["what"] = (
+                "dn_layer_prefill: the prologue formed in the prefill's prep (three launches: prep, "
+                "scan, epilogue); bitwise the result of the three separate calls")
+            del lws, cst3
         if T == 1:
             # the same layer step as one kernel (dn_layer_decode_step): checked
             # once through the binding, then timed as a bare C-ABI call

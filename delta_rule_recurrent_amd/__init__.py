@@ -496,6 +496,72 @@ def layer_decode_step(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, S, *
     return out, conv_state_out
 
 
+def layer_prefill_workspace(B, T, Hk, Hv, d, dtype, device):
+    """Workspace of layer_prefill (uninitialised device bytes)."""
+    n = lib().dn_layer_prefill_workspace(B, T, Hk, Hv, d, _DT[dtype])
+    if n == 0 and T > 0:
+        raise ValueError("layer_prefill supports bfloat16 with d = 128 only")
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def layer_prefill(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *, conv_state=None,
+                  conv_state_out=None, update_conv_state=True, S0=None, S_final=None, eps=1e-6,
+                  allow_neg_eigval=False, out=None, workspace=None, stream=None):
+    """The gated layer between its projections for a prefill (bf16, d = 128):
+    the prologue formed in the prefill's chunk-parallel phase, the scan, the
+    gated RMSNorm; bitwise the result of layer_prologue, chunk_fwd_gqa and
+    layer_epilogue.
+
+    qkv [B,T,C], z [B,T,Hv*d], b, a [B,T,Hv] (a, A_log, dt_bias None: no decay
+    gate); conv_state [B,C,3] or None (zeros); S0 [B,Hv,d,d] fp32 or None. The
+    new conv state goes to conv_state_out (default: a new tensor, or None when
+    update_conv_state is False; it must not overlap conv_state). Returns
+    (out [B,T,Hv*d], new conv state, S_final).
+    """
+    if qkv.dim() != 3:
+        raise ValueError("qkv must be [B,T,C]")
+    B, T, C = qkv.shape
+    dev, dt = qkv.device, qkv.dtype
+    if dt not in _DT:
+        raise TypeError("qkv must be bfloat16 or float32")
+    if Hk < 1 or Hv < 1 or C % (2 * Hk + Hv):
+        raise ValueError("C = %d is not (2*Hk + Hv) * d for Hk=%d, Hv=%d" % (C, Hk, Hv))
+    d = C // (2 * Hk + Hv)
+    _check_tensor("conv_w", conv_w, (C, 4), dt, dev)
+    _check_tensor("b", b, (B, T, Hv), dt, dev)
+    if a is not None:
+        _check_tensor("a", a, (B, T, Hv), dt, dev)
+        _check_tensor("A_log", A_log, (Hv,), torch.float32, dev)
+        _check_tensor("dt_bias", dt_bias, (Hv,), torch.float32, dev)
+    _check_tensor("z", z, (B, T, Hv * d), dt, dev)
+    _check_tensor("norm_w", norm_w, (d,), dt, dev)
+    if conv_state is not None:
+        _check_tensor("conv_state", conv_state, (B, C, 3), dt, dev)
+    if conv_state_out is None and update_conv_state:
+        conv_state_out = torch.empty(B, C, 3, dtype=dt, device=dev)
+    elif conv_state_out is not None:
+        _check_tensor("conv_state_out", conv_state_out, (B, C, 3), dt, dev)
+    if S0 is not None:
+        _check_tensor("S0", S0, (B, Hv, d, d), torch.float32, dev)
+    if S_final is None:
+        S_final = torch.empty(B, Hv, d, d, dtype=torch.float32, device=dev)
+    else:
+        _check_tensor("S_final", S_final, (B, Hv, d, d), torch.float32, dev)
+    if out is None:
+        out = torch.empty(B, T, Hv * d, dtype=dt, device=dev)
+    else:
+        _check_tensor("out", out, (B, T, Hv * d), dt, dev)
+    if workspace is None:
+        workspace = layer_prefill_workspace(B, T, Hk, Hv, d, dt, dev)
+    st = lib().dn_layer_prefill(_ptr(qkv), _ptr(conv_w), _ptr(conv_state), _ptr(conv_state_out),
+                                _ptr(b), _ptr(a), _ptr(A_log), _ptr(dt_bias), _ptr(z), _ptr(norm_w),
+                                float(eps), _ptr(S0), _ptr(S_final), _ptr(out),
+                                int(bool(allow_neg_eigval)), B, T, Hk, Hv, d, _DT[dt], _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check("dn_layer_prefill", st)
+    return out, conv_state_out, S_final
+
+
 def gated_deltanet_layer(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *,
                          conv_state=None, S=None, eps=1e-6, allow_neg_eigval=False,
                          workspace=None, stream=None):

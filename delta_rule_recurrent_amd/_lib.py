@@ -43,6 +43,8 @@ SIGNATURES = {
     "dn_ssm_decode_step": (_i, [_vp] * 6 + [_i] * 5 + [_vp]),
     "dn_layer_epilogue": (_i, [_vp] * 4 + [_i] * 4 + [ctypes.c_float, _i, _vp]),
     "dn_layer_decode_step": (_i, [_vp] * 10 + [ctypes.c_float, _vp, _vp] + [_i] * 6 + [_vp]),
+    "dn_layer_prefill_workspace": (_sz, [_i] * 6),
+    "dn_layer_prefill": (_i, [_vp] * 10 + [ctypes.c_float, _vp, _vp, _vp] + [_i] * 7 + [_vp, _sz, _vp]),
     "dn_gdr_recurrent_fwd": (_i, [_vp] * 9 + [_i] * 6 + [_vp]),
     "dn_gdr_decode_step": (_i, [_vp] * 8 + [_i] * 5 + [_vp]),
     "dn_gdr_chunk_workspace": (_sz, [_i] * 7),

@@ -422,6 +422,52 @@ int dn_layer_decode_step(const void* qkv, const void* conv_w, const void* conv_s
                                               B, Hk, Hv, d, as_stream(stream)));
 }
 
+size_t dn_layer_prefill_workspace(int B, int T, int Hk, int Hv, int d, int dtype) {
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || d != 128 || dtype != DN_BF16) return 0;
+    return dn::layer_prefill_workspace_bytes(B, T, Hk, Hv);
+}
+
+int dn_layer_prefill(const void* qkv, const void* conv_w, const void* conv_state, void* conv_state_out,
+                     const void* b, const void* a, const float* A_log, const float* dt_bias, const void* z,
+                     const void* norm_w, float eps, const float* S0, float* S_final, void* out,
+                     int allow_neg_eigval, int B, int T, int Hk, int Hv, int d, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+    if (B < 1 || T < 0 || Hk < 1 || Hv < 1 || Hv % Hk != 0 || !(eps >= 0.0f && eps < 3.0e38f)) return DN_EINVAL;
+    if (dtype != DN_F32 && dtype != DN_BF16) return DN_EINVAL;
+    if ((long long)B * Hv > (1 << 24) || (long long)B * Hv * ((T + 63) / 64) > 0x7fffffffLL) return DN_EINVAL;
+    if (!conv_w || !norm_w || !S_final) return DN_EINVAL;
+    if (T > 0 && (!qkv || !b || !z || !out)) return DN_EINVAL;
+    if (a && (!A_log || !dt_bias)) return DN_EINVAL;
+    const unsigned esz = dtype == DN_F32 ? 4u : 2u;
+    if (misaligned(qkv) || misaligned(conv_w) || misaligned(conv_state) || misaligned(conv_state_out) ||
+        misaligned(z) || misaligned(norm_w) || misaligned(out) || misaligned(S0) || misaligned(S_final) ||
+        misaligned(b, esz) || misaligned(a, esz) || misaligned(A_log, 4) || misaligned(dt_bias, 4))
+        return DN_EINVAL;
+    if (d != 128 || dtype != DN_BF16) return DN_ENOTSUP;
+    // the last chunk's items write the new history while the first chunk's read
+    // the old one: the two must not overlap at all
+    if (conv_state && conv_state_out) {
+        const long long bytes = (long long)B * (2LL * Hk + Hv) * d * 3 * esz;
+        const char* x0 = static_cast<const char*>(conv_state);
+        const char* y0 = static_cast<const char*>(conv_state_out);
+        if (x0 < y0 + bytes && y0 < x0 + bytes) return DN_EINVAL;
+    }
+    if (T == 0) {
+        // no token: the history passes through, the state is copied
+        const hipError_t e = dn::launch_layer_prologue(dtype, qkv, conv_w, conv_state, conv_state_out, b, nullptr,
+                                                       nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                       nullptr, 1.0f, B, 0, Hk, Hv, d, as_stream(stream));
+        if (e != hipSuccess) return hip_status(e);
+        return hip_status(dn::launch_state_copy(S0, S_final, (long long)B * Hv * d * d, as_stream(stream)));
+    }
+    if (!workspace || misaligned(workspace, 256) ||
+        workspace_bytes < dn::layer_prefill_workspace_bytes(B, T, Hk, Hv))
+        return DN_EWORKSPACE;
+    return hip_status(dn::launch_layer_prefill(qkv, conv_w, conv_state, conv_state_out, b, a, A_log, dt_bias, z,
+                                               norm_w, eps, S0, S_final, out, allow_neg_eigval ? 2.0f : 1.0f, B, T,
+                                               Hk, Hv, workspace, as_stream(stream)));
+}
+
 int dn_ssm_chunk_fwd(const void* q, const void* k, const void* v, const void* g,
                      const float* S0, void* o, float* S_final, int B, int H, int T, int dk, int dv,
                      int dtype, void* workspace, size_t workspace_bytes, void* stream) {

@@ -41,6 +41,7 @@
 #include "dn_launch.h"
 #include "dn_chunk.h"
 #include "dn_kda_prep.h"
+#include "dn_conv.h"
 
 namespace dn {
 
@@ -359,6 +360,27 @@ void chunk_prep_kernel(const E* __restrict__ q,
 //  * Each scaled T is rounded once to the operand type.
 
 
+// The gated layer's inputs for the prep that runs the layer's prologue in its
+// load stage (bf16, d = 128): the projected channel rows qkv [B][T][C] with
+// C = (2 Hk + Hv) 128 (q of the key heads, then k, then v of the value heads),
+// the filter taps [C][4], the carried history [B][C][3] (or null: zeros) and
+// its successor (written by the items of each sequence's last chunk; must not
+// overlap the old one), the gate inputs b, a [B][T][Hv] (a null: no decay),
+// and where the normalised, scaled q rows go for the scan ([B][Hk][T][128]).
+struct LayerIn {
+    const bf16* qkv;
+    const bf16* conv_w;
+    const bf16* cstate;
+    bf16* cout;
+    const bf16* bin;
+    const bf16* ain;
+    const float* A_log;
+    const float* dt_bias;
+    bf16* qhat;
+    float bscale;
+    int T, Hk, Hv;
+};
+
 template <typename E, int DK, int DV, int CH = CHUNK>
 struct Prep2Smem {
     static constexpr int LDF = CH + 4;                 // fp32 CH x CH: A, then T's diagonal blocks
@@ -411,12 +433,16 @@ struct Prep2Lds {
 // One (head bh, chunk c) item of CH tokens (32, 64 or 128) on two wavefronts
 // (w = 0, 1 of the unit), its results written to the workspace block `blk`.
 // Each of the two wavefronts passes exactly one workgroup barrier.
-template <typename E, int DK, int DV, int KIND, int CH = CHUNK>
+// LAYER: q, k, v, beta and g are not read; the item forms them from the
+// layer's inputs `li` for sequence lb, value head lh, tokens lt0 .. lt0+L-1
+// (section 1 below), exactly as the layer's prologue kernel would.
+template <typename E, int DK, int DV, int KIND, int CH = CHUNK, bool LAYER = false>
 __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __restrict__ k,
                                            const E* __restrict__ v, const E* __restrict__ beta,
                                            const E* __restrict__ g, char* __restrict__ blk,
                                            Prep2Lds<E, DK, DV, CH>& lds, long tok0, long tokk, int L,
-                                           int w, int lane) {
+                                           int w, int lane, const LayerIn& li = LayerIn{}, long lb = 0,
+                                           int lh = 0, long lt0 = 0) {
     typedef WsLayout<E, DK, DV, CH> Lw;
     typedef Prep2Smem<E, DK, DV, CH> Sm;
     typedef typename Frag<E>::type F;
@@ -451,28 +477,129 @@ __device__ __forceinline__ void prep2_item(const E* __restrict__ q, const E* __r
     //         key channels, in the 8-consecutive-channel order; both
     //         wavefronts), then (wavefront 1) Q and V in the same order
     E braw[TH], graw[TH];
-#pragma unroll
-    for (int h = 0; h < TH; ++h) {
-        const long tk = tok0 + min(64 * h + lane, L - 1);
-        braw[h] = KIND == KIND_SSM ? E{} : beta[tk];
-        graw[h] = (KIND == KIND_GATED || KIND == KIND_SSM) ? g[tk] : E{};
-    }
     F kf[NT][KB];
-#pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) kf[tt][kb] = frag_rows8_g<E>(k + tokk * DK, DK, 16 * tt, 32 * kb, lane, L);
     F qa[NT][KB], vf[NT][VB];
-    if (w == 1) {
+    if constexpr (LAYER) {
+        // ---- 1'. the layer's prologue in the load stage. Wavefront 0 forms the
+        //          64 k rows (its key head), wavefront 1 the v rows (its value
+        //          head), four lane groups x two runs of eight tokens each, into
+        //          the two LDS regions that A and V's fragments use later; after
+        //          a barrier both read their fragments (same order as the global
+        //          loads below), and after a second one wavefront 1 forms the q
+        //          rows over V's region (and stores them for the scan) while
+        //          wavefront 0 starts on A. The gates are formed per token.
+        static_assert(sizeof(E) == 2 && DK == 128 && DV == 128 && CH == 64,
+                      "the layer prep is built for bf16, d = 128, chunks of 64");
+        constexpr int LDK = DK + 8;   // padded k rows in the A region
+        constexpr float QSCALE = 0.08838834764831845f;   // 128^-1/2
+        const long C = (long)(2 * li.Hk + li.Hv) * DK;
+        const int grpv = li.Hv / li.Hk, hk = lh / grpv;
+        const long T = li.T;
+        const bf16* xs0 = li.qkv + lb * T * C;   // the sequence's token 0
+        const int lg = lane >> 4, l16 = lane & 15;
+        {
+            const long gi = (lb * T + lt0 + min(lane, L - 1)) * li.Hv + lh;
+            braw[0] = from_f32<E>(li.bscale / (1.0f + __expf(-to_f32(li.bin[gi]))));
+            graw[0] = E{};
+            if (KIND == KIND_GATED) {
+                const float zz = to_f32(li.ain[gi]) + li.dt_bias[lh];
+                graw[0] = from_f32<E>(-__expf(li.A_log[lh]) * (fmaxf(zz, 0.0f) + log1pf(__expf(-fabsf(zz)))));
+            }
+        }
+        E* ktile = reinterpret_cast<E*>(smem);                 // k rows over A's region
+        E* vtile = reinterpret_cast<E*>(smem + Sm::AT_BYTES);  // v, then q rows over V's region
+        const bf16* cst0 = li.cstate ? li.cstate + lb * C * 3 : nullptr;
+        {
+            const long cs = (w == 0 ? (long)(li.Hk + hk) * DK : (long)(2 * li.Hk + lh) * DK) + 8 * l16;
+            E* tile = w == 0 ? ktile : vtile;
+            const int ldt = w == 0 ? LDK : DV;
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                const int r0 = 16 * lg + 8 * run;
+                prologue_run8<DK>(xs0 + cs, C, T, lt0 + r0, li.conv_w + cs * 4, cst0 ? cst0 + cs * 3 : nullptr,
+                                  w == 0, 1.0f, tile + r0 * ldt + 8 * l16, ldt, nullptr);
+            }
+        }
+        // the sequence's last chunk: the new history (the last three inputs of
+        // each channel) of this head's v channels, and of its key head's q and k
+        // channels from the first value head of the key head's group
+        if (li.cout && lt0 + CH >= T) {
+            const int seg = w == 0 ? (lg == 1 ? 0 : lg == 2 ? 1 : -1) : (lg == 1 ? 2 : -1);
+            if (seg >= 0 && (seg == 2 || lh % grpv == 0)) {
+                const long cs = (seg < 2 ? (long)(seg * li.Hk + hk) * DK : (long)(2 * li.Hk + lh) * DK) + 8 * l16;
+                float nh[24];
+#pragma unroll
+                for (int j = 0; j < 3; ++j) {
+                    const long tt = T - 3 + j;
+                    float rv[8];
+                    if (tt >= 0) {
+                        load8(xs0 + tt * C + cs, rv);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) rv[i] = cst0 ? to_f32(cst0[(cs + i) * 3 + 3 + tt]) : 0.0f;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) nh[3 * i + j] = rv[i];
+                }
+                bf16* co = li.cout + (lb * C + cs) * 3;
+                store8(co, *reinterpret_cast<const float(*)[8]>(nh));
+                store8(co + 8, *reinterpret_cast<const float(*)[8]>(nh + 8));
+                store8(co + 16, *reinterpret_cast<const float(*)[8]>(nh + 16));
+            }
+        }
+        lds_barrier();   // the k and v rows are in LDS
 #pragma unroll
         for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) qa[tt][kb] = frag_rows8_g<E>(q + tokk * DK, DK, 16 * tt, 32 * kb, lane, L);
-        if (!LATE_V) {
+            for (int kb = 0; kb < KB; ++kb)
+                kf[tt][kb] = *reinterpret_cast<const F*>(ktile + (16 * tt + n) * LDK + 32 * kb + 8 * gq);
+        if (w == 1) {
 #pragma unroll
             for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-                for (int kb = 0; kb < VB; ++kb) vf[tt][kb] = frag_rows8_g<E>(v + tok0 * DV, DV, 16 * tt, 32 * kb, lane, L);
+                for (int kb = 0; kb < VB; ++kb)
+                    vf[tt][kb] = *reinterpret_cast<const F*>(vtile + (16 * tt + n) * DV + 32 * kb + 8 * gq);
+        }
+        lds_barrier();   // both wavefronts have their fragments: the regions are free
+        if (w == 1) {
+            const long cs = (long)hk * DK + 8 * l16;
+            bf16* qdst = lh % grpv == 0 ? li.qhat + ((lb * li.Hk + hk) * T + lt0) * DK + 8 * l16 : nullptr;
+#pragma unroll
+            for (int run = 0; run < 2; ++run) {
+                const int r0 = 16 * lg + 8 * run;
+                prologue_run8<DK>(xs0 + cs, C, T, lt0 + r0, li.conv_w + cs * 4, cst0 ? cst0 + cs * 3 : nullptr,
+                                  true, QSCALE, vtile + r0 * DV + 8 * l16, DV, qdst ? qdst + r0 * DK : nullptr);
+            }
+            lds_fence();
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+                    qa[tt][kb] = *reinterpret_cast<const F*>(vtile + (16 * tt + n) * DV + 32 * kb + 8 * gq);
+            lds_fence();   // read before V's fragments go over them
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < TH; ++h) {
+            const long tk = tok0 + min(64 * h + lane, L - 1);
+            braw[h] = KIND == KIND_SSM ? E{} : beta[tk];
+            graw[h] = (KIND == KIND_GATED || KIND == KIND_SSM) ? g[tk] : E{};
+        }
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb) kf[tt][kb] = frag_rows8_g<E>(k + tokk * DK, DK, 16 * tt, 32 * kb, lane, L);
+        if (w == 1) {
+#pragma unroll
+            for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb) qa[tt][kb] = frag_rows8_g<E>(q + tokk * DK, DK, 16 * tt, 32 * kb, lane, L);
+            if (!LATE_V) {
+#pragma unroll
+                for (int tt = 0; tt < NT; ++tt)
+#pragma unroll
+                    for (int kb = 0; kb < VB; ++kb) vf[tt][kb] = frag_rows8_g<E>(v + tok0 * DV, DV, 16 * tt, 32 * kb, lane, L);
+            }
         }
     }
 
@@ -709,6 +836,23 @@ __global__ __launch_bounds__(128, CH > 64 ? 1 : 2) void chunk_prep2_kernel(const
     prep2_item<E, DK, DV, KIND, CH>(q, k, v, beta, g, ws + item * WsLayout<E, DK, DV, CH>::BYTES, lds,
                                     bh * T + t0, hm.key(bh) * T + t0, min(CH, T - t0),
                                     (int)(threadIdx.x >> 6), (int)(threadIdx.x & 63));
+}
+
+// The prep of the gated layer's prefill: one item per (head row, chunk) as
+// chunk_prep2_kernel, the layer's prologue formed in the item's load stage
+// (prep2_item with LAYER) instead of read from q, k, v, beta, g.
+template <int KIND>
+__global__ __launch_bounds__(128, 2) void chunk_prep2_layer_kernel(LayerIn li, char* __restrict__ ws,
+                                                                  int nchunks) {
+    __shared__ Prep2Lds<bf16, 128, 128> lds;
+    const long item = blockIdx.x;
+    const long bh = item / nchunks;
+    const int c = (int)(item % nchunks);
+    const long t0 = (long)c * CHUNK;
+    prep2_item<bf16, 128, 128, KIND, CHUNK, true>(nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                  ws + item * WsLayout<bf16, 128, 128>::BYTES, lds, 0, 0,
+                                                  (int)min((long)CHUNK, li.T - t0), (int)(threadIdx.x >> 6),
+                                                  (int)(threadIdx.x & 63), li, bh / li.Hv, (int)(bh % li.Hv), t0);
 }
 
 // The same prep as the recomputation after a one-launch call: it runs only if
@@ -2083,6 +2227,41 @@ hipError_t launch_chunk_fwd(int kind, int dtype, const void* q, const void* k, c
                          : fwd_t<bf16, 64>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st, hm);
     return dk == 128 ? fwd_t<float, 128>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st, hm)
                      : fwd_t<float, 64>(kind, q, k, v, beta, g, S0, o, S_final, ws, BH, T, mode, st, hm);
+}
+
+// The gated layer's prefill between its projections (bf16, d = 128): the prep
+// with the prologue in its load stage, the scan (reading the q rows the prep
+// stored), the epilogue. Workspace: the prefill's blocks, then the q rows
+// [B][Hk][T][128], then the read-out [B][Hv][T][128] (each 256-byte aligned).
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+size_t layer_prefill_workspace_bytes(long long B, long long T, int Hk, int Hv) {
+    return align256(chunk_workspace_bytes(B * Hv, T, 128, 128, DT_BF16)) + align256((size_t)(B * Hk * T * 128 * 2)) +
+           align256((size_t)(B * Hv * T * 128 * 2));
+}
+
+hipError_t launch_layer_prefill(const void* qkv, const void* conv_w, const void* conv_state, void* conv_state_out,
+                                const void* b, const void* a, const float* A_log, const float* dt_bias,
+                                const void* z, const void* norm_w, float eps, const float* S0, float* S_final,
+                                void* out, float bscale, int B, int T, int Hk, int Hv, void* ws, hipStream_t st) {
+    const int BH = B * Hv;
+    const int nchunks = (T + CHUNK - 1) / CHUNK;
+    char* w = static_cast<char*>(ws);
+    bf16* qhat = reinterpret_cast<bf16*>(w + align256(chunk_workspace_bytes(BH, T, 128, 128, DT_BF16)));
+    bf16* o = reinterpret_cast<bf16*>(reinterpret_cast<char*>(qhat) + align256((size_t)B * Hk * T * 128 * 2));
+    LayerIn li{static_cast<const bf16*>(qkv), static_cast<const bf16*>(conv_w), static_cast<const bf16*>(conv_state),
+               static_cast<bf16*>(conv_state_out), static_cast<const bf16*>(b), static_cast<const bf16*>(a), A_log,
+               dt_bias, qhat, bscale, T, Hk, Hv};
+    const unsigned items = (unsigned)((long)BH * nchunks);
+    if (a) hipLaunchKernelGGL((chunk_prep2_layer_kernel<KIND_GATED>), dim3(items), dim3(128), 0, st, li, w, nchunks);
+    else hipLaunchKernelGGL((chunk_prep2_layer_kernel<KIND_DELTANET>), dim3(items), dim3(128), 0, st, li, w, nchunks);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    HeadMap hm;
+    hm.hv = Hv;
+    hm.g = Hv / Hk;
+    e = scan_t<bf16, 128, KIND_GATED>(qhat, S0, o, S_final, w, BH, T, st, hm, nullptr);
+    if (e != hipSuccess) return e;
+    return launch_layer_epilogue(DT_BF16, o, z, norm_w, out, B, Hv, T, 128, eps, st);
 }
 
 }  // namespace dn

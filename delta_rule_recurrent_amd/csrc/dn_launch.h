@@ -131,6 +131,17 @@ hipError_t launch_layer_decode(int dtype, const void* qkv, const void* conv_w, c
                                const float* dt_bias, const void* z, const void* norm_w, float eps, float* S,
                                void* out, float beta_scale, int B, int Hk, int Hv, int d, hipStream_t st);
 
+// The gated layer's prefill between its projections in three launches (bf16,
+// d = 128, T >= 1): the prefill's prep with the layer's prologue in its load
+// stage, the scan, the gated RMSNorm. conv_state_out must not overlap
+// conv_state; a == NULL: no decay gate. ws: layer_prefill_workspace_bytes.
+size_t layer_prefill_workspace_bytes(long long B, long long T, int Hk, int Hv);
+hipError_t launch_layer_prefill(const void* qkv, const void* conv_w, const void* conv_state, void* conv_state_out,
+                                const void* b, const void* a, const float* A_log, const float* dt_bias,
+                                const void* z, const void* norm_w, float eps, const float* S0, float* S_final,
+                                void* out, float beta_scale, int B, int T, int Hk, int Hv, void* ws,
+                                hipStream_t st);
+
 // Generalized delta rule, token by token: S = (diag(exp g) - (a * kr) kr^T) S
 // + kw v^T, o = S^T q; q, kw, kr, a, g [BH][T][d], v, o [BH][T][d]. S0 and
 // S_final may be the same buffer (the decode step is T = 1 in place).

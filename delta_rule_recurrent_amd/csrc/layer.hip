@@ -18,6 +18,7 @@
 
 #include "dn_device.h"
 #include "dn_launch.h"
+#include "dn_conv.h"
 
 namespace dn {
 namespace {
@@ -26,95 +27,6 @@ constexpr int LAYER_WG = 256;   // threads per workgroup of the layer kernels
 constexpr int RUN = 8;          // consecutive tokens one lane group convolves in registers
 constexpr int CONV_K = 4;       // convolution width (its state: the last 3 inputs)
 constexpr int EPI_ROWS = 32;    // rows of the output per epilogue workgroup
-
-// Eight consecutive elements <-> fp32.
-__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
-    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
-}
-__device__ __forceinline__ void load8(const bf16* p, float (&x)[8]) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = (float)a[i];
-}
-__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
-    f32x4 a, b;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) { a[i] = x[i]; b[i] = x[4 + i]; }
-    *reinterpret_cast<f32x4*>(p) = a;
-    *reinterpret_cast<f32x4*>(p + 4) = b;
-}
-__device__ __forceinline__ void store8(bf16* p, const float (&x)[8]) {
-    bf16x8 a;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = (bf16)x[i];
-    *reinterpret_cast<bf16x8*>(p) = a;
-}
-
-// Eight consecutive elements kept in their storage type (fewer registers while in flight).
-template <typename E> struct Raw8;
-template <> struct Raw8<bf16> { bf16x8 v; };
-template <> struct Raw8<float> { f32x4 a, b; };
-__device__ __forceinline__ void load_raw(const bf16* p, Raw8<bf16>& r) {
-    r.v = *reinterpret_cast<const bf16x8*>(p);
-}
-__device__ __forceinline__ void load_raw(const float* p, Raw8<float>& r) {
-    r.a = *reinterpret_cast<const f32x4*>(p);
-    r.b = *reinterpret_cast<const f32x4*>(p + 4);
-}
-__device__ __forceinline__ float elem(const Raw8<bf16>& r, int i) { return (float)r.v[i]; }
-__device__ __forceinline__ float elem(const Raw8<float>& r, int i) { return i < 4 ? r.a[i] : r.b[i - 4]; }
-__device__ __forceinline__ void set_elem(Raw8<bf16>& r, int i, bf16 x) { r.v[i] = x; }
-__device__ __forceinline__ void set_elem(Raw8<float>& r, int i, float x) {
-    if (i < 4) r.a[i] = x;
-    else r.b[i - 4] = x;
-}
-
-// bf16 pairs: channel i of two rows as one 32-bit word (the earlier row in the
-// low half), picked with a byte permute; and the fp32 dot product of two pairs
-// plus an accumulator (products of bf16 values are exact in fp32).
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ unsigned pair_of(const Raw8<bf16>& early, const Raw8<bf16>& late, int i) {
-    const unsigned a = __builtin_bit_cast(u32x4, early.v)[i / 2];
-    const unsigned b = __builtin_bit_cast(u32x4, late.v)[i / 2];
-    return __builtin_amdgcn_perm(b, a, (i & 1) ? 0x07060302u : 0x05040100u);
-}
-__device__ __forceinline__ float dot2(unsigned x, unsigned w, float acc) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), __builtin_bit_cast(bf16x2, w),
-                                           acc, false);
-}
-
-// SiLU with the hardware exp2 and reciprocal (each within 1 ulp): x / (1 + e^-x).
-// Large negative x gives e^-x = inf and a zero reciprocal, so the result is -0.
-__device__ __forceinline__ float silu(float x) {
-    return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
-}
-
-// 1 / max(sqrt(s), 1e-12) for a sum of squares s >= 0, with the hardware rsqrt.
-__device__ __forceinline__ float inv_norm(float s) { return __builtin_amdgcn_rsqf(fmaxf(s, 1e-24f)); }
-
-// Sum over the `WIDTH` consecutive lanes that hold one row (8 or 16, aligned), with
-// data-parallel-primitive moves inside a row of 16 lanes: swap neighbours, swap
-// pairs (each quad then holds its sum), mirror within eight lanes, mirror within
-// sixteen. The additions pair up as in a butterfly, so every lane of the row ends
-// with the same bits.
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float s) {
-    return s + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), CTRL,
-                                                                  0xF, 0xF, false));
-}
-template <int WIDTH>
-__device__ __forceinline__ float row_sum(float s) {
-    static_assert(WIDTH == 8 || WIDTH == 16, "rows of 8 or 16 lanes");
-    s = dpp_add<0xB1>(s);    // quad_perm [1,0,3,2]
-    s = dpp_add<0x4E>(s);    // quad_perm [2,3,0,1]
-    s = dpp_add<0x141>(s);   // row_half_mirror
-    if (WIDTH == 16) s = dpp_add<0x140>(s);   // row_mirror
-    return s;
-}
 
 // ---------------------------------------------------------------------------
 // Prologue. Grid (ceil(T / (GROUPS*RUN)), 2*Hk + Hv, B), 256 threads. Block y

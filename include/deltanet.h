@@ -408,6 +408,37 @@ int dn_layer_epilogue(const void* o, const void* z, const void* norm_w, void* ou
                       int T, int dv, float eps, int dtype, void* stream);
 
 /*
+ * The gated layer between its projections for a prefill of T tokens (page "28.
+ * Linear attention and Gated DeltaNet", section "The full layer", steps 2-7):
+ * the work of dn_layer_prologue, dn_chunk_fwd_gqa and dn_layer_epilogue in
+ * order, with the prologue formed inside the prefill's chunk-parallel phase
+ * (its load stage) instead of written to memory and read back. Three launches:
+ * that phase, the sequential scan, the gated RMSNorm.
+ *   qkv, b, a, conv_w, conv_state, conv_state_out, A_log, dt_bias, allow_neg_eigval
+ *               as in dn_layer_prologue; a == NULL selects no decay gate. Here
+ *               conv_state_out must not overlap conv_state at all (DN_EINVAL),
+ *               or may be NULL (not written)
+ *   z, norm_w, eps, out  as in dn_layer_epilogue
+ *   S0          [B,Hv,d,d] fp32 start state or NULL (zeros); S_final [B,Hv,d,d]
+ *               fp32 end state (may be S0)
+ *   workspace   at least dn_layer_prefill_workspace(B,T,Hk,Hv,d,dtype) bytes,
+ *               256-byte aligned (DN_EWORKSPACE otherwise); it holds the chunk
+ *               blocks, the normalised q rows and the read-out
+ * The results are bitwise those of the three separate calls (dn_chunk_fwd_gqa
+ * in its two-launch form, which its one-launch form equals). bf16 with
+ * d = dk = dv = 128 only (DN_ENOTSUP otherwise: the three calls cover the
+ * rest); Hv a multiple of Hk; T == 0 only passes the history through and
+ * copies the state. Alignment: qkv, conv_w, the conv states, z, norm_w, out,
+ * S0, S_final 16 bytes; b, a element; A_log, dt_bias 4 bytes.
+ */
+size_t dn_layer_prefill_workspace(int B, int T, int Hk, int Hv, int d, int dtype);
+int dn_layer_prefill(const void* qkv, const void* conv_w, const void* conv_state, void* conv_state_out,
+                     const void* b, const void* a, const float* A_log, const float* dt_bias, const void* z,
+                     const void* norm_w, float eps, const float* S0, float* S_final, void* out,
+                     int allow_neg_eigval, int B, int T, int Hk, int Hv, int d, int dtype, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * The whole gated layer between its projections for ONE token per sequence
  * (decode), in a single kernel (page "28. Linear attention and Gated
  * DeltaNet", section "The full layer", steps 2-7, around the recurrent step

@@ -30,7 +30,7 @@ def declared_functions():
 def test_exports_every_declared_symbol():
     lib = _lib.lib()
     names = declared_functions()
-    assert len(names) == 32, names
+    assert len(names) == 34, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_lib.SIGNATURES)
@@ -380,6 +380,45 @@ def test_layer_decode_validation():
     assert _layer_decode(conv_state_out=P) == E
     assert _layer_decode(conv_state_out=P + 16) == E
     assert _layer_decode(Hk=2, Hv=2, conv_state_out=P + 16) == E
+
+
+def _layer_prefill(**kw):
+    args = dict(qkv=P, conv_w=P, conv_state=P, conv_state_out=P + 0x100000, b=P, a=P, A_log=P,
+                dt_bias=P, z=P, norm_w=P, eps=1e-6, S0=P, S_final=P, out=P, neg=0, B=2, T=100, Hk=1,
+                Hv=2, d=128, dtype=1, ws=WS, wsb=1 << 30, stream=None)
+    args.update(kw)
+    return _lib.lib().dn_layer_prefill(*[args[n] for n in (
+        "qkv", "conv_w", "conv_state", "conv_state_out", "b", "a", "A_log", "dt_bias", "z", "norm_w",
+        "eps", "S0", "S_final", "out", "neg", "B", "T", "Hk", "Hv", "d", "dtype", "ws", "wsb",
+        "stream")])
+
+
+def test_layer_prefill_validation():
+    E, N, W = _lib.DN_EINVAL, _lib.DN_ENOTSUP, _lib.DN_EWORKSPACE
+    lib = _lib.lib()
+    need = lib.dn_layer_prefill_workspace(2, 100, 1, 2, 128, 1)
+    assert need > 0 and need % 256 == 0
+    assert lib.dn_layer_prefill_workspace(2, 100, 1, 2, 64, 1) == 0      # bf16, d = 128 only
+    assert lib.dn_layer_prefill_workspace(2, 100, 1, 2, 128, 0) == 0
+    assert _layer_prefill(Hv=3, Hk=2) == E
+    assert _layer_prefill(B=0) == E
+    assert _layer_prefill(T=-1) == E
+    assert _layer_prefill(dtype=4) == E
+    assert _layer_prefill(eps=float("nan")) == E
+    for name in ("qkv", "conv_w", "b", "z", "norm_w", "S_final", "out"):
+        assert _layer_prefill(**{name: None}) == E, name
+    assert _layer_prefill(A_log=None) == E
+    for name in ("qkv", "conv_w", "conv_state", "conv_state_out", "z", "norm_w", "out", "S0",
+                 "S_final"):
+        assert _layer_prefill(**{name: MIS}) == E, name
+    assert _layer_prefill(b=ODD) == E
+    assert _layer_prefill(d=64) == N
+    assert _layer_prefill(dtype=0) == N
+    assert _layer_prefill(conv_state_out=P) == E          # no in-place history
+    assert _layer_prefill(conv_state_out=P + 16) == E
+    assert _layer_prefill(ws=None) == W
+    assert _layer_prefill(ws=WS + 16) == W
+    assert _layer_prefill(wsb=need - 1) == W
 
 
 def _ssm(fn, **kw):
