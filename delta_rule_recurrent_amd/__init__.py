@@ -573,7 +573,8 @@ def gated_deltanet_layer(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *
 
     S [B,Hv,d,d] fp32 (or None: zeros) is the carried recurrent state; it is
     updated in place when given. One token with a carried state runs as the
-    single-kernel layer step (layer_decode_step). Returns (out [B,T,Hv*d], new conv state,
+    single-kernel layer step (layer_decode_step); a bf16 prefill at d = 128 as
+    layer_prefill (the prologue inside the prefill's prep). Returns (out [B,T,Hv*d], new conv state,
     new recurrent state).
     """
     if qkv.dim() == 3 and qkv.shape[1] == 1 and S is not None:
@@ -582,6 +583,16 @@ def gated_deltanet_layer(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv, *
                                      conv_state=conv_state, eps=eps,
                                      allow_neg_eigval=allow_neg_eigval, stream=stream)
         return out, cst, S
+    B, T, C = qkv.shape
+    d = C // (2 * Hk + Hv) if Hk >= 1 and Hv >= 1 else 0
+    if qkv.dtype == torch.bfloat16 and d == 128 and T >= 1:
+        # the prologue inside the prefill's prep (bitwise the three calls below)
+        need = lib().dn_layer_prefill_workspace(B, T, Hk, Hv, d, _DT[qkv.dtype])
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = None
+        return layer_prefill(qkv, z, b, a, conv_w, A_log, dt_bias, norm_w, Hk, Hv,
+                             conv_state=conv_state, S0=S, S_final=S, eps=eps,
+                             allow_neg_eigval=allow_neg_eigval, workspace=workspace, stream=stream)
     q, k, v, beta, g, cst = layer_prologue(qkv, conv_w, b, a, A_log, dt_bias, Hk, Hv,
                                            conv_state=conv_state,
                                            allow_neg_eigval=allow_neg_eigval, stream=stream)
