@@ -77,23 +77,23 @@ CHUNK_SOURCES = ("delta_rule_recurrent_amd/csrc/chunk.hip", "delta_rule_recurren
 DECODE_SOURCES = ("delta_rule_recurrent_amd/csrc/decode.hip", "delta_rule_recurrent_amd/csrc/dn_device.h",
                   "delta_rule_recurrent_amd/csrc/dn_launch.h")
 TRAFFIC = {
-    # B=4 H=8 T=2048 d=128 (grid 1024 x 128 threads; 3670 / 4150 dispatches)
-    "chunk_prep2_kernel": {"fetch_kib": 28830.0, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
-                           "sha256": "8f02349f4bbec025861f6f2946c3688193aa35035aa7947518041e2d983cdb60"},
-    # B=4 H=8 T=2048 d=128 (grid 256 x 256 threads; 3670 / 4150 dispatches)
-    "chunk_scan_kernel": {"fetch_kib": 37109.5, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
-                          "sha256": "8f02349f4bbec025861f6f2946c3688193aa35035aa7947518041e2d983cdb60"},
-    # B=1 H=16 T=65536 d=128 (grid 240 x 256 threads; 810 / 850 dispatches)
-    "chunk_fused_kernel": {"fetch_kib": 987833.1, "write_kib": 1193989.1, "sources": CHUNK_SOURCES,
-                           "sha256": "8f02349f4bbec025861f6f2946c3688193aa35035aa7947518041e2d983cdb60"},
+    # B=4 H=8 T=2048 d=128 (grid 1024 x 128 threads; 3750 / 3990 dispatches)
+    "chunk_prep2_kernel": {"fetch_kib": 29217.2, "write_kib": 58112.0, "sources": CHUNK_SOURCES,
+                           "sha256": "87099bb4c798a6b8ed7d39510f1a473bd23d8cd85533d5a2f712a9f0248da651"},
+    # B=4 H=8 T=2048 d=128 (grid 256 x 256 threads; 3750 / 3990 dispatches)
+    "chunk_scan_kernel": {"fetch_kib": 37107.0, "write_kib": 18432.0, "sources": CHUNK_SOURCES,
+                          "sha256": "87099bb4c798a6b8ed7d39510f1a473bd23d8cd85533d5a2f712a9f0248da651"},
+    # B=1 H=16 T=65536 d=128 (grid 240 x 256 threads; 810 / 830 dispatches)
+    "chunk_fused_kernel": {"fetch_kib": 987842.3, "write_kib": 1193988.6, "sources": CHUNK_SOURCES,
+                           "sha256": "87099bb4c798a6b8ed7d39510f1a473bd23d8cd85533d5a2f712a9f0248da651"},
     # KDA B=2 H=16 T=8192 d=128 (grid 512 x 256 threads; 54 / 54 dispatches), from
     #   rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) -- python3 bench.py --no-cpu
     #       --no-prefill --no-long --no-decode
-    "chunk_fused_kda_kernel": {"fetch_kib": 283455.2, "write_kib": 367160.7, "sources": CHUNK_SOURCES,
-                               "sha256": "8f02349f4bbec025861f6f2946c3688193aa35035aa7947518041e2d983cdb60"},
+    "chunk_fused_kda_kernel": {"fetch_kib": 283280.2, "write_kib": 366915.4, "sources": CHUNK_SOURCES,
+                               "sha256": "87099bb4c798a6b8ed7d39510f1a473bd23d8cd85533d5a2f712a9f0248da651"},
     # B=256 H=16 d=128, one token (311 dispatches each)
-    "decode_step_kernel": {"fetch_kib": 136308.1, "write_kib": 263168.0, "sources": DECODE_SOURCES,
-                           "sha256": "30c4d9876956cf16da601e96b7a9b43da185fae986768f731528ff048ecaba7c"},
+    "decode_step_kernel": {"fetch_kib": 136307.8, "write_kib": 263168.0, "sources": DECODE_SOURCES,
+                           "sha256": "f4ef3522c6770c548689c443524ee18ffe39ad6d04accfc58b54f4519dfe8c8a"},
 }
 
 
