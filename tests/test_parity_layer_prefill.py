@@ -15,7 +15,8 @@ the prologue kernel's arithmetic. Checked:
     gated RMSNorm) at T in {37, 200}: bound 2e-2 (bf16), history bit for bit;
   * the bench's prefill layer size (B=4, T=2048, 8 + 8 heads of 128) bitwise
     against the three calls, whose full-size oracle parity
-    test_parity_layer_full.py checks.
+    test_parity_layer_full.py checks;
+  * T = 0: the history passes through and the state is copied.
 """
 import numpy as np
 import pytest
@@ -122,3 +123,18 @@ def test_layer_prefill_full_size_bitwise():
     assert torch.equal(cst1, cst2)
     assert torch.equal(S1, S2)
     assert torch.equal(out1, out2)
+
+
+def test_layer_prefill_no_tokens():
+    """T = 0: the history passes through unchanged and the state is copied."""
+    dn = _dn()
+    B, Hk, Hv, d = 2, 1, 2, 128
+    x = to_dev(synthetic.make_layer(B, 1, Hk, Hv, d, "bf16", seed=77, conv_state=True))
+    e = lambda t: t[:, :0].contiguous()   # noqa: E731  (no tokens)
+    S0 = _state(B, Hv, d, seed=78).cuda()
+    out, cst, S = dn.layer_prefill(e(x["qkv"]), e(x["z"]), e(x["b"]), e(x["a"]), x["conv_w"], x["A_log"],
+                                   x["dt_bias"], x["norm_w"], Hk, Hv, conv_state=x["conv_state"], S0=S0)
+    torch.cuda.synchronize()
+    assert out.shape == (B, 0, Hv * d)
+    assert torch.equal(cst, x["conv_state"])
+    assert torch.equal(S, S0)
