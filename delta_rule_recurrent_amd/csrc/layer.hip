@@ -9,11 +9,13 @@
 // the rule, each value head's read-out is RMS-normalised, multiplied by a weight
 // vector and by SiLU(z).
 //
-// All three kernels move every byte once: the prologue reads the projected rows
-// and writes the head-major q, k, v that the chunk and decode kernels take; the
-// epilogue reads the head-major read-out and z and writes token-major rows for the
-// output projection. Arithmetic is fp32 with one rounding to the storage type at
-// each output.
+// The prologue and epilogue kernels move every byte once: the prologue reads the
+// projected rows and writes the head-major q, k, v that the chunk and decode
+// kernels take; the epilogue reads the head-major read-out and z and writes
+// token-major rows for the output projection. For one decode token the whole
+// layer step is one kernel (the prologue in the decode step's load stage, the
+// norm in its store stage). Arithmetic is fp32 with one rounding to the storage
+// type at each output.
 #include <type_traits>
 
 #include "dn_device.h"
