@@ -20,6 +20,15 @@ memory each (q, k, v, o and the prefill's workspace).
 The decode step likewise on a state of 2.15G fp32 elements (8200 sequences x
 16 heads of 128 x 128): the heads that hold element 2^31 and the last head
 equal their copies, and the last one matches one step of the oracle.
+
+The gated layer's two one-call forms (dn_layer_prefill, dn_layer_decode_step)
+on seeded base sequences (``synthetic.make_layer``) tiled along the batch:
+the prefill with 2.42G elements of qkv (48 sequences x 8192 tokens, 16 + 16
+heads of 128), the decode step with a state of 2.15G fp32 elements (8200
+sequences x 16 heads). The sequences that hold element 2^31 and the last one
+equal their copies among the base sequences, bit for bit, in out, the end
+state and the new convolution history; the base sequences themselves are the
+layer parity tests' cases.
 """
 import pytest
 import torch
@@ -110,4 +119,59 @@ def test_decode_offsets_past_2_31():
     assert e <= TOL["bf16"], e
     assert eS <= TOL["bf16"], eS
     del o, S
+    torch.cuda.empty_cache()
+
+
+def _tile_layer(x, B, nb):
+    """The base sequences of ``make_layer`` repeated along the batch on the GPU
+    (sequence s carries base sequence s % nb); shared weights moved as they are."""
+    idx = torch.arange(B, device="cuda") % nb
+    out = {}
+    for n, t in x.items():
+        if n in ("qkv", "z", "b", "a", "conv_state"):
+            out[n] = t.cuda()[idx].contiguous()
+        elif isinstance(t, torch.Tensor):
+            out[n] = t.cuda()
+    return out
+
+
+def _same_as_copies(seqs, nb, *tensors):
+    for s in seqs:
+        for t in tensors:
+            assert torch.equal(t[s], t[s % nb]), s
+
+
+def test_layer_prefill_offsets_past_2_31():
+    import delta_rule_recurrent_amd as dn
+    B, T, H, d, nb = 48, 8192, 16, 128, 4
+    C = 3 * H * d
+    assert B * T * C > 2 ** 31
+    say("layer prefill past 2^31 qkv elements: B=%d T=%d H=%d+%d d=%d (%.2fG elements)"
+        % (B, T, H, H, d, B * T * C / 1e9))
+    x = _tile_layer(synthetic.make_layer(nb, T, H, H, d, "bf16", seed=4400, conv_state=True), B, nb)
+    out, cst, S = dn.layer_prefill(x["qkv"], x["z"], x["b"], x["a"], x["conv_w"], x["A_log"], x["dt_bias"],
+                                   x["norm_w"], H, H, conv_state=x["conv_state"])
+    torch.cuda.synchronize()
+    seqs = (2 ** 31 // (T * C), 2 ** 31 // (T * C) + 1, B - 1)
+    _same_as_copies(seqs, nb, out, cst, S)
+    say("  sequences %s equal their copies" % (seqs,))
+    del x, out, cst, S
+    torch.cuda.empty_cache()
+
+
+def test_layer_decode_offsets_past_2_31():
+    import delta_rule_recurrent_amd as dn
+    B, H, d, nb = 8200, 16, 128, 8
+    assert B * H * d * d > 2 ** 31
+    say("layer decode step past 2^31 state elements: B=%d H=%d+%d d=%d" % (B, H, H, d))
+    x = _tile_layer(synthetic.make_layer(nb, 1, H, H, d, "bf16", seed=4500, conv_state=True), B, nb)
+    gen = torch.Generator().manual_seed(4501)
+    S = (torch.randn(nb, H, d, d, generator=gen) * 0.02).cuda()[torch.arange(B, device="cuda") % nb]
+    out, cst = dn.layer_decode_step(x["qkv"], x["z"], x["b"], x["a"], x["conv_w"], x["A_log"], x["dt_bias"],
+                                    x["norm_w"], H, H, S, conv_state=x["conv_state"])
+    torch.cuda.synchronize()
+    seqs = (2 ** 31 // (H * d * d), 2 ** 31 // (H * d * d) + 1, B - 1)
+    _same_as_copies(seqs, nb, out, cst, S)
+    say("  sequences %s equal their copies" % (seqs,))
+    del x, out, cst, S
     torch.cuda.empty_cache()
