@@ -21,6 +21,11 @@ The decode step likewise on a state of 2.15G fp32 elements (8200 sequences x
 16 heads of 128 x 128): the heads that hold element 2^31 and the last head
 equal their copies, and the last one matches one step of the oracle.
 
+KDA's chunked prefill (dn_kda_chunk_fwd, per-channel decay g [B,H,T,dk]) the
+same way at 2 x 1040 heads x 8192 tokens (two launches; the last head also
+against the oracle) and 2 x 16 heads x 540672 tokens (the one-launch form,
+which KDA takes at 32 heads or fewer).
+
 The gated layer's two one-call forms (dn_layer_prefill, dn_layer_decode_step)
 on seeded base sequences (``synthetic.make_layer``) tiled along the batch:
 the prefill with 2.42G elements of qkv (48 sequences x 8192 tokens, 16 + 16
@@ -174,4 +179,43 @@ def test_layer_decode_offsets_past_2_31():
     _same_as_copies(seqs, nb, out, cst, S)
     say("  sequences %s equal their copies" % (seqs,))
     del x, out, cst, S
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T,H,nb", [(8192, 1040, 8), (540672, 16, 2)])
+def test_kda_offsets_past_2_31(T, H, nb):
+    import delta_rule_recurrent_amd as dn
+    B, d = 2, 128
+    BH = B * H
+    assert BH * T * d > 2 ** 31
+    say("KDA prefill past 2^31 elements: B=%d H=%d T=%d d=%d (%.2fG elements per tensor)"
+        % (B, H, T, d, BH * T * d / 1e9))
+    x = synthetic.make("kda", 1, nb, T, d, d, "bf16", seed=4600 + nb, decay_scale=0.1)
+    idx = torch.arange(BH, device="cuda") % nb
+
+    def tile(t):
+        return t[0].cuda()[idx].view(B, H, *t.shape[2:]).contiguous()
+
+    q, k, v, beta, g = (tile(x[n]) for n in ("q", "k", "v", "beta", "g"))
+    o, S = dn.kda_chunk_fwd(q, k, v, beta, g)
+    torch.cuda.synchronize()
+    del q, k, v, beta, g
+    o, S = o.view(BH, T, d), S.view(BH, d, d)
+    h_wrap = 2 ** 31 // (T * d)
+    heads = sorted({h_wrap, min(h_wrap + 1, BH - 1), BH - 1})
+    for h in heads:
+        assert torch.equal(o[h], o[h % nb]), h
+        assert torch.equal(S[h], S[h % nb]), h
+    msg = "  heads %s equal their copies" % heads
+    if T <= 8192:
+        last = (BH - 1) % nb
+        sl = lambda n: x[n][:, last:last + 1].double().numpy()   # noqa: E731
+        o_ref, S_ref = oracle.recurrent(sl("q"), sl("k"), sl("v"), sl("beta"), sl("g"), None, kind=oracle.KDA)
+        e = rel_err(o[BH - 1].unsqueeze(0).unsqueeze(0), o_ref)
+        eS = rel_err(S[BH - 1].unsqueeze(0).unsqueeze(0), S_ref)
+        msg += "; last head vs oracle: out %.3g, state %.3g" % (e, eS)
+        assert e <= TOL["bf16"], e
+        assert eS <= TOL["bf16"], eS
+    say(msg)
+    del o, S
     torch.cuda.empty_cache()
